@@ -1,0 +1,231 @@
+"""CPU oracle for the DSA hot path -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the bench's CPU-baseline leg may import
+this package.  The arithmetic lives in ``dsa_oracle.c`` (plain C, double
+precision, explicit loops); this module compiles it with gcc, converts the
+seeded inputs to float64 (exact for bf16 and f32) and marshals arguments.
+
+For sampled rows of large workloads the inputs are cut down to the requests
+that own those rows: their pages are copied into a compact pool under a
+re-numbered page table.  That copy moves values only; the oracle still reads
+every token through a page table.
+
+Parity status of each function (what pins it; see tests/test_oracle_pins.py):
+  index_scores  pinned: closed forms, ReLU/sign/head-pairing cases, causal
+                boundary, paging invariance, brute force on tiny inputs
+  topk          pinned: hand-derived tie fixtures, identity below K, dominance
+                property, numpy lexsort selection, batched == per row
+  sparse_mla    pinned: dense invariant below K vs torch SDPA, absorption
+                identity, mask equivalence, closed forms (K=1, q=0), re-masking
+  e4m3 decode   pinned: all 256 codes against torch.float8_e4m3fn
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dsa_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+FMT_F32, FMT_BF16, FMT_FP8 = 0, 1, 2
+
+
+def build(force: bool = True) -> str:
+    """Compile dsa_oracle.c into liboracle.so next to it (gcc, OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp",
+                               "-Wall", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        f64p = ctypes.POINTER(ctypes.c_double)
+        c_int, c_i64 = ctypes.c_int, ctypes.c_int64
+        lib.oracle_index_scores.argtypes = [c_int, i32p, i32p, i32p, c_int, c_int, c_int,
+                                            f64p, f64p, f64p, c_int, c_int, i32p, c_int,
+                                            f64p, c_i64]
+        lib.oracle_topk.argtypes = [c_int, i32p, i32p, f64p, c_i64, c_int, i32p, c_int, i32p]
+        lib.oracle_sparse_mla.argtypes = [c_int, i32p, i32p, i32p, c_int, c_int, c_int,
+                                          f64p, c_int, ctypes.c_void_p, i32p, c_int,
+                                          c_int, c_int, c_int, ctypes.c_double, i32p, c_int,
+                                          f64p, f64p]
+        lib.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_to_double.restype = ctypes.c_double
+        lib.oracle_decode_fp8_rows.argtypes = [ctypes.c_void_p, c_i64, c_int, c_int, f64p]
+        for f in (lib.oracle_index_scores, lib.oracle_topk, lib.oracle_sparse_mla):
+            f.restype = c_int
+        _lib = lib
+    return _lib
+
+
+def _p(a, ct):
+    return a.ctypes.data_as(ctypes.POINTER(ct))
+
+
+def _i32(x):
+    if isinstance(x, torch.Tensor):
+        x = x.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def _f64(x):
+    if isinstance(x, torch.Tensor):
+        x = x.detach().cpu().to(torch.float64).numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+class _View:
+    """A batch restricted to the requests that own `rows`, pages compacted."""
+
+    def __init__(self, batch, rows):
+        self.batch = batch
+        cu = [0]
+        for ql in batch.q_lens:
+            cu.append(cu[-1] + ql)
+        T = cu[-1]
+        self.rows = np.arange(T, dtype=np.int32) if rows is None else _i32(rows)
+        owners = sorted({int(np.searchsorted(cu, int(t), side="right") - 1) for t in self.rows})
+        self.owners = owners
+        P = batch.cfg.page_size
+        pt_old = batch.page_table.detach().cpu()
+        self.pt_stride = pt_old.shape[1]
+        pt_new = torch.full_like(pt_old, -1)
+        src_pages = []
+        for b in owners:
+            n = (batch.seq_lens[b] + P - 1) // P
+            ids = pt_old[b, :n]
+            pt_new[b, :n] = torch.arange(len(src_pages), len(src_pages) + n, dtype=torch.int32)
+            src_pages.extend(ids.tolist())
+        self.src_pages = torch.tensor(src_pages, dtype=torch.long)
+        self.num_pages = len(src_pages)
+        self.page_table = _i32(pt_new)
+        self.cu_q = _i32(cu)
+        self.seq_lens = _i32(batch.seq_lens)
+        self.n = len(self.rows)
+        self.rows_t = torch.from_numpy(self.rows.astype(np.int64))
+
+    def pool(self, pool):
+        """Compact copy of a [num_pages, P, ...] pool (on any device) to host."""
+        idx = self.src_pages.to(pool.device)
+        return pool.index_select(0, idx).cpu()
+
+    def per_row(self, x):
+        return x.index_select(0, self.rows_t.to(x.device)).cpu()
+
+
+def index_scores(batch, rows=None, ld=None):
+    """Scores [n_rows, ld] (float64, NaN beyond each row's pos)."""
+    lib = _load()
+    v = _View(batch, rows)
+    cfg = batch.cfg
+    ld = ld or max(batch.max_seq_len, 1)
+    q = _f64(v.per_row(batch.q_idx))
+    w = _f64(v.per_row(batch.w))
+    k = _f64(v.pool(batch.k_pool))
+    out = np.full((v.n, ld), np.nan, dtype=np.float64)
+    st = lib.oracle_index_scores(batch.B, _p(v.cu_q, ctypes.c_int32), _p(v.seq_lens, ctypes.c_int32),
+                                 _p(v.page_table, ctypes.c_int32), v.pt_stride, cfg.page_size,
+                                 v.num_pages, _p(q, ctypes.c_double), _p(w, ctypes.c_double),
+                                 _p(k, ctypes.c_double), cfg.hi, cfg.di,
+                                 _p(v.rows, ctypes.c_int32), v.n, _p(out, ctypes.c_double), ld)
+    if st != 0:
+        raise RuntimeError("oracle_index_scores failed with status %d" % st)
+    return out
+
+
+def topk(batch, scores, k=None, rows=None):
+    """Selected positions [n_rows, k] (int32, ascending, -1 padded).
+
+    `scores` holds the listed rows' scores ([n_rows, ld], any float type).
+    """
+    lib = _load()
+    v = _View(batch, rows)
+    k = k or batch.cfg.topk
+    s = _f64(scores)
+    assert s.shape[0] == v.n
+    out = np.empty((v.n, k), dtype=np.int32)
+    st = lib.oracle_topk(batch.B, _p(v.cu_q, ctypes.c_int32), _p(v.seq_lens, ctypes.c_int32),
+                         _p(s, ctypes.c_double), s.shape[1], k, _p(v.rows, ctypes.c_int32), v.n,
+                         _p(out, ctypes.c_int32))
+    if st != 0:
+        raise RuntimeError("oracle_topk failed with status %d" % st)
+    return out
+
+
+def sparse_mla(batch, layer, idx, rows=None, k=None):
+    """(out [n_rows, H, Dc], lse [n_rows, H]) in float64.
+
+    idx holds the listed rows' selected positions ([n_rows, k]).
+    """
+    lib = _load()
+    v = _View(batch, rows)
+    cfg = batch.cfg
+    idx = _i32(idx)
+    k = k or idx.shape[1]
+    assert idx.shape == (v.n, k)
+    q = _f64(v.per_row(batch.q[layer]))
+    pool = v.pool(batch.kv_pool[layer])
+    if cfg.kv_fmt == FMT_FP8:
+        kv = np.ascontiguousarray(pool.numpy())
+        fp8 = 1
+    else:
+        kv = _f64(pool)
+        fp8 = 0
+    out = np.zeros((v.n, cfg.heads, cfg.dc), dtype=np.float64)
+    lse = np.zeros((v.n, cfg.heads), dtype=np.float64)
+    st = lib.oracle_sparse_mla(batch.B, _p(v.cu_q, ctypes.c_int32), _p(v.seq_lens, ctypes.c_int32),
+                               _p(v.page_table, ctypes.c_int32), v.pt_stride, cfg.page_size,
+                               v.num_pages, _p(q, ctypes.c_double), fp8,
+                               kv.ctypes.data_as(ctypes.c_void_p), _p(idx, ctypes.c_int32), k,
+                               cfg.heads, cfg.dc, cfg.dr, cfg.sm_scale,
+                               _p(v.rows, ctypes.c_int32), v.n, _p(out, ctypes.c_double),
+                               _p(lse, ctypes.c_double))
+    if st != 0:
+        raise RuntimeError("oracle_sparse_mla failed with status %d" % st)
+    return out, lse
+
+
+def e4m3_to_double(byte: int) -> float:
+    return _load().oracle_e4m3_to_double(byte)
+
+
+def decode_fp8_rows(rows_u8, dc=512, dr=64):
+    """Decode [n, 656] fp8 rows into float64 [n, dc+dr] with the oracle's decoder."""
+    lib = _load()
+    if isinstance(rows_u8, torch.Tensor):
+        rows_u8 = rows_u8.detach().cpu().numpy()
+    a = np.ascontiguousarray(rows_u8, dtype=np.uint8)
+    a = a.reshape(-1, 656)
+    out = np.empty((a.shape[0], dc + dr), dtype=np.float64)
+    lib.oracle_decode_fp8_rows(a.ctypes.data_as(ctypes.c_void_p), a.shape[0], dc, dr,
+                               _p(out, ctypes.c_double))
+    return out
+
+
+def run_path(batch, rows=None):
+    """Scores -> top-k -> sparse MLA on every layer, for the listed rows.
+
+    Layer 0 is the full layer; later layers reuse its indices (IndexShare).
+    Returns dict(scores, idx, out=[per layer], lse=[per layer]).
+    """
+    sc = index_scores(batch, rows)
+    idx = topk(batch, sc, rows=rows)
+    outs, lses = [], []
+    for layer in range(len(batch.q)):
+        o, l = sparse_mla(batch, layer, idx, rows=rows)
+        outs.append(o)
+        lses.append(l)
+    return dict(scores=sc, idx=idx, out=outs, lse=lses)

@@ -1,0 +1,339 @@
+"""Pins for the CPU oracle: each test ties it to something other than itself.
+
+A plausible mistake anywhere in the oracle (a dropped ReLU, a wrong sign, a
+transposed head or dimension index, an off-by-one causal bound, an ignored
+page table, a wrong tie rule, a missing scale, V taken with the rope part,
+a wrong e4m3 exponent bias) fails at least one of these.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_07_amd import synth
+from tests import _batches
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- indexer
+
+
+def test_scores_closed_form_fixture():
+    g = _gold("index_scores_closed_form.json")
+    keys = torch.tensor(g["keys"], dtype=torch.float32)
+    b = _batches.make([1], [keys.shape[0]], [keys], torch.tensor(g["q_idx"]),
+                      torch.tensor(g["w"]), page_size=g["page_size"])
+    sc = oracle.index_scores(b)
+    assert sc[0].tolist() == g["expected_scores"]
+
+
+def test_scores_causal_boundary_and_untouched_tail():
+    # two draft rows at pos 3 and 4 of a 5-token request; row 0 must not see token 4
+    keys = [torch.ones(5, 2)]
+    b = _batches.make([2], [5], keys, torch.ones(2, 1, 2), torch.ones(2, 1), page_size=2)
+    sc = oracle.index_scores(b, ld=6)
+    assert np.all(sc[0, :4] == 2.0) and np.isnan(sc[0, 4]) and np.isnan(sc[0, 5])
+    assert np.all(sc[1, :5] == 2.0) and np.isnan(sc[1, 5])
+
+
+def test_scores_linear_in_w_and_head_permutation_invariant():
+    b = synth.make_batch(0)
+    base = oracle.index_scores(b)
+    b2 = synth.make_batch(0)
+    b2.w = b2.w * 2
+    assert np.array_equal(oracle.index_scores(b2), base * 2, equal_nan=True)
+    perm = torch.tensor([2, 0, 3, 1])
+    b3 = synth.make_batch(0)
+    b3.q_idx = b3.q_idx[:, perm]
+    b3.w = b3.w[:, perm]
+    assert np.array_equal(oracle.index_scores(b3), base, equal_nan=True)
+
+
+def test_scores_paging_invariance():
+    b = synth.make_batch(1, batch=3, ctx=(40, 300), topk=64, page_size=16)
+    base = oracle.index_scores(b)
+    for P, ident in ((16, True), (5, False), (64, False)):
+        rb = synth.repage(b, P, ident)
+        assert np.array_equal(oracle.index_scores(rb), base, equal_nan=True)
+
+
+def test_scores_brute_force_tiny():
+    # the definition summed over an explicit token list (no pages), plain Python loops
+    g = torch.Generator().manual_seed(5)
+    q_lens, seq_lens = [2, 1, 3], [7, 3, 9]
+    hi, di = 3, 4
+    keys = [torch.randint(-8, 9, (s, di), generator=g).float() / 8 for s in seq_lens]
+    T = sum(q_lens)
+    q = torch.randint(-8, 9, (T, hi, di), generator=g).float() / 8
+    w = torch.randint(-4, 5, (T, hi), generator=g).float() / 4
+    b = _batches.make(q_lens, seq_lens, keys, q, w, page_size=2, permute_seed=3)
+    sc = oracle.index_scores(b, ld=9)
+    t = 0
+    for r, (ql, sl) in enumerate(zip(q_lens, seq_lens)):
+        for j in range(ql):
+            pos = sl - ql + j
+            for s in range(9):
+                if s > pos:
+                    assert math.isnan(sc[t, s])
+                    continue
+                acc = 0.0
+                for h in range(hi):
+                    dot = sum(float(q[t, h, d]) * float(keys[r][s, d]) for d in range(di))
+                    acc += float(w[t, h]) * max(dot, 0.0)
+                assert sc[t, s] == acc
+            t += 1
+
+
+# ---------------------------------------------------------------- top-k
+
+
+def _one_row(scores):
+    n = len(scores)
+    keys = [torch.zeros(n, 1)]
+    b = _batches.make([1], [n], keys, torch.zeros(1, 1, 1), torch.zeros(1, 1), page_size=4)
+    return b, np.array([scores], dtype=np.float64)
+
+
+def test_topk_tie_fixture():
+    g = _gold("topk_ties.json")
+    b, sc = _one_row(g["scores"])
+    for case in g["cases"]:
+        got = oracle.topk(b, sc, k=case["k"])
+        assert got[0].tolist() == case["expected"], case
+
+
+def test_topk_identity_below_k_and_padding():
+    b = synth.make_batch(1, batch=4, ctx=(10, 60), topk=64)
+    sc = oracle.index_scores(b)
+    idx = oracle.topk(b, sc)
+    for t, pos in enumerate(b.positions()):
+        assert idx[t, :pos + 1].tolist() == list(range(pos + 1))
+        assert np.all(idx[t, pos + 1:] == -1)
+
+
+def _check_dominance(score_row, sel, k):
+    n = len(score_row)
+    chosen = set(int(s) for s in sel if s >= 0)
+    assert len(chosen) == min(k, n)
+    assert list(sel[:len(chosen)]) == sorted(chosen)
+    rest = [s for s in range(n) if s not in chosen]
+    if not rest:
+        return
+    worst_sel = min(score_row[s] for s in chosen)
+    best_rest = max(score_row[s] for s in rest)
+    assert worst_sel >= best_rest
+    if worst_sel == best_rest:
+        # ties at the boundary go to lower positions
+        tied_sel = [s for s in chosen if score_row[s] == worst_sel]
+        tied_rest = [s for s in rest if score_row[s] == worst_sel]
+        assert max(tied_sel) < min(tied_rest)
+
+
+def test_topk_dominance_property_with_many_ties():
+    g = torch.Generator().manual_seed(11)
+    for n, k in ((50, 7), (300, 64), (1000, 999), (129, 128)):
+        row = (torch.randint(-3, 4, (n,), generator=g).double() / 2).numpy()
+        row[::17] = -0.0
+        b, sc = _one_row(row)
+        sel = oracle.topk(b, sc, k=k)[0]
+        _check_dominance(row, sel, k)
+
+
+def test_topk_matches_numpy_lexsort():
+    g = np.random.default_rng(3)
+    for n, k in ((200, 10), (5000, 2048), (2049, 2048)):
+        row = g.integers(-50, 50, n).astype(np.float64)
+        b, sc = _one_row(row)
+        sel = oracle.topk(b, sc, k=k)[0]
+        order = np.lexsort((np.arange(n), -row))    # primary: score desc, then position
+        assert sel.tolist() == sorted(order[:k].tolist())
+
+
+def test_topk_batched_equals_per_row():
+    b = synth.make_batch(0)
+    sc = oracle.index_scores(b)
+    allrows = oracle.topk(b, sc)
+    for t in range(b.T):
+        one = oracle.topk(b, sc[t:t + 1], rows=[t])
+        assert np.array_equal(one[0], allrows[t])
+
+
+# ---------------------------------------------------------------- sparse MLA
+
+
+def _sdpa_masked(q, rows, mask, scale, dc):
+    """Library attention (torch SDPA, float64) of q [H, D] over rows [n, D] with a boolean mask."""
+    qq = q[None, :, None, :]                        # [1, H, 1, D]
+    kk = rows[None, None].expand(1, q.shape[0], -1, -1)
+    vv = rows[None, None, :, :dc].expand(1, q.shape[0], -1, -1)
+    m = mask[None, None, None, :].expand(1, q.shape[0], 1, -1)
+    out = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, attn_mask=m, scale=scale)
+    logits = (q @ rows.T) * scale
+    logits = logits.masked_fill(~mask[None, :], -math.inf)
+    return out[0, :, 0], torch.logsumexp(logits, dim=-1)
+
+
+def _tokens_of(batch, layer, b):
+    """Request b's latent rows in logical order, float64 (pages read back)."""
+    P = batch.cfg.page_size
+    pool = batch.kv_pool[layer]
+    s = torch.arange(batch.seq_lens[b])
+    rows = pool[batch.page_table[b, s // P].long(), s % P]
+    if batch.cfg.kv_fmt == synth.FMT_FP8_E4M3_B128:
+        return torch.from_numpy(oracle.decode_fp8_rows(rows))
+    return rows.double()
+
+
+def test_mla_dense_invariant_below_topk():
+    # contexts shorter than index_topk: top-k is the identity and sparse == dense
+    b = synth.make_batch(0, ctx=(40, 40), topk=64)
+    sc = oracle.index_scores(b)
+    idx = oracle.topk(b, sc)
+    out, lse = oracle.sparse_mla(b, 0, idx)
+    rows = _tokens_of(b, 0, 0)
+    for t, pos in enumerate(b.positions()):
+        mask = torch.arange(rows.shape[0]) <= pos
+        ref, ref_lse = _sdpa_masked(b.q[0][t].double(), rows, mask, b.cfg.sm_scale, b.cfg.dc)
+        assert np.allclose(out[t], ref.numpy(), rtol=0, atol=1e-12)
+        assert np.allclose(lse[t], ref_lse.numpy(), rtol=0, atol=1e-12)
+
+
+def test_mla_mask_equivalence_with_invalid_entries():
+    b = synth.make_batch(0)
+    g = torch.Generator().manual_seed(9)
+    K = b.cfg.topk
+    rows = _tokens_of(b, 0, 0)
+    idx = np.empty((b.T, K), dtype=np.int32)
+    for t, pos in enumerate(b.positions()):
+        sel = torch.randperm(pos + 1, generator=g)[:K - 6].sort().values
+        bad = torch.tensor([-1, -5, pos + 1, pos + 7, 10 ** 6, -1])
+        idx[t] = torch.cat([sel, bad]).numpy()
+    out, lse = oracle.sparse_mla(b, 0, idx)
+    for t, pos in enumerate(b.positions()):
+        mask = torch.zeros(rows.shape[0], dtype=torch.bool)
+        v = idx[t][(idx[t] >= 0) & (idx[t] <= pos)]
+        mask[torch.from_numpy(v).long()] = True
+        ref, ref_lse = _sdpa_masked(b.q[0][t].double(), rows, mask, b.cfg.sm_scale, b.cfg.dc)
+        assert np.allclose(out[t], ref.numpy(), rtol=0, atol=1e-12)
+        assert np.allclose(lse[t], ref_lse.numpy(), rtol=0, atol=1e-12)
+
+
+def test_mla_absorption_identity():
+    # textbook MHA with per-head up-projections equals absorbed attention then W_UV
+    g = torch.Generator().manual_seed(21)
+    H, dc, dr, dn, dv, n = 3, 8, 4, 5, 6, 11
+    c = torch.randn(n, dc, generator=g, dtype=torch.float64)
+    krope = torch.randn(n, dr, generator=g, dtype=torch.float64)
+    w_uk = torch.randn(H, dc, dn, generator=g, dtype=torch.float64)
+    w_uv = torch.randn(H, dc, dv, generator=g, dtype=torch.float64)
+    q_nope = torch.randn(H, dn, generator=g, dtype=torch.float64)
+    q_rope = torch.randn(H, dr, generator=g, dtype=torch.float64)
+    scale = 1.0 / math.sqrt(dn + dr)
+    sel = [0, 2, 3, 7, 10]
+    # textbook: per-head keys/values through the up-projections
+    ref = []
+    for h in range(H):
+        k_h = torch.cat([c @ w_uk[h], krope], dim=1)[sel]
+        v_h = (c @ w_uv[h])[sel]
+        p = torch.softmax(scale * (k_h @ torch.cat([q_nope[h], q_rope[h]])), dim=0)
+        ref.append(p @ v_h)
+    ref = torch.stack(ref)
+    # absorbed: q folded through W_UK, keys and values are the latent row itself
+    q_abs = torch.cat([torch.einsum("hcd,hd->hc", w_uk, q_nope), q_rope], dim=1)
+    latent = torch.cat([c, krope], dim=1)
+    keys, qi, wi = _batches.dummy_index([1], [n])
+    b = _batches.make([1], [n], keys, qi, wi, page_size=4, permute_seed=1,
+                      q_layers=[q_abs[None].float().double()], latent_layers=[[latent]],
+                      dr=dr, sm_scale=scale)
+    b.q[0] = q_abs[None]
+    b.kv_pool[0] = _batches.paginate([latent], 4, 1)[0]
+    idx = np.array([sel + [-1] * 3], dtype=np.int32)
+    out_lat, _ = oracle.sparse_mla(b, 0, idx)
+    out = torch.einsum("hc,hcv->hv", torch.from_numpy(out_lat[0]), w_uv)
+    assert torch.allclose(out, ref, rtol=0, atol=1e-10)
+
+
+def test_mla_closed_forms():
+    b = synth.make_batch(0)
+    rows = _tokens_of(b, 0, 0)
+    K = b.cfg.topk
+    # K = 1: output is that row's latent, lse is its scaled logit
+    idx1 = np.full((b.T, K), -1, dtype=np.int32)
+    picks = [3, 100, 247, 0, 5, 9, 250, 199]
+    idx1[:, 0] = picks
+    out, lse = oracle.sparse_mla(b, 0, idx1)
+    for t in range(b.T):
+        assert np.array_equal(out[t], rows[picks[t], :b.cfg.dc].numpy()[None].repeat(b.cfg.heads, 0))
+        logit = b.cfg.sm_scale * (b.q[0][t].double() @ rows[picks[t]])
+        assert np.allclose(lse[t], logit.numpy(), rtol=0, atol=1e-12)
+    # q = 0: uniform weights -> mean of selected latents, lse = log(n)
+    bz = synth.make_batch(0)
+    bz.q[0] = torch.zeros_like(bz.q[0])
+    idx = oracle.topk(bz, oracle.index_scores(bz))
+    out, lse = oracle.sparse_mla(bz, 0, idx)
+    for t in range(bz.T):
+        sel = idx[t][idx[t] >= 0]
+        mean = rows[torch.from_numpy(sel).long(), :bz.cfg.dc].mean(0).numpy()
+        assert np.allclose(out[t], mean[None], rtol=0, atol=1e-12)
+        assert np.allclose(lse[t], math.log(len(sel)), rtol=0, atol=1e-12)
+    # nothing usable: zeros and -inf
+    out, lse = oracle.sparse_mla(b, 0, np.full((b.T, K), -1, dtype=np.int32))
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+def test_mla_paging_invariance():
+    b = synth.make_batch(0)
+    idx = oracle.topk(b, oracle.index_scores(b))
+    base = oracle.sparse_mla(b, 0, idx)
+    for P, ident in ((16, False), (7, False), (64, True)):
+        rb = synth.repage(b, P, ident)
+        got = oracle.sparse_mla(rb, 0, idx)
+        assert np.array_equal(got[0], base[0]) and np.array_equal(got[1], base[1])
+
+
+def test_indexshare_layers_reuse_full_layer_indices():
+    b = synth.make_batch(1, batch=3, ctx=(300, 900), topk=128, layers=3)
+    r = oracle.run_path(b)
+    for layer in (1, 2):
+        out, lse = oracle.sparse_mla(b, layer, r["idx"])
+        assert np.array_equal(out, r["out"][layer]) and np.array_equal(lse, r["lse"][layer])
+
+
+# ---------------------------------------------------------------- fp8
+
+
+def test_e4m3_decoder_all_codes_match_torch():
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float32).double()
+    for c in range(256):
+        got = oracle.e4m3_to_double(c)
+        if math.isnan(ref[c]):
+            assert math.isnan(got), c
+        else:
+            assert got == float(ref[c]), c
+    assert oracle.e4m3_to_double(0x7E) == 448.0
+    assert oracle.e4m3_to_double(0x01) == 2.0 ** -9
+
+
+def test_fp8_row_layout_roundtrip():
+    g = torch.Generator().manual_seed(4)
+    lat = torch.randn(40, 512, generator=g)
+    rope = torch.randn(40, 64, generator=g).to(torch.bfloat16)
+    rows = synth.quantize_fp8_rows(lat, rope)
+    dec = torch.from_numpy(oracle.decode_fp8_rows(rows))
+    assert torch.equal(dec[:, 512:], rope.double())
+    # e4m3 has 3 mantissa bits: relative error <= 2^-4 for normals, plus the
+    # subnormal step of the block scale
+    amax = lat.reshape(40, 4, 128).abs().amax(-1).repeat_interleave(128, 1).double()
+    err = (dec[:, :512] - lat.double()).abs()
+    assert torch.all(err <= lat.double().abs() * 2.0 ** -4 + amax / 448 * 2.0 ** -9)
