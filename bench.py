@@ -1,0 +1,214 @@
+"""Throughput of the DSA hot path on one MI355X.
+
+One step = the whole path over one batch: lightning-indexer scores, per-row
+top-k, then sparse MLA on every layer (one full layer, plus IndexShare layers
+where the workload has them).  Inputs are seeded synthetic tensors already
+resident in HBM; several independent input sets are rotated so the 256 MB
+MALL cannot serve repeat reads.
+
+Default workload: 64 decode requests, contexts U[1024, 8192], one query each,
+index_topk 2048, indexer 64 x 128 bf16, sparse MLA with 16 heads over a
+512+64 bf16 paged latent cache (page size 64, random page tables).
+`--config N` benchmarks another workload of the same family instead.
+
+Prints one JSON line.  `value` is query rows through the whole path per
+second; `roofline` reports the dominant kernel against MI355X's HBM (8 TB/s)
+or dense bf16 MFMA (2.5 PFLOP/s) peak, with its average duration taken from
+HIP events on the launch stream inside the timed region; `cpu_baseline` is
+the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-MLA decode queries/s + indexer top-k rows/s; % HBM / MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--sets", type=int, default=0, help="input sets rotated (0 = auto)")
+    ap.add_argument("--mode", default="perf", choices=["perf", "parity"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    return ap.parse_args()
+
+
+def algorithmic(sb, path):
+    """Algorithmic bytes / flops per launch of each stage (what the method must move)."""
+    cfg = sb.cfg
+    T, K = sb.T, cfg.topk
+    pos = np.array(sb.positions(), dtype=np.int64)
+    n_scored = int((pos + 1).sum())
+    idx_es = 2 if cfg.idx_fmt == 1 else 4
+    q_es = 2 if cfg.q_fmt == 1 else 4
+    st = {}
+    st["index_scores"] = dict(
+        bytes=int(sum(sb.seq_lens)) * cfg.di * idx_es + T * cfg.hi * cfg.di * idx_es + T * cfg.hi * 4
+        + n_scored * 4,
+        flops=n_scored * 2 * cfg.hi * cfg.di)
+    st["topk"] = dict(bytes=n_scored * 4 + T * K * 4, flops=0)
+    from sparse_attention_07_amd.synth import kv_row_bytes
+    row = kv_row_bytes(cfg.kv_fmt, cfg.dc, cfg.dr)
+    idx = path.idx.cpu().numpy()
+    union = 0
+    n_valid = int((idx >= 0).sum())
+    cu = np.cumsum([0] + sb.q_lens)
+    for b in range(sb.B):
+        sel = idx[cu[b]:cu[b + 1]]
+        union += len(np.unique(sel[sel >= 0]))
+    per_layer_bytes = union * row + T * cfg.heads * (cfg.dc + cfg.dr) * q_es \
+        + T * cfg.heads * cfg.dc * q_es + T * cfg.heads * 4
+    st["sparse_mla"] = dict(bytes=per_layer_bytes * len(sb.q),
+                            flops=n_valid * cfg.heads * 2 * (cfg.dc + cfg.dr + cfg.dc) * len(sb.q),
+                            launches_per_step=len(sb.q))
+    return st
+
+
+def cpu_baseline(cfg_id, budget_s=20.0):
+    """The oracle on a bounded sample of the same workload (rows of one input set)."""
+    import oracle
+    from sparse_attention_07_amd import synth
+    sb = synth.make_batch(cfg_id, mode="perf", device="cpu", layers=1)
+    order = np.random.default_rng(0).permutation(sb.T)
+    t0 = time.perf_counter()
+    done = 0
+    # chunks of rows (one per oracle thread), repeated until about `budget_s` has passed
+    chunk = max(1, oracle.threads())
+    while time.perf_counter() - t0 < budget_s:
+        for i in range(0, sb.T, chunk):
+            oracle.run_path(sb, rows=sorted(order[i:i + chunk].tolist()))
+            done += len(order[i:i + chunk])
+            if time.perf_counter() - t0 > budget_s:
+                break
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "queries/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": "%d query rows (batch of %d, %s workload, one input set, repeated) through "
+                      "the whole path (scores, top-k, 1 MLA layer) in float64, %.1f s"
+                      % (done, sb.T, sb.cfg.name, dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    from sparse_attention_07_amd import synth
+    from sparse_attention_07_amd.path import DSAPath
+
+    cfg_id = args.config
+    base = synth.CONFIGS[cfg_id]
+    sets = args.sets or {0: 1, 1: 8, 2: 1, 3: 1, 4: 2}[cfg_id]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    paths = []
+    for i in range(sets):
+        sb = synth.make_batch(cfg_id, mode=args.mode, device=dev, seed_offset=i)
+        paths.append(DSAPath(sb))
+    torch.cuda.synchronize()
+
+    stages = ["index_scores", "topk", "sparse_mla"]
+    for i in range(args.warmup):
+        paths[i % sets].step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = {s: [] for s in stages}
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        p = paths[i % sets]
+        e = evs[i]
+        e[0].record(stream)
+        p.index_scores()
+        e[1].record(stream)
+        p.topk()
+        e[2].record(stream)
+        for layer in range(len(p.kv)):
+            p.mla(layer)
+        e[3].record(stream)
+        ev["index_scores"].append((e[0], e[1]))
+        ev["topk"].append((e[1], e[2]))
+        ev["sparse_mla"].append((e[2], e[3]))
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    stage_ms = {s: float(np.mean([a.elapsed_time(b) for a, b in ev[s]])) for s in stages}
+
+    T = paths[0].sb.T
+    alg = [algorithmic(p.sb, p) for p in paths]
+    report = {}
+    for s in stages:
+        by = float(np.mean([a[s]["bytes"] for a in alg]))
+        fl = float(np.mean([a[s]["flops"] for a in alg]))
+        launches = alg[0][s].get("launches_per_step", 1)
+        t = stage_ms[s] / 1e3
+        report[s] = {"ms": stage_ms[s], "launches_per_step": launches,
+                     "alg_bytes": by, "alg_flops": fl,
+                     "GB_s": by / t / 1e9, "TFLOP_s": fl / t / 1e12,
+                     "frac_hbm": by / t / 1e9 / HBM_PEAK_GBS,
+                     "frac_mfma": fl / t / 1e12 / MFMA_BF16_PEAK_TFS}
+    dom = max(stages, key=lambda s: stage_ms[s])
+    r = report[dom]
+    t_hbm = r["alg_bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = r["alg_flops"] / (MFMA_BF16_PEAK_TFS * 1e12)
+    bound = "hbm" if t_hbm >= t_mfma else "mfma"
+    launches = r["launches_per_step"]
+    if bound == "hbm":
+        ach = r["alg_bytes"] / launches / (stage_ms[dom] / launches / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": ach / HBM_PEAK_GBS, "traffic": None}
+    else:
+        ach = r["alg_flops"] / (stage_ms[dom] / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": ach / MFMA_BF16_PEAK_TFS, "traffic": None}
+    roof["kernel"] = dom
+    roof["alg_bytes_per_launch"] = r["alg_bytes"] / launches
+    roof["alg_flops_per_launch"] = r["alg_flops"] / launches
+    roof["avg_launch_ms"] = stage_ms[dom] / launches
+
+    cfg = paths[0].sb.cfg
+    out = {
+        "metric": METRIC,
+        "value": T / (ms_step / 1e3),
+        "unit": "queries/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.q_fmt == 1 else "f32",
+        "data": "synthetic (seeded, %s mode; %d rotated input sets)" % (args.mode, sets),
+        "config": {"workload": "%s: batch %d, q_len %d, contexts U[%d,%d], index_topk %d, "
+                               "indexer %dx%d, MLA %d heads %d+%d %s cache, page %d, %d layer(s)"
+                               % (cfg.name, cfg.batch, cfg.q_len, cfg.ctx_lo, cfg.ctx_hi, cfg.topk,
+                                  cfg.hi, cfg.di, cfg.heads, cfg.dc, cfg.dr,
+                                  {0: "f32", 1: "bf16", 2: "fp8-e4m3-b128"}[cfg.kv_fmt],
+                                  cfg.page_size, cfg.layers),
+                   "query_rows": T},
+        "indexer_topk_rows_per_s": T / ((stage_ms["index_scores"] + stage_ms["topk"]) / 1e3),
+        "sparse_mla_queries_per_s": T / (stage_ms["sparse_mla"] / len(paths[0].kv) / 1e3),
+        "stages": report,
+        "roofline": roof,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(cfg_id)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,191 @@
+/*
+ * dsa.h -- C ABI of the MI355X (gfx950) DeepSeek-Sparse-Attention hot path.
+ *
+ * Three steps run per full layer, in this order, all on one HIP stream:
+ *
+ *   dsa_index_scores   lightning-indexer score of every earlier cached token
+ *   dsa_topk           per query row, the index_topk best tokens
+ *   dsa_sparse_mla_*   absorbed MLA over only the selected latent rows
+ *
+ * IndexShare "shared" layers skip the first two calls and pass the full
+ * layer's index buffer to dsa_sparse_mla_* again (mlx-lm PR 1419 "GLM-5.2
+ * (glm_moe_dsa) inference: IndexShare, indexer RoPE/eps, int8 MLA-KV",
+ * description: only full layers run the indexer, shared layers reuse the
+ * previous full layer's top-k).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers named in dsa_batch / dsa_pool and every array argument are
+ *   DEVICE pointers, except the two structs themselves, which live on the
+ *   host and are read during the call only.  The caller owns all memory;
+ *   the library allocates nothing and keeps no state between calls.
+ * - Every call only validates its host-side arguments and enqueues kernels
+ *   on `stream` (a hipStream_t; NULL = the legacy default stream).  It never
+ *   synchronises and never reads device memory on the host, so a sequence
+ *   of calls can be captured into a HIP graph.  Grid sizes come from the
+ *   host bounds max_q_len / max_seq_len, never from device data.
+ * - A query row t of request b (cu_q_lens[b] <= t < cu_q_lens[b+1]) is the
+ *   j-th new token of that request and sits at position
+ *       pos(t) = seq_lens[b] - q_len[b] + j,   q_len[b] = cu_q_lens[b+1]-cu_q_lens[b].
+ *   It sees cached tokens 0..pos(t): multi-token (MTP draft) rows are causal
+ *   inside the draft (lmdeploy PR 4737 "feat: support GLM-5.2", section
+ *   "Changes": multi-token query handling; mlx-lm PR 1419, the commit that
+ *   re-masks gathered keys when a position has fewer valid keys than K).
+ * - Token s of request b is stored in page page_table[b*pt_stride + s/page_size]
+ *   at slot s % page_size.  Both pools (indexer keys and MLA latent) use the
+ *   same page table.  Pages are read in place, never copied (lmdeploy PR 4737,
+ *   section "Five-layer ablations": a zero-copy strided view replaced the
+ *   materialised paged cache).
+ * - Selected indices are LOGICAL token positions, ascending, padded with -1
+ *   (lmdeploy PR 4968 "add glm5.3-flash support", commit notes: sparse
+ *   FlashMLA indices are padded with invalid entries, negative means
+ *   invalid).  The page-table remap happens inside the attention kernel.
+ * - cu_q_lens must be consistent with batch and num_q_rows (cu_q_lens[B] = T).
+ *   Other device data that contradicts the host bounds (seq_lens[b] >
+ *   max_seq_len, a page id outside [0, num_pages), an index beyond pos) never
+ *   causes an out-of-bounds access: such tokens are skipped.  Each pool must
+ *   span num_pages * page_stride_bytes bytes.
+ * - Device pointers must be 16-byte aligned (DSA_ERR_ALIGN otherwise).
+ * - num_q_rows == 0 returns DSA_OK without launching anything.
+ * - After each launch hipGetLastError() is checked (DSA_ERR_HIP).
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t dsa_status;
+#define DSA_OK 0
+#define DSA_ERR_NULL 1        /* a required pointer is NULL */
+#define DSA_ERR_SHAPE 2       /* sizes inconsistent (e.g. ld < max_seq_len, k <= 0) */
+#define DSA_ERR_UNSUPPORTED 3 /* format / dimension combination not built */
+#define DSA_ERR_WORKSPACE 4   /* workspace NULL or smaller than the query says */
+#define DSA_ERR_HIP 5         /* a HIP launch failed */
+#define DSA_ERR_ALIGN 6       /* a device pointer or stride is not 16-byte aligned */
+
+/* Element formats. */
+#define DSA_F32 0
+#define DSA_BF16 1
+/* 656-byte latent rows: 512 OCP e4m3fn bytes (latent dims 0..511), four
+ * little-endian f32 scales (scale i multiplies dims 128*i..128*i+127), then
+ * the 64 rope dims as bf16.  Value = e4m3(byte) * scale.  Only valid for the
+ * MLA latent pool with dc = 512, dr = 64 (the BF16/FP8 sparse cache paths of
+ * lmdeploy PR 4737, section "Changes"; the block layout is this library's). */
+#define DSA_FP8_E4M3_B128 2
+
+/* A ragged batch of B requests and T = cu_q_lens[B] query rows. */
+typedef struct {
+  int32_t batch;          /* B >= 1 */
+  int32_t num_q_rows;     /* T >= 0; must equal cu_q_lens[B] */
+  int32_t max_q_len;      /* >= every q_len[b] (host bound, sizes grids) */
+  int32_t max_seq_len;    /* >= every seq_lens[b] (host bound, sizes grids) */
+  const int32_t *cu_q_lens;  /* device [B+1], cu_q_lens[0] = 0, non-decreasing */
+  const int32_t *seq_lens;   /* device [B], cache length including this step's rows */
+  const int32_t *page_table; /* device [B, pt_stride]; -1 marks an unused entry */
+  int32_t pt_stride;      /* entries per request in page_table */
+  int32_t page_size;      /* tokens per page, >= 1 */
+  int32_t num_pages;      /* pages in each pool */
+} dsa_batch;
+
+/* One paged pool viewed in place: token slot (page, i) starts at
+ *   base + page*page_stride_bytes + i*row_stride_bytes. */
+typedef struct {
+  const void *base;          /* device */
+  int32_t format;            /* DSA_F32 | DSA_BF16 | DSA_FP8_E4M3_B128 */
+  int32_t dim;               /* elements per row: D_I for index keys, dc+dr for latent */
+  int64_t page_stride_bytes;
+  int64_t row_stride_bytes;
+} dsa_pool;
+
+/* Library version (major*10000 + minor*100 + patch). */
+int32_t dsa_version(void);
+
+/* Static description of a status code. */
+const char *dsa_status_string(dsa_status status);
+
+/*
+ * Lightning-indexer scores (the DSA indexer of lmdeploy PR 4737, section
+ * "Changes", and mlx-lm PR 1419's description; the pages give no formula,
+ * this library computes the plain one):
+ *
+ *   scores[t*ld + s] = sum_h w[t,h] * max(0, dot(q_idx[t,h,:], k(s)))   for 0 <= s <= pos(t)
+ *
+ * q_idx    device [T, n_heads, head_dim], format q_format, contiguous
+ * w        device [T, n_heads] f32 (any extra scale is folded in by the caller)
+ * k_idx    indexer key pool, dim == head_dim, format == q_format
+ * scores   device [T, ld] f32, ld >= max_seq_len.  Entries s > pos(t) are NOT
+ *          written.
+ * Built combinations: (DSA_BF16, n_heads 64, head_dim 128) on MFMA;
+ * (DSA_F32, n_heads <= 64, head_dim <= 256) on the vector ALUs.
+ */
+dsa_status dsa_index_scores(const dsa_batch *batch, const void *q_idx, int32_t q_format,
+                            const float *w, const dsa_pool *k_idx, int32_t n_heads,
+                            int32_t head_dim, float *scores, int64_t ld, void *stream);
+
+/* Workspace bytes dsa_topk needs for these sizes (0 today; query it anyway). */
+size_t dsa_topk_workspace_bytes(int32_t num_q_rows, int32_t max_seq_len, int32_t k);
+
+/*
+ * Per-row top-k (radix top-k of lmdeploy PR 4737, section "Changes"):
+ * among s = 0..pos(t), keep the k largest scores; equal scores go to the
+ * lower s, and -0.0 equals +0.0.  When pos(t)+1 <= k every valid token is
+ * kept (mstar PR 387 "GLM-5.2 with MLA, fp8 MoE and DSA", section "Body":
+ * below index_topk the sparse pick is all tokens).  Output idx[t*k + j]:
+ * selected positions in ascending order, then -1.  Only entries
+ * s <= min(pos(t), ld-1) of each score row are read.  Scores must be
+ * finite.
+ * scores   device [T, ld] f32;  idx  device [T, k] int32
+ * ws       device workspace of dsa_topk_workspace_bytes() bytes (may be NULL when 0)
+ */
+dsa_status dsa_topk(const dsa_batch *batch, const float *scores, int64_t ld, int32_t k,
+                    int32_t *idx, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes dsa_sparse_mla_decode (prefill != 0: _prefill) needs. */
+size_t dsa_sparse_mla_workspace_bytes(int32_t num_q_rows, int32_t n_heads, int32_t k,
+                                      int32_t dc, int32_t prefill);
+
+/*
+ * Sparse weight-absorbed MLA over the selected latent rows (FlashMLA sparse
+ * decode of lmdeploy PR 4737 section "Changes"; the single- and small-L
+ * gather path of mlx-lm PR 1419; mstar PR 387 section "Shared code",
+ * MLA with weight absorption).  For each row t and head h:
+ *
+ *   l_j = sm_scale * dot(q[t,h,0:dc+dr], row(idx[t,j])[0:dc+dr])   for usable j
+ *   out[t,h,:] = sum_j softmax(l)_j * row(idx[t,j])[0:dc]
+ *   lse[t,h]   = log(sum_j exp(l_j))          (natural log; NULL to skip)
+ *
+ * A j is usable when 0 <= idx[t,j] <= pos(t) and its page is mapped; others
+ * are skipped.  A row with no usable j gives out = 0 and lse = -inf.
+ * q        device [T, n_heads, dc+dr], format q_format, contiguous
+ * kv       latent pool, dim == dc+dr
+ * idx      device [T, k] int32 (the dsa_topk output, or a shared layer's copy)
+ * out      device [T, n_heads, dc], format q_format
+ * ws       device workspace of dsa_sparse_mla_workspace_bytes() bytes
+ * Built combinations: q DSA_BF16 with kv DSA_BF16 or DSA_FP8_E4M3_B128,
+ * dc 512, dr 64, n_heads a multiple of 16 up to 128 (MFMA); q and kv DSA_F32
+ * with dc+dr <= 1024, n_heads <= 128, k <= 4096 (vector ALUs).
+ * _decode and _prefill compute the same function; they differ only in how
+ * the work is split across workgroups (decode splits the selected rows of
+ * each query to fill the GPU, prefill does not).
+ */
+dsa_status dsa_sparse_mla_decode(const dsa_batch *batch, const void *q, int32_t q_format,
+                                 const dsa_pool *kv, const int32_t *idx, int32_t k,
+                                 int32_t n_heads, int32_t dc, int32_t dr, float sm_scale,
+                                 void *out, float *lse, void *ws, size_t ws_bytes, void *stream);
+
+dsa_status dsa_sparse_mla_prefill(const dsa_batch *batch, const void *q, int32_t q_format,
+                                  const dsa_pool *kv, const int32_t *idx, int32_t k,
+                                  int32_t n_heads, int32_t dc, int32_t dr, float sm_scale,
+                                  void *out, float *lse, void *ws, size_t ws_bytes,
+                                  void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

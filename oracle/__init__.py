@@ -67,6 +67,7 @@ def _load():
         lib.oracle_decode_fp8_rows.argtypes = [ctypes.c_void_p, c_i64, c_int, c_int, f64p]
         for f in (lib.oracle_index_scores, lib.oracle_topk, lib.oracle_sparse_mla):
             f.restype = c_int
+        lib.oracle_threads.restype = c_int
         _lib = lib
     return _lib
 
@@ -105,7 +106,7 @@ class _View:
         pt_new = torch.full_like(pt_old, -1)
         src_pages = []
         for b in owners:
-            n = (batch.seq_lens[b] + P - 1) // P
+            n = min((batch.seq_lens[b] + P - 1) // P, self.pt_stride)
             ids = pt_old[b, :n]
             pt_new[b, :n] = torch.arange(len(src_pages), len(src_pages) + n, dtype=torch.int32)
             src_pages.extend(ids.tolist())
@@ -196,6 +197,11 @@ def sparse_mla(batch, layer, idx, rows=None, k=None):
     if st != 0:
         raise RuntimeError("oracle_sparse_mla failed with status %d" % st)
     return out, lse
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's row loops run on."""
+    return _load().oracle_threads()
 
 
 def e4m3_to_double(byte: int) -> float:

@@ -302,3 +302,15 @@ int oracle_sparse_mla(int B, const int32_t *cu_q, const int32_t *seq_lens,
 void oracle_decode_fp8_rows(const uint8_t *rows, int64_t n_rows, int Dc, int Dr, double *dst) {
   for (int64_t r = 0; r < n_rows; ++r) decode_fp8_row(rows + r * 656, Dc, Dr, dst + r * (Dc + Dr));
 }
+
+/* Threads the OpenMP loops above use (1 when built without OpenMP). */
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+int oracle_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

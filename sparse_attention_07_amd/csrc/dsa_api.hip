@@ -1,0 +1,172 @@
+// C ABI of the DSA library: host-side validation, then kernel launches on the
+// caller's stream.  Nothing here allocates, synchronises or reads device memory.
+#include <hip/hip_runtime.h>
+
+#include "../../include/dsa.h"
+#include "dsa_launch.h"
+
+namespace {
+
+using dsa::BatchArgs;
+using dsa::PoolArgs;
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Shared batch checks.  Returns DSA_OK and fills `ba`, or an error.
+dsa_status check_batch(const dsa_batch* b, BatchArgs* ba) {
+  if (b == nullptr) return DSA_ERR_NULL;
+  if (b->batch < 1 || b->num_q_rows < 0 || b->max_q_len < 0 || b->max_seq_len < 0 ||
+      b->page_size < 1 || b->pt_stride < 1 || b->num_pages < 0)
+    return DSA_ERR_SHAPE;
+  if (b->num_q_rows > 0) {
+    if (b->cu_q_lens == nullptr || b->seq_lens == nullptr || b->page_table == nullptr)
+      return DSA_ERR_NULL;
+    if (b->max_q_len < 1 || (int64_t)b->max_q_len * b->batch < b->num_q_rows) return DSA_ERR_SHAPE;
+    if (!aligned(b->cu_q_lens, 4) || !aligned(b->seq_lens, 4) || !aligned(b->page_table, 4))
+      return DSA_ERR_ALIGN;
+  }
+  *ba = BatchArgs{b->batch, b->num_q_rows, b->max_q_len, b->max_seq_len, b->cu_q_lens,
+                  b->seq_lens, b->page_table, b->pt_stride, b->page_size, b->num_pages};
+  return DSA_OK;
+}
+
+dsa_status check_pool(const dsa_pool* p, int64_t row_bytes, size_t align, PoolArgs* pa) {
+  if (p == nullptr || p->base == nullptr) return DSA_ERR_NULL;
+  if (p->row_stride_bytes < row_bytes || p->page_stride_bytes < 0) return DSA_ERR_SHAPE;
+  if (!aligned(p->base, align) || (p->row_stride_bytes % (int64_t)align) != 0 ||
+      (p->page_stride_bytes % (int64_t)align) != 0)
+    return DSA_ERR_ALIGN;
+  *pa = PoolArgs{p->base, p->format, p->dim, p->page_stride_bytes, p->row_stride_bytes};
+  return DSA_OK;
+}
+
+dsa_status hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
+
+dsa_status sparse_mla(const dsa_batch* batch, const void* q, int32_t q_format, const dsa_pool* kv,
+                      const int32_t* idx, int32_t k, int32_t n_heads, int32_t dc, int32_t dr,
+                      float sm_scale, void* out, float* lse, void* ws, size_t ws_bytes,
+                      hipStream_t stream, bool prefill) {
+  BatchArgs ba;
+  dsa_status st = check_batch(batch, &ba);
+  if (st != DSA_OK) return st;
+  if (ba.num_q_rows == 0) return DSA_OK;
+  if (q == nullptr || kv == nullptr || idx == nullptr || out == nullptr) return DSA_ERR_NULL;
+  if (k < 1 || n_heads < 1 || dc < 1 || dr < 0) return DSA_ERR_SHAPE;
+  if (kv->dim != dc + dr) return DSA_ERR_SHAPE;
+  if (!aligned(idx, 4) || (lse != nullptr && !aligned(lse, 4))) return DSA_ERR_ALIGN;
+  PoolArgs pa;
+  if (q_format == DSA_BF16 && (kv->format == DSA_BF16 || kv->format == DSA_FP8_E4M3_B128)) {
+    if (dc != 512 || dr != 64 || n_heads % 16 != 0 || n_heads > 128) return DSA_ERR_UNSUPPORTED;
+    const int64_t row_bytes = kv->format == DSA_BF16 ? 1152 : 656;
+    if ((st = check_pool(kv, row_bytes, 16, &pa)) != DSA_OK) return st;
+    if (!aligned(q, 16) || !aligned(out, 16)) return DSA_ERR_ALIGN;
+    const dsa::MlaPlan plan = dsa::plan_sparse_mla(ba.num_q_rows, n_heads, k, dc, prefill);
+    if (plan.ws_bytes > 0) {
+      if (ws == nullptr) return DSA_ERR_WORKSPACE;
+      if (ws_bytes < plan.ws_bytes) return DSA_ERR_WORKSPACE;
+      if (!aligned(ws, 16)) return DSA_ERR_ALIGN;
+    }
+    return hip_status(dsa::launch_sparse_mla_bf16(ba, q, pa, idx, k, n_heads, sm_scale, out, lse,
+                                                  ws, plan, stream));
+  }
+  if (q_format == DSA_F32 && kv->format == DSA_F32) {
+    if (dc + dr > 1024 || k > 4096) return DSA_ERR_UNSUPPORTED;
+    if ((st = check_pool(kv, (int64_t)(dc + dr) * 4, 4, &pa)) != DSA_OK) return st;
+    if (!aligned(q, 4) || !aligned(out, 4)) return DSA_ERR_ALIGN;
+    return hip_status(dsa::launch_sparse_mla_f32(ba, q, pa, idx, k, n_heads, dc, dr, sm_scale, out,
+                                                 lse, stream));
+  }
+  return DSA_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t dsa_version(void) { return 100; }
+
+const char* dsa_status_string(dsa_status status) {
+  switch (status) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_NULL: return "a required pointer is NULL";
+    case DSA_ERR_SHAPE: return "inconsistent sizes";
+    case DSA_ERR_UNSUPPORTED: return "format or dimension combination not supported";
+    case DSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case DSA_ERR_HIP: return "HIP launch failed";
+    case DSA_ERR_ALIGN: return "pointer or stride not aligned";
+    default: return "unknown status";
+  }
+}
+
+dsa_status dsa_index_scores(const dsa_batch* batch, const void* q_idx, int32_t q_format,
+                            const float* w, const dsa_pool* k_idx, int32_t n_heads,
+                            int32_t head_dim, float* scores, int64_t ld, void* stream) {
+  BatchArgs ba;
+  dsa_status st = check_batch(batch, &ba);
+  if (st != DSA_OK) return st;
+  if (ba.num_q_rows == 0) return DSA_OK;
+  if (q_idx == nullptr || w == nullptr || k_idx == nullptr || scores == nullptr) return DSA_ERR_NULL;
+  if (n_heads < 1 || head_dim < 1 || ld < 1 || ld < ba.max_seq_len) return DSA_ERR_SHAPE;
+  if (k_idx->format != q_format || k_idx->dim != head_dim) return DSA_ERR_SHAPE;
+  if (!aligned(w, 4) || !aligned(scores, 4)) return DSA_ERR_ALIGN;
+  PoolArgs pa;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (q_format == DSA_BF16) {
+    if (n_heads != 64 || head_dim != 128) return DSA_ERR_UNSUPPORTED;
+    if ((st = check_pool(k_idx, 256, 16, &pa)) != DSA_OK) return st;
+    if (!aligned(q_idx, 16)) return DSA_ERR_ALIGN;
+    return hip_status(dsa::launch_index_scores_bf16(ba, q_idx, w, pa, scores, ld, s));
+  }
+  if (q_format == DSA_F32) {
+    if (n_heads > 64 || head_dim > 256 || n_heads * head_dim > 8192) return DSA_ERR_UNSUPPORTED;
+    if ((st = check_pool(k_idx, (int64_t)head_dim * 4, 4, &pa)) != DSA_OK) return st;
+    if (!aligned(q_idx, 4)) return DSA_ERR_ALIGN;
+    return hip_status(dsa::launch_index_scores_f32(ba, q_idx, w, pa, n_heads, head_dim, scores, ld, s));
+  }
+  return DSA_ERR_UNSUPPORTED;
+}
+
+size_t dsa_topk_workspace_bytes(int32_t num_q_rows, int32_t max_seq_len, int32_t k) {
+  (void)num_q_rows;
+  (void)max_seq_len;
+  (void)k;
+  return 0;
+}
+
+dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld, int32_t k,
+                    int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  BatchArgs ba;
+  dsa_status st = check_batch(batch, &ba);
+  if (st != DSA_OK) return st;
+  if (ba.num_q_rows == 0) return DSA_OK;
+  if (scores == nullptr || idx == nullptr) return DSA_ERR_NULL;
+  if (k < 1 || ld < 1 || ld < ba.max_seq_len) return DSA_ERR_SHAPE;
+  if (!aligned(scores, 4) || !aligned(idx, 4)) return DSA_ERR_ALIGN;
+  return hip_status(dsa::launch_topk(ba, scores, ld, k, idx, static_cast<hipStream_t>(stream)));
+}
+
+size_t dsa_sparse_mla_workspace_bytes(int32_t num_q_rows, int32_t n_heads, int32_t k, int32_t dc,
+                                      int32_t prefill) {
+  return dsa::plan_sparse_mla(num_q_rows, n_heads, k, dc, prefill != 0).ws_bytes;
+}
+
+dsa_status dsa_sparse_mla_decode(const dsa_batch* batch, const void* q, int32_t q_format,
+                                 const dsa_pool* kv, const int32_t* idx, int32_t k,
+                                 int32_t n_heads, int32_t dc, int32_t dr, float sm_scale,
+                                 void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return sparse_mla(batch, q, q_format, kv, idx, k, n_heads, dc, dr, sm_scale, out, lse, ws,
+                    ws_bytes, static_cast<hipStream_t>(stream), false);
+}
+
+dsa_status dsa_sparse_mla_prefill(const dsa_batch* batch, const void* q, int32_t q_format,
+                                  const dsa_pool* kv, const int32_t* idx, int32_t k,
+                                  int32_t n_heads, int32_t dc, int32_t dr, float sm_scale,
+                                  void* out, float* lse, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  return sparse_mla(batch, q, q_format, kv, idx, k, n_heads, dc, dr, sm_scale, out, lse, ws,
+                    ws_bytes, static_cast<hipStream_t>(stream), true);
+}
+
+}  // extern "C"

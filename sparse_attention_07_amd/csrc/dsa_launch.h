@@ -1,0 +1,52 @@
+// Host-side launch interface between the C ABI (dsa_api.hip) and the kernels.
+// Every launcher trusts that dsa_api.hip validated its arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+struct BatchArgs {
+  int batch, num_q_rows, max_q_len, max_seq_len;
+  const int32_t* cu_q;
+  const int32_t* seq_lens;
+  const int32_t* page_table;
+  int pt_stride, page_size, num_pages;
+};
+
+struct PoolArgs {
+  const void* base;
+  int format, dim;
+  int64_t page_stride, row_stride;
+};
+
+hipError_t launch_index_scores_bf16(const BatchArgs& ba, const void* q_idx, const float* w,
+                                    const PoolArgs& pool, float* scores, int64_t ld,
+                                    hipStream_t stream);
+hipError_t launch_index_scores_f32(const BatchArgs& ba, const void* q_idx, const float* w,
+                                   const PoolArgs& pool, int n_heads, int head_dim, float* scores,
+                                   int64_t ld, hipStream_t stream);
+
+hipError_t launch_topk(const BatchArgs& ba, const float* scores, int64_t ld, int k, int32_t* idx,
+                       hipStream_t stream);
+
+// Split plan of the MFMA sparse-MLA kernel (rows of each query cut into `splits`
+// ranges of `rows_per_split`); workspace holds the partial results.
+struct MlaPlan {
+  int splits;
+  int rows_per_split;
+  size_t ws_bytes;
+};
+MlaPlan plan_sparse_mla(int num_q_rows, int n_heads, int k, int dc, bool prefill);
+
+hipError_t launch_sparse_mla_bf16(const BatchArgs& ba, const void* q, const PoolArgs& kv,
+                                  const int32_t* idx, int k, int n_heads, float sm_scale,
+                                  void* out, float* lse, void* ws, const MlaPlan& plan,
+                                  hipStream_t stream);
+hipError_t launch_sparse_mla_f32(const BatchArgs& ba, const void* q, const PoolArgs& kv,
+                                 const int32_t* idx, int k, int n_heads, int dc, int dr,
+                                 float sm_scale, void* out, float* lse, hipStream_t stream);
+
+}  // namespace dsa

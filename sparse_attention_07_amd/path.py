@@ -1,0 +1,61 @@
+"""The DSA hot path over one batch: indexer scores -> top-k -> sparse MLA per layer.
+
+Allocates the outputs once (torch, on the batch's device) and enqueues the
+library calls on the current stream.  Layer 0 is a full layer; layers 1..L-1
+are IndexShare layers that reuse its indices (mlx-lm PR 1419, description:
+shared layers reuse the previous full layer's top-k).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import dsa
+from .synth import torch_dtype
+
+
+class DSAPath:
+    def __init__(self, sb, prefill: bool | None = None):
+        cfg = sb.cfg
+        self.sb = sb
+        self.cfg = cfg
+        dev = sb.q_idx.device
+        self.batch = dsa.batch_from(sb)
+        self.k_pool = dsa.make_pool(sb.k_pool, cfg.idx_fmt, cfg.di)
+        self.kv = [dsa.make_pool(p, cfg.kv_fmt, cfg.dc + cfg.dr) for p in sb.kv_pool]
+        T = sb.T
+        # score rows padded to a multiple of 64 entries (256 B)
+        self.ld = max(64, (sb.max_seq_len + 63) // 64 * 64)
+        self.scores = torch.empty((T, self.ld), dtype=torch.float32, device=dev)
+        self.idx = torch.empty((T, cfg.topk), dtype=torch.int32, device=dev)
+        odt = torch_dtype(cfg.q_fmt)
+        self.out = [torch.empty((T, cfg.heads, cfg.dc), dtype=odt, device=dev) for _ in sb.q]
+        self.lse = [torch.empty((T, cfg.heads), dtype=torch.float32, device=dev) for _ in sb.q]
+        self.prefill = (sb.max_q_len > 64) if prefill is None else prefill
+        self.ws_bytes = dsa.dsa_sparse_mla_workspace_bytes(T, cfg.heads, cfg.topk, cfg.dc, self.prefill)
+        self.ws = torch.empty((max(self.ws_bytes, 16),), dtype=torch.uint8, device=dev)
+        self.topk_ws_bytes = dsa.dsa_topk_workspace_bytes(T, sb.max_seq_len, cfg.topk)
+        self.topk_ws = (torch.empty((self.topk_ws_bytes,), dtype=torch.uint8, device=dev)
+                        if self.topk_ws_bytes else None)
+
+    def index_scores(self, stream=None):
+        c = self.cfg
+        dsa.dsa_index_scores(self.batch, self.sb.q_idx, c.idx_fmt, self.sb.w, self.k_pool, c.hi, c.di,
+                             self.scores, self.ld, stream)
+
+    def topk(self, stream=None):
+        dsa.dsa_topk(self.batch, self.scores, self.ld, self.cfg.topk, self.idx, self.topk_ws,
+                     self.topk_ws_bytes, stream)
+
+    def mla(self, layer: int, idx=None, stream=None):
+        c = self.cfg
+        fn = dsa.dsa_sparse_mla_prefill if self.prefill else dsa.dsa_sparse_mla_decode
+        fn(self.batch, self.sb.q[layer], c.q_fmt, self.kv[layer], self.idx if idx is None else idx,
+           c.topk, c.heads, c.dc, c.dr, c.sm_scale, self.out[layer], self.lse[layer], self.ws,
+           self.ws_bytes, stream)
+
+    def step(self, stream=None):
+        """One pass of the whole path: full layer, then the IndexShare layers."""
+        self.index_scores(stream)
+        self.topk(stream)
+        for layer in range(len(self.kv)):
+            self.mla(layer, stream=stream)

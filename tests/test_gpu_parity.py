@@ -1,0 +1,219 @@
+"""GPU path vs the CPU oracle, through the C ABI (needs an MI355X).
+
+Indices must match bit-exactly (indexer tensors are drawn as small
+power-of-two-scaled integers, so every fp32 score is exact); scores must equal
+the oracle's exactly; attention outputs and lse within
+|g - r| <= atol + 1e-2 |r| (atol 2e-2 bf16, 6e-2 fp8 cache, 1e-4 f32).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_07_amd import synth
+from tests import _parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _say(*a):
+    print("[gpu-test]", *a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sparse_attention_07_amd import dsa  # noqa: F401  (raises if libdsa.so is missing)
+    yield
+
+
+def _run(sb, prefill=None):
+    from sparse_attention_07_amd.path import DSAPath
+    p = DSAPath(sb, prefill=prefill)
+    p.step()
+    torch.cuda.synchronize()
+    return p
+
+
+def test_tiny_full_path():
+    sb = synth.make_batch(0, device=DEV)
+    _say("tiny config, all rows")
+    p = _run(sb)
+    _parity.check_path(sb, p)
+
+
+REDUCED = {
+    "decode16": dict(cfg=1, batch=6, ctx=(100, 3000), topk=512),
+    "decode16_p16": dict(cfg=1, batch=5, ctx=(1, 2100), topk=256, page_size=16),
+    "decode16_p5": dict(cfg=1, batch=4, ctx=(300, 1300), topk=256, page_size=5),
+    "decode128_share": dict(cfg=2, batch=5, ctx=(600, 5000), topk=512, layers=3),
+    "prefill": dict(cfg=3, q_len=300, ctx=(2000, 2000), topk=512),
+    "prefill_short": dict(cfg=3, q_len=130, ctx=(700, 700), topk=512),
+    "mtp_fp8": dict(cfg=4, batch=3, ctx=(3000, 9000), topk=512),
+    "mtp_fp8_near_k": dict(cfg=4, batch=4, ctx=(509, 516), topk=512),
+}
+
+
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_reduced_configs_all_rows(name):
+    kw = dict(REDUCED[name])
+    cfg = kw.pop("cfg")
+    sb = synth.make_batch(cfg, device=DEV, **kw)
+    _say(name, "T=%d B=%d max_seq=%d" % (sb.T, sb.B, sb.max_seq_len))
+    p = _run(sb)
+    _parity.check_path(sb, p)
+
+
+def _sample_rows(sb, n=6):
+    pos = sb.positions()
+    T = sb.T
+    picks = {0, T - 1, int(np.argmax(pos)), int(np.argmin(pos))}
+    g = np.random.default_rng(123)
+    while len(picks) < min(n, T):
+        picks.add(int(g.integers(0, T)))
+    return sorted(picks)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_full_size_sampled_rows(cfg):
+    sb = synth.make_batch(cfg, device=DEV)
+    _say("full config", cfg, synth.CONFIGS[cfg].name, "T=%d B=%d max_seq=%d" % (sb.T, sb.B, sb.max_seq_len))
+    p = _run(sb)
+    rows = _sample_rows(sb)
+    _parity.check_path(sb, p, rows=rows)
+    # every row: indices ascending, valid count = min(K, pos+1), all within [0, pos]
+    idx = p.idx.cpu().numpy()
+    pos = np.array(sb.positions())
+    K = sb.cfg.topk
+    nvalid = (idx >= 0).sum(1)
+    assert np.array_equal(nvalid, np.minimum(K, pos + 1))
+    for t in range(0, sb.T, max(1, sb.T // 64)):
+        v = idx[t, :nvalid[t]]
+        assert np.all(np.diff(v) > 0) and v[0] >= 0 and v[-1] <= pos[t]
+        assert np.all(idx[t, nvalid[t]:] == -1)
+    for out in p.out:
+        assert torch.isfinite(out.float()).all()
+
+
+def _row_batch(scores_rows, K):
+    """One request per score row, q_len 1, seq_len = row length."""
+    n = [len(r) for r in scores_rows]
+    sb = synth.make_batch(1, batch=len(n), ctx=(1, 1), topk=K, layers=0)
+    sb.seq_lens = n
+    sb.q_lens = [1] * len(n)
+    sb.seq_lens_t = torch.tensor(n, dtype=torch.int32)
+    sb.cu_q = torch.arange(len(n) + 1, dtype=torch.int32)
+    sb.page_table = torch.zeros((len(n), 1), dtype=torch.int32)
+    return sb
+
+
+@pytest.mark.parametrize("K", [1, 7, 64, 2048])
+def test_topk_ties_and_lengths(K):
+    from sparse_attention_07_amd import dsa
+    g = torch.Generator().manual_seed(K)
+    lens = [1, K - 1 if K > 1 else 1, K, K + 1, 3 * K + 5, 1000, 32768, 32769, 70001]
+    rows = []
+    for i, n in enumerate(lens):
+        if i % 3 == 0:
+            r = torch.randint(-3, 4, (n,), generator=g).float() / 2       # heavy ties
+        elif i % 3 == 1:
+            r = torch.randint(-1000, 1000, (n,), generator=g).float() / 64
+        else:
+            r = torch.zeros(n)                                              # all equal
+        r[::13] = -0.0
+        rows.append(r)
+    sb = _row_batch(rows, K)
+    ld = max(lens)
+    scores = torch.full((len(rows), ld), float("nan"))
+    for i, r in enumerate(rows):
+        scores[i, :len(r)] = r
+    ref = oracle.topk(sb, scores.double().numpy(), k=K)
+    _say("topk ties K=%d" % K)
+    b = dsa.make_batch(sb.cu_q.to(DEV), sb.seq_lens_t.to(DEV), sb.page_table.to(DEV), len(rows), 1,
+                       ld, 16, 1)
+    sd = scores.to(DEV)
+    idx = torch.full((len(rows), K), 12345, dtype=torch.int32, device=DEV)
+    dsa.dsa_topk(b, sd, ld, K, idx)
+    torch.cuda.synchronize()
+    _parity.check_idx_exact(idx, ref)
+
+
+def test_mla_invalid_entries_and_closed_forms():
+    from sparse_attention_07_amd import dsa
+    from sparse_attention_07_amd.path import DSAPath
+    sb = synth.make_batch(1, batch=4, ctx=(300, 900), topk=64, device=DEV)
+    p = DSAPath(sb)
+    K = sb.cfg.topk
+    pos = sb.positions()
+    g = torch.Generator().manual_seed(3)
+    idx = torch.full((sb.T, K), -1, dtype=torch.int32)
+    for t in range(sb.T):
+        if t == 0:
+            continue                                       # no usable entry at all
+        sel = torch.randperm(pos[t] + 1, generator=g)[:K - 8].to(torch.int32)
+        if t == 1:
+            sel = sel[:1]                                  # a single row: out = that latent
+        junk = torch.tensor([-1, -7, pos[t] + 1, pos[t] + 100, 2 ** 30, -1, -1, -1], dtype=torch.int32)
+        idx[t, :len(sel)] = sel
+        idx[t, len(sel):len(sel) + 8] = junk
+    idx_d = idx.to(DEV)
+    _say("mla with invalid entries")
+    p.mla(0, idx=idx_d)
+    torch.cuda.synchronize()
+    out, lse = oracle.sparse_mla(sb, 0, idx.numpy())
+    _parity.assert_within(p.out[0].float().cpu().numpy(), out, _parity.ATOL_BF16, what="out")
+    _parity.assert_within(p.lse[0].cpu().numpy(), lse, _parity.ATOL_BF16, what="lse")
+    assert torch.all(p.out[0][0] == 0) and torch.all(torch.isneginf(p.lse[0][0]))
+
+
+def test_empty_batch_is_a_no_op():
+    from sparse_attention_07_amd import dsa
+    sb = synth.make_batch(1, batch=2, ctx=(100, 200), topk=64, device=DEV)
+    b = dsa.batch_from(sb)
+    b.num_q_rows = 0
+    scores = torch.full((2, 256), 7.0, device=DEV)
+    idx = torch.full((2, 64), 9, dtype=torch.int32, device=DEV)
+    out = torch.full((2, 16, 512), 3.0, dtype=torch.bfloat16, device=DEV)
+    kp = dsa.make_pool(sb.k_pool, sb.cfg.idx_fmt, 128)
+    kv = dsa.make_pool(sb.kv_pool[0], sb.cfg.kv_fmt, 576)
+    dsa.dsa_index_scores(b, sb.q_idx, 1, sb.w, kp, 64, 128, scores, 256)
+    dsa.dsa_topk(b, scores, 256, 64, idx)
+    dsa.dsa_sparse_mla_decode(b, sb.q[0], 1, kv, idx, 64, 16, 512, 64, 0.1, out)
+    torch.cuda.synchronize()
+    assert torch.all(scores == 7.0) and torch.all(idx == 9) and torch.all(out == 3.0)
+
+
+def test_determinism_bitwise():
+    sb = synth.make_batch(4, batch=3, ctx=(3000, 6000), topk=512, mode="perf", device=DEV)
+    _say("determinism")
+    a = _run(sb)
+    b = _run(sb)
+    assert torch.equal(a.scores, b.scores) or torch.equal(
+        torch.nan_to_num(a.scores, nan=0.0), torch.nan_to_num(b.scores, nan=0.0))
+    assert torch.equal(a.idx, b.idx)
+    assert torch.equal(a.out[0], b.out[0]) and torch.equal(a.lse[0], b.lse[0])
+
+
+def test_perf_mode_index_overlap():
+    """Real-valued draws: fp32 summation order may move boundary picks; overlap stays near 1."""
+    sb = synth.make_batch(1, batch=8, ctx=(3000, 8192), mode="perf", device=DEV)
+    _say("perf-mode overlap")
+    p = _run(sb)
+    rows = [0, 3, 7]
+    ref_scores = oracle.index_scores(sb, rows, ld=p.ld)
+    ref_idx = oracle.topk(sb, ref_scores, rows=rows)
+    g_idx = p.idx.cpu().numpy()[rows]
+    for i in range(len(rows)):
+        a = set(g_idx[i][g_idx[i] >= 0].tolist())
+        b = set(ref_idx[i][ref_idx[i] >= 0].tolist())
+        assert len(a & b) >= 0.99 * len(b)
+        n = sb.positions()[rows[i]] + 1
+        g = p.scores[rows[i], :n].double().cpu().numpy()
+        r = ref_scores[i, :n]
+        assert np.max(np.abs(g - r)) <= 1e-3 * max(1.0, np.max(np.abs(r)))
