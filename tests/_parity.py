@@ -25,7 +25,8 @@ def assert_within(gpu, ref, atol, rtol=RTOL, what=""):
     r = np.asarray(ref, dtype=np.float64)
     assert g.shape == r.shape, (what, g.shape, r.shape)
     both_inf = np.isinf(g) & np.isinf(r) & (np.sign(g) == np.sign(r))
-    err = np.where(both_inf, 0.0, np.abs(g - r))
+    with np.errstate(invalid="ignore"):
+        err = np.where(both_inf, 0.0, np.abs(g - r))
     bound = atol + rtol * np.abs(np.where(np.isinf(r), 0.0, r))
     bad = ~(err <= bound)
     if bad.any():
