@@ -14,22 +14,22 @@
 // page is mapped, otherwise it is masked (lmdeploy PR 4968, invalid -1
 // entries; mlx-lm PR 1419, re-masking of gathered keys).
 //
-// Both MFMA kernels run four waves per workgroup on one query row and one
-// range of its selected rows:
+// The kernel runs four waves per workgroup on one query row and one range of
+// its selected rows:
 //
 // * Gather.  A prologue turns the range's indices into byte offsets (page
-//   table applied, unusable entries marked) in LDS.  Tiles of 32 rows are then
-//   copied from HBM straight into an LDS ring of 2-4 buffers with 16-byte
-//   global_load_lds (no register staging), each wave issuing the same number
-//   of copies per tile, so "all copies of tile i are done" is one
-//   s_waitcnt vmcnt(copies issued after tile i).  Up to three tiles are in
-//   flight while one is computed.  Rows are padded to 1168 B so that 16 lanes
-//   reading 16 rows at one column hit 16 distinct bank groups.  Unusable rows
-//   are copied from a usable row of the same range (finite data) and masked
-//   in the softmax.  fp8 rows arrive raw (656 B) and a pass decodes them
-//   (e4m3 * block scale -> bf16) into one compute tile.
+//   table applied, unusable entries marked -1) and a usable-row bitmask per
+//   32-row tile, in LDS.  Each tile is loaded with plain 16-byte global loads
+//   into registers (9 per thread for bf16 rows; 5 for fp8 rows, which are
+//   decoded to bf16 as e4m3 * block scale on the way), one or two tiles ahead
+//   of the tile being computed, and written to a single LDS tile whose rows
+//   are padded to 1168 B (16 lanes reading 16 rows at one column then hit 16
+//   distinct bank groups).  Measured on MI355X, random 1152-byte row gathers
+//   this way run at the rate of a sequential read (about 6 TB/s), while
+//   global_load_lds copies of the same rows reached only 2-3.4 TB/s.
 // * QK^T.  S^T = rows x q^T on MFMA with the rows as the A operand read from
-//   LDS and q held in registers as the B operand for the whole range.
+//   LDS (kept four k steps ahead of their MFMAs) and q held in registers as
+//   the B operand for the whole range.
 // * Softmax.  Online, in registers, in log2 units; the running max is only
 //   raised (and O rescaled) when a new tile beats it by more than 2^8, which
 //   keeps the O rescale off the common path without changing the result.
@@ -40,13 +40,14 @@
 //   addressed by lanes i/4, 4+i/4, 8+i/4, 12+i/4), so every lane gets eight
 //   rows of one output column without register shuffles.
 //
-// Both use v_mfma_f32_16x16x32_bf16 with 16 heads per wave.  For 16-head
-// workloads every wave computes the (cheap) 32x16 score tile and then its own
-// quarter of the 512 output columns, so one query's work spreads over four
-// SIMDs.  For 64+ heads a workgroup owns 64 heads, 16 per wave, each wave all
-// 512 columns (one wave per SIMD: 72 VGPRs of q, a 128-register accumulator).
-// (32 heads per wave would halve the LDS operand traffic, but 144 VGPRs of q
-// next to a 256-register accumulator do not fit and q ends up spilled.)
+// Both variants use v_mfma_f32_16x16x32_bf16 with 16 heads per wave.  For
+// 16-head workloads every wave computes the (cheap) 32x16 score tile and then
+// its own quarter of the 512 output columns, so one query's work spreads over
+// four SIMDs.  For 64+ heads a workgroup owns 64 heads, 16 per wave, each wave
+// all 512 columns (one wave per SIMD: 72 VGPRs of q, a 128-register
+// accumulator).  (32 heads per wave would halve the LDS operand traffic, but
+// 144 VGPRs of q next to a 256-register accumulator do not fit and q ends up
+// spilled.)
 //
 // When the selected rows of a query are split across workgroups, each writes
 // (m, l, unnormalised O) partials and a second kernel merges them by
@@ -63,57 +64,22 @@ constexpr int kDr = 64;
 constexpr int kD = kDc + kDr;
 constexpr int kThreads = 256;                          // four waves
 constexpr int kTileRows = 32;
-constexpr int kSlotsPerRow = 73;                       // 72 chunks of 16 B + 1 pad chunk
-constexpr int kRowLds = kSlotsPerRow * 16;             // 1168 B
-constexpr int kTileSlots = kTileRows * kSlotsPerRow;   // 2336
-constexpr int kTileLds = kTileSlots * 16;              // 37376 B
-constexpr int kBf16Copies = (kTileSlots + kThreads - 1) / kThreads;   // 10 per thread
-constexpr int kBf16CopiesMin = kTileSlots / kThreads;                 // 9 for the waves past the end
-constexpr int kFp8Chunks = 41;                         // 656-byte row
-constexpr int kFp8TileSlots = kTileRows * kFp8Chunks;  // 1312
-constexpr int kFp8TileLds = kFp8TileSlots * 16;        // 20992 B
-constexpr int kFp8Copies = (kFp8TileSlots + kThreads - 1) / kThreads; // 6
-constexpr int kFp8CopiesMin = kFp8TileSlots / kThreads;               // 5
+constexpr int kRowLds = 73 * 16;                       // 1152 B of row + one 16-byte pad
+constexpr int kTileLds = kTileRows * kRowLds;          // 37376 B
+constexpr int kBf16Items = kTileRows * 72 / kThreads;  // 9 16-byte chunks per thread
+constexpr int kFp8Items = kTileRows * 40 / kThreads;   // 5: 32 latent + 8 rope chunks per row
+constexpr int kSbufLds = kThreads * 16;                // one f32x4 of partial scores per thread
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kRescaleSlack = 8.f;                   // log2 units
 
-static_assert(kBf16CopiesMin == 9 && kFp8CopiesMin == 5, "wait immediates below assume these");
-
-typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
-// Wait until at most `after` tiles' copies are still outstanding for this wave,
-// then barrier.  The inline asm is also a compiler memory barrier, and no
-// other wait is implied (a C++ fence would add vmcnt(0) and drain the ring).
-template <int L>
-__device__ inline void wait_tiles_barrier(int after) {
-  static_assert(L == 9 || L == 5, "immediates");
-  if (L == 9) {
-    switch (after) {
-      case 0: asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); break;
-      case 1: asm volatile("s_waitcnt vmcnt(9)\n\ts_barrier" ::: "memory"); break;
-      case 2: asm volatile("s_waitcnt vmcnt(18)\n\ts_barrier" ::: "memory"); break;
-      default: asm volatile("s_waitcnt vmcnt(27)\n\ts_barrier" ::: "memory"); break;
-    }
-  } else {
-    switch (after) {
-      case 0: asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); break;
-      case 1: asm volatile("s_waitcnt vmcnt(5)\n\ts_barrier" ::: "memory"); break;
-      case 2: asm volatile("s_waitcnt vmcnt(10)\n\ts_barrier" ::: "memory"); break;
-      default: asm volatile("s_waitcnt vmcnt(15)\n\ts_barrier" ::: "memory"); break;
-    }
-  }
-}
-
 // All of this wave's LDS accesses are done, then barrier.
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-__device__ inline void copy16_to_lds(const uint8_t* src, uint8_t* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
-                                   (lds_void_t*)(lds_wave_base), 16, 0, 0);
-}
+__device__ inline bf16x8 lds16(const uint8_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
 __device__ inline s16x4 lds_read_tr16(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
@@ -142,52 +108,62 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// Copies of one bf16 tile: slot q -> (row q/73, chunk q%73); chunk 72 pads.
-// Every wave issues the same copies per tile except the last round (only wave 0).
-__device__ inline void issue_bf16_tile(uint8_t* buf, const int64_t* offs, int64_t fallback,
-                                       const uint8_t* kv, int tid) {
+// One tile's rows in flight in registers: bf16 rows as 9 chunks per thread
+// (item = it*256 + tid -> row item/72, chunk item%72); fp8 rows as 5 items
+// per thread (item -> row item/40, chunk item%40: 32 latent chunks of 16 e4m3
+// bytes, each with its block scale, then 8 rope chunks of bf16).
+template <bool FP8>
+struct Stage {
+  u32x4 v[FP8 ? kFp8Items : kBf16Items];
+  float sc[FP8 ? kFp8Items : 1];
+};
+
+__device__ inline u32x4 ld_global16(const uint8_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+template <bool FP8>
+__device__ inline void stage_load(Stage<FP8>& st, const int64_t* toffs, const uint8_t* kv, int tid) {
+  constexpr int kItems = FP8 ? kFp8Items : kBf16Items;
+  constexpr int kPerRow = FP8 ? 40 : 72;
+  int64_t off[kItems];
 #pragma unroll
-  for (int it = 0; it < kBf16Copies; ++it) {
-    const int q = it * kThreads + tid;
-    if (it < kBf16CopiesMin || q < kTileSlots) {
-      const int row = q / kSlotsPerRow;
-      const int ch = q - row * kSlotsPerRow;
-      int64_t off = offs[row];
-      if (off < 0) off = fallback;
-      copy16_to_lds(kv + off + (ch < 72 ? ch * 16 : 0), buf + (it * kThreads + (tid & ~63)) * 16);
+  for (int it = 0; it < kItems; ++it) off[it] = toffs[(it * kThreads + tid) / kPerRow];
+#pragma unroll
+  for (int it = 0; it < kItems; ++it) {
+    const int item = it * kThreads + tid;
+    const int ch = item % kPerRow;
+    st.v[it] = u32x4{};
+    if (off[it] >= 0) {
+      const uint8_t* row = kv + off[it];
+      if (!FP8) {
+        st.v[it] = ld_global16(row + ch * 16);
+      } else if (ch < 32) {
+        st.v[it] = ld_global16(row + ch * 16);
+        st.sc[it] = *reinterpret_cast<const float*>(row + 512 + (ch >> 3) * 4);
+      } else {
+        st.v[it] = ld_global16(row + 528 + (ch - 32) * 16);
+      }
     }
+    if (FP8 && (off[it] < 0 || ch >= 32)) st.sc[it] = 0.f;
   }
 }
 
-// Copies of one raw fp8 tile: 41 chunks of 16 B per 656-byte row, unpadded.
-__device__ inline void issue_fp8_tile(uint8_t* buf, const int64_t* offs, int64_t fallback,
-                                      const uint8_t* kv, int tid) {
+template <bool FP8>
+__device__ inline void stage_store(const Stage<FP8>& st, uint8_t* tile, int tid) {
+  constexpr int kItems = FP8 ? kFp8Items : kBf16Items;
+  constexpr int kPerRow = FP8 ? 40 : 72;
 #pragma unroll
-  for (int it = 0; it < kFp8Copies; ++it) {
-    const int q = it * kThreads + tid;
-    if (it < kFp8CopiesMin || q < kFp8TileSlots) {
-      const int row = q / kFp8Chunks;
-      const int ch = q - row * kFp8Chunks;
-      int64_t off = offs[row];
-      if (off < 0) off = fallback;
-      copy16_to_lds(kv + off + ch * 16, buf + (it * kThreads + (tid & ~63)) * 16);
-    }
-  }
-}
-
-// Raw fp8 tile -> bf16 compute tile (value = e4m3 * block scale, rounded to bf16).
-__device__ inline void decode_fp8_tile(const uint8_t* raw, uint8_t* tile, int tid) {
-  for (int c = tid; c < kTileRows * 40; c += kThreads) {
-    const int r = c / 40, ch = c - r * 40;
-    const uint8_t* rr = raw + r * 656;
+  for (int it = 0; it < kItems; ++it) {
+    const int item = it * kThreads + tid;
+    const int r = item / kPerRow, ch = item % kPerRow;
     uint8_t* dst = tile + r * kRowLds;
-    if (ch < 32) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(rr + ch * 16);
-      const float sc = *reinterpret_cast<const float*>(rr + 512 + (ch >> 3) * 4);
+    if (!FP8) {
+      *reinterpret_cast<u32x4*>(dst + ch * 16) = st.v[it];
+    } else if (ch < 32) {
+      const float sc = st.sc[it];
       u32x4 lo, hi;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const uint32_t x = v[w];
+        const uint32_t x = st.v[it][w];
         const uint32_t p0 = pack_bf16x2(e4m3_to_f32(x & 0xFFu) * sc, e4m3_to_f32((x >> 8) & 0xFFu) * sc);
         const uint32_t p1 = pack_bf16x2(e4m3_to_f32((x >> 16) & 0xFFu) * sc, e4m3_to_f32(x >> 24) * sc);
         if (w < 2) { lo[2 * w] = p0; lo[2 * w + 1] = p1; }
@@ -196,8 +172,7 @@ __device__ inline void decode_fp8_tile(const uint8_t* raw, uint8_t* tile, int ti
       *reinterpret_cast<u32x4*>(dst + ch * 32) = lo;
       *reinterpret_cast<u32x4*>(dst + ch * 32 + 16) = hi;
     } else {
-      *reinterpret_cast<u32x4*>(dst + 1024 + (ch - 32) * 16) =
-          *reinterpret_cast<const u32x4*>(rr + 528 + (ch - 32) * 16);
+      *reinterpret_cast<u32x4*>(dst + 1024 + (ch - 32) * 16) = st.v[it];
     }
   }
 }
@@ -205,11 +180,12 @@ __device__ inline void decode_fp8_tile(const uint8_t* raw, uint8_t* tile, int ti
 // Prologue: byte offsets of the range's rows (page table applied; -1 when not
 // usable), padded with -1 to whole tiles.  Returns the first usable slot, or
 // INT32_MAX when the range has none.  Ends with a barrier.
-__device__ inline int build_offsets(int64_t* offs, int* first_valid, const int32_t* idx_row,
+__device__ inline int build_offsets(int64_t* offs, uint32_t* vmask, int* first_valid, const int32_t* idx_row,
                                     int j_begin, int j_end, int n_pad, int pos, int b,
                                     const int32_t* page_table, int pt_stride, int page_size,
                                     int num_pages, int64_t page_stride, int64_t row_stride, int tid) {
   if (tid == 0) *first_valid = INT32_MAX;
+  for (int i = tid; i < n_pad / kTileRows; i += kThreads) vmask[i] = 0u;
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   for (int i = tid; i < n_pad; i += kThreads) {
     const int j = j_begin + i;
@@ -220,7 +196,10 @@ __device__ inline int build_offsets(int64_t* offs, int* first_valid, const int32
         off = token_offset(page_table, pt_stride, page_size, num_pages, b, s, page_stride, row_stride);
     }
     offs[i] = off;
-    if (off >= 0) atomicMin(first_valid, i);
+    if (off >= 0) {
+      atomicMin(first_valid, i);
+      atomicOr(&vmask[i / kTileRows], 1u << (i % kTileRows));
+    }
   }
   __syncthreads();
   return *first_valid;
@@ -240,7 +219,7 @@ struct MlaArgs {
   uint16_t* out;
   float* lse;
   float* ws;
-  int splits, rows_per_split, nbuf;
+  int splits, rows_per_split;
 };
 
 // Online-softmax bookkeeping shared by both kernels.  `mt` is this lane's
@@ -267,8 +246,8 @@ __device__ inline bool softmax_step(float mt, float& m_run, float& alpha) {
 // per query, linear workgroup ids are laid out so that the groups of one query
 // are 8 ids apart: they land on the same XCD at about the same time and the
 // second gather of each tile is served by that XCD's L2.
-template <int DSPLIT, bool FP8>
-__global__ __launch_bounds__(kThreads) void sparse_mla_tiles(MlaArgs a, int n_groups, int T) {
+template <int DSPLIT, bool FP8, int STAGES>
+__global__ __launch_bounds__(kThreads, DSPLIT == 4 ? 2 : 1) void sparse_mla_tiles(MlaArgs a, int n_groups, int T) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int kHeadsPerGroup = 64 / DSPLIT;
   constexpr int kCols = kDc / DSPLIT;          // output columns per wave
@@ -287,13 +266,13 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_tiles(MlaArgs a, int n_gr
   const int ntiles = (j_end - j_begin + kTileRows - 1) / kTileRows;
   const int b = find_request(a.cu_q, a.B, t);
   const int pos = row_position(a.cu_q, a.seq_lens, b, t);
-  const int buf_bytes = FP8 ? kFp8TileLds : kTileLds;
-  const int nbuf = a.nbuf;
-  uint8_t* ctile = smem + nbuf * buf_bytes;  // fp8 decode target
-  int64_t* offs = reinterpret_cast<int64_t*>(ctile + (FP8 ? kTileLds : 0));
-  int* first_valid = reinterpret_cast<int*>(offs + ntiles * kTileRows);
+  uint8_t* tile = smem;                                                 // one 32-row tile
+  f32x4* sbuf = reinterpret_cast<f32x4*>(smem + kTileLds);              // partial scores (16 heads)
+  int64_t* offs = reinterpret_cast<int64_t*>(smem + kTileLds + kSbufLds);
+  uint32_t* vmask = reinterpret_cast<uint32_t*>(offs + ntiles * kTileRows);  // usable rows per tile
+  int* first_valid = reinterpret_cast<int*>(vmask + ntiles);
 
-  const int fv = build_offsets(offs, first_valid, a.idx + (int64_t)t * a.K, j_begin, j_end,
+  const int fv = build_offsets(offs, vmask, first_valid, a.idx + (int64_t)t * a.K, j_begin, j_end,
                                ntiles * kTileRows, pos, b, a.page_table, a.pt_stride, a.page_size,
                                a.num_pages, a.page_stride, a.row_stride, tid);
 
@@ -303,51 +282,84 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_tiles(MlaArgs a, int n_gr
   float m_run = kNegInf, l_run = 0.f;
 
   if (fv != INT32_MAX) {
-    const int64_t fallback = offs[fv];
-    // q as the B operand of S^T: lane (head c16, group g) holds dims 32 ks + 8 g .. +7.
-    bf16x8 qreg[18];
+    // With 16 heads per workgroup the four waves split QK: wave w takes tile
+    // rows 16(w&1) .. +15 over k steps 9(w>>1) .. +8 (half of the 576 dims),
+    // so each tile byte is read once for QK; the partial scores are summed
+    // through LDS.  With 64 heads each wave does all of QK for its 16 heads.
+    constexpr bool kSplitQk = DSPLIT == 4;
+    constexpr int kQSteps = kSplitQk ? 9 : 18;
+    const int ks0 = kSplitQk ? 9 * (wave >> 1) : 0;
+    bf16x8 qreg[kQSteps];
     {
-      const uint16_t* qp = a.q + ((int64_t)t * a.H + head0 + c16) * kD + g * 8;
+      const uint16_t* qp = a.q + ((int64_t)t * a.H + head0 + c16) * kD + g * 8 + ks0 * 32;
 #pragma unroll
-      for (int ks = 0; ks < 18; ++ks) qreg[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32);
+      for (int ks = 0; ks < kQSteps; ++ks) qreg[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32);
     }
-    const int D = nbuf - 1;
-    for (int i = 0; i < D && i < ntiles; ++i) {
-      if (FP8) issue_fp8_tile(smem + i * buf_bytes, offs + i * kTileRows, fallback, a.kv, tid);
-      else issue_bf16_tile(smem + i * buf_bytes, offs + i * kTileRows, fallback, a.kv, tid);
-    }
-#pragma unroll 1
-    for (int i = 0; i < ntiles; ++i) {
-      if (i + D < ntiles) {
-        uint8_t* nb = smem + ((i + D) % nbuf) * buf_bytes;
-        if (FP8) issue_fp8_tile(nb, offs + (i + D) * kTileRows, fallback, a.kv, tid);
-        else issue_bf16_tile(nb, offs + (i + D) * kTileRows, fallback, a.kv, tid);
-      }
-      const int after = min(D, ntiles - 1 - i);
-      if (FP8) wait_tiles_barrier<kFp8CopiesMin>(after);
-      else wait_tiles_barrier<kBf16CopiesMin>(after);
-      const uint8_t* tile = smem + (i % nbuf) * buf_bytes;
-      if (FP8) {
-        decode_fp8_tile(tile, ctile, tid);
-        lds_barrier();
-        tile = ctile;
-      }
-      const int64_t* toffs = offs + i * kTileRows;
+    auto compute_tile = [&](int i) {
+      const uint32_t valid = vmask[i];
 
-      // S^T: accumulator r of lane = tile row nt*16 + 4g + r, head c16.
+      // S^T: accumulator r of lane = tile row nt*16 + 4g + r, head c16.  The
+      // A operands are read kQkAhead k steps ahead of their MFMA.
+      constexpr int kQkAhead = 4;
       f32x4 s0 = f32x4{}, s1 = f32x4{};
+      if constexpr (kSplitQk) {
+        f32x4 sp = f32x4{};
+        const uint8_t* ap = tile + (16 * (wave & 1) + c16) * kRowLds + g * 16 + ks0 * 64;
+        bf16x8 ra[kQkAhead];
+#pragma unroll
+        for (int k = 0; k < kQkAhead; ++k) ra[k] = lds16(ap + k * 64);
+#pragma unroll
+        for (int ks = 0; ks < kQSteps; ++ks) {
+          const bf16x8 xk = ra[ks % kQkAhead];
+          if (ks + kQkAhead < kQSteps) ra[ks % kQkAhead] = lds16(ap + (ks + kQkAhead) * 64);
+          sp = mfma16(xk, qreg[ks], sp);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, kQkAhead, 0);
+#pragma unroll
+        for (int ks = 0; ks < kQSteps - kQkAhead; ++ks) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kQkAhead, 0);
+        sbuf[wave * 64 + lane] = sp;
+        lds_barrier();
+        // same summation order in every wave: k half 0, then k half 1
+        s0 = sbuf[0 * 64 + lane] + sbuf[2 * 64 + lane];
+        s1 = sbuf[1 * 64 + lane] + sbuf[3 * 64 + lane];
+      } else {
       const uint8_t* ap = tile + c16 * kRowLds + g * 16;
+      bf16x8 ra0[kQkAhead], ra1[kQkAhead];
+#pragma unroll
+      for (int k = 0; k < kQkAhead; ++k) {
+        ra0[k] = lds16(ap + k * 64);
+        ra1[k] = lds16(ap + 16 * kRowLds + k * 64);
+      }
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) {
-        s0 = mfma16(*reinterpret_cast<const bf16x8*>(ap + ks * 64), qreg[ks], s0);
-        s1 = mfma16(*reinterpret_cast<const bf16x8*>(ap + 16 * kRowLds + ks * 64), qreg[ks], s1);
+        const bf16x8 x0 = ra0[ks % kQkAhead], x1 = ra1[ks % kQkAhead];
+        if (ks + kQkAhead < 18) {
+          ra0[ks % kQkAhead] = lds16(ap + (ks + kQkAhead) * 64);
+          ra1[ks % kQkAhead] = lds16(ap + 16 * kRowLds + (ks + kQkAhead) * 64);
+        }
+        s0 = mfma16(x0, qreg[ks], s0);
+        s1 = mfma16(x1, qreg[ks], s1);
+      }
+      // Keep the operand reads kQkAhead steps ahead of their MFMAs (the default
+      // schedule pulls them back next to their use and exposes LDS latency).
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kQkAhead, 0);
+#pragma unroll
+      for (int ks = 0; ks < 18 - kQkAhead; ++ks) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * kQkAhead, 0);
       }
       float xv[8];
       float mt = kNegInf;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        xv[r] = toffs[4 * g + r] >= 0 ? s0[r] * a.scale_log2 : kNegInf;
-        xv[4 + r] = toffs[16 + 4 * g + r] >= 0 ? s1[r] * a.scale_log2 : kNegInf;
+        xv[r] = (valid >> (4 * g + r)) & 1u ? s0[r] * a.scale_log2 : kNegInf;
+        xv[4 + r] = (valid >> (16 + 4 * g + r)) & 1u ? s1[r] * a.scale_log2 : kNegInf;
         mt = fmaxf(mt, fmaxf(xv[r], xv[4 + r]));
       }
       mt = fmaxf(mt, __shfl_xor(mt, 16));
@@ -372,14 +384,46 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_tiles(MlaArgs a, int n_gr
       // O[:, col0 + 16 i .. +16] += P V.  k slot (g, e) <-> tile row 4g + e,
       // (g, 4 + e) <-> 16 + 4g + e, matching the S^T accumulator rows.
       const uint8_t* vp = tile + (4 * g + (c16 >> 2)) * kRowLds + (col0 + 4 * (c16 & 3)) * 2;
+      constexpr int kPvAhead = 4;
+      s16x4 tv1[kPvAhead], tv2[kPvAhead];
+#pragma unroll
+      for (int k = 0; k < kPvAhead; ++k) {
+        tv1[k] = lds_read_tr16(vp + k * 32);
+        tv2[k] = lds_read_tr16(vp + 16 * kRowLds + k * 32);
+      }
 #pragma unroll
       for (int i2 = 0; i2 < kColTiles; ++i2) {
-        const s16x4 v1 = lds_read_tr16(vp + i2 * 32);
-        const s16x4 v2 = lds_read_tr16(vp + 16 * kRowLds + i2 * 32);
+        const s16x4 v1 = tv1[i2 % kPvAhead], v2 = tv2[i2 % kPvAhead];
+        if (i2 + kPvAhead < kColTiles) {
+          tv1[i2 % kPvAhead] = lds_read_tr16(vp + (i2 + kPvAhead) * 32);
+          tv2[i2 % kPvAhead] = lds_read_tr16(vp + 16 * kRowLds + (i2 + kPvAhead) * 32);
+        }
         o[i2] = mfma16(pa, join(v1, v2), o[i2]);
-        if ((i2 & 7) == 7) __builtin_amdgcn_sched_barrier(0);  // bound operand prefetch
       }
-      lds_barrier();
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPvAhead, 1);
+#pragma unroll
+      for (int i2 = 0; i2 < kColTiles - kPvAhead; ++i2) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kPvAhead, 1);
+    };
+    // Tile i is written to LDS from stage i%STAGES, whose registers then take
+    // the loads of tile i+STAGES; the compiler's own vmcnt waits cover the loads.
+    auto step = [&](Stage<FP8>& st, int i) {
+      lds_barrier();                       // every wave is done with tile i-1
+      stage_store<FP8>(st, tile, tid);
+      if (i + STAGES < ntiles) stage_load<FP8>(st, offs + (i + STAGES) * kTileRows, a.kv, tid);
+      lds_barrier();                       // tile i visible to every wave
+      compute_tile(i);
+    };
+    Stage<FP8> st0, st1;
+    stage_load<FP8>(st0, offs, a.kv, tid);
+    if (STAGES == 2 && ntiles > 1) stage_load<FP8>(st1, offs + kTileRows, a.kv, tid);
+#pragma unroll 1
+    for (int i = 0; i < ntiles; i += STAGES) {
+      step(st0, i);
+      if (STAGES == 2 && i + 1 < ntiles) step(st1, i + 1);
     }
   }
 
@@ -531,12 +575,10 @@ namespace {
 
 constexpr size_t kMaxLds = 160 * 1024;
 
-// LDS bytes of a launch with `nbuf` ring buffers.
-size_t mla_lds(bool wide, bool fp8, int nbuf, int rps) {
-  const size_t buf = fp8 ? kFp8TileLds : kTileLds;
-  (void)wide;
-  return nbuf * buf + (fp8 ? kTileLds : 0) +
-         (size_t)(rps + kTileRows - 1) / kTileRows * kTileRows * 8 + 16;
+// LDS bytes: the tile, then the range's row offsets, tile masks and a flag.
+size_t mla_lds(int rps) {
+  const size_t ntiles = (size_t)(rps + kTileRows - 1) / kTileRows;
+  return kTileLds + kSbufLds + ntiles * (kTileRows * 8 + 4) + 16;
 }
 
 template <typename Kernel>
@@ -557,25 +599,25 @@ hipError_t launch_sparse_mla_bf16(const BatchArgs& ba, const void* q, const Pool
                                   hipStream_t stream) {
   const bool wide = n_heads % 64 == 0;
   const bool fp8 = kv.format == 2;
-  int nbuf = 4;
-  while (nbuf > 2 && mla_lds(wide, fp8, nbuf, plan.rows_per_split) > kMaxLds) --nbuf;
-  const size_t lds = mla_lds(wide, fp8, nbuf, plan.rows_per_split);
+  const size_t lds = mla_lds(plan.rows_per_split);
   if (lds > kMaxLds) return hipErrorInvalidValue;
   MlaArgs args{ba.cu_q, ba.seq_lens, ba.page_table, ba.batch, ba.pt_stride, ba.page_size,
                ba.num_pages, static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(kv.base),
                kv.page_stride, kv.row_stride, idx, k, n_heads, sm_scale * kLog2e,
                static_cast<uint16_t*>(out), lse, static_cast<float*>(ws), plan.splits,
-               plan.rows_per_split, nbuf};
+               plan.rows_per_split};
   const int T = ba.num_q_rows;
   const int n_groups = wide ? n_heads / 64 : n_heads / 16;
   const dim3 grid((unsigned)((T + 7) / 8 * 8 * n_groups), 1, plan.splits);
   hipError_t e;
+  // Tiles of loads in flight per workgroup: two for 16-head groups (two
+  // workgroups per CU), one for 64-head groups (a second would spill).
   if (wide)
-    e = fp8 ? launch_with_lds(sparse_mla_tiles<1, true>, grid, lds, stream, args, n_groups, T)
-            : launch_with_lds(sparse_mla_tiles<1, false>, grid, lds, stream, args, n_groups, T);
+    e = fp8 ? launch_with_lds(sparse_mla_tiles<1, true, 1>, grid, lds, stream, args, n_groups, T)
+            : launch_with_lds(sparse_mla_tiles<1, false, 1>, grid, lds, stream, args, n_groups, T);
   else
-    e = fp8 ? launch_with_lds(sparse_mla_tiles<4, true>, grid, lds, stream, args, n_groups, T)
-            : launch_with_lds(sparse_mla_tiles<4, false>, grid, lds, stream, args, n_groups, T);
+    e = fp8 ? launch_with_lds(sparse_mla_tiles<4, true, 2>, grid, lds, stream, args, n_groups, T)
+            : launch_with_lds(sparse_mla_tiles<4, false, 2>, grid, lds, stream, args, n_groups, T);
   if (e != hipSuccess || plan.splits == 1) return e;
   hipLaunchKernelGGL(sparse_mla_combine, dim3(ba.num_q_rows, n_heads), dim3(kWave), 0, stream,
                      static_cast<const float*>(ws), n_heads, plan.splits,
