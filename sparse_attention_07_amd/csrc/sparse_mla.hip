@@ -178,27 +178,47 @@ __device__ inline void stage_store(const Stage<FP8>& st, uint8_t* tile, int tid)
 }
 
 // Prologue: byte offsets of the range's rows (page table applied; -1 when not
-// usable), padded with -1 to whole tiles.  Returns the first usable slot, or
-// INT32_MAX when the range has none.  Ends with a barrier.
-__device__ inline int build_offsets(int64_t* offs, uint32_t* vmask, int* first_valid, const int32_t* idx_row,
-                                    int j_begin, int j_end, int n_pad, int pos, int b,
-                                    const int32_t* page_table, int pt_stride, int page_size,
-                                    int num_pages, int64_t page_stride, int64_t row_stride, int tid) {
+// usable), padded with -1 to whole tiles, and a usable-row bitmask per tile.
+// Each thread handles rows tid, tid+256, ...; the index loads of a batch of
+// eight rows are all issued before the dependent page-table loads, so the
+// prologue costs two memory latencies per 2048 rows rather than two per row.
+// Returns the first usable slot, or INT32_MAX when the range has none.  Ends
+// with a barrier.
+__device__ inline int build_offsets(int64_t* offs, uint32_t* vmask, int* first_valid,
+                                    const int32_t* idx_row, int j_begin, int j_end, int n_pad,
+                                    int pos, int b, const int32_t* page_table, int pt_stride,
+                                    int page_size, int num_pages, int64_t page_stride,
+                                    int64_t row_stride, int tid) {
+  constexpr int kBatch = 8;
   if (tid == 0) *first_valid = INT32_MAX;
   for (int i = tid; i < n_pad / kTileRows; i += kThreads) vmask[i] = 0u;
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  for (int i = tid; i < n_pad; i += kThreads) {
-    const int j = j_begin + i;
-    int64_t off = -1;
-    if (j < j_end) {
-      const int s = idx_row[j];
-      if (s >= 0 && s <= pos)
-        off = token_offset(page_table, pt_stride, page_size, num_pages, b, s, page_stride, row_stride);
+  for (int base = 0; base < n_pad; base += kBatch * kThreads) {
+    int sv[kBatch], pg[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int i = base + k * kThreads + tid;
+      const int j = j_begin + i;
+      sv[k] = (i < n_pad && j < j_end) ? idx_row[j] : -1;
     }
-    offs[i] = off;
-    if (off >= 0) {
-      atomicMin(first_valid, i);
-      atomicOr(&vmask[i / kTileRows], 1u << (i % kTileRows));
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int sk = sv[k];
+      const bool ok = sk >= 0 && sk <= pos && sk / page_size < pt_stride;
+      pg[k] = ok ? page_table[(int64_t)b * pt_stride + sk / page_size] : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int i = base + k * kThreads + tid;
+      if (i >= n_pad) continue;
+      int64_t off = -1;
+      if (pg[k] >= 0 && pg[k] < num_pages)
+        off = (int64_t)pg[k] * page_stride + (int64_t)(sv[k] % page_size) * row_stride;
+      offs[i] = off;
+      if (off >= 0) {
+        atomicMin(first_valid, i);
+        atomicOr(&vmask[i / kTileRows], 1u << (i % kTileRows));
+      }
     }
   }
   __syncthreads();
@@ -459,6 +479,198 @@ __global__ __launch_bounds__(kThreads, DSPLIT == 4 ? 2 : 1) void sparse_mla_tile
   }
 }
 
+// ---------------------------------------------------------------- 16 heads
+
+// One workgroup owns 16 heads of one query row and one range of its selected
+// rows.  Wave w splits QK with its siblings: it owns tile rows 16(w&1) .. +15
+// and k steps 9(w>>1) .. +8 (half of the 576 dims).  It loads exactly that
+// part of each tile from HBM into registers, already in the A-operand layout
+// of v_mfma_f32_16x16x32_bf16 (lane: row c16, dims 32 ks + 8 g .. +7), so QK
+// reads no LDS at all; the latent dims are also written to the LDS tile, from
+// which every wave then reads V for its quarter (128) of the output columns.
+// Partial scores of the two k halves are summed through LDS in a fixed order.
+// Registers: 36 of q, 32 of accumulator, 36 per tile in flight (two tiles).
+template <bool FP8>
+struct RegTile {
+  u32x4 v[9];   // bf16: 16 B per k step; fp8: 8 latent bytes (v.x, v.y) or 16 B of rope
+  f32x4 sc;     // fp8 block scales of the row
+};
+
+template <bool FP8>
+__device__ inline void regtile_load(RegTile<FP8>& st, int64_t off, const uint8_t* kv, int ks0, int g) {
+#pragma unroll
+  for (int k = 0; k < 9; ++k) st.v[k] = u32x4{};
+  st.sc = f32x4{};
+  if (off < 0) return;
+  const uint8_t* row = kv + off;
+#pragma unroll
+  for (int k = 0; k < 9; ++k) {
+    const int ks = ks0 + k;
+    if (!FP8) {
+      st.v[k] = ld_global16(row + ks * 64 + g * 16);
+    } else if (ks < 16) {
+      const uint2 x = *reinterpret_cast<const uint2*>(row + ks * 32 + g * 8);
+      st.v[k] = u32x4{x.x, x.y, 0u, 0u};
+    } else {
+      st.v[k] = ld_global16(row + 528 + ((ks - 16) * 32 + g * 8) * 2);
+    }
+  }
+  if (FP8) st.sc = *reinterpret_cast<const f32x4*>(row + 512);
+}
+
+// The bf16 A operand of k step ks (fp8: e4m3 * block scale, rounded to bf16).
+template <bool FP8>
+__device__ inline bf16x8 regtile_operand(const RegTile<FP8>& st, int k, int ks) {
+  if (!FP8 || ks >= 16) return __builtin_bit_cast(bf16x8, st.v[k]);
+  const float sc = st.sc[ks >> 2];
+  const uint32_t x0 = st.v[k][0], x1 = st.v[k][1];
+  u32x4 r;
+  r[0] = pack_bf16x2(e4m3_to_f32(x0 & 0xFFu) * sc, e4m3_to_f32((x0 >> 8) & 0xFFu) * sc);
+  r[1] = pack_bf16x2(e4m3_to_f32((x0 >> 16) & 0xFFu) * sc, e4m3_to_f32(x0 >> 24) * sc);
+  r[2] = pack_bf16x2(e4m3_to_f32(x1 & 0xFFu) * sc, e4m3_to_f32((x1 >> 8) & 0xFFu) * sc);
+  r[3] = pack_bf16x2(e4m3_to_f32((x1 >> 16) & 0xFFu) * sc, e4m3_to_f32(x1 >> 24) * sc);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+template <bool FP8>
+__global__ __launch_bounds__(kThreads, 2) void sparse_mla_q16(MlaArgs a, int n_groups, int T) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int x = blockIdx.x, sp = blockIdx.z;
+  const int t = (x / (8 * n_groups)) * 8 + (x & 7);
+  const int grp = (x >> 3) % n_groups;
+  if (t >= T) return;                          // padding ids of the XCD-aware layout
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int rb = wave & 1, ks0 = 9 * (wave >> 1);
+  const int head0 = grp * 16;
+  const int col0 = 128 * wave;
+  const int j_begin = sp * a.rows_per_split;
+  const int j_end = min(a.K, j_begin + a.rows_per_split);
+  const int ntiles = (j_end - j_begin + kTileRows - 1) / kTileRows;
+  const int b = find_request(a.cu_q, a.B, t);
+  const int pos = row_position(a.cu_q, a.seq_lens, b, t);
+  uint8_t* tile = smem;
+  f32x4* sbuf = reinterpret_cast<f32x4*>(smem + kTileLds);
+  int64_t* offs = reinterpret_cast<int64_t*>(smem + kTileLds + kSbufLds);
+  uint32_t* vmask = reinterpret_cast<uint32_t*>(offs + ntiles * kTileRows);
+  int* first_valid = reinterpret_cast<int*>(vmask + ntiles);
+
+  // q for this wave's k half: lane (head c16, group g) holds dims 32 ks + 8 g .. +7.
+  bf16x8 qreg[9];
+  {
+    const uint16_t* qp = a.q + ((int64_t)t * a.H + head0 + c16) * kD + g * 8 + ks0 * 32;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) qreg[k] = *reinterpret_cast<const bf16x8*>(qp + k * 32);
+  }
+  const int fv = build_offsets(offs, vmask, first_valid, a.idx + (int64_t)t * a.K, j_begin, j_end,
+                               ntiles * kTileRows, pos, b, a.page_table, a.pt_stride, a.page_size,
+                               a.num_pages, a.page_stride, a.row_stride, tid);
+
+  f32x4 o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = f32x4{};
+  float m_run = kNegInf, l_run = 0.f;
+
+  if (fv != INT32_MAX) {
+    const int my_row = 16 * rb + c16;
+    auto step = [&](RegTile<FP8>& st, int i) {
+      lds_barrier();                                       // every wave is done with tile i-1
+      f32x4 spart = f32x4{};
+      uint8_t* trow = tile + my_row * kRowLds + g * 16;
+#pragma unroll
+      for (int k = 0; k < 9; ++k) {
+        const int ks = ks0 + k;
+        const bf16x8 av = regtile_operand<FP8>(st, k, ks);
+        if (ks < 16) *reinterpret_cast<bf16x8*>(trow + ks * 64) = av;  // latent dims feed PV
+        spart = mfma16(av, qreg[k], spart);
+      }
+      sbuf[wave * 64 + lane] = spart;
+      if (i + 2 < ntiles) regtile_load<FP8>(st, offs[(i + 2) * kTileRows + my_row], a.kv, ks0, g);
+      lds_barrier();                                       // tile i and partial scores visible
+      const uint32_t valid = vmask[i];
+      // rows 0..15 from waves 0 and 2, rows 16..31 from waves 1 and 3; k half 0 first
+      const f32x4 s0 = sbuf[0 * 64 + lane] + sbuf[2 * 64 + lane];
+      const f32x4 s1 = sbuf[1 * 64 + lane] + sbuf[3 * 64 + lane];
+      float xv[8];
+      float mt = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        xv[r] = (valid >> (4 * g + r)) & 1u ? s0[r] * a.scale_log2 : kNegInf;
+        xv[4 + r] = (valid >> (16 + 4 * g + r)) & 1u ? s1[r] * a.scale_log2 : kNegInf;
+        mt = fmaxf(mt, fmaxf(xv[r], xv[4 + r]));
+      }
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      float alpha;
+      if (softmax_step(mt, m_run, alpha)) {
+        l_run *= alpha;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float ar = __shfl(alpha, 4 * g + r);  // O row r holds head 4g + r
+#pragma unroll
+          for (int i2 = 0; i2 < 8; ++i2) o[i2][r] *= ar;
+        }
+      }
+      bf16x8 pa;
+#pragma unroll
+      for (int i2 = 0; i2 < 8; ++i2) {
+        const float p = xv[i2] == kNegInf ? 0.f : exp2f(xv[i2] - m_run);
+        l_run += p;
+        pa[i2] = (__bf16)p;
+      }
+      // O[:, col0 + 16 i .. +16] += P V.  k slot (g, e) <-> tile row 4g + e,
+      // (g, 4 + e) <-> 16 + 4g + e, matching the S^T accumulator rows.
+      const uint8_t* vp = tile + (4 * g + (c16 >> 2)) * kRowLds + (col0 + 4 * (c16 & 3)) * 2;
+      s16x4 tv1[8], tv2[8];
+#pragma unroll
+      for (int i2 = 0; i2 < 8; ++i2) {
+        tv1[i2] = lds_read_tr16(vp + i2 * 32);
+        tv2[i2] = lds_read_tr16(vp + 16 * kRowLds + i2 * 32);
+      }
+#pragma unroll
+      for (int i2 = 0; i2 < 8; ++i2) o[i2] = mfma16(pa, join(tv1[i2], tv2[i2]), o[i2]);
+    };
+    RegTile<FP8> st0, st1;
+    regtile_load<FP8>(st0, offs[my_row], a.kv, ks0, g);
+    if (ntiles > 1) regtile_load<FP8>(st1, offs[kTileRows + my_row], a.kv, ks0, g);
+#pragma unroll 1
+    for (int i = 0; i < ntiles; i += 2) {
+      step(st0, i);
+      if (i + 1 < ntiles) step(st1, i + 1);
+    }
+  }
+
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  // O accumulator r of lane: head 4g + r, column col0 + 16 i + c16.
+  if (a.splits == 1) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * g + r;
+      const float lh = __shfl(l_run, h);
+      const float inv = lh > 0.f ? 1.f / lh : 0.f;
+      uint16_t* op = a.out + ((int64_t)t * a.H + head0 + h) * kDc + col0 + c16;
+#pragma unroll
+      for (int i2 = 0; i2 < 8; ++i2) op[16 * i2] = __builtin_bit_cast(uint16_t, (__bf16)(o[i2][r] * inv));
+    }
+    if (a.lse != nullptr && wave == 0 && lane < 16)
+      a.lse[(int64_t)t * a.H + head0 + lane] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : kNegInf;
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * g + r;
+      float* wp = a.ws + (((int64_t)t * a.H + head0 + h) * a.splits + sp) * 516 + col0 + c16;
+#pragma unroll
+      for (int i2 = 0; i2 < 8; ++i2) wp[16 * i2] = o[i2][r];
+    }
+    if (wave == 0 && lane < 16) {
+      float* wp = a.ws + (((int64_t)t * a.H + head0 + lane) * a.splits + sp) * 516 + 512;
+      wp[0] = m_run;
+      wp[1] = l_run;
+    }
+  }
+}
+
 // Merge per-split partials: one wave per (row, head); lane covers 8 columns.
 __global__ __launch_bounds__(kWave) void sparse_mla_combine(const float* __restrict__ ws, int H,
                                                             int splits, uint16_t* __restrict__ out,
@@ -616,8 +828,8 @@ hipError_t launch_sparse_mla_bf16(const BatchArgs& ba, const void* q, const Pool
     e = fp8 ? launch_with_lds(sparse_mla_tiles<1, true, 1>, grid, lds, stream, args, n_groups, T)
             : launch_with_lds(sparse_mla_tiles<1, false, 1>, grid, lds, stream, args, n_groups, T);
   else
-    e = fp8 ? launch_with_lds(sparse_mla_tiles<4, true, 2>, grid, lds, stream, args, n_groups, T)
-            : launch_with_lds(sparse_mla_tiles<4, false, 2>, grid, lds, stream, args, n_groups, T);
+    e = fp8 ? launch_with_lds(sparse_mla_q16<true>, grid, lds, stream, args, n_groups, T)
+            : launch_with_lds(sparse_mla_q16<false>, grid, lds, stream, args, n_groups, T);
   if (e != hipSuccess || plan.splits == 1) return e;
   hipLaunchKernelGGL(sparse_mla_combine, dim3(ba.num_q_rows, n_heads), dim3(kWave), 0, stream,
                      static_cast<const float*>(ws), n_heads, plan.splits,

@@ -178,7 +178,8 @@ def quantize_fp8_rows(latent: torch.Tensor, rope: torch.Tensor) -> torch.Tensor:
 def make_batch(cfg_id: int, mode: str = "parity", device="cpu", layers: int | None = None,
                seed_offset: int = 0, batch: int | None = None, q_len: int | None = None,
                ctx: tuple | None = None, topk: int | None = None,
-               page_size: int | None = None, identity_pages: bool | None = None) -> Batch:
+               page_size: int | None = None, identity_pages: bool | None = None,
+               heads: int | None = None, kv_fmt: int | None = None) -> Batch:
     """Draw one batch of config `cfg_id`.
 
     The keyword overrides (batch, q_len, ctx range, top-k, page size) give
@@ -203,6 +204,10 @@ def make_batch(cfg_id: int, mode: str = "parity", device="cpu", layers: int | No
         cfg.identity_pages = identity_pages
     if layers is not None:
         cfg.layers = layers
+    if heads is not None:
+        cfg.heads = heads
+    if kv_fmt is not None:
+        cfg.kv_fmt = kv_fmt
     assert mode in ("parity", "perf")
     device = torch.device(device)
     g = _gen(device, cfg.seed + 7919 * seed_offset)

@@ -56,6 +56,13 @@ REDUCED = {
     "prefill_short": dict(cfg=3, q_len=130, ctx=(700, 700), topk=512),
     "mtp_fp8": dict(cfg=4, batch=3, ctx=(3000, 9000), topk=512),
     "mtp_fp8_near_k": dict(cfg=4, batch=4, ctx=(509, 516), topk=512),
+    # head counts and cache formats outside the five workloads (kernel dispatch coverage)
+    "decode16_fp8": dict(cfg=1, batch=5, ctx=(300, 3000), topk=512, kv_fmt=synth.FMT_FP8_E4M3_B128),
+    "decode_h32": dict(cfg=1, batch=3, ctx=(500, 2500), topk=256, heads=32),
+    "decode_h48": dict(cfg=1, batch=3, ctx=(500, 2500), topk=256, heads=48),
+    "decode_h64_fp8": dict(cfg=2, batch=3, ctx=(900, 3000), topk=512, heads=64, layers=1,
+                           kv_fmt=synth.FMT_FP8_E4M3_B128),
+    "decode_h16_split_ragged": dict(cfg=1, batch=7, ctx=(1, 700), topk=640),
 }
 
 
