@@ -118,8 +118,8 @@ const char *dsa_status_string(dsa_status status);
  * q_idx    device [T, n_heads, head_dim], format q_format, contiguous
  * w        device [T, n_heads] f32 (any extra scale is folded in by the caller)
  * k_idx    indexer key pool, dim == head_dim, format == q_format
- * scores   device [T, ld] f32, ld >= max_seq_len.  Entries s > pos(t) are NOT
- *          written.
+ * scores   device [T, ld] f32, ld >= max_seq_len.  Entries s > pos(t), and
+ *          entries of tokens whose page is not mapped, are NOT written.
  * Built combinations: (DSA_BF16, n_heads 64, head_dim 128) on MFMA;
  * (DSA_F32, n_heads <= 64, head_dim <= 256) on the vector ALUs.
  */

@@ -2,8 +2,29 @@
 // caller's stream.  Nothing here allocates, synchronises or reads device memory.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+#include <set>
+#include <utility>
+
 #include "../../include/dsa.h"
 #include "dsa_launch.h"
+
+namespace dsa {
+
+hipError_t ensure_max_lds(const void* kernel) {
+  static std::mutex mu;
+  static std::set<std::pair<int, const void*>> done;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done.count({dev, kernel})) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (e == hipSuccess) done.insert({dev, kernel});
+  return e;
+}
+
+}  // namespace dsa
 
 namespace {
 
@@ -115,6 +136,7 @@ dsa_status dsa_index_scores(const dsa_batch* batch, const void* q_idx, int32_t q
     if (n_heads != 64 || head_dim != 128) return DSA_ERR_UNSUPPORTED;
     if ((st = check_pool(k_idx, 256, 16, &pa)) != DSA_OK) return st;
     if (!aligned(q_idx, 16)) return DSA_ERR_ALIGN;
+    if (ba.num_pages == 0) return DSA_OK;  // no token is mapped: nothing is written
     return hip_status(dsa::launch_index_scores_bf16(ba, q_idx, w, pa, scores, ld, s));
   }
   if (q_format == DSA_F32) {

@@ -22,6 +22,10 @@ struct PoolArgs {
   int64_t page_stride, row_stride;
 };
 
+// Lets `kernel` use up to the 160 KB of LDS of a gfx950 CU.  The attribute is
+// set once per kernel and device; later calls only look it up.
+hipError_t ensure_max_lds(const void* kernel);
+
 hipError_t launch_index_scores_bf16(const BatchArgs& ba, const void* q_idx, const float* w,
                                     const PoolArgs& pool, float* scores, int64_t ld,
                                     hipStream_t stream);

@@ -6,16 +6,18 @@
 // "Changes", and of mlx-lm PR 1419's description; the pages name the
 // indexer without a formula and this is its plain reading.)
 //
-// MFMA kernel (bf16, 64 heads x 128 dims).  One workgroup of four waves owns
-// one request, a chunk of 256 consecutive cached tokens and a group of up to
-// eight consecutive query rows of that request.  Each wave holds the keys of
-// 64 tokens in registers, already in the B-operand layout of
-// v_mfma_f32_32x32x16_bf16, and reuses them for every row of the group; the
-// query rows sit in LDS and feed the A operand (heads on M, tokens on N).
-// The ReLU, the per-head weight and the sum over heads are applied to the
-// accumulators in registers: a lane owns one token column and half of the
-// heads, so one cross-lane add finishes each score.  Keys are read straight
-// from their pages (no copy of the cache), once per row group.
+// MFMA kernel (bf16, 64 heads x 128 dims).  A workgroup of four waves owns one
+// request, a chunk of 512 consecutive cached tokens and a group of up to
+// eight consecutive query rows of that request.  Each wave walks two blocks
+// of 64 tokens; a block's keys are loaded straight from their pages into
+// registers, already in the B-operand layout of v_mfma_f32_32x32x16_bf16, and
+// used for every row of the group (two waves per SIMD hide each other's load
+// latency).  The group's query rows sit in LDS (copied in with
+// global_load_lds while the page lookups and first keys load) and feed the A operand
+// (heads on M, tokens on N).  The ReLU, the per-head weight and the sum over
+// heads are applied to the accumulators in registers: a lane owns one token
+// column and half of the heads, so one cross-lane add finishes each score.
+// Keys are read in place (no copy of the cache), once per row group.
 //
 // Reduction-index layout: the dot product over the 128 dims is summed in any
 // order, so the k slots of each MFMA are mapped to dims such that every lane
@@ -31,12 +33,44 @@ namespace {
 constexpr int kHeads = 64;
 constexpr int kDim = 128;
 constexpr int kWaves = 4;
-constexpr int kKeysPerWave = 64;
-constexpr int kKeysPerBlock = kWaves * kKeysPerWave;  // 256
-constexpr int kHeadStrideLds = kDim * 2 + 16;         // 272 B: rows start on different banks
-constexpr int kRowBytesLds = kHeads * kHeadStrideLds; // 17408 B per staged query row
+constexpr int kThreads = kWaves * kWave;
+constexpr int kKeysPerStep = 64;                                  // per wave and step
+constexpr int kSteps = 2;                                         // steps per wave
+constexpr int kKeysPerBlock = kWaves * kSteps * kKeysPerStep;     // 512 per workgroup
+constexpr int kHeadSlots = 17;                                    // 16 chunks of 16 B + 1 pad
+constexpr int kHeadStrideLds = kHeadSlots * 16;                   // 272 B: heads start on distinct banks
+constexpr int kRowSlots = kHeads * kHeadSlots;                    // 1088
+constexpr int kRowBytesLds = kRowSlots * 16;                      // 17408 B per staged query row
 
-__global__ __launch_bounds__(kWaves * kWave) void index_scores_bf16_mfma(
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+
+// 16-byte copy HBM -> LDS for every active lane of the wave: lane i's bytes land
+// at lds_wave_base + 16 i (global_load_lds_dwordx4, LDS base in M0).
+__device__ inline void copy16_to_lds(const void* src, uint8_t* lds_wave_base) {
+  const uint32_t l = (uint32_t)(uintptr_t)(lds_u8_t*)lds_wave_base;
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(l))
+               : "memory");
+}
+
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Keys of one wave step: two 32-token column tiles x eight k steps.  The loads
+// are unconditional (a token without a mapped page reads the pool's first row
+// and its score is not written), so every step issues exactly 16 loads per lane.
+struct Keys {
+  bf16x8 v[2][8];
+};
+
+__device__ inline void load_keys(Keys& kk, const int64_t (&off)[2], const uint8_t* k_base, int lane) {
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const uint8_t* p = k_base + (off[nt] < 0 ? 0 : off[nt]) + (lane >> 5) * 128;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) kk.v[nt][ks] = *reinterpret_cast<const bf16x8*>(p + ks * 16);
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 2) void index_scores_bf16_mfma(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ page_table, int pt_stride, int page_size, int num_pages,
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
@@ -58,73 +92,88 @@ __global__ __launch_bounds__(kWaves * kWave) void index_scores_bf16_mfma(
   const int k0 = blockIdx.x * kKeysPerBlock;
   if (k0 > pos_last) return;  // uniform across the block: causal skip
 
-  // Stage the group's query rows (16 B chunks) and weights into LDS.
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int64_t row0 = (int64_t)q0 + r0;
-  for (int c = threadIdx.x; c < nr * kHeads * 16; c += kWaves * kWave) {
-    const int r = c >> 10, h = (c >> 4) & 63, ch = c & 15;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(q_idx + ((row0 + r) * kHeads + h) * kDim + ch * 8);
-    *reinterpret_cast<u32x4*>(q_lds + r * kRowBytesLds + h * kHeadStrideLds + ch * 16) = v;
-  }
-  for (int c = threadIdx.x; c < nr * kHeads; c += kWaves * kWave) w_lds[c] = w[row0 * kHeads + c];
-  __syncthreads();
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int s_base = k0 + wave * kKeysPerWave;
-  if (s_base > pos_last) return;  // no barrier follows
-
-  // Keys of this wave's 64 tokens: two 32-token column tiles, eight K steps.
-  bf16x8 bk[2][8];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int s = s_base + nt * 32 + (lane & 31);
-    int64_t off = -1;
-    if (s <= pos_last)
-      off = token_offset(page_table, pt_stride, page_size, num_pages, b, s, k_page_stride, k_row_stride);
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) bk[nt][ks] = bf16x8{};
-    if (off >= 0) {
-      const uint8_t* p = k_base + off + (lane >> 5) * 128;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) bk[nt][ks] = *reinterpret_cast<const bf16x8*>(p + ks * 16);
+  // 1. Query rows -> LDS (padded per head; the pad slot repeats chunk 15).
+  {
+    const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(q_idx + row0 * kHeads * kDim);
+    const int n_slots = nr * kRowSlots;
+    for (int base = 0; base < n_slots; base += kThreads) {
+      const int slot = base + tid;
+      const int r = slot / kRowSlots, rem = slot - r * kRowSlots;
+      const int h = rem / kHeadSlots, ch = min(rem - h * kHeadSlots, 15);
+      if (slot < n_slots)
+        copy16_to_lds(qsrc + ((r * kHeads + h) * kDim + ch * 8) * 2, smem + (base + wave * kWave) * 16);
     }
   }
+  float wv[2] = {0.f, 0.f};  // nr * 64 <= 512 weights, two per thread
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    if (tid + k * kThreads < nr * kHeads) wv[k] = w[row0 * kHeads + tid + k * kThreads];
 
-  for (int r = 0; r < nr; ++r) {
-    const int pos_r = (int)min<int64_t>((int64_t)pos_first + r, ld_last);
-    if (s_base > pos_r) continue;
-    f32x16 acc[2][2];
+  // 2. Page lookups for this wave's tokens, then the first step's 16 key loads.
+  int64_t off[kSteps][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-    const uint8_t* qa = q_lds + r * kRowBytesLds + (lane & 31) * kHeadStrideLds + (lane >> 5) * 128;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(qa + ks * 16);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(qa + 32 * kHeadStrideLds + ks * 16);
-      acc[0][0] = mfma32(a0, bk[0][ks], acc[0][0]);
-      acc[0][1] = mfma32(a1, bk[0][ks], acc[0][1]);
-      acc[1][0] = mfma32(a0, bk[1][ks], acc[1][0]);
-      acc[1][1] = mfma32(a1, bk[1][ks], acc[1][1]);
-    }
-    // Accumulator (i, lane) of a 32x32 tile holds head 8*(i/4) + 4*(lane/32) + i%4
-    // and token column lane%32.
-    const float* wr = w_lds + r * kHeads + 4 * (lane >> 5);
-    float wv[2][16];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) wv[mt][i] = wr[mt * 32 + 8 * (i >> 2) + (i & 3)];
+  for (int j = 0; j < kSteps; ++j)
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      float part = 0.f;
+      const int s = k0 + (j * kWaves + wave) * kKeysPerStep + nt * 32 + (lane & 31);
+      off[j][nt] = s <= pos_last ? token_offset(page_table, pt_stride, page_size, num_pages, b, s,
+                                                k_page_stride, k_row_stride)
+                                 : -1;
+    }
+  Keys kk;
+  load_keys(kk, off[0], k_base, lane);
+  // Everything issued before those 16 loads (the copies above) is complete.
+  asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+  for (int k = 0; k < 2; ++k)
+    if (tid + k * kThreads < nr * kHeads) w_lds[tid + k * kThreads] = wv[k];
+  lds_barrier();  // q and w visible to every wave; the keys stay in flight
+
+  // 3. Steps of 64 tokens: every row of the group against the step's keys.
 #pragma unroll
-        for (int i = 0; i < 16; ++i) part += wv[mt][i] * fmaxf(acc[nt][mt][i], 0.f);
-      part += __shfl_xor(part, 32);
-      const int s = s_base + nt * 32 + (lane & 31);
-      if (lane < 32 && s <= pos_r) scores[(row0 + r) * ld + s] = part;
+  for (int j = 0; j < kSteps; ++j) {
+    const int s_base = k0 + (j * kWaves + wave) * kKeysPerStep;
+    if (s_base > pos_last) break;                        // later steps are further right
+    if (j > 0) load_keys(kk, off[j], k_base, lane);
+    for (int r = 0; r < nr; ++r) {
+      const int pos_r = (int)min<int64_t>((int64_t)pos_first + r, ld_last);
+      if (s_base > pos_r) continue;
+      f32x16 acc[2][2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) acc[i][jj] = f32x16{};
+      const uint8_t* qa = q_lds + r * kRowBytesLds + (lane & 31) * kHeadStrideLds + (lane >> 5) * 128;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(qa + ks * 16);
+        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(qa + 32 * kHeadStrideLds + ks * 16);
+        acc[0][0] = mfma32(a0, kk.v[0][ks], acc[0][0]);
+        acc[0][1] = mfma32(a1, kk.v[0][ks], acc[0][1]);
+        acc[1][0] = mfma32(a0, kk.v[1][ks], acc[1][0]);
+        acc[1][1] = mfma32(a1, kk.v[1][ks], acc[1][1]);
+      }
+      // Accumulator (i, lane) of a 32x32 tile holds head 8*(i/4) + 4*(lane/32) + i%4
+      // and token column lane%32.
+      const float* wr = w_lds + r * kHeads + 4 * (lane >> 5);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        float part = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 wq = *reinterpret_cast<const f32x4*>(wr + mt * 32 + 8 * q4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) part += wq[e] * fmaxf(acc[nt][mt][4 * q4 + e], 0.f);
+          }
+        part += __shfl_xor(part, 32);
+        const int s = s_base + nt * 32 + (lane & 31);
+        if (lane < 32 && s <= pos_r && off[j][nt] >= 0) scores[(row0 + r) * ld + s] = part;
+      }
     }
   }
 }
@@ -161,25 +210,23 @@ __global__ __launch_bounds__(256) void index_scores_f32_valu(
   scores[(int64_t)t * ld + s] = acc;
 }
 
+
 }  // namespace
 
 hipError_t launch_index_scores_bf16(const BatchArgs& ba, const void* q_idx, const float* w,
                                     const PoolArgs& pool, float* scores, int64_t ld,
                                     hipStream_t stream) {
-  // Row groups: one row per group for single-token decode, the whole draft
-  // for short multi-token rows, four rows for long prefill chunks.
+  // Row groups: the whole draft for decode-sized q_len, four rows for long
+  // prefill chunks (LDS: 17 KB per staged row).
   int rg = ba.max_q_len <= 8 ? ba.max_q_len : 4;
   if (rg < 1) rg = 1;
   const size_t lds = (size_t)rg * kRowBytesLds + (size_t)rg * kHeads * sizeof(float);
   dim3 grid((ba.max_seq_len + kKeysPerBlock - 1) / kKeysPerBlock,
             (ba.max_q_len + rg - 1) / rg, ba.batch);
   if (grid.x == 0 || grid.y == 0) return hipSuccess;
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(index_scores_bf16_mfma),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(index_scores_bf16_mfma, grid, dim3(kWaves * kWave), lds, stream,
+  hipError_t e = ensure_max_lds(reinterpret_cast<const void*>(index_scores_bf16_mfma));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(index_scores_bf16_mfma, grid, dim3(kThreads), lds, stream,
                      ba.cu_q, ba.seq_lens, ba.page_table, ba.pt_stride, ba.page_size, ba.num_pages,
                      static_cast<const uint16_t*>(q_idx), w, static_cast<const uint8_t*>(pool.base),
                      pool.page_stride, pool.row_stride, scores, ld, rg);

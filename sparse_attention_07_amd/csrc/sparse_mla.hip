@@ -796,8 +796,7 @@ size_t mla_lds(int rps) {
 template <typename Kernel>
 hipError_t launch_with_lds(Kernel kernel, dim3 grid, size_t lds, hipStream_t stream, const MlaArgs& args,
                            int n_groups, int T) {
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = ensure_max_lds(reinterpret_cast<const void*>(kernel));
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kernel, grid, dim3(kThreads), lds, stream, args, n_groups, T);
   return hipGetLastError();
