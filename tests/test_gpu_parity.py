@@ -224,3 +224,26 @@ def test_perf_mode_index_overlap():
         g = p.scores[rows[i], :n].double().cpu().numpy()
         r = ref_scores[i, :n]
         assert np.max(np.abs(g - r)) <= 1e-3 * max(1.0, np.max(np.abs(r)))
+
+
+def test_graph_replay_matches_eager():
+    """A captured step replays to the eager result bitwise, replay after replay."""
+    from sparse_attention_07_amd.path import DSAPath
+    sb = synth.make_batch(2, batch=6, ctx=(600, 4000), topk=512, layers=2, mode="perf", device=DEV)
+    p = DSAPath(sb)
+    p.step()
+    torch.cuda.synchronize()
+    ref = [p.idx.clone()] + [o.clone() for o in p.out] + [l.clone() for l in p.lse]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        p.step()
+    for rep in range(3):
+        for t in [p.idx] + p.out + p.lse:
+            t.fill_(7)                                    # eager work between replays
+        torch.cuda.synchronize()
+        _say("graph replay", rep)
+        g.replay()
+        torch.cuda.synchronize()
+        got = [p.idx] + p.out + p.lse
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b), "replay %d differs" % rep
