@@ -45,7 +45,42 @@ def parse():
     ap.add_argument("--sets", type=int, default=0, help="input sets rotated (0 = auto)")
     ap.add_argument("--mode", default="perf", choices=["perf", "parity"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (f32 multiply by 1) four times, the "
+                         "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
+
+
+# HBM traffic of the dominant kernel per launch, from two rocprofv3 --pmc passes
+# (FETCH_SIZE, then WRITE_SIZE) over `bench.py --no-cpu --steps 8 --warmup 2`,
+# each counter scaled by bytes / counter-bytes of the copy calibration kernel.
+# Keyed by workload; `src` is the sha256 of the kernel's sources when the
+# counters were taken -- a changed kernel reports traffic null.
+TRAFFIC = {}
+KERNEL_SOURCES = {"sparse_mla": ["sparse_mla.hip", "dsa_device.h"],
+                  "index_scores": ["index_scores.hip", "dsa_device.h"],
+                  "topk": ["topk.hip", "dsa_device.h"]}
+
+
+def source_digest(stage):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[stage]:
+        with open(os.path.join(ROOT, "sparse_attention_07_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def copy_calibration():
+    n = 1 << 28                                    # 2^28 f32 = 1 GiB read + 1 GiB written
+    src = torch.ones(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"read_bytes": 4 * n, "write_bytes": 4 * n, "launches": 4}}),
+          flush=True)
 
 
 def algorithmic(sb, path):
@@ -105,9 +140,12 @@ def cpu_baseline(cfg_id, budget_s=20.0):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(use --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     from sparse_attention_07_amd import synth
     from sparse_attention_07_amd.path import DSAPath
 
@@ -221,6 +259,10 @@ def main():
         ach = r["alg_flops"] / (stage_ms[dom] / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": ach, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                 "frac": ach / MFMA_BF16_PEAK_TFS, "traffic": None}
+    tr = TRAFFIC.get((cfg_id, dom))
+    if tr is not None and tr["src"] == source_digest(dom):
+        roof["traffic"] = tr["fetch_bytes"] + tr["write_bytes"]
+        roof["traffic_detail"] = tr
     roof["kernel"] = dom
     roof["alg_bytes_per_launch"] = r["alg_bytes"] / launches
     roof["alg_flops_per_launch"] = r["alg_flops"] / launches

@@ -18,7 +18,8 @@
  * - Pointers named in dsa_batch / dsa_pool and every array argument are
  *   DEVICE pointers, except the two structs themselves, which live on the
  *   host and are read during the call only.  The caller owns all memory;
- *   the library allocates nothing and keeps no state between calls.
+ *   the library allocates nothing and keeps no state between calls other
+ *   than what a workspace holds.
  * - Every call only validates its host-side arguments and enqueues kernels
  *   on `stream` (a hipStream_t; NULL = the legacy default stream).  It never
  *   synchronises and never reads device memory on the host, so a sequence
@@ -165,7 +166,11 @@ size_t dsa_sparse_mla_workspace_bytes(int32_t num_q_rows, int32_t n_heads, int32
  * kv       latent pool, dim == dc+dr
  * idx      device [T, k] int32 (the dsa_topk output, or a shared layer's copy)
  * out      device [T, n_heads, dc], format q_format
- * ws       device workspace of dsa_sparse_mla_workspace_bytes() bytes
+ * ws       device workspace of dsa_sparse_mla_workspace_bytes() bytes.  It
+ *          holds per-split partials and arrival counters; the caller must
+ *          zero-fill it once before its first use, and every call returns it
+ *          with the counters zero again.  Calls that may run at the same time
+ *          (other streams) need workspaces of their own.
  * Built combinations: q DSA_BF16 with kv DSA_BF16 or DSA_FP8_E4M3_B128,
  * dc 512, dr 64, n_heads a multiple of 16 up to 128 (MFMA); q and kv DSA_F32
  * with dc+dr <= 1024, n_heads <= 128, k <= 4096 (vector ALUs).

@@ -19,7 +19,11 @@ hipError_t ensure_max_lds(const void* kernel) {
   if (e != hipSuccess) return e;
   std::lock_guard<std::mutex> lock(mu);
   if (done.count({dev, kernel})) return hipSuccess;
-  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  hipFuncAttributes attr;
+  e = hipFuncGetAttributes(&attr, kernel);
+  if (e != hipSuccess) return e;
+  const int dyn = 160 * 1024 - static_cast<int>(attr.sharedSizeBytes);  // static LDS counts too
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, dyn);
   if (e == hipSuccess) done.insert({dev, kernel});
   return e;
 }

@@ -41,7 +41,8 @@ hipError_t launch_topk(const BatchArgs& ba, const float* scores, int64_t ld, int
 struct MlaPlan {
   int splits;
   int rows_per_split;
-  size_t ws_bytes;
+  size_t ws_bytes;         // split partials, then arrival counters (0 when splits == 1)
+  size_t counters_offset;  // byte offset of the counters in the workspace
 };
 MlaPlan plan_sparse_mla(int num_q_rows, int n_heads, int k, int dc, bool prefill);
 

@@ -50,8 +50,9 @@
 // spilled.)
 //
 // When the selected rows of a query are split across workgroups, each writes
-// (m, l, unnormalised O) partials and a second kernel merges them by
-// log-sum-exp.
+// (m, l, unnormalised O) partials; the last split of a (query, head group) to
+// finish, found with an arrival counter, merges them by log-sum-exp in the
+// same launch.
 #include "dsa_device.h"
 #include "dsa_launch.h"
 
@@ -238,7 +239,8 @@ struct MlaArgs {
   float scale_log2;
   uint16_t* out;
   float* lse;
-  float* ws;
+  float* ws;       // split partials: [T, head groups, splits] blocks of 514 f32 per head
+  int* counters;   // [T, head groups] arrivals per row and head group
   int splits, rows_per_split;
 };
 
@@ -255,6 +257,123 @@ __device__ inline bool softmax_step(float mt, float& m_run, float& alpha) {
     return true;
   }
   return false;
+}
+
+// Split partials are exchanged between workgroups with device-scope (sc1)
+// stores and loads, the cache policy the compiler gives relaxed agent-scope
+// atomics on gfx950: they are performed at the device coherence point, past
+// the per-XCD L2, so the only ordering needed is that a workgroup's partial
+// stores are complete before its arrival is counted.  (A device-scope fence
+// would also do, but its release writes back the XCD's whole L2, and hundreds
+// of workgroups doing that serialise.)  The 16-byte forms are inline asm, so
+// the compiler does not track them: ld16_agent results are only valid after
+// wait_loads().
+__device__ inline void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float ld_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void st16_agent(float* p, f32x4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
+__device__ inline f32x4 ld16_agent(const float* p) {
+  f32x4 v;
+  asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+
+// Partials of one (row, head group, split): O exactly as the waves hold it,
+// [wave][column tile][lane] f32x4 (the four heads 4g..4g+3 of lane group g at
+// one column), so each store instruction writes 1 KB contiguous; then (m, l)
+// per head.  nh * 514 floats.
+__device__ inline float* split_block(const MlaArgs& a, int t, int grp, int n_groups, int nh, int sp) {
+  return a.ws + (((int64_t)t * n_groups + grp) * a.splits + sp) * nh * 514;
+}
+
+// Called by every thread of a workgroup after it stored its split's block.
+// The last of the (row, head group)'s splits to arrive, found with an arrival
+// counter, merges all splits by log-sum-exp into out/lse and resets the
+// counter to zero, so no separate merge launch is needed and the counters are
+// left as they were found.  WIDE: 64 heads, each wave 16 heads x 512 columns;
+// else 16 heads, each wave 16 heads x 128 columns.  `wgt` is LDS space for
+// 2 * nh * splits floats (the tile buffer, free by now); `is_last` one LDS int.
+template <bool WIDE>
+__device__ inline void merge_splits_if_last(const MlaArgs& a, int t, int grp, int n_groups,
+                                            int* counter, float* wgt, int* is_last, int tid) {
+  constexpr int kNh = WIDE ? 64 : 16;
+  constexpr int kTiles = WIDE ? 32 : 8;  // 16-column tiles per wave
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's partial stores are done
+  __syncthreads();                                    // ... and every other thread's
+  if (tid == 0)
+    *is_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               a.splits - 1;
+  __syncthreads();
+  if (!*is_last) return;
+  const int S = a.splits, h0 = grp * kNh;
+  const float* blk0 = split_block(a, t, grp, n_groups, kNh, 0);
+  const int64_t bstride = (int64_t)kNh * 514;
+  float* ls = wgt + kNh * S;
+  for (int i = tid; i < kNh * S; i += kThreads) {  // i = h * S + s
+    const float* st = blk0 + (i % S) * bstride + kNh * 512 + 2 * (i / S);
+    wgt[i] = ld_agent(st);
+    ls[i] = ld_agent(st + 1);
+  }
+  __syncthreads();
+  for (int h = tid; h < kNh; h += kThreads) {  // m -> merge weight exp2(m - M) / L, in place
+    float* wh = wgt + h * S;
+    float M = kNegInf;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, wh[s]);
+    float L = 0.f;
+    if (M != kNegInf)
+      for (int s = 0; s < S; ++s) L += exp2f(wh[s] - M) * ls[h * S + s];  // empty split: 0
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    for (int s = 0; s < S; ++s) wh[s] = L > 0.f ? exp2f(wh[s] - M) * inv : 0.f;
+    if (a.lse != nullptr) a.lse[(int64_t)t * a.H + h0 + h] = L > 0.f ? (M + __log2f(L)) * kLn2 : kNegInf;
+  }
+  __syncthreads();
+  // Weighted sum over splits of each 16-byte chunk (four heads at one column):
+  // a thread takes four chunks at a time and issues their loads for eight
+  // splits before using any, so the merge costs a few memory latencies.
+  constexpr int kIt = 4, kSp = 8, kChunks = kNh * 128;
+  for (int c0 = tid; c0 < kChunks; c0 += kThreads * kIt) {
+    f32x4 acc[kIt];
+#pragma unroll
+    for (int u = 0; u < kIt; ++u) acc[u] = f32x4{};
+    for (int s0 = 0; s0 < S; s0 += kSp) {
+      const int ns = min(kSp, S - s0);
+      f32x4 v[kIt][kSp];
+#pragma unroll
+      for (int u = 0; u < kIt; ++u)
+#pragma unroll
+        for (int s = 0; s < kSp; ++s)
+          if (s < ns) v[u][s] = ld16_agent(blk0 + (s0 + s) * bstride + (c0 + u * kThreads) * 4);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int u = 0; u < kIt; ++u) {
+        const int c = c0 + u * kThreads, lane = c & 63, w = c / (kTiles * 64);
+        const int hb = (WIDE ? 16 * w : 0) + 4 * (lane >> 4);
+#pragma unroll
+        for (int s = 0; s < kSp; ++s) {
+          if (s < ns) {
+            asm volatile("" : "+v"(v[u][s]));  // consumed only after the wait above
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[u][r] += wgt[(hb + r) * S + s0 + s] * v[u][s][r];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kIt; ++u) {
+      const int c = c0 + u * kThreads, lane = c & 63, w = c / (kTiles * 64), i2 = (c >> 6) % kTiles;
+      const int hb = (WIDE ? 16 * w : 0) + 4 * (lane >> 4);
+      const int col = (WIDE ? 0 : 128 * w) + 16 * i2 + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        a.out[((int64_t)t * a.H + h0 + hb + r) * kDc + col] = __builtin_bit_cast(uint16_t, (__bf16)acc[u][r]);
+    }
+  }
+  if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------- kernel
@@ -464,18 +583,16 @@ __global__ __launch_bounds__(kThreads, DSPLIT == 4 ? 2 : 1) void sparse_mla_tile
     if (a.lse != nullptr && writes_stats && lane < 16)
       a.lse[(int64_t)t * a.H + head0 + lane] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : kNegInf;
   } else {
+    float* blk = split_block(a, t, grp, n_groups, kHeadsPerGroup, sp);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int h = 4 * g + r;
-      float* wp = a.ws + (((int64_t)t * a.H + head0 + h) * a.splits + sp) * 516 + col0 + c16;
-#pragma unroll
-      for (int i2 = 0; i2 < kColTiles; ++i2) wp[16 * i2] = o[i2][r];
-    }
+    for (int i2 = 0; i2 < kColTiles; ++i2) st16_agent(blk + ((wave * kColTiles + i2) * 64 + lane) * 4, o[i2]);
     if (writes_stats && lane < 16) {
-      float* wp = a.ws + (((int64_t)t * a.H + head0 + lane) * a.splits + sp) * 516 + 512;
-      wp[0] = m_run;
-      wp[1] = l_run;
+      float* st = blk + kHeadsPerGroup * 512 + 2 * (head0 - grp * kHeadsPerGroup + lane);
+      st_agent(st, m_run);
+      st_agent(st + 1, l_run);
     }
+    merge_splits_if_last<DSPLIT == 1>(a, t, grp, n_groups, a.counters + (int64_t)t * n_groups + grp,
+                                      reinterpret_cast<float*>(tile), first_valid + 1, tid);
   }
 }
 
@@ -656,52 +773,16 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_q16(MlaArgs a, int n_g
     if (a.lse != nullptr && wave == 0 && lane < 16)
       a.lse[(int64_t)t * a.H + head0 + lane] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : kNegInf;
   } else {
+    float* blk = split_block(a, t, grp, n_groups, 16, sp);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int h = 4 * g + r;
-      float* wp = a.ws + (((int64_t)t * a.H + head0 + h) * a.splits + sp) * 516 + col0 + c16;
-#pragma unroll
-      for (int i2 = 0; i2 < 8; ++i2) wp[16 * i2] = o[i2][r];
-    }
+    for (int i2 = 0; i2 < 8; ++i2) st16_agent(blk + ((wave * 8 + i2) * 64 + lane) * 4, o[i2]);
     if (wave == 0 && lane < 16) {
-      float* wp = a.ws + (((int64_t)t * a.H + head0 + lane) * a.splits + sp) * 516 + 512;
-      wp[0] = m_run;
-      wp[1] = l_run;
+      st_agent(blk + 16 * 512 + 2 * lane, m_run);
+      st_agent(blk + 16 * 512 + 2 * lane + 1, l_run);
     }
+    merge_splits_if_last<false>(a, t, grp, n_groups, a.counters + (int64_t)t * n_groups + grp,
+                                reinterpret_cast<float*>(tile), first_valid + 1, tid);
   }
-}
-
-// Merge per-split partials: one wave per (row, head); lane covers 8 columns.
-__global__ __launch_bounds__(kWave) void sparse_mla_combine(const float* __restrict__ ws, int H,
-                                                            int splits, uint16_t* __restrict__ out,
-                                                            float* __restrict__ lse) {
-  const int t = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
-  const float* base = ws + ((int64_t)t * H + h) * splits * 516;
-  float M = kNegInf;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, base[s * 516 + 512]);
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float L = 0.f;
-  if (M != kNegInf) {
-    for (int s = 0; s < splits; ++s) {
-      const float* p = base + s * 516;
-      const float wgt = exp2f(p[512] - M);  // an empty split has m = -inf, weight 0
-      L += wgt * p[513];
-      const f32x4 a = *reinterpret_cast<const f32x4*>(p + lane * 8);
-      const f32x4 c = *reinterpret_cast<const f32x4*>(p + lane * 8 + 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[i] += wgt * a[i];
-        acc[4 + i] += wgt * c[i];
-      }
-    }
-  }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  u32x4 pk;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) pk[c] = pack_bf16x2(acc[2 * c] * inv, acc[2 * c + 1] * inv);
-  *reinterpret_cast<u32x4*>(out + ((int64_t)t * H + h) * kDc + lane * 8) = pk;
-  if (lse != nullptr && lane == 0)
-    lse[(int64_t)t * H + h] = L > 0.f ? (M + __log2f(L)) * kLn2 : kNegInf;
 }
 
 // f32 path on the vector ALUs: one wave per (row, head), up to 4096 selected
@@ -763,14 +844,15 @@ __global__ __launch_bounds__(kWave) void sparse_mla_f32_valu(
 }  // namespace
 
 MlaPlan plan_sparse_mla(int num_q_rows, int n_heads, int k, int dc, bool prefill) {
-  MlaPlan p{1, k, 0};
+  MlaPlan p{1, k, 0, 0};
   if (dc != kDc || n_heads % 16 != 0 || k <= 0 || num_q_rows <= 0) return p;
   const bool wide = n_heads % 64 == 0;
   const int64_t blocks = (int64_t)num_q_rows * (wide ? n_heads / 64 : n_heads / 16);
   int splits = 1;
   if (!prefill) {
     const int64_t target = wide ? 384 : 512;
-    const int max_splits = k / 256 > 1 ? k / 256 : 1;
+    // at most 64 splits: the merge keeps 2 x 64 heads x splits floats in the tile buffer
+    const int max_splits = k / 256 > 64 ? 64 : (k / 256 > 1 ? k / 256 : 1);
     const int64_t want = (target + blocks - 1) / blocks;
     splits = (int)(want < 1 ? 1 : (want > max_splits ? max_splits : want));
   }
@@ -779,7 +861,12 @@ MlaPlan plan_sparse_mla(int num_q_rows, int n_heads, int k, int dc, bool prefill
   splits = (k + rps - 1) / rps;
   p.splits = splits;
   p.rows_per_split = rps;
-  p.ws_bytes = splits > 1 ? (size_t)num_q_rows * n_heads * splits * 516 * sizeof(float) : 0;
+  if (splits > 1) {
+    // partials, then one arrival counter per (row, head group)
+    p.counters_offset = ((size_t)num_q_rows * n_heads * splits * 514 * sizeof(float) + 255) / 256 * 256;
+    p.ws_bytes = p.counters_offset +
+                 ((size_t)num_q_rows * (wide ? n_heads / 64 : n_heads / 16) * sizeof(int) + 255) / 256 * 256;
+  }
   return p;
 }
 
@@ -815,8 +902,10 @@ hipError_t launch_sparse_mla_bf16(const BatchArgs& ba, const void* q, const Pool
   MlaArgs args{ba.cu_q, ba.seq_lens, ba.page_table, ba.batch, ba.pt_stride, ba.page_size,
                ba.num_pages, static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(kv.base),
                kv.page_stride, kv.row_stride, idx, k, n_heads, sm_scale * kLog2e,
-               static_cast<uint16_t*>(out), lse, static_cast<float*>(ws), plan.splits,
-               plan.rows_per_split};
+               static_cast<uint16_t*>(out), lse, static_cast<float*>(ws),
+               plan.splits > 1 ? reinterpret_cast<int*>(static_cast<uint8_t*>(ws) + plan.counters_offset)
+                               : nullptr,
+               plan.splits, plan.rows_per_split};
   const int T = ba.num_q_rows;
   const int n_groups = wide ? n_heads / 64 : n_heads / 16;
   const dim3 grid((unsigned)((T + 7) / 8 * 8 * n_groups), 1, plan.splits);
@@ -829,11 +918,7 @@ hipError_t launch_sparse_mla_bf16(const BatchArgs& ba, const void* q, const Pool
   else
     e = fp8 ? launch_with_lds(sparse_mla_q16<true>, grid, lds, stream, args, n_groups, T)
             : launch_with_lds(sparse_mla_q16<false>, grid, lds, stream, args, n_groups, T);
-  if (e != hipSuccess || plan.splits == 1) return e;
-  hipLaunchKernelGGL(sparse_mla_combine, dim3(ba.num_q_rows, n_heads), dim3(kWave), 0, stream,
-                     static_cast<const float*>(ws), n_heads, plan.splits,
-                     static_cast<uint16_t*>(out), lse);
-  return hipGetLastError();
+  return e;
 }
 
 hipError_t launch_sparse_mla_f32(const BatchArgs& ba, const void* q, const PoolArgs& kv,

@@ -32,7 +32,9 @@ class DSAPath:
         self.lse = [torch.empty((T, cfg.heads), dtype=torch.float32, device=dev) for _ in sb.q]
         self.prefill = (sb.max_q_len > 64) if prefill is None else prefill
         self.ws_bytes = dsa.dsa_sparse_mla_workspace_bytes(T, cfg.heads, cfg.topk, cfg.dc, self.prefill)
-        self.ws = torch.empty((max(self.ws_bytes, 16),), dtype=torch.uint8, device=dev)
+        # zero-filled once: the split-merge counters in it start at 0 and every call
+        # leaves them at 0
+        self.ws = torch.zeros((max(self.ws_bytes, 16),), dtype=torch.uint8, device=dev)
         self.topk_ws_bytes = dsa.dsa_topk_workspace_bytes(T, sb.max_seq_len, cfg.topk)
         self.topk_ws = (torch.empty((self.topk_ws_bytes,), dtype=torch.uint8, device=dev)
                         if self.topk_ws_bytes else None)
