@@ -56,7 +56,15 @@ def parse():
 # each counter scaled by bytes / counter-bytes of the copy calibration kernel.
 # Keyed by workload; `src` is the sha256 of the kernel's sources when the
 # counters were taken -- a changed kernel reports traffic null.
-TRAFFIC = {}
+# Copy calibration of those runs: FETCH_SIZE x 2.000, WRITE_SIZE x 1.000.
+TRAFFIC = {
+    (1, "sparse_mla"): {"src": "65641cdba03f15e8", "fetch_bytes": 1.659e+08, "write_bytes": 1.798e+07,
+                        "dispatches": 42},
+    (1, "index_scores"): {"src": "82d73a2c9c04c901", "fetch_bytes": 8.335e+07, "write_bytes": 1.183e+06,
+                          "dispatches": 42},
+    (1, "topk"): {"src": "b7c699e962083794", "fetch_bytes": 1.214e+06, "write_bytes": 5.243e+05,
+                  "dispatches": 42},
+}
 KERNEL_SOURCES = {"sparse_mla": ["sparse_mla.hip", "dsa_device.h"],
                   "index_scores": ["index_scores.hip", "dsa_device.h"],
                   "topk": ["topk.hip", "dsa_device.h"]}
@@ -69,6 +77,15 @@ def source_digest(stage):
         with open(os.path.join(ROOT, "sparse_attention_07_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def traffic(cfg_id, stage):
+    """Measured HBM bytes per launch (fetch + write), or None if not measured for
+    this workload or the kernel's sources changed since."""
+    tr = TRAFFIC.get((cfg_id, stage))
+    if tr is None or tr["src"] != source_digest(stage):
+        return None
+    return tr["fetch_bytes"] + tr["write_bytes"]
 
 
 def copy_calibration():
@@ -244,7 +261,8 @@ def main():
                      "alg_bytes": by, "alg_flops": fl,
                      "GB_s": by / t / 1e9, "TFLOP_s": fl / t / 1e12,
                      "frac_hbm": by / t / 1e9 / HBM_PEAK_GBS,
-                     "frac_mfma": fl / t / 1e12 / MFMA_BF16_PEAK_TFS}
+                     "frac_mfma": fl / t / 1e12 / MFMA_BF16_PEAK_TFS,
+                     "traffic": traffic(cfg_id, s)}
     dom = max(stages, key=lambda s: stage_ms[s])
     r = report[dom]
     t_hbm = r["alg_bytes"] / (HBM_PEAK_GBS * 1e9)
@@ -259,10 +277,7 @@ def main():
         ach = r["alg_flops"] / (stage_ms[dom] / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": ach, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                 "frac": ach / MFMA_BF16_PEAK_TFS, "traffic": None}
-    tr = TRAFFIC.get((cfg_id, dom))
-    if tr is not None and tr["src"] == source_digest(dom):
-        roof["traffic"] = tr["fetch_bytes"] + tr["write_bytes"]
-        roof["traffic_detail"] = tr
+    roof["traffic"] = r["traffic"]
     roof["kernel"] = dom
     roof["alg_bytes_per_launch"] = r["alg_bytes"] / launches
     roof["alg_flops_per_launch"] = r["alg_flops"] / launches
