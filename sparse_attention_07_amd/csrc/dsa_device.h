@@ -15,23 +15,43 @@ constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Query row t belongs to the request b with cu_q[b] <= t < cu_q[b+1].  The
-// search is clamped to [0, B-1] so inconsistent device data cannot index out
-// of bounds.
-__device__ inline int find_request(const int32_t* __restrict__ cu_q, int B, int t) {
-  int lo = 0, hi = B - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (cu_q[mid] <= t) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
+// Request b owning query row t (cu_q[b] <= t < cu_q[b+1]) and the row's
+// position seq_len[b] - q_len[b] + (t - cu_q[b]), found by one wave in one
+// round of loads per 256 requests: lane i tests request i of each 64-request
+// chunk and the owner's values are broadcast from its lane.  Every lane of
+// the wave must call it (wave-uniform result).  With inconsistent device data
+// (no owner) it returns request B-1, so callers stay in bounds.
+struct RowLoc {
+  int b, pos;
+};
 
-// Position of row t (request b) in its sequence: seq_len - q_len + j.
-__device__ inline int row_position(const int32_t* __restrict__ cu_q,
-                                   const int32_t* __restrict__ seq_lens, int b, int t) {
-  int q0 = cu_q[b], q1 = cu_q[b + 1];
-  return seq_lens[b] - (q1 - q0) + (t - q0);
+__device__ inline RowLoc locate_row(const int32_t* __restrict__ cu_q,
+                                    const int32_t* __restrict__ seq_lens, int B, int t) {
+  const int lane = threadIdx.x & (kWave - 1);
+  for (int i0 = 0; i0 < B; i0 += 4 * kWave) {
+    int lo[4], hi[4], sl[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int i = i0 + c * kWave + lane;
+      lo[c] = hi[c] = sl[c] = 0;
+      if (i < B) {
+        lo[c] = cu_q[i];
+        hi[c] = cu_q[i + 1];
+        sl[c] = seq_lens[i];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint64_t m = __ballot(lo[c] <= t && t < hi[c]);
+      if (m != 0) {
+        const int src = __ffsll((unsigned long long)m) - 1;
+        const int q0 = __shfl(lo[c], src), q1 = __shfl(hi[c], src), s = __shfl(sl[c], src);
+        return RowLoc{i0 + c * kWave + src, s - (q1 - q0) + (t - q0)};
+      }
+    }
+  }
+  const int q0 = cu_q[B - 1], q1 = cu_q[B];
+  return RowLoc{B - 1, seq_lens[B - 1] - (q1 - q0) + (t - q0)};
 }
 
 // Byte offset of logical token s of request b inside a pool, or -1 when the

@@ -189,8 +189,9 @@ __global__ __launch_bounds__(256) void index_scores_f32_valu(
   float* qs = reinterpret_cast<float*>(smem);
   float* ws = qs + n_heads * head_dim;
   const int t = blockIdx.y;
-  const int b = find_request(cu_q, B, t);
-  const int pos = (int)min<int64_t>(row_position(cu_q, seq_lens, b, t), ld - 1);
+  const RowLoc loc = locate_row(cu_q, seq_lens, B, t);
+  const int b = loc.b;
+  const int pos = (int)min<int64_t>(loc.pos, ld - 1);
   const int s0 = blockIdx.x * 256;
   if (s0 > pos) return;
   for (int i = threadIdx.x; i < n_heads * head_dim; i += 256) qs[i] = q_idx[(int64_t)t * n_heads * head_dim + i];

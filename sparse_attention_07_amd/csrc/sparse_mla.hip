@@ -403,8 +403,8 @@ __global__ __launch_bounds__(kThreads, DSPLIT == 4 ? 2 : 1) void sparse_mla_tile
   const int j_begin = sp * a.rows_per_split;
   const int j_end = min(a.K, j_begin + a.rows_per_split);
   const int ntiles = (j_end - j_begin + kTileRows - 1) / kTileRows;
-  const int b = find_request(a.cu_q, a.B, t);
-  const int pos = row_position(a.cu_q, a.seq_lens, b, t);
+  const RowLoc loc = locate_row(a.cu_q, a.seq_lens, a.B, t);
+  const int b = loc.b, pos = loc.pos;
   uint8_t* tile = smem;                                                 // one 32-row tile
   f32x4* sbuf = reinterpret_cast<f32x4*>(smem + kTileLds);              // partial scores (16 heads)
   int64_t* offs = reinterpret_cast<int64_t*>(smem + kTileLds + kSbufLds);
@@ -664,8 +664,8 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_q16(MlaArgs a, int n_g
   const int j_begin = sp * a.rows_per_split;
   const int j_end = min(a.K, j_begin + a.rows_per_split);
   const int ntiles = (j_end - j_begin + kTileRows - 1) / kTileRows;
-  const int b = find_request(a.cu_q, a.B, t);
-  const int pos = row_position(a.cu_q, a.seq_lens, b, t);
+  const RowLoc loc = locate_row(a.cu_q, a.seq_lens, a.B, t);
+  const int b = loc.b, pos = loc.pos;
   uint8_t* tile = smem;
   f32x4* sbuf = reinterpret_cast<f32x4*>(smem + kTileLds);
   int64_t* offs = reinterpret_cast<int64_t*>(smem + kTileLds + kSbufLds);
@@ -801,8 +801,8 @@ __global__ __launch_bounds__(kWave) void sparse_mla_f32_valu(
   __shared__ int64_t offs[kF32MaxK];
   const int t = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
   const int D = Dc + Dr;
-  const int b = find_request(cu_q, B, t);
-  const int pos = row_position(cu_q, seq_lens, b, t);
+  const RowLoc loc = locate_row(cu_q, seq_lens, B, t);
+  const int b = loc.b, pos = loc.pos;
   for (int d = lane; d < D; d += kWave) qs[d] = q[((int64_t)t * H + h) * D + d];
   __syncthreads();
   float m = kNegInf;
