@@ -2,6 +2,7 @@
 // caller's stream.  Nothing here allocates, synchronises or reads device memory.
 #include <hip/hip_runtime.h>
 
+#include <map>
 #include <mutex>
 #include <set>
 #include <utility>
@@ -26,6 +27,20 @@ hipError_t ensure_max_lds(const void* kernel) {
   e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, dyn);
   if (e == hipSuccess) done.insert({dev, kernel});
   return e;
+}
+
+int device_cu_count() {
+  static std::mutex mu;
+  static std::map<int, int> cus;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cus.find(dev);
+  if (it != cus.end()) return it->second;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+  cus[dev] = n;
+  return n;
 }
 
 }  // namespace dsa
@@ -139,7 +154,7 @@ dsa_status dsa_index_scores(const dsa_batch* batch, const void* q_idx, int32_t q
   if (q_format == DSA_BF16) {
     if (n_heads != 64 || head_dim != 128) return DSA_ERR_UNSUPPORTED;
     if ((st = check_pool(k_idx, 256, 16, &pa)) != DSA_OK) return st;
-    if (!aligned(q_idx, 16)) return DSA_ERR_ALIGN;
+    if (!aligned(q_idx, 16) || !aligned(w, 16)) return DSA_ERR_ALIGN;
     if (ba.num_pages == 0) return DSA_OK;  // no token is mapped: nothing is written
     return hip_status(dsa::launch_index_scores_bf16(ba, q_idx, w, pa, scores, ld, s));
   }

@@ -25,6 +25,8 @@ struct PoolArgs {
 // Lets `kernel` use up to the 160 KB of LDS of a gfx950 CU.  The attribute is
 // set once per kernel and device; later calls only look it up.
 hipError_t ensure_max_lds(const void* kernel);
+// Compute units of the current device (cached per device).
+int device_cu_count();
 
 hipError_t launch_index_scores_bf16(const BatchArgs& ba, const void* q_idx, const float* w,
                                     const PoolArgs& pool, float* scores, int64_t ld,

@@ -7,7 +7,8 @@
 // indexer without a formula and this is its plain reading.)
 //
 // MFMA kernel (bf16, 64 heads x 128 dims).  A workgroup of four waves owns one
-// request, a chunk of 512 consecutive cached tokens and a group of up to
+// request, a chunk of 512 consecutive cached tokens (chunk index outermost in
+// the grid, so that requests' empty tails dispatch last) and a group of up to
 // eight consecutive query rows of that request.  Each wave walks two blocks
 // of 64 tokens; a block's keys are loaded straight from their pages into
 // registers, already in the B-operand layout of v_mfma_f32_32x32x16_bf16, and
@@ -23,6 +24,8 @@
 // order, so the k slots of each MFMA are mapped to dims such that every lane
 // reads 128 contiguous bytes of one key: lane l (group g = l/32) supplies dims
 // g*64 + ks*8 .. +7 in step ks.  The query operand uses the same mapping.
+#include <algorithm>
+
 #include "dsa_device.h"
 #include "dsa_launch.h"
 
@@ -70,6 +73,53 @@ __device__ inline void load_keys(Keys& kk, const int64_t (&off)[2], const uint8_
   }
 }
 
+// One wave: scores of a 64-token block (keys kk, tokens s_base + 32 nt + lane%32,
+// page offsets off, -1 when unmapped) against the nr staged query rows; row r
+// sits at position pos_first + r (clamped to ld_last) and its output row is
+// row0 + r.
+__device__ inline void score_block(const Keys& kk, const int64_t (&off)[2], const uint8_t* q_lds,
+                                   const float* w_lds, int nr, int s_base, int pos_first,
+                                   int64_t ld_last, float* __restrict__ scores, int64_t row0,
+                                   int64_t ld, int lane) {
+  for (int r = 0; r < nr; ++r) {
+    const int pos_r = (int)min<int64_t>((int64_t)pos_first + r, ld_last);
+    if (s_base > pos_r) continue;
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) acc[i][jj] = f32x16{};
+    const uint8_t* qa = q_lds + r * kRowBytesLds + (lane & 31) * kHeadStrideLds + (lane >> 5) * 128;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(qa + ks * 16);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(qa + 32 * kHeadStrideLds + ks * 16);
+      acc[0][0] = mfma32(a0, kk.v[0][ks], acc[0][0]);
+      acc[0][1] = mfma32(a1, kk.v[0][ks], acc[0][1]);
+      acc[1][0] = mfma32(a0, kk.v[1][ks], acc[1][0]);
+      acc[1][1] = mfma32(a1, kk.v[1][ks], acc[1][1]);
+    }
+    // Accumulator (i, lane) of a 32x32 tile holds head 8*(i/4) + 4*(lane/32) + i%4
+    // and token column lane%32.
+    const float* wr = w_lds + r * kHeads + 4 * (lane >> 5);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float part = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 wq = *reinterpret_cast<const f32x4*>(wr + mt * 32 + 8 * q4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) part += wq[e] * fmaxf(acc[nt][mt][4 * q4 + e], 0.f);
+        }
+      part += __shfl_xor(part, 32);
+      const int s = s_base + nt * 32 + (lane & 31);
+      if (lane < 32 && s <= pos_r && off[nt] >= 0) scores[(row0 + r) * ld + s] = part;
+    }
+  }
+}
+
 __global__ __launch_bounds__(kThreads, 2) void index_scores_bf16_mfma(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ page_table, int pt_stride, int page_size, int num_pages,
@@ -80,7 +130,7 @@ __global__ __launch_bounds__(kThreads, 2) void index_scores_bf16_mfma(
   uint8_t* q_lds = smem;
   float* w_lds = reinterpret_cast<float*>(smem + (size_t)row_group * kRowBytesLds);
 
-  const int b = blockIdx.z;
+  const int b = blockIdx.x;
   const int q0 = cu_q[b];
   const int q_len = cu_q[b + 1] - q0;
   const int r0 = blockIdx.y * row_group;
@@ -89,7 +139,7 @@ __global__ __launch_bounds__(kThreads, 2) void index_scores_bf16_mfma(
   const int pos_first = seq_lens[b] - q_len + r0;
   const int64_t ld_last = ld - 1;
   const int pos_last = (int)min<int64_t>((int64_t)pos_first + nr - 1, ld_last);
-  const int k0 = blockIdx.x * kKeysPerBlock;
+  const int k0 = blockIdx.z * kKeysPerBlock;
   if (k0 > pos_last) return;  // uniform across the block: causal skip
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -123,10 +173,12 @@ __global__ __launch_bounds__(kThreads, 2) void index_scores_bf16_mfma(
                                                 k_page_stride, k_row_stride)
                                  : -1;
     }
-  Keys kk;
-  load_keys(kk, off[0], k_base, lane);
-  // Everything issued before those 16 loads (the copies above) is complete.
-  asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  // Both steps' keys go out at once (32 loads per lane).
+  Keys kk[kSteps];
+#pragma unroll
+  for (int j = 0; j < kSteps; ++j) load_keys(kk[j], off[j], k_base, lane);
+  // Everything issued before those 32 loads (the copies above) is complete.
+  asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
 #pragma unroll
   for (int k = 0; k < 2; ++k)
     if (tid + k * kThreads < nr * kHeads) w_lds[tid + k * kThreads] = wv[k];
@@ -137,44 +189,198 @@ __global__ __launch_bounds__(kThreads, 2) void index_scores_bf16_mfma(
   for (int j = 0; j < kSteps; ++j) {
     const int s_base = k0 + (j * kWaves + wave) * kKeysPerStep;
     if (s_base > pos_last) break;                        // later steps are further right
-    if (j > 0) load_keys(kk, off[j], k_base, lane);
-    for (int r = 0; r < nr; ++r) {
-      const int pos_r = (int)min<int64_t>((int64_t)pos_first + r, ld_last);
-      if (s_base > pos_r) continue;
-      f32x16 acc[2][2];
+    score_block(kk[j], off[j], q_lds, w_lds, nr, s_base, pos_first, ld_last, scores, row0, ld, lane);
+  }
+}
+
+// Persistent form for decode and draft batches (at most 8 rows per request):
+// one workgroup of eight waves per CU, each taking an equal share of all
+// requests' 64-token key blocks (concatenated request after request), so no
+// workgroup of the grid is empty and none waits for a second round.  The
+// share is walked in segments of one request: the request's query rows are
+// staged in LDS, then wave w scores blocks w, w+8, ... of the segment with the
+// page lookups two blocks ahead and the key loads one block ahead.
+constexpr int kFlatWaves = 8;
+constexpr int kFlatThreads = kFlatWaves * kWave;
+
+// Page offsets of the two 32-token halves a lane reads in block `blk` of
+// request b (-1 past pos_last or when unmapped).
+__device__ inline void block_offsets(int64_t (&off)[2], int blk_tok0, int pos_last,
+                                     const int32_t* __restrict__ page_table, int pt_stride,
+                                     int page_size, int num_pages, int b, int64_t page_stride,
+                                     int64_t row_stride, int lane) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) acc[i][jj] = f32x16{};
-      const uint8_t* qa = q_lds + r * kRowBytesLds + (lane & 31) * kHeadStrideLds + (lane >> 5) * 128;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(qa + ks * 16);
-        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(qa + 32 * kHeadStrideLds + ks * 16);
-        acc[0][0] = mfma32(a0, kk.v[0][ks], acc[0][0]);
-        acc[0][1] = mfma32(a1, kk.v[0][ks], acc[0][1]);
-        acc[1][0] = mfma32(a0, kk.v[1][ks], acc[1][0]);
-        acc[1][1] = mfma32(a1, kk.v[1][ks], acc[1][1]);
-      }
-      // Accumulator (i, lane) of a 32x32 tile holds head 8*(i/4) + 4*(lane/32) + i%4
-      // and token column lane%32.
-      const float* wr = w_lds + r * kHeads + 4 * (lane >> 5);
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        float part = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const f32x4 wq = *reinterpret_cast<const f32x4*>(wr + mt * 32 + 8 * q4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) part += wq[e] * fmaxf(acc[nt][mt][4 * q4 + e], 0.f);
-          }
-        part += __shfl_xor(part, 32);
-        const int s = s_base + nt * 32 + (lane & 31);
-        if (lane < 32 && s <= pos_r && off[j][nt] >= 0) scores[(row0 + r) * ld + s] = part;
-      }
+  for (int nt = 0; nt < 2; ++nt) {
+    const int s = blk_tok0 + nt * 32 + (lane & 31);
+    off[nt] = s <= pos_last ? token_offset(page_table, pt_stride, page_size, num_pages, b, s,
+                                           page_stride, row_stride)
+                            : -1;
+  }
+}
+
+// Last request b in [0, B) whose first block is at or below blk (the owner of
+// block blk; requests without blocks are passed over).  pre is in LDS.
+__device__ inline int last_at_or_below(const int* pre, int B, int blk) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] <= blk) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+struct FlatBlock {
+  int b, tok;       // request and its first token of the block
+  int64_t off[2];   // page offsets of this lane's two tokens
+};
+
+// Request and page offsets of block blk, walking forward from request b_from.
+__device__ inline void prep_block(FlatBlock& x, int blk, int b_from, const int* pre, const int* rql,
+                                  const int* rsl, int max_rows, int64_t ld_last,
+                                  const int32_t* __restrict__ page_table, int pt_stride,
+                                  int page_size, int num_pages, int64_t page_stride,
+                                  int64_t row_stride, int lane) {
+  int b = b_from;
+  while (pre[b + 1] <= blk) ++b;
+  x.b = b;
+  x.tok = (blk - pre[b]) * kKeysPerStep;
+  const int ql = rql[b], nr = min(ql, max_rows);
+  const int pos_last = (int)min<int64_t>((int64_t)rsl[b] - ql + nr - 1, ld_last);
+  block_offsets(x.off, x.tok, pos_last, page_table, pt_stride, page_size, num_pages, b, page_stride,
+                row_stride, lane);
+}
+
+__global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_lens, int B,
+    const int32_t* __restrict__ page_table, int pt_stride, int page_size, int num_pages,
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
+    const uint8_t* __restrict__ k_base, int64_t k_page_stride, int64_t k_row_stride,
+    float* __restrict__ scores, int64_t ld, int max_rows, int nslots) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  // LDS: nslots staged requests (query rows, then their weights), then the tables.
+  uint8_t* q_area = smem;
+  float* w_area = reinterpret_cast<float*>(smem + (size_t)nslots * max_rows * kRowBytesLds);
+  int* pre = reinterpret_cast<int*>(w_area + nslots * max_rows * kHeads);  // [B+1] first block of each request
+  int* rq0 = pre + B + 1;                                         // [B] cu_q[b]
+  int* rql = rq0 + B;                                             // [B] q_len
+  int* rsl = rql + B;                                             // [B] seq_len
+  int* wsum = rsl + B;                                            // [kFlatWaves]
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int64_t ld_last = ld - 1;
+
+  // 1. Blocks per request, ceil(min(seq_len, ld) / 64) for requests with rows,
+  //    and their exclusive prefix.
+  int carry = 0;
+  for (int c0 = 0; c0 < B; c0 += kFlatThreads) {
+    const int bb = c0 + tid;
+    int nb = 0;
+    if (bb < B) {
+      const int q0 = cu_q[bb], ql = cu_q[bb + 1] - q0, sl = seq_lens[bb];
+      rq0[bb] = q0;
+      rql[bb] = ql;
+      rsl[bb] = sl;
+      const int64_t n = min<int64_t>(sl, ld);
+      nb = (ql > 0 && n > 0) ? (int)((n + kKeysPerStep - 1) / kKeysPerStep) : 0;
     }
+    int x = nb;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int y = __shfl_up(x, d);
+      if (lane >= d) x += y;
+    }
+    if (lane == kWave - 1) wsum[wave] = x;
+    __syncthreads();
+    int before = carry, all = 0;
+#pragma unroll
+    for (int v = 0; v < kFlatWaves; ++v) {
+      const int c = wsum[v];
+      before += v < wave ? c : 0;
+      all += c;
+    }
+    if (bb < B) pre[bb] = before + x - nb;
+    carry += all;
+    __syncthreads();
+  }
+  if (tid == 0) pre[B] = carry;
+  __syncthreads();
+  const int per = (carry + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int start = (int)blockIdx.x * per, end = min(carry, start + per);
+
+  if (start >= end) return;
+
+  // 2. The requests the share touches are staged in LDS all at once when they
+  //    fit (slot = request - first staged request); otherwise the share is
+  //    walked one request at a time through slot 0.
+  const int b_first = last_at_or_below(pre, B, start), b_last = last_at_or_below(pre, B, end - 1);
+  const bool all_staged = b_last - b_first + 1 <= nslots;
+  int lo = start, b0 = b_first;
+  while (lo < end) {
+    const int hi = all_staged ? end : min(end, pre[b0 + 1]);
+    const int b_hi = all_staged ? b_last : b0;
+    for (int bb = b0; bb <= b_hi; ++bb) {  // query rows and weights -> LDS slot bb - b0
+      const int q0 = rq0[bb], nr = min(rql[bb], max_rows);
+      uint8_t* qd = q_area + (size_t)(bb - b0) * max_rows * kRowBytesLds;
+      const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(q_idx + (int64_t)q0 * kHeads * kDim);
+      const int n_slots = nr * kRowSlots;  // padded per head; the pad slot repeats chunk 15
+      for (int base = 0; base < n_slots; base += kFlatThreads) {
+        const int slot = base + tid;
+        const int r = slot / kRowSlots, rem = slot - r * kRowSlots;
+        const int h = rem / kHeadSlots, ch = min(rem - h * kHeadSlots, 15);
+        if (slot < n_slots)
+          copy16_to_lds(qsrc + ((r * kHeads + h) * kDim + ch * 8) * 2, qd + (base + wave * kWave) * 16);
+      }
+      uint8_t* wd = reinterpret_cast<uint8_t*>(w_area + (size_t)(bb - b0) * max_rows * kHeads);
+      const uint8_t* wsrc = reinterpret_cast<const uint8_t*>(w + (int64_t)q0 * kHeads);
+      for (int base = 0; base < nr * (kHeads / 4); base += kFlatThreads)
+        if (base + tid < nr * (kHeads / 4)) copy16_to_lds(wsrc + (base + tid) * 16, wd + (base + wave * kWave) * 16);
+    }
+
+    // This wave's blocks lo + wave + 8 i < hi.  A, B, C: the block being scored
+    // and the next two (keys of B in flight, page lookups of C in flight).
+    int j = lo + wave;
+    FlatBlock A{b0, 0, {-1, -1}}, Bk{b0, 0, {-1, -1}}, C{b0, 0, {-1, -1}};
+    if (j < hi) prep_block(A, j, b0, pre, rql, rsl, max_rows, ld_last, page_table, pt_stride, page_size,
+                           num_pages, k_page_stride, k_row_stride, lane);
+    if (j + kFlatWaves < hi)
+      prep_block(Bk, j + kFlatWaves, A.b, pre, rql, rsl, max_rows, ld_last, page_table, pt_stride,
+                 page_size, num_pages, k_page_stride, k_row_stride, lane);
+    Keys k0, k1;
+    load_keys(k0, A.off, k_base, lane);
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // staging copies and page lookups have landed
+    lds_barrier();
+
+#define DSA_SCORE(KK, X)                                                                           \
+  score_block(KK, X.off, q_area + (size_t)(X.b - b0) * max_rows * kRowBytesLds,                    \
+              w_area + (size_t)(X.b - b0) * max_rows * kHeads, min(rql[X.b], max_rows), X.tok,      \
+              rsl[X.b] - rql[X.b], ld_last, scores, rq0[X.b], ld, lane)
+    while (j < hi) {
+      // block j with k0, block j + 8 with k1
+      const bool has1 = j + kFlatWaves < hi;
+      if (has1) load_keys(k1, Bk.off, k_base, lane);
+      if (j + 2 * kFlatWaves < hi)
+        prep_block(C, j + 2 * kFlatWaves, Bk.b, pre, rql, rsl, max_rows, ld_last, page_table, pt_stride,
+                   page_size, num_pages, k_page_stride, k_row_stride, lane);
+      DSA_SCORE(k0, A);
+      if (!has1) break;
+      j += kFlatWaves;
+      A = Bk;
+      Bk = C;
+      const bool has1b = j + kFlatWaves < hi;
+      if (has1b) load_keys(k0, Bk.off, k_base, lane);
+      if (j + 2 * kFlatWaves < hi)
+        prep_block(C, j + 2 * kFlatWaves, Bk.b, pre, rql, rsl, max_rows, ld_last, page_table, pt_stride,
+                   page_size, num_pages, k_page_stride, k_row_stride, lane);
+      DSA_SCORE(k1, A);
+      if (!has1b) break;
+      j += kFlatWaves;
+      A = Bk;
+      Bk = C;
+    }
+#undef DSA_SCORE
+    lds_barrier();  // every wave is done with the staged rows
+    lo = hi;
+    if (lo < end) b0 = last_at_or_below(pre, B, lo);
   }
 }
 
@@ -217,14 +423,35 @@ __global__ __launch_bounds__(256) void index_scores_f32_valu(
 hipError_t launch_index_scores_bf16(const BatchArgs& ba, const void* q_idx, const float* w,
                                     const PoolArgs& pool, float* scores, int64_t ld,
                                     hipStream_t stream) {
+  if (ba.max_q_len >= 1 && ba.max_q_len <= 8) {
+    // Up to 8 requests staged at once, as many as fit next to the tables.
+    const size_t tables = ((size_t)(4 * ba.batch + 1 + kFlatWaves) * sizeof(int) + 15) / 16 * 16;
+    const size_t per_req = (size_t)ba.max_q_len * (kRowBytesLds + kHeads * sizeof(float));
+    const size_t avail = tables < 160 * 1024 ? 160 * 1024 - tables : 0;
+    const int nslots = (int)std::min<size_t>(8, avail / per_req);
+    const size_t lds = tables + (size_t)nslots * per_req;
+    if (nslots >= 1) {
+      hipError_t e = ensure_max_lds(reinterpret_cast<const void*>(index_scores_flat));
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(index_scores_flat, dim3(device_cu_count()), dim3(kFlatThreads), lds, stream,
+                         ba.cu_q, ba.seq_lens, ba.batch, ba.page_table, ba.pt_stride, ba.page_size,
+                         ba.num_pages, static_cast<const uint16_t*>(q_idx), w,
+                         static_cast<const uint8_t*>(pool.base), pool.page_stride, pool.row_stride,
+                         scores, ld, ba.max_q_len, nslots);
+      return hipGetLastError();
+    }
+  }
   // Row groups: the whole draft for decode-sized q_len, four rows for long
   // prefill chunks (LDS: 17 KB per staged row).
   int rg = ba.max_q_len <= 8 ? ba.max_q_len : 4;
   if (rg < 1) rg = 1;
   const size_t lds = (size_t)rg * kRowBytesLds + (size_t)rg * kHeads * sizeof(float);
-  dim3 grid((ba.max_seq_len + kKeysPerBlock - 1) / kKeysPerBlock,
-            (ba.max_q_len + rg - 1) / rg, ba.batch);
-  if (grid.x == 0 || grid.y == 0) return hipSuccess;
+  // Token chunks outermost: the early chunks, which every request has, are
+  // dispatched first and the empty tails of short requests last, so that they
+  // do not hold dispatch slots while real work waits.
+  dim3 grid(ba.batch, (ba.max_q_len + rg - 1) / rg,
+            (ba.max_seq_len + kKeysPerBlock - 1) / kKeysPerBlock);
+  if (grid.y == 0 || grid.z == 0) return hipSuccess;
   hipError_t e = ensure_max_lds(reinterpret_cast<const void*>(index_scores_bf16_mfma));
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(index_scores_bf16_mfma, grid, dim3(kThreads), lds, stream,
