@@ -21,7 +21,7 @@
 //   table applied, unusable entries marked -1) and a usable-row bitmask per
 //   32-row tile, in LDS.  Each tile is loaded with plain 16-byte global loads
 //   into registers (9 per thread for bf16 rows; 5 for fp8 rows, which are
-//   decoded to bf16 as e4m3 * block scale on the way), one or two tiles ahead
+//   decoded to bf16 as e4m3 * block scale on the way), one to three tiles ahead
 //   of the tile being computed, and written to a single LDS tile whose rows
 //   are padded to 1168 B (16 lanes reading 16 rows at one column then hit 16
 //   distinct bank groups).  Measured on MI355X, random 1152-byte row gathers
@@ -185,12 +185,27 @@ __device__ inline void stage_store(const Stage<FP8>& st, uint8_t* tile, int tid)
 // prologue costs two memory latencies per 2048 rows rather than two per row.
 // Returns the first usable slot, or INT32_MAX when the range has none.  Ends
 // with a barrier.
+constexpr int kIdxBatch = 8;
+
+// The first batch of a range's indices (thread tid: entries tid + 256 k).
+// They depend only on the row, so they are loaded before the row's request
+// and position are known.
+__device__ inline void preload_indices(int (&sv)[kIdxBatch], const int32_t* idx_row, int j_begin,
+                                       int j_end, int n_pad, int tid) {
+#pragma unroll
+  for (int k = 0; k < kIdxBatch; ++k) {
+    const int i = k * kThreads + tid;
+    const int j = j_begin + i;
+    sv[k] = (i < n_pad && j < j_end) ? idx_row[j] : -1;
+  }
+}
+
 __device__ inline int build_offsets(int64_t* offs, uint32_t* vmask, int* first_valid,
-                                    const int32_t* idx_row, int j_begin, int j_end, int n_pad,
-                                    int pos, int b, const int32_t* page_table, int pt_stride,
-                                    int page_size, int num_pages, int64_t page_stride,
-                                    int64_t row_stride, int tid) {
-  constexpr int kBatch = 8;
+                                    const int (&sv0)[kIdxBatch], const int32_t* idx_row,
+                                    int j_begin, int j_end, int n_pad, int pos, int b,
+                                    const int32_t* page_table, int pt_stride, int page_size,
+                                    int num_pages, int64_t page_stride, int64_t row_stride, int tid) {
+  constexpr int kBatch = kIdxBatch;
   if (tid == 0) *first_valid = INT32_MAX;
   for (int i = tid; i < n_pad / kTileRows; i += kThreads) vmask[i] = 0u;
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -200,7 +215,7 @@ __device__ inline int build_offsets(int64_t* offs, uint32_t* vmask, int* first_v
     for (int k = 0; k < kBatch; ++k) {
       const int i = base + k * kThreads + tid;
       const int j = j_begin + i;
-      sv[k] = (i < n_pad && j < j_end) ? idx_row[j] : -1;
+      sv[k] = base == 0 ? sv0[k] : ((i < n_pad && j < j_end) ? idx_row[j] : -1);
     }
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
@@ -239,7 +254,7 @@ struct MlaArgs {
   float scale_log2;
   uint16_t* out;
   float* lse;
-  float* ws;       // split partials: [T, head groups, splits] blocks of 514 f32 per head
+  float* ws;       // split partials: [T, head groups, splits] blocks of kPartBytes(heads per group)
   int* counters;   // [T, head groups] arrivals per row and head group
   int splits, rows_per_split;
 };
@@ -260,35 +275,66 @@ __device__ inline bool softmax_step(float mt, float& m_run, float& alpha) {
 }
 
 // Split partials are exchanged between workgroups with device-scope (sc1)
-// stores and loads, the cache policy the compiler gives relaxed agent-scope
-// atomics on gfx950: they are performed at the device coherence point, past
-// the per-XCD L2, so the only ordering needed is that a workgroup's partial
-// stores are complete before its arrival is counted.  (A device-scope fence
-// would also do, but its release writes back the XCD's whole L2, and hundreds
-// of workgroups doing that serialise.)  The 16-byte forms are inline asm, so
-// the compiler does not track them: ld16_agent results are only valid after
-// wait_loads().
-__device__ inline void st_agent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline float ld_agent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline void st16_agent(float* p, f32x4 v) {
-  asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
-}
-__device__ inline f32x4 ld16_agent(const float* p) {
-  f32x4 v;
-  asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(v) : "v"(p) : "memory");
-  return v;
+// buffer stores and loads, the cache policy the compiler gives relaxed
+// agent-scope atomics on gfx950: they are performed at the device coherence
+// point, past the per-XCD L2, so the only ordering needed is that a
+// workgroup's partial stores are complete before its arrival is counted.  (A
+// device-scope fence would also do, but its release writes back the XCD's
+// whole L2, and hundreds of workgroups doing that serialise.)  Buffer
+// intrinsics keep the accesses visible to the compiler's wait counting, and
+// the descriptor's size bounds them.
+constexpr int kSc1 = 16;                     // cache policy: device scope
+constexpr int kRawBufferWord3 = 0x00020000;  // gfx9-family raw buffer descriptor flags
+
+__device__ inline __amdgpu_buffer_rsrc_t raw_buffer(void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, bytes, kRawBufferWord3);
 }
 
-// Partials of one (row, head group, split): O exactly as the waves hold it,
-// [wave][column tile][lane] f32x4 (the four heads 4g..4g+3 of lane group g at
-// one column), so each store instruction writes 1 KB contiguous; then (m, l)
-// per head.  nh * 514 floats.
-__device__ inline float* split_block(const MlaArgs& a, int t, int grp, int n_groups, int nh, int sp) {
-  return a.ws + (((int64_t)t * n_groups + grp) * a.splits + sp) * nh * 514;
+// Partials of one (row, head group, split), kPartBytes(nh) bytes: O / l as
+// bf16, exactly as the waves hold it -- [wave][16-column tile][lane] x 4 heads
+// (the heads 4g..4g+3 of lane group g at one column), so each store
+// instruction writes 512 B contiguous -- then (m, l) per head as f32.
+// Normalised partials are bounded by the values attended, so bf16 keeps them
+// within the output's own rounding.
+__host__ __device__ constexpr int kPartBytes(int nh) { return nh * (kDc * 2 + 8); }
+
+// Descriptor over the partials of every split of (row t, head group grp).
+__device__ inline __amdgpu_buffer_rsrc_t split_blocks(const MlaArgs& a, int t, int grp, int n_groups, int nh) {
+  uint8_t* p = reinterpret_cast<uint8_t*>(a.ws) + ((int64_t)t * n_groups + grp) * a.splits * (int64_t)kPartBytes(nh);
+  return raw_buffer(p, a.splits * kPartBytes(nh));
+}
+
+// A split's partials: O / l of this lane's four heads (4g..4g+3) at its
+// columns as bf16, and when stat_h0 >= 0 (one wave per 16 heads) the (m, l)
+// of heads stat_h0 + lane for lanes < 16.  l_run is already the full sum.
+template <int NH, int TILES>
+__device__ inline void store_partials(const MlaArgs& a, int t, int grp, int n_groups, int sp, int wave,
+                                      int lane, const f32x4 (&o)[TILES], float m_run, float l_run,
+                                      int stat_h0) {
+  const __amdgpu_buffer_rsrc_t rs = split_blocks(a, t, grp, n_groups, NH);
+  const int base = sp * kPartBytes(NH);
+  const int g = lane >> 4;
+  float inv[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float lh = __shfl(l_run, 4 * g + r);  // lane h holds head h's l
+    inv[r] = lh > 0.f ? 1.f / lh : 0.f;
+  }
+#pragma unroll
+  for (int i2 = 0; i2 < TILES; ++i2) {
+    uint2 pk;
+    pk.x = pack_bf16x2(o[i2][0] * inv[0], o[i2][1] * inv[1]);
+    pk.y = pack_bf16x2(o[i2][2] * inv[2], o[i2][3] * inv[3]);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((__vector_size__(2 * sizeof(int)))) int, pk), rs,
+                                          base + ((wave * TILES + i2) * 64 + lane) * 8, 0, kSc1);
+  }
+  if (stat_h0 >= 0 && lane < 16) {
+    uint2 ml;
+    ml.x = __float_as_uint(m_run);
+    ml.y = __float_as_uint(l_run);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((__vector_size__(2 * sizeof(int)))) int, ml), rs,
+                                          base + NH * kDc * 2 + 8 * (stat_h0 + lane), 0, kSc1);
+  }
 }
 
 // Called by every thread of a workgroup after it stored its split's block.
@@ -311,66 +357,97 @@ __device__ inline void merge_splits_if_last(const MlaArgs& a, int t, int grp, in
   __syncthreads();
   if (!*is_last) return;
   const int S = a.splits, h0 = grp * kNh;
-  const float* blk0 = split_block(a, t, grp, n_groups, kNh, 0);
-  const int64_t bstride = (int64_t)kNh * 514;
+  const __amdgpu_buffer_rsrc_t rs = split_blocks(a, t, grp, n_groups, kNh);
+  constexpr int kStride = kPartBytes(kNh);
+  // Issue the first round of O loads before the statistics are reduced.
+  constexpr int kIt = 4, kSp = 8, kChunks = kNh * kDc * 2 / 16;  // 16-byte chunks of O per split
+  u32x4 v[kIt][kSp];
+  auto issue = [&](int c0, int s0) {
+#pragma unroll
+    for (int u = 0; u < kIt; ++u)
+#pragma unroll
+      for (int s = 0; s < kSp; ++s)
+        if (s0 + s < S)
+          v[u][s] = __builtin_amdgcn_raw_buffer_load_b128(rs, (s0 + s) * kStride + (c0 + u * kThreads) * 16, 0, kSc1);
+  };
+  issue(tid, 0);
   float* ls = wgt + kNh * S;
   for (int i = tid; i < kNh * S; i += kThreads) {  // i = h * S + s
-    const float* st = blk0 + (i % S) * bstride + kNh * 512 + 2 * (i / S);
-    wgt[i] = ld_agent(st);
-    ls[i] = ld_agent(st + 1);
+    const int off = (i % S) * kStride + kNh * kDc * 2 + 8 * (i / S);
+    const uint2 ml = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kSc1));
+    wgt[i] = __uint_as_float(ml.x);
+    ls[i] = __uint_as_float(ml.y);
   }
   __syncthreads();
-  for (int h = tid; h < kNh; h += kThreads) {  // m -> merge weight exp2(m - M) / L, in place
-    float* wh = wgt + h * S;
-    float M = kNegInf;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, wh[s]);
-    float L = 0.f;
-    if (M != kNegInf)
-      for (int s = 0; s < S; ++s) L += exp2f(wh[s] - M) * ls[h * S + s];  // empty split: 0
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    for (int s = 0; s < S; ++s) wh[s] = L > 0.f ? exp2f(wh[s] - M) * inv : 0.f;
-    if (a.lse != nullptr) a.lse[(int64_t)t * a.H + h0 + h] = L > 0.f ? (M + __log2f(L)) * kLn2 : kNegInf;
+  // Merge weight of (head h, split s): l_s exp2(m_s - M) / L, one thread per pair.
+  float wnew[(kNh * 64 + kThreads - 1) / kThreads];
+#pragma unroll
+  for (int k = 0; k < (kNh * 64 + kThreads - 1) / kThreads; ++k) {
+    const int i = tid + k * kThreads, h = i / S;
+    wnew[k] = 0.f;
+    if (i < kNh * S) {
+      const float* mh = wgt + h * S;
+      const float* lh = ls + h * S;
+      float M = kNegInf;
+      for (int s = 0; s < S; ++s) M = fmaxf(M, mh[s]);
+      float L = 0.f;
+      if (M != kNegInf)
+        for (int s = 0; s < S; ++s) L += exp2f(mh[s] - M) * lh[s];  // empty split: 0
+      const float ms = mh[i % S];
+      wnew[k] = L > 0.f ? exp2f(ms - M) * lh[i % S] / L : 0.f;
+      if (i % S == 0 && a.lse != nullptr)
+        a.lse[(int64_t)t * a.H + h0 + h] = L > 0.f ? (M + __log2f(L)) * kLn2 : kNegInf;
+    }
   }
   __syncthreads();
-  // Weighted sum over splits of each 16-byte chunk (four heads at one column):
-  // a thread takes four chunks at a time and issues their loads for eight
-  // splits before using any, so the merge costs a few memory latencies.
-  constexpr int kIt = 4, kSp = 8, kChunks = kNh * 128;
+#pragma unroll
+  for (int k = 0; k < (kNh * 64 + kThreads - 1) / kThreads; ++k)
+    if (tid + k * kThreads < kNh * S) wgt[tid + k * kThreads] = wnew[k];
+  __syncthreads();
+  // Chunk c holds lanes 2m, 2m+1 (m = c % 32) of tile (c / 32) % kTiles of
+  // wave c / (32 kTiles): heads hb..hb+3 at columns col, col+1.  A thread's
+  // chunks c0 + 256 u all share m, so for one wave their heads differ only by
+  // wave (wide) -- the weights of the thread's heads are read once per round.
   for (int c0 = tid; c0 < kChunks; c0 += kThreads * kIt) {
-    f32x4 acc[kIt];
+    float acc[kIt][8];
 #pragma unroll
-    for (int u = 0; u < kIt; ++u) acc[u] = f32x4{};
+    for (int u = 0; u < kIt; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[u][e] = 0.f;
     for (int s0 = 0; s0 < S; s0 += kSp) {
-      const int ns = min(kSp, S - s0);
-      f32x4 v[kIt][kSp];
-#pragma unroll
-      for (int u = 0; u < kIt; ++u)
-#pragma unroll
-        for (int s = 0; s < kSp; ++s)
-          if (s < ns) v[u][s] = ld16_agent(blk0 + (s0 + s) * bstride + (c0 + u * kThreads) * 4);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (c0 != tid || s0 != 0) issue(c0, s0);
 #pragma unroll
       for (int u = 0; u < kIt; ++u) {
-        const int c = c0 + u * kThreads, lane = c & 63, w = c / (kTiles * 64);
+        const int c = c0 + u * kThreads, lane = 2 * (c & 31), w = c / (32 * kTiles);
         const int hb = (WIDE ? 16 * w : 0) + 4 * (lane >> 4);
+        float wt[4][kSp];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int s = 0; s < kSp; ++s) wt[r][s] = s0 + s < S ? wgt[(hb + r) * S + s0 + s] : 0.f;
 #pragma unroll
         for (int s = 0; s < kSp; ++s) {
-          if (s < ns) {
-            asm volatile("" : "+v"(v[u][s]));  // consumed only after the wait above
+          if (s0 + s < S) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[u][r] += wgt[(hb + r) * S + s0 + s] * v[u][s][r];
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t x = v[u][s][e];
+              acc[u][2 * e] += wt[(2 * e) % 4][s] * __uint_as_float(x << 16);
+              acc[u][2 * e + 1] += wt[(2 * e + 1) % 4][s] * __uint_as_float(x & 0xFFFF0000u);
+            }
           }
         }
       }
     }
 #pragma unroll
     for (int u = 0; u < kIt; ++u) {
-      const int c = c0 + u * kThreads, lane = c & 63, w = c / (kTiles * 64), i2 = (c >> 6) % kTiles;
+      const int c = c0 + u * kThreads, lane = 2 * (c & 31), w = c / (32 * kTiles), i2 = (c / 32) % kTiles;
       const int hb = (WIDE ? 16 * w : 0) + 4 * (lane >> 4);
       const int col = (WIDE ? 0 : 128 * w) + 16 * i2 + (lane & 15);
+      // acc[u][e]: e < 4 -> head hb + e at col, e >= 4 -> head hb + e - 4 at col + 1
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        a.out[((int64_t)t * a.H + h0 + hb + r) * kDc + col] = __builtin_bit_cast(uint16_t, (__bf16)acc[u][r]);
+        *reinterpret_cast<uint32_t*>(a.out + ((int64_t)t * a.H + h0 + hb + r) * kDc + col) =
+            pack_bf16x2(acc[u][r], acc[u][4 + r]);
     }
   }
   if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -403,6 +480,8 @@ __global__ __launch_bounds__(kThreads, DSPLIT == 4 ? 2 : 1) void sparse_mla_tile
   const int j_begin = sp * a.rows_per_split;
   const int j_end = min(a.K, j_begin + a.rows_per_split);
   const int ntiles = (j_end - j_begin + kTileRows - 1) / kTileRows;
+  int sv0[kIdxBatch];
+  preload_indices(sv0, a.idx + (int64_t)t * a.K, j_begin, j_end, ntiles * kTileRows, tid);
   const RowLoc loc = locate_row(a.cu_q, a.seq_lens, a.B, t);
   const int b = loc.b, pos = loc.pos;
   uint8_t* tile = smem;                                                 // one 32-row tile
@@ -411,7 +490,7 @@ __global__ __launch_bounds__(kThreads, DSPLIT == 4 ? 2 : 1) void sparse_mla_tile
   uint32_t* vmask = reinterpret_cast<uint32_t*>(offs + ntiles * kTileRows);  // usable rows per tile
   int* first_valid = reinterpret_cast<int*>(vmask + ntiles);
 
-  const int fv = build_offsets(offs, vmask, first_valid, a.idx + (int64_t)t * a.K, j_begin, j_end,
+  const int fv = build_offsets(offs, vmask, first_valid, sv0, a.idx + (int64_t)t * a.K, j_begin, j_end,
                                ntiles * kTileRows, pos, b, a.page_table, a.pt_stride, a.page_size,
                                a.num_pages, a.page_stride, a.row_stride, tid);
 
@@ -583,14 +662,8 @@ __global__ __launch_bounds__(kThreads, DSPLIT == 4 ? 2 : 1) void sparse_mla_tile
     if (a.lse != nullptr && writes_stats && lane < 16)
       a.lse[(int64_t)t * a.H + head0 + lane] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : kNegInf;
   } else {
-    float* blk = split_block(a, t, grp, n_groups, kHeadsPerGroup, sp);
-#pragma unroll
-    for (int i2 = 0; i2 < kColTiles; ++i2) st16_agent(blk + ((wave * kColTiles + i2) * 64 + lane) * 4, o[i2]);
-    if (writes_stats && lane < 16) {
-      float* st = blk + kHeadsPerGroup * 512 + 2 * (head0 - grp * kHeadsPerGroup + lane);
-      st_agent(st, m_run);
-      st_agent(st + 1, l_run);
-    }
+    store_partials<kHeadsPerGroup, kColTiles>(a, t, grp, n_groups, sp, wave, lane, o, m_run, l_run,
+                                             writes_stats ? head0 - grp * kHeadsPerGroup : -1);
     merge_splits_if_last<DSPLIT == 1>(a, t, grp, n_groups, a.counters + (int64_t)t * n_groups + grp,
                                       reinterpret_cast<float*>(tile), first_valid + 1, tid);
   }
@@ -649,13 +722,18 @@ __device__ inline bf16x8 regtile_operand(const RegTile<FP8>& st, int k, int ks) 
   return __builtin_bit_cast(bf16x8, r);
 }
 
-template <bool FP8>
+template <bool FP8, int STAGES>
 __global__ __launch_bounds__(kThreads, 2) void sparse_mla_q16(MlaArgs a, int n_groups, int T) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int x = blockIdx.x, sp = blockIdx.z;
-  const int t = (x / (8 * n_groups)) * 8 + (x & 7);
-  const int grp = (x >> 3) % n_groups;
-  if (t >= T) return;                          // padding ids of the XCD-aware layout
+  // Workgroup ids: head group outermost over a block of P = (T * splits
+  // rounded up to 8) ids, so the head groups of one (row, split) are a
+  // multiple of 8 apart -- same XCD, sharing the gathered rows in its L2 --
+  // while consecutive splits and rows go to different XCDs and every XCD gets
+  // a like share of long and short rows.
+  const int P = (T * a.splits + 7) / 8 * 8;
+  const int grp = (int)blockIdx.x / P, u = (int)blockIdx.x % P;
+  if (u >= T * a.splits) return;               // padding ids
+  const int t = u / a.splits, sp = u % a.splits;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, c16 = lane & 15;
   const int rb = wave & 1, ks0 = 9 * (wave >> 1);
@@ -664,6 +742,8 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_q16(MlaArgs a, int n_g
   const int j_begin = sp * a.rows_per_split;
   const int j_end = min(a.K, j_begin + a.rows_per_split);
   const int ntiles = (j_end - j_begin + kTileRows - 1) / kTileRows;
+  int sv0[kIdxBatch];
+  preload_indices(sv0, a.idx + (int64_t)t * a.K, j_begin, j_end, ntiles * kTileRows, tid);
   const RowLoc loc = locate_row(a.cu_q, a.seq_lens, a.B, t);
   const int b = loc.b, pos = loc.pos;
   uint8_t* tile = smem;
@@ -679,7 +759,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_q16(MlaArgs a, int n_g
 #pragma unroll
     for (int k = 0; k < 9; ++k) qreg[k] = *reinterpret_cast<const bf16x8*>(qp + k * 32);
   }
-  const int fv = build_offsets(offs, vmask, first_valid, a.idx + (int64_t)t * a.K, j_begin, j_end,
+  const int fv = build_offsets(offs, vmask, first_valid, sv0, a.idx + (int64_t)t * a.K, j_begin, j_end,
                                ntiles * kTileRows, pos, b, a.page_table, a.pt_stride, a.page_size,
                                a.num_pages, a.page_stride, a.row_stride, tid);
 
@@ -702,7 +782,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_q16(MlaArgs a, int n_g
         spart = mfma16(av, qreg[k], spart);
       }
       sbuf[wave * 64 + lane] = spart;
-      if (i + 2 < ntiles) regtile_load<FP8>(st, offs[(i + 2) * kTileRows + my_row], a.kv, ks0, g);
+      if (i + STAGES < ntiles) regtile_load<FP8>(st, offs[(i + STAGES) * kTileRows + my_row], a.kv, ks0, g);
       lds_barrier();                                       // tile i and partial scores visible
       const uint32_t valid = vmask[i];
       // rows 0..15 from waves 0 and 2, rows 16..31 from waves 1 and 3; k half 0 first
@@ -747,13 +827,15 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_q16(MlaArgs a, int n_g
 #pragma unroll
       for (int i2 = 0; i2 < 8; ++i2) o[i2] = mfma16(pa, join(tv1[i2], tv2[i2]), o[i2]);
     };
-    RegTile<FP8> st0, st1;
+    RegTile<FP8> st0, st1, st2;
     regtile_load<FP8>(st0, offs[my_row], a.kv, ks0, g);
     if (ntiles > 1) regtile_load<FP8>(st1, offs[kTileRows + my_row], a.kv, ks0, g);
+    if (STAGES == 3 && ntiles > 2) regtile_load<FP8>(st2, offs[2 * kTileRows + my_row], a.kv, ks0, g);
 #pragma unroll 1
-    for (int i = 0; i < ntiles; i += 2) {
+    for (int i = 0; i < ntiles; i += STAGES) {
       step(st0, i);
       if (i + 1 < ntiles) step(st1, i + 1);
+      if (STAGES == 3 && i + 2 < ntiles) step(st2, i + 2);
     }
   }
 
@@ -773,13 +855,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_q16(MlaArgs a, int n_g
     if (a.lse != nullptr && wave == 0 && lane < 16)
       a.lse[(int64_t)t * a.H + head0 + lane] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : kNegInf;
   } else {
-    float* blk = split_block(a, t, grp, n_groups, 16, sp);
-#pragma unroll
-    for (int i2 = 0; i2 < 8; ++i2) st16_agent(blk + ((wave * 8 + i2) * 64 + lane) * 4, o[i2]);
-    if (wave == 0 && lane < 16) {
-      st_agent(blk + 16 * 512 + 2 * lane, m_run);
-      st_agent(blk + 16 * 512 + 2 * lane + 1, l_run);
-    }
+    store_partials<16, 8>(a, t, grp, n_groups, sp, wave, lane, o, m_run, l_run, wave == 0 ? 0 : -1);
     merge_splits_if_last<false>(a, t, grp, n_groups, a.counters + (int64_t)t * n_groups + grp,
                                 reinterpret_cast<float*>(tile), first_valid + 1, tid);
   }
@@ -863,7 +939,7 @@ MlaPlan plan_sparse_mla(int num_q_rows, int n_heads, int k, int dc, bool prefill
   p.rows_per_split = rps;
   if (splits > 1) {
     // partials, then one arrival counter per (row, head group)
-    p.counters_offset = ((size_t)num_q_rows * n_heads * splits * 514 * sizeof(float) + 255) / 256 * 256;
+    p.counters_offset = ((size_t)num_q_rows * n_heads * splits * (kDc * 2 + 8) + 255) / 256 * 256;
     p.ws_bytes = p.counters_offset +
                  ((size_t)num_q_rows * (wide ? n_heads / 64 : n_heads / 16) * sizeof(int) + 255) / 256 * 256;
   }
@@ -908,7 +984,9 @@ hipError_t launch_sparse_mla_bf16(const BatchArgs& ba, const void* q, const Pool
                plan.splits, plan.rows_per_split};
   const int T = ba.num_q_rows;
   const int n_groups = wide ? n_heads / 64 : n_heads / 16;
-  const dim3 grid((unsigned)((T + 7) / 8 * 8 * n_groups), 1, plan.splits);
+  // 64-head groups: ids t, split on z (row-major XCD layout); 16-head groups: see sparse_mla_q16.
+  const dim3 grid = wide ? dim3((unsigned)((T + 7) / 8 * 8 * n_groups), 1, plan.splits)
+                         : dim3((unsigned)(n_groups * ((T * plan.splits + 7) / 8 * 8)), 1, 1);
   hipError_t e;
   // Tiles of loads in flight per workgroup: two for 16-head groups (two
   // workgroups per CU), one for 64-head groups (a second would spill).
@@ -916,8 +994,8 @@ hipError_t launch_sparse_mla_bf16(const BatchArgs& ba, const void* q, const Pool
     e = fp8 ? launch_with_lds(sparse_mla_tiles<1, true, 1>, grid, lds, stream, args, n_groups, T)
             : launch_with_lds(sparse_mla_tiles<1, false, 1>, grid, lds, stream, args, n_groups, T);
   else
-    e = fp8 ? launch_with_lds(sparse_mla_q16<true>, grid, lds, stream, args, n_groups, T)
-            : launch_with_lds(sparse_mla_q16<false>, grid, lds, stream, args, n_groups, T);
+    e = fp8 ? launch_with_lds(sparse_mla_q16<true, 2>, grid, lds, stream, args, n_groups, T)
+            : launch_with_lds(sparse_mla_q16<false, 3>, grid, lds, stream, args, n_groups, T);
   return e;
 }
 

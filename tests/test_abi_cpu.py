@@ -119,9 +119,9 @@ def test_sparse_mla_validation():
 def test_split_workspace_is_consistent(T, H, k):
     ws = dsa.dsa_sparse_mla_workspace_bytes(T, H, k, 512, False)
     if ws:
-        # partials (514 f32 per row, head and split) and one int32 counter per
-        # (row, head group), each region padded to 256 bytes
-        per = T * H * 514 * 4
+        # partials (512 bf16 + two f32 per row, head and split) and one int32
+        # counter per (row, head group), each region padded to 256 bytes
+        per = T * H * (512 * 2 + 8)
         groups = T * (H // 64 if H % 64 == 0 else H // 16)
         cnt = (groups * 4 + 255) // 256 * 256
         part = ws - cnt
