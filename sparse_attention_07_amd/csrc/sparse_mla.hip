@@ -91,22 +91,26 @@ __device__ inline bf16x8 join(s16x4 a, s16x4 b) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
-// e4m3fn (OCP OFP8) byte -> float, exact.  Exponent bias 7, subnormals
-// m/8 * 2^-6; the NaN code (S.1111.111) is not expected in a cache.
-__device__ inline float e4m3_to_f32(uint32_t byte) {
-  const uint32_t sign = (byte & 0x80u) << 24;
-  const uint32_t e = (byte >> 3) & 0xFu, m = byte & 0x7u;
-  float mag;
-  if (e == 0)
-    mag = (float)m * 0.001953125f;  // m * 2^-9
-  else
-    mag = __uint_as_float(((e + 120u) << 23) | (m << 20));  // rebias 7 -> 127
-  return __uint_as_float(__float_as_uint(mag) | sign);
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+
+// Two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
-__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
-  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+// Four e4m3 bytes (one dword, byte 0 first) -> four bf16 of e4m3 * sc.  The
+// hardware conversion at scale 1 is exact (every e4m3 value is a bf16; its
+// scale operand only takes a power of two), then the block scale is applied
+// in f32 and rounded to bf16 once -- the same value as decoding e4m3 into f32
+// and rounding the product.
+__device__ inline uint2 fp8x4_to_bf16x4(uint32_t x, float sc) {
+  const uint32_t a = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false));
+  const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true));
+  uint2 r;
+  r.x = pack_bf16x2(__uint_as_float(a << 16) * sc, __uint_as_float(a & 0xFFFF0000u) * sc);
+  r.y = pack_bf16x2(__uint_as_float(b << 16) * sc, __uint_as_float(b & 0xFFFF0000u) * sc);
+  return r;
 }
 
 // One tile's rows in flight in registers: bf16 rows as 9 chunks per thread
@@ -164,11 +168,9 @@ __device__ inline void stage_store(const Stage<FP8>& st, uint8_t* tile, int tid)
       u32x4 lo, hi;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const uint32_t x = st.v[it][w];
-        const uint32_t p0 = pack_bf16x2(e4m3_to_f32(x & 0xFFu) * sc, e4m3_to_f32((x >> 8) & 0xFFu) * sc);
-        const uint32_t p1 = pack_bf16x2(e4m3_to_f32((x >> 16) & 0xFFu) * sc, e4m3_to_f32(x >> 24) * sc);
-        if (w < 2) { lo[2 * w] = p0; lo[2 * w + 1] = p1; }
-        else { hi[2 * w - 4] = p0; hi[2 * w - 3] = p1; }
+        const uint2 pr = fp8x4_to_bf16x4(st.v[it][w], sc);
+        if (w < 2) { lo[2 * w] = pr.x; lo[2 * w + 1] = pr.y; }
+        else { hi[2 * w - 4] = pr.x; hi[2 * w - 3] = pr.y; }
       }
       *reinterpret_cast<u32x4*>(dst + ch * 32) = lo;
       *reinterpret_cast<u32x4*>(dst + ch * 32 + 16) = hi;
@@ -713,12 +715,8 @@ template <bool FP8>
 __device__ inline bf16x8 regtile_operand(const RegTile<FP8>& st, int k, int ks) {
   if (!FP8 || ks >= 16) return __builtin_bit_cast(bf16x8, st.v[k]);
   const float sc = st.sc[ks >> 2];
-  const uint32_t x0 = st.v[k][0], x1 = st.v[k][1];
-  u32x4 r;
-  r[0] = pack_bf16x2(e4m3_to_f32(x0 & 0xFFu) * sc, e4m3_to_f32((x0 >> 8) & 0xFFu) * sc);
-  r[1] = pack_bf16x2(e4m3_to_f32((x0 >> 16) & 0xFFu) * sc, e4m3_to_f32(x0 >> 24) * sc);
-  r[2] = pack_bf16x2(e4m3_to_f32(x1 & 0xFFu) * sc, e4m3_to_f32((x1 >> 8) & 0xFFu) * sc);
-  r[3] = pack_bf16x2(e4m3_to_f32((x1 >> 16) & 0xFFu) * sc, e4m3_to_f32(x1 >> 24) * sc);
+  const uint2 p0 = fp8x4_to_bf16x4(st.v[k][0], sc), p1 = fp8x4_to_bf16x4(st.v[k][1], sc);
+  const u32x4 r = {p0.x, p0.y, p1.x, p1.y};
   return __builtin_bit_cast(bf16x8, r);
 }
 
