@@ -231,24 +231,46 @@ __device__ inline int last_at_or_below(const int* pre, int B, int blk) {
 }
 
 struct FlatBlock {
-  int b, tok;       // request and its first token of the block
+  int u, tok;       // unit and its first token of the block
   int64_t off[2];   // page offsets of this lane's two tokens
 };
 
-// Request and page offsets of block blk, walking forward from request b_from.
-__device__ inline void prep_block(FlatBlock& x, int blk, int b_from, const int* pre, const int* rql,
-                                  const int* rsl, int max_rows, int64_t ld_last,
+// Unit and page offsets of block blk, walking forward from unit u_from.
+__device__ inline void prep_block(FlatBlock& x, int blk, int u_from, const int* pre, const int* unr,
+                                  const int* upf, const int* ub, int64_t ld_last,
                                   const int32_t* __restrict__ page_table, int pt_stride,
                                   int page_size, int num_pages, int64_t page_stride,
                                   int64_t row_stride, int lane) {
-  int b = b_from;
-  while (pre[b + 1] <= blk) ++b;
-  x.b = b;
-  x.tok = (blk - pre[b]) * kKeysPerStep;
-  const int ql = rql[b], nr = min(ql, max_rows);
-  const int pos_last = (int)min<int64_t>((int64_t)rsl[b] - ql + nr - 1, ld_last);
-  block_offsets(x.off, x.tok, pos_last, page_table, pt_stride, page_size, num_pages, b, page_stride,
+  int u = u_from;
+  while (pre[u + 1] <= blk) ++u;
+  x.u = u;
+  x.tok = (blk - pre[u]) * kKeysPerStep;
+  const int pos_last = (int)min<int64_t>((int64_t)upf[u] + unr[u] - 1, ld_last);
+  block_offsets(x.off, x.tok, pos_last, page_table, pt_stride, page_size, num_pages, ub[u], page_stride,
                 row_stride, lane);
+}
+
+// Block exclusive scan over the workgroup of one int per thread (carry added);
+// returns this thread's exclusive prefix and adds the total to carry.
+__device__ inline int flat_excl_scan(int v, int* wsum, int& carry, int lane, int wave) {
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == kWave - 1) wsum[wave] = x;
+  __syncthreads();
+  int before = carry, all = 0;
+#pragma unroll
+  for (int w = 0; w < kFlatWaves; ++w) {
+    const int c = wsum[w];
+    before += w < wave ? c : 0;
+    all += c;
+  }
+  carry += all;
+  __syncthreads();
+  return before + x - v;
 }
 
 __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
@@ -256,71 +278,80 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
     const int32_t* __restrict__ page_table, int pt_stride, int page_size, int num_pages,
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint8_t* __restrict__ k_base, int64_t k_page_stride, int64_t k_row_stride,
-    float* __restrict__ scores, int64_t ld, int max_rows, int nslots) {
+    float* __restrict__ scores, int64_t ld, int rg, int nslots, int u_max) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  // LDS: nslots staged requests (query rows, then their weights), then the tables.
+  // LDS: nslots staged units (query rows, then their weights), then the tables.
   uint8_t* q_area = smem;
-  float* w_area = reinterpret_cast<float*>(smem + (size_t)nslots * max_rows * kRowBytesLds);
-  int* pre = reinterpret_cast<int*>(w_area + nslots * max_rows * kHeads);  // [B+1] first block of each request
-  int* rq0 = pre + B + 1;                                         // [B] cu_q[b]
+  float* w_area = reinterpret_cast<float*>(smem + (size_t)nslots * rg * kRowBytesLds);
+  int* rq0 = reinterpret_cast<int*>(w_area + nslots * rg * kHeads);  // [B] cu_q[b]
   int* rql = rq0 + B;                                             // [B] q_len
   int* rsl = rql + B;                                             // [B] seq_len
-  int* wsum = rsl + B;                                            // [kFlatWaves]
+  int* ubase = rsl + B;                                           // [B+1] first unit of each request
+  int* pre = ubase + B + 1;                                       // [u_max+1] first block of each unit
+  int* uq0 = pre + u_max + 1;                                     // [u_max] first row of the unit
+  int* unr = uq0 + u_max;                                         // [u_max] rows in the unit
+  int* upf = unr + u_max;                                         // [u_max] position of its first row
+  int* ub = upf + u_max;                                          // [u_max] its request
+  int* wsum = ub + u_max;                                         // [kFlatWaves]
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int64_t ld_last = ld - 1;
 
-  // 1. Blocks per request, ceil(min(seq_len, ld) / 64) for requests with rows,
-  //    and their exclusive prefix.
-  int carry = 0;
+  // 1. Units: runs of up to rg consecutive rows of one request.
+  int n_units = 0;
   for (int c0 = 0; c0 < B; c0 += kFlatThreads) {
     const int bb = c0 + tid;
-    int nb = 0;
+    int nu = 0;
     if (bb < B) {
-      const int q0 = cu_q[bb], ql = cu_q[bb + 1] - q0, sl = seq_lens[bb];
+      const int q0 = cu_q[bb], ql = cu_q[bb + 1] - q0;
       rq0[bb] = q0;
       rql[bb] = ql;
-      rsl[bb] = sl;
-      const int64_t n = min<int64_t>(sl, ld);
-      nb = (ql > 0 && n > 0) ? (int)((n + kKeysPerStep - 1) / kKeysPerStep) : 0;
+      rsl[bb] = seq_lens[bb];
+      nu = ql > 0 ? (ql + rg - 1) / rg : 0;
     }
-    int x = nb;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-      const int y = __shfl_up(x, d);
-      if (lane >= d) x += y;
-    }
-    if (lane == kWave - 1) wsum[wave] = x;
-    __syncthreads();
-    int before = carry, all = 0;
-#pragma unroll
-    for (int v = 0; v < kFlatWaves; ++v) {
-      const int c = wsum[v];
-      before += v < wave ? c : 0;
-      all += c;
-    }
-    if (bb < B) pre[bb] = before + x - nb;
-    carry += all;
-    __syncthreads();
+    const int e = flat_excl_scan(nu, wsum, n_units, lane, wave);
+    if (bb < B) ubase[bb] = e;
   }
-  if (tid == 0) pre[B] = carry;
+  n_units = min(n_units, u_max);  // rows beyond the host bound are not scored
+  if (tid == 0) ubase[B] = n_units;
+  __syncthreads();
+  // 2. Per unit: rows, position, and its 64-token blocks, ceil(min(pos_last + 1, ld) / 64).
+  int carry = 0;
+  for (int c0 = 0; c0 < n_units; c0 += kFlatThreads) {
+    const int u = c0 + tid;
+    int nb = 0;
+    if (u < n_units) {
+      const int b = last_at_or_below(ubase, B, u), j = u - ubase[b];
+      const int nr = min(rg, rql[b] - rg * j);
+      const int pf = rsl[b] - rql[b] + rg * j;
+      uq0[u] = rq0[b] + rg * j;
+      unr[u] = nr;
+      upf[u] = pf;
+      ub[u] = b;
+      const int64_t n = min<int64_t>((int64_t)pf + nr, ld);
+      nb = n > 0 ? (int)((n + kKeysPerStep - 1) / kKeysPerStep) : 0;
+    }
+    const int e = flat_excl_scan(nb, wsum, carry, lane, wave);
+    if (u < n_units) pre[u] = e;
+  }
+  if (tid == 0) pre[n_units] = carry;
   __syncthreads();
   const int per = (carry + (int)gridDim.x - 1) / (int)gridDim.x;
   const int start = (int)blockIdx.x * per, end = min(carry, start + per);
 
   if (start >= end) return;
 
-  // 2. The requests the share touches are staged in LDS all at once when they
-  //    fit (slot = request - first staged request); otherwise the share is
-  //    walked one request at a time through slot 0.
-  const int b_first = last_at_or_below(pre, B, start), b_last = last_at_or_below(pre, B, end - 1);
-  const bool all_staged = b_last - b_first + 1 <= nslots;
-  int lo = start, b0 = b_first;
+  // 3. The units the share touches are staged in LDS all at once when they
+  //    fit (slot = unit - first staged unit); otherwise the share is walked
+  //    one unit at a time through slot 0.
+  const int u_first = last_at_or_below(pre, n_units, start), u_last = last_at_or_below(pre, n_units, end - 1);
+  const bool all_staged = u_last - u_first + 1 <= nslots;
+  int lo = start, u0 = u_first;
   while (lo < end) {
-    const int hi = all_staged ? end : min(end, pre[b0 + 1]);
-    const int b_hi = all_staged ? b_last : b0;
-    for (int bb = b0; bb <= b_hi; ++bb) {  // query rows and weights -> LDS slot bb - b0
-      const int q0 = rq0[bb], nr = min(rql[bb], max_rows);
-      uint8_t* qd = q_area + (size_t)(bb - b0) * max_rows * kRowBytesLds;
+    const int hi = all_staged ? end : min(end, pre[u0 + 1]);
+    const int u_hi = all_staged ? u_last : u0;
+    for (int uu = u0; uu <= u_hi; ++uu) {  // query rows and weights -> LDS slot uu - u0
+      const int q0 = uq0[uu], nr = unr[uu];
+      uint8_t* qd = q_area + (size_t)(uu - u0) * rg * kRowBytesLds;
       const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(q_idx + (int64_t)q0 * kHeads * kDim);
       const int n_slots = nr * kRowSlots;  // padded per head; the pad slot repeats chunk 15
       for (int base = 0; base < n_slots; base += kFlatThreads) {
@@ -330,7 +361,7 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
         if (slot < n_slots)
           copy16_to_lds(qsrc + ((r * kHeads + h) * kDim + ch * 8) * 2, qd + (base + wave * kWave) * 16);
       }
-      uint8_t* wd = reinterpret_cast<uint8_t*>(w_area + (size_t)(bb - b0) * max_rows * kHeads);
+      uint8_t* wd = reinterpret_cast<uint8_t*>(w_area + (size_t)(uu - u0) * rg * kHeads);
       const uint8_t* wsrc = reinterpret_cast<const uint8_t*>(w + (int64_t)q0 * kHeads);
       for (int base = 0; base < nr * (kHeads / 4); base += kFlatThreads)
         if (base + tid < nr * (kHeads / 4)) copy16_to_lds(wsrc + (base + tid) * 16, wd + (base + wave * kWave) * 16);
@@ -339,11 +370,11 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
     // This wave's blocks lo + wave + 8 i < hi.  A, B, C: the block being scored
     // and the next two (keys of B in flight, page lookups of C in flight).
     int j = lo + wave;
-    FlatBlock A{b0, 0, {-1, -1}}, Bk{b0, 0, {-1, -1}}, C{b0, 0, {-1, -1}};
-    if (j < hi) prep_block(A, j, b0, pre, rql, rsl, max_rows, ld_last, page_table, pt_stride, page_size,
+    FlatBlock A{u0, 0, {-1, -1}}, Bk{u0, 0, {-1, -1}}, C{u0, 0, {-1, -1}};
+    if (j < hi) prep_block(A, j, u0, pre, unr, upf, ub, ld_last, page_table, pt_stride, page_size,
                            num_pages, k_page_stride, k_row_stride, lane);
     if (j + kFlatWaves < hi)
-      prep_block(Bk, j + kFlatWaves, A.b, pre, rql, rsl, max_rows, ld_last, page_table, pt_stride,
+      prep_block(Bk, j + kFlatWaves, A.u, pre, unr, upf, ub, ld_last, page_table, pt_stride,
                  page_size, num_pages, k_page_stride, k_row_stride, lane);
     Keys k0, k1;
     load_keys(k0, A.off, k_base, lane);
@@ -351,15 +382,15 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
     lds_barrier();
 
 #define DSA_SCORE(KK, X)                                                                           \
-  score_block(KK, X.off, q_area + (size_t)(X.b - b0) * max_rows * kRowBytesLds,                    \
-              w_area + (size_t)(X.b - b0) * max_rows * kHeads, min(rql[X.b], max_rows), X.tok,      \
-              rsl[X.b] - rql[X.b], ld_last, scores, rq0[X.b], ld, lane)
+  score_block(KK, X.off, q_area + (size_t)(X.u - u0) * rg * kRowBytesLds,                          \
+              w_area + (size_t)(X.u - u0) * rg * kHeads, unr[X.u], X.tok, upf[X.u], ld_last, scores, \
+              uq0[X.u], ld, lane)
     while (j < hi) {
       // block j with k0, block j + 8 with k1
       const bool has1 = j + kFlatWaves < hi;
       if (has1) load_keys(k1, Bk.off, k_base, lane);
       if (j + 2 * kFlatWaves < hi)
-        prep_block(C, j + 2 * kFlatWaves, Bk.b, pre, rql, rsl, max_rows, ld_last, page_table, pt_stride,
+        prep_block(C, j + 2 * kFlatWaves, Bk.u, pre, unr, upf, ub, ld_last, page_table, pt_stride,
                    page_size, num_pages, k_page_stride, k_row_stride, lane);
       DSA_SCORE(k0, A);
       if (!has1) break;
@@ -369,7 +400,7 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
       const bool has1b = j + kFlatWaves < hi;
       if (has1b) load_keys(k0, Bk.off, k_base, lane);
       if (j + 2 * kFlatWaves < hi)
-        prep_block(C, j + 2 * kFlatWaves, Bk.b, pre, rql, rsl, max_rows, ld_last, page_table, pt_stride,
+        prep_block(C, j + 2 * kFlatWaves, Bk.u, pre, unr, upf, ub, ld_last, page_table, pt_stride,
                    page_size, num_pages, k_page_stride, k_row_stride, lane);
       DSA_SCORE(k1, A);
       if (!has1b) break;
@@ -380,7 +411,7 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
 #undef DSA_SCORE
     lds_barrier();  // every wave is done with the staged rows
     lo = hi;
-    if (lo < end) b0 = last_at_or_below(pre, B, lo);
+    if (lo < end) u0 = last_at_or_below(pre, n_units, lo);
   }
 }
 
@@ -423,13 +454,17 @@ __global__ __launch_bounds__(256) void index_scores_f32_valu(
 hipError_t launch_index_scores_bf16(const BatchArgs& ba, const void* q_idx, const float* w,
                                     const PoolArgs& pool, float* scores, int64_t ld,
                                     hipStream_t stream) {
-  if (ba.max_q_len >= 1 && ba.max_q_len <= 8) {
-    // Up to 8 requests staged at once, as many as fit next to the tables.
-    const size_t tables = ((size_t)(4 * ba.batch + 1 + kFlatWaves) * sizeof(int) + 15) / 16 * 16;
-    const size_t per_req = (size_t)ba.max_q_len * (kRowBytesLds + kHeads * sizeof(float));
+  if (ba.max_q_len >= 1) {
+    // Units of up to rg rows (the whole draft for decode-sized q_len, four
+    // rows for long prefill chunks); up to 8 units staged at once, as many as
+    // fit next to the tables.
+    const int rg = ba.max_q_len <= 8 ? ba.max_q_len : 4;
+    const int64_t u_max = (int64_t)ba.batch * ((ba.max_q_len + rg - 1) / rg);
+    const size_t tables = ((size_t)(4 * (int64_t)ba.batch + 1 + 5 * u_max + 1 + kFlatWaves) * sizeof(int) + 15) / 16 * 16;
+    const size_t per_unit = (size_t)rg * (kRowBytesLds + kHeads * sizeof(float));
     const size_t avail = tables < 160 * 1024 ? 160 * 1024 - tables : 0;
-    const int nslots = (int)std::min<size_t>(8, avail / per_req);
-    const size_t lds = tables + (size_t)nslots * per_req;
+    const int nslots = (int)std::min<size_t>(8, avail / per_unit);
+    const size_t lds = tables + (size_t)nslots * per_unit;
     if (nslots >= 1) {
       hipError_t e = ensure_max_lds(reinterpret_cast<const void*>(index_scores_flat));
       if (e != hipSuccess) return e;
@@ -437,7 +472,7 @@ hipError_t launch_index_scores_bf16(const BatchArgs& ba, const void* q_idx, cons
                          ba.cu_q, ba.seq_lens, ba.batch, ba.page_table, ba.pt_stride, ba.page_size,
                          ba.num_pages, static_cast<const uint16_t*>(q_idx), w,
                          static_cast<const uint8_t*>(pool.base), pool.page_stride, pool.row_stride,
-                         scores, ld, ba.max_q_len, nslots);
+                         scores, ld, rg, nslots, (int)u_max);
       return hipGetLastError();
     }
   }
