@@ -179,12 +179,14 @@ def make_batch(cfg_id: int, mode: str = "parity", device="cpu", layers: int | No
                seed_offset: int = 0, batch: int | None = None, q_len: int | None = None,
                ctx: tuple | None = None, topk: int | None = None,
                page_size: int | None = None, identity_pages: bool | None = None,
-               heads: int | None = None, kv_fmt: int | None = None) -> Batch:
+               heads: int | None = None, kv_fmt: int | None = None,
+               q_lens: list | None = None) -> Batch:
     """Draw one batch of config `cfg_id`.
 
     The keyword overrides (batch, q_len, ctx range, top-k, page size) give
     reduced-size variants of the same recipe for tests; the defaults are the
-    full workload.  seed_offset picks an independent input set of the same
+    full workload.  q_lens gives each request its own number of query rows
+    (zero allowed; its length sets the batch size).  seed_offset picks an independent input set of the same
     shape (the bench rotates several to keep the 256 MB MALL from serving
     repeat reads).
     """
@@ -208,6 +210,9 @@ def make_batch(cfg_id: int, mode: str = "parity", device="cpu", layers: int | No
         cfg.heads = heads
     if kv_fmt is not None:
         cfg.kv_fmt = kv_fmt
+    if q_lens is not None:
+        cfg.batch = len(q_lens)
+        cfg.q_len = max(q_lens)
     assert mode in ("parity", "perf")
     device = torch.device(device)
     g = _gen(device, cfg.seed + 7919 * seed_offset)
@@ -219,8 +224,8 @@ def make_batch(cfg_id: int, mode: str = "parity", device="cpu", layers: int | No
         seq_lens = [cfg.ctx_lo] * B
     else:
         seq_lens = torch.randint(cfg.ctx_lo, cfg.ctx_hi + 1, (B,), generator=gcpu).tolist()
-    seq_lens = [max(int(s), cfg.q_len) for s in seq_lens]
-    q_lens = [cfg.q_len] * B
+    q_lens = [int(x) for x in q_lens] if q_lens is not None else [cfg.q_len] * B
+    seq_lens = [max(int(s), ql, 1) for s, ql in zip(seq_lens, q_lens)]
     pages_per = [(s + P - 1) // P for s in seq_lens]
     num_pages = sum(pages_per)
     pt_stride = max(pages_per)

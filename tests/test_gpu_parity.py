@@ -63,6 +63,9 @@ REDUCED = {
     "decode_h64_fp8": dict(cfg=2, batch=3, ctx=(900, 3000), topk=512, heads=64, layers=1,
                            kv_fmt=synth.FMT_FP8_E4M3_B128),
     "decode_h16_split_ragged": dict(cfg=1, batch=7, ctx=(1, 700), topk=640),
+    # requests with no rows and mixed draft lengths; more than 256 requests
+    "ragged_q_lens_empty": dict(cfg=4, q_lens=[5, 0, 3, 1, 0, 5, 2], ctx=(600, 3000), topk=512),
+    "many_requests": dict(cfg=1, batch=300, ctx=(40, 700), topk=256),
 }
 
 
