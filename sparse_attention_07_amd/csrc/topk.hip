@@ -6,7 +6,8 @@
 // "Body": below index_topk the pick is all tokens).  One workgroup of 1024
 // threads per query row; the selection itself (order, ties, passes,
 // compaction) is in topk_select.h.  Rows of up to 32768 entries are cached in
-// LDS as keys after one read; longer rows are re-read in each pass.
+// LDS as keys after one read; longer rows are re-read in each pass (the two
+// cases are separate instantiations).
 #include "dsa_device.h"
 #include "dsa_launch.h"
 #include "topk_select.h"
@@ -18,12 +19,22 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kCache = 32768;
 
+template <bool Cached>
+__device__ inline void select_row(const float* __restrict__ row, int n, int K, int32_t* __restrict__ out,
+                                  uint32_t* cache, uint32_t* hist, uint32_t* wcount, uint32_t* pick) {
+  const bool vec = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
+  const topk::Threshold th = topk::select<kThreads, Cached>(row, vec, n, K, cache, hist, pick);
+  topk::compact<kThreads, Cached>(row, vec, n, cache, th, wcount, [out, K](uint32_t o, int s) {
+    if (o < (uint32_t)K) out[o] = s;
+  });
+}
+
 __global__ __launch_bounds__(kThreads) void topk_radix(const int32_t* __restrict__ cu_q,
                                                        const int32_t* __restrict__ seq_lens, int B,
                                                        const float* __restrict__ scores, int64_t ld,
                                                        int K, int32_t* __restrict__ idx) {
-  __shared__ uint32_t cache[kCache];
-  __shared__ uint32_t hist[2 * topk::kHistWords];
+  __shared__ __align__(16) uint32_t cache[kCache];
+  __shared__ __align__(16) uint32_t hist[2 * topk::kHistWords];
   __shared__ uint32_t wcount[2 * kThreads / kWave];
   __shared__ uint32_t pick[3];
 
@@ -38,12 +49,8 @@ __global__ __launch_bounds__(kThreads) void topk_radix(const int32_t* __restrict
     return;
   }
   const float* row = scores + (int64_t)t * ld;
-  const bool cached = n <= kCache;
-  auto load = [row](int s) { return row[s]; };
-  const topk::Threshold th = topk::select<kThreads>(load, n, K, cached, cache, hist, pick);
-  topk::compact<kThreads>(load, n, cached, cache, th, wcount, [out, K](uint32_t o, int s) {
-    if (o < (uint32_t)K) out[o] = s;
-  });
+  if (n <= kCache) select_row<true>(row, n, K, out, cache, hist, wcount, pick);
+  else select_row<false>(row, n, K, out, cache, hist, wcount, pick);
 }
 
 }  // namespace

@@ -1,21 +1,23 @@
-// Radix selection of a row's k best scores on gfx950: shared by the top-k
-// kernel and by the 16-head sparse-MLA kernel that selects its own rows.
+// Radix selection of a row's k best scores on gfx950, for the top-k kernel.
 //
 // Order: higher score first, equal scores to the lower position, -0.0 equal
 // to +0.0.  Scores map to 32-bit keys whose unsigned order is the score
 // order.  Up to three histogram passes over 11, 11 and 10 key bits (LDS
 // histograms, LDS atomics) narrow down the key prefix of the k-th best
 // element; the first pass runs while the row is read (and cached in LDS as
-// keys when the caller has room), and the passes stop as soon as the chosen
-// bin is taken whole.  After each pass a single wave scans the histogram
-// (bins padded so that its lanes' ranges fall in distinct banks) to find the
-// bin holding the k-th element.  The selection is then "key prefix above the
+// keys when it fits), and the passes stop as soon as the chosen bin is taken
+// whole.  After each pass a single wave scans the histogram to find the bin
+// holding the k-th element.  The selection is then "key prefix above the
 // chosen one, or equal to it and among the first `need` such positions".
 // Compaction: each wave owns a contiguous range of the row, counts its
-// selected elements with ballots, one workgroup-wide prefix over the wave
-// counts places the ranges, and a second walk hands every selected position
-// with its rank in ascending position order to the caller -- the ascending
-// output and the position tie-break come without sorting.
+// selected elements, one workgroup-wide prefix over the wave counts places
+// the ranges, and a second walk hands every selected position with its rank
+// in ascending position order to the caller -- the ascending output and the
+// position tie-break come without sorting.
+//
+// The row is read in quads (four consecutive positions): 16-byte loads when
+// the row is 16-byte aligned, and 16-byte LDS accesses for the key cache, so
+// that one round of loads per thread covers a whole cached row.
 #pragma once
 
 #include "dsa_device.h"
@@ -24,7 +26,7 @@ namespace dsa {
 namespace topk {
 
 constexpr int kBins = 2048;
-constexpr int kHistWords = kBins + kBins / 32;  // one pad word per 32 bins
+constexpr int kHistWords = kBins + kBins / 32 * 4;  // four pad words per 32 bins
 
 __device__ inline uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -32,82 +34,115 @@ __device__ inline uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);     // unsigned order == float order
 }
 
-// Padded histogram slot of a bin: the 32 bins a lane of the picking wave owns
-// then start on distinct banks.
-__device__ inline int hslot(uint32_t bin) { return (int)(bin + (bin >> 5)); }
+// Padded histogram slot of a bin.  A run of 16 or 32 bins starting at a
+// multiple of its length is contiguous and 16-byte aligned, and the 32-bin
+// runs of consecutive lanes start 36 words apart (distinct banks for 16-byte
+// reads).
+__device__ inline int hslot(uint32_t bin) { return (int)(bin + (bin >> 5) * 4); }
 
-// Wave 0: in a histogram of nb bins (a larger bin holds larger keys) find the
+// Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts inside
+// each row of 16 lanes, then row broadcasts of lanes 15 and 31).
+__device__ inline uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
+__device__ inline uint32_t wave_sum(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(x), kWave - 1);
+}
+
+// Wave 0: in a histogram of NB bins (a larger bin holds larger keys) find the
 // bin containing the need-th largest element; writes (bin, need left inside
-// the bin, bin count) to pick[0..2].  Lane l owns bins nb-1-per*l down to
-// nb-per*(l+1).  The histogram's total must be >= need.
-__device__ inline void pick_bin(const uint32_t* hist, int nb, uint32_t need, uint32_t* pick) {
+// the bin, bin count) to pick[0..2].  Lane l owns the PER bins
+// NB-PER*(l+1) .. NB-1-PER*l.  The histogram's total must be >= need.
+template <int NB>
+__device__ inline void pick_bin(const uint32_t* hist, uint32_t need, uint32_t* pick) {
+  constexpr int kPer = NB / kWave;  // 32 or 16
   const int lane = threadIdx.x & (kWave - 1);
-  const int per = nb / kWave;  // 32 or 16
-  const int top = nb - 1 - per * lane;
+  const int lo = NB - kPer * (lane + 1);
+  const u32x4* p = reinterpret_cast<const u32x4*>(hist + hslot((uint32_t)lo));
   uint32_t sum = 0;
-#pragma unroll 8
-  for (int j = 0; j < per; ++j) sum += hist[hslot((uint32_t)(top - j))];
-  uint32_t inc = sum;
 #pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const uint32_t y = __shfl_up(inc, d);
-    if (lane >= d) inc += y;
+  for (int j = 0; j < kPer / 4; ++j) {
+    const u32x4 v = p[j];
+    sum += v[0] + v[1] + v[2] + v[3];
   }
+  const uint32_t inc = wave_incl_scan(sum);
   // The one lane whose range holds the need-th element hands it to the wave,
-  // which scans those bins one per lane.
+  // which scans those bins (from the top) one per lane.
   const uint64_t owner = __ballot(inc - sum < need && need <= inc);
-  const int src = __ffsll((unsigned long long)owner) - 1;
-  const int top_s = __shfl(top, src);
-  const uint32_t acc = __shfl(inc - sum, src);
-  const uint32_t c = lane < per ? hist[hslot((uint32_t)(top_s - lane))] : 0u;
-  uint32_t ci = c;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const uint32_t y = __shfl_up(ci, d);
-    if (lane >= d) ci += y;
-  }
-  const uint32_t before = acc + ci - c;
-  if (lane < per && before < need && need <= before + c) {
+  const int src = __builtin_ctzll(owner);
+  const int top_s = __builtin_amdgcn_readlane(lo + kPer - 1, src);
+  const uint32_t acc = (uint32_t)__builtin_amdgcn_readlane((int)(inc - sum), src);
+  const uint32_t c = lane < kPer ? hist[hslot((uint32_t)(top_s - lane))] : 0u;
+  const uint32_t before = acc + wave_incl_scan(c) - c;
+  if (lane < kPer && before < need && need <= before + c) {
     pick[0] = (uint32_t)(top_s - lane);
     pick[1] = need - before;
     pick[2] = c;
   }
 }
 
+// Scores of positions 4q .. 4q+3 of a row of n (positions >= n read as 0).
+// vec: the row is 16-byte aligned.
+__device__ inline f32x4 load_quad(const float* __restrict__ row, int q, int n, bool vec) {
+  const int s = 4 * q;
+  if (vec && s + 3 < n) return *reinterpret_cast<const f32x4*>(row + s);
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (s + j < n) v[j] = row[s + j];
+  return v;
+}
+
+__device__ inline u32x4 quad_keys(f32x4 v) {
+  return u32x4{order_key(v[0]), order_key(v[1]), order_key(v[2]), order_key(v[3])};
+}
+
 struct Threshold {
   uint32_t prefix, mask, need;
 };
 
-// Threshold of the k best of the n > k scores load(0) .. load(n-1), for a
-// workgroup of NT threads.  hist: 2 * kHistWords LDS words; pick: 3 LDS
-// words; cache: n LDS words, used when `cached`.  Begins and ends with a
-// barrier.
-template <int NT, typename Load>
-__device__ inline Threshold select(Load load, int n, int k, bool cached, uint32_t* cache, uint32_t* hist,
-                                   uint32_t* pick) {
+// Threshold of the k best of the n > k scores row[0] .. row[n-1], for a
+// workgroup of NT threads.  hist: 2 * kHistWords LDS words, 16-byte aligned;
+// pick: 3 LDS words; cache (Cached only): round_up(n, 4) LDS words,
+// 16-byte aligned.  Begins and ends with a barrier.
+template <int NT, bool Cached>
+__device__ inline Threshold select(const float* __restrict__ row, bool vec, int n, int k,
+                                   uint32_t* cache, uint32_t* hist, uint32_t* pick) {
+  constexpr int kBatch = 8;  // quads in flight per thread
   const int tid = threadIdx.x, wave = tid / kWave;
+  const int nq = (n + 3) >> 2;
+  u32x4* cache4 = reinterpret_cast<u32x4*>(cache);
   for (int i = tid; i < 2 * kHistWords; i += NT) hist[i] = 0u;
   __syncthreads();
-  // Pass 0 (key bits 21..31) while the row is read; eight loads in flight per thread.
-  for (int s0 = 0; s0 < n; s0 += 8 * NT) {
-    float v[8];
+  // Pass 0 (key bits 21..31) while the row is read.
+  for (int q0 = 0; q0 < nq; q0 += kBatch * NT) {
+    f32x4 v[kBatch];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int s = s0 + i * NT + tid;
-      v[i] = s < n ? load(s) : 0.f;
+    for (int i = 0; i < kBatch; ++i) {
+      const int q = q0 + i * NT + tid;
+      if (q < nq) v[i] = load_quad(row, q, n, vec);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int s = s0 + i * NT + tid;
-      if (s < n) {
-        const uint32_t u = order_key(v[i]);
-        if (cached) cache[s] = u;
-        atomicAdd(&hist[hslot(u >> 21)], 1u);
+    for (int i = 0; i < kBatch; ++i) {
+      const int q = q0 + i * NT + tid;
+      if (q < nq) {
+        const u32x4 u = quad_keys(v[i]);
+        if (Cached) cache4[q] = u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (4 * q + j < n) atomicAdd(&hist[hslot(u[j] >> 21)], 1u);
       }
     }
   }
   __syncthreads();
-  if (wave == 0) pick_bin(hist, kBins, (uint32_t)k, pick);
+  if (wave == 0) pick_bin<kBins>(hist, (uint32_t)k, pick);
   __syncthreads();
   Threshold th{pick[0] << 21, 0xFFE00000u, pick[1]};
   bool done = pick[2] == th.need;  // the whole bin is taken
@@ -115,19 +150,36 @@ __device__ inline Threshold select(Load load, int n, int k, bool cached, uint32_
 #pragma unroll 1
   for (int pass = 1; pass < 3 && !done; ++pass) {
     const int shift = pass == 1 ? 10 : 0;
-    const int nb = pass == 1 ? 2048 : 1024;
+    const uint32_t bmask = pass == 1 ? 2047u : 1023u;
     uint32_t* h = hist + (pass & 1) * kHistWords;
     if (pass == 1)  // pass 0's histogram was read before the last barrier; pass 2 reuses it
       for (int i = tid; i < kHistWords; i += NT) hist[i] = 0u;
-    for (int s = tid; s < n; s += NT) {
-      const uint32_t u = cached ? cache[s] : order_key(load(s));
-      if ((u & th.mask) == th.prefix) atomicAdd(&h[hslot((u >> shift) & (uint32_t)(nb - 1))], 1u);
+    for (int q0 = 0; q0 < nq; q0 += kBatch * NT) {
+      u32x4 u[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int q = q0 + i * NT + tid;
+        if (q < nq) u[i] = Cached ? cache4[q] : quad_keys(load_quad(row, q, n, vec));
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int q = q0 + i * NT + tid;
+        if (q < nq) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (4 * q + j < n && (u[i][j] & th.mask) == th.prefix)
+              atomicAdd(&h[hslot((u[i][j] >> shift) & bmask)], 1u);
+        }
+      }
     }
     __syncthreads();
-    if (wave == 0) pick_bin(h, nb, th.need, pick);
+    if (wave == 0) {
+      if (pass == 1) pick_bin<2048>(h, th.need, pick);
+      else pick_bin<1024>(h, th.need, pick);
+    }
     __syncthreads();
     th.prefix |= pick[0] << shift;
-    th.mask |= (uint32_t)(nb - 1) << shift;
+    th.mask |= bmask << shift;
     th.need = pick[1];
     done = pick[2] == th.need;
   }
@@ -138,21 +190,43 @@ __device__ inline Threshold select(Load load, int n, int k, bool cached, uint32_
 // Calls emit(o, s) for every selected position s, o = its rank (0 .. k-1) in
 // ascending position order.  Selected: (key & mask) > prefix, or == prefix
 // among the first `need` such positions.  wcount: 2 * NT / 64 LDS words.
-template <int NT, typename Load, typename Emit>
-__device__ inline void compact(Load load, int n, bool cached, const uint32_t* cache, Threshold th,
-                               uint32_t* wcount, Emit emit) {
+template <int NT, bool Cached, typename Emit>
+__device__ inline void compact(const float* __restrict__ row, bool vec, int n, const uint32_t* cache,
+                               Threshold th, uint32_t* wcount, Emit emit) {
   constexpr int kW = NT / kWave;
+  constexpr int kChunk = 4 * kWave;          // positions per wave step: a quad per lane
+  constexpr int kBatch = Cached ? 4 : 8;     // steps in flight
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int R = ((n + kW - 1) / kW + kWave - 1) / kWave * kWave;  // wave w owns [w R, (w+1) R)
+  // wave w owns [w R, (w+1) R), R a multiple of kChunk
+  const int R = ((n + kW - 1) / kW + kChunk - 1) / kChunk * kChunk;
   const int r0 = wave * R, r1 = min(n, r0 + R);
-  const uint64_t below = (1ull << lane) - 1ull;
+  const u32x4* cache4 = reinterpret_cast<const u32x4*>(cache);
+  // Masked keys of the quads at c + b*kChunk + 4*lane, b < kBatch (steps past r1 left unread).
+  auto keys = [&](int c, u32x4 (&u)[kBatch]) {
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int q = (c + b * kChunk) / 4 + lane;
+      u[b] = u32x4{0u, 0u, 0u, 0u};
+      if (c + b * kChunk < r1) u[b] = Cached ? cache4[q] : quad_keys(load_quad(row, q, r1, vec));
+    }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) u[b] &= th.mask;
+  };
   uint32_t cg = 0, ce = 0;
-  for (int c = r0; c < r1; c += kWave) {
-    const int s = c + lane;
-    const uint32_t u = s < r1 ? ((cached ? cache[s] : order_key(load(s))) & th.mask) : 0u;
-    cg += (uint32_t)__popcll(__ballot(s < r1 && u > th.prefix));
-    ce += (uint32_t)__popcll(__ballot(s < r1 && u == th.prefix));
+  for (int c = r0; c < r1; c += kBatch * kChunk) {
+    u32x4 u[kBatch];
+    keys(c, u);
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool in = c + b * kChunk + 4 * lane + j < r1;
+        cg += (in && u[b][j] > th.prefix) ? 1u : 0u;
+        ce += (in && u[b][j] == th.prefix) ? 1u : 0u;
+      }
   }
+  cg = wave_sum(cg);
+  ce = wave_sum(ce);
   if (lane == 0) {
     wcount[wave] = cg;
     wcount[kW + wave] = ce;
@@ -163,16 +237,39 @@ __device__ inline void compact(Load load, int n, bool cached, const uint32_t* ca
     run_gt += wcount[w];
     run_eq += wcount[kW + w];
   }
-  for (int c = r0; c < r1; c += kWave) {
-    const int s = c + lane;
-    const uint32_t u = s < r1 ? ((cached ? cache[s] : order_key(load(s))) & th.mask) : 0u;
-    const bool gt = s < r1 && u > th.prefix, eq = s < r1 && u == th.prefix;
-    const uint64_t mg = __ballot(gt), me = __ballot(eq);
-    const uint32_t eq_rank = run_eq + (uint32_t)__popcll(me & below);
-    if (gt || (eq && eq_rank < th.need))
-      emit(run_gt + (uint32_t)__popcll(mg & below) + min(eq_rank, th.need), s);
-    run_gt += (uint32_t)__popcll(mg);
-    run_eq += (uint32_t)__popcll(me);
+  for (int c = r0; c < r1; c += kBatch * kChunk) {
+    u32x4 u[kBatch];
+    keys(c, u);
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      if (c + b * kChunk >= r1) break;  // wave-uniform
+      const int s0 = c + b * kChunk + 4 * lane;
+      uint32_t ng = 0, ne = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool in = s0 + j < r1;
+        ng += (in && u[b][j] > th.prefix) ? 1u : 0u;
+        ne += (in && u[b][j] == th.prefix) ? 1u : 0u;
+      }
+      // counts of the lanes below (per chunk at most 256 each: packed in 16 bits)
+      const uint32_t packed = ng | (ne << 16);
+      const uint32_t inc = wave_incl_scan(packed);
+      const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)inc, kWave - 1);
+      uint32_t gtb = run_gt + ((inc - packed) & 0xFFFFu), eqb = run_eq + ((inc - packed) >> 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (s0 + j >= r1) continue;
+        if (u[b][j] > th.prefix) {
+          emit(gtb + min(eqb, th.need), s0 + j);
+          ++gtb;
+        } else if (u[b][j] == th.prefix) {
+          if (eqb < th.need) emit(gtb + eqb, s0 + j);
+          ++eqb;
+        }
+      }
+      run_gt += tot & 0xFFFFu;
+      run_eq += tot >> 16;
+    }
   }
   __syncthreads();  // wcount may be rewritten by the next compaction
 }
