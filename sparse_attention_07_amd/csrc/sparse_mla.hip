@@ -67,8 +67,6 @@ constexpr int kThreads = 256;                          // four waves
 constexpr int kTileRows = 32;
 constexpr int kRowLds = 73 * 16;                       // 1152 B of row + one 16-byte pad
 constexpr int kTileLds = kTileRows * kRowLds;          // 37376 B
-constexpr int kBf16Items = kTileRows * 72 / kThreads;  // 9 16-byte chunks per thread
-constexpr int kFp8Items = kTileRows * 40 / kThreads;   // 5: 32 latent + 8 rope chunks per row
 constexpr int kSbufLds = kThreads * 16;                // one f32x4 of partial scores per thread
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kRescaleSlack = 8.f;                   // log2 units
@@ -113,28 +111,38 @@ __device__ inline uint2 fp8x4_to_bf16x4(uint32_t x, float sc) {
   return r;
 }
 
-// One tile's rows in flight in registers: bf16 rows as 9 chunks per thread
-// (item = it*256 + tid -> row item/72, chunk item%72); fp8 rows as 5 items
-// per thread (item -> row item/40, chunk item%40: 32 latent chunks of 16 e4m3
-// bytes, each with its block scale, then 8 rope chunks of bf16).
+// One tile's rows in flight in registers, for a workgroup of NT threads:
+// bf16 rows as 72 16-byte chunks per row (item = it*NT + tid -> row item/72,
+// chunk item%72); fp8 rows as 40 items per row (item -> row item/40, chunk
+// item%40: 32 latent chunks of 16 e4m3 bytes, each with its block scale, then
+// 8 rope chunks of bf16).
 template <bool FP8>
+constexpr int kPerRowItems = FP8 ? 40 : 72;
+template <bool FP8, int NT>
+constexpr int kStageItems = (kTileRows * kPerRowItems<FP8> + NT - 1) / NT;
+
+template <bool FP8, int NT = kThreads>
 struct Stage {
-  u32x4 v[FP8 ? kFp8Items : kBf16Items];
-  float sc[FP8 ? kFp8Items : 1];
+  u32x4 v[kStageItems<FP8, NT>];
+  float sc[FP8 ? kStageItems<FP8, NT> : 1];
 };
 
 __device__ inline u32x4 ld_global16(const uint8_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
-template <bool FP8>
-__device__ inline void stage_load(Stage<FP8>& st, const int64_t* toffs, const uint8_t* kv, int tid) {
-  constexpr int kItems = FP8 ? kFp8Items : kBf16Items;
-  constexpr int kPerRow = FP8 ? 40 : 72;
+template <bool FP8, int NT = kThreads>
+__device__ inline void stage_load(Stage<FP8, NT>& st, const int64_t* toffs, const uint8_t* kv, int tid) {
+  constexpr int kItems = kStageItems<FP8, NT>;
+  constexpr int kPerRow = kPerRowItems<FP8>;
+  constexpr int kTotal = kTileRows * kPerRow;
   int64_t off[kItems];
 #pragma unroll
-  for (int it = 0; it < kItems; ++it) off[it] = toffs[(it * kThreads + tid) / kPerRow];
+  for (int it = 0; it < kItems; ++it) {
+    const int item = it * NT + tid;
+    off[it] = (kTotal % NT == 0 || item < kTotal) ? toffs[item / kPerRow] : -1;
+  }
 #pragma unroll
   for (int it = 0; it < kItems; ++it) {
-    const int item = it * kThreads + tid;
+    const int item = it * NT + tid;
     const int ch = item % kPerRow;
     st.v[it] = u32x4{};
     if (off[it] >= 0) {
@@ -152,13 +160,15 @@ __device__ inline void stage_load(Stage<FP8>& st, const int64_t* toffs, const ui
   }
 }
 
-template <bool FP8>
-__device__ inline void stage_store(const Stage<FP8>& st, uint8_t* tile, int tid) {
-  constexpr int kItems = FP8 ? kFp8Items : kBf16Items;
-  constexpr int kPerRow = FP8 ? 40 : 72;
+template <bool FP8, int NT = kThreads>
+__device__ inline void stage_store(const Stage<FP8, NT>& st, uint8_t* tile, int tid) {
+  constexpr int kItems = kStageItems<FP8, NT>;
+  constexpr int kPerRow = kPerRowItems<FP8>;
+  constexpr int kTotal = kTileRows * kPerRow;
 #pragma unroll
   for (int it = 0; it < kItems; ++it) {
-    const int item = it * kThreads + tid;
+    const int item = it * NT + tid;
+    if (kTotal % NT != 0 && item >= kTotal) break;
     const int r = item / kPerRow, ch = item % kPerRow;
     uint8_t* dst = tile + r * kRowLds;
     if (!FP8) {
@@ -182,26 +192,28 @@ __device__ inline void stage_store(const Stage<FP8>& st, uint8_t* tile, int tid)
 
 // Prologue: byte offsets of the range's rows (page table applied; -1 when not
 // usable), padded with -1 to whole tiles, and a usable-row bitmask per tile.
-// Each thread handles rows tid, tid+256, ...; the index loads of a batch of
+// Each thread handles rows tid, tid+NT, ...; the index loads of a batch of
 // eight rows are all issued before the dependent page-table loads, so the
 // prologue costs two memory latencies per 2048 rows rather than two per row.
 // Returns the first usable slot, or INT32_MAX when the range has none.  Ends
 // with a barrier.
 constexpr int kIdxBatch = 8;
 
-// The first batch of a range's indices (thread tid: entries tid + 256 k).
+// The first batch of a range's indices (thread tid: entries tid + NT k).
 // They depend only on the row, so they are loaded before the row's request
 // and position are known.
+template <int NT = kThreads>
 __device__ inline void preload_indices(int (&sv)[kIdxBatch], const int32_t* idx_row, int j_begin,
                                        int j_end, int n_pad, int tid) {
 #pragma unroll
   for (int k = 0; k < kIdxBatch; ++k) {
-    const int i = k * kThreads + tid;
+    const int i = k * NT + tid;
     const int j = j_begin + i;
     sv[k] = (i < n_pad && j < j_end) ? idx_row[j] : -1;
   }
 }
 
+template <int NT = kThreads>
 __device__ inline int build_offsets(int64_t* offs, uint32_t* vmask, int* first_valid,
                                     const int (&sv0)[kIdxBatch], const int32_t* idx_row,
                                     int j_begin, int j_end, int n_pad, int pos, int b,
@@ -209,13 +221,13 @@ __device__ inline int build_offsets(int64_t* offs, uint32_t* vmask, int* first_v
                                     int num_pages, int64_t page_stride, int64_t row_stride, int tid) {
   constexpr int kBatch = kIdxBatch;
   if (tid == 0) *first_valid = INT32_MAX;
-  for (int i = tid; i < n_pad / kTileRows; i += kThreads) vmask[i] = 0u;
+  for (int i = tid; i < n_pad / kTileRows; i += NT) vmask[i] = 0u;
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  for (int base = 0; base < n_pad; base += kBatch * kThreads) {
+  for (int base = 0; base < n_pad; base += kBatch * NT) {
     int sv[kBatch], pg[kBatch];
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
-      const int i = base + k * kThreads + tid;
+      const int i = base + k * NT + tid;
       const int j = j_begin + i;
       sv[k] = base == 0 ? sv0[k] : ((i < n_pad && j < j_end) ? idx_row[j] : -1);
     }
@@ -227,7 +239,7 @@ __device__ inline int build_offsets(int64_t* offs, uint32_t* vmask, int* first_v
     }
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
-      const int i = base + k * kThreads + tid;
+      const int i = base + k * NT + tid;
       if (i >= n_pad) continue;
       int64_t off = -1;
       if (pg[k] >= 0 && pg[k] < num_pages)
@@ -261,19 +273,76 @@ struct MlaArgs {
   int splits, rows_per_split;
 };
 
-// Online-softmax bookkeeping shared by both kernels.  `mt` is this lane's
-// tile max for its head (already reduced over the lanes holding that head).
-// Returns true when the wave must rescale O by `alpha`.
-__device__ inline bool softmax_step(float mt, float& m_run, float& alpha) {
+// Reductions over the four lane groups (lanes l, l^16, l^32, l^48) that hold
+// one head's scores: a permlane swap exchanges row pairs of a wave in one
+// VALU instruction, and each lane ends up with its own and its partner's
+// value in a fixed order (same result in both lanes of a pair).
+__device__ inline float max_over_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ inline float sum_over_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// 2^x on the hardware exponential (v_exp_f32); results below the normal
+// range flush to zero, which no softmax weight here can notice.
+__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Online softmax of one 32-row tile for 16 heads, in log2 units.  s0 / s1:
+// S^T accumulators (lane (g, c16): rows 4g+r and 16+4g+r, head c16);
+// valid: usable-row bits of the tile.  The running max is raised (and O and
+// l rescaled) only when the tile beats it by more than kRescaleSlack.
+// Returns P as the PV A operand (k slot (g, e) <-> row 4g + e, (g, 4 + e) <->
+// row 16 + 4g + e).  O accumulator r of lane (g, c16) holds head 4g + r.
+template <int TILES>
+__device__ inline bf16x8 tile_softmax(const f32x4& s0, const f32x4& s1, uint32_t valid, float scale_log2,
+                                      float& m_run, float& l_run, f32x4 (&o)[TILES]) {
+  const int lane = threadIdx.x & (kWave - 1), g = lane >> 4;
+  float xv[8];
+  if (valid == 0xFFFFFFFFu) {  // wave-uniform: every row usable
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      xv[r] = s0[r] * scale_log2;
+      xv[4 + r] = s1[r] * scale_log2;
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      xv[r] = (valid >> (4 * g + r)) & 1u ? s0[r] * scale_log2 : kNegInf;
+      xv[4 + r] = (valid >> (16 + 4 * g + r)) & 1u ? s1[r] * scale_log2 : kNegInf;
+    }
+  }
+  float mt = fmaxf(fmaxf(fmaxf(xv[0], xv[1]), fmaxf(xv[2], xv[3])),
+                   fmaxf(fmaxf(xv[4], xv[5]), fmaxf(xv[6], xv[7])));
+  mt = max_over_groups(mt);
   const bool raise = mt > m_run + kRescaleSlack;
-  alpha = 1.f;
   if (__any(raise)) {
     const float m_new = raise ? mt : m_run;
-    alpha = (m_run == kNegInf) ? 0.f : exp2f(m_run - m_new);
+    const float alpha = (m_run == kNegInf) ? 0.f : exp2_fast(m_run - m_new);
     m_run = m_new;
-    return true;
+    l_run *= alpha;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float ar = __shfl(alpha, 4 * g + r);  // O row r holds head 4g + r
+#pragma unroll
+      for (int i2 = 0; i2 < TILES; ++i2) o[i2][r] *= ar;
+    }
   }
-  return false;
+  bf16x8 pa;
+#pragma unroll
+  for (int i2 = 0; i2 < 8; ++i2) {
+    const float p = xv[i2] == kNegInf ? 0.f : exp2_fast(xv[i2] - m_run);
+    l_run += p;
+    pa[i2] = (__bf16)p;
+  }
+  return pa;
 }
 
 // Split partials are exchanged between workgroups with device-scope (sc1)
@@ -307,10 +376,11 @@ __device__ inline __amdgpu_buffer_rsrc_t split_blocks(const MlaArgs& a, int t, i
 }
 
 // A split's partials: O / l of this lane's four heads (4g..4g+3) at its
-// columns as bf16, and when stat_h0 >= 0 (one wave per 16 heads) the (m, l)
-// of heads stat_h0 + lane for lanes < 16.  l_run is already the full sum.
+// columns as bf16 (layout tiles slot0 .. slot0+TILES-1), and when
+// stat_h0 >= 0 (one wave per 16 heads) the (m, l) of heads stat_h0 + lane for
+// lanes < 16.  l_run is already the full sum.
 template <int NH, int TILES>
-__device__ inline void store_partials(const MlaArgs& a, int t, int grp, int n_groups, int sp, int wave,
+__device__ inline void store_partials(const MlaArgs& a, int t, int grp, int n_groups, int sp, int slot0,
                                       int lane, const f32x4 (&o)[TILES], float m_run, float l_run,
                                       int stat_h0) {
   const __amdgpu_buffer_rsrc_t rs = split_blocks(a, t, grp, n_groups, NH);
@@ -328,7 +398,7 @@ __device__ inline void store_partials(const MlaArgs& a, int t, int grp, int n_gr
     pk.x = pack_bf16x2(o[i2][0] * inv[0], o[i2][1] * inv[1]);
     pk.y = pack_bf16x2(o[i2][2] * inv[2], o[i2][3] * inv[3]);
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((__vector_size__(2 * sizeof(int)))) int, pk), rs,
-                                          base + ((wave * TILES + i2) * 64 + lane) * 8, 0, kSc1);
+                                          base + ((slot0 + i2) * 64 + lane) * 8, 0, kSc1);
   }
   if (stat_h0 >= 0 && lane < 16) {
     uint2 ml;
@@ -346,9 +416,10 @@ __device__ inline void store_partials(const MlaArgs& a, int t, int grp, int n_gr
 // left as they were found.  WIDE: 64 heads, each wave 16 heads x 512 columns;
 // else 16 heads, each wave 16 heads x 128 columns.  `wgt` is LDS space for
 // 2 * nh * splits floats (the tile buffer, free by now); `is_last` one LDS int.
-template <bool WIDE>
+template <bool WIDE, int NT = kThreads>
 __device__ inline void merge_splits_if_last(const MlaArgs& a, int t, int grp, int n_groups,
                                             int* counter, float* wgt, int* is_last, int tid) {
+  constexpr int kThreads = NT;
   constexpr int kNh = WIDE ? 64 : 16;
   constexpr int kTiles = WIDE ? 32 : 8;  // 16-column tiles per wave
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's partial stores are done
@@ -362,7 +433,8 @@ __device__ inline void merge_splits_if_last(const MlaArgs& a, int t, int grp, in
   const __amdgpu_buffer_rsrc_t rs = split_blocks(a, t, grp, n_groups, kNh);
   constexpr int kStride = kPartBytes(kNh);
   // Issue the first round of O loads before the statistics are reduced.
-  constexpr int kIt = 4, kSp = 8, kChunks = kNh * kDc * 2 / 16;  // 16-byte chunks of O per split
+  // 16-byte chunks of O per split; 1024 of them per load round
+  constexpr int kIt = 1024 / NT, kSp = 8, kChunks = kNh * kDc * 2 / 16;
   u32x4 v[kIt][kSp];
   auto issue = [&](int c0, int s0) {
 #pragma unroll
@@ -455,46 +527,53 @@ __device__ inline void merge_splits_if_last(const MlaArgs& a, int t, int grp, in
   if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// ---------------------------------------------------------------- kernel
+// ---------------------------------------------------------------- 64 heads, 8 waves
 
-// DSPLIT = 4: a workgroup owns 16 heads; each wave computes the 32x16 score
-// tile and a quarter (128) of the output columns.  DSPLIT = 1: a workgroup
-// owns 64 heads, 16 per wave, each wave all 512 columns (1 wave per SIMD:
-// 72 VGPRs of q plus a 128-register accumulator).  With several head groups
-// per query, linear workgroup ids are laid out so that the groups of one query
-// are 8 ids apart: they land on the same XCD at about the same time and the
-// second gather of each tile is served by that XCD's L2.
-template <int DSPLIT, bool FP8, int STAGES>
-__global__ __launch_bounds__(kThreads, DSPLIT == 4 ? 2 : 1) void sparse_mla_tiles(MlaArgs a, int n_groups, int T) {
+// A workgroup owns 64 heads of one query row and one range of its selected
+// rows, with eight waves: two per SIMD, so that one wave's LDS waits,
+// barriers and softmax overlap its sibling's MFMAs.  The siblings w and w+4
+// share 16 heads (16(w&3) .. of the group):
+// * QK is split by k: wave w takes k steps 9(w>>2) .. +8 (half of the 576
+//   dims) over all 32 tile rows, with its half of q (36 VGPRs) as the B
+//   operand and the rows read from LDS as the A operand; the two partial
+//   score tiles are summed through LDS in a fixed order, so both siblings
+//   hold the same scores and run the same online softmax.
+// * PV is split by columns: wave w accumulates columns 256(w>>2) .. +255 of
+//   its 16 heads (64 accumulator registers), V read transposed from the tile.
+// Registers left over hold three tiles of gathered rows in flight.
+constexpr int kWideThreads = 512;
+constexpr int kSbufWide = kWideThreads * 2 * 16;   // two f32x4 partial scores per thread
+
+template <bool FP8, int STAGES>
+__global__ __launch_bounds__(kWideThreads, 1) void sparse_mla_wide(MlaArgs a, int n_groups, int T) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  constexpr int kHeadsPerGroup = 64 / DSPLIT;
-  constexpr int kCols = kDc / DSPLIT;          // output columns per wave
-  constexpr int kColTiles = kCols / 16;
+  constexpr int NT = kWideThreads;
+  constexpr int kColTiles = 16;                // 256 columns per wave
   const int x = blockIdx.x, sp = blockIdx.z;
   const int t = (x / (8 * n_groups)) * 8 + (x & 7);
   const int grp = (x >> 3) % n_groups;
   if (t >= T) return;                          // padding ids of the XCD-aware layout
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, c16 = lane & 15;
-  const int head0 = grp * kHeadsPerGroup + (DSPLIT == 1 ? 16 * wave : 0);
-  const int col0 = DSPLIT == 1 ? 0 : kCols * wave;
-  const bool writes_stats = DSPLIT == 1 || wave == 0;
+  const int hg = wave & 3, kh = wave >> 2;     // head group of 16, k / column half
+  const int head0 = grp * 64 + 16 * hg;
+  const int col0 = 256 * kh;
   const int j_begin = sp * a.rows_per_split;
   const int j_end = min(a.K, j_begin + a.rows_per_split);
   const int ntiles = (j_end - j_begin + kTileRows - 1) / kTileRows;
   int sv0[kIdxBatch];
-  preload_indices(sv0, a.idx + (int64_t)t * a.K, j_begin, j_end, ntiles * kTileRows, tid);
+  preload_indices<NT>(sv0, a.idx + (int64_t)t * a.K, j_begin, j_end, ntiles * kTileRows, tid);
   const RowLoc loc = locate_row(a.cu_q, a.seq_lens, a.B, t);
   const int b = loc.b, pos = loc.pos;
   uint8_t* tile = smem;                                                 // one 32-row tile
-  f32x4* sbuf = reinterpret_cast<f32x4*>(smem + kTileLds);              // partial scores (16 heads)
-  int64_t* offs = reinterpret_cast<int64_t*>(smem + kTileLds + kSbufLds);
+  f32x4* sbuf = reinterpret_cast<f32x4*>(smem + kTileLds);              // partial scores
+  int64_t* offs = reinterpret_cast<int64_t*>(smem + kTileLds + kSbufWide);
   uint32_t* vmask = reinterpret_cast<uint32_t*>(offs + ntiles * kTileRows);  // usable rows per tile
   int* first_valid = reinterpret_cast<int*>(vmask + ntiles);
 
-  const int fv = build_offsets(offs, vmask, first_valid, sv0, a.idx + (int64_t)t * a.K, j_begin, j_end,
-                               ntiles * kTileRows, pos, b, a.page_table, a.pt_stride, a.page_size,
-                               a.num_pages, a.page_stride, a.row_stride, tid);
+  const int fv = build_offsets<NT>(offs, vmask, first_valid, sv0, a.idx + (int64_t)t * a.K, j_begin, j_end,
+                                   ntiles * kTileRows, pos, b, a.page_table, a.pt_stride, a.page_size,
+                                   a.num_pages, a.page_stride, a.row_stride, tid);
 
   f32x4 o[kColTiles];
 #pragma unroll
@@ -502,13 +581,8 @@ __global__ __launch_bounds__(kThreads, DSPLIT == 4 ? 2 : 1) void sparse_mla_tile
   float m_run = kNegInf, l_run = 0.f;
 
   if (fv != INT32_MAX) {
-    // With 16 heads per workgroup the four waves split QK: wave w takes tile
-    // rows 16(w&1) .. +15 over k steps 9(w>>1) .. +8 (half of the 576 dims),
-    // so each tile byte is read once for QK; the partial scores are summed
-    // through LDS.  With 64 heads each wave does all of QK for its 16 heads.
-    constexpr bool kSplitQk = DSPLIT == 4;
-    constexpr int kQSteps = kSplitQk ? 9 : 18;
-    const int ks0 = kSplitQk ? 9 * (wave >> 1) : 0;
+    constexpr int kQSteps = 9;
+    const int ks0 = 9 * kh;
     bf16x8 qreg[kQSteps];
     {
       const uint16_t* qp = a.q + ((int64_t)t * a.H + head0 + c16) * kD + g * 8 + ks0 * 32;
@@ -517,37 +591,11 @@ __global__ __launch_bounds__(kThreads, DSPLIT == 4 ? 2 : 1) void sparse_mla_tile
     }
     auto compute_tile = [&](int i) {
       const uint32_t valid = vmask[i];
-
-      // S^T: accumulator r of lane = tile row nt*16 + 4g + r, head c16.  The
-      // A operands are read kQkAhead k steps ahead of their MFMA.
-      constexpr int kQkAhead = 4;
-      f32x4 s0 = f32x4{}, s1 = f32x4{};
-      if constexpr (kSplitQk) {
-        f32x4 sp = f32x4{};
-        const uint8_t* ap = tile + (16 * (wave & 1) + c16) * kRowLds + g * 16 + ks0 * 64;
-        bf16x8 ra[kQkAhead];
-#pragma unroll
-        for (int k = 0; k < kQkAhead; ++k) ra[k] = lds16(ap + k * 64);
-#pragma unroll
-        for (int ks = 0; ks < kQSteps; ++ks) {
-          const bf16x8 xk = ra[ks % kQkAhead];
-          if (ks + kQkAhead < kQSteps) ra[ks % kQkAhead] = lds16(ap + (ks + kQkAhead) * 64);
-          sp = mfma16(xk, qreg[ks], sp);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, kQkAhead, 0);
-#pragma unroll
-        for (int ks = 0; ks < kQSteps - kQkAhead; ++ks) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, kQkAhead, 0);
-        sbuf[wave * 64 + lane] = sp;
-        lds_barrier();
-        // same summation order in every wave: k half 0, then k half 1
-        s0 = sbuf[0 * 64 + lane] + sbuf[2 * 64 + lane];
-        s1 = sbuf[1 * 64 + lane] + sbuf[3 * 64 + lane];
-      } else {
-      const uint8_t* ap = tile + c16 * kRowLds + g * 16;
+      // Partial S^T over this wave's k half: accumulator r of lane = tile row
+      // nt*16 + 4g + r, head c16.  A operands read kQkAhead k steps ahead.
+      constexpr int kQkAhead = 3;
+      f32x4 p0 = f32x4{}, p1 = f32x4{};
+      const uint8_t* ap = tile + c16 * kRowLds + g * 16 + ks0 * 64;
       bf16x8 ra0[kQkAhead], ra1[kQkAhead];
 #pragma unroll
       for (int k = 0; k < kQkAhead; ++k) {
@@ -555,52 +603,29 @@ __global__ __launch_bounds__(kThreads, DSPLIT == 4 ? 2 : 1) void sparse_mla_tile
         ra1[k] = lds16(ap + 16 * kRowLds + k * 64);
       }
 #pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
+      for (int ks = 0; ks < kQSteps; ++ks) {
         const bf16x8 x0 = ra0[ks % kQkAhead], x1 = ra1[ks % kQkAhead];
-        if (ks + kQkAhead < 18) {
+        if (ks + kQkAhead < kQSteps) {
           ra0[ks % kQkAhead] = lds16(ap + (ks + kQkAhead) * 64);
           ra1[ks % kQkAhead] = lds16(ap + 16 * kRowLds + (ks + kQkAhead) * 64);
         }
-        s0 = mfma16(x0, qreg[ks], s0);
-        s1 = mfma16(x1, qreg[ks], s1);
+        p0 = mfma16(x0, qreg[ks], p0);
+        p1 = mfma16(x1, qreg[ks], p1);
       }
-      // Keep the operand reads kQkAhead steps ahead of their MFMAs (the default
-      // schedule pulls them back next to their use and exposes LDS latency).
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * kQkAhead, 0);
 #pragma unroll
-      for (int ks = 0; ks < 18 - kQkAhead; ++ks) {
+      for (int ks = 0; ks < kQSteps - kQkAhead; ++ks) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 2 * kQkAhead, 0);
-      }
-      float xv[8];
-      float mt = kNegInf;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        xv[r] = (valid >> (4 * g + r)) & 1u ? s0[r] * a.scale_log2 : kNegInf;
-        xv[4 + r] = (valid >> (16 + 4 * g + r)) & 1u ? s1[r] * a.scale_log2 : kNegInf;
-        mt = fmaxf(mt, fmaxf(xv[r], xv[4 + r]));
-      }
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      float alpha;
-      if (softmax_step(mt, m_run, alpha)) {
-        l_run *= alpha;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float ar = __shfl(alpha, 4 * g + r);  // O row r holds head 4g + r
-#pragma unroll
-          for (int i2 = 0; i2 < kColTiles; ++i2) o[i2][r] *= ar;
-        }
-      }
-      bf16x8 pa;
-#pragma unroll
-      for (int i2 = 0; i2 < 8; ++i2) {
-        const float p = xv[i2] == kNegInf ? 0.f : exp2f(xv[i2] - m_run);
-        l_run += p;
-        pa[i2] = (__bf16)p;
-      }
+      sbuf[(2 * wave) * 64 + lane] = p0;
+      sbuf[(2 * wave + 1) * 64 + lane] = p1;
+      lds_barrier();
+      // same summation order in both siblings: k half 0, then k half 1
+      const f32x4 s0 = sbuf[(2 * hg) * 64 + lane] + sbuf[(2 * (hg + 4)) * 64 + lane];
+      const f32x4 s1 = sbuf[(2 * hg + 1) * 64 + lane] + sbuf[(2 * (hg + 4) + 1) * 64 + lane];
+      const bf16x8 pa = tile_softmax(s0, s1, valid, a.scale_log2, m_run, l_run, o);
       // O[:, col0 + 16 i .. +16] += P V.  k slot (g, e) <-> tile row 4g + e,
       // (g, 4 + e) <-> 16 + 4g + e, matching the S^T accumulator rows.
       const uint8_t* vp = tile + (4 * g + (c16 >> 2)) * kRowLds + (col0 + 4 * (c16 & 3)) * 2;
@@ -630,25 +655,26 @@ __global__ __launch_bounds__(kThreads, DSPLIT == 4 ? 2 : 1) void sparse_mla_tile
     };
     // Tile i is written to LDS from stage i%STAGES, whose registers then take
     // the loads of tile i+STAGES; the compiler's own vmcnt waits cover the loads.
-    auto step = [&](Stage<FP8>& st, int i) {
-      lds_barrier();                       // every wave is done with tile i-1
-      stage_store<FP8>(st, tile, tid);
-      if (i + STAGES < ntiles) stage_load<FP8>(st, offs + (i + STAGES) * kTileRows, a.kv, tid);
+    auto step = [&](Stage<FP8, NT>& st, int i) {
+      lds_barrier();                       // every wave is done with tile i-1 and its scores
+      stage_store<FP8, NT>(st, tile, tid);
+      if (i + STAGES < ntiles) stage_load<FP8, NT>(st, offs + (i + STAGES) * kTileRows, a.kv, tid);
       lds_barrier();                       // tile i visible to every wave
       compute_tile(i);
     };
-    Stage<FP8> st0, st1;
-    stage_load<FP8>(st0, offs, a.kv, tid);
-    if (STAGES == 2 && ntiles > 1) stage_load<FP8>(st1, offs + kTileRows, a.kv, tid);
+    Stage<FP8, NT> st[STAGES];
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s)
+      if (s < ntiles) stage_load<FP8, NT>(st[s], offs + s * kTileRows, a.kv, tid);
 #pragma unroll 1
     for (int i = 0; i < ntiles; i += STAGES) {
-      step(st0, i);
-      if (STAGES == 2 && i + 1 < ntiles) step(st1, i + 1);
+#pragma unroll
+      for (int s = 0; s < STAGES; ++s)
+        if (i + s < ntiles) step(st[s], i + s);
     }
   }
 
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = sum_over_groups(l_run);
   // O accumulator r of lane: head 4g + r, column col0 + 16 i + c16.
   if (a.splits == 1) {
 #pragma unroll
@@ -661,13 +687,14 @@ __global__ __launch_bounds__(kThreads, DSPLIT == 4 ? 2 : 1) void sparse_mla_tile
       for (int i2 = 0; i2 < kColTiles; ++i2)
         op[16 * i2] = __builtin_bit_cast(uint16_t, (__bf16)(o[i2][r] * inv));
     }
-    if (a.lse != nullptr && writes_stats && lane < 16)
+    if (a.lse != nullptr && kh == 0 && lane < 16)
       a.lse[(int64_t)t * a.H + head0 + lane] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : kNegInf;
   } else {
-    store_partials<kHeadsPerGroup, kColTiles>(a, t, grp, n_groups, sp, wave, lane, o, m_run, l_run,
-                                             writes_stats ? head0 - grp * kHeadsPerGroup : -1);
-    merge_splits_if_last<DSPLIT == 1>(a, t, grp, n_groups, a.counters + (int64_t)t * n_groups + grp,
-                                      reinterpret_cast<float*>(tile), first_valid + 1, tid);
+    // layout of the 64-head partials: tile slot (16 heads of group hg) x 32 + column tile
+    store_partials<64, kColTiles>(a, t, grp, n_groups, sp, hg * 32 + kColTiles * kh, lane, o, m_run, l_run,
+                                  kh == 0 ? 16 * hg : -1);
+    merge_splits_if_last<true, NT>(a, t, grp, n_groups, a.counters + (int64_t)t * n_groups + grp,
+                                   reinterpret_cast<float*>(tile), first_valid + 1, tid);
   }
 }
 
@@ -786,33 +813,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_q16(MlaArgs a, int n_g
       // rows 0..15 from waves 0 and 2, rows 16..31 from waves 1 and 3; k half 0 first
       const f32x4 s0 = sbuf[0 * 64 + lane] + sbuf[2 * 64 + lane];
       const f32x4 s1 = sbuf[1 * 64 + lane] + sbuf[3 * 64 + lane];
-      float xv[8];
-      float mt = kNegInf;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        xv[r] = (valid >> (4 * g + r)) & 1u ? s0[r] * a.scale_log2 : kNegInf;
-        xv[4 + r] = (valid >> (16 + 4 * g + r)) & 1u ? s1[r] * a.scale_log2 : kNegInf;
-        mt = fmaxf(mt, fmaxf(xv[r], xv[4 + r]));
-      }
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      float alpha;
-      if (softmax_step(mt, m_run, alpha)) {
-        l_run *= alpha;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float ar = __shfl(alpha, 4 * g + r);  // O row r holds head 4g + r
-#pragma unroll
-          for (int i2 = 0; i2 < 8; ++i2) o[i2][r] *= ar;
-        }
-      }
-      bf16x8 pa;
-#pragma unroll
-      for (int i2 = 0; i2 < 8; ++i2) {
-        const float p = xv[i2] == kNegInf ? 0.f : exp2f(xv[i2] - m_run);
-        l_run += p;
-        pa[i2] = (__bf16)p;
-      }
+      const bf16x8 pa = tile_softmax(s0, s1, valid, a.scale_log2, m_run, l_run, o);
       // O[:, col0 + 16 i .. +16] += P V.  k slot (g, e) <-> tile row 4g + e,
       // (g, 4 + e) <-> 16 + 4g + e, matching the S^T accumulator rows.
       const uint8_t* vp = tile + (4 * g + (c16 >> 2)) * kRowLds + (col0 + 4 * (c16 & 3)) * 2;
@@ -837,8 +838,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_q16(MlaArgs a, int n_g
     }
   }
 
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = sum_over_groups(l_run);
   // O accumulator r of lane: head 4g + r, column col0 + 16 i + c16.
   if (a.splits == 1) {
 #pragma unroll
@@ -853,7 +853,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_q16(MlaArgs a, int n_g
     if (a.lse != nullptr && wave == 0 && lane < 16)
       a.lse[(int64_t)t * a.H + head0 + lane] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : kNegInf;
   } else {
-    store_partials<16, 8>(a, t, grp, n_groups, sp, wave, lane, o, m_run, l_run, wave == 0 ? 0 : -1);
+    store_partials<16, 8>(a, t, grp, n_groups, sp, wave * 8, lane, o, m_run, l_run, wave == 0 ? 0 : -1);
     merge_splits_if_last<false>(a, t, grp, n_groups, a.counters + (int64_t)t * n_groups + grp,
                                 reinterpret_cast<float*>(tile), first_valid + 1, tid);
   }
@@ -948,18 +948,19 @@ namespace {
 
 constexpr size_t kMaxLds = 160 * 1024;
 
-// LDS bytes: the tile, then the range's row offsets, tile masks and a flag.
-size_t mla_lds(int rps) {
+// LDS bytes: the tile, the partial scores, then the range's row offsets, tile
+// masks and a flag.
+size_t mla_lds(int rps, size_t sbuf) {
   const size_t ntiles = (size_t)(rps + kTileRows - 1) / kTileRows;
-  return kTileLds + kSbufLds + ntiles * (kTileRows * 8 + 4) + 16;
+  return kTileLds + sbuf + ntiles * (kTileRows * 8 + 4) + 16;
 }
 
 template <typename Kernel>
-hipError_t launch_with_lds(Kernel kernel, dim3 grid, size_t lds, hipStream_t stream, const MlaArgs& args,
-                           int n_groups, int T) {
+hipError_t launch_with_lds(Kernel kernel, dim3 grid, int threads, size_t lds, hipStream_t stream,
+                           const MlaArgs& args, int n_groups, int T) {
   hipError_t e = ensure_max_lds(reinterpret_cast<const void*>(kernel));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kernel, grid, dim3(kThreads), lds, stream, args, n_groups, T);
+  hipLaunchKernelGGL(kernel, grid, dim3(threads), lds, stream, args, n_groups, T);
   return hipGetLastError();
 }
 
@@ -971,7 +972,7 @@ hipError_t launch_sparse_mla_bf16(const BatchArgs& ba, const void* q, const Pool
                                   hipStream_t stream) {
   const bool wide = n_heads % 64 == 0;
   const bool fp8 = kv.format == 2;
-  const size_t lds = mla_lds(plan.rows_per_split);
+  const size_t lds = mla_lds(plan.rows_per_split, wide ? kSbufWide : kSbufLds);
   if (lds > kMaxLds) return hipErrorInvalidValue;
   MlaArgs args{ba.cu_q, ba.seq_lens, ba.page_table, ba.batch, ba.pt_stride, ba.page_size,
                ba.num_pages, static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(kv.base),
@@ -986,14 +987,13 @@ hipError_t launch_sparse_mla_bf16(const BatchArgs& ba, const void* q, const Pool
   const dim3 grid = wide ? dim3((unsigned)((T + 7) / 8 * 8 * n_groups), 1, plan.splits)
                          : dim3((unsigned)(n_groups * ((T * plan.splits + 7) / 8 * 8)), 1, 1);
   hipError_t e;
-  // Tiles of loads in flight per workgroup: two for 16-head groups (two
-  // workgroups per CU), one for 64-head groups (a second would spill).
+  // Tiles of loads in flight per workgroup: two or three.
   if (wide)
-    e = fp8 ? launch_with_lds(sparse_mla_tiles<1, true, 1>, grid, lds, stream, args, n_groups, T)
-            : launch_with_lds(sparse_mla_tiles<1, false, 1>, grid, lds, stream, args, n_groups, T);
+    e = fp8 ? launch_with_lds(sparse_mla_wide<true, 3>, grid, kWideThreads, lds, stream, args, n_groups, T)
+            : launch_with_lds(sparse_mla_wide<false, 3>, grid, kWideThreads, lds, stream, args, n_groups, T);
   else
-    e = fp8 ? launch_with_lds(sparse_mla_q16<true, 2>, grid, lds, stream, args, n_groups, T)
-            : launch_with_lds(sparse_mla_q16<false, 3>, grid, lds, stream, args, n_groups, T);
+    e = fp8 ? launch_with_lds(sparse_mla_q16<true, 2>, grid, kThreads, lds, stream, args, n_groups, T)
+            : launch_with_lds(sparse_mla_q16<false, 3>, grid, kThreads, lds, stream, args, n_groups, T);
   return e;
 }
 
