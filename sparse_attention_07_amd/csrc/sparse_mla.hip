@@ -111,83 +111,69 @@ __device__ inline uint2 fp8x4_to_bf16x4(uint32_t x, float sc) {
   return r;
 }
 
-// One tile's rows in flight in registers, for a workgroup of NT threads:
-// bf16 rows as 72 16-byte chunks per row (item = it*NT + tid -> row item/72,
-// chunk item%72); fp8 rows as 40 items per row (item -> row item/40, chunk
-// item%40: 32 latent chunks of 16 e4m3 bytes, each with its block scale, then
-// 8 rope chunks of bf16).
-template <bool FP8>
-constexpr int kPerRowItems = FP8 ? 40 : 72;
-template <bool FP8, int NT>
-constexpr int kStageItems = (kTileRows * kPerRowItems<FP8> + NT - 1) / NT;
+// One tile's rows in flight in registers, for a workgroup of 512 threads.
+// Each thread keeps one chunk column, so its items differ only by row: bf16
+// rows -- latent chunk tid%64 (16 B) of rows tid/64 + 8k, k < 4; fp8 rows --
+// latent chunk tid%32 (16 e4m3 bytes, with its block scale) of rows tid/32 +
+// 16k, k < 2.  Every thread also loads 8 bytes of rope (bf16 dims 4(tid%16)
+// .. +3 of row tid/16).  A wave reads 1 KB (bf16) or 512 B (fp8) contiguous
+// of a row per latent load.
+constexpr int kStageThreads = 512;
 
-template <bool FP8, int NT = kThreads>
+template <bool FP8>
 struct Stage {
-  u32x4 v[kStageItems<FP8, NT>];
-  float sc[FP8 ? kStageItems<FP8, NT> : 1];
+  u32x4 lat[FP8 ? 2 : 4];
+  float sc[FP8 ? 2 : 1];
+  uint2 rope;
 };
 
 __device__ inline u32x4 ld_global16(const uint8_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
-template <bool FP8, int NT = kThreads>
-__device__ inline void stage_load(Stage<FP8, NT>& st, const int64_t* toffs, const uint8_t* kv, int tid) {
-  constexpr int kItems = kStageItems<FP8, NT>;
-  constexpr int kPerRow = kPerRowItems<FP8>;
-  constexpr int kTotal = kTileRows * kPerRow;
-  int64_t off[kItems];
+template <bool FP8>
+__device__ inline void stage_load(Stage<FP8>& st, const int64_t* toffs, const uint8_t* kv, int tid) {
+  constexpr int kLat = FP8 ? 2 : 4, kStep = FP8 ? 16 : 8;
+  const int ch = FP8 ? (tid & 31) : (tid & 63);
+  const int r0 = FP8 ? (tid >> 5) : (tid >> 6);
+  int64_t off[kLat];
 #pragma unroll
-  for (int it = 0; it < kItems; ++it) {
-    const int item = it * NT + tid;
-    off[it] = (kTotal % NT == 0 || item < kTotal) ? toffs[item / kPerRow] : -1;
-  }
+  for (int k = 0; k < kLat; ++k) off[k] = toffs[r0 + kStep * k];
+  const int64_t roff = toffs[tid >> 4];
 #pragma unroll
-  for (int it = 0; it < kItems; ++it) {
-    const int item = it * NT + tid;
-    const int ch = item % kPerRow;
-    st.v[it] = u32x4{};
-    if (off[it] >= 0) {
-      const uint8_t* row = kv + off[it];
-      if (!FP8) {
-        st.v[it] = ld_global16(row + ch * 16);
-      } else if (ch < 32) {
-        st.v[it] = ld_global16(row + ch * 16);
-        st.sc[it] = *reinterpret_cast<const float*>(row + 512 + (ch >> 3) * 4);
-      } else {
-        st.v[it] = ld_global16(row + 528 + (ch - 32) * 16);
-      }
+  for (int k = 0; k < kLat; ++k) {
+    st.lat[k] = u32x4{};
+    if (FP8) st.sc[k] = 0.f;
+    if (off[k] >= 0) {
+      st.lat[k] = ld_global16(kv + off[k] + ch * 16);
+      if (FP8) st.sc[k] = *reinterpret_cast<const float*>(kv + off[k] + 512 + (ch >> 3) * 4);
     }
-    if (FP8 && (off[it] < 0 || ch >= 32)) st.sc[it] = 0.f;
   }
+  st.rope = uint2{0u, 0u};
+  if (roff >= 0) st.rope = *reinterpret_cast<const uint2*>(kv + roff + (FP8 ? 528 : 1024) + (tid & 15) * 8);
 }
 
-template <bool FP8, int NT = kThreads>
-__device__ inline void stage_store(const Stage<FP8, NT>& st, uint8_t* tile, int tid) {
-  constexpr int kItems = kStageItems<FP8, NT>;
-  constexpr int kPerRow = kPerRowItems<FP8>;
-  constexpr int kTotal = kTileRows * kPerRow;
+template <bool FP8>
+__device__ inline void stage_store(const Stage<FP8>& st, uint8_t* tile, int tid) {
+  constexpr int kLat = FP8 ? 2 : 4, kStep = FP8 ? 16 : 8;
+  const int ch = FP8 ? (tid & 31) : (tid & 63);
+  const int r0 = FP8 ? (tid >> 5) : (tid >> 6);
 #pragma unroll
-  for (int it = 0; it < kItems; ++it) {
-    const int item = it * NT + tid;
-    if (kTotal % NT != 0 && item >= kTotal) break;
-    const int r = item / kPerRow, ch = item % kPerRow;
-    uint8_t* dst = tile + r * kRowLds;
+  for (int k = 0; k < kLat; ++k) {
+    uint8_t* dst = tile + (r0 + kStep * k) * kRowLds;
     if (!FP8) {
-      *reinterpret_cast<u32x4*>(dst + ch * 16) = st.v[it];
-    } else if (ch < 32) {
-      const float sc = st.sc[it];
+      *reinterpret_cast<u32x4*>(dst + ch * 16) = st.lat[k];
+    } else {
       u32x4 lo, hi;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const uint2 pr = fp8x4_to_bf16x4(st.v[it][w], sc);
+        const uint2 pr = fp8x4_to_bf16x4(st.lat[k][w], st.sc[k]);
         if (w < 2) { lo[2 * w] = pr.x; lo[2 * w + 1] = pr.y; }
         else { hi[2 * w - 4] = pr.x; hi[2 * w - 3] = pr.y; }
       }
       *reinterpret_cast<u32x4*>(dst + ch * 32) = lo;
       *reinterpret_cast<u32x4*>(dst + ch * 32 + 16) = hi;
-    } else {
-      *reinterpret_cast<u32x4*>(dst + 1024 + (ch - 32) * 16) = st.v[it];
     }
   }
+  *reinterpret_cast<uint2*>(tile + (tid >> 4) * kRowLds + 1024 + (tid & 15) * 8) = st.rope;
 }
 
 // Prologue: byte offsets of the range's rows (page table applied; -1 when not
@@ -336,11 +322,20 @@ __device__ inline bf16x8 tile_softmax(const f32x4& s0, const f32x4& s1, uint32_t
     }
   }
   bf16x8 pa;
+  if (valid == 0xFFFFFFFFu) {  // finite scores, finite running max
 #pragma unroll
-  for (int i2 = 0; i2 < 8; ++i2) {
-    const float p = xv[i2] == kNegInf ? 0.f : exp2_fast(xv[i2] - m_run);
-    l_run += p;
-    pa[i2] = (__bf16)p;
+    for (int i2 = 0; i2 < 8; ++i2) {
+      const float p = exp2_fast(xv[i2] - m_run);
+      l_run += p;
+      pa[i2] = (__bf16)p;
+    }
+  } else {
+#pragma unroll
+    for (int i2 = 0; i2 < 8; ++i2) {
+      const float p = xv[i2] == kNegInf ? 0.f : exp2_fast(xv[i2] - m_run);
+      l_run += p;
+      pa[i2] = (__bf16)p;
+    }
   }
   return pa;
 }
@@ -530,9 +525,8 @@ __device__ inline void merge_splits_if_last(const MlaArgs& a, int t, int grp, in
 // ---------------------------------------------------------------- 64 heads, 8 waves
 
 // A workgroup owns 64 heads of one query row and one range of its selected
-// rows, with eight waves: two per SIMD, so that one wave's LDS waits,
-// barriers and softmax overlap its sibling's MFMAs.  The siblings w and w+4
-// share 16 heads (16(w&3) .. of the group):
+// rows, with eight waves: two per SIMD.  The siblings w and w+4 share 16 heads
+// (16(w&3) .. of the group):
 // * QK is split by k: wave w takes k steps 9(w>>2) .. +8 (half of the 576
 //   dims) over all 32 tile rows, with its half of q (36 VGPRs) as the B
 //   operand and the rows read from LDS as the A operand; the two partial
@@ -540,14 +534,23 @@ __device__ inline void merge_splits_if_last(const MlaArgs& a, int t, int grp, in
 //   hold the same scores and run the same online softmax.
 // * PV is split by columns: wave w accumulates columns 256(w>>2) .. +255 of
 //   its 16 heads (64 accumulator registers), V read transposed from the tile.
-// Registers left over hold three tiles of gathered rows in flight.
+// The tiles are software-pipelined over three LDS tile buffers and two
+// partial-score buffers, with one barrier per tile: iteration i sums tile
+// i's partial scores, issues the QK MFMAs of tile i+1 while the softmax of
+// tile i runs on the VALU, then the PV MFMAs of tile i; tile i+2 is written
+// to LDS from registers and the gathers of tile i+4 are issued (two tiles of
+// gathers in flight in registers, two more waiting in LDS).
 constexpr int kWideThreads = 512;
-constexpr int kSbufWide = kWideThreads * 2 * 16;   // two f32x4 partial scores per thread
+constexpr int kWideBufs = 3;                         // LDS tile buffers
+constexpr int kWideStages = 2;                       // register stages of gathers
+constexpr int kSbufWide = kWideThreads * 2 * 16;     // two f32x4 partial scores per thread
 
-template <bool FP8, int STAGES>
+template <bool FP8>
 __global__ __launch_bounds__(kWideThreads, 1) void sparse_mla_wide(MlaArgs a, int n_groups, int T) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int NT = kWideThreads;
+  constexpr int STAGES = kWideStages;
+  static_assert(NT == kStageThreads, "the gather layout assumes 512 threads");
   constexpr int kColTiles = 16;                // 256 columns per wave
   const int x = blockIdx.x, sp = blockIdx.z;
   const int t = (x / (8 * n_groups)) * 8 + (x & 7);
@@ -565,9 +568,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void sparse_mla_wide(MlaArgs a, in
   preload_indices<NT>(sv0, a.idx + (int64_t)t * a.K, j_begin, j_end, ntiles * kTileRows, tid);
   const RowLoc loc = locate_row(a.cu_q, a.seq_lens, a.B, t);
   const int b = loc.b, pos = loc.pos;
-  uint8_t* tile = smem;                                                 // one 32-row tile
-  f32x4* sbuf = reinterpret_cast<f32x4*>(smem + kTileLds);              // partial scores
-  int64_t* offs = reinterpret_cast<int64_t*>(smem + kTileLds + kSbufWide);
+  uint8_t* tiles = smem;                                                // kWideBufs tiles
+  f32x4* sbuf = reinterpret_cast<f32x4*>(smem + kWideBufs * kTileLds);  // 2 x partial scores
+  int64_t* offs = reinterpret_cast<int64_t*>(smem + kWideBufs * kTileLds + 2 * kSbufWide);
   uint32_t* vmask = reinterpret_cast<uint32_t*>(offs + ntiles * kTileRows);  // usable rows per tile
   int* first_valid = reinterpret_cast<int*>(vmask + ntiles);
 
@@ -589,13 +592,13 @@ __global__ __launch_bounds__(kWideThreads, 1) void sparse_mla_wide(MlaArgs a, in
 #pragma unroll
       for (int ks = 0; ks < kQSteps; ++ks) qreg[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32);
     }
-    auto compute_tile = [&](int i) {
-      const uint32_t valid = vmask[i];
-      // Partial S^T over this wave's k half: accumulator r of lane = tile row
-      // nt*16 + 4g + r, head c16.  A operands read kQkAhead k steps ahead.
+    // Partial S^T of a tile over this wave's k half: accumulator r of lane =
+    // tile row nt*16 + 4g + r, head c16.
+    auto qk = [&](const uint8_t* tl, f32x4& p0, f32x4& p1) {
       constexpr int kQkAhead = 3;
-      f32x4 p0 = f32x4{}, p1 = f32x4{};
-      const uint8_t* ap = tile + c16 * kRowLds + g * 16 + ks0 * 64;
+      p0 = f32x4{};
+      p1 = f32x4{};
+      const uint8_t* ap = tl + c16 * kRowLds + g * 16 + ks0 * 64;
       bf16x8 ra0[kQkAhead], ra1[kQkAhead];
 #pragma unroll
       for (int k = 0; k < kQkAhead; ++k) {
@@ -612,65 +615,79 @@ __global__ __launch_bounds__(kWideThreads, 1) void sparse_mla_wide(MlaArgs a, in
         p0 = mfma16(x0, qreg[ks], p0);
         p1 = mfma16(x1, qreg[ks], p1);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kQkAhead, 0);
-#pragma unroll
-      for (int ks = 0; ks < kQSteps - kQkAhead; ++ks) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * kQkAhead, 0);
-      sbuf[(2 * wave) * 64 + lane] = p0;
-      sbuf[(2 * wave + 1) * 64 + lane] = p1;
-      lds_barrier();
-      // same summation order in both siblings: k half 0, then k half 1
-      const f32x4 s0 = sbuf[(2 * hg) * 64 + lane] + sbuf[(2 * (hg + 4)) * 64 + lane];
-      const f32x4 s1 = sbuf[(2 * hg + 1) * 64 + lane] + sbuf[(2 * (hg + 4) + 1) * 64 + lane];
-      const bf16x8 pa = tile_softmax(s0, s1, valid, a.scale_log2, m_run, l_run, o);
-      // O[:, col0 + 16 i .. +16] += P V.  k slot (g, e) <-> tile row 4g + e,
-      // (g, 4 + e) <-> 16 + 4g + e, matching the S^T accumulator rows.
-      const uint8_t* vp = tile + (4 * g + (c16 >> 2)) * kRowLds + (col0 + 4 * (c16 & 3)) * 2;
+    };
+    auto write_partials = [&](int i, const f32x4& p0, const f32x4& p1) {
+      f32x4* sb = sbuf + (i & 1) * (2 * NT);
+      sb[(2 * wave) * 64 + lane] = p0;
+      sb[(2 * wave + 1) * 64 + lane] = p1;
+    };
+    // O[:, col0 + 16 i .. +16] += P V.  k slot (g, e) <-> tile row 4g + e,
+    // (g, 4 + e) <-> 16 + 4g + e, matching the S^T accumulator rows.
+    auto pv = [&](const uint8_t* tl, const bf16x8& pa) {
+      const uint8_t* vp = tl + (4 * g + (c16 >> 2)) * kRowLds + (col0 + 4 * (c16 & 3)) * 2;
       constexpr int kPvAhead = 4;
-      s16x4 tv1[kPvAhead], tv2[kPvAhead];
+      bf16x8 vb[kPvAhead];  // both 16-row halves of a column tile, joined as they are read
 #pragma unroll
-      for (int k = 0; k < kPvAhead; ++k) {
-        tv1[k] = lds_read_tr16(vp + k * 32);
-        tv2[k] = lds_read_tr16(vp + 16 * kRowLds + k * 32);
-      }
+      for (int k = 0; k < kPvAhead; ++k)
+        vb[k] = join(lds_read_tr16(vp + k * 32), lds_read_tr16(vp + 16 * kRowLds + k * 32));
 #pragma unroll
       for (int i2 = 0; i2 < kColTiles; ++i2) {
-        const s16x4 v1 = tv1[i2 % kPvAhead], v2 = tv2[i2 % kPvAhead];
-        if (i2 + kPvAhead < kColTiles) {
-          tv1[i2 % kPvAhead] = lds_read_tr16(vp + (i2 + kPvAhead) * 32);
-          tv2[i2 % kPvAhead] = lds_read_tr16(vp + 16 * kRowLds + (i2 + kPvAhead) * 32);
-        }
-        o[i2] = mfma16(pa, join(v1, v2), o[i2]);
+        const bf16x8 v = vb[i2 % kPvAhead];
+        if (i2 + kPvAhead < kColTiles)
+          vb[i2 % kPvAhead] = join(lds_read_tr16(vp + (i2 + kPvAhead) * 32),
+                                   lds_read_tr16(vp + 16 * kRowLds + (i2 + kPvAhead) * 32));
+        o[i2] = mfma16(pa, v, o[i2]);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPvAhead, 1);
-#pragma unroll
-      for (int i2 = 0; i2 < kColTiles - kPvAhead; ++i2) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    };
+    // Iteration i: tiles i and i+1 are in LDS buffers b0 and b1, and tile i's
+    // partial scores are exchanged; tile i+2 goes to buffer b2 from stage
+    // st_next (i % 2).  The QK of tile i+1 and the store of tile i+2 also run
+    // past the last tile (on buffers no longer read; their results are dropped).
+    auto iter = [&](int i, Stage<FP8>& st_next, uint8_t* b0, uint8_t* b1, uint8_t* b2) {
+      const f32x4* sb = sbuf + (i & 1) * (2 * NT);
+      // same summation order in both siblings: k half 0, then k half 1
+      const f32x4 s0 = sb[(2 * hg) * 64 + lane] + sb[(2 * (hg + 4)) * 64 + lane];
+      const f32x4 s1 = sb[(2 * hg + 1) * 64 + lane] + sb[(2 * (hg + 4) + 1) * 64 + lane];
+      {
+        f32x4 p0, p1;
+        qk(b1, p0, p1);
+        write_partials(i + 1, p0, p1);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, kPvAhead, 1);
+      const bf16x8 pa = tile_softmax(s0, s1, vmask[i], a.scale_log2, m_run, l_run, o);
+      pv(b0, pa);
+      stage_store<FP8>(st_next, b2, tid);
+      if (i + 2 + STAGES < ntiles) stage_load<FP8>(st_next, offs + (i + 2 + STAGES) * kTileRows, a.kv, tid);
+      lds_barrier();
     };
-    // Tile i is written to LDS from stage i%STAGES, whose registers then take
-    // the loads of tile i+STAGES; the compiler's own vmcnt waits cover the loads.
-    auto step = [&](Stage<FP8, NT>& st, int i) {
-      lds_barrier();                       // every wave is done with tile i-1 and its scores
-      stage_store<FP8, NT>(st, tile, tid);
-      if (i + STAGES < ntiles) stage_load<FP8, NT>(st, offs + (i + STAGES) * kTileRows, a.kv, tid);
-      lds_barrier();                       // tile i visible to every wave
-      compute_tile(i);
-    };
-    Stage<FP8, NT> st[STAGES];
+    Stage<FP8> st[STAGES];
 #pragma unroll
     for (int s = 0; s < STAGES; ++s)
-      if (s < ntiles) stage_load<FP8, NT>(st[s], offs + s * kTileRows, a.kv, tid);
-#pragma unroll 1
-    for (int i = 0; i < ntiles; i += STAGES) {
+      if (s < ntiles) stage_load<FP8>(st[s], offs + s * kTileRows, a.kv, tid);
+    // tiles 0 and 1 to LDS, then tile 0's partial scores
 #pragma unroll
-      for (int s = 0; s < STAGES; ++s)
-        if (i + s < ntiles) step(st[s], i + s);
+    for (int s = 0; s < 2; ++s) {
+      stage_store<FP8>(st[s], tiles + s * kTileLds, tid);
+      if (s + STAGES < ntiles) stage_load<FP8>(st[s], offs + (s + STAGES) * kTileRows, a.kv, tid);
+    }
+    lds_barrier();
+    {
+      f32x4 p0, p1;
+      qk(tiles, p0, p1);
+      write_partials(0, p0, p1);
+    }
+    lds_barrier();
+    // buffers of tiles i, i+1, i+2 rotate; stage (i+2) % 2 == i % 2
+    uint8_t* b0 = tiles;
+    uint8_t* b1 = tiles + kTileLds;
+    uint8_t* b2 = tiles + 2 * kTileLds;
+#pragma unroll 1
+    for (int i = 0; i < ntiles; i += 2) {
+      iter(i, st[0], b0, b1, b2);
+      if (i + 1 < ntiles) iter(i + 1, st[1], b1, b2, b0);
+      uint8_t* const nb = b0;  // advance by two tiles
+      b0 = b2;
+      b2 = b1;
+      b1 = nb;
     }
   }
 
@@ -694,7 +711,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void sparse_mla_wide(MlaArgs a, in
     store_partials<64, kColTiles>(a, t, grp, n_groups, sp, hg * 32 + kColTiles * kh, lane, o, m_run, l_run,
                                   kh == 0 ? 16 * hg : -1);
     merge_splits_if_last<true, NT>(a, t, grp, n_groups, a.counters + (int64_t)t * n_groups + grp,
-                                   reinterpret_cast<float*>(tile), first_valid + 1, tid);
+                                   reinterpret_cast<float*>(tiles), first_valid + 1, tid);
   }
 }
 
@@ -948,11 +965,11 @@ namespace {
 
 constexpr size_t kMaxLds = 160 * 1024;
 
-// LDS bytes: the tile, the partial scores, then the range's row offsets, tile
-// masks and a flag.
-size_t mla_lds(int rps, size_t sbuf) {
+// LDS bytes: the first tile, `more` bytes of further tiles and partial
+// scores, then the range's row offsets, tile masks and a flag.
+size_t mla_lds(int rps, size_t more) {
   const size_t ntiles = (size_t)(rps + kTileRows - 1) / kTileRows;
-  return kTileLds + sbuf + ntiles * (kTileRows * 8 + 4) + 16;
+  return kTileLds + more + ntiles * (kTileRows * 8 + 4) + 16;
 }
 
 template <typename Kernel>
@@ -972,7 +989,8 @@ hipError_t launch_sparse_mla_bf16(const BatchArgs& ba, const void* q, const Pool
                                   hipStream_t stream) {
   const bool wide = n_heads % 64 == 0;
   const bool fp8 = kv.format == 2;
-  const size_t lds = mla_lds(plan.rows_per_split, wide ? kSbufWide : kSbufLds);
+  const size_t lds = wide ? mla_lds(plan.rows_per_split, (kWideBufs - 1) * kTileLds + 2 * kSbufWide)
+                         : mla_lds(plan.rows_per_split, kSbufLds);
   if (lds > kMaxLds) return hipErrorInvalidValue;
   MlaArgs args{ba.cu_q, ba.seq_lens, ba.page_table, ba.batch, ba.pt_stride, ba.page_size,
                ba.num_pages, static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(kv.base),
@@ -989,8 +1007,8 @@ hipError_t launch_sparse_mla_bf16(const BatchArgs& ba, const void* q, const Pool
   hipError_t e;
   // Tiles of loads in flight per workgroup: two or three.
   if (wide)
-    e = fp8 ? launch_with_lds(sparse_mla_wide<true, 3>, grid, kWideThreads, lds, stream, args, n_groups, T)
-            : launch_with_lds(sparse_mla_wide<false, 3>, grid, kWideThreads, lds, stream, args, n_groups, T);
+    e = fp8 ? launch_with_lds(sparse_mla_wide<true>, grid, kWideThreads, lds, stream, args, n_groups, T)
+            : launch_with_lds(sparse_mla_wide<false>, grid, kWideThreads, lds, stream, args, n_groups, T);
   else
     e = fp8 ? launch_with_lds(sparse_mla_q16<true, 2>, grid, kThreads, lds, stream, args, n_groups, T)
             : launch_with_lds(sparse_mla_q16<false, 3>, grid, kThreads, lds, stream, args, n_groups, T);
