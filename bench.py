@@ -58,16 +58,16 @@ def parse():
 # counters were taken -- a changed kernel reports traffic null.
 # Copy calibration of those runs: FETCH_SIZE x 2.000, WRITE_SIZE x 1.000.
 TRAFFIC = {
-    (1, "sparse_mla"): {"src": "65641cdba03f15e8", "fetch_bytes": 1.659e+08, "write_bytes": 1.798e+07,
+    (1, "sparse_mla"): {"src": "0763ddd7d7210be3", "fetch_bytes": 1.660e+08, "write_bytes": 9.525e+06,
                         "dispatches": 42},
-    (1, "index_scores"): {"src": "82d73a2c9c04c901", "fetch_bytes": 8.335e+07, "write_bytes": 1.183e+06,
+    (1, "index_scores"): {"src": "a5ac9e58e91bff31", "fetch_bytes": 8.103e+07, "write_bytes": 1.183e+06,
                           "dispatches": 42},
-    (1, "topk"): {"src": "b7c699e962083794", "fetch_bytes": 1.214e+06, "write_bytes": 5.243e+05,
+    (1, "topk"): {"src": "aba5a8fcb705a592", "fetch_bytes": 1.460e+06, "write_bytes": 5.243e+05,
                   "dispatches": 42},
 }
 KERNEL_SOURCES = {"sparse_mla": ["sparse_mla.hip", "dsa_device.h"],
                   "index_scores": ["index_scores.hip", "dsa_device.h"],
-                  "topk": ["topk.hip", "dsa_device.h"]}
+                  "topk": ["topk.hip", "topk_select.h", "dsa_device.h"]}
 
 
 def source_digest(stage):
