@@ -60,7 +60,7 @@ def parse():
 TRAFFIC = {
     (1, "sparse_mla"): {"src": "0763ddd7d7210be3", "fetch_bytes": 1.660e+08, "write_bytes": 9.525e+06,
                         "dispatches": 42},
-    (1, "index_scores"): {"src": "a5ac9e58e91bff31", "fetch_bytes": 8.103e+07, "write_bytes": 1.183e+06,
+    (1, "index_scores"): {"src": "3570f397d9d52e58", "fetch_bytes": 8.103e+07, "write_bytes": 1.183e+06,
                           "dispatches": 42},
     (1, "topk"): {"src": "aba5a8fcb705a592", "fetch_bytes": 1.460e+06, "write_bytes": 5.243e+05,
                   "dispatches": 42},

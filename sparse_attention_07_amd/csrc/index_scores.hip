@@ -6,11 +6,12 @@
 // "Changes", and of mlx-lm PR 1419's description; the pages name the
 // indexer without a formula and this is its plain reading.)
 //
-// MFMA kernel (bf16, 64 heads x 128 dims).  A workgroup of four waves owns one
-// request, a chunk of 512 consecutive cached tokens (chunk index outermost in
-// the grid, so that requests' empty tails dispatch last) and a group of up to
-// eight consecutive query rows of that request.  Each wave walks two blocks
-// of 64 tokens; a block's keys are loaded straight from their pages into
+// MFMA kernels (bf16, 64 heads x 128 dims).  The grid form (kept for
+// launches the persistent form below cannot stage): a workgroup of four waves
+// owns one request, a chunk of 512 consecutive cached tokens (chunk index
+// outermost in the grid, so that requests' empty tails dispatch last) and a
+// group of up to eight consecutive query rows of that request.  Each wave
+// walks two blocks of 64 tokens; a block's keys are loaded straight from their pages into
 // registers, already in the B-operand layout of v_mfma_f32_32x32x16_bf16, and
 // used for every row of the group (two waves per SIMD hide each other's load
 // latency).  The group's query rows sit in LDS (copied in with
@@ -193,13 +194,16 @@ __global__ __launch_bounds__(kThreads, 2) void index_scores_bf16_mfma(
   }
 }
 
-// Persistent form for decode and draft batches (at most 8 rows per request):
-// one workgroup of eight waves per CU, each taking an equal share of all
-// requests' 64-token key blocks (concatenated request after request), so no
-// workgroup of the grid is empty and none waits for a second round.  The
-// share is walked in segments of one request: the request's query rows are
-// staged in LDS, then wave w scores blocks w, w+8, ... of the segment with the
-// page lookups two blocks ahead and the key loads one block ahead.
+// Persistent form, used for every batch: one workgroup of eight waves per CU.
+// A request's query rows are cut into units of up to rg consecutive rows (the
+// whole draft at decode, four rows of a prefill chunk); a unit's work is the
+// 64-token key blocks up to its last row's position.  Each workgroup takes an
+// equal share of all units' blocks (concatenated unit after unit), so no
+// workgroup is empty and none waits for a second round.  The share is walked
+// in segments of one unit: the unit's query rows and weights are staged in LDS
+// (all units of the share at once when they fit), then wave w scores blocks
+// w, w+8, ... of the segment with the page lookups two blocks ahead and the
+// key loads one block ahead.
 constexpr int kFlatWaves = 8;
 constexpr int kFlatThreads = kFlatWaves * kWave;
 
