@@ -353,6 +353,19 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
   while (lo < end) {
     const int hi = all_staged ? end : min(end, pre[u0 + 1]);
     const int u_hi = all_staged ? u_last : u0;
+    // This wave's blocks lo + wave + 8 i < hi.  A, B, C: the block being scored
+    // and the next two (keys of B in flight, page lookups of C in flight).  The
+    // first two blocks' page lookups and A's keys go out before the staging
+    // copies, so waiting for them does not also wait for the copies.
+    int j = lo + wave;
+    FlatBlock A{u0, 0, {-1, -1}}, Bk{u0, 0, {-1, -1}}, C{u0, 0, {-1, -1}};
+    if (j < hi) prep_block(A, j, u0, pre, unr, upf, ub, ld_last, page_table, pt_stride, page_size,
+                           num_pages, k_page_stride, k_row_stride, lane);
+    Keys k0, k1;
+    load_keys(k0, A.off, k_base, lane);
+    if (j + kFlatWaves < hi)
+      prep_block(Bk, j + kFlatWaves, A.u, pre, unr, upf, ub, ld_last, page_table, pt_stride,
+                 page_size, num_pages, k_page_stride, k_row_stride, lane);
     for (int uu = u0; uu <= u_hi; ++uu) {  // query rows and weights -> LDS slot uu - u0
       const int q0 = uq0[uu], nr = unr[uu];
       uint8_t* qd = q_area + (size_t)(uu - u0) * rg * kRowBytesLds;
@@ -371,18 +384,15 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
         if (base + tid < nr * (kHeads / 4)) copy16_to_lds(wsrc + (base + tid) * 16, wd + (base + wave * kWave) * 16);
     }
 
-    // This wave's blocks lo + wave + 8 i < hi.  A, B, C: the block being scored
-    // and the next two (keys of B in flight, page lookups of C in flight).
-    int j = lo + wave;
-    FlatBlock A{u0, 0, {-1, -1}}, Bk{u0, 0, {-1, -1}}, C{u0, 0, {-1, -1}};
-    if (j < hi) prep_block(A, j, u0, pre, unr, upf, ub, ld_last, page_table, pt_stride, page_size,
-                           num_pages, k_page_stride, k_row_stride, lane);
-    if (j + kFlatWaves < hi)
-      prep_block(Bk, j + kFlatWaves, A.u, pre, unr, upf, ub, ld_last, page_table, pt_stride,
-                 page_size, num_pages, k_page_stride, k_row_stride, lane);
-    Keys k0, k1;
-    load_keys(k0, A.off, k_base, lane);
-    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // staging copies and page lookups have landed
+    // B's keys go out after the copies: the wait below covers the copies (and
+    // everything issued before them) but not B's 16 key loads.
+    const bool has_b = j + kFlatWaves < hi;
+    if (has_b) {
+      load_keys(k1, Bk.off, k_base, lane);
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     lds_barrier();
 
 #define DSA_SCORE(KK, X)                                                                           \
@@ -390,9 +400,8 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
               w_area + (size_t)(X.u - u0) * rg * kHeads, unr[X.u], X.tok, upf[X.u], ld_last, scores, \
               uq0[X.u], ld, lane)
     while (j < hi) {
-      // block j with k0, block j + 8 with k1
+      // block j with k0 (loaded), block j + 8 with k1 (in flight)
       const bool has1 = j + kFlatWaves < hi;
-      if (has1) load_keys(k1, Bk.off, k_base, lane);
       if (j + 2 * kFlatWaves < hi)
         prep_block(C, j + 2 * kFlatWaves, Bk.u, pre, unr, upf, ub, ld_last, page_table, pt_stride,
                    page_size, num_pages, k_page_stride, k_row_stride, lane);
@@ -411,6 +420,7 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
       j += kFlatWaves;
       A = Bk;
       Bk = C;
+      if (j + kFlatWaves < hi) load_keys(k1, Bk.off, k_base, lane);
     }
 #undef DSA_SCORE
     lds_barrier();  // every wave is done with the staged rows

@@ -385,7 +385,7 @@ __device__ inline void store_partials(const MlaArgs& a, int t, int grp, int n_gr
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const float lh = __shfl(l_run, 4 * g + r);  // lane h holds head h's l
-    inv[r] = lh > 0.f ? 1.f / lh : 0.f;
+    inv[r] = lh > 0.f ? __builtin_amdgcn_rcpf(lh) : 0.f;
   }
 #pragma unroll
   for (int i2 = 0; i2 < TILES; ++i2) {
@@ -427,7 +427,8 @@ __device__ inline void merge_splits_if_last(const MlaArgs& a, int t, int grp, in
   const int S = a.splits, h0 = grp * kNh;
   const __amdgpu_buffer_rsrc_t rs = split_blocks(a, t, grp, n_groups, kNh);
   constexpr int kStride = kPartBytes(kNh);
-  // Issue the first round of O loads before the statistics are reduced.
+  // The statistics are loaded first and the first round of O loads right
+  // after them, so the weights are computed while O is in flight.
   // 16-byte chunks of O per split; 1024 of them per load round
   constexpr int kIt = 1024 / NT, kSp = 8, kChunks = kNh * kDc * 2 / 16;
   u32x4 v[kIt][kSp];
@@ -439,13 +440,24 @@ __device__ inline void merge_splits_if_last(const MlaArgs& a, int t, int grp, in
         if (s0 + s < S)
           v[u][s] = __builtin_amdgcn_raw_buffer_load_b128(rs, (s0 + s) * kStride + (c0 + u * kThreads) * 16, 0, kSc1);
   };
-  issue(tid, 0);
   float* ls = wgt + kNh * S;
-  for (int i = tid; i < kNh * S; i += kThreads) {  // i = h * S + s
-    const int off = (i % S) * kStride + kNh * kDc * 2 + 8 * (i / S);
-    const uint2 ml = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kSc1));
-    wgt[i] = __uint_as_float(ml.x);
-    ls[i] = __uint_as_float(ml.y);
+  constexpr int kStatIt = (kNh * 64 + kThreads - 1) / kThreads;  // S <= 64
+  uint2 ml[kStatIt];
+#pragma unroll
+  for (int k = 0; k < kStatIt; ++k) {  // i = h * S + s
+    const int i = tid + k * kThreads;
+    ml[k] = i < kNh * S ? __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                        rs, (i % S) * kStride + kNh * kDc * 2 + 8 * (i / S), 0, kSc1))
+                        : uint2{0u, 0u};
+  }
+  issue(tid, 0);
+#pragma unroll
+  for (int k = 0; k < kStatIt; ++k) {
+    const int i = tid + k * kThreads;
+    if (i < kNh * S) {
+      wgt[i] = __uint_as_float(ml[k].x);
+      ls[i] = __uint_as_float(ml[k].y);
+    }
   }
   __syncthreads();
   // Merge weight of (head h, split s): l_s exp2(m_s - M) / L, one thread per pair.
@@ -461,9 +473,9 @@ __device__ inline void merge_splits_if_last(const MlaArgs& a, int t, int grp, in
       for (int s = 0; s < S; ++s) M = fmaxf(M, mh[s]);
       float L = 0.f;
       if (M != kNegInf)
-        for (int s = 0; s < S; ++s) L += exp2f(mh[s] - M) * lh[s];  // empty split: 0
+        for (int s = 0; s < S; ++s) L += exp2_fast(mh[s] - M) * lh[s];  // empty split: 0
       const float ms = mh[i % S];
-      wnew[k] = L > 0.f ? exp2f(ms - M) * lh[i % S] / L : 0.f;
+      wnew[k] = L > 0.f ? exp2_fast(ms - M) * lh[i % S] / L : 0.f;
       if (i % S == 0 && a.lse != nullptr)
         a.lse[(int64_t)t * a.H + h0 + h] = L > 0.f ? (M + __log2f(L)) * kLn2 : kNegInf;
     }
@@ -475,25 +487,26 @@ __device__ inline void merge_splits_if_last(const MlaArgs& a, int t, int grp, in
   __syncthreads();
   // Chunk c holds lanes 2m, 2m+1 (m = c % 32) of tile (c / 32) % kTiles of
   // wave c / (32 kTiles): heads hb..hb+3 at columns col, col+1.  A thread's
-  // chunks c0 + 256 u all share m, so for one wave their heads differ only by
-  // wave (wide) -- the weights of the thread's heads are read once per round.
+  // chunks c0 + NT u (u < kIt) share m and, as NT kIt is 1024 = 32 kTiles
+  // (wide) or the heads do not depend on the wave, also hb: the weights of
+  // the thread's heads are read once per round.
+  static_assert(!WIDE || kThreads * kIt == 32 * kTiles, "one wave slot per round");
   for (int c0 = tid; c0 < kChunks; c0 += kThreads * kIt) {
     float acc[kIt][8];
 #pragma unroll
     for (int u = 0; u < kIt; ++u)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[u][e] = 0.f;
+    const int hb = (WIDE ? 16 * (c0 / (32 * kTiles)) : 0) + 4 * ((2 * (c0 & 31)) >> 4);
     for (int s0 = 0; s0 < S; s0 += kSp) {
       if (c0 != tid || s0 != 0) issue(c0, s0);
+      float wt[4][kSp];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int s = 0; s < kSp; ++s) wt[r][s] = s0 + s < S ? wgt[(hb + r) * S + s0 + s] : 0.f;
 #pragma unroll
       for (int u = 0; u < kIt; ++u) {
-        const int c = c0 + u * kThreads, lane = 2 * (c & 31), w = c / (32 * kTiles);
-        const int hb = (WIDE ? 16 * w : 0) + 4 * (lane >> 4);
-        float wt[4][kSp];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-          for (int s = 0; s < kSp; ++s) wt[r][s] = s0 + s < S ? wgt[(hb + r) * S + s0 + s] : 0.f;
 #pragma unroll
         for (int s = 0; s < kSp; ++s) {
           if (s0 + s < S) {
