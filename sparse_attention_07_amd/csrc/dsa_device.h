@@ -54,6 +54,18 @@ __device__ inline RowLoc locate_row(const int32_t* __restrict__ cu_q,
   return RowLoc{B - 1, seq_lens[B - 1] - (q1 - q0) + (t - q0)};
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts inside
+// each row of 16 lanes, then row broadcasts of lanes 15 and 31).
+__device__ inline uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
 // Byte offset of logical token s of request b inside a pool, or -1 when the
 // token is not mapped (negative s, logical page beyond the table, or a page
 // id outside [0, num_pages)).

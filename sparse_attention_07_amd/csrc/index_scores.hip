@@ -257,12 +257,7 @@ __device__ inline void prep_block(FlatBlock& x, int blk, int u_from, const int* 
 // Block exclusive scan over the workgroup of one int per thread (carry added);
 // returns this thread's exclusive prefix and adds the total to carry.
 __device__ inline int flat_excl_scan(int v, int* wsum, int& carry, int lane, int wave) {
-  int x = v;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
+  const int x = (int)wave_incl_scan((uint32_t)v);
   if (lane == kWave - 1) wsum[wave] = x;
   __syncthreads();
   int before = carry, all = 0;
@@ -300,22 +295,36 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int64_t ld_last = ld - 1;
 
-  // 1. Units: runs of up to rg consecutive rows of one request.
+  // 1. Units: runs of up to rg consecutive rows of one request.  When no
+  //    request has more than rg rows (decode, drafts), unit u is request u
+  //    (a request without rows is an empty unit) and no scan is needed.
+  const bool per_request = u_max == B;
   int n_units = 0;
-  for (int c0 = 0; c0 < B; c0 += kFlatThreads) {
-    const int bb = c0 + tid;
-    int nu = 0;
-    if (bb < B) {
-      const int q0 = cu_q[bb], ql = cu_q[bb + 1] - q0;
+  if (per_request) {
+    for (int bb = tid; bb < B; bb += kFlatThreads) {
+      const int q0 = cu_q[bb];
       rq0[bb] = q0;
-      rql[bb] = ql;
+      rql[bb] = cu_q[bb + 1] - q0;
       rsl[bb] = seq_lens[bb];
-      nu = ql > 0 ? (ql + rg - 1) / rg : 0;
+      ubase[bb] = bb;
     }
-    const int e = flat_excl_scan(nu, wsum, n_units, lane, wave);
-    if (bb < B) ubase[bb] = e;
+    n_units = B;
+  } else {
+    for (int c0 = 0; c0 < B; c0 += kFlatThreads) {
+      const int bb = c0 + tid;
+      int nu = 0;
+      if (bb < B) {
+        const int q0 = cu_q[bb], ql = cu_q[bb + 1] - q0;
+        rq0[bb] = q0;
+        rql[bb] = ql;
+        rsl[bb] = seq_lens[bb];
+        nu = ql > 0 ? (ql + rg - 1) / rg : 0;
+      }
+      const int e = flat_excl_scan(nu, wsum, n_units, lane, wave);
+      if (bb < B) ubase[bb] = e;
+    }
+    n_units = min(n_units, u_max);  // rows beyond the host bound are not scored
   }
-  n_units = min(n_units, u_max);  // rows beyond the host bound are not scored
   if (tid == 0) ubase[B] = n_units;
   __syncthreads();
   // 2. Per unit: rows, position, and its 64-token blocks, ceil(min(pos_last + 1, ld) / 64).
@@ -324,7 +333,7 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
     const int u = c0 + tid;
     int nb = 0;
     if (u < n_units) {
-      const int b = last_at_or_below(ubase, B, u), j = u - ubase[b];
+      const int b = per_request ? u : last_at_or_below(ubase, B, u), j = u - ubase[b];
       const int nr = min(rg, rql[b] - rg * j);
       const int pf = rsl[b] - rql[b] + rg * j;
       uq0[u] = rq0[b] + rg * j;
@@ -332,7 +341,7 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
       upf[u] = pf;
       ub[u] = b;
       const int64_t n = min<int64_t>((int64_t)pf + nr, ld);
-      nb = n > 0 ? (int)((n + kKeysPerStep - 1) / kKeysPerStep) : 0;
+      nb = (nr > 0 && n > 0) ? (int)((n + kKeysPerStep - 1) / kKeysPerStep) : 0;  // an empty unit has none
     }
     const int e = flat_excl_scan(nb, wsum, carry, lane, wave);
     if (u < n_units) pre[u] = e;

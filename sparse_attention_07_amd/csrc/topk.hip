@@ -24,9 +24,11 @@ __device__ inline void select_row(const float* __restrict__ row, int n, int K, i
                                   uint32_t* cache, uint32_t* hist, uint32_t* wcount, uint32_t* pick) {
   const bool vec = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
   const topk::Threshold th = topk::select<kThreads, Cached>(row, vec, n, K, cache, hist, pick);
-  topk::compact<kThreads, Cached>(row, vec, n, cache, th, wcount, [out, K](uint32_t o, int s) {
+  auto emit = [out, K](uint32_t o, int s) {
     if (o < (uint32_t)K) out[o] = s;
-  });
+  };
+  if (Cached) topk::compact_cached<kThreads>(n, cache, th, wcount, emit);
+  else topk::compact<kThreads, Cached>(row, vec, n, cache, th, wcount, emit);
 }
 
 __global__ __launch_bounds__(kThreads) void topk_radix(const int32_t* __restrict__ cu_q,

@@ -40,18 +40,6 @@ __device__ inline uint32_t order_key(float f) {
 // reads).
 __device__ inline int hslot(uint32_t bin) { return (int)(bin + (bin >> 5) * 4); }
 
-// Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts inside
-// each row of 16 lanes, then row broadcasts of lanes 15 and 31).
-__device__ inline uint32_t wave_incl_scan(uint32_t x) {
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr:1
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr:2
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);  // row_shr:4
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);  // row_shr:8
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
-  return x;
-}
-
 __device__ inline uint32_t wave_sum(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(x), kWave - 1);
 }
@@ -102,6 +90,11 @@ __device__ inline f32x4 load_quad(const float* __restrict__ row, int q, int n, b
 
 __device__ inline u32x4 quad_keys(f32x4 v) {
   return u32x4{order_key(v[0]), order_key(v[1]), order_key(v[2]), order_key(v[3])};
+}
+
+// Lanes below this one whose bit is set in m.
+__device__ inline uint32_t lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 struct Threshold {
@@ -272,6 +265,65 @@ __device__ inline void compact(const float* __restrict__ row, bool vec, int n, c
     }
   }
   __syncthreads();  // wcount may be rewritten by the next compaction
+}
+
+// compact() for a row cached in LDS as keys, in one walk of the row: each
+// wave stages the positions of its range's elements above or at the
+// threshold prefix in its own part of the cache (tagged by bit 31 when at
+// it; the staged count never passes the positions already read, so it
+// overwrites only keys already consumed), then, once the waves' counts are
+// known, walks its staged list to apply the global cut among the elements at
+// the prefix and emit.  Same result as compact().
+template <int NT, typename Emit>
+__device__ inline void compact_cached(int n, uint32_t* cache, Threshold th, uint32_t* wcount, Emit emit) {
+  constexpr int kW = NT / kWave;
+  constexpr int kBatch = 8;  // 64-position steps in flight
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int R = ((n + kW - 1) / kW + kWave - 1) / kWave * kWave;
+  const int r0 = wave * R, r1 = min(n, r0 + R);
+  uint32_t n_gt = 0, n_eq = 0, n_st = 0;  // wave-uniform
+  for (int c = r0; c < r1; c += kBatch * kWave) {
+    uint32_t u[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int s = c + b * kWave + lane;
+      u[b] = s < r1 ? cache[s] & th.mask : 0u;
+    }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int s = c + b * kWave + lane;
+      const bool in = s < r1;
+      const bool gt = in && u[b] > th.prefix, eq = in && u[b] == th.prefix;
+      const uint64_t mg = __ballot(gt), me = __ballot(eq), m = mg | me;
+      if (gt || eq) cache[r0 + n_st + lanes_below(m)] = (uint32_t)s | (eq ? 0x80000000u : 0u);
+      n_st += (uint32_t)__popcll(m);
+      n_gt += (uint32_t)__popcll(mg);
+      n_eq += (uint32_t)__popcll(me);
+    }
+  }
+  if (lane == 0) {
+    wcount[wave] = n_gt;
+    wcount[kW + wave] = n_eq;
+  }
+  __syncthreads();
+  uint32_t gt_before = 0, run_eq = 0;
+  for (int w = 0; w < wave; ++w) {
+    gt_before += wcount[w];
+    run_eq += wcount[kW + w];
+  }
+  uint32_t run_sel = gt_before + min(run_eq, th.need);
+  for (uint32_t i0 = 0; i0 < n_st; i0 += kWave) {
+    const bool in = i0 + lane < n_st;
+    const uint32_t e = in ? cache[r0 + i0 + lane] : 0u;
+    const bool at = in && (e >> 31) != 0u;
+    const uint64_t meq = __ballot(at);
+    const bool sel = in && (!at || run_eq + lanes_below(meq) < th.need);
+    const uint64_t msel = __ballot(sel);
+    if (sel) emit(run_sel + lanes_below(msel), (int)(e & 0x7FFFFFFFu));
+    run_sel += (uint32_t)__popcll(msel);
+    run_eq += (uint32_t)__popcll(meq);
+  }
+  __syncthreads();  // wcount and the cache may be rewritten by the next row
 }
 
 }  // namespace topk
