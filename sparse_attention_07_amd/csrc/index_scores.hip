@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kThreads, 2) void index_scores_bf16_mfma(
 
 // Persistent form, used for every batch: one workgroup of eight waves per CU.
 // A request's query rows are cut into units of up to rg consecutive rows (the
-// whole draft at decode, four rows of a prefill chunk); a unit's work is the
+// whole draft at decode, eight rows of a prefill chunk); a unit's work is the
 // 64-token key blocks up to its last row's position.  Each workgroup takes an
 // equal share of all units' blocks (concatenated unit after unit), so no
 // workgroup is empty and none waits for a second round.  The share is walked
@@ -478,10 +478,11 @@ hipError_t launch_index_scores_bf16(const BatchArgs& ba, const void* q_idx, cons
                                     const PoolArgs& pool, float* scores, int64_t ld,
                                     hipStream_t stream) {
   if (ba.max_q_len >= 1) {
-    // Units of up to rg rows (the whole draft for decode-sized q_len, four
-    // rows for long prefill chunks); up to 8 units staged at once, as many as
-    // fit next to the tables.
-    const int rg = ba.max_q_len <= 8 ? ba.max_q_len : 4;
+    // Units of up to rg rows (the whole draft for decode-sized q_len, eight
+    // rows -- the most whose query rows fit in LDS -- for long prefill chunks,
+    // so each key block loaded serves eight rows); up to 8 units staged at
+    // once, as many as fit next to the tables.
+    const int rg = ba.max_q_len <= 8 ? ba.max_q_len : 8;
     const int64_t u_max = (int64_t)ba.batch * ((ba.max_q_len + rg - 1) / rg);
     const size_t tables = ((size_t)(4 * (int64_t)ba.batch + 1 + 5 * u_max + 1 + kFlatWaves) * sizeof(int) + 15) / 16 * 16;
     const size_t per_unit = (size_t)rg * (kRowBytesLds + kHeads * sizeof(float));
