@@ -58,11 +58,11 @@ def parse():
 # counters were taken -- a changed kernel reports traffic null.
 # Copy calibration of those runs: FETCH_SIZE x 2.000, WRITE_SIZE x 1.000.
 TRAFFIC = {
-    (1, "sparse_mla"): {"src": "0763ddd7d7210be3", "fetch_bytes": 1.660e+08, "write_bytes": 9.525e+06,
+    (1, "sparse_mla"): {"src": "6b3d0888b9427560", "fetch_bytes": 1.659e+08, "write_bytes": 9.525e+06,
                         "dispatches": 42},
-    (1, "index_scores"): {"src": "3570f397d9d52e58", "fetch_bytes": 8.103e+07, "write_bytes": 1.183e+06,
+    (1, "index_scores"): {"src": "3548ffd6fdfc2fe4", "fetch_bytes": 8.102e+07, "write_bytes": 1.183e+06,
                           "dispatches": 42},
-    (1, "topk"): {"src": "aba5a8fcb705a592", "fetch_bytes": 1.460e+06, "write_bytes": 5.243e+05,
+    (1, "topk"): {"src": "3d28ab2f22b00af9", "fetch_bytes": 1.408e+06, "write_bytes": 5.243e+05,
                   "dispatches": 42},
 }
 KERNEL_SOURCES = {"sparse_mla": ["sparse_mla.hip", "dsa_device.h"],
