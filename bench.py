@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--sets", type=int, default=0, help="input sets rotated (0 = auto)")
     ap.add_argument("--mode", default="perf", choices=["perf", "parity"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--key-fp8", action="store_true",
+                    help="indexer keys cached as e4m3 codes with one f32 scale per token "
+                         "(queries stay bf16); reports the top-k overlap with bf16 keys")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (f32 multiply by 1) four times, the "
                          "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
@@ -54,15 +57,15 @@ def parse():
 # HBM traffic of the dominant kernel per launch, from two rocprofv3 --pmc passes
 # (FETCH_SIZE, then WRITE_SIZE) over `bench.py --no-cpu --steps 8 --warmup 2`,
 # each counter scaled by bytes / counter-bytes of the copy calibration kernel.
-# Keyed by workload; `src` is the sha256 of the kernel's sources when the
+# Keyed by (workload name, stage); `src` is the sha256 of the kernel's sources when the
 # counters were taken -- a changed kernel reports traffic null.
 # Copy calibration of those runs: FETCH_SIZE x 2.000, WRITE_SIZE x 1.000.
 TRAFFIC = {
-    (1, "sparse_mla"): {"src": "6b3d0888b9427560", "fetch_bytes": 1.659e+08, "write_bytes": 9.525e+06,
+    ("decode16", "sparse_mla"): {"src": "6b3d0888b9427560", "fetch_bytes": 1.659e+08, "write_bytes": 9.525e+06,
                         "dispatches": 42},
-    (1, "index_scores"): {"src": "3548ffd6fdfc2fe4", "fetch_bytes": 8.102e+07, "write_bytes": 1.183e+06,
+    ("decode16", "index_scores"): {"src": "3548ffd6fdfc2fe4", "fetch_bytes": 8.102e+07, "write_bytes": 1.183e+06,
                           "dispatches": 42},
-    (1, "topk"): {"src": "3d28ab2f22b00af9", "fetch_bytes": 1.408e+06, "write_bytes": 5.243e+05,
+    ("decode16", "topk"): {"src": "3d28ab2f22b00af9", "fetch_bytes": 1.408e+06, "write_bytes": 5.243e+05,
                   "dispatches": 42},
 }
 KERNEL_SOURCES = {"sparse_mla": ["sparse_mla.hip", "dsa_device.h"],
@@ -79,10 +82,10 @@ def source_digest(stage):
     return h.hexdigest()[:16]
 
 
-def traffic(cfg_id, stage):
+def traffic(workload, stage):
     """Measured HBM bytes per launch (fetch + write), or None if not measured for
     this workload or the kernel's sources changed since."""
-    tr = TRAFFIC.get((cfg_id, stage))
+    tr = TRAFFIC.get((workload, stage))
     if tr is None or tr["src"] != source_digest(stage):
         return None
     return tr["fetch_bytes"] + tr["write_bytes"]
@@ -108,9 +111,11 @@ def algorithmic(sb, path):
     n_scored = int((pos + 1).sum())
     idx_es = 2 if cfg.idx_fmt == 1 else 4
     q_es = 2 if cfg.q_fmt == 1 else 4
+    # a cached key: di elements, or di e4m3 codes plus one f32 scale
+    key_bytes = cfg.di + 4 if cfg.key_fmt == 2 else cfg.di * idx_es
     st = {}
     st["index_scores"] = dict(
-        bytes=int(sum(sb.seq_lens)) * cfg.di * idx_es + T * cfg.hi * cfg.di * idx_es + T * cfg.hi * 4
+        bytes=int(sum(sb.seq_lens)) * key_bytes + T * cfg.hi * cfg.di * idx_es + T * cfg.hi * 4
         + n_scored * 4,
         flops=n_scored * 2 * cfg.hi * cfg.di)
     st["topk"] = dict(bytes=n_scored * 4 + T * K * 4, flops=0)
@@ -129,6 +134,25 @@ def algorithmic(sb, path):
                             flops=n_valid * cfg.heads * 2 * (cfg.dc + cfg.dr + cfg.dc) * len(sb.q),
                             launches_per_step=len(sb.q))
     return st
+
+
+def key_fp8_overlap(path, cfg_id, mode):
+    """Mean fraction of each row's selected tokens that stay selected when the
+    same key draws are cached in bf16 instead of fp8 (input set 0)."""
+    from sparse_attention_07_amd import synth
+    from sparse_attention_07_amd.path import DSAPath
+    ref = DSAPath(synth.make_batch(cfg_id, mode=mode, device=path.sb.q_idx.device, layers=0))
+    ref.index_scores()
+    ref.topk()
+    path.index_scores()
+    path.topk()
+    torch.cuda.synchronize()
+    a, b = path.idx.cpu().numpy(), ref.idx.cpu().numpy()
+    frac = []
+    for x, y in zip(a, b):
+        x, y = x[x >= 0], y[y >= 0]
+        frac.append(len(np.intersect1d(x, y)) / max(1, len(y)))
+    return float(np.mean(frac))
 
 
 def cpu_baseline(cfg_id, budget_s=20.0):
@@ -173,8 +197,10 @@ def main():
     torch.cuda.set_device(dev)
     paths = []
     for i in range(sets):
-        sb = synth.make_batch(cfg_id, mode=args.mode, device=dev, seed_offset=i)
+        sb = synth.make_batch(cfg_id, mode=args.mode, device=dev, seed_offset=i,
+                              key_fmt=synth.FMT_FP8_E4M3_B128 if args.key_fp8 else None)
         paths.append(DSAPath(sb))
+    workload = base.name + ("+fp8keys" if args.key_fp8 else "")
     torch.cuda.synchronize()
 
     stages = ["index_scores", "topk", "sparse_mla"]
@@ -262,7 +288,7 @@ def main():
                      "GB_s": by / t / 1e9, "TFLOP_s": fl / t / 1e12,
                      "frac_hbm": by / t / 1e9 / HBM_PEAK_GBS,
                      "frac_mfma": fl / t / 1e12 / MFMA_BF16_PEAK_TFS,
-                     "traffic": traffic(cfg_id, s)}
+                     "traffic": traffic(workload, s)}
     dom = max(stages, key=lambda s: stage_ms[s])
     r = report[dom]
     t_hbm = r["alg_bytes"] / (HBM_PEAK_GBS * 1e9)
@@ -297,7 +323,8 @@ def main():
                                % (cfg.name, cfg.batch, cfg.q_len, cfg.ctx_lo, cfg.ctx_hi, cfg.topk,
                                   cfg.hi, cfg.di, cfg.heads, cfg.dc, cfg.dr,
                                   {0: "f32", 1: "bf16", 2: "fp8-e4m3-b128"}[cfg.kv_fmt],
-                                  cfg.page_size, cfg.layers),
+                                  cfg.page_size, cfg.layers)
+                               + (", fp8 index keys (per-token scale)" if args.key_fp8 else ""),
                    "query_rows": T},
         "indexer_topk_rows_per_s": T / ((stage_ms["index_scores"] + stage_ms["topk"]) / 1e3),
         "sparse_mla_queries_per_s": T / (stage_ms["sparse_mla"] / len(paths[0].kv) / 1e3),
@@ -308,7 +335,9 @@ def main():
         "stages": report,
         "roofline": roof,
     }
-    if not args.no_cpu:
+    if args.key_fp8:
+        out["topk_overlap_vs_bf16_keys"] = key_fp8_overlap(paths[0], cfg_id, args.mode)
+    if not args.no_cpu and not args.key_fp8:
         out["cpu_baseline"] = cpu_baseline(cfg_id)
     print(json.dumps(out), flush=True)
 

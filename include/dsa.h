@@ -72,11 +72,14 @@ typedef int32_t dsa_status;
 /* Element formats. */
 #define DSA_F32 0
 #define DSA_BF16 1
-/* 656-byte latent rows: 512 OCP e4m3fn bytes (latent dims 0..511), four
- * little-endian f32 scales (scale i multiplies dims 128*i..128*i+127), then
- * the 64 rope dims as bf16.  Value = e4m3(byte) * scale.  Only valid for the
- * MLA latent pool with dc = 512, dr = 64 (the BF16/FP8 sparse cache paths of
- * lmdeploy PR 4737, section "Changes"; the block layout is this library's). */
+/* OCP e4m3fn values with an f32 scale per 128 elements; value = e4m3(byte) *
+ * scale.  For the MLA latent pool (dc = 512, dr = 64): 656-byte rows of 512
+ * e4m3 bytes (latent dims 0..511), four little-endian f32 scales (scale i
+ * multiplies dims 128*i..128*i+127), then the 64 rope dims as bf16 (the
+ * BF16/FP8 sparse cache paths of lmdeploy PR 4737, section "Changes"; the
+ * block layout is this library's).  For an indexer key pool (dim 128): 128
+ * codes per token and one scale per token, page-blocked (see
+ * dsa_index_scores). */
 #define DSA_FP8_E4M3_B128 2
 
 /* A ragged batch of B requests and T = cu_q_lens[B] query rows. */
@@ -118,11 +121,18 @@ const char *dsa_status_string(dsa_status status);
  *
  * q_idx    device [T, n_heads, head_dim], format q_format, contiguous
  * w        device [T, n_heads] f32 (any extra scale is folded in by the caller)
- * k_idx    indexer key pool, dim == head_dim, format == q_format
+ * k_idx    indexer key pool, dim == head_dim, format == q_format -- or, with
+ *          bf16 queries, DSA_FP8_E4M3_B128 keys: each page holds page_size
+ *          rows of 128 e4m3fn codes (row_stride_bytes apart, a multiple of
+ *          16, >= 128), followed at byte page_size*row_stride_bytes of the
+ *          page by page_size little-endian f32 scales, one per token;
+ *          k(s) = code * scale.  Scales must be non-negative (a quantiser's
+ *          amax/448 is); page_stride_bytes >= page_size*(row_stride_bytes+4).
+ *          (The FP8 index keys of the pages' "next" items: half the key bytes.)
  * scores   device [T, ld] f32, ld >= max_seq_len.  Entries s > pos(t), and
  *          entries of tokens whose page is not mapped, are NOT written.
- * Built combinations: (DSA_BF16, n_heads 64, head_dim 128) on MFMA;
- * (DSA_F32, n_heads <= 64, head_dim <= 256) on the vector ALUs.
+ * Built combinations: (DSA_BF16, n_heads 64, head_dim 128) on MFMA, with bf16
+ * or fp8 keys; (DSA_F32, n_heads <= 64, head_dim <= 256) on the vector ALUs.
  */
 dsa_status dsa_index_scores(const dsa_batch *batch, const void *q_idx, int32_t q_format,
                             const float *w, const dsa_pool *k_idx, int32_t n_heads,

@@ -18,6 +18,8 @@ Parity status of each function (what pins it; see tests/test_oracle_pins.py):
   sparse_mla    pinned: dense invariant below K vs torch SDPA, absorption
                 identity, mask equivalence, closed forms (K=1, q=0), re-masking
   e4m3 decode   pinned: all 256 codes against torch.float8_e4m3fn
+  fp8 index keys (page-blocked codes + per-token scales) pinned: a hand-built
+                page decoded against values written out by hand
 """
 from __future__ import annotations
 
@@ -65,6 +67,7 @@ def _load():
         lib.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
         lib.oracle_e4m3_to_double.restype = ctypes.c_double
         lib.oracle_decode_fp8_rows.argtypes = [ctypes.c_void_p, c_i64, c_int, c_int, f64p]
+        lib.oracle_decode_fp8_keys.argtypes = [ctypes.c_void_p, c_i64, c_int, c_int, c_i64, c_i64, f64p]
         for f in (lib.oracle_index_scores, lib.oracle_topk, lib.oracle_sparse_mla):
             f.restype = c_int
         lib.oracle_threads.restype = c_int
@@ -135,7 +138,10 @@ def index_scores(batch, rows=None, ld=None):
     ld = ld or max(batch.max_seq_len, 1)
     q = _f64(v.per_row(batch.q_idx))
     w = _f64(v.per_row(batch.w))
-    k = _f64(v.pool(batch.k_pool))
+    if cfg.key_fmt == FMT_FP8:  # page-blocked fp8 keys: decoded to doubles first
+        k = decode_fp8_keys(v.pool(batch.k_pool), cfg.page_size, cfg.di)
+    else:
+        k = _f64(v.pool(batch.k_pool))
     out = np.full((v.n, ld), np.nan, dtype=np.float64)
     st = lib.oracle_index_scores(batch.B, _p(v.cu_q, ctypes.c_int32), _p(v.seq_lens, ctypes.c_int32),
                                  _p(v.page_table, ctypes.c_int32), v.pt_stride, cfg.page_size,
@@ -217,6 +223,21 @@ def decode_fp8_rows(rows_u8, dc=512, dr=64):
     a = a.reshape(-1, 656)
     out = np.empty((a.shape[0], dc + dr), dtype=np.float64)
     lib.oracle_decode_fp8_rows(a.ctypes.data_as(ctypes.c_void_p), a.shape[0], dc, dr,
+                               _p(out, ctypes.c_double))
+    return out
+
+
+def decode_fp8_keys(pages_u8, page_size, di=128, row_stride=128):
+    """Decode page-blocked fp8 index keys ([num_pages, page_size*(row_stride+4)]
+    bytes) into float64 [num_pages * page_size, di] with the oracle's decoder."""
+    lib = _load()
+    if isinstance(pages_u8, torch.Tensor):
+        pages_u8 = pages_u8.detach().cpu().numpy()
+    a = np.ascontiguousarray(pages_u8, dtype=np.uint8)
+    n = a.shape[0]
+    a = a.reshape(n, -1)
+    out = np.empty((n * page_size, di), dtype=np.float64)
+    lib.oracle_decode_fp8_keys(a.ctypes.data_as(ctypes.c_void_p), n, page_size, di, row_stride, a.shape[1],
                                _p(out, ctypes.c_double))
     return out
 

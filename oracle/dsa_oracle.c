@@ -303,6 +303,23 @@ void oracle_decode_fp8_rows(const uint8_t *rows, int64_t n_rows, int Dc, int Dr,
   for (int64_t r = 0; r < n_rows; ++r) decode_fp8_row(rows + r * 656, Dc, Dr, dst + r * (Dc + Dr));
 }
 
+/* Decode a page-blocked fp8 index-key pool into `dst` ([num_pages * P, Di]
+ * doubles): page p holds P rows of Di e4m3 codes (row_stride bytes apart),
+ * then, at byte P * row_stride of the page, P little-endian f32 scales, one
+ * per token; key value = e4m3(code) * scale. */
+void oracle_decode_fp8_keys(const uint8_t *pool, int64_t num_pages, int P, int Di, int64_t row_stride,
+                            int64_t page_stride, double *dst) {
+  for (int64_t p = 0; p < num_pages; ++p) {
+    const uint8_t *page = pool + p * page_stride;
+    for (int i = 0; i < P; ++i) {
+      float scale;
+      memcpy(&scale, page + (int64_t)P * row_stride + 4 * i, sizeof scale);
+      for (int d = 0; d < Di; ++d)
+        dst[(p * P + i) * Di + d] = oracle_e4m3_to_double(page[i * row_stride + d]) * (double)scale;
+    }
+  }
+}
+
 /* Threads the OpenMP loops above use (1 when built without OpenMP). */
 #ifdef _OPENMP
 #include <omp.h>

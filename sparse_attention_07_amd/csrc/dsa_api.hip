@@ -147,13 +147,21 @@ dsa_status dsa_index_scores(const dsa_batch* batch, const void* q_idx, int32_t q
   if (ba.num_q_rows == 0) return DSA_OK;
   if (q_idx == nullptr || w == nullptr || k_idx == nullptr || scores == nullptr) return DSA_ERR_NULL;
   if (n_heads < 1 || head_dim < 1 || ld < 1 || ld < ba.max_seq_len) return DSA_ERR_SHAPE;
-  if (k_idx->format != q_format || k_idx->dim != head_dim) return DSA_ERR_SHAPE;
+  const bool fp8_keys = q_format == DSA_BF16 && k_idx->format == DSA_FP8_E4M3_B128;
+  if ((k_idx->format != q_format && !fp8_keys) || k_idx->dim != head_dim) return DSA_ERR_SHAPE;
   if (!aligned(w, 4) || !aligned(scores, 4)) return DSA_ERR_ALIGN;
   PoolArgs pa;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (q_format == DSA_BF16) {
     if (n_heads != 64 || head_dim != 128) return DSA_ERR_UNSUPPORTED;
-    if ((st = check_pool(k_idx, 256, 16, &pa)) != DSA_OK) return st;
+    if (fp8_keys) {
+      // page-blocked: page_size rows of 128 codes, then page_size f32 scales
+      if ((st = check_pool(k_idx, 128, 16, &pa)) != DSA_OK) return st;
+      if (k_idx->page_stride_bytes < (int64_t)ba.page_size * (k_idx->row_stride_bytes + 4))
+        return DSA_ERR_SHAPE;
+    } else if ((st = check_pool(k_idx, 256, 16, &pa)) != DSA_OK) {
+      return st;
+    }
     if (!aligned(q_idx, 16) || !aligned(w, 16)) return DSA_ERR_ALIGN;
     if (ba.num_pages == 0) return DSA_OK;  // no token is mapped: nothing is written
     return hip_status(dsa::launch_index_scores_bf16(ba, q_idx, w, pa, scores, ld, s));

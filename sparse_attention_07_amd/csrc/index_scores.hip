@@ -26,6 +26,7 @@
 // reads 128 contiguous bytes of one key: lane l (group g = l/32) supplies dims
 // g*64 + ks*8 .. +7 in step ks.  The query operand uses the same mapping.
 #include <algorithm>
+#include <type_traits>
 
 #include "dsa_device.h"
 #include "dsa_launch.h"
@@ -65,7 +66,8 @@ struct Keys {
   bf16x8 v[2][8];
 };
 
-__device__ inline void load_keys(Keys& kk, const int64_t (&off)[2], const uint8_t* k_base, int lane) {
+__device__ inline void load_keys(Keys& kk, const int64_t (&off)[2], const uint8_t* k_base, int lane, int,
+                                 int, int64_t) {
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const uint8_t* p = k_base + (off[nt] < 0 ? 0 : off[nt]) + (lane >> 5) * 128;
@@ -74,14 +76,65 @@ __device__ inline void load_keys(Keys& kk, const int64_t (&off)[2], const uint8_
   }
 }
 
+// fp8 keys (e4m3, one f32 scale per token, page-blocked: a page holds
+// page_size rows of 128 codes, row_stride bytes apart, then the page_size
+// scales).  Raw codes of one wave step: this lane's 64 dims of its two tokens,
+// plus the tokens' scales; every step issues exactly 10 loads per lane (a
+// token without a mapped page reads page 0 and its score is not written).
+struct Keys8 {
+  u32x4 v[2][4];
+  float sc[2];
+};
+
+__device__ inline void load_keys(Keys8& kk, const int64_t (&off)[2], const uint8_t* k_base, int lane,
+                                 int s_first, int page_size, int64_t row_stride) {
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int64_t o = off[nt] < 0 ? 0 : off[nt];
+    const uint8_t* p = k_base + o + (lane >> 5) * 64;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) kk.v[nt][c] = *reinterpret_cast<const u32x4*>(p + c * 16);
+    // row offset o = page * page_stride + slot * row_stride; the scale sits at
+    // page * page_stride + page_size * row_stride + slot * 4
+    const int slot = off[nt] < 0 ? 0 : (s_first + nt * 32 + (lane & 31)) % page_size;
+    kk.sc[nt] = *reinterpret_cast<const float*>(k_base + o + (int64_t)(page_size - slot) * row_stride + slot * 4);
+  }
+}
+
+// e4m3 codes -> bf16 (exact: every e4m3 value is a bf16), in the bf16 key
+// layout (step ks: dims 8 ks .. +7 of the lane's 64).
+__device__ inline void keys_from_fp8(Keys& kk, const Keys8& k8) {
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        u32x4 b;
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          const uint32_t x = k8.v[nt][c][2 * half + d];
+          b[2 * d] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false));
+          b[2 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true));
+        }
+        kk.v[nt][2 * c + half] = __builtin_bit_cast(bf16x8, b);
+      }
+}
+
+template <bool KFP8>
+using KeyRegs = typename std::conditional<KFP8, Keys8, Keys>::type;
+template <bool KFP8>
+constexpr int kLoadsPerStep = KFP8 ? 10 : 16;
+
 // One wave: scores of a 64-token block (keys kk, tokens s_base + 32 nt + lane%32,
 // page offsets off, -1 when unmapped) against the nr staged query rows; row r
 // sits at position pos_first + r (clamped to ld_last) and its output row is
 // row0 + r.
+template <bool SCALED = false>
 __device__ inline void score_block(const Keys& kk, const int64_t (&off)[2], const uint8_t* q_lds,
                                    const float* w_lds, int nr, int s_base, int pos_first,
                                    int64_t ld_last, float* __restrict__ scores, int64_t row0,
-                                   int64_t ld, int lane) {
+                                   int64_t ld, int lane, const float* ksc = nullptr) {
   for (int r = 0; r < nr; ++r) {
     const int pos_r = (int)min<int64_t>((int64_t)pos_first + r, ld_last);
     if (s_base > pos_r) continue;
@@ -115,12 +168,31 @@ __device__ inline void score_block(const Keys& kk, const int64_t (&off)[2], cons
           for (int e = 0; e < 4; ++e) part += wq[e] * fmaxf(acc[nt][mt][4 * q4 + e], 0.f);
         }
       part += __shfl_xor(part, 32);
+      // a token's non-negative scale factors out of the ReLU and the head sum
+      if (SCALED) part *= ksc[nt];
       const int s = s_base + nt * 32 + (lane & 31);
       if (lane < 32 && s <= pos_r && off[nt] >= 0) scores[(row0 + r) * ld + s] = part;
     }
   }
 }
 
+// Scores of one key step from its key registers (fp8 codes are converted to
+// bf16 first and each token's scale applied to its scores).
+__device__ inline void score_keys(const Keys& kk, const int64_t (&off)[2], const uint8_t* q_lds,
+                                  const float* w_lds, int nr, int s_base, int pos_first, int64_t ld_last,
+                                  float* __restrict__ scores, int64_t row0, int64_t ld, int lane) {
+  score_block<false>(kk, off, q_lds, w_lds, nr, s_base, pos_first, ld_last, scores, row0, ld, lane);
+}
+
+__device__ inline void score_keys(const Keys8& k8, const int64_t (&off)[2], const uint8_t* q_lds,
+                                  const float* w_lds, int nr, int s_base, int pos_first, int64_t ld_last,
+                                  float* __restrict__ scores, int64_t row0, int64_t ld, int lane) {
+  Keys kk;
+  keys_from_fp8(kk, k8);
+  score_block<true>(kk, off, q_lds, w_lds, nr, s_base, pos_first, ld_last, scores, row0, ld, lane, k8.sc);
+}
+
+template <bool KFP8>
 __global__ __launch_bounds__(kThreads, 2) void index_scores_bf16_mfma(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ page_table, int pt_stride, int page_size, int num_pages,
@@ -175,11 +247,14 @@ __global__ __launch_bounds__(kThreads, 2) void index_scores_bf16_mfma(
                                  : -1;
     }
   // Both steps' keys go out at once (32 loads per lane).
-  Keys kk[kSteps];
+  KeyRegs<KFP8> kk[kSteps];
 #pragma unroll
-  for (int j = 0; j < kSteps; ++j) load_keys(kk[j], off[j], k_base, lane);
-  // Everything issued before those 32 loads (the copies above) is complete.
-  asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+  for (int j = 0; j < kSteps; ++j)
+    load_keys(kk[j], off[j], k_base, lane, k0 + (j * kWaves + wave) * kKeysPerStep, page_size, k_row_stride);
+  // Everything issued before those key loads (the copies above) is complete.
+  static_assert(kSteps * kLoadsPerStep<KFP8> == (KFP8 ? 20 : 32), "vmcnt below");
+  if (KFP8) asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
 #pragma unroll
   for (int k = 0; k < 2; ++k)
     if (tid + k * kThreads < nr * kHeads) w_lds[tid + k * kThreads] = wv[k];
@@ -190,7 +265,7 @@ __global__ __launch_bounds__(kThreads, 2) void index_scores_bf16_mfma(
   for (int j = 0; j < kSteps; ++j) {
     const int s_base = k0 + (j * kWaves + wave) * kKeysPerStep;
     if (s_base > pos_last) break;                        // later steps are further right
-    score_block(kk[j], off[j], q_lds, w_lds, nr, s_base, pos_first, ld_last, scores, row0, ld, lane);
+    score_keys(kk[j], off[j], q_lds, w_lds, nr, s_base, pos_first, ld_last, scores, row0, ld, lane);
   }
 }
 
@@ -272,6 +347,7 @@ __device__ inline int flat_excl_scan(int v, int* wsum, int& carry, int lane, int
   return before + x - v;
 }
 
+template <bool KFP8>
 __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_lens, int B,
     const int32_t* __restrict__ page_table, int pt_stride, int page_size, int num_pages,
@@ -370,8 +446,8 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
     FlatBlock A{u0, 0, {-1, -1}}, Bk{u0, 0, {-1, -1}}, C{u0, 0, {-1, -1}};
     if (j < hi) prep_block(A, j, u0, pre, unr, upf, ub, ld_last, page_table, pt_stride, page_size,
                            num_pages, k_page_stride, k_row_stride, lane);
-    Keys k0, k1;
-    load_keys(k0, A.off, k_base, lane);
+    KeyRegs<KFP8> k0, k1;
+    load_keys(k0, A.off, k_base, lane, A.tok, page_size, k_row_stride);
     if (j + kFlatWaves < hi)
       prep_block(Bk, j + kFlatWaves, A.u, pre, unr, upf, ub, ld_last, page_table, pt_stride,
                  page_size, num_pages, k_page_stride, k_row_stride, lane);
@@ -397,15 +473,17 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
     // everything issued before them) but not B's 16 key loads.
     const bool has_b = j + kFlatWaves < hi;
     if (has_b) {
-      load_keys(k1, Bk.off, k_base, lane);
-      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      load_keys(k1, Bk.off, k_base, lane, Bk.tok, page_size, k_row_stride);
+      if (KFP8) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      static_assert(kLoadsPerStep<KFP8> == (KFP8 ? 10 : 16), "vmcnt above");
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     lds_barrier();
 
 #define DSA_SCORE(KK, X)                                                                           \
-  score_block(KK, X.off, q_area + (size_t)(X.u - u0) * rg * kRowBytesLds,                          \
+  score_keys(KK, X.off, q_area + (size_t)(X.u - u0) * rg * kRowBytesLds,                          \
               w_area + (size_t)(X.u - u0) * rg * kHeads, unr[X.u], X.tok, upf[X.u], ld_last, scores, \
               uq0[X.u], ld, lane)
     while (j < hi) {
@@ -420,7 +498,7 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
       A = Bk;
       Bk = C;
       const bool has1b = j + kFlatWaves < hi;
-      if (has1b) load_keys(k0, Bk.off, k_base, lane);
+      if (has1b) load_keys(k0, Bk.off, k_base, lane, Bk.tok, page_size, k_row_stride);
       if (j + 2 * kFlatWaves < hi)
         prep_block(C, j + 2 * kFlatWaves, Bk.u, pre, unr, upf, ub, ld_last, page_table, pt_stride,
                    page_size, num_pages, k_page_stride, k_row_stride, lane);
@@ -429,7 +507,7 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
       j += kFlatWaves;
       A = Bk;
       Bk = C;
-      if (j + kFlatWaves < hi) load_keys(k1, Bk.off, k_base, lane);
+      if (j + kFlatWaves < hi) load_keys(k1, Bk.off, k_base, lane, Bk.tok, page_size, k_row_stride);
     }
 #undef DSA_SCORE
     lds_barrier();  // every wave is done with the staged rows
@@ -474,7 +552,10 @@ __global__ __launch_bounds__(256) void index_scores_f32_valu(
 
 }  // namespace
 
-hipError_t launch_index_scores_bf16(const BatchArgs& ba, const void* q_idx, const float* w,
+namespace {
+
+template <bool KFP8>
+hipError_t launch_index_scores_mfma(const BatchArgs& ba, const void* q_idx, const float* w,
                                     const PoolArgs& pool, float* scores, int64_t ld,
                                     hipStream_t stream) {
   if (ba.max_q_len >= 1) {
@@ -490,9 +571,9 @@ hipError_t launch_index_scores_bf16(const BatchArgs& ba, const void* q_idx, cons
     const int nslots = (int)std::min<size_t>(8, avail / per_unit);
     const size_t lds = tables + (size_t)nslots * per_unit;
     if (nslots >= 1) {
-      hipError_t e = ensure_max_lds(reinterpret_cast<const void*>(index_scores_flat));
+      hipError_t e = ensure_max_lds(reinterpret_cast<const void*>(index_scores_flat<KFP8>));
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(index_scores_flat, dim3(device_cu_count()), dim3(kFlatThreads), lds, stream,
+      hipLaunchKernelGGL(index_scores_flat<KFP8>, dim3(device_cu_count()), dim3(kFlatThreads), lds, stream,
                          ba.cu_q, ba.seq_lens, ba.batch, ba.page_table, ba.pt_stride, ba.page_size,
                          ba.num_pages, static_cast<const uint16_t*>(q_idx), w,
                          static_cast<const uint8_t*>(pool.base), pool.page_stride, pool.row_stride,
@@ -511,13 +592,22 @@ hipError_t launch_index_scores_bf16(const BatchArgs& ba, const void* q_idx, cons
   dim3 grid(ba.batch, (ba.max_q_len + rg - 1) / rg,
             (ba.max_seq_len + kKeysPerBlock - 1) / kKeysPerBlock);
   if (grid.y == 0 || grid.z == 0) return hipSuccess;
-  hipError_t e = ensure_max_lds(reinterpret_cast<const void*>(index_scores_bf16_mfma));
+  hipError_t e = ensure_max_lds(reinterpret_cast<const void*>(index_scores_bf16_mfma<KFP8>));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(index_scores_bf16_mfma, grid, dim3(kThreads), lds, stream,
+  hipLaunchKernelGGL(index_scores_bf16_mfma<KFP8>, grid, dim3(kThreads), lds, stream,
                      ba.cu_q, ba.seq_lens, ba.page_table, ba.pt_stride, ba.page_size, ba.num_pages,
                      static_cast<const uint16_t*>(q_idx), w, static_cast<const uint8_t*>(pool.base),
                      pool.page_stride, pool.row_stride, scores, ld, rg);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_index_scores_bf16(const BatchArgs& ba, const void* q_idx, const float* w,
+                                    const PoolArgs& pool, float* scores, int64_t ld,
+                                    hipStream_t stream) {
+  return pool.format == 2 ? launch_index_scores_mfma<true>(ba, q_idx, w, pool, scores, ld, stream)
+                          : launch_index_scores_mfma<false>(ba, q_idx, w, pool, scores, ld, stream);
 }
 
 hipError_t launch_index_scores_f32(const BatchArgs& ba, const void* q_idx, const float* w,

@@ -119,6 +119,19 @@ def make_pool(pool: torch.Tensor, fmt: int, dim: int) -> dsa_pool:
     return p
 
 
+def make_key_pool(sb) -> dsa_pool:
+    """dsa_pool of a synth.Batch's indexer keys: [num_pages, P, di] in idx_fmt,
+    or page-blocked fp8 pages ([num_pages, page_bytes]: P rows of 128 codes,
+    then P f32 scales, page_bytes >= P*132 and a multiple of 16)."""
+    cfg = sb.cfg
+    if cfg.key_fmt == DSA_FP8_E4M3_B128:
+        pool = sb.k_pool
+        p = dsa_pool(pool.data_ptr(), DSA_FP8_E4M3_B128, cfg.di, pool.stride(0), 128)
+        p._keep = pool
+        return p
+    return make_pool(sb.k_pool, cfg.idx_fmt, cfg.di)
+
+
 def batch_from(sb) -> dsa_batch:
     """dsa_batch of a synth.Batch whose tensors are on the GPU."""
     return make_batch(sb.cu_q, sb.seq_lens_t, sb.page_table, sb.T, sb.max_q_len, sb.max_seq_len,

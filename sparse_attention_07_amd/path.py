@@ -20,7 +20,7 @@ class DSAPath:
         self.cfg = cfg
         dev = sb.q_idx.device
         self.batch = dsa.batch_from(sb)
-        self.k_pool = dsa.make_pool(sb.k_pool, cfg.idx_fmt, cfg.di)
+        self.k_pool = dsa.make_key_pool(sb)
         self.kv = [dsa.make_pool(p, cfg.kv_fmt, cfg.dc + cfg.dr) for p in sb.kv_pool]
         T = sb.T
         # score rows padded to a multiple of 64 entries (256 B)

@@ -45,6 +45,8 @@ FMT_FP8_E4M3_B128 = 2
 FP8_ROW_BYTES = 656       # 512 e4m3 bytes + 4 f32 block scales + 64 bf16 rope
 FP8_BLOCK = 128
 FP8_MAX = 448.0
+FP8_KEY_CODES = 128       # fp8 index keys: 128 e4m3 codes per token, page-blocked with
+FP8_KEY_BYTES = 132       # one f32 scale per token (P rows of codes, then P scales)
 
 
 @dataclass
@@ -68,6 +70,7 @@ class Config:
     layers: int = 1             # 1 full layer + (layers-1) IndexShare layers
     identity_pages: bool = False
     seed: int = 1000
+    key_fmt: int | None = None  # k_I pool format when it differs from idx_fmt (fp8 keys)
 
 
 CONFIGS = {
@@ -110,7 +113,7 @@ class Batch:
     num_pages: int
     q_idx: torch.Tensor         # [T, hi, di]
     w: torch.Tensor             # f32 [T, hi]
-    k_pool: torch.Tensor        # [num_pages, P, di]
+    k_pool: torch.Tensor        # [num_pages, P, di]; fp8 keys: uint8 [num_pages, P*132]
     q: list = field(default_factory=list)        # per layer [T, H, dc+dr]
     kv_pool: list = field(default_factory=list)  # per layer [num_pages, P, row] (uint8 for fp8)
 
@@ -175,12 +178,37 @@ def quantize_fp8_rows(latent: torch.Tensor, rope: torch.Tensor) -> torch.Tensor:
     return out
 
 
+def fp8_key_page_bytes(P: int) -> int:
+    """Bytes of one page-blocked fp8 key page of P tokens, 16-byte aligned."""
+    return (P * FP8_KEY_BYTES + 15) // 16 * 16
+
+
+def quantize_fp8_keys(k: torch.Tensor, scale: torch.Tensor | None = None) -> torch.Tensor:
+    """Pack index keys [num_pages, P, 128] (f32) into page-blocked fp8 pages.
+
+    Page layout: P rows of 128 e4m3fn codes, then P f32 scales, one per token
+    (scale = token amax / 448 unless given as [num_pages, P]), then zero bytes
+    up to a multiple of 16.  The e4m3 rounding is torch's own float8_e4m3fn
+    conversion.
+    """
+    n, P, d = k.shape
+    assert d == FP8_KEY_CODES
+    if scale is None:
+        amax = k.abs().amax(dim=-1)
+        scale = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax))
+    codes = (k / scale[..., None]).clamp(-FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn)
+    out = torch.zeros(n, fp8_key_page_bytes(P), dtype=torch.uint8, device=k.device)
+    out[:, :P * FP8_KEY_CODES] = codes.reshape(n, P * FP8_KEY_CODES).view(torch.uint8)
+    out[:, P * FP8_KEY_CODES:P * FP8_KEY_BYTES] = scale.to(torch.float32).contiguous().view(torch.uint8).reshape(n, P * 4)
+    return out
+
+
 def make_batch(cfg_id: int, mode: str = "parity", device="cpu", layers: int | None = None,
                seed_offset: int = 0, batch: int | None = None, q_len: int | None = None,
                ctx: tuple | None = None, topk: int | None = None,
                page_size: int | None = None, identity_pages: bool | None = None,
                heads: int | None = None, kv_fmt: int | None = None,
-               q_lens: list | None = None) -> Batch:
+               q_lens: list | None = None, key_fmt: int | None = None) -> Batch:
     """Draw one batch of config `cfg_id`.
 
     The keyword overrides (batch, q_len, ctx range, top-k, page size) give
@@ -210,6 +238,8 @@ def make_batch(cfg_id: int, mode: str = "parity", device="cpu", layers: int | No
         cfg.heads = heads
     if kv_fmt is not None:
         cfg.kv_fmt = kv_fmt
+    if key_fmt is not None:
+        cfg.key_fmt = key_fmt
     if q_lens is not None:
         cfg.batch = len(q_lens)
         cfg.q_len = max(q_lens)
@@ -244,13 +274,20 @@ def make_batch(cfg_id: int, mode: str = "parity", device="cpu", layers: int | No
     T = cu[-1]
 
     idt = torch_dtype(cfg.idx_fmt)
+    fp8_keys = cfg.key_fmt == FMT_FP8_E4M3_B128
+    if fp8_keys:
+        assert cfg.idx_fmt == FMT_BF16 and cfg.di == FP8_KEY_CODES
     if mode == "parity":
         q_idx = _int_scaled((T, cfg.hi, cfg.di), -8, 8, 1.0 / 8, g, device, idt)
-        k_pool = _int_scaled((num_pages, P, cfg.di), -8, 8, 1.0 / 8, g, device, idt)
+        k_pool = _int_scaled((num_pages, P, cfg.di), -8, 8, 1.0 / 8, g, device,
+                             torch.float32 if fp8_keys else idt)
         w = _int_scaled((T, cfg.hi), -4, 4, 1.0 / 4, g, device, torch.float32)
+        if fp8_keys:  # codes are the integers themselves: exact in e4m3 with scale 1/8
+            k_pool = quantize_fp8_keys(k_pool, torch.full((num_pages, P), 1.0 / 8, device=device))
     else:
         q_idx = torch.randn((T, cfg.hi, cfg.di), generator=g, device=device).to(idt)
-        k_pool = torch.randn((num_pages, P, cfg.di), generator=g, device=device).to(idt)
+        k_pool = torch.randn((num_pages, P, cfg.di), generator=g, device=device)
+        k_pool = quantize_fp8_keys(k_pool) if fp8_keys else k_pool.to(idt)
         w = torch.randn((T, cfg.hi), generator=g, device=device) / 8.0
 
     D = cfg.dc + cfg.dr
@@ -277,6 +314,7 @@ def make_batch(cfg_id: int, mode: str = "parity", device="cpu", layers: int | No
 def repage(batch: Batch, new_page_size: int, identity: bool, seed: int = 77) -> Batch:
     """Same token contents under another page size / page order (paging invariance)."""
     cfg = Config(**{**batch.cfg.__dict__})
+    assert cfg.key_fmt in (None, cfg.idx_fmt), "page-blocked fp8 key pools are not re-paged"
     P0, P1 = cfg.page_size, new_page_size
     cfg.page_size = P1
     B = batch.B

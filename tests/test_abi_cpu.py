@@ -72,6 +72,25 @@ def test_index_scores_validation():
     assert _scores(bad) == 1
 
 
+
+def test_index_scores_fp8_key_validation():
+    # bf16 queries over page-blocked fp8 keys: P rows of row bytes, then P f32 scales
+    def fp8(row, page, dim=128, base=FAKE):
+        return dsa.dsa_pool(base.value, dsa.DSA_FP8_E4M3_B128, dim, page, row)
+    ok = 16 * (128 + 4)
+    assert _scores(_batch(T=0), pool=fp8(128, ok)) == 0
+    assert _scores(_batch(), pool=fp8(128, ok), q=None) == 1
+    assert _scores(_batch(), pool=fp8(128, ok - 16)) == 2          # no room for the scales
+    assert _scores(_batch(), pool=fp8(112, ok)) == 2               # row shorter than 128 codes
+    assert _scores(_batch(), pool=fp8(136, 16 * 140)) == 6         # row stride not 16-aligned
+    assert _scores(_batch(), pool=fp8(128, ok + 8)) == 6           # page stride not 16-aligned
+    assert _scores(_batch(), pool=fp8(128, ok, base=ODD)) == 6
+    assert _scores(_batch(), pool=fp8(128, ok, dim=64), D=64) == 3  # MFMA indexer is 64 x 128 only
+    assert _scores(_batch(), pool=fp8(128, ok, dim=64)) == 2       # pool dim != head_dim
+    assert _scores(_batch(), pool=fp8(128, ok), H=32) == 3
+    assert _scores(_batch(), q_fmt=dsa.DSA_F32, pool=fp8(128, ok)) == 2  # fp8 keys need bf16 q
+
+
 def test_topk_validation():
     b = _batch()
     assert L.dsa_topk(None, FAKE, 128, 8, FAKE, None, 0, None) == 1

@@ -66,6 +66,14 @@ REDUCED = {
     # requests with no rows and mixed draft lengths; more than 256 requests
     "ragged_q_lens_empty": dict(cfg=4, q_lens=[5, 0, 3, 1, 0, 5, 2], ctx=(600, 3000), topk=512),
     "many_requests": dict(cfg=1, batch=300, ctx=(40, 700), topk=256),
+    # fp8 index keys (one scale per token) under bf16 queries: decode, drafts, prefill rows
+    "decode16_fp8_keys": dict(cfg=1, batch=6, ctx=(100, 3000), topk=512, key_fmt=synth.FMT_FP8_E4M3_B128),
+    "decode16_p5_fp8_keys": dict(cfg=1, batch=4, ctx=(300, 1300), topk=256, page_size=5,
+                                 key_fmt=synth.FMT_FP8_E4M3_B128),
+    "mtp_fp8_keys": dict(cfg=4, batch=3, ctx=(3000, 9000), topk=512, key_fmt=synth.FMT_FP8_E4M3_B128),
+    "ragged_fp8_keys": dict(cfg=4, q_lens=[5, 0, 3, 1, 0, 5, 2], ctx=(600, 3000), topk=512,
+                            key_fmt=synth.FMT_FP8_E4M3_B128),
+    "prefill_fp8_keys": dict(cfg=3, q_len=130, ctx=(700, 700), topk=512, key_fmt=synth.FMT_FP8_E4M3_B128),
 }
 
 

@@ -337,3 +337,61 @@ def test_fp8_row_layout_roundtrip():
     amax = lat.reshape(40, 4, 128).abs().amax(-1).repeat_interleave(128, 1).double()
     err = (dec[:, :512] - lat.double()).abs()
     assert torch.all(err <= lat.double().abs() * 2.0 ** -4 + amax / 448 * 2.0 ** -9)
+
+
+def _key_page(P, row, codes, scales, pad=0xFF):
+    """One page-blocked fp8 key page: P rows of `row` bytes (128 codes, then
+    padding), then P f32 scales."""
+    page = np.full(P * row + 4 * P, pad, dtype=np.uint8)
+    for i in range(P):
+        page[i * row:i * row + 128] = codes[i]
+    page[P * row:] = np.asarray(scales, dtype=np.float32).view(np.uint8)
+    return page
+
+
+@pytest.mark.parametrize("row", [128, 144])
+def test_fp8_key_page_hand_decoded(row):
+    # row 0: 1.0, 2.0, -1.0, 2^-9, 448 (codes 0x38, 0x40, 0xB8, 0x01, 0x7E), rest +0, scale 0.5
+    # row 1: every code 0x30 (0.5), scale 2.0 -> all ones
+    # row 2: -0 and the largest subnormal 0x07 (7 * 2^-9), scale 4.0
+    c0 = np.zeros(128, np.uint8)
+    c0[:5] = [0x38, 0x40, 0xB8, 0x01, 0x7E]
+    c1 = np.full(128, 0x30, np.uint8)
+    c2 = np.zeros(128, np.uint8)
+    c2[0], c2[127] = 0x80, 0x07
+    page = _key_page(3, row, [c0, c1, c2], [0.5, 2.0, 4.0])
+    # padding bytes are NaN codes: any read of them shows up
+    dec = oracle.decode_fp8_keys(page[None], 3, 128, row)
+    want = np.zeros((3, 128))
+    want[0, :5] = [0.5, 1.0, -0.5, 2.0 ** -10, 224.0]
+    want[1, :] = 1.0
+    want[2, 127] = 7 * 2.0 ** -9 * 4.0
+    assert np.array_equal(dec, want)
+    assert math.copysign(1.0, dec[2, 0]) == -1.0
+
+
+def test_fp8_key_quantiser_against_torch_decoding():
+    # per-token scales differ, so a scale taken from the wrong token or page fails
+    g = torch.Generator().manual_seed(11)
+    k = torch.randn(3, 5, 128, generator=g) * torch.rand(3, 5, 1, generator=g) * 10
+    pages = synth.quantize_fp8_keys(k)
+    dec = torch.from_numpy(oracle.decode_fp8_keys(pages, 5)).reshape(3, 5, 128)
+    codes = pages[:, :5 * 128].reshape(3, 5, 128).contiguous().view(torch.float8_e4m3fn)
+    scale = pages[:, 5 * 128:5 * 132].contiguous().view(torch.float32).reshape(3, 5)
+    assert torch.equal(dec, codes.double() * scale.double()[..., None])
+    # the token amax maps to 448 exactly, and every element is within e4m3's rounding
+    amax = k.abs().amax(-1, keepdim=True).double()
+    assert torch.allclose(dec.abs().amax(-1, keepdim=True), amax, rtol=2 ** -4, atol=0)
+    assert torch.all((dec - k.double()).abs() <= k.double().abs() * 2.0 ** -4 + amax / 448 * 2.0 ** -9)
+
+
+def test_fp8_keys_exact_integers_give_bf16_scores():
+    # parity batches draw the same integers for both key formats; with scale
+    # 1/8 the e4m3 codes are those integers, so the scores must agree exactly
+    a = synth.make_batch(4, batch=3, ctx=(200, 700), topk=128, layers=0)
+    b = synth.make_batch(4, batch=3, ctx=(200, 700), topk=128, layers=0, key_fmt=synth.FMT_FP8_E4M3_B128)
+    assert b.k_pool.dtype == torch.uint8 and b.k_pool.shape[1] == synth.fp8_key_page_bytes(a.cfg.page_size)
+    sa, sb_ = oracle.index_scores(a), oracle.index_scores(b)
+    assert np.array_equal(np.isnan(sa), np.isnan(sb_))
+    assert np.array_equal(np.nan_to_num(sa), np.nan_to_num(sb_))
+    assert np.array_equal(oracle.topk(a, sa), oracle.topk(b, sb_))
