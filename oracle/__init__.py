@@ -20,6 +20,11 @@ Parity status of each function (what pins it; see tests/test_oracle_pins.py):
   e4m3 decode   pinned: all 256 codes against torch.float8_e4m3fn
   fp8 index keys (page-blocked codes + per-token scales) pinned: a hand-built
                 page decoded against values written out by hand
+  indexer_prepare  pinned: LayerNorm against torch's layer_norm; RoPE against
+                complex multiplication by unit phasors (interleaved) and the
+                dims permutation that maps one pair layout onto the other;
+                a hand-worked rotation; identity at angle 0; norm
+                preservation; keys found at their slots through the page table
 """
 from __future__ import annotations
 
@@ -68,6 +73,12 @@ def _load():
         lib.oracle_e4m3_to_double.restype = ctypes.c_double
         lib.oracle_decode_fp8_rows.argtypes = [ctypes.c_void_p, c_i64, c_int, c_int, f64p]
         lib.oracle_decode_fp8_keys.argtypes = [ctypes.c_void_p, c_i64, c_int, c_int, c_i64, c_i64, f64p]
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        lib.oracle_indexer_prepare.argtypes = [c_int, i32p, i32p, i32p, c_int, c_int, c_int, c_int,
+                                               f64p, f64p, f64p, f64p, ctypes.c_double, f64p, f64p,
+                                               c_i64, c_int, c_int, c_int, c_int, f64p, f64p, f64p,
+                                               i64p]
+        lib.oracle_indexer_prepare.restype = c_int
         for f in (lib.oracle_index_scores, lib.oracle_topk, lib.oracle_sparse_mla):
             f.restype = c_int
         lib.oracle_threads.restype = c_int
@@ -240,6 +251,47 @@ def decode_fp8_keys(pages_u8, page_size, di=128, row_stride=128):
     lib.oracle_decode_fp8_keys(a.ctypes.data_as(ctypes.c_void_p), n, page_size, di, row_stride, a.shape[1],
                                _p(out, ctypes.c_double))
     return out
+
+
+def indexer_prepare(batch, prep, with_pool=True):
+    """Rotated queries, normalised and rotated keys, and the key pool after the
+    keys are written (float64).
+
+    `prep` carries q_in [T,H,D], k_in [T,D], gamma/beta [D], eps, cos/sin
+    tables [rows, R/2], rope_dim R and interleaved.  Returns dict(q [T,H,D],
+    k [T,D], pos [T], pool [num_pages*P, D] or None).  The pool image starts
+    as the batch's key pool (bf16 / f32 values) and only the rows' slots
+    change.
+    """
+    lib = _load()
+    cfg = batch.cfg
+    T, H, D = prep.q_in.shape
+    q_in, k_in = _f64(prep.q_in), _f64(prep.k_in)
+    gamma, beta = _f64(prep.gamma), _f64(prep.beta)
+    cos, sin = _f64(prep.cos), _f64(prep.sin)
+    cu = [0]
+    for ql in batch.q_lens:
+        cu.append(cu[-1] + ql)
+    cu_q, seq_lens, pt = _i32(cu), _i32(batch.seq_lens), _i32(batch.page_table)
+    pool = None
+    num_pages = batch.k_pool.shape[0]
+    if with_pool:
+        pool = _f64(batch.k_pool).reshape(num_pages * cfg.page_size, D).copy()
+    q_out = np.empty((T, H, D), dtype=np.float64)
+    k_out = np.empty((T, D), dtype=np.float64)
+    pos = np.empty(T, dtype=np.int64)
+    st = lib.oracle_indexer_prepare(batch.B, _p(cu_q, ctypes.c_int32), _p(seq_lens, ctypes.c_int32),
+                                    _p(pt, ctypes.c_int32), pt.shape[1], cfg.page_size, num_pages, T,
+                                    _p(q_in, ctypes.c_double), _p(k_in, ctypes.c_double),
+                                    _p(gamma, ctypes.c_double), _p(beta, ctypes.c_double),
+                                    float(prep.eps), _p(cos, ctypes.c_double), _p(sin, ctypes.c_double),
+                                    cos.shape[0], prep.rope_dim, int(prep.interleaved), H, D,
+                                    _p(q_out, ctypes.c_double), _p(k_out, ctypes.c_double),
+                                    _p(pool, ctypes.c_double) if pool is not None else None,
+                                    _p(pos, ctypes.c_int64))
+    if st != 0:
+        raise RuntimeError("oracle_indexer_prepare failed with status %d" % st)
+    return {"q": q_out, "k": k_out, "pos": pos, "pool": pool}
 
 
 def run_path(batch, rows=None):

@@ -32,6 +32,13 @@
  *  4. OCP OFP8 E4M3 decoding of block-scaled fp8 latent rows (the BF16/FP8
  *     sparse cache paths of lmdeploy PR 4737, section "Changes"); the
  *     decoder follows the OCP 8-bit floating point specification.
+ *  5. Indexer query/key preparation before the scores (the fused indexer
+ *     preparation of lmdeploy PR 4737, section "Changes"; mlx-lm PR 1419's
+ *     description: GLM-5.2's indexer uses non-interleaved RoPE and a key
+ *     LayerNorm with eps 1e-6, DeepSeek-V3.2 the interleaved form and 1e-5).
+ *     Each new row's query heads are rotated at the row's position, its key
+ *     is layer-normalised and rotated, and the key is written into the paged
+ *     pool at that position.
  *
  * Batch convention: request b owns query rows cu_q[b] .. cu_q[b+1]-1; the
  * j-th of them sits at position pos = seq_len[b] - q_len[b] + j and sees the
@@ -318,6 +325,79 @@ void oracle_decode_fp8_keys(const uint8_t *pool, int64_t num_pages, int P, int D
         dst[(p * P + i) * Di + d] = oracle_e4m3_to_double(page[i * row_stride + d]) * (double)scale;
     }
   }
+}
+
+/* ---- 5. indexer preparation ------------------------------------------- */
+
+/* Rotary embedding of the first R dims of x (length D) at table row `row`:
+ * pair i (0 <= i < R/2) is dims (i, i + R/2) when not interleaved and
+ * (2i, 2i+1) when interleaved; it turns by the angle whose cosine and sine
+ * are cos_tab[row*R/2 + i] and sin_tab[row*R/2 + i]:
+ *     (a, b) -> (a cos - b sin, a sin + b cos).
+ * Dims R .. D-1 pass through unchanged. */
+static void rope(const double *x, double *y, int D, int R, int interleaved,
+                 const double *cos_row, const double *sin_row) {
+  for (int d = R; d < D; ++d) y[d] = x[d];
+  for (int i = 0; i < R / 2; ++i) {
+    int ia = interleaved ? 2 * i : i;
+    int ib = interleaved ? 2 * i + 1 : i + R / 2;
+    double a = x[ia], b = x[ib], c = cos_row[i], s = sin_row[i];
+    y[ia] = a * c - b * s;
+    y[ib] = a * s + b * c;
+  }
+}
+
+/* LayerNorm over D values: (x - mean) / sqrt(var + eps) * gamma + beta, with
+ * var the mean squared deviation (population variance). */
+static void layer_norm(const double *x, double *y, int D, const double *gamma,
+                       const double *beta, double eps) {
+  double mean = 0.0, var = 0.0;
+  for (int d = 0; d < D; ++d) mean += x[d];
+  mean /= D;
+  for (int d = 0; d < D; ++d) var += (x[d] - mean) * (x[d] - mean);
+  var /= D;
+  double inv = 1.0 / sqrt(var + eps);
+  for (int d = 0; d < D; ++d) y[d] = (x[d] - mean) * inv * gamma[d] + beta[d];
+}
+
+/* For every query row t (position p = pos(t)):
+ *   q_out[t,h,:] = rope(q_in[t,h,:], p)          for each of the H heads
+ *   k_out[t,:]   = rope(layer_norm(k_in[t,:]), p)
+ * and, when pool != NULL, k_out[t,:] is stored at the row's token slot of
+ * the pool image ([num_pages*P, D], page table applied; rows whose page is
+ * not mapped are not stored).  pos_out[t] receives p.  Returns ORC_BAD_ARG
+ * when a position falls outside the rope table. */
+int oracle_indexer_prepare(int B, const int32_t *cu_q, const int32_t *seq_lens,
+                           const int32_t *page_table, int pt_stride, int page_size, int num_pages,
+                           int T, const double *q_in, const double *k_in, const double *gamma,
+                           const double *beta, double eps, const double *cos_tab,
+                           const double *sin_tab, int64_t tab_rows, int R, int interleaved,
+                           int H, int D, double *q_out, double *k_out, double *pool,
+                           int64_t *pos_out) {
+  if (R < 0 || R > D || R % 2 != 0) return ORC_BAD_ARG;
+  double *kn = (double *)malloc(sizeof(double) * (size_t)D);
+  if (!kn) return ORC_BAD_ARG;
+  int st = ORC_OK;
+  for (int t = 0; t < T && st == ORC_OK; ++t) {
+    int b;
+    int64_t p;
+    if (row_info(B, cu_q, seq_lens, t, &b, &p) != ORC_OK || p < 0 || p >= tab_rows) {
+      st = ORC_BAD_ARG;
+      break;
+    }
+    pos_out[t] = p;
+    const double *c = cos_tab + p * (R / 2), *s = sin_tab + p * (R / 2);
+    for (int h = 0; h < H; ++h)
+      rope(q_in + ((int64_t)t * H + h) * D, q_out + ((int64_t)t * H + h) * D, D, R, interleaved, c, s);
+    layer_norm(k_in + (int64_t)t * D, kn, D, gamma, beta, eps);
+    rope(kn, k_out + (int64_t)t * D, D, R, interleaved, c, s);
+    if (pool) {
+      int64_t slot = token_slot(page_table, pt_stride, page_size, num_pages, b, p);
+      if (slot >= 0) memcpy(pool + slot * D, k_out + (int64_t)t * D, sizeof(double) * (size_t)D);
+    }
+  }
+  free(kn);
+  return st;
 }
 
 /* Threads the OpenMP loops above use (1 when built without OpenMP). */

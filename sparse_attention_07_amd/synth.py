@@ -311,6 +311,51 @@ def make_batch(cfg_id: int, mode: str = "parity", device="cpu", layers: int | No
                  q_idx=q_idx, w=w, k_pool=k_pool, q=qs, kv_pool=kvs)
 
 
+@dataclass
+class Prep:
+    """Inputs of the indexer preparation for one batch's new rows."""
+    q_in: torch.Tensor      # [T, hi, di] indexer queries before RoPE (idx dtype)
+    k_in: torch.Tensor      # [T, di] indexer keys before LayerNorm and RoPE (idx dtype)
+    gamma: torch.Tensor     # f32 [di] LayerNorm weight
+    beta: torch.Tensor      # f32 [di] LayerNorm bias
+    eps: float
+    cos: torch.Tensor       # f32 [rows, rope_dim/2], row p = position p
+    sin: torch.Tensor
+    rope_dim: int
+    interleaved: bool
+
+
+def rope_tables(rows: int, rope_dim: int, theta: float = 10000.0, device="cpu", dtype=torch.float32):
+    """The usual rotary tables: angle(p, i) = p * theta^(-2i/rope_dim), computed
+    in float64 and stored as cosines and sines [rows, rope_dim/2] (f32 unless
+    another dtype is asked for)."""
+    i = torch.arange(rope_dim // 2, dtype=torch.float64)
+    inv = theta ** (-2.0 * i / rope_dim)
+    ang = torch.arange(rows, dtype=torch.float64)[:, None] * inv[None, :]
+    return (torch.cos(ang).to(dtype).to(device), torch.sin(ang).to(dtype).to(device))
+
+
+def make_prep(batch: Batch, rope_dim: int | None = None, interleaved: bool = False,
+              eps: float = 1e-6, seed: int = 4242, device=None) -> Prep:
+    """Draw the preparation inputs for `batch`'s rows.  Defaults follow the GLM
+    indexer (non-interleaved RoPE over half the head, eps 1e-6); its own seed,
+    so the batch's draws do not change.  Keys get a non-zero mean and spread so
+    the LayerNorm has work to do."""
+    cfg = batch.cfg
+    device = device or batch.q_idx.device
+    g = _gen(device, seed)
+    dt = torch_dtype(cfg.idx_fmt)
+    R = cfg.di // 2 if rope_dim is None else rope_dim
+    T = batch.T
+    q_in = torch.randn((T, cfg.hi, cfg.di), generator=g, device=device).to(dt)
+    k_in = (torch.randn((T, cfg.di), generator=g, device=device) * 2.0 + 0.5).to(dt)
+    gamma = 1.0 + 0.25 * torch.randn((cfg.di,), generator=g, device=device)
+    beta = 0.1 * torch.randn((cfg.di,), generator=g, device=device)
+    cos, sin = rope_tables(max(batch.max_seq_len, 1), R, device=device)
+    return Prep(q_in=q_in, k_in=k_in, gamma=gamma, beta=beta, eps=eps, cos=cos, sin=sin,
+                rope_dim=R, interleaved=interleaved)
+
+
 def repage(batch: Batch, new_page_size: int, identity: bool, seed: int = 77) -> Batch:
     """Same token contents under another page size / page order (paging invariance)."""
     cfg = Config(**{**batch.cfg.__dict__})

@@ -395,3 +395,144 @@ def test_fp8_keys_exact_integers_give_bf16_scores():
     assert np.array_equal(np.isnan(sa), np.isnan(sb_))
     assert np.array_equal(np.nan_to_num(sa), np.nan_to_num(sb_))
     assert np.array_equal(oracle.topk(a, sa), oracle.topk(b, sb_))
+
+
+# ---------------------------------------------------------------- indexer preparation
+
+
+def _prep_batch(q_lens=(1, 3), seq_lens=(9, 6), hi=3, di=16, P=4, seed=0):
+    keys = [torch.randn(s, di, generator=torch.Generator().manual_seed(seed + i)).double()
+            for i, s in enumerate(seq_lens)]
+    T = sum(q_lens)
+    return _batches.make(list(q_lens), list(seq_lens), keys, torch.zeros(T, hi, di), torch.zeros(T, hi),
+                         page_size=P, permute_seed=seed + 7)
+
+
+def _prep(b, R, interleaved=False, eps=1e-6, cos=None, sin=None, seed=1, gamma=None, beta=None):
+    g = torch.Generator().manual_seed(seed)
+    T, hi, di = b.q_idx.shape
+    if cos is None:
+        cos, sin = synth.rope_tables(b.max_seq_len, R)
+    return synth.Prep(q_in=torch.randn(T, hi, di, generator=g).double(),
+                      k_in=torch.randn(T, di, generator=g).double() * 3 + 1,
+                      gamma=torch.randn(di, generator=g).double() if gamma is None else gamma,
+                      beta=torch.randn(di, generator=g).double() if beta is None else beta,
+                      eps=eps, cos=cos, sin=sin, rope_dim=R, interleaved=interleaved)
+
+
+def test_prep_layer_norm_matches_torch():
+    # with no rotated dims the key is LayerNorm alone and the queries pass through
+    b = _prep_batch()
+    for eps in (1e-6, 1e-5, 0.5):
+        pr = _prep(b, 0, eps=eps, cos=torch.zeros(b.max_seq_len, 0), sin=torch.zeros(b.max_seq_len, 0))
+        r = oracle.indexer_prepare(b, pr)
+        ref = torch.nn.functional.layer_norm(pr.k_in, (pr.k_in.shape[1],), pr.gamma, pr.beta, eps)
+        assert np.allclose(r["k"], ref.numpy(), rtol=1e-13, atol=1e-13)
+        assert np.array_equal(r["q"], pr.q_in.numpy())
+
+
+def test_prep_interleaved_rope_is_complex_multiplication():
+    b = _prep_batch()
+    for R in (16, 8):
+        pr = _prep(b, R, interleaved=True)
+        r = oracle.indexer_prepare(b, pr)
+        pos = torch.tensor(b.positions())
+        # pairs (2i, 2i+1) as complex numbers, times cos + i sin of the row's angle
+        ph = torch.complex(pr.cos[pos].double(), pr.sin[pos].double())          # [T, R/2]
+        zq = torch.view_as_complex(pr.q_in[..., :R].reshape(b.T, -1, R // 2, 2).contiguous())
+        want_q = torch.view_as_real(zq * ph[:, None, :]).reshape(b.T, -1, R)
+        assert torch.allclose(torch.from_numpy(r["q"][..., :R]), want_q, rtol=0, atol=1e-14)
+        assert np.array_equal(r["q"][..., R:], pr.q_in[..., R:].numpy())
+        kn = torch.nn.functional.layer_norm(pr.k_in, (16,), pr.gamma, pr.beta, pr.eps)
+        zk = torch.view_as_complex(kn[:, :R].reshape(b.T, R // 2, 2).contiguous())
+        want_k = torch.view_as_real(zk * ph).reshape(b.T, R)
+        assert torch.allclose(torch.from_numpy(r["k"][:, :R]), want_k, rtol=0, atol=1e-12)
+        # and the table is e^{i p theta_i}, theta_i = 10000^(-2i/R)
+        ang = pos[:, None].double() * 10000.0 ** (-2.0 * torch.arange(R // 2).double() / R)
+        assert torch.allclose(ph, torch.polar(torch.ones_like(ang), ang), atol=1e-6)
+
+
+def test_prep_non_interleaved_is_a_permutation_of_interleaved():
+    # non-interleaved pairs (i, i+R/2) are the interleaved pairs (2i, 2i+1)
+    # after moving dim i to 2i and dim i+R/2 to 2i+1
+    b = _prep_batch()
+    R, D = 8, 16
+    perm = torch.arange(D)
+    perm[:R:2], perm[1:R:2] = torch.arange(R // 2), torch.arange(R // 2, R)   # new dim j <- old perm[j]
+    pn = _prep(b, R, interleaved=False)
+    pi = synth.Prep(q_in=pn.q_in[..., perm], k_in=pn.k_in[:, perm], gamma=pn.gamma[perm], beta=pn.beta[perm],
+                    eps=pn.eps, cos=pn.cos, sin=pn.sin, rope_dim=R, interleaved=True)
+    rn, ri = oracle.indexer_prepare(b, pn), oracle.indexer_prepare(b, pi)
+    assert np.array_equal(rn["q"][..., perm.numpy()], ri["q"])
+    assert np.allclose(rn["k"][:, perm.numpy()], ri["k"], rtol=1e-14, atol=1e-14)
+
+
+def test_prep_hand_worked_rotation():
+    # one row at position 2; pair 0 turns by (cos, sin) = (0.6, 0.8), other pairs by 0
+    b = _prep_batch(q_lens=(1,), seq_lens=(3,), hi=1, di=16)
+    R = 8
+    cos = torch.ones(3, R // 2, dtype=torch.float64)
+    sin = torch.zeros(3, R // 2, dtype=torch.float64)
+    cos[2, 0], sin[2, 0] = 0.6, 0.8
+    q = torch.zeros(1, 1, 16, dtype=torch.float64)
+    q[0, 0, 0], q[0, 0, 4] = 1.0, 2.0      # pair 0 of the non-interleaved layout: dims 0 and R/2
+    q[0, 0, 9] = 5.0                       # outside the rotated dims
+    pr = synth.Prep(q_in=q, k_in=torch.arange(16).double()[None], gamma=torch.ones(16, dtype=torch.float64),
+                    beta=torch.zeros(16, dtype=torch.float64), eps=0.0, cos=cos,
+                    sin=sin, rope_dim=R, interleaved=False)
+    r = oracle.indexer_prepare(b, pr)
+    want = np.zeros(16)
+    want[0], want[4], want[9] = 0.6 * 1 - 0.8 * 2, 0.8 * 1 + 0.6 * 2, 5.0
+    assert np.allclose(r["q"][0, 0], want, rtol=0, atol=1e-15)
+    # key 0..15: mean 7.5, population variance (16^2-1)/12 = 21.25
+    kn = (np.arange(16) - 7.5) / math.sqrt(21.25)
+    kw = kn.copy()
+    kw[0], kw[4] = 0.6 * kn[0] - 0.8 * kn[4], 0.8 * kn[0] + 0.6 * kn[4]
+    assert np.allclose(r["k"][0], kw, rtol=0, atol=1e-14)
+
+
+def test_prep_position_zero_and_norm_preservation():
+    b = _prep_batch(q_lens=(1, 2), seq_lens=(1, 5))       # row 0 sits at position 0
+    cos, sin = synth.rope_tables(b.max_seq_len, 16, dtype=torch.float64)
+    pr = _prep(b, 16, cos=cos, sin=sin)
+    r = oracle.indexer_prepare(b, pr)
+    assert r["pos"].tolist() == [0, 3, 4]
+    assert np.allclose(r["q"][0], pr.q_in[0].numpy(), rtol=0, atol=1e-15)
+    assert np.allclose(np.linalg.norm(r["q"], axis=-1), np.linalg.norm(pr.q_in.numpy(), axis=-1), rtol=1e-13)
+    kn = torch.nn.functional.layer_norm(pr.k_in, (16,), pr.gamma, pr.beta, pr.eps).numpy()
+    assert np.allclose(np.linalg.norm(r["k"], axis=-1), np.linalg.norm(kn, axis=-1), rtol=1e-13)
+
+
+def test_prep_relative_position():
+    # q at m and k at n score the same as q at m+d and k at n+d (rotations compose)
+    b = _prep_batch(q_lens=(1, 1, 1, 1), seq_lens=(11, 7, 40, 36), hi=1, di=16)
+    pr = _prep(b, 16)
+    q1 = pr.q_in[0:1].repeat(4, 1, 1)
+    k1 = pr.k_in[0:1].repeat(4, 1)
+    pr2 = synth.Prep(q_in=q1, k_in=k1, gamma=torch.ones(16, dtype=torch.float64),
+                     beta=torch.zeros(16, dtype=torch.float64), eps=1e-6, cos=pr.cos, sin=pr.sin,
+                     rope_dim=16, interleaved=False)
+    r = oracle.indexer_prepare(b, pr2)
+    q, k = r["q"][:, 0], r["k"]
+    # rows 0/1 sit at 10/6 and rows 2/3 at 39/35: both pairs are 4 apart
+    assert abs(q[0] @ k[1] - q[2] @ k[3]) < 1e-5 * (1 + abs(q[0] @ k[1]))
+    assert abs(q[0] @ k[1] - q[0] @ k[0]) > 1e-3      # the offset does matter
+
+
+def test_prep_keys_land_at_their_slots():
+    b = _prep_batch(q_lens=(2, 3), seq_lens=(9, 6), P=4, seed=3)
+    pr = _prep(b, 16)
+    r = oracle.indexer_prepare(b, pr)
+    pool0 = b.k_pool.reshape(-1, 16).numpy()
+    pt = b.page_table.numpy().copy()         # the table is edited below
+    want = pool0.copy()
+    for t, (req, p) in enumerate(zip(b.row_request(), b.positions())):
+        want[pt[req, p // 4] * 4 + p % 4] = r["k"][t]
+    assert np.array_equal(r["pool"], want)
+    # an unmapped page: that row's key goes nowhere
+    b.page_table[1, 1] = -1                     # request 1's positions 4, 5
+    r2 = oracle.indexer_prepare(b, pr)
+    for t, (req, p) in enumerate(zip(b.row_request(), b.positions())):
+        if req == 1 and p >= 4:
+            want[pt[req, p // 4] * 4 + p % 4] = pool0[pt[req, p // 4] * 4 + p % 4]
+    assert np.array_equal(r2["pool"], want)
