@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--sets", type=int, default=0, help="input sets rotated (0 = auto)")
     ap.add_argument("--mode", default="perf", choices=["perf", "parity"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--prep", action="store_true",
+                    help="each step starts with the indexer preparation (query RoPE, key LayerNorm "
+                         "and RoPE, paged key store)")
     ap.add_argument("--key-fp8", action="store_true",
                     help="indexer keys cached as e4m3 codes with one f32 scale per token "
                          "(queries stay bf16); reports the top-k overlap with bf16 keys")
@@ -119,6 +122,12 @@ def algorithmic(sb, path):
         + n_scored * 4,
         flops=n_scored * 2 * cfg.hi * cfg.di)
     st["topk"] = dict(bytes=n_scored * 4 + T * K * 4, flops=0)
+    if path.prep is not None:
+        pr = path.prep
+        # queries read and written, keys read and stored, two table rows per row, LayerNorm params
+        st["indexer_prepare"] = dict(
+            bytes=2 * T * cfg.hi * cfg.di * idx_es + 2 * T * cfg.di * idx_es + T * pr.rope_dim * 4
+            + 2 * cfg.di * 4, flops=0)
     from sparse_attention_07_amd.synth import kv_row_bytes
     row = kv_row_bytes(cfg.kv_fmt, cfg.dc, cfg.dr)
     idx = path.idx.cpu().numpy()
@@ -199,11 +208,23 @@ def main():
     for i in range(sets):
         sb = synth.make_batch(cfg_id, mode=args.mode, device=dev, seed_offset=i,
                               key_fmt=synth.FMT_FP8_E4M3_B128 if args.key_fp8 else None)
-        paths.append(DSAPath(sb))
-    workload = base.name + ("+fp8keys" if args.key_fp8 else "")
+        paths.append(DSAPath(sb, prep=synth.make_prep(sb, seed=4242 + i) if args.prep else None))
+    workload = base.name + ("+fp8keys" if args.key_fp8 else "") + ("+prep" if args.prep else "")
     torch.cuda.synchronize()
 
-    stages = ["index_scores", "topk", "sparse_mla"]
+    stages = (["indexer_prepare"] if args.prep else []) + ["index_scores", "topk", "sparse_mla"]
+
+    def run_stage(p, s):
+        if s == "indexer_prepare":
+            p.indexer_prepare()
+        elif s == "index_scores":
+            p.index_scores()
+        elif s == "topk":
+            p.topk()
+        else:
+            for layer in range(len(p.kv)):
+                p.mla(layer)
+
     for i in range(args.warmup):
         paths[i % sets].step()
     torch.cuda.synchronize()
@@ -213,23 +234,17 @@ def main():
     ev = {s: [] for s in stages}
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     n_eager = min(args.steps, 4 * sets)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_eager)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(n_eager)]
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(n_eager):
         p = paths[i % sets]
         e = evs[i]
         e[0].record(stream)
-        p.index_scores()
-        e[1].record(stream)
-        p.topk()
-        e[2].record(stream)
-        for layer in range(len(p.kv)):
-            p.mla(layer)
-        e[3].record(stream)
-        ev["index_scores"].append((e[0], e[1]))
-        ev["topk"].append((e[1], e[2]))
-        ev["sparse_mla"].append((e[2], e[3]))
+        for j, s in enumerate(stages):
+            run_stage(p, s)
+            e[j + 1].record(stream)
+            ev[s].append((e[j], e[j + 1]))
     stop.record(stream)
     torch.cuda.synchronize()
     eager_ms_step = start.elapsed_time(stop) / n_eager
@@ -253,19 +268,17 @@ def main():
     ms_step = start.elapsed_time(stop) / n_steps
 
     # Per-kernel durations: one graph per stage over all input sets, events
-    # around its replays on the launch stream.
+    # around its replays on the launch stream.  A graph holds at least 8
+    # launches (the rotation repeated when there are fewer sets), so that a
+    # short kernel's replays are not bound by the host's graph submissions.
     stage_ms = {}
+    rounds = max(1, (8 + sets - 1) // sets)
     for s in stages:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for p in paths:
-                if s == "index_scores":
-                    p.index_scores()
-                elif s == "topk":
-                    p.topk()
-                else:
-                    for layer in range(len(p.kv)):
-                        p.mla(layer)
+            for _ in range(rounds):
+                for p in paths:
+                    run_stage(p, s)
         g.replay()
         torch.cuda.synchronize()
         start.record(stream)
@@ -273,7 +286,7 @@ def main():
             g.replay()
         stop.record(stream)
         torch.cuda.synchronize()
-        stage_ms[s] = start.elapsed_time(stop) / n_steps
+        stage_ms[s] = start.elapsed_time(stop) / (n_steps * rounds)
 
     T = paths[0].sb.T
     alg = [algorithmic(p.sb, p) for p in paths]
@@ -324,12 +337,14 @@ def main():
                                   cfg.hi, cfg.di, cfg.heads, cfg.dc, cfg.dr,
                                   {0: "f32", 1: "bf16", 2: "fp8-e4m3-b128"}[cfg.kv_fmt],
                                   cfg.page_size, cfg.layers)
-                               + (", fp8 index keys (per-token scale)" if args.key_fp8 else ""),
+                               + (", fp8 index keys (per-token scale)" if args.key_fp8 else "")
+                               + (", indexer preparation in the step" if args.prep else ""),
                    "query_rows": T},
         "indexer_topk_rows_per_s": T / ((stage_ms["index_scores"] + stage_ms["topk"]) / 1e3),
         "sparse_mla_queries_per_s": T / (stage_ms["sparse_mla"] / len(paths[0].kv) / 1e3),
         "timing": "HIP graph replay of whole steps (one per input set); stage times from "
-                  "per-stage graphs; eager figures include host launch gaps",
+                  "per-stage graphs of >= 8 launches (input sets repeated when fewer); eager "
+                  "figures include host launch gaps",
         "eager_ms_per_step": eager_ms_step,
         "eager_stage_ms": eager_stage_ms,
         "stages": report,
@@ -337,7 +352,7 @@ def main():
     }
     if args.key_fp8:
         out["topk_overlap_vs_bf16_keys"] = key_fp8_overlap(paths[0], cfg_id, args.mode)
-    if not args.no_cpu and not args.key_fp8:
+    if not args.no_cpu and not args.key_fp8 and not args.prep:
         out["cpu_baseline"] = cpu_baseline(cfg_id)
     print(json.dumps(out), flush=True)
 

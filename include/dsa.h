@@ -1,7 +1,9 @@
 /*
  * dsa.h -- C ABI of the MI355X (gfx950) DeepSeek-Sparse-Attention hot path.
  *
- * Three steps run per full layer, in this order, all on one HIP stream:
+ * Three steps run per full layer, in this order, all on one HIP stream
+ * (optionally preceded by dsa_indexer_prepare, which rotates the indexer
+ * queries and stores this step's normalised, rotated index keys):
  *
  *   dsa_index_scores   lightning-indexer score of every earlier cached token
  *   dsa_topk           per query row, the index_topk best tokens
@@ -137,6 +139,47 @@ const char *dsa_status_string(dsa_status status);
 dsa_status dsa_index_scores(const dsa_batch *batch, const void *q_idx, int32_t q_format,
                             const float *w, const dsa_pool *k_idx, int32_t n_heads,
                             int32_t head_dim, float *scores, int64_t ld, void *stream);
+
+/*
+ * Indexer query/key preparation for this step's new rows, in one launch (the
+ * fused indexer preparation of lmdeploy PR 4737, section "Changes", and its
+ * section "DSA indexer fusion"; mlx-lm PR 1419's description: GLM-5.2's
+ * indexer uses non-interleaved RoPE and LayerNorm eps 1e-6, DeepSeek-V3.2
+ * interleaved RoPE and eps 1e-5).  For each query row t at position p = pos(t):
+ *
+ *   q_out[t,h,:] = rope(q_in[t,h,:], p)                      h < n_heads
+ *   key(p)       = rope(layernorm(k_in[t,:]), p)   stored into k_idx at token p
+ *
+ *   layernorm(x) = (x - mean(x)) / sqrt(var(x) + ln_eps) * ln_weight + ln_bias
+ *                  (var: mean squared deviation)
+ *   rope(x, p)   turns the first rope_dim dims in rope_dim/2 pairs -- pair i is
+ *                dims (i, i + rope_dim/2), or (2i, 2i+1) when rope_interleaved --
+ *                by the angle with cosine rope_cos[p*rope_dim/2 + i] and sine
+ *                rope_sin[p*rope_dim/2 + i]: (a, b) -> (a cos - b sin, a sin + b cos);
+ *                the other dims pass through.
+ *
+ * q_in, q_out  device [T, n_heads, head_dim], `format` (DSA_BF16 or DSA_F32);
+ *              q_out may equal q_in (in place) but may not overlap it otherwise
+ * k_in         device [T, head_dim], `format`
+ * ln_weight, ln_bias  device [head_dim] f32
+ * rope_cos, rope_sin  device [rope_rows, rope_dim/2] f32 (caller-built tables,
+ *              any frequency scaling included); rope_rows >= max_seq_len.  May
+ *              be NULL when rope_dim == 0.
+ * k_idx        the index-key pool (format == `format`, dim == head_dim).  Its
+ *              base IS WRITTEN: the key of row t goes to token pos(t) of its
+ *              request (nothing is written when that page is not mapped).
+ * Work is done in f32; bf16 results are rounded to nearest even.  A row whose
+ * position is outside [0, rope_rows) is left untouched.  Run it before
+ * dsa_index_scores of the same step (which reads the keys it stores).
+ * Built: head_dim a multiple of 16 up to 128, rope_dim a multiple of 16 up to
+ * head_dim, n_heads <= 1024.
+ */
+dsa_status dsa_indexer_prepare(const dsa_batch *batch, const void *q_in, void *q_out,
+                               const void *k_in, int32_t format, const float *ln_weight,
+                               const float *ln_bias, float ln_eps, const float *rope_cos,
+                               const float *rope_sin, int32_t rope_rows, int32_t rope_dim,
+                               int32_t rope_interleaved, const dsa_pool *k_idx, int32_t n_heads,
+                               int32_t head_dim, void *stream);
 
 /* Workspace bytes dsa_topk needs for these sizes (0 today; query it anyway). */
 size_t dsa_topk_workspace_bytes(int32_t num_q_rows, int32_t max_seq_len, int32_t k);

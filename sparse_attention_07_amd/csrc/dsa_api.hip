@@ -175,6 +175,41 @@ dsa_status dsa_index_scores(const dsa_batch* batch, const void* q_idx, int32_t q
   return DSA_ERR_UNSUPPORTED;
 }
 
+dsa_status dsa_indexer_prepare(const dsa_batch* batch, const void* q_in, void* q_out,
+                               const void* k_in, int32_t format, const float* ln_weight,
+                               const float* ln_bias, float ln_eps, const float* rope_cos,
+                               const float* rope_sin, int32_t rope_rows, int32_t rope_dim,
+                               int32_t rope_interleaved, const dsa_pool* k_idx, int32_t n_heads,
+                               int32_t head_dim, void* stream) {
+  BatchArgs ba;
+  dsa_status st = check_batch(batch, &ba);
+  if (st != DSA_OK) return st;
+  if (ba.num_q_rows == 0) return DSA_OK;
+  if (q_in == nullptr || q_out == nullptr || k_in == nullptr || ln_weight == nullptr ||
+      ln_bias == nullptr || k_idx == nullptr)
+    return DSA_ERR_NULL;
+  if (rope_dim > 0 && (rope_cos == nullptr || rope_sin == nullptr)) return DSA_ERR_NULL;
+  if (format != DSA_BF16 && format != DSA_F32) return DSA_ERR_UNSUPPORTED;
+  if (k_idx->format == DSA_FP8_E4M3_B128) return DSA_ERR_UNSUPPORTED;
+  if (k_idx->format != format || k_idx->dim != head_dim) return DSA_ERR_SHAPE;
+  if (n_heads < 1 || head_dim < 1 || rope_dim < 0 || rope_dim > head_dim || !(ln_eps >= 0.f))
+    return DSA_ERR_SHAPE;
+  if (n_heads > 1024 || head_dim > 128 || head_dim % 16 != 0 || rope_dim % 16 != 0)
+    return DSA_ERR_UNSUPPORTED;
+  if (rope_dim > 0 && rope_rows < ba.max_seq_len) return DSA_ERR_SHAPE;
+  if (rope_dim == 0) rope_rows = INT32_MAX;  // no table is read
+  const int es = format == DSA_BF16 ? 2 : 4;
+  PoolArgs pa;
+  if ((st = check_pool(k_idx, (int64_t)head_dim * es, 16, &pa)) != DSA_OK) return st;
+  if (!aligned(q_in, 16) || !aligned(q_out, 16) || !aligned(k_in, 16) || !aligned(ln_weight, 4) ||
+      !aligned(ln_bias, 4) || (rope_dim > 0 && (!aligned(rope_cos, 16) || !aligned(rope_sin, 16))))
+    return DSA_ERR_ALIGN;
+  return hip_status(dsa::launch_indexer_prepare(ba, q_in, q_out, k_in, format, ln_weight, ln_bias,
+                                                ln_eps, rope_cos, rope_sin, rope_rows, rope_dim,
+                                                rope_interleaved != 0, pa, n_heads, head_dim,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 size_t dsa_topk_workspace_bytes(int32_t num_q_rows, int32_t max_seq_len, int32_t k) {
   (void)num_q_rows;
   (void)max_seq_len;

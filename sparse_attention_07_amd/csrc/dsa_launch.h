@@ -35,6 +35,12 @@ hipError_t launch_index_scores_f32(const BatchArgs& ba, const void* q_idx, const
                                    const PoolArgs& pool, int n_heads, int head_dim, float* scores,
                                    int64_t ld, hipStream_t stream);
 
+hipError_t launch_indexer_prepare(const BatchArgs& ba, const void* q_in, void* q_out, const void* k_in,
+                                  int format, const float* gamma, const float* beta, float eps,
+                                  const float* cos_tab, const float* sin_tab, int rope_rows,
+                                  int rope_dim, int interleaved, const PoolArgs& pool, int n_heads,
+                                  int head_dim, hipStream_t stream);
+
 hipError_t launch_topk(const BatchArgs& ba, const float* scores, int64_t ld, int k, int32_t* idx,
                        hipStream_t stream);
 

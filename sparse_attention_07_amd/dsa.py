@@ -20,7 +20,8 @@ STATUS_NAMES = {0: "DSA_OK", 1: "DSA_ERR_NULL", 2: "DSA_ERR_SHAPE", 3: "DSA_ERR_
                 4: "DSA_ERR_WORKSPACE", 5: "DSA_ERR_HIP", 6: "DSA_ERR_ALIGN"}
 DSA_F32, DSA_BF16, DSA_FP8_E4M3_B128 = 0, 1, 2
 
-ENTRY_POINTS = ("dsa_version", "dsa_status_string", "dsa_index_scores", "dsa_topk_workspace_bytes",
+ENTRY_POINTS = ("dsa_version", "dsa_status_string", "dsa_indexer_prepare", "dsa_index_scores",
+                "dsa_topk_workspace_bytes",
                 "dsa_topk", "dsa_sparse_mla_workspace_bytes", "dsa_sparse_mla_decode",
                 "dsa_sparse_mla_prefill")
 
@@ -56,6 +57,9 @@ def _load():
     lib.dsa_status_string.argtypes = [i32]
     lib.dsa_status_string.restype = ctypes.c_char_p
     lib.dsa_index_scores.argtypes = [bp, vp, i32, vp, pp, i32, i32, vp, i64, vp]
+    lib.dsa_indexer_prepare.argtypes = [bp, vp, vp, vp, i32, vp, vp, ctypes.c_float, vp, vp, i32, i32,
+                                        i32, pp, i32, i32, vp]
+    lib.dsa_indexer_prepare.restype = i32
     lib.dsa_topk_workspace_bytes.argtypes = [i32, i32, i32]
     lib.dsa_topk_workspace_bytes.restype = sz
     lib.dsa_topk.argtypes = [bp, vp, i64, i32, vp, vp, sz, vp]
@@ -143,6 +147,15 @@ def dsa_index_scores(batch, q_idx, q_format, w, k_pool: dsa_pool, n_heads, head_
     _check("dsa_index_scores", _lib.dsa_index_scores(
         ctypes.byref(batch), _ptr(q_idx), q_format, _ptr(w), ctypes.byref(k_pool), n_heads,
         head_dim, _ptr(scores), ld, _stream(stream)))
+
+
+def dsa_indexer_prepare(batch, q_in, q_out, k_in, fmt, ln_weight, ln_bias, ln_eps, rope_cos, rope_sin,
+                        rope_rows, rope_dim, rope_interleaved, k_pool: dsa_pool, n_heads, head_dim,
+                        stream=None):
+    _check("dsa_indexer_prepare", _lib.dsa_indexer_prepare(
+        ctypes.byref(batch), _ptr(q_in), _ptr(q_out), _ptr(k_in), fmt, _ptr(ln_weight), _ptr(ln_bias),
+        ln_eps, _ptr(rope_cos), _ptr(rope_sin), rope_rows, rope_dim, 1 if rope_interleaved else 0,
+        ctypes.byref(k_pool), n_heads, head_dim, _stream(stream)))
 
 
 def dsa_topk_workspace_bytes(num_q_rows, max_seq_len, k) -> int:

@@ -14,9 +14,12 @@ from .synth import torch_dtype
 
 
 class DSAPath:
-    def __init__(self, sb, prefill: bool | None = None):
+    def __init__(self, sb, prefill: bool | None = None, prep=None):
         cfg = sb.cfg
         self.sb = sb
+        # optional indexer preparation inputs (synth.Prep): when given, each step
+        # first rotates them into sb.q_idx and stores the keys into the key pool
+        self.prep = prep
         self.cfg = cfg
         dev = sb.q_idx.device
         self.batch = dsa.batch_from(sb)
@@ -39,6 +42,12 @@ class DSAPath:
         self.topk_ws = (torch.empty((self.topk_ws_bytes,), dtype=torch.uint8, device=dev)
                         if self.topk_ws_bytes else None)
 
+    def indexer_prepare(self, stream=None):
+        c, pr = self.cfg, self.prep
+        dsa.dsa_indexer_prepare(self.batch, pr.q_in, self.sb.q_idx, pr.k_in, c.idx_fmt, pr.gamma, pr.beta,
+                                pr.eps, pr.cos, pr.sin, pr.cos.shape[0], pr.rope_dim, pr.interleaved,
+                                self.k_pool, c.hi, c.di, stream)
+
     def index_scores(self, stream=None):
         c = self.cfg
         dsa.dsa_index_scores(self.batch, self.sb.q_idx, c.idx_fmt, self.sb.w, self.k_pool, c.hi, c.di,
@@ -57,6 +66,8 @@ class DSAPath:
 
     def step(self, stream=None):
         """One pass of the whole path: full layer, then the IndexShare layers."""
+        if self.prep is not None:
+            self.indexer_prepare(stream)
         self.index_scores(stream)
         self.topk(stream)
         for layer in range(len(self.kv)):

@@ -48,8 +48,10 @@ L = dsa.lib()
 
 def _scores(batch, q_fmt=dsa.DSA_BF16, pool=None, H=64, D=128, ld=128, q=FAKE, w=FAKE, out=FAKE):
     pool = pool or _pool(dsa.DSA_BF16, 128, 256)
-    return L.dsa_index_scores(ctypes.byref(batch) if batch is not None else None, q, q_fmt, w,
-                              ctypes.byref(pool), H, D, out, ld, None)
+    st = L.dsa_index_scores(ctypes.byref(batch) if batch is not None else None, q, q_fmt, w,
+                            ctypes.byref(pool), H, D, out, ld, None)
+    assert st != 5, "a validation case got as far as a kernel launch"
+    return st
 
 
 def test_index_scores_validation():
@@ -89,6 +91,40 @@ def test_index_scores_fp8_key_validation():
     assert _scores(_batch(), pool=fp8(128, ok, dim=64)) == 2       # pool dim != head_dim
     assert _scores(_batch(), pool=fp8(128, ok), H=32) == 3
     assert _scores(_batch(), q_fmt=dsa.DSA_F32, pool=fp8(128, ok)) == 2  # fp8 keys need bf16 q
+
+
+
+def _prep(batch, fmt=dsa.DSA_BF16, pool=None, H=64, D=128, R=64, rows=100, eps=1e-6, q_in=FAKE, q_out=FAKE,
+          k_in=FAKE, g=FAKE, b=FAKE, cos=FAKE, sin=FAKE):
+    pool = pool or _pool(fmt, D, D * (2 if fmt == dsa.DSA_BF16 else 4))
+    st = L.dsa_indexer_prepare(ctypes.byref(batch) if batch is not None else None, q_in, q_out, k_in, fmt,
+                               g, b, eps, cos, sin, rows, R, 0, ctypes.byref(pool), H, D, None)
+    assert st != 5, "a validation case got as far as a kernel launch"
+    return st
+
+
+def test_indexer_prepare_validation():
+    assert _prep(None) == 1
+    assert _prep(_batch(T=0)) == 0
+    assert _prep(_batch(), q_out=None) == 1
+    assert _prep(_batch(), cos=None) == 1
+    assert _prep(_batch(), R=0, cos=None, sin=None, q_in=ODD) == 6   # no table needed without rotation
+    assert _prep(_batch(), fmt=dsa.DSA_FP8_E4M3_B128) == 3
+    assert _prep(_batch(), pool=_pool(dsa.DSA_FP8_E4M3_B128, 128, 128)) == 3
+    assert _prep(_batch(), pool=_pool(dsa.DSA_F32, 128, 512)) == 2      # pool format differs
+    assert _prep(_batch(), pool=_pool(dsa.DSA_BF16, 64, 128)) == 2      # pool dim differs
+    assert _prep(_batch(), R=72) == 3                                    # not a multiple of 16
+    assert _prep(_batch(), R=144) == 2                                   # more than the head
+    assert _prep(_batch(), D=136, pool=_pool(dsa.DSA_BF16, 136, 272)) == 3
+    assert _prep(_batch(), D=256, pool=_pool(dsa.DSA_BF16, 256, 512), R=64) == 3
+    assert _prep(_batch(), rows=99) == 2                                 # table shorter than max_seq_len
+    assert _prep(_batch(), eps=-1.0) == 2
+    assert _prep(_batch(), eps=float("nan")) == 2
+    assert _prep(_batch(), H=0) == 2
+    assert _prep(_batch(), q_in=ODD) == 6
+    assert _prep(_batch(), cos=ODD) == 6
+    assert _prep(_batch(), pool=_pool(dsa.DSA_BF16, 128, 256, base=ODD)) == 6
+    assert _prep(_batch(), pool=_pool(dsa.DSA_BF16, 128, 128)) == 2     # row stride below the key
 
 
 def test_topk_validation():

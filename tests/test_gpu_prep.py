@@ -1,0 +1,137 @@
+"""Indexer preparation on the GPU vs the CPU oracle, through the C ABI.
+
+The kernel works in f32 and rounds bf16 results to nearest even once, so an
+element g is compared with the oracle's float64 value r as
+|g - r| <= 2^-8 |r| + 1e-4 for bf16 (twice the rounding bound, plus room
+for f32 rounding inside LayerNorm and the rotation) and 1e-5 (1 + |r|) for
+f32.  Pool bytes outside the rows' slots must not change at all.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_07_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _say(*a):
+    print("[gpu-test]", *a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sparse_attention_07_amd import dsa  # noqa: F401  (raises if libdsa.so is missing)
+    yield
+
+
+def _close(g, r, bf16, what):
+    g = np.asarray(g, dtype=np.float64)
+    tol = (2.0 ** -8 * np.abs(r) + 1e-4) if bf16 else 1e-5 * (1 + np.abs(r))
+    bad = np.abs(g - r) > tol
+    assert not bad.any(), "%s: %d of %d outside tolerance, worst |g-r| %.3g" % (
+        what, int(bad.sum()), bad.size, float(np.abs(g - r).max()))
+
+
+def _run_and_check(sb, pr, in_place=False):
+    from sparse_attention_07_amd import dsa
+    cfg = sb.cfg
+    pool_before = sb.k_pool.clone()
+    ref = oracle.indexer_prepare(sb, pr)            # host copies of the same inputs
+    kp = dsa.make_key_pool(sb)
+    b = dsa.batch_from(sb)
+    if in_place:
+        q = pr.q_in.clone()
+        q_in = q_out = q
+    else:
+        q_in, q_out = pr.q_in, torch.full_like(pr.q_in, 7.0)
+    dsa.dsa_indexer_prepare(b, q_in, q_out, pr.k_in, cfg.idx_fmt, pr.gamma, pr.beta, pr.eps, pr.cos, pr.sin,
+                            pr.cos.shape[0], pr.rope_dim, pr.interleaved, kp, cfg.hi, cfg.di)
+    torch.cuda.synchronize()
+    bf16 = cfg.idx_fmt == synth.FMT_BF16
+    _close(q_out.double().cpu().numpy(), ref["q"], bf16, "q")
+    P = cfg.page_size
+    pool = sb.k_pool.double().cpu().reshape(-1, cfg.di).numpy()
+    pt = sb.page_table.cpu().numpy()
+    written = np.zeros(pool.shape[0], dtype=bool)
+    for t, (req, p) in enumerate(zip(sb.row_request(), sb.positions())):
+        page = pt[req, p // P] if p // P < pt.shape[1] else -1
+        if 0 <= page < sb.k_pool.shape[0]:
+            slot = page * P + p % P
+            written[slot] = True
+            _close(pool[slot], ref["k"][t], bf16, "key of row %d" % t)
+    before = pool_before.cpu().reshape(-1, cfg.di)
+    after = sb.k_pool.cpu().reshape(-1, cfg.di)
+    keep = torch.from_numpy(~written)
+    assert torch.equal(before[keep], after[keep]), "bytes outside the rows' slots changed"
+    return ref
+
+
+CASES = {
+    # GLM indexer: non-interleaved RoPE over half the head, eps 1e-6
+    "decode16_glm": dict(cfg=1, kw=dict(batch=6, ctx=(100, 3000), topk=512), prep=dict()),
+    # DeepSeek-V3.2: interleaved, eps 1e-5; drafts of 5 rows
+    "mtp_v32": dict(cfg=4, kw=dict(batch=3, ctx=(3000, 9000), topk=512),
+                    prep=dict(interleaved=True, eps=1e-5)),
+    "ragged_empty": dict(cfg=4, kw=dict(q_lens=[5, 0, 3, 1, 0, 5, 2], ctx=(600, 3000), topk=512), prep=dict()),
+    "page5": dict(cfg=1, kw=dict(batch=4, ctx=(1, 1300), topk=256, page_size=5), prep=dict(interleaved=True)),
+    "prefill_rows": dict(cfg=3, kw=dict(q_len=130, ctx=(700, 700), topk=512), prep=dict()),
+    "no_rope": dict(cfg=1, kw=dict(batch=3, ctx=(100, 900), topk=256), prep=dict(rope_dim=0)),
+    "full_rope": dict(cfg=1, kw=dict(batch=3, ctx=(100, 900), topk=256), prep=dict(rope_dim=128)),
+    "tiny_f32": dict(cfg=0, kw=dict(), prep=dict(rope_dim=16)),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_prepare_matches_oracle(name):
+    c = CASES[name]
+    sb = synth.make_batch(c["cfg"], device=DEV, layers=0, **c["kw"])
+    pr = synth.make_prep(sb, **c["prep"])
+    if pr.rope_dim == 0:
+        pr.cos, pr.sin = pr.cos[:, :0].contiguous(), pr.sin[:, :0].contiguous()
+    _say(name, "T=%d B=%d R=%d interleaved=%s" % (sb.T, sb.B, pr.rope_dim, pr.interleaved))
+    _run_and_check(sb, pr)
+
+
+def test_prepare_in_place_and_unmapped_page():
+    sb = synth.make_batch(1, device=DEV, layers=0, batch=4, ctx=(200, 800), topk=256)
+    pt = sb.page_table.cpu()
+    pos = sb.positions()
+    # unmap the page of request 2's new token: its key must go nowhere
+    pt[2, pos[2] // sb.cfg.page_size] = -1
+    sb.page_table = pt.to(DEV)
+    pr = synth.make_prep(sb, interleaved=True)
+    _say("in place, one unmapped page")
+    _run_and_check(sb, pr, in_place=True)
+
+
+def test_prepare_then_scores_on_the_written_keys():
+    # the path order: prepare, then scores read the keys it stored (same step)
+    from sparse_attention_07_amd.path import DSAPath
+    sb = synth.make_batch(4, device=DEV, layers=1, batch=2, ctx=(600, 1500), topk=256)
+    pr = synth.make_prep(sb)
+    ref = oracle.indexer_prepare(sb, pr)
+    p = DSAPath(sb, prep=pr)
+    _say("prepare + path step")
+    p.step()
+    torch.cuda.synchronize()
+    # every row's own key now holds the prepared key, and its score against itself
+    # is sum_h w * relu(q_h . k) of the prepared vectors
+    k_pool = sb.k_pool.float().cpu().reshape(-1, sb.cfg.di)
+    pt = sb.page_table.cpu().numpy()
+    P = sb.cfg.page_size
+    for t, (req, ps) in enumerate(zip(sb.row_request(), sb.positions())):
+        key = k_pool[pt[req, ps // P] * P + ps % P].double().numpy()
+        _close(key, ref["k"][t], True, "key of row %d" % t)
+        q = sb.q_idx[t].double().cpu().numpy()
+        w = sb.w[t].double().cpu().numpy()
+        want = float(np.sum(w * np.maximum(q @ key, 0.0)))
+        got = float(p.scores[t, ps].item())
+        assert abs(got - want) <= 1e-4 * (1 + np.abs(w).sum() * np.abs(q @ key).max()), (t, got, want)
