@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--prep", action="store_true",
                     help="each step starts with the indexer preparation (query RoPE, key LayerNorm "
                          "and RoPE, paged key store)")
+    ap.add_argument("--score-budget", type=float, default=None, metavar="MB",
+                    help="scores + top-k through dsa_index_topk with a score workspace of at most "
+                         "this many MB (query rows in chunks) instead of a [T, ld] score buffer")
     ap.add_argument("--key-fp8", action="store_true",
                     help="indexer keys cached as e4m3 codes with one f32 scale per token "
                          "(queries stay bf16); reports the top-k overlap with bf16 keys")
@@ -122,6 +125,8 @@ def algorithmic(sb, path):
         + n_scored * 4,
         flops=n_scored * 2 * cfg.hi * cfg.di)
     st["topk"] = dict(bytes=n_scored * 4 + T * K * 4, flops=0)
+    st["index_topk"] = dict(bytes=st["index_scores"]["bytes"] + st["topk"]["bytes"],
+                            flops=st["index_scores"]["flops"])
     if path.prep is not None:
         pr = path.prep
         # queries read and written, keys read and stored, two table rows per row, LayerNorm params
@@ -208,15 +213,22 @@ def main():
     for i in range(sets):
         sb = synth.make_batch(cfg_id, mode=args.mode, device=dev, seed_offset=i,
                               key_fmt=synth.FMT_FP8_E4M3_B128 if args.key_fp8 else None)
-        paths.append(DSAPath(sb, prep=synth.make_prep(sb, seed=4242 + i) if args.prep else None))
-    workload = base.name + ("+fp8keys" if args.key_fp8 else "") + ("+prep" if args.prep else "")
+        paths.append(DSAPath(sb, prep=synth.make_prep(sb, seed=4242 + i) if args.prep else None,
+                             score_budget=None if args.score_budget is None
+                             else int(args.score_budget * 2 ** 20)))
+    workload = (base.name + ("+fp8keys" if args.key_fp8 else "") + ("+prep" if args.prep else "")
+                + ("+budget" if args.score_budget is not None else ""))
     torch.cuda.synchronize()
 
-    stages = (["indexer_prepare"] if args.prep else []) + ["index_scores", "topk", "sparse_mla"]
+    stages = ((["indexer_prepare"] if args.prep else [])
+              + (["index_topk"] if args.score_budget is not None else ["index_scores", "topk"])
+              + ["sparse_mla"])
 
     def run_stage(p, s):
         if s == "indexer_prepare":
             p.indexer_prepare()
+        elif s == "index_topk":
+            p.index_topk()
         elif s == "index_scores":
             p.index_scores()
         elif s == "topk":
@@ -338,9 +350,14 @@ def main():
                                   {0: "f32", 1: "bf16", 2: "fp8-e4m3-b128"}[cfg.kv_fmt],
                                   cfg.page_size, cfg.layers)
                                + (", fp8 index keys (per-token scale)" if args.key_fp8 else "")
-                               + (", indexer preparation in the step" if args.prep else ""),
+                               + (", indexer preparation in the step" if args.prep else "")
+                               + (", scores + top-k in a %.0f MB workspace (%d rows per chunk)"
+                                  % (paths[0].itk_ws_bytes / 2 ** 20,
+                                     paths[0].itk_ws_bytes // (4 * ((paths[0].sb.max_seq_len + 63) // 64 * 64)))
+                                  if args.score_budget is not None else ""),
                    "query_rows": T},
-        "indexer_topk_rows_per_s": T / ((stage_ms["index_scores"] + stage_ms["topk"]) / 1e3),
+        "indexer_topk_rows_per_s": T / ((stage_ms["index_topk"] if "index_topk" in stage_ms
+                                         else stage_ms["index_scores"] + stage_ms["topk"]) / 1e3),
         "sparse_mla_queries_per_s": T / (stage_ms["sparse_mla"] / len(paths[0].kv) / 1e3),
         "timing": "HIP graph replay of whole steps (one per input set); stage times from "
                   "per-stage graphs of >= 8 launches (input sets repeated when fewer); eager "
@@ -352,7 +369,7 @@ def main():
     }
     if args.key_fp8:
         out["topk_overlap_vs_bf16_keys"] = key_fp8_overlap(paths[0], cfg_id, args.mode)
-    if not args.no_cpu and not args.key_fp8 and not args.prep:
+    if not args.no_cpu and not args.key_fp8 and not args.prep and args.score_budget is None:
         out["cpu_baseline"] = cpu_baseline(cfg_id)
     print(json.dumps(out), flush=True)
 

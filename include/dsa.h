@@ -181,6 +181,36 @@ dsa_status dsa_indexer_prepare(const dsa_batch *batch, const void *q_in, void *q
                                int32_t rope_interleaved, const dsa_pool *k_idx, int32_t n_heads,
                                int32_t head_dim, void *stream);
 
+/*
+ * Scores and top-k in one call with a bounded score workspace (the bounded
+ * "KPool" scoring of lmdeploy PR 4968, section "Capacity improvement":
+ * a reserved score budget, deterministic top-k taken per query chunk at
+ * once, the same selected indices as the unbounded path).  The query rows
+ * are walked in chunks of as many rows as the workspace holds; each chunk's
+ * scores (dsa_index_scores' formula) go to the workspace and its top-k
+ * (dsa_topk's rule) is taken before the next chunk overwrites them.  idx is
+ * bit-identical to dsa_index_scores followed by dsa_topk, whatever the
+ * chunking, so a [T, max_seq_len] score buffer is never needed.
+ *
+ * q_idx, q_format, w, k_idx, n_heads, head_dim: as dsa_index_scores
+ *          (every token below seq_len should be mapped: the score entry of an
+ *          unmapped token is not written, so its place in the ranking is
+ *          unspecified, though every access stays in bounds)
+ * k, idx   as dsa_topk
+ * ws       device workspace of ws_bytes; it must hold at least one score row
+ *          of dsa_index_topk_workspace_bytes(1, max_seq_len, ...) bytes, else
+ *          DSA_ERR_WORKSPACE.  Its contents need no initialisation.
+ */
+dsa_status dsa_index_topk(const dsa_batch *batch, const void *q_idx, int32_t q_format, const float *w,
+                          const dsa_pool *k_idx, int32_t n_heads, int32_t head_dim, int32_t k,
+                          int32_t *idx, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes dsa_index_topk uses within a budget: as many score rows of
+ * round_up(max_seq_len, 64) f32 as fit in budget_bytes, at most num_q_rows.
+ * Returns 0 when the budget is below the minimum of one score row (or when
+ * num_q_rows <= 0): such a budget cannot run the call. */
+size_t dsa_index_topk_workspace_bytes(int32_t num_q_rows, int32_t max_seq_len, int64_t budget_bytes);
+
 /* Workspace bytes dsa_topk needs for these sizes (0 today; query it anyway). */
 size_t dsa_topk_workspace_bytes(int32_t num_q_rows, int32_t max_seq_len, int32_t k);
 

@@ -2,6 +2,7 @@
 // caller's stream.  Nothing here allocates, synchronises or reads device memory.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <set>
@@ -82,6 +83,63 @@ dsa_status check_pool(const dsa_pool* p, int64_t row_bytes, size_t align, PoolAr
 
 dsa_status hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
 
+// A validated indexer launch, shared by dsa_index_scores and dsa_index_topk.
+struct IndexArgs {
+  const void* q_idx;
+  const float* w;
+  PoolArgs pa;
+  int q_format, n_heads, head_dim;
+};
+
+dsa_status check_index(const BatchArgs& ba, const void* q_idx, int32_t q_format, const float* w,
+                       const dsa_pool* k_idx, int32_t n_heads, int32_t head_dim, IndexArgs* ia) {
+  if (q_idx == nullptr || w == nullptr || k_idx == nullptr) return DSA_ERR_NULL;
+  if (n_heads < 1 || head_dim < 1) return DSA_ERR_SHAPE;
+  const bool fp8_keys = q_format == DSA_BF16 && k_idx->format == DSA_FP8_E4M3_B128;
+  if ((k_idx->format != q_format && !fp8_keys) || k_idx->dim != head_dim) return DSA_ERR_SHAPE;
+  if (!aligned(w, 4)) return DSA_ERR_ALIGN;
+  dsa_status st;
+  *ia = IndexArgs{q_idx, w, PoolArgs{}, q_format, n_heads, head_dim};
+  if (q_format == DSA_BF16) {
+    if (n_heads != 64 || head_dim != 128) return DSA_ERR_UNSUPPORTED;
+    if (fp8_keys) {
+      // page-blocked: page_size rows of 128 codes, then page_size f32 scales
+      if ((st = check_pool(k_idx, 128, 16, &ia->pa)) != DSA_OK) return st;
+      if (k_idx->page_stride_bytes < (int64_t)ba.page_size * (k_idx->row_stride_bytes + 4))
+        return DSA_ERR_SHAPE;
+    } else if ((st = check_pool(k_idx, 256, 16, &ia->pa)) != DSA_OK) {
+      return st;
+    }
+    if (!aligned(q_idx, 16) || !aligned(w, 16)) return DSA_ERR_ALIGN;
+    return DSA_OK;
+  }
+  if (q_format == DSA_F32) {
+    if (n_heads > 64 || head_dim > 256 || n_heads * head_dim > 8192) return DSA_ERR_UNSUPPORTED;
+    if ((st = check_pool(k_idx, (int64_t)head_dim * 4, 4, &ia->pa)) != DSA_OK) return st;
+    if (!aligned(q_idx, 4)) return DSA_ERR_ALIGN;
+    return DSA_OK;
+  }
+  return DSA_ERR_UNSUPPORTED;
+}
+
+// Scores of the query rows [row_lo, row_hi), row t at scores + (t - row_lo) * ld.
+hipError_t launch_index(const BatchArgs& ba, const IndexArgs& ia, float* scores, int64_t ld,
+                        hipStream_t s, int row_lo, int row_hi) {
+  if (ia.q_format == DSA_BF16) {
+    if (ba.num_pages == 0) return hipSuccess;  // no token is mapped: nothing is written
+    return dsa::launch_index_scores_bf16(ba, ia.q_idx, ia.w, ia.pa, scores, ld, s, row_lo, row_hi);
+  }
+  return dsa::launch_index_scores_f32(ba, ia.q_idx, ia.w, ia.pa, ia.n_heads, ia.head_dim, scores, ld,
+                                      s, row_lo, row_hi);
+}
+
+// Bytes of one workspace score row of dsa_index_topk: max_seq_len rounded up
+// to 64 entries (256-byte rows).
+int64_t score_row_bytes(int32_t max_seq_len) {
+  const int64_t n = max_seq_len < 1 ? 1 : max_seq_len;
+  return (n + 63) / 64 * 64 * 4;
+}
+
 dsa_status sparse_mla(const dsa_batch* batch, const void* q, int32_t q_format, const dsa_pool* kv,
                       const int32_t* idx, int32_t k, int32_t n_heads, int32_t dc, int32_t dr,
                       float sm_scale, void* out, float* lse, void* ws, size_t ws_bytes,
@@ -145,34 +203,46 @@ dsa_status dsa_index_scores(const dsa_batch* batch, const void* q_idx, int32_t q
   dsa_status st = check_batch(batch, &ba);
   if (st != DSA_OK) return st;
   if (ba.num_q_rows == 0) return DSA_OK;
-  if (q_idx == nullptr || w == nullptr || k_idx == nullptr || scores == nullptr) return DSA_ERR_NULL;
-  if (n_heads < 1 || head_dim < 1 || ld < 1 || ld < ba.max_seq_len) return DSA_ERR_SHAPE;
-  const bool fp8_keys = q_format == DSA_BF16 && k_idx->format == DSA_FP8_E4M3_B128;
-  if ((k_idx->format != q_format && !fp8_keys) || k_idx->dim != head_dim) return DSA_ERR_SHAPE;
-  if (!aligned(w, 4) || !aligned(scores, 4)) return DSA_ERR_ALIGN;
-  PoolArgs pa;
+  if (scores == nullptr) return DSA_ERR_NULL;
+  IndexArgs ia;
+  if ((st = check_index(ba, q_idx, q_format, w, k_idx, n_heads, head_dim, &ia)) != DSA_OK) return st;
+  if (ld < 1 || ld < ba.max_seq_len) return DSA_ERR_SHAPE;
+  if (!aligned(scores, 4)) return DSA_ERR_ALIGN;
+  return hip_status(launch_index(ba, ia, scores, ld, static_cast<hipStream_t>(stream), 0, ba.num_q_rows));
+}
+
+size_t dsa_index_topk_workspace_bytes(int32_t num_q_rows, int32_t max_seq_len, int64_t budget_bytes) {
+  if (num_q_rows <= 0 || max_seq_len < 0 || budget_bytes <= 0) return 0;
+  const int64_t row = score_row_bytes(max_seq_len);
+  const int64_t rows = std::min<int64_t>(num_q_rows, budget_bytes / row);
+  return rows < 1 ? 0 : (size_t)(rows * row);
+}
+
+dsa_status dsa_index_topk(const dsa_batch* batch, const void* q_idx, int32_t q_format, const float* w,
+                          const dsa_pool* k_idx, int32_t n_heads, int32_t head_dim, int32_t k,
+                          int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  BatchArgs ba;
+  dsa_status st = check_batch(batch, &ba);
+  if (st != DSA_OK) return st;
+  if (ba.num_q_rows == 0) return DSA_OK;
+  if (idx == nullptr) return DSA_ERR_NULL;
+  IndexArgs ia;
+  if ((st = check_index(ba, q_idx, q_format, w, k_idx, n_heads, head_dim, &ia)) != DSA_OK) return st;
+  if (k < 1) return DSA_ERR_SHAPE;
+  const int64_t row = score_row_bytes(ba.max_seq_len);
+  const int64_t per = ws == nullptr ? 0 : std::min<int64_t>(ba.num_q_rows, (int64_t)(ws_bytes / (size_t)row));
+  if (per < 1) return DSA_ERR_WORKSPACE;  // below the minimum: one score row
+  if (!aligned(ws, 16) || !aligned(idx, 4)) return DSA_ERR_ALIGN;
+  float* scores = static_cast<float*>(ws);
+  const int64_t ld = row / 4;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (q_format == DSA_BF16) {
-    if (n_heads != 64 || head_dim != 128) return DSA_ERR_UNSUPPORTED;
-    if (fp8_keys) {
-      // page-blocked: page_size rows of 128 codes, then page_size f32 scales
-      if ((st = check_pool(k_idx, 128, 16, &pa)) != DSA_OK) return st;
-      if (k_idx->page_stride_bytes < (int64_t)ba.page_size * (k_idx->row_stride_bytes + 4))
-        return DSA_ERR_SHAPE;
-    } else if ((st = check_pool(k_idx, 256, 16, &pa)) != DSA_OK) {
-      return st;
-    }
-    if (!aligned(q_idx, 16) || !aligned(w, 16)) return DSA_ERR_ALIGN;
-    if (ba.num_pages == 0) return DSA_OK;  // no token is mapped: nothing is written
-    return hip_status(dsa::launch_index_scores_bf16(ba, q_idx, w, pa, scores, ld, s));
+  // Chunks of `per` query rows: each chunk's scores, then at once its top-k.
+  for (int r0 = 0; r0 < ba.num_q_rows; r0 += (int)per) {
+    const int r1 = (int)std::min<int64_t>(ba.num_q_rows, r0 + per);
+    if ((st = hip_status(launch_index(ba, ia, scores, ld, s, r0, r1))) != DSA_OK) return st;
+    if ((st = hip_status(dsa::launch_topk(ba, scores, ld, k, idx, s, r0, r1))) != DSA_OK) return st;
   }
-  if (q_format == DSA_F32) {
-    if (n_heads > 64 || head_dim > 256 || n_heads * head_dim > 8192) return DSA_ERR_UNSUPPORTED;
-    if ((st = check_pool(k_idx, (int64_t)head_dim * 4, 4, &pa)) != DSA_OK) return st;
-    if (!aligned(q_idx, 4)) return DSA_ERR_ALIGN;
-    return hip_status(dsa::launch_index_scores_f32(ba, q_idx, w, pa, n_heads, head_dim, scores, ld, s));
-  }
-  return DSA_ERR_UNSUPPORTED;
+  return DSA_OK;
 }
 
 dsa_status dsa_indexer_prepare(const dsa_batch* batch, const void* q_in, void* q_out,
@@ -228,7 +298,8 @@ dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld, int
   if (scores == nullptr || idx == nullptr) return DSA_ERR_NULL;
   if (k < 1 || ld < 1 || ld < ba.max_seq_len) return DSA_ERR_SHAPE;
   if (!aligned(scores, 4) || !aligned(idx, 4)) return DSA_ERR_ALIGN;
-  return hip_status(dsa::launch_topk(ba, scores, ld, k, idx, static_cast<hipStream_t>(stream)));
+  return hip_status(dsa::launch_topk(ba, scores, ld, k, idx, static_cast<hipStream_t>(stream), 0,
+                                     ba.num_q_rows));
 }
 
 size_t dsa_sparse_mla_workspace_bytes(int32_t num_q_rows, int32_t n_heads, int32_t k, int32_t dc,

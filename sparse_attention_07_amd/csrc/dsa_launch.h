@@ -28,12 +28,14 @@ hipError_t ensure_max_lds(const void* kernel);
 // Compute units of the current device (cached per device).
 int device_cu_count();
 
+// Scores and top-k of the query rows [row_lo, row_hi) only; score row t is
+// stored at scores + (t - row_lo) * ld (index rows keep their absolute t).
 hipError_t launch_index_scores_bf16(const BatchArgs& ba, const void* q_idx, const float* w,
                                     const PoolArgs& pool, float* scores, int64_t ld,
-                                    hipStream_t stream);
+                                    hipStream_t stream, int row_lo, int row_hi);
 hipError_t launch_index_scores_f32(const BatchArgs& ba, const void* q_idx, const float* w,
                                    const PoolArgs& pool, int n_heads, int head_dim, float* scores,
-                                   int64_t ld, hipStream_t stream);
+                                   int64_t ld, hipStream_t stream, int row_lo, int row_hi);
 
 hipError_t launch_indexer_prepare(const BatchArgs& ba, const void* q_in, void* q_out, const void* k_in,
                                   int format, const float* gamma, const float* beta, float eps,
@@ -42,7 +44,7 @@ hipError_t launch_indexer_prepare(const BatchArgs& ba, const void* q_in, void* q
                                   int head_dim, hipStream_t stream);
 
 hipError_t launch_topk(const BatchArgs& ba, const float* scores, int64_t ld, int k, int32_t* idx,
-                       hipStream_t stream);
+                       hipStream_t stream, int row_lo, int row_hi);
 
 // Split plan of the MFMA sparse-MLA kernel (rows of each query cut into `splits`
 // ranges of `rows_per_split`); workspace holds the partial results.

@@ -198,7 +198,7 @@ __global__ __launch_bounds__(kThreads, 2) void index_scores_bf16_mfma(
     const int32_t* __restrict__ page_table, int pt_stride, int page_size, int num_pages,
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint8_t* __restrict__ k_base, int64_t k_page_stride, int64_t k_row_stride,
-    float* __restrict__ scores, int64_t ld, int row_group) {
+    float* __restrict__ scores, int64_t ld, int row_group, int row_lo, int row_hi) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* q_lds = smem;
   float* w_lds = reinterpret_cast<float*>(smem + (size_t)row_group * kRowBytesLds);
@@ -206,9 +206,11 @@ __global__ __launch_bounds__(kThreads, 2) void index_scores_bf16_mfma(
   const int b = blockIdx.x;
   const int q0 = cu_q[b];
   const int q_len = cu_q[b + 1] - q0;
-  const int r0 = blockIdx.y * row_group;
-  if (r0 >= q_len) return;
-  const int nr = min(row_group, q_len - r0);
+  // this group's rows, clipped to the window [row_lo, row_hi)
+  const int g0 = blockIdx.y * row_group;
+  const int r0 = max(g0, row_lo - q0), r1 = min(min(q_len, g0 + row_group), row_hi - q0);
+  if (r0 >= r1) return;
+  const int nr = r1 - r0;
   const int pos_first = seq_lens[b] - q_len + r0;
   const int64_t ld_last = ld - 1;
   const int pos_last = (int)min<int64_t>((int64_t)pos_first + nr - 1, ld_last);
@@ -265,7 +267,7 @@ __global__ __launch_bounds__(kThreads, 2) void index_scores_bf16_mfma(
   for (int j = 0; j < kSteps; ++j) {
     const int s_base = k0 + (j * kWaves + wave) * kKeysPerStep;
     if (s_base > pos_last) break;                        // later steps are further right
-    score_keys(kk[j], off[j], q_lds, w_lds, nr, s_base, pos_first, ld_last, scores, row0, ld, lane);
+    score_keys(kk[j], off[j], q_lds, w_lds, nr, s_base, pos_first, ld_last, scores, row0 - row_lo, ld, lane);
   }
 }
 
@@ -353,15 +355,15 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
     const int32_t* __restrict__ page_table, int pt_stride, int page_size, int num_pages,
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const uint8_t* __restrict__ k_base, int64_t k_page_stride, int64_t k_row_stride,
-    float* __restrict__ scores, int64_t ld, int rg, int nslots, int u_max) {
+    float* __restrict__ scores, int64_t ld, int rg, int nslots, int u_max, int row_lo, int row_hi) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   // LDS: nslots staged units (query rows, then their weights), then the tables.
   uint8_t* q_area = smem;
   float* w_area = reinterpret_cast<float*>(smem + (size_t)nslots * rg * kRowBytesLds);
-  int* rq0 = reinterpret_cast<int*>(w_area + nslots * rg * kHeads);  // [B] cu_q[b]
-  int* rql = rq0 + B;                                             // [B] q_len
-  int* rsl = rql + B;                                             // [B] seq_len
-  int* ubase = rsl + B;                                           // [B+1] first unit of each request
+  int* rq0 = reinterpret_cast<int*>(w_area + nslots * rg * kHeads);  // [B] first row in the window
+  int* rql = rq0 + B;                                             // [B] its rows in the window
+  int* rpf = rql + B;                                             // [B] position of the first
+  int* ubase = rpf + B;                                           // [B+1] first unit of each request
   int* pre = ubase + B + 1;                                       // [u_max+1] first block of each unit
   int* uq0 = pre + u_max + 1;                                     // [u_max] first row of the unit
   int* unr = uq0 + u_max;                                         // [u_max] rows in the unit
@@ -371,17 +373,19 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int64_t ld_last = ld - 1;
 
-  // 1. Units: runs of up to rg consecutive rows of one request.  When no
-  //    request has more than rg rows (decode, drafts), unit u is request u
-  //    (a request without rows is an empty unit) and no scan is needed.
+  // 1. Units: runs of up to rg consecutive rows of one request, counting only
+  //    rows inside [row_lo, row_hi).  When no request has more than rg rows
+  //    (decode, drafts), unit u is request u (a request without rows in the
+  //    window is an empty unit) and no scan is needed.
   const bool per_request = u_max == B;
   int n_units = 0;
   if (per_request) {
     for (int bb = tid; bb < B; bb += kFlatThreads) {
-      const int q0 = cu_q[bb];
-      rq0[bb] = q0;
-      rql[bb] = cu_q[bb + 1] - q0;
-      rsl[bb] = seq_lens[bb];
+      const int q0 = cu_q[bb], q1 = cu_q[bb + 1];
+      const int lo = max(q0, row_lo), hi = min(q1, row_hi);
+      rq0[bb] = lo;
+      rql[bb] = max(0, hi - lo);
+      rpf[bb] = seq_lens[bb] - (q1 - q0) + (lo - q0);
       ubase[bb] = bb;
     }
     n_units = B;
@@ -390,10 +394,11 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
       const int bb = c0 + tid;
       int nu = 0;
       if (bb < B) {
-        const int q0 = cu_q[bb], ql = cu_q[bb + 1] - q0;
-        rq0[bb] = q0;
+        const int q0 = cu_q[bb], q1 = cu_q[bb + 1];
+        const int lo = max(q0, row_lo), hi = min(q1, row_hi), ql = max(0, hi - lo);
+        rq0[bb] = lo;
         rql[bb] = ql;
-        rsl[bb] = seq_lens[bb];
+        rpf[bb] = seq_lens[bb] - (q1 - q0) + (lo - q0);
         nu = ql > 0 ? (ql + rg - 1) / rg : 0;
       }
       const int e = flat_excl_scan(nu, wsum, n_units, lane, wave);
@@ -411,7 +416,7 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
     if (u < n_units) {
       const int b = per_request ? u : last_at_or_below(ubase, B, u), j = u - ubase[b];
       const int nr = min(rg, rql[b] - rg * j);
-      const int pf = rsl[b] - rql[b] + rg * j;
+      const int pf = rpf[b] + rg * j;
       uq0[u] = rq0[b] + rg * j;
       unr[u] = nr;
       upf[u] = pf;
@@ -485,7 +490,7 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
 #define DSA_SCORE(KK, X)                                                                           \
   score_keys(KK, X.off, q_area + (size_t)(X.u - u0) * rg * kRowBytesLds,                          \
               w_area + (size_t)(X.u - u0) * rg * kHeads, unr[X.u], X.tok, upf[X.u], ld_last, scores, \
-              uq0[X.u], ld, lane)
+              (int64_t)uq0[X.u] - row_lo, ld, lane)
     while (j < hi) {
       // block j with k0 (loaded), block j + 8 with k1 (in flight)
       const bool has1 = j + kFlatWaves < hi;
@@ -522,11 +527,11 @@ __global__ __launch_bounds__(256) void index_scores_f32_valu(
     const int32_t* __restrict__ page_table, int B, int pt_stride, int page_size, int num_pages,
     const float* __restrict__ q_idx, const float* __restrict__ w,
     const uint8_t* __restrict__ k_base, int64_t k_page_stride, int64_t k_row_stride,
-    int n_heads, int head_dim, float* __restrict__ scores, int64_t ld) {
+    int n_heads, int head_dim, float* __restrict__ scores, int64_t ld, int row_lo) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   float* qs = reinterpret_cast<float*>(smem);
   float* ws = qs + n_heads * head_dim;
-  const int t = blockIdx.y;
+  const int t = row_lo + (int)blockIdx.y;
   const RowLoc loc = locate_row(cu_q, seq_lens, B, t);
   const int b = loc.b;
   const int pos = (int)min<int64_t>(loc.pos, ld - 1);
@@ -546,7 +551,7 @@ __global__ __launch_bounds__(256) void index_scores_f32_valu(
     for (int d = 0; d < head_dim; ++d) dot = fmaf(qs[h * head_dim + d], k[d], dot);
     acc = fmaf(ws[h], fmaxf(dot, 0.f), acc);
   }
-  scores[(int64_t)t * ld + s] = acc;
+  scores[(int64_t)(t - row_lo) * ld + s] = acc;
 }
 
 
@@ -557,7 +562,7 @@ namespace {
 template <bool KFP8>
 hipError_t launch_index_scores_mfma(const BatchArgs& ba, const void* q_idx, const float* w,
                                     const PoolArgs& pool, float* scores, int64_t ld,
-                                    hipStream_t stream) {
+                                    hipStream_t stream, int row_lo, int row_hi) {
   if (ba.max_q_len >= 1) {
     // Units of up to rg rows (the whole draft for decode-sized q_len, eight
     // rows -- the most whose query rows fit in LDS -- for long prefill chunks,
@@ -577,7 +582,7 @@ hipError_t launch_index_scores_mfma(const BatchArgs& ba, const void* q_idx, cons
                          ba.cu_q, ba.seq_lens, ba.batch, ba.page_table, ba.pt_stride, ba.page_size,
                          ba.num_pages, static_cast<const uint16_t*>(q_idx), w,
                          static_cast<const uint8_t*>(pool.base), pool.page_stride, pool.row_stride,
-                         scores, ld, rg, nslots, (int)u_max);
+                         scores, ld, rg, nslots, (int)u_max, row_lo, row_hi);
       return hipGetLastError();
     }
   }
@@ -597,7 +602,7 @@ hipError_t launch_index_scores_mfma(const BatchArgs& ba, const void* q_idx, cons
   hipLaunchKernelGGL(index_scores_bf16_mfma<KFP8>, grid, dim3(kThreads), lds, stream,
                      ba.cu_q, ba.seq_lens, ba.page_table, ba.pt_stride, ba.page_size, ba.num_pages,
                      static_cast<const uint16_t*>(q_idx), w, static_cast<const uint8_t*>(pool.base),
-                     pool.page_stride, pool.row_stride, scores, ld, rg);
+                     pool.page_stride, pool.row_stride, scores, ld, rg, row_lo, row_hi);
   return hipGetLastError();
 }
 
@@ -605,21 +610,22 @@ hipError_t launch_index_scores_mfma(const BatchArgs& ba, const void* q_idx, cons
 
 hipError_t launch_index_scores_bf16(const BatchArgs& ba, const void* q_idx, const float* w,
                                     const PoolArgs& pool, float* scores, int64_t ld,
-                                    hipStream_t stream) {
-  return pool.format == 2 ? launch_index_scores_mfma<true>(ba, q_idx, w, pool, scores, ld, stream)
-                          : launch_index_scores_mfma<false>(ba, q_idx, w, pool, scores, ld, stream);
+                                    hipStream_t stream, int row_lo, int row_hi) {
+  return pool.format == 2
+             ? launch_index_scores_mfma<true>(ba, q_idx, w, pool, scores, ld, stream, row_lo, row_hi)
+             : launch_index_scores_mfma<false>(ba, q_idx, w, pool, scores, ld, stream, row_lo, row_hi);
 }
 
 hipError_t launch_index_scores_f32(const BatchArgs& ba, const void* q_idx, const float* w,
                                    const PoolArgs& pool, int n_heads, int head_dim, float* scores,
-                                   int64_t ld, hipStream_t stream) {
+                                   int64_t ld, hipStream_t stream, int row_lo, int row_hi) {
   const size_t lds = (size_t)(n_heads * head_dim + n_heads) * sizeof(float);
-  dim3 grid((ba.max_seq_len + 255) / 256, ba.num_q_rows);
+  dim3 grid((ba.max_seq_len + 255) / 256, row_hi - row_lo);
   if (grid.x == 0 || grid.y == 0) return hipSuccess;
   hipLaunchKernelGGL(index_scores_f32_valu, grid, dim3(256), lds, stream, ba.cu_q, ba.seq_lens,
                      ba.page_table, ba.batch, ba.pt_stride, ba.page_size, ba.num_pages,
                      static_cast<const float*>(q_idx), w, static_cast<const uint8_t*>(pool.base),
-                     pool.page_stride, pool.row_stride, n_heads, head_dim, scores, ld);
+                     pool.page_stride, pool.row_stride, n_heads, head_dim, scores, ld, row_lo);
   return hipGetLastError();
 }
 

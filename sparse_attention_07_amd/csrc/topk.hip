@@ -34,13 +34,13 @@ __device__ inline void select_row(const float* __restrict__ row, int n, int K, i
 __global__ __launch_bounds__(kThreads) void topk_radix(const int32_t* __restrict__ cu_q,
                                                        const int32_t* __restrict__ seq_lens, int B,
                                                        const float* __restrict__ scores, int64_t ld,
-                                                       int K, int32_t* __restrict__ idx) {
+                                                       int K, int32_t* __restrict__ idx, int row_lo) {
   __shared__ __align__(16) uint32_t cache[kCache];
   __shared__ __align__(16) uint32_t hist[2 * topk::kHistWords];
   __shared__ uint32_t wcount[2 * kThreads / kWave];
   __shared__ uint32_t pick[3];
 
-  const int t = blockIdx.x;
+  const int t = row_lo + (int)blockIdx.x;  // score row t - row_lo, index row t
   const int tid = threadIdx.x;
   const RowLoc loc = locate_row(cu_q, seq_lens, B, t);
   const int n = (int)max<int64_t>(0, min<int64_t>((int64_t)loc.pos + 1, ld));
@@ -50,7 +50,7 @@ __global__ __launch_bounds__(kThreads) void topk_radix(const int32_t* __restrict
     for (int j = tid; j < K; j += kThreads) out[j] = j < n ? j : -1;
     return;
   }
-  const float* row = scores + (int64_t)t * ld;
+  const float* row = scores + (int64_t)(t - row_lo) * ld;
   if (n <= kCache) select_row<true>(row, n, K, out, cache, hist, wcount, pick);
   else select_row<false>(row, n, K, out, cache, hist, wcount, pick);
 }
@@ -58,10 +58,10 @@ __global__ __launch_bounds__(kThreads) void topk_radix(const int32_t* __restrict
 }  // namespace
 
 hipError_t launch_topk(const BatchArgs& ba, const float* scores, int64_t ld, int k, int32_t* idx,
-                       hipStream_t stream) {
-  if (ba.num_q_rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_radix, dim3(ba.num_q_rows), dim3(kThreads), 0, stream, ba.cu_q,
-                     ba.seq_lens, ba.batch, scores, ld, k, idx);
+                       hipStream_t stream, int row_lo, int row_hi) {
+  if (row_hi <= row_lo) return hipSuccess;
+  hipLaunchKernelGGL(topk_radix, dim3(row_hi - row_lo), dim3(kThreads), 0, stream, ba.cu_q,
+                     ba.seq_lens, ba.batch, scores, ld, k, idx, row_lo);
   return hipGetLastError();
 }
 

@@ -21,7 +21,7 @@ STATUS_NAMES = {0: "DSA_OK", 1: "DSA_ERR_NULL", 2: "DSA_ERR_SHAPE", 3: "DSA_ERR_
 DSA_F32, DSA_BF16, DSA_FP8_E4M3_B128 = 0, 1, 2
 
 ENTRY_POINTS = ("dsa_version", "dsa_status_string", "dsa_indexer_prepare", "dsa_index_scores",
-                "dsa_topk_workspace_bytes",
+                "dsa_index_topk", "dsa_index_topk_workspace_bytes", "dsa_topk_workspace_bytes",
                 "dsa_topk", "dsa_sparse_mla_workspace_bytes", "dsa_sparse_mla_decode",
                 "dsa_sparse_mla_prefill")
 
@@ -60,6 +60,10 @@ def _load():
     lib.dsa_indexer_prepare.argtypes = [bp, vp, vp, vp, i32, vp, vp, ctypes.c_float, vp, vp, i32, i32,
                                         i32, pp, i32, i32, vp]
     lib.dsa_indexer_prepare.restype = i32
+    lib.dsa_index_topk.argtypes = [bp, vp, i32, vp, pp, i32, i32, i32, vp, vp, sz, vp]
+    lib.dsa_index_topk.restype = i32
+    lib.dsa_index_topk_workspace_bytes.argtypes = [i32, i32, i64]
+    lib.dsa_index_topk_workspace_bytes.restype = sz
     lib.dsa_topk_workspace_bytes.argtypes = [i32, i32, i32]
     lib.dsa_topk_workspace_bytes.restype = sz
     lib.dsa_topk.argtypes = [bp, vp, i64, i32, vp, vp, sz, vp]
@@ -156,6 +160,17 @@ def dsa_indexer_prepare(batch, q_in, q_out, k_in, fmt, ln_weight, ln_bias, ln_ep
         ctypes.byref(batch), _ptr(q_in), _ptr(q_out), _ptr(k_in), fmt, _ptr(ln_weight), _ptr(ln_bias),
         ln_eps, _ptr(rope_cos), _ptr(rope_sin), rope_rows, rope_dim, 1 if rope_interleaved else 0,
         ctypes.byref(k_pool), n_heads, head_dim, _stream(stream)))
+
+
+def dsa_index_topk_workspace_bytes(num_q_rows, max_seq_len, budget_bytes) -> int:
+    return _lib.dsa_index_topk_workspace_bytes(num_q_rows, max_seq_len, budget_bytes)
+
+
+def dsa_index_topk(batch, q_idx, q_format, w, k_pool: dsa_pool, n_heads, head_dim, k, idx, ws, ws_bytes,
+                   stream=None):
+    _check("dsa_index_topk", _lib.dsa_index_topk(
+        ctypes.byref(batch), _ptr(q_idx), q_format, _ptr(w), ctypes.byref(k_pool), n_heads, head_dim, k,
+        _ptr(idx), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def dsa_topk_workspace_bytes(num_q_rows, max_seq_len, k) -> int:

@@ -14,7 +14,7 @@ from .synth import torch_dtype
 
 
 class DSAPath:
-    def __init__(self, sb, prefill: bool | None = None, prep=None):
+    def __init__(self, sb, prefill: bool | None = None, prep=None, score_budget: int | None = None):
         cfg = sb.cfg
         self.sb = sb
         # optional indexer preparation inputs (synth.Prep): when given, each step
@@ -41,6 +41,14 @@ class DSAPath:
         self.topk_ws_bytes = dsa.dsa_topk_workspace_bytes(T, sb.max_seq_len, cfg.topk)
         self.topk_ws = (torch.empty((self.topk_ws_bytes,), dtype=torch.uint8, device=dev)
                         if self.topk_ws_bytes else None)
+        # bounded scoring: with a budget (bytes), scores + top-k run through
+        # dsa_index_topk over a workspace of whole score rows instead of [T, ld]
+        self.itk_ws_bytes = 0
+        if score_budget is not None:
+            self.itk_ws_bytes = dsa.dsa_index_topk_workspace_bytes(T, sb.max_seq_len, score_budget)
+            if self.itk_ws_bytes == 0 and T > 0:
+                raise ValueError("score budget %d B is below one score row" % score_budget)
+            self.itk_ws = torch.empty((max(self.itk_ws_bytes, 16) // 4,), dtype=torch.float32, device=dev)
 
     def indexer_prepare(self, stream=None):
         c, pr = self.cfg, self.prep
@@ -57,6 +65,11 @@ class DSAPath:
         dsa.dsa_topk(self.batch, self.scores, self.ld, self.cfg.topk, self.idx, self.topk_ws,
                      self.topk_ws_bytes, stream)
 
+    def index_topk(self, stream=None):
+        c = self.cfg
+        dsa.dsa_index_topk(self.batch, self.sb.q_idx, c.idx_fmt, self.sb.w, self.k_pool, c.hi, c.di, c.topk,
+                           self.idx, self.itk_ws, self.itk_ws_bytes, stream)
+
     def mla(self, layer: int, idx=None, stream=None):
         c = self.cfg
         fn = dsa.dsa_sparse_mla_prefill if self.prefill else dsa.dsa_sparse_mla_decode
@@ -68,7 +81,10 @@ class DSAPath:
         """One pass of the whole path: full layer, then the IndexShare layers."""
         if self.prep is not None:
             self.indexer_prepare(stream)
-        self.index_scores(stream)
-        self.topk(stream)
+        if self.itk_ws_bytes:
+            self.index_topk(stream)
+        else:
+            self.index_scores(stream)
+            self.topk(stream)
         for layer in range(len(self.kv)):
             self.mla(layer, stream=stream)

@@ -127,6 +127,42 @@ def test_indexer_prepare_validation():
     assert _prep(_batch(), pool=_pool(dsa.DSA_BF16, 128, 128)) == 2     # row stride below the key
 
 
+
+def test_index_topk_workspace_sizes():
+    W = L.dsa_index_topk_workspace_bytes
+    row = 128 * 4                                   # max_seq_len 100 -> 128 entries
+    assert W(4, 100, 10 ** 9) == 4 * row            # never more rows than the batch
+    assert W(4, 100, 3 * row + 5) == 3 * row        # whole rows only
+    assert W(4, 100, row) == row
+    assert W(4, 100, row - 1) == 0                  # below the minimum: rejected
+    assert W(0, 100, 10 ** 9) == 0
+    assert W(4, 0, 10 ** 9) == 4 * 256              # an empty context still has a 64-entry row
+    assert W(3, 1 << 20, 1 << 30) == 3 * (1 << 22)  # 1M-token rows
+
+
+def _itopk(batch, ws=FAKE, ws_bytes=1 << 20, k=8, idx=FAKE, **kw):
+    pool = kw.pop("pool", None) or _pool(dsa.DSA_BF16, 128, 256)
+    st = L.dsa_index_topk(ctypes.byref(batch) if batch is not None else None, kw.pop("q", FAKE),
+                          kw.pop("q_fmt", dsa.DSA_BF16), FAKE, ctypes.byref(pool), kw.pop("H", 64),
+                          kw.pop("D", 128), k, idx, ws, ws_bytes, None)
+    assert st != 5, "a validation case got as far as a kernel launch"
+    return st
+
+
+def test_index_topk_validation():
+    assert _itopk(None) == 1
+    assert _itopk(_batch(T=0), ws=None, ws_bytes=0) == 0
+    assert _itopk(_batch(), idx=None) == 1
+    assert _itopk(_batch(), q=None) == 1
+    assert _itopk(_batch(), k=0) == 2
+    assert _itopk(_batch(), H=32) == 3
+    assert _itopk(_batch(), pool=_pool(dsa.DSA_F32, 128, 512)) == 2
+    assert _itopk(_batch(), ws=None) == 4
+    assert _itopk(_batch(), ws_bytes=128 * 4 - 1) == 4                  # less than one score row
+    assert _itopk(_batch(), ws=ODD) == 6
+    assert _itopk(_batch(), idx=ctypes.c_void_p(0x10002)) == 6
+
+
 def test_topk_validation():
     b = _batch()
     assert L.dsa_topk(None, FAKE, 128, 8, FAKE, None, 0, None) == 1
