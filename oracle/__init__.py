@@ -20,6 +20,9 @@ Parity status of each function (what pins it; see tests/test_oracle_pins.py):
   e4m3 decode   pinned: all 256 codes against torch.float8_e4m3fn
   fp8 index keys (page-blocked codes + per-token scales) pinned: a hand-built
                 page decoded against values written out by hand
+  int8 latent rows (affine codes, per-128 scale and bias) pinned: a hand-built
+                row decoded against values written out by hand; sparse_mla over
+                int8 rows equals sparse_mla over the decoded rows
   indexer_prepare  pinned: LayerNorm against torch's layer_norm; RoPE against
                 complex multiplication by unit phasors (interleaved) and the
                 dims permutation that maps one pair layout onto the other;
@@ -40,7 +43,7 @@ _SRC = os.path.join(_HERE, "dsa_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-FMT_F32, FMT_BF16, FMT_FP8 = 0, 1, 2
+FMT_F32, FMT_BF16, FMT_FP8, FMT_INT8 = 0, 1, 2, 3
 
 
 def build(force: bool = True) -> str:
@@ -72,6 +75,7 @@ def _load():
         lib.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
         lib.oracle_e4m3_to_double.restype = ctypes.c_double
         lib.oracle_decode_fp8_rows.argtypes = [ctypes.c_void_p, c_i64, c_int, c_int, f64p]
+        lib.oracle_decode_int8_rows.argtypes = [ctypes.c_void_p, c_i64, c_int, c_int, f64p]
         lib.oracle_decode_fp8_keys.argtypes = [ctypes.c_void_p, c_i64, c_int, c_int, c_i64, c_i64, f64p]
         i64p = ctypes.POINTER(ctypes.c_int64)
         lib.oracle_indexer_prepare.argtypes = [c_int, i32p, i32p, i32p, c_int, c_int, c_int, c_int,
@@ -196,17 +200,17 @@ def sparse_mla(batch, layer, idx, rows=None, k=None):
     assert idx.shape == (v.n, k)
     q = _f64(v.per_row(batch.q[layer]))
     pool = v.pool(batch.kv_pool[layer])
-    if cfg.kv_fmt == FMT_FP8:
+    if cfg.kv_fmt in (FMT_FP8, FMT_INT8):   # raw rows, decoded by the oracle
         kv = np.ascontiguousarray(pool.numpy())
-        fp8 = 1
+        kv_fmt = 1 if cfg.kv_fmt == FMT_FP8 else 2
     else:
         kv = _f64(pool)
-        fp8 = 0
+        kv_fmt = 0
     out = np.zeros((v.n, cfg.heads, cfg.dc), dtype=np.float64)
     lse = np.zeros((v.n, cfg.heads), dtype=np.float64)
     st = lib.oracle_sparse_mla(batch.B, _p(v.cu_q, ctypes.c_int32), _p(v.seq_lens, ctypes.c_int32),
                                _p(v.page_table, ctypes.c_int32), v.pt_stride, cfg.page_size,
-                               v.num_pages, _p(q, ctypes.c_double), fp8,
+                               v.num_pages, _p(q, ctypes.c_double), kv_fmt,
                                kv.ctypes.data_as(ctypes.c_void_p), _p(idx, ctypes.c_int32), k,
                                cfg.heads, cfg.dc, cfg.dr, cfg.sm_scale,
                                _p(v.rows, ctypes.c_int32), v.n, _p(out, ctypes.c_double),
@@ -235,6 +239,19 @@ def decode_fp8_rows(rows_u8, dc=512, dr=64):
     out = np.empty((a.shape[0], dc + dr), dtype=np.float64)
     lib.oracle_decode_fp8_rows(a.ctypes.data_as(ctypes.c_void_p), a.shape[0], dc, dr,
                                _p(out, ctypes.c_double))
+    return out
+
+
+def decode_int8_rows(rows_u8, dc=512, dr=64):
+    """Decode [n, 672] affine int8 rows into float64 [n, dc+dr] with the oracle's decoder."""
+    lib = _load()
+    if isinstance(rows_u8, torch.Tensor):
+        rows_u8 = rows_u8.detach().cpu().numpy()
+    a = np.ascontiguousarray(rows_u8, dtype=np.uint8)
+    a = a.reshape(-1, dc + 8 * (dc // 128) + 2 * dr)
+    out = np.empty((a.shape[0], dc + dr), dtype=np.float64)
+    lib.oracle_decode_int8_rows(a.ctypes.data_as(ctypes.c_void_p), a.shape[0], dc, dr,
+                                _p(out, ctypes.c_double))
     return out
 
 

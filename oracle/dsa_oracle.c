@@ -32,6 +32,10 @@
  *  4. OCP OFP8 E4M3 decoding of block-scaled fp8 latent rows (the BF16/FP8
  *     sparse cache paths of lmdeploy PR 4737, section "Changes"); the
  *     decoder follows the OCP 8-bit floating point specification.
+ *  6. Affine 8-bit latent rows (the int8 MLA latent cache of mlx-lm PR 1419's
+ *     description: only the latent is quantised, and dequantised on read):
+ *     dim d of the latent is scale[d/128] * code + bias[d/128] with code an
+ *     unsigned byte; the rope part stays bf16.
  *  5. Indexer query/key preparation before the scores (the fused indexer
  *     preparation of lmdeploy PR 4737, section "Changes"; mlx-lm PR 1419's
  *     description: GLM-5.2's indexer uses non-interleaved RoPE and a key
@@ -120,6 +124,24 @@ static void decode_fp8_row(const uint8_t *row, int dc, int dr, double *dst) {
   for (int d = 0; d < dr; ++d) {
     uint16_t bits;
     memcpy(&bits, row + 528 + 2 * d, 2);
+    dst[dc + d] = bf16_bits_to_double(bits);
+  }
+}
+
+/* Affine int8 latent row (672 bytes for Dc = 512, Dr = 64): Dc unsigned codes,
+ * Dc/128 f32 scales, Dc/128 f32 biases, then Dr bf16 rope values;
+ * latent dim d = scale[d/128] * code[d] + bias[d/128]. */
+static void decode_int8_row(const uint8_t *row, int dc, int dr, double *dst) {
+  const int nb = dc / 128;
+  for (int d = 0; d < dc; ++d) {
+    float scale, bias;
+    memcpy(&scale, row + dc + 4 * (d / 128), sizeof scale);
+    memcpy(&bias, row + dc + 4 * nb + 4 * (d / 128), sizeof bias);
+    dst[d] = (double)scale * (double)row[d] + (double)bias;
+  }
+  for (int d = 0; d < dr; ++d) {
+    uint16_t bits;
+    memcpy(&bits, row + dc + 8 * nb + 2 * d, sizeof bits);
     dst[dc + d] = bf16_bits_to_double(bits);
   }
 }
@@ -236,15 +258,15 @@ int oracle_topk(int B, const int32_t *cu_q, const int32_t *seq_lens,
 /*
  * Per-row inputs are compact over the call's rows (row i is query row
  * rows[i]): q [n_rows, H, Dc+Dr] doubles, idx [n_rows, K] logical positions.
- * kv: when kv_fp8 == 0, doubles [num_pages*P, Dc+Dr]; when kv_fp8 != 0, raw
- * 656-byte rows [num_pages*P, 656].  An entry is used when 0 <= s <= pos(t) and its
+ * kv: when kv_fmt == 0, doubles [num_pages*P, Dc+Dr]; kv_fmt == 1, raw fp8
+ * 656-byte rows [num_pages*P, 656]; kv_fmt == 2, raw affine int8 672-byte rows.  An entry is used when 0 <= s <= pos(t) and its
  * page is mapped; others are skipped (re-masked).  Rows are accumulated in
  * ascending j.  out [n_rows, H, Dc], lse [n_rows, H] (natural log).  A row with
  * no usable entry gives out = 0 and lse = -inf.
  */
 int oracle_sparse_mla(int B, const int32_t *cu_q, const int32_t *seq_lens,
                       const int32_t *page_table, int pt_stride, int page_size, int num_pages,
-                      const double *q, int kv_fp8, const void *kv, const int32_t *idx, int K,
+                      const double *q, int kv_fmt, const void *kv, const int32_t *idx, int K,
                       int H, int Dc, int Dr, double scale, const int32_t *rows, int n_rows,
                       double *out, double *lse) {
   const int D = Dc + Dr;
@@ -268,8 +290,10 @@ int oracle_sparse_mla(int B, const int32_t *cu_q, const int32_t *seq_lens,
       int64_t slot = token_slot(page_table, pt_stride, page_size, num_pages, b, s);
       if (slot < 0) continue;
       double *dst = rowbuf + (int64_t)n_used * D;
-      if (kv_fp8)
+      if (kv_fmt == 1)
         decode_fp8_row((const uint8_t *)kv + slot * 656, Dc, Dr, dst);
+      else if (kv_fmt == 2)
+        decode_int8_row((const uint8_t *)kv + slot * (Dc + 8 * (Dc / 128) + 2 * Dr), Dc, Dr, dst);
       else
         memcpy(dst, (const double *)kv + slot * D, (size_t)D * sizeof(double));
       ++n_used;
@@ -303,6 +327,12 @@ int oracle_sparse_mla(int B, const int32_t *cu_q, const int32_t *seq_lens,
     free(logit);
   }
   return status;
+}
+
+/* Decode a whole int8 pool [n_rows, 672] into doubles [n_rows, Dc+Dr]. */
+void oracle_decode_int8_rows(const uint8_t *rows, int64_t n_rows, int Dc, int Dr, double *dst) {
+  const int64_t rb = Dc + 8 * (Dc / 128) + 2 * Dr;
+  for (int64_t r = 0; r < n_rows; ++r) decode_int8_row(rows + r * rb, Dc, Dr, dst + r * (Dc + Dr));
 }
 
 /* Decode a whole fp8 pool [n_rows, 656] into doubles [n_rows, Dc+Dr]. */

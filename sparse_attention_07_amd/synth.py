@@ -41,8 +41,10 @@ import torch
 FMT_F32 = 0
 FMT_BF16 = 1
 FMT_FP8_E4M3_B128 = 2
+FMT_INT8_AFFINE_B128 = 3
 
 FP8_ROW_BYTES = 656       # 512 e4m3 bytes + 4 f32 block scales + 64 bf16 rope
+INT8_ROW_BYTES = 672      # 512 unsigned codes + 4 f32 scales + 4 f32 biases + 64 bf16 rope
 FP8_BLOCK = 128
 FP8_MAX = 448.0
 FP8_KEY_CODES = 128       # fp8 index keys: 128 e4m3 codes per token, page-blocked with
@@ -98,6 +100,9 @@ def kv_row_bytes(fmt: int, dc: int, dr: int) -> int:
     if fmt == FMT_FP8_E4M3_B128:
         assert dc == 512 and dr == 64
         return FP8_ROW_BYTES
+    if fmt == FMT_INT8_AFFINE_B128:
+        assert dc == 512 and dr == 64
+        return INT8_ROW_BYTES
     return (dc + dr) * (4 if fmt == FMT_F32 else 2)
 
 
@@ -175,6 +180,27 @@ def quantize_fp8_rows(latent: torch.Tensor, rope: torch.Tensor) -> torch.Tensor:
     out[..., :512] = codes.reshape(*lead, 512).view(torch.uint8)
     out[..., 512:528] = scale.reshape(*lead, 4).to(torch.float32).contiguous().view(torch.uint8)
     out[..., 528:656] = rope.to(torch.bfloat16).contiguous().view(torch.uint8)
+    return out
+
+
+def quantize_int8_rows(latent: torch.Tensor, rope: torch.Tensor) -> torch.Tensor:
+    """Pack latent [..., 512] (f32) and rope [..., 64] (bf16) into 672-byte rows.
+
+    Layout per row: 512 unsigned codes, four f32 scales, four f32 biases (one
+    pair per 128-wide block: bias = block min, scale = (max - min) / 255), then
+    64 bf16 rope values; code = round((x - bias) / scale), clamped to [0, 255].
+    """
+    lead = latent.shape[:-1]
+    blocks = latent.reshape(*lead, 4, 128).to(torch.float32)
+    mn = blocks.amin(dim=-1, keepdim=True)
+    mx = blocks.amax(dim=-1, keepdim=True)
+    scale = torch.where(mx > mn, (mx - mn) / 255.0, torch.ones_like(mx))
+    codes = torch.round((blocks - mn) / scale).clamp(0, 255).to(torch.uint8)
+    out = torch.empty(*lead, INT8_ROW_BYTES, dtype=torch.uint8, device=latent.device)
+    out[..., :512] = codes.reshape(*lead, 512)
+    out[..., 512:528] = scale.reshape(*lead, 4).contiguous().view(torch.uint8)
+    out[..., 528:544] = mn.reshape(*lead, 4).contiguous().view(torch.uint8)
+    out[..., 544:672] = rope.to(torch.bfloat16).contiguous().view(torch.uint8)
     return out
 
 
@@ -295,10 +321,11 @@ def make_batch(cfg_id: int, mode: str = "parity", device="cpu", layers: int | No
     qs, kvs = [], []
     for _ in range(cfg.layers):
         qs.append(torch.randn((T, cfg.heads, D), generator=g, device=device).to(qdt))
-        if cfg.kv_fmt == FMT_FP8_E4M3_B128:
+        if cfg.kv_fmt in (FMT_FP8_E4M3_B128, FMT_INT8_AFFINE_B128):
             lat = torch.randn((num_pages, P, cfg.dc), generator=g, device=device)
             rope = torch.randn((num_pages, P, cfg.dr), generator=g, device=device)
-            kvs.append(quantize_fp8_rows(lat, rope))
+            kvs.append(quantize_fp8_rows(lat, rope) if cfg.kv_fmt == FMT_FP8_E4M3_B128
+                       else quantize_int8_rows(lat, rope))
             del lat, rope
         else:
             kvs.append(torch.randn((num_pages, P, D), generator=g, device=device)

@@ -536,3 +536,60 @@ def test_prep_keys_land_at_their_slots():
         if req == 1 and p >= 4:
             want[pt[req, p // 4] * 4 + p % 4] = pool0[pt[req, p // 4] * 4 + p % 4]
     assert np.array_equal(r2["pool"], want)
+
+
+# ---------------------------------------------------------------- int8 latent rows
+
+
+def test_int8_row_hand_decoded():
+    # block 0: scale 0.5, bias -2 -> codes 0, 1, 255, 128 give -2, -1.5, 125.5, 62
+    # block 1: scale 2^-8, bias 0; block 2: scale 1, bias 0.25; block 3: scale 3, bias -384
+    row = np.zeros(672, dtype=np.uint8)
+    row[:4] = [0, 1, 255, 128]
+    row[128], row[255] = 255, 7
+    row[256:384] = np.arange(128)
+    row[384:512] = 128
+    row[512:528] = np.array([0.5, 2.0 ** -8, 1.0, 3.0], dtype=np.float32).view(np.uint8)
+    row[528:544] = np.array([-2.0, 0.0, 0.25, -384.0], dtype=np.float32).view(np.uint8)
+    rope = torch.tensor([1.0, -2.5] + [0.0] * 62, dtype=torch.bfloat16)
+    row[544:672] = rope.view(torch.uint8).numpy()
+    dec = oracle.decode_int8_rows(row[None])[0]
+    want = np.zeros(576)
+    want[:128] = -2.0
+    want[:4] = [-2.0, -1.5, 125.5, 62.0]
+    want[128], want[255] = 255 * 2.0 ** -8, 7 * 2.0 ** -8
+    want[256:384] = np.arange(128) + 0.25
+    want[384:512] = 0.0
+    want[512], want[513] = 1.0, -2.5
+    assert np.array_equal(dec, want)
+
+
+def test_int8_quantiser_round_trip():
+    g = torch.Generator().manual_seed(5)
+    lat = torch.randn(30, 512, generator=g) * torch.rand(30, 1, generator=g) * 4
+    rope = torch.randn(30, 64, generator=g).to(torch.bfloat16)
+    rows = synth.quantize_int8_rows(lat, rope)
+    dec = torch.from_numpy(oracle.decode_int8_rows(rows))
+    assert torch.equal(dec[:, 512:], rope.double())
+    blk = lat.double().reshape(30, 4, 128)
+    step = ((blk.amax(-1) - blk.amin(-1)) / 255).repeat_interleave(128, 1)
+    err = (dec[:, :512] - lat.double()).abs()
+    # half a code step, plus the f32 rounding of scale and bias
+    assert torch.all(err <= step * (0.5 + 1e-5) + 1e-6)
+    # each block's minimum is its bias exactly (code 0)
+    assert torch.equal(dec[:, :512].reshape(30, 4, 128).amin(-1), blk.float().double().amin(-1))
+
+
+def test_mla_over_int8_rows_equals_mla_over_decoded_rows():
+    # the oracle's int8 gather decodes each selected row with the 672-byte stride
+    b8 = synth.make_batch(1, batch=3, ctx=(300, 900), topk=128, layers=1, kv_fmt=synth.FMT_INT8_AFFINE_B128)
+    P = b8.cfg.page_size
+    dec = oracle.decode_int8_rows(b8.kv_pool[0].reshape(-1, 672)).reshape(-1, P, 576)
+    bd = synth.Batch(**{**b8.__dict__})
+    bd.cfg = synth.Config(**{**b8.cfg.__dict__})
+    bd.cfg.kv_fmt = synth.FMT_F32
+    bd.kv_pool = [torch.from_numpy(dec)]
+    idx = oracle.topk(b8, oracle.index_scores(b8))
+    o8, l8 = oracle.sparse_mla(b8, 0, idx)
+    od, ld = oracle.sparse_mla(bd, 0, idx)
+    assert np.array_equal(o8, od) and np.array_equal(l8, ld)
