@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--score-budget", type=float, default=None, metavar="MB",
                     help="scores + top-k through dsa_index_topk with a score workspace of at most "
                          "this many MB (query rows in chunks) instead of a [T, ld] score buffer")
+    ap.add_argument("--kv", choices=["bf16", "fp8", "int8"], default=None,
+                    help="latent cache format instead of the workload's own (fp8: e4m3 with a scale "
+                         "per 128 dims; int8: affine codes with a scale and bias per 128 dims)")
     ap.add_argument("--key-fp8", action="store_true",
                     help="indexer keys cached as e4m3 codes with one f32 scale per token "
                          "(queries stay bf16); reports the top-k overlap with bf16 keys")
@@ -212,11 +215,15 @@ def main():
     paths = []
     for i in range(sets):
         sb = synth.make_batch(cfg_id, mode=args.mode, device=dev, seed_offset=i,
-                              key_fmt=synth.FMT_FP8_E4M3_B128 if args.key_fp8 else None)
+                              key_fmt=synth.FMT_FP8_E4M3_B128 if args.key_fp8 else None,
+                              kv_fmt=None if args.kv is None else
+                              {"bf16": synth.FMT_BF16, "fp8": synth.FMT_FP8_E4M3_B128,
+                               "int8": synth.FMT_INT8_AFFINE_B128}[args.kv])
         paths.append(DSAPath(sb, prep=synth.make_prep(sb, seed=4242 + i) if args.prep else None,
                              score_budget=None if args.score_budget is None
                              else int(args.score_budget * 2 ** 20)))
     workload = (base.name + ("+fp8keys" if args.key_fp8 else "") + ("+prep" if args.prep else "")
+                + ("+kv-" + args.kv if args.kv is not None else "")
                 + ("+budget" if args.score_budget is not None else ""))
     torch.cuda.synchronize()
 
@@ -347,7 +354,7 @@ def main():
                                "indexer %dx%d, MLA %d heads %d+%d %s cache, page %d, %d layer(s)"
                                % (cfg.name, cfg.batch, cfg.q_len, cfg.ctx_lo, cfg.ctx_hi, cfg.topk,
                                   cfg.hi, cfg.di, cfg.heads, cfg.dc, cfg.dr,
-                                  {0: "f32", 1: "bf16", 2: "fp8-e4m3-b128"}[cfg.kv_fmt],
+                                  {0: "f32", 1: "bf16", 2: "fp8-e4m3-b128", 3: "int8-affine-b128"}[cfg.kv_fmt],
                                   cfg.page_size, cfg.layers)
                                + (", fp8 index keys (per-token scale)" if args.key_fp8 else "")
                                + (", indexer preparation in the step" if args.prep else "")
@@ -369,7 +376,8 @@ def main():
     }
     if args.key_fp8:
         out["topk_overlap_vs_bf16_keys"] = key_fp8_overlap(paths[0], cfg_id, args.mode)
-    if not args.no_cpu and not args.key_fp8 and not args.prep and args.score_budget is None:
+    if (not args.no_cpu and not args.key_fp8 and not args.prep and args.score_budget is None
+            and args.kv is None):
         out["cpu_baseline"] = cpu_baseline(cfg_id)
     print(json.dumps(out), flush=True)
 

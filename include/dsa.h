@@ -83,6 +83,13 @@ typedef int32_t dsa_status;
  * codes per token and one scale per token, page-blocked (see
  * dsa_index_scores). */
 #define DSA_FP8_E4M3_B128 2
+/* Affine 8-bit latent rows (the int8 MLA latent cache of mlx-lm PR 1419's
+ * description: only the latent is quantised, and it is dequantised on read;
+ * the block layout is this library's): 672-byte rows of 512 unsigned codes,
+ * four little-endian f32 scales, four f32 biases (pair i covers latent dims
+ * 128*i..128*i+127), then the 64 rope dims as bf16;
+ * latent dim d = scale[d/128] * code[d] + bias[d/128].  Latent pools only. */
+#define DSA_INT8_AFFINE_B128 3
 
 /* A ragged batch of B requests and T = cu_q_lens[B] query rows. */
 typedef struct {
@@ -254,7 +261,7 @@ size_t dsa_sparse_mla_workspace_bytes(int32_t num_q_rows, int32_t n_heads, int32
  *          zero-fill it once before its first use, and every call returns it
  *          with the counters zero again.  Calls that may run at the same time
  *          (other streams) need workspaces of their own.
- * Built combinations: q DSA_BF16 with kv DSA_BF16 or DSA_FP8_E4M3_B128,
+ * Built combinations: q DSA_BF16 with kv DSA_BF16, DSA_FP8_E4M3_B128 or DSA_INT8_AFFINE_B128,
  * dc 512, dr 64, n_heads a multiple of 16 up to 128 (MFMA); q and kv DSA_F32
  * with dc+dr <= 1024, n_heads <= 128, k <= 4096 (vector ALUs).
  * _decode and _prefill compute the same function; they differ only in how

@@ -153,9 +153,10 @@ dsa_status sparse_mla(const dsa_batch* batch, const void* q, int32_t q_format, c
   if (kv->dim != dc + dr) return DSA_ERR_SHAPE;
   if (!aligned(idx, 4) || (lse != nullptr && !aligned(lse, 4))) return DSA_ERR_ALIGN;
   PoolArgs pa;
-  if (q_format == DSA_BF16 && (kv->format == DSA_BF16 || kv->format == DSA_FP8_E4M3_B128)) {
+  if (q_format == DSA_BF16 && (kv->format == DSA_BF16 || kv->format == DSA_FP8_E4M3_B128 ||
+                                kv->format == DSA_INT8_AFFINE_B128)) {
     if (dc != 512 || dr != 64 || n_heads % 16 != 0 || n_heads > 128) return DSA_ERR_UNSUPPORTED;
-    const int64_t row_bytes = kv->format == DSA_BF16 ? 1152 : 656;
+    const int64_t row_bytes = kv->format == DSA_BF16 ? 1152 : (kv->format == DSA_FP8_E4M3_B128 ? 656 : 672);
     if ((st = check_pool(kv, row_bytes, 16, &pa)) != DSA_OK) return st;
     if (!aligned(q, 16) || !aligned(out, 16)) return DSA_ERR_ALIGN;
     const dsa::MlaPlan plan = dsa::plan_sparse_mla(ba.num_q_rows, n_heads, k, dc, prefill);

@@ -111,29 +111,56 @@ __device__ inline uint2 fp8x4_to_bf16x4(uint32_t x, float sc) {
   return r;
 }
 
+// Four unsigned 8-bit codes (one dword, byte 0 first) -> four bf16 of
+// sc * code + bi, each computed with one f32 fma and rounded to bf16 once.
+__device__ inline uint2 u8x4_to_bf16x4(uint32_t x, float sc, float bi) {
+  const float v0 = fmaf((float)(x & 0xFFu), sc, bi), v1 = fmaf((float)((x >> 8) & 0xFFu), sc, bi);
+  const float v2 = fmaf((float)((x >> 16) & 0xFFu), sc, bi), v3 = fmaf((float)(x >> 24), sc, bi);
+  return uint2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+}
+
+// Latent cache formats of the MFMA kernels: bf16 rows (1152 B), fp8 rows
+// (656 B: 512 e4m3 codes, 4 block scales, bf16 rope) and affine int8 rows
+// (672 B: 512 unsigned codes, 4 block scales, 4 block biases, bf16 rope).
+// Both 8-bit forms keep one scale (and bias) per 128 latent dims.
+constexpr int kFmtBf16 = 0, kFmtFp8 = 1, kFmtInt8 = 2;
+template <int F>
+constexpr bool kQ8 = F != kFmtBf16;  // 8-bit latent codes
+template <int F>
+constexpr int kRopeOff = F == kFmtBf16 ? 1024 : (F == kFmtFp8 ? 528 : 544);
+
+// Four latent codes of 8-bit format F -> four bf16.
+template <int F>
+__device__ inline uint2 decode4(uint32_t x, float sc, float bi) {
+  if (F == kFmtFp8) return fp8x4_to_bf16x4(x, sc);
+  return u8x4_to_bf16x4(x, sc, bi);
+}
+
 // One tile's rows in flight in registers, for a workgroup of 512 threads.
 // Each thread keeps one chunk column, so its items differ only by row: bf16
-// rows -- latent chunk tid%64 (16 B) of rows tid/64 + 8k, k < 4; fp8 rows --
-// latent chunk tid%32 (16 e4m3 bytes, with its block scale) of rows tid/32 +
-// 16k, k < 2.  Every thread also loads 8 bytes of rope (bf16 dims 4(tid%16)
-// .. +3 of row tid/16).  A wave reads 1 KB (bf16) or 512 B (fp8) contiguous
-// of a row per latent load.
+// rows -- latent chunk tid%64 (16 B) of rows tid/64 + 8k, k < 4; 8-bit rows --
+// latent chunk tid%32 (16 codes, with its block scale and bias) of rows
+// tid/32 + 16k, k < 2.  Every thread also loads 8 bytes of rope (bf16 dims
+// 4(tid%16) .. +3 of row tid/16).  A wave reads 1 KB (bf16) or 512 B (8-bit)
+// contiguous of a row per latent load.
 constexpr int kStageThreads = 512;
 
-template <bool FP8>
+template <int F>
 struct Stage {
-  u32x4 lat[FP8 ? 2 : 4];
-  float sc[FP8 ? 2 : 1];
+  u32x4 lat[kQ8<F> ? 2 : 4];
+  float sc[kQ8<F> ? 2 : 1];
+  float bi[F == kFmtInt8 ? 2 : 1];
   uint2 rope;
 };
 
 __device__ inline u32x4 ld_global16(const uint8_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
-template <bool FP8>
-__device__ inline void stage_load(Stage<FP8>& st, const int64_t* toffs, const uint8_t* kv, int tid) {
-  constexpr int kLat = FP8 ? 2 : 4, kStep = FP8 ? 16 : 8;
-  const int ch = FP8 ? (tid & 31) : (tid & 63);
-  const int r0 = FP8 ? (tid >> 5) : (tid >> 6);
+template <int F>
+__device__ inline void stage_load(Stage<F>& st, const int64_t* toffs, const uint8_t* kv, int tid) {
+  constexpr bool Q8 = kQ8<F>;
+  constexpr int kLat = Q8 ? 2 : 4, kStep = Q8 ? 16 : 8;
+  const int ch = Q8 ? (tid & 31) : (tid & 63);
+  const int r0 = Q8 ? (tid >> 5) : (tid >> 6);
   int64_t off[kLat];
 #pragma unroll
   for (int k = 0; k < kLat; ++k) off[k] = toffs[r0 + kStep * k];
@@ -141,31 +168,34 @@ __device__ inline void stage_load(Stage<FP8>& st, const int64_t* toffs, const ui
 #pragma unroll
   for (int k = 0; k < kLat; ++k) {
     st.lat[k] = u32x4{};
-    if (FP8) st.sc[k] = 0.f;
+    if (Q8) st.sc[k] = 0.f;
+    if (F == kFmtInt8) st.bi[k] = 0.f;
     if (off[k] >= 0) {
       st.lat[k] = ld_global16(kv + off[k] + ch * 16);
-      if (FP8) st.sc[k] = *reinterpret_cast<const float*>(kv + off[k] + 512 + (ch >> 3) * 4);
+      if (Q8) st.sc[k] = *reinterpret_cast<const float*>(kv + off[k] + 512 + (ch >> 3) * 4);
+      if (F == kFmtInt8) st.bi[k] = *reinterpret_cast<const float*>(kv + off[k] + 528 + (ch >> 3) * 4);
     }
   }
   st.rope = uint2{0u, 0u};
-  if (roff >= 0) st.rope = *reinterpret_cast<const uint2*>(kv + roff + (FP8 ? 528 : 1024) + (tid & 15) * 8);
+  if (roff >= 0) st.rope = *reinterpret_cast<const uint2*>(kv + roff + kRopeOff<F> + (tid & 15) * 8);
 }
 
-template <bool FP8>
-__device__ inline void stage_store(const Stage<FP8>& st, uint8_t* tile, int tid) {
-  constexpr int kLat = FP8 ? 2 : 4, kStep = FP8 ? 16 : 8;
-  const int ch = FP8 ? (tid & 31) : (tid & 63);
-  const int r0 = FP8 ? (tid >> 5) : (tid >> 6);
+template <int F>
+__device__ inline void stage_store(const Stage<F>& st, uint8_t* tile, int tid) {
+  constexpr bool Q8 = kQ8<F>;
+  constexpr int kLat = Q8 ? 2 : 4, kStep = Q8 ? 16 : 8;
+  const int ch = Q8 ? (tid & 31) : (tid & 63);
+  const int r0 = Q8 ? (tid >> 5) : (tid >> 6);
 #pragma unroll
   for (int k = 0; k < kLat; ++k) {
     uint8_t* dst = tile + (r0 + kStep * k) * kRowLds;
-    if (!FP8) {
+    if (!Q8) {
       *reinterpret_cast<u32x4*>(dst + ch * 16) = st.lat[k];
     } else {
       u32x4 lo, hi;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const uint2 pr = fp8x4_to_bf16x4(st.lat[k][w], st.sc[k]);
+        const uint2 pr = decode4<F>(st.lat[k][w], st.sc[k], F == kFmtInt8 ? st.bi[k] : 0.f);
         if (w < 2) { lo[2 * w] = pr.x; lo[2 * w + 1] = pr.y; }
         else { hi[2 * w - 4] = pr.x; hi[2 * w - 3] = pr.y; }
       }
@@ -558,7 +588,7 @@ constexpr int kWideBufs = 3;                         // LDS tile buffers
 constexpr int kWideStages = 2;                       // register stages of gathers
 constexpr int kSbufWide = kWideThreads * 2 * 16;     // two f32x4 partial scores per thread
 
-template <bool FP8>
+template <int F>
 __global__ __launch_bounds__(kWideThreads, 1) void sparse_mla_wide(MlaArgs a, int n_groups, int T) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int NT = kWideThreads;
@@ -656,7 +686,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void sparse_mla_wide(MlaArgs a, in
     // partial scores are exchanged; tile i+2 goes to buffer b2 from stage
     // st_next (i % 2).  The QK of tile i+1 and the store of tile i+2 also run
     // past the last tile (on buffers no longer read; their results are dropped).
-    auto iter = [&](int i, Stage<FP8>& st_next, uint8_t* b0, uint8_t* b1, uint8_t* b2) {
+    auto iter = [&](int i, Stage<F>& st_next, uint8_t* b0, uint8_t* b1, uint8_t* b2) {
       const f32x4* sb = sbuf + (i & 1) * (2 * NT);
       // same summation order in both siblings: k half 0, then k half 1
       const f32x4 s0 = sb[(2 * hg) * 64 + lane] + sb[(2 * (hg + 4)) * 64 + lane];
@@ -668,19 +698,19 @@ __global__ __launch_bounds__(kWideThreads, 1) void sparse_mla_wide(MlaArgs a, in
       }
       const bf16x8 pa = tile_softmax(s0, s1, vmask[i], a.scale_log2, m_run, l_run, o);
       pv(b0, pa);
-      stage_store<FP8>(st_next, b2, tid);
-      if (i + 2 + STAGES < ntiles) stage_load<FP8>(st_next, offs + (i + 2 + STAGES) * kTileRows, a.kv, tid);
+      stage_store<F>(st_next, b2, tid);
+      if (i + 2 + STAGES < ntiles) stage_load<F>(st_next, offs + (i + 2 + STAGES) * kTileRows, a.kv, tid);
       lds_barrier();
     };
-    Stage<FP8> st[STAGES];
+    Stage<F> st[STAGES];
 #pragma unroll
     for (int s = 0; s < STAGES; ++s)
-      if (s < ntiles) stage_load<FP8>(st[s], offs + s * kTileRows, a.kv, tid);
+      if (s < ntiles) stage_load<F>(st[s], offs + s * kTileRows, a.kv, tid);
     // tiles 0 and 1 to LDS, then tile 0's partial scores
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      stage_store<FP8>(st[s], tiles + s * kTileLds, tid);
-      if (s + STAGES < ntiles) stage_load<FP8>(st[s], offs + (s + STAGES) * kTileRows, a.kv, tid);
+      stage_store<F>(st[s], tiles + s * kTileLds, tid);
+      if (s + STAGES < ntiles) stage_load<F>(st[s], offs + (s + STAGES) * kTileRows, a.kv, tid);
     }
     lds_barrier();
     {
@@ -739,45 +769,50 @@ __global__ __launch_bounds__(kWideThreads, 1) void sparse_mla_wide(MlaArgs a, in
 // which every wave then reads V for its quarter (128) of the output columns.
 // Partial scores of the two k halves are summed through LDS in a fixed order.
 // Registers: 36 of q, 32 of accumulator, 36 per tile in flight (two tiles).
-template <bool FP8>
+template <int F>
 struct RegTile {
-  u32x4 v[9];   // bf16: 16 B per k step; fp8: 8 latent bytes (v.x, v.y) or 16 B of rope
-  f32x4 sc;     // fp8 block scales of the row
+  u32x4 v[9];   // bf16: 16 B per k step; 8-bit: 8 latent codes (v.x, v.y) or 16 B of rope
+  f32x4 sc;     // 8-bit: block scales of the row
+  f32x4 bi;     // int8: block biases of the row
 };
 
-template <bool FP8>
-__device__ inline void regtile_load(RegTile<FP8>& st, int64_t off, const uint8_t* kv, int ks0, int g) {
+template <int F>
+__device__ inline void regtile_load(RegTile<F>& st, int64_t off, const uint8_t* kv, int ks0, int g) {
+  constexpr bool Q8 = kQ8<F>;
 #pragma unroll
   for (int k = 0; k < 9; ++k) st.v[k] = u32x4{};
   st.sc = f32x4{};
+  st.bi = f32x4{};
   if (off < 0) return;
   const uint8_t* row = kv + off;
 #pragma unroll
   for (int k = 0; k < 9; ++k) {
     const int ks = ks0 + k;
-    if (!FP8) {
+    if (!Q8) {
       st.v[k] = ld_global16(row + ks * 64 + g * 16);
     } else if (ks < 16) {
       const uint2 x = *reinterpret_cast<const uint2*>(row + ks * 32 + g * 8);
       st.v[k] = u32x4{x.x, x.y, 0u, 0u};
     } else {
-      st.v[k] = ld_global16(row + 528 + ((ks - 16) * 32 + g * 8) * 2);
+      st.v[k] = ld_global16(row + kRopeOff<F> + ((ks - 16) * 32 + g * 8) * 2);
     }
   }
-  if (FP8) st.sc = *reinterpret_cast<const f32x4*>(row + 512);
+  if (Q8) st.sc = *reinterpret_cast<const f32x4*>(row + 512);
+  if (F == kFmtInt8) st.bi = *reinterpret_cast<const f32x4*>(row + 528);
 }
 
-// The bf16 A operand of k step ks (fp8: e4m3 * block scale, rounded to bf16).
-template <bool FP8>
-__device__ inline bf16x8 regtile_operand(const RegTile<FP8>& st, int k, int ks) {
-  if (!FP8 || ks >= 16) return __builtin_bit_cast(bf16x8, st.v[k]);
-  const float sc = st.sc[ks >> 2];
-  const uint2 p0 = fp8x4_to_bf16x4(st.v[k][0], sc), p1 = fp8x4_to_bf16x4(st.v[k][1], sc);
+// The bf16 A operand of k step ks (8-bit: decoded with the block scale and
+// bias, rounded to bf16).
+template <int F>
+__device__ inline bf16x8 regtile_operand(const RegTile<F>& st, int k, int ks) {
+  if (!kQ8<F> || ks >= 16) return __builtin_bit_cast(bf16x8, st.v[k]);
+  const float sc = st.sc[ks >> 2], bi = F == kFmtInt8 ? st.bi[ks >> 2] : 0.f;
+  const uint2 p0 = decode4<F>(st.v[k][0], sc, bi), p1 = decode4<F>(st.v[k][1], sc, bi);
   const u32x4 r = {p0.x, p0.y, p1.x, p1.y};
   return __builtin_bit_cast(bf16x8, r);
 }
 
-template <bool FP8, int STAGES>
+template <int F, int STAGES>
 __global__ __launch_bounds__(kThreads, 2) void sparse_mla_q16(MlaArgs a, int n_groups, int T) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   // Workgroup ids: head group outermost over a block of P = (T * splits
@@ -825,19 +860,19 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_q16(MlaArgs a, int n_g
 
   if (fv != INT32_MAX) {
     const int my_row = 16 * rb + c16;
-    auto step = [&](RegTile<FP8>& st, int i) {
+    auto step = [&](RegTile<F>& st, int i) {
       lds_barrier();                                       // every wave is done with tile i-1
       f32x4 spart = f32x4{};
       uint8_t* trow = tile + my_row * kRowLds + g * 16;
 #pragma unroll
       for (int k = 0; k < 9; ++k) {
         const int ks = ks0 + k;
-        const bf16x8 av = regtile_operand<FP8>(st, k, ks);
+        const bf16x8 av = regtile_operand<F>(st, k, ks);
         if (ks < 16) *reinterpret_cast<bf16x8*>(trow + ks * 64) = av;  // latent dims feed PV
         spart = mfma16(av, qreg[k], spart);
       }
       sbuf[wave * 64 + lane] = spart;
-      if (i + STAGES < ntiles) regtile_load<FP8>(st, offs[(i + STAGES) * kTileRows + my_row], a.kv, ks0, g);
+      if (i + STAGES < ntiles) regtile_load<F>(st, offs[(i + STAGES) * kTileRows + my_row], a.kv, ks0, g);
       lds_barrier();                                       // tile i and partial scores visible
       const uint32_t valid = vmask[i];
       // rows 0..15 from waves 0 and 2, rows 16..31 from waves 1 and 3; k half 0 first
@@ -856,10 +891,10 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_q16(MlaArgs a, int n_g
 #pragma unroll
       for (int i2 = 0; i2 < 8; ++i2) o[i2] = mfma16(pa, join(tv1[i2], tv2[i2]), o[i2]);
     };
-    RegTile<FP8> st0, st1, st2;
-    regtile_load<FP8>(st0, offs[my_row], a.kv, ks0, g);
-    if (ntiles > 1) regtile_load<FP8>(st1, offs[kTileRows + my_row], a.kv, ks0, g);
-    if (STAGES == 3 && ntiles > 2) regtile_load<FP8>(st2, offs[2 * kTileRows + my_row], a.kv, ks0, g);
+    RegTile<F> st0, st1, st2;
+    regtile_load<F>(st0, offs[my_row], a.kv, ks0, g);
+    if (ntiles > 1) regtile_load<F>(st1, offs[kTileRows + my_row], a.kv, ks0, g);
+    if (STAGES == 3 && ntiles > 2) regtile_load<F>(st2, offs[2 * kTileRows + my_row], a.kv, ks0, g);
 #pragma unroll 1
     for (int i = 0; i < ntiles; i += STAGES) {
       step(st0, i);
@@ -1001,7 +1036,7 @@ hipError_t launch_sparse_mla_bf16(const BatchArgs& ba, const void* q, const Pool
                                   void* out, float* lse, void* ws, const MlaPlan& plan,
                                   hipStream_t stream) {
   const bool wide = n_heads % 64 == 0;
-  const bool fp8 = kv.format == 2;
+  const int fmt = kv.format == 2 ? kFmtFp8 : (kv.format == 3 ? kFmtInt8 : kFmtBf16);
   const size_t lds = wide ? mla_lds(plan.rows_per_split, (kWideBufs - 1) * kTileLds + 2 * kSbufWide)
                          : mla_lds(plan.rows_per_split, kSbufLds);
   if (lds > kMaxLds) return hipErrorInvalidValue;
@@ -1020,11 +1055,13 @@ hipError_t launch_sparse_mla_bf16(const BatchArgs& ba, const void* q, const Pool
   hipError_t e;
   // Tiles of loads in flight per workgroup: two or three.
   if (wide)
-    e = fp8 ? launch_with_lds(sparse_mla_wide<true>, grid, kWideThreads, lds, stream, args, n_groups, T)
-            : launch_with_lds(sparse_mla_wide<false>, grid, kWideThreads, lds, stream, args, n_groups, T);
+    e = fmt == kFmtFp8    ? launch_with_lds(sparse_mla_wide<kFmtFp8>, grid, kWideThreads, lds, stream, args, n_groups, T)
+        : fmt == kFmtInt8 ? launch_with_lds(sparse_mla_wide<kFmtInt8>, grid, kWideThreads, lds, stream, args, n_groups, T)
+                          : launch_with_lds(sparse_mla_wide<kFmtBf16>, grid, kWideThreads, lds, stream, args, n_groups, T);
   else
-    e = fp8 ? launch_with_lds(sparse_mla_q16<true, 2>, grid, kThreads, lds, stream, args, n_groups, T)
-            : launch_with_lds(sparse_mla_q16<false, 3>, grid, kThreads, lds, stream, args, n_groups, T);
+    e = fmt == kFmtFp8    ? launch_with_lds(sparse_mla_q16<kFmtFp8, 2>, grid, kThreads, lds, stream, args, n_groups, T)
+        : fmt == kFmtInt8 ? launch_with_lds(sparse_mla_q16<kFmtInt8, 2>, grid, kThreads, lds, stream, args, n_groups, T)
+                          : launch_with_lds(sparse_mla_q16<kFmtBf16, 3>, grid, kThreads, lds, stream, args, n_groups, T);
   return e;
 }
 

@@ -13,8 +13,8 @@ ATOL_F32 = 1e-4
 
 def atol_for(cfg):
     from sparse_attention_07_amd import synth
-    if cfg.kv_fmt == synth.FMT_FP8_E4M3_B128:
-        return ATOL_FP8
+    if cfg.kv_fmt in (synth.FMT_FP8_E4M3_B128, synth.FMT_INT8_AFFINE_B128):
+        return ATOL_FP8   # 8-bit caches: each decoded element is rounded to bf16 once
     if cfg.q_fmt == synth.FMT_F32:
         return ATOL_F32
     return ATOL_BF16

@@ -3,7 +3,7 @@
 Indices must match bit-exactly (indexer tensors are drawn as small
 power-of-two-scaled integers, so every fp32 score is exact); scores must equal
 the oracle's exactly; attention outputs and lse within
-|g - r| <= atol + 1e-2 |r| (atol 2e-2 bf16, 6e-2 fp8 cache, 1e-4 f32).
+|g - r| <= atol + 1e-2 |r| (atol 2e-2 bf16, 6e-2 fp8 or int8 cache, 1e-4 f32).
 """
 import sys
 
@@ -66,6 +66,14 @@ REDUCED = {
     # requests with no rows and mixed draft lengths; more than 256 requests
     "ragged_q_lens_empty": dict(cfg=4, q_lens=[5, 0, 3, 1, 0, 5, 2], ctx=(600, 3000), topk=512),
     "many_requests": dict(cfg=1, batch=300, ctx=(40, 700), topk=256),
+    # affine int8 latent cache: 16-head groups, 64-head groups, drafts, prefill, page size 5
+    "decode16_int8": dict(cfg=1, batch=5, ctx=(300, 3000), topk=512, kv_fmt=synth.FMT_INT8_AFFINE_B128),
+    "decode16_p5_int8": dict(cfg=1, batch=4, ctx=(300, 1300), topk=256, page_size=5,
+                             kv_fmt=synth.FMT_INT8_AFFINE_B128),
+    "decode_h64_int8": dict(cfg=2, batch=3, ctx=(900, 3000), topk=512, heads=64, layers=1,
+                            kv_fmt=synth.FMT_INT8_AFFINE_B128),
+    "mtp_int8": dict(cfg=4, batch=3, ctx=(3000, 9000), topk=512, kv_fmt=synth.FMT_INT8_AFFINE_B128),
+    "prefill_int8": dict(cfg=3, q_len=130, ctx=(700, 700), topk=512, kv_fmt=synth.FMT_INT8_AFFINE_B128),
     # fp8 index keys (one scale per token) under bf16 queries: decode, drafts, prefill rows
     "decode16_fp8_keys": dict(cfg=1, batch=6, ctx=(100, 3000), topk=512, key_fmt=synth.FMT_FP8_E4M3_B128),
     "decode16_p5_fp8_keys": dict(cfg=1, batch=4, ctx=(300, 1300), topk=256, page_size=5,
