@@ -130,6 +130,11 @@ constexpr int kLoadsPerStep = KFP8 ? 10 : 16;
 // page offsets off, -1 when unmapped) against the nr staged query rows; row r
 // sits at position pos_first + r (clamped to ld_last) and its output row is
 // row0 + r.
+// max(x, 0) as a signed-integer max of the bit pattern: a negative float is a
+// negative integer (and -0 gives +0).  One v_max_i32, where fmaxf on an MFMA
+// result also costs a NaN-quieting v_max_f32 first.
+__device__ inline float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 template <bool SCALED = false>
 __device__ inline void score_block(const Keys& kk, const int64_t (&off)[2], const uint8_t* q_lds,
                                    const float* w_lds, int nr, int s_base, int pos_first,
@@ -165,7 +170,7 @@ __device__ inline void score_block(const Keys& kk, const int64_t (&off)[2], cons
         for (int q4 = 0; q4 < 4; ++q4) {
           const f32x4 wq = *reinterpret_cast<const f32x4*>(wr + mt * 32 + 8 * q4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) part += wq[e] * fmaxf(acc[nt][mt][4 * q4 + e], 0.f);
+          for (int e = 0; e < 4; ++e) part += wq[e] * relu_bits(acc[nt][mt][4 * q4 + e]);
         }
       part += __shfl_xor(part, 32);
       // a token's non-negative scale factors out of the ReLU and the head sum

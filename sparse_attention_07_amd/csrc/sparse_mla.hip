@@ -989,7 +989,11 @@ MlaPlan plan_sparse_mla(int num_q_rows, int n_heads, int k, int dc, bool prefill
   const int64_t blocks = (int64_t)num_q_rows * (wide ? n_heads / 64 : n_heads / 16);
   int splits = 1;
   if (!prefill) {
-    const int64_t target = wide ? 384 : 512;
+    // Workgroups wanted: 16-head groups, one per CU (a lone resident workgroup
+    // streams a longer range and leaves half the split partials to merge;
+    // two per CU measured 6% slower at 64 decode rows); 64-head groups, 1.5
+    // waves of the 512-thread workgroups.
+    const int64_t target = wide ? 384 : 256;
     // at most 64 splits: the merge keeps 2 x 64 heads x splits floats in the tile buffer
     const int max_splits = k / 256 > 64 ? 64 : (k / 256 > 1 ? k / 256 : 1);
     const int64_t want = (target + blocks - 1) / blocks;
