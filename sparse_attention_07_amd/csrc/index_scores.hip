@@ -161,23 +161,31 @@ __device__ inline void score_block(const Keys& kk, const int64_t (&off)[2], cons
     // Accumulator (i, lane) of a 32x32 tile holds head 8*(i/4) + 4*(lane/32) + i%4
     // and token column lane%32.
     const float* wr = w_lds + r * kHeads + 4 * (lane >> 5);
+    float part[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      float part = 0.f;
+      part[nt] = 0.f;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const f32x4 wq = *reinterpret_cast<const f32x4*>(wr + mt * 32 + 8 * q4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) part += wq[e] * relu_bits(acc[nt][mt][4 * q4 + e]);
+          for (int e = 0; e < 4; ++e) part[nt] += wq[e] * relu_bits(acc[nt][mt][4 * q4 + e]);
         }
-      part += __shfl_xor(part, 32);
-      // a token's non-negative scale factors out of the ReLU and the head sum
-      if (SCALED) part *= ksc[nt];
-      const int s = s_base + nt * 32 + (lane & 31);
-      if (lane < 32 && s <= pos_r && off[nt] >= 0) scores[(row0 + r) * ld + s] = part;
     }
+    // Each token's head sum is split over lanes l and l + 32.  One swap of the
+    // upper half of part[0] with the lower half of part[1] puts both halves of
+    // token l (first 32 tokens) in lane l < 32 and of token l (last 32) in
+    // lane l >= 32, so after one add lane l holds the score of token s_base + l.
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[1]),
+                                                     false, false);
+    float score = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    const int nt = lane >> 5;
+    // a token's non-negative scale factors out of the ReLU and the head sum
+    if (SCALED) score *= nt ? ksc[1] : ksc[0];
+    const int s = s_base + lane;
+    if (s <= pos_r && (nt ? off[1] : off[0]) >= 0) scores[(row0 + r) * ld + s] = score;
   }
 }
 
