@@ -236,7 +236,9 @@ size_t dsa_topk_workspace_bytes(int32_t num_q_rows, int32_t max_seq_len, int32_t
 dsa_status dsa_topk(const dsa_batch *batch, const float *scores, int64_t ld, int32_t k,
                     int32_t *idx, void *ws, size_t ws_bytes, void *stream);
 
-/* Workspace bytes dsa_sparse_mla_decode (prefill != 0: _prefill) needs. */
+/* Workspace bytes dsa_sparse_mla_decode (prefill != 0: _prefill) needs, for
+ * any latent cache format (the split plan may differ between bf16 and 8-bit
+ * rows; the size returned covers both). */
 size_t dsa_sparse_mla_workspace_bytes(int32_t num_q_rows, int32_t n_heads, int32_t k,
                                       int32_t dc, int32_t prefill);
 

@@ -159,7 +159,8 @@ dsa_status sparse_mla(const dsa_batch* batch, const void* q, int32_t q_format, c
     const int64_t row_bytes = kv->format == DSA_BF16 ? 1152 : (kv->format == DSA_FP8_E4M3_B128 ? 656 : 672);
     if ((st = check_pool(kv, row_bytes, 16, &pa)) != DSA_OK) return st;
     if (!aligned(q, 16) || !aligned(out, 16)) return DSA_ERR_ALIGN;
-    const dsa::MlaPlan plan = dsa::plan_sparse_mla(ba.num_q_rows, n_heads, k, dc, prefill);
+    const dsa::MlaPlan plan = dsa::plan_sparse_mla(ba.num_q_rows, n_heads, k, dc, prefill,
+                                                   kv->format != DSA_BF16);
     if (plan.ws_bytes > 0) {
       if (ws == nullptr) return DSA_ERR_WORKSPACE;
       if (ws_bytes < plan.ws_bytes) return DSA_ERR_WORKSPACE;
@@ -305,7 +306,9 @@ dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld, int
 
 size_t dsa_sparse_mla_workspace_bytes(int32_t num_q_rows, int32_t n_heads, int32_t k, int32_t dc,
                                       int32_t prefill) {
-  return dsa::plan_sparse_mla(num_q_rows, n_heads, k, dc, prefill != 0).ws_bytes;
+  // enough for every latent format (their split plans may differ)
+  return std::max(dsa::plan_sparse_mla(num_q_rows, n_heads, k, dc, prefill != 0, false).ws_bytes,
+                  dsa::plan_sparse_mla(num_q_rows, n_heads, k, dc, prefill != 0, true).ws_bytes);
 }
 
 dsa_status dsa_sparse_mla_decode(const dsa_batch* batch, const void* q, int32_t q_format,

@@ -54,7 +54,8 @@ struct MlaPlan {
   size_t ws_bytes;         // split partials, then arrival counters (0 when splits == 1)
   size_t counters_offset;  // byte offset of the counters in the workspace
 };
-MlaPlan plan_sparse_mla(int num_q_rows, int n_heads, int k, int dc, bool prefill);
+// q8: the latent rows are 8-bit (fp8 or int8), which changes the 16-head split.
+MlaPlan plan_sparse_mla(int num_q_rows, int n_heads, int k, int dc, bool prefill, bool q8);
 
 hipError_t launch_sparse_mla_bf16(const BatchArgs& ba, const void* q, const PoolArgs& kv,
                                   const int32_t* idx, int k, int n_heads, float sm_scale,

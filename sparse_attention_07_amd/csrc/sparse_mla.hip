@@ -812,8 +812,10 @@ __device__ inline bf16x8 regtile_operand(const RegTile<F>& st, int k, int ks) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-template <int F, int STAGES>
-__global__ __launch_bounds__(kThreads, 2) void sparse_mla_q16(MlaArgs a, int n_groups, int T) {
+// MINW: workgroups per CU the register budget is sized for (1 when the grid
+// fits the CUs in one round, so each wave may use a SIMD's whole register file).
+template <int F, int STAGES, int MINW>
+__global__ __launch_bounds__(kThreads, MINW) void sparse_mla_q16(MlaArgs a, int n_groups, int T) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   // Workgroup ids: head group outermost over a block of P = (T * splits
   // rounded up to 8) ids, so the head groups of one (row, split) are a
@@ -891,15 +893,15 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_q16(MlaArgs a, int n_g
 #pragma unroll
       for (int i2 = 0; i2 < 8; ++i2) o[i2] = mfma16(pa, join(tv1[i2], tv2[i2]), o[i2]);
     };
-    RegTile<F> st0, st1, st2;
-    regtile_load<F>(st0, offs[my_row], a.kv, ks0, g);
-    if (ntiles > 1) regtile_load<F>(st1, offs[kTileRows + my_row], a.kv, ks0, g);
-    if (STAGES == 3 && ntiles > 2) regtile_load<F>(st2, offs[2 * kTileRows + my_row], a.kv, ks0, g);
+    RegTile<F> st[STAGES];
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s)
+      if (s < ntiles) regtile_load<F>(st[s], offs[s * kTileRows + my_row], a.kv, ks0, g);
 #pragma unroll 1
     for (int i = 0; i < ntiles; i += STAGES) {
-      step(st0, i);
-      if (i + 1 < ntiles) step(st1, i + 1);
-      if (STAGES == 3 && i + 2 < ntiles) step(st2, i + 2);
+#pragma unroll
+      for (int s = 0; s < STAGES; ++s)
+        if (i + s < ntiles) step(st[s], i + s);
     }
   }
 
@@ -982,18 +984,20 @@ __global__ __launch_bounds__(kWave) void sparse_mla_f32_valu(
 
 }  // namespace
 
-MlaPlan plan_sparse_mla(int num_q_rows, int n_heads, int k, int dc, bool prefill) {
+MlaPlan plan_sparse_mla(int num_q_rows, int n_heads, int k, int dc, bool prefill, bool q8) {
   MlaPlan p{1, k, 0, 0};
   if (dc != kDc || n_heads % 16 != 0 || k <= 0 || num_q_rows <= 0) return p;
   const bool wide = n_heads % 64 == 0;
   const int64_t blocks = (int64_t)num_q_rows * (wide ? n_heads / 64 : n_heads / 16);
   int splits = 1;
   if (!prefill) {
-    // Workgroups wanted: 16-head groups, one per CU (a lone resident workgroup
-    // streams a longer range and leaves half the split partials to merge;
-    // two per CU measured 6% slower at 64 decode rows); 64-head groups, 1.5
-    // waves of the 512-thread workgroups.
-    const int64_t target = wide ? 384 : 256;
+    // Workgroups wanted.  16-head groups over bf16 rows: one per CU (a lone
+    // resident workgroup streams a longer range and leaves half the split
+    // partials to merge; two per CU measured 6% slower at 64 decode rows).
+    // Over 8-bit rows, whose decode is VALU work, two per CU (a second wave
+    // per SIMD hides it: 57 against 73+ us at 64 decode rows).  64-head
+    // groups: 1.5 waves of the 512-thread workgroups.
+    const int64_t target = wide ? 384 : (q8 ? 512 : 256);
     // at most 64 splits: the merge keeps 2 x 64 heads x splits floats in the tile buffer
     const int max_splits = k / 256 > 64 ? 64 : (k / 256 > 1 ? k / 256 : 1);
     const int64_t want = (target + blocks - 1) / blocks;
@@ -1062,10 +1066,14 @@ hipError_t launch_sparse_mla_bf16(const BatchArgs& ba, const void* q, const Pool
     e = fmt == kFmtFp8    ? launch_with_lds(sparse_mla_wide<kFmtFp8>, grid, kWideThreads, lds, stream, args, n_groups, T)
         : fmt == kFmtInt8 ? launch_with_lds(sparse_mla_wide<kFmtInt8>, grid, kWideThreads, lds, stream, args, n_groups, T)
                           : launch_with_lds(sparse_mla_wide<kFmtBf16>, grid, kWideThreads, lds, stream, args, n_groups, T);
+  else if (fmt == kFmtFp8)
+    e = launch_with_lds(sparse_mla_q16<kFmtFp8, 2, 2>, grid, kThreads, lds, stream, args, n_groups, T);
+  else if (fmt == kFmtInt8)
+    e = launch_with_lds(sparse_mla_q16<kFmtInt8, 2, 2>, grid, kThreads, lds, stream, args, n_groups, T);
+  else if ((int)grid.x <= device_cu_count())  // one round of workgroups: one per CU
+    e = launch_with_lds(sparse_mla_q16<kFmtBf16, 3, 1>, grid, kThreads, lds, stream, args, n_groups, T);
   else
-    e = fmt == kFmtFp8    ? launch_with_lds(sparse_mla_q16<kFmtFp8, 2>, grid, kThreads, lds, stream, args, n_groups, T)
-        : fmt == kFmtInt8 ? launch_with_lds(sparse_mla_q16<kFmtInt8, 2>, grid, kThreads, lds, stream, args, n_groups, T)
-                          : launch_with_lds(sparse_mla_q16<kFmtBf16, 3>, grid, kThreads, lds, stream, args, n_groups, T);
+    e = launch_with_lds(sparse_mla_q16<kFmtBf16, 3, 2>, grid, kThreads, lds, stream, args, n_groups, T);
   return e;
 }
 
