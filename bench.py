@@ -158,7 +158,12 @@ def key_fp8_overlap(path, cfg_id, mode):
     same key draws are cached in bf16 instead of fp8 (input set 0)."""
     from sparse_attention_07_amd import synth
     from sparse_attention_07_amd.path import DSAPath
-    ref = DSAPath(synth.make_batch(cfg_id, mode=mode, device=path.sb.q_idx.device, layers=0))
+    sb = synth.make_batch(cfg_id, mode=mode, device=path.sb.q_idx.device, layers=0)
+    # with the preparation in the step, both sides rotate the same queries and store the same keys
+    ref = DSAPath(sb, prep=synth.make_prep(sb, seed=4242) if path.prep is not None else None)
+    if ref.prep is not None:
+        ref.indexer_prepare()
+        path.indexer_prepare()
     ref.index_scores()
     ref.topk()
     path.index_scores()

@@ -172,14 +172,18 @@ dsa_status dsa_index_scores(const dsa_batch *batch, const void *q_idx, int32_t q
  * rope_cos, rope_sin  device [rope_rows, rope_dim/2] f32 (caller-built tables,
  *              any frequency scaling included); rope_rows >= max_seq_len.  May
  *              be NULL when rope_dim == 0.
- * k_idx        the index-key pool (format == `format`, dim == head_dim).  Its
+ * k_idx        the index-key pool (format == `format`, dim == head_dim), or,
+ *              with bf16 inputs and head_dim 128, a DSA_FP8_E4M3_B128 key pool
+ *              laid out as dsa_index_scores describes: the key is stored as
+ *              e4m3fn codes of key / scale (rounded to nearest even) with
+ *              scale = max|key| / 448 (1 for a zero key) in its scale slot.  Its
  *              base IS WRITTEN: the key of row t goes to token pos(t) of its
  *              request (nothing is written when that page is not mapped).
  * Work is done in f32; bf16 results are rounded to nearest even.  A row whose
  * position is outside [0, rope_rows) is left untouched.  Run it before
  * dsa_index_scores of the same step (which reads the keys it stores).
  * Built: head_dim a multiple of 16 up to 128, rope_dim a multiple of 16 up to
- * head_dim, n_heads <= 1024.
+ * head_dim, n_heads <= 1024; fp8 key pools with bf16 inputs and head_dim 128.
  */
 dsa_status dsa_indexer_prepare(const dsa_batch *batch, const void *q_in, void *q_out,
                                const void *k_in, int32_t format, const float *ln_weight,

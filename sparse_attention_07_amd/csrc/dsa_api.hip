@@ -262,8 +262,9 @@ dsa_status dsa_indexer_prepare(const dsa_batch* batch, const void* q_in, void* q
     return DSA_ERR_NULL;
   if (rope_dim > 0 && (rope_cos == nullptr || rope_sin == nullptr)) return DSA_ERR_NULL;
   if (format != DSA_BF16 && format != DSA_F32) return DSA_ERR_UNSUPPORTED;
-  if (k_idx->format == DSA_FP8_E4M3_B128) return DSA_ERR_UNSUPPORTED;
-  if (k_idx->format != format || k_idx->dim != head_dim) return DSA_ERR_SHAPE;
+  const bool fp8_keys = k_idx->format == DSA_FP8_E4M3_B128;
+  if (fp8_keys && (format != DSA_BF16 || head_dim != 128)) return DSA_ERR_UNSUPPORTED;
+  if ((k_idx->format != format && !fp8_keys) || k_idx->dim != head_dim) return DSA_ERR_SHAPE;
   if (n_heads < 1 || head_dim < 1 || rope_dim < 0 || rope_dim > head_dim || !(ln_eps >= 0.f))
     return DSA_ERR_SHAPE;
   if (n_heads > 1024 || head_dim > 128 || head_dim % 16 != 0 || rope_dim % 16 != 0)
@@ -272,7 +273,14 @@ dsa_status dsa_indexer_prepare(const dsa_batch* batch, const void* q_in, void* q
   if (rope_dim == 0) rope_rows = INT32_MAX;  // no table is read
   const int es = format == DSA_BF16 ? 2 : 4;
   PoolArgs pa;
-  if ((st = check_pool(k_idx, (int64_t)head_dim * es, 16, &pa)) != DSA_OK) return st;
+  if (fp8_keys) {
+    // page-blocked: page_size rows of 128 codes, then page_size f32 scales
+    if ((st = check_pool(k_idx, 128, 16, &pa)) != DSA_OK) return st;
+    if (k_idx->page_stride_bytes < (int64_t)ba.page_size * (k_idx->row_stride_bytes + 4))
+      return DSA_ERR_SHAPE;
+  } else if ((st = check_pool(k_idx, (int64_t)head_dim * es, 16, &pa)) != DSA_OK) {
+    return st;
+  }
   if (!aligned(q_in, 16) || !aligned(q_out, 16) || !aligned(k_in, 16) || !aligned(ln_weight, 4) ||
       !aligned(ln_bias, 4) || (rope_dim > 0 && (!aligned(rope_cos, 16) || !aligned(rope_sin, 16))))
     return DSA_ERR_ALIGN;

@@ -9,7 +9,9 @@
 // One workgroup of 256 threads per query row.  Wave 0 normalises the key (one
 // or two dims per lane, two-pass mean and variance by wave reductions) into
 // LDS while every wave rotates the query heads in 16-element units; after one
-// barrier the key's units are rotated from LDS and stored into the pool.
+// barrier the key's units are rotated from LDS and stored into the pool.  An
+// fp8 key pool (page-blocked: P rows of 128 e4m3 codes, then P f32 scales)
+// gets the rotated key's codes at scale amax/448 and that scale.
 //
 // A unit is two 8-element chunks of one head: a rotated unit holds whole
 // rotation pairs -- chunks u and u + R/16 when not interleaved (dims i and
@@ -49,7 +51,10 @@ struct PrepArgs {
   int n_heads, head_dim;
   uint8_t* pool;
   int64_t page_stride, row_stride;
+  int key_fp8;
 };
+
+typedef short __attribute__((ext_vector_type(2))) s16x2;
 
 // Eight elements of one chunk as f32 (bf16: one 16-byte load; f32: two).
 template <bool BF16>
@@ -191,29 +196,55 @@ __global__ __launch_bounds__(kPrepThreads) void indexer_prepare_kernel(PrepArgs 
   __syncthreads();
 
   // Key: rotate from LDS and store at the row's token slot.
+  const int64_t off = token_offset(a.page_table, a.pt_stride, a.page_size, a.num_pages, loc.b, pos,
+                                   a.page_stride, a.row_stride);
   if (tid < upr) {
-    const int64_t off = token_offset(a.page_table, a.pt_stride, a.page_size, a.num_pages, loc.b, pos,
-                                     a.page_stride, a.row_stride);
-    if (off >= 0) {
-      int c0, c1;
-      const bool rot = unit_chunks(tid, R, inter, c0, c1);
-      float x0[8], x1[8];
+    int c0, c1;
+    const bool rot = unit_chunks(tid, R, inter, c0, c1);
+    float x0[8], x1[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x0[e] = kn[c0 * 8 + e];
+      x1[e] = kn[c1 * 8 + e];
+    }
+    if (rot) {
+      float c[8], s[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        x0[e] = kn[c0 * 8 + e];
-        x1[e] = kn[c1 * 8 + e];
+        c[e] = ct[8 * tid + e];
+        s[e] = st[8 * tid + e];
       }
-      if (rot) {
-        float c[8], s[8];
+      rotate_unit(x0, x1, c, s, inter);
+    }
+    if (!a.key_fp8) {
+      if (off >= 0) {
+        store8<BF16>(a.pool + off + c0 * 8 * es, x0);
+        store8<BF16>(a.pool + off + c1 * 8 * es, x1);
+      }
+    } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          c[e] = ct[8 * tid + e];
-          s[e] = st[8 * tid + e];
-        }
-        rotate_unit(x0, x1, c, s, inter);
+      for (int e = 0; e < 8; ++e) {  // the rotated key back in place (same unit, same thread)
+        kn[c0 * 8 + e] = x0[e];
+        kn[c1 * 8 + e] = x1[e];
       }
-      store8<BF16>(a.pool + off + c0 * 8 * es, x0);
-      store8<BF16>(a.pool + off + c1 * 8 * es, x1);
+    }
+  }
+  if (!a.key_fp8) return;
+  __syncthreads();
+  if (wave != 0) return;
+  // fp8 key (D = 128): lane l quantises dims 2l and 2l+1 at scale amax / 448.
+  const float v0 = kn[2 * lane], v1 = kn[2 * lane + 1];
+  float amax = fmaxf(fabsf(v0), fabsf(v1));
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+  const float scale = amax > 0.f ? amax / 448.f : 1.f;
+  if (off >= 0) {
+    s16x2 pk = {0, 0};
+    pk = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(pk, v0 / scale, v1 / scale, 1.0f, false);
+    *reinterpret_cast<uint16_t*>(a.pool + off + 2 * lane) = (uint16_t)pk[0];
+    if (lane == 0) {
+      const int slot = pos % a.page_size;  // off = page * page_stride + slot * row_stride
+      *reinterpret_cast<float*>(a.pool + off + (int64_t)(a.page_size - slot) * a.row_stride + slot * 4) = scale;
     }
   }
 }
@@ -226,6 +257,7 @@ hipError_t launch_indexer_prepare(const BatchArgs& ba, const void* q_in, void* q
                                   int rope_dim, int interleaved, const PoolArgs& pool, int n_heads,
                                   int head_dim, hipStream_t stream) {
   PrepArgs a;
+  a.key_fp8 = pool.format == 2;
   a.cu_q = ba.cu_q;
   a.seq_lens = ba.seq_lens;
   a.page_table = ba.page_table;

@@ -110,7 +110,12 @@ def test_indexer_prepare_validation():
     assert _prep(_batch(), cos=None) == 1
     assert _prep(_batch(), R=0, cos=None, sin=None, q_in=ODD) == 6   # no table needed without rotation
     assert _prep(_batch(), fmt=dsa.DSA_FP8_E4M3_B128) == 3
-    assert _prep(_batch(), pool=_pool(dsa.DSA_FP8_E4M3_B128, 128, 128)) == 3
+    # fp8 key pools (page-blocked codes + scales): bf16 keys of 128 dims only
+    fp8 = lambda page, row=128, dim=128: dsa.dsa_pool(FAKE.value, dsa.DSA_FP8_E4M3_B128, dim, page, row)
+    assert _prep(_batch(), pool=fp8(16 * 132), q_in=ODD) == 6            # valid pool: reaches the checks after it
+    assert _prep(_batch(), pool=fp8(16 * 128)) == 2                      # no room for the scales
+    assert _prep(_batch(), pool=fp8(16 * 132), fmt=dsa.DSA_F32) == 3     # fp8 keys need bf16 inputs
+    assert _prep(_batch(), pool=fp8(16 * 132, dim=64), D=64) == 3
     assert _prep(_batch(), pool=_pool(dsa.DSA_F32, 128, 512)) == 2      # pool format differs
     assert _prep(_batch(), pool=_pool(dsa.DSA_BF16, 64, 128)) == 2      # pool dim differs
     assert _prep(_batch(), R=72) == 3                                    # not a multiple of 16

@@ -4,7 +4,11 @@ The kernel works in f32 and rounds bf16 results to nearest even once, so an
 element g is compared with the oracle's float64 value r as
 |g - r| <= 2^-8 |r| + 1e-4 for bf16 (twice the rounding bound, plus room
 for f32 rounding inside LayerNorm and the rotation) and 1e-5 (1 + |r|) for
-f32.  Pool bytes outside the rows' slots must not change at all.
+f32.  Pool bytes outside the rows' slots must not change at all.  An fp8
+key pool's stored key, decoded with the oracle's e4m3 decoder, must lie
+within one e4m3 rounding of the oracle's float64 key, and its scale within
+1e-5 of amax / 448 (the codes themselves are a rounding decision taken on
+differently rounded f32 inputs, so they are not compared bit for bit).
 """
 import sys
 
@@ -40,11 +44,21 @@ def _close(g, r, bf16, what):
         what, int(bad.sum()), bad.size, float(np.abs(g - r).max()))
 
 
+def _fp8_key_close(dec, r, scale, what):
+    # one e4m3 rounding of r / scale: half a step of 3 mantissa bits (2^-4 relative)
+    # for normals, half the subnormal step 2^-10 times the scale below 2^-6
+    tol = np.maximum(2.0 ** -4 * np.abs(r), 2.0 ** -10 * scale) * (1 + 1e-5) + 1e-6
+    bad = np.abs(dec - r) > tol
+    assert not bad.any(), "%s: %d of %d outside one e4m3 rounding, worst %.3g" % (
+        what, int(bad.sum()), bad.size, float(np.abs(dec - r).max()))
+
+
 def _run_and_check(sb, pr, in_place=False):
     from sparse_attention_07_amd import dsa
     cfg = sb.cfg
     pool_before = sb.k_pool.clone()
-    ref = oracle.indexer_prepare(sb, pr)            # host copies of the same inputs
+    fp8 = cfg.key_fmt == synth.FMT_FP8_E4M3_B128
+    ref = oracle.indexer_prepare(sb, pr, with_pool=not fp8)   # host copies of the same inputs
     kp = dsa.make_key_pool(sb)
     b = dsa.batch_from(sb)
     if in_place:
@@ -58,8 +72,30 @@ def _run_and_check(sb, pr, in_place=False):
     bf16 = cfg.idx_fmt == synth.FMT_BF16
     _close(q_out.double().cpu().numpy(), ref["q"], bf16, "q")
     P = cfg.page_size
-    pool = sb.k_pool.double().cpu().reshape(-1, cfg.di).numpy()
     pt = sb.page_table.cpu().numpy()
+    if fp8:
+        pages = sb.k_pool.cpu().numpy()
+        dec = oracle.decode_fp8_keys(pages, P)                 # [num_pages * P, 128]
+        scales = pages[:, P * 128:P * 132].copy().view(np.float32).reshape(-1)
+        written = np.zeros(dec.shape[0], dtype=bool)
+        for t, (req, p) in enumerate(zip(sb.row_request(), sb.positions())):
+            page = pt[req, p // P] if p // P < pt.shape[1] else -1
+            if 0 <= page < pages.shape[0]:
+                slot = page * P + p % P
+                written[slot] = True
+                amax = np.abs(ref["k"][t]).max()
+                assert abs(scales[slot] - amax / 448) <= 1e-5 * amax / 448, (t, scales[slot], amax / 448)
+                _fp8_key_close(dec[slot], ref["k"][t], scales[slot], "fp8 key of row %d" % t)
+        before = pool_before.cpu().numpy()
+        codes_b = before[:, :P * 128].reshape(-1, 128)
+        codes_a = pages[:, :P * 128].reshape(-1, 128)
+        sc_b = before[:, P * 128:P * 132].reshape(-1, 4)
+        sc_a = pages[:, P * 128:P * 132].reshape(-1, 4)
+        assert np.array_equal(codes_b[~written], codes_a[~written]), "codes outside the rows' slots changed"
+        assert np.array_equal(sc_b[~written], sc_a[~written]), "scales outside the rows' slots changed"
+        assert np.array_equal(before[:, P * 132:], pages[:, P * 132:]), "page padding changed"
+        return ref
+    pool = sb.k_pool.double().cpu().reshape(-1, cfg.di).numpy()
     written = np.zeros(pool.shape[0], dtype=bool)
     for t, (req, p) in enumerate(zip(sb.row_request(), sb.positions())):
         page = pt[req, p // P] if p // P < pt.shape[1] else -1
@@ -86,6 +122,11 @@ CASES = {
     "no_rope": dict(cfg=1, kw=dict(batch=3, ctx=(100, 900), topk=256), prep=dict(rope_dim=0)),
     "full_rope": dict(cfg=1, kw=dict(batch=3, ctx=(100, 900), topk=256), prep=dict(rope_dim=128)),
     "tiny_f32": dict(cfg=0, kw=dict(), prep=dict(rope_dim=16)),
+    # fp8 index keys: codes at the rotated key's amax / 448 plus that scale
+    "decode16_fp8_keys": dict(cfg=1, kw=dict(batch=6, ctx=(100, 3000), topk=512, key_fmt=synth.FMT_FP8_E4M3_B128),
+                              prep=dict()),
+    "mtp_fp8_keys_page5": dict(cfg=4, kw=dict(batch=3, ctx=(600, 3000), topk=512, page_size=5,
+                                              key_fmt=synth.FMT_FP8_E4M3_B128), prep=dict(interleaved=True)),
 }
 
 
