@@ -222,7 +222,10 @@ dsa_status dsa_index_topk(const dsa_batch *batch, const void *q_idx, int32_t q_f
  * num_q_rows <= 0): such a budget cannot run the call. */
 size_t dsa_index_topk_workspace_bytes(int32_t num_q_rows, int32_t max_seq_len, int64_t budget_bytes);
 
-/* Workspace bytes dsa_topk needs for these sizes (0 today; query it anyway). */
+/* Workspace bytes dsa_topk needs for these sizes: 0 when max_seq_len <= 32768
+ * or max_seq_len <= k; otherwise room for the candidates of a two-level
+ * selection (an f32 score and an int32 position for each of k slots of each
+ * 32768-entry segment of each row). */
 size_t dsa_topk_workspace_bytes(int32_t num_q_rows, int32_t max_seq_len, int32_t k);
 
 /*
@@ -235,7 +238,11 @@ size_t dsa_topk_workspace_bytes(int32_t num_q_rows, int32_t max_seq_len, int32_t
  * s <= min(pos(t), ld-1) of each score row are read.  Scores must be
  * finite.
  * scores   device [T, ld] f32;  idx  device [T, k] int32
- * ws       device workspace of dsa_topk_workspace_bytes() bytes (may be NULL when 0)
+ * ws       device workspace of dsa_topk_workspace_bytes() bytes (may be NULL when
+ *          0; DSA_ERR_WORKSPACE when smaller).  Rows longer than 32768 entries
+ *          are then selected in two levels: the exact top-k of each 32768-entry
+ *          segment, then the top-k of those candidates.  Both levels use the
+ *          order above, so the result is the same set in the same order.
  */
 dsa_status dsa_topk(const dsa_batch *batch, const float *scores, int64_t ld, int32_t k,
                     int32_t *idx, void *ws, size_t ws_bytes, void *stream);

@@ -291,16 +291,11 @@ dsa_status dsa_indexer_prepare(const dsa_batch* batch, const void* q_in, void* q
 }
 
 size_t dsa_topk_workspace_bytes(int32_t num_q_rows, int32_t max_seq_len, int32_t k) {
-  (void)num_q_rows;
-  (void)max_seq_len;
-  (void)k;
-  return 0;
+  return dsa::topk_workspace_bytes(num_q_rows, max_seq_len, k);
 }
 
 dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld, int32_t k,
                     int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   BatchArgs ba;
   dsa_status st = check_batch(batch, &ba);
   if (st != DSA_OK) return st;
@@ -308,8 +303,13 @@ dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld, int
   if (scores == nullptr || idx == nullptr) return DSA_ERR_NULL;
   if (k < 1 || ld < 1 || ld < ba.max_seq_len) return DSA_ERR_SHAPE;
   if (!aligned(scores, 4) || !aligned(idx, 4)) return DSA_ERR_ALIGN;
+  const size_t need = dsa::topk_workspace_bytes(ba.num_q_rows, ba.max_seq_len, k);
+  if (need > 0) {
+    if (ws == nullptr || ws_bytes < need) return DSA_ERR_WORKSPACE;
+    if (!aligned(ws, 16)) return DSA_ERR_ALIGN;
+  }
   return hip_status(dsa::launch_topk(ba, scores, ld, k, idx, static_cast<hipStream_t>(stream), 0,
-                                     ba.num_q_rows));
+                                     ba.num_q_rows, ws, ws_bytes));
 }
 
 size_t dsa_sparse_mla_workspace_bytes(int32_t num_q_rows, int32_t n_heads, int32_t k, int32_t dc,

@@ -43,8 +43,13 @@ hipError_t launch_indexer_prepare(const BatchArgs& ba, const void* q_in, void* q
                                   int rope_dim, int interleaved, const PoolArgs& pool, int n_heads,
                                   int head_dim, hipStream_t stream);
 
+// With a workspace of topk_workspace_bytes(rows, max_seq_len, k) bytes, rows
+// longer than the LDS cache are selected in two levels; without one (or when
+// it is 0), one workgroup per row re-reads long rows in each pass.
+size_t topk_workspace_bytes(int num_q_rows, int max_seq_len, int k);
 hipError_t launch_topk(const BatchArgs& ba, const float* scores, int64_t ld, int k, int32_t* idx,
-                       hipStream_t stream, int row_lo, int row_hi);
+                       hipStream_t stream, int row_lo, int row_hi, void* ws = nullptr,
+                       size_t ws_bytes = 0);
 
 // Split plan of the MFMA sparse-MLA kernel (rows of each query cut into `splits`
 // ranges of `rows_per_split`); workspace holds the partial results.

@@ -7,7 +7,8 @@
 // threads per query row; the selection itself (order, ties, passes,
 // compaction) is in topk_select.h.  Rows of up to 32768 entries are cached in
 // LDS as keys after one read; longer rows are re-read in each pass (the two
-// cases are separate instantiations).
+// cases are separate instantiations), or, when the caller gives a workspace,
+// selected in two levels (topk_segments, then topk_merge).
 #include "dsa_device.h"
 #include "dsa_launch.h"
 #include "topk_select.h"
@@ -19,16 +20,24 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kCache = 32768;
 
+// Top-K of row[0, n): emit(o, s) for the o-th selected position s, o < K, in
+// ascending s.
+template <bool Cached, typename Emit>
+__device__ inline void select_emit(const float* __restrict__ row, int n, int K, uint32_t* cache,
+                                   uint32_t* hist, uint32_t* wcount, uint32_t* pick, Emit emit) {
+  const bool vec = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
+  const topk::Threshold th = topk::select<kThreads, Cached>(row, vec, n, K, cache, hist, pick);
+  auto emit_k = [emit, K](uint32_t o, int s) {
+    if (o < (uint32_t)K) emit(o, s);
+  };
+  if (Cached) topk::compact_cached<kThreads>(n, cache, th, wcount, emit_k);
+  else topk::compact<kThreads, Cached>(row, vec, n, cache, th, wcount, emit_k);
+}
+
 template <bool Cached>
 __device__ inline void select_row(const float* __restrict__ row, int n, int K, int32_t* __restrict__ out,
                                   uint32_t* cache, uint32_t* hist, uint32_t* wcount, uint32_t* pick) {
-  const bool vec = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
-  const topk::Threshold th = topk::select<kThreads, Cached>(row, vec, n, K, cache, hist, pick);
-  auto emit = [out, K](uint32_t o, int s) {
-    if (o < (uint32_t)K) out[o] = s;
-  };
-  if (Cached) topk::compact_cached<kThreads>(n, cache, th, wcount, emit);
-  else topk::compact<kThreads, Cached>(row, vec, n, cache, th, wcount, emit);
+  select_emit<Cached>(row, n, K, cache, hist, wcount, pick, [out](uint32_t o, int s) { out[o] = s; });
 }
 
 __global__ __launch_bounds__(kThreads) void topk_radix(const int32_t* __restrict__ cu_q,
@@ -55,12 +64,105 @@ __global__ __launch_bounds__(kThreads) void topk_radix(const int32_t* __restrict
   else select_row<false>(row, n, K, out, cache, hist, wcount, pick);
 }
 
+// Two-level selection for rows longer than the LDS cache.  Level 1: each
+// kSegLen-entry segment of a row gets its exact top-K (its entries cached in
+// LDS), stored as candidates: scores and positions, segment after segment,
+// ascending inside each segment, padded with (-inf, -1).  Level 2: the top-K
+// of a row's candidates.  Both levels use the same order (higher score, then
+// lower position), so the row's top-K lies in the union of its segments' and
+// level 2 picks exactly it; candidate order is position order, so ties still
+// go to the lower position.  Rows with n <= K use no candidates.  Segments
+// are as long as the cache: each workgroup's selection is mostly a fixed
+// chain of latencies, so fewer, fuller segments win (mtp_fp8 rows of 64-128K
+// entries: 84 us at 32768, 93 at 16384, 127 at 8192, 112 single-level).
+constexpr int kSegLen = kCache;
+
+__global__ __launch_bounds__(kThreads) void topk_segments(const int32_t* __restrict__ cu_q,
+                                                          const int32_t* __restrict__ seq_lens, int B,
+                                                          const float* __restrict__ scores, int64_t ld,
+                                                          int K, int row_lo, int segs, float* __restrict__ cand_sc,
+                                                          int32_t* __restrict__ cand_ix) {
+  __shared__ __align__(16) uint32_t cache[kSegLen];
+  __shared__ __align__(16) uint32_t hist[2 * topk::kHistWords];
+  __shared__ uint32_t wcount[2 * kThreads / kWave];
+  __shared__ uint32_t pick[3];
+
+  const int t = row_lo + (int)blockIdx.x, seg = (int)blockIdx.y;
+  const int tid = threadIdx.x;
+  const RowLoc loc = locate_row(cu_q, seq_lens, B, t);
+  const int n = (int)max<int64_t>(0, min<int64_t>((int64_t)loc.pos + 1, ld));
+  if (n <= K) return;  // topk_merge writes such rows directly
+  const int64_t base = ((int64_t)(t - row_lo) * segs + seg) * K;
+  const int s0 = seg * kSegLen, len = max(0, min(n - s0, kSegLen));
+  const float* row = scores + (int64_t)(t - row_lo) * ld + s0;
+  if (len <= K) {  // the whole segment, then padding
+    for (int j = tid; j < K; j += kThreads) {
+      cand_ix[base + j] = j < len ? s0 + j : -1;
+      cand_sc[base + j] = j < len ? row[j] : -INFINITY;
+    }
+    return;
+  }
+  select_emit<true>(row, len, K, cache, hist, wcount, pick, [=](uint32_t o, int s) {
+    cand_ix[base + o] = s0 + s;
+    cand_sc[base + o] = row[s];
+  });
+}
+
+__global__ __launch_bounds__(kThreads) void topk_merge(const int32_t* __restrict__ cu_q,
+                                                       const int32_t* __restrict__ seq_lens, int B, int64_t ld,
+                                                       int K, int32_t* __restrict__ idx, int row_lo, int segs,
+                                                       const float* __restrict__ cand_sc,
+                                                       const int32_t* __restrict__ cand_ix) {
+  __shared__ __align__(16) uint32_t cache[kCache];
+  __shared__ __align__(16) uint32_t hist[2 * topk::kHistWords];
+  __shared__ uint32_t wcount[2 * kThreads / kWave];
+  __shared__ uint32_t pick[3];
+
+  const int t = row_lo + (int)blockIdx.x;
+  const int tid = threadIdx.x;
+  const RowLoc loc = locate_row(cu_q, seq_lens, B, t);
+  const int n = (int)max<int64_t>(0, min<int64_t>((int64_t)loc.pos + 1, ld));
+  int32_t* out = idx + (int64_t)t * K;
+  if (n <= K) {
+    for (int j = tid; j < K; j += kThreads) out[j] = j < n ? j : -1;
+    return;
+  }
+  const int n2 = segs * K;
+  const float* row = cand_sc + (int64_t)(t - row_lo) * n2;
+  const int32_t* ix = cand_ix + (int64_t)(t - row_lo) * n2;
+  auto emit = [out, ix](uint32_t o, int s) { out[o] = ix[s]; };
+  if (n2 <= kCache) select_emit<true>(row, n2, K, cache, hist, wcount, pick, emit);
+  else select_emit<false>(row, n2, K, cache, hist, wcount, pick, emit);
+}
+
 }  // namespace
 
+size_t topk_workspace_bytes(int num_q_rows, int max_seq_len, int k) {
+  if (num_q_rows <= 0 || k <= 0 || max_seq_len <= kCache || max_seq_len <= k) return 0;
+  const int64_t segs = (max_seq_len + kSegLen - 1) / kSegLen;
+  const int64_t per = segs * k;  // candidates per row: a score and a position each
+  return (size_t)((num_q_rows * per * 4 + 255) / 256 * 256 + num_q_rows * per * 4);
+}
+
 hipError_t launch_topk(const BatchArgs& ba, const float* scores, int64_t ld, int k, int32_t* idx,
-                       hipStream_t stream, int row_lo, int row_hi) {
+                       hipStream_t stream, int row_lo, int row_hi, void* ws, size_t ws_bytes) {
   if (row_hi <= row_lo) return hipSuccess;
-  hipLaunchKernelGGL(topk_radix, dim3(row_hi - row_lo), dim3(kThreads), 0, stream, ba.cu_q,
+  const int rows = row_hi - row_lo;
+  const size_t need = topk_workspace_bytes(rows, ba.max_seq_len, k);
+  if (need > 0 && ws != nullptr && ws_bytes >= need) {
+    const int segs = (ba.max_seq_len + kSegLen - 1) / kSegLen;
+    float* cand_sc = static_cast<float*>(ws);
+    int32_t* cand_ix = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) +
+                                                  ((int64_t)rows * segs * k * 4 + 255) / 256 * 256);
+    hipLaunchKernelGGL(topk_segments, dim3(rows, segs), dim3(kThreads), 0, stream, ba.cu_q, ba.seq_lens,
+                       ba.batch, scores, ld, k, row_lo, segs, cand_sc, cand_ix);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_merge, dim3(rows), dim3(kThreads), 0, stream, ba.cu_q, ba.seq_lens, ba.batch, ld,
+                       k, idx, row_lo, segs, cand_sc, cand_ix);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(topk_radix, dim3(rows), dim3(kThreads), 0, stream, ba.cu_q,
                      ba.seq_lens, ba.batch, scores, ld, k, idx, row_lo);
   return hipGetLastError();
 }

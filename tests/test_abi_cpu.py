@@ -176,7 +176,18 @@ def test_topk_validation():
     assert L.dsa_topk(ctypes.byref(b), FAKE, 50, 8, FAKE, None, 0, None) == 2
     assert L.dsa_topk(ctypes.byref(b), None, 128, 8, FAKE, None, 0, None) == 1
     assert L.dsa_topk(ctypes.byref(b), FAKE, 128, 8, ctypes.c_void_p(0x10002), None, 0, None) == 6
-    assert dsa.dsa_topk_workspace_bytes(160, 131072, 2048) == 0
+    # rows that fit the LDS cache need no workspace; longer rows take a
+    # two-level selection whose candidates (an f32 score and an int32 position
+    # per segment slot: 32768-entry segments x k) live in the workspace
+    W = dsa.dsa_topk_workspace_bytes
+    assert W(64, 8192, 2048) == 0 and W(4, 32768, 2048) == 0 and W(4, 40000, 40000) == 0
+    assert W(160, 131072, 2048) == 160 * 4 * 2048 * 8
+    assert W(3, 40000, 7) == (3 * 2 * 7 * 4 + 255) // 256 * 256 + 3 * 2 * 7 * 4
+    long = _batch(max_seq=40000)
+    need = W(long.num_q_rows, 40000, 8)
+    assert L.dsa_topk(ctypes.byref(long), FAKE, 40064, 8, FAKE, None, 0, None) == 4          # workspace missing
+    assert L.dsa_topk(ctypes.byref(long), FAKE, 40064, 8, FAKE, FAKE, need - 1, None) == 4   # too small
+    assert L.dsa_topk(ctypes.byref(long), FAKE, 40064, 8, FAKE, ODD, need, None) == 6        # misaligned
 
 
 def _mla(batch, q_fmt=dsa.DSA_BF16, pool=None, k=2048, H=128, dc=512, dr=64, ws=None, ws_bytes=0,

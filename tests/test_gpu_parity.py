@@ -165,7 +165,11 @@ def test_topk_ties_and_lengths(K):
                        ld, 16, 1)
     sd = scores.to(DEV)
     idx = torch.full((len(rows), K), 12345, dtype=torch.int32, device=DEV)
-    dsa.dsa_topk(b, sd, ld, K, idx)
+    # rows past 32768 entries take the two-level selection (segments, then candidates)
+    ws_bytes = dsa.dsa_topk_workspace_bytes(len(rows), ld, K)
+    assert ws_bytes > 0
+    ws = torch.full((ws_bytes,), 0xAB, dtype=torch.uint8, device=DEV)   # stale contents must not matter
+    dsa.dsa_topk(b, sd, ld, K, idx, ws, ws_bytes)
     torch.cuda.synchronize()
     _parity.check_idx_exact(idx, ref)
 
