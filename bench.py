@@ -70,12 +70,12 @@ def parse():
 # counters were taken -- a changed kernel reports traffic null.
 # Copy calibration of those runs: FETCH_SIZE x 2.000, WRITE_SIZE x 1.000.
 TRAFFIC = {
-    ("decode16", "sparse_mla"): {"src": "6b3d0888b9427560", "fetch_bytes": 1.659e+08, "write_bytes": 9.525e+06,
-                        "dispatches": 42},
-    ("decode16", "index_scores"): {"src": "3548ffd6fdfc2fe4", "fetch_bytes": 8.102e+07, "write_bytes": 1.183e+06,
-                          "dispatches": 42},
-    ("decode16", "topk"): {"src": "3d28ab2f22b00af9", "fetch_bytes": 1.408e+06, "write_bytes": 5.243e+05,
-                  "dispatches": 42},
+    ("decode16", "sparse_mla"): {"src": "23a72b49629aaf8a", "fetch_bytes": 1.57e+08, "write_bytes": 5.29e+06,
+                                 "dispatches": 42},
+    ("decode16", "index_scores"): {"src": "8327363501a95fa5", "fetch_bytes": 8.101e+07, "write_bytes": 1.183e+06,
+                                   "dispatches": 42},
+    ("decode16", "topk"): {"src": "4e9ea48094ef7bbe", "fetch_bytes": 1.507e+06, "write_bytes": 7.552e+05,
+                           "dispatches": 42},
 }
 KERNEL_SOURCES = {"sparse_mla": ["sparse_mla.hip", "dsa_device.h"],
                   "index_scores": ["index_scores.hip", "dsa_device.h"],
@@ -110,6 +110,27 @@ def copy_calibration():
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration": {"read_bytes": 4 * n, "write_bytes": 4 * n, "launches": 4}}),
           flush=True)
+
+
+def measured_stream_peak():
+    """Bytes/s a plain 1 GiB f32 multiply (read + write) reaches on this GPU: the
+    practical HBM stream rate, reported beside the published peak."""
+    n = 1 << 28
+    src = torch.ones(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(10):
+        torch.mul(src, 1.0, out=dst)
+    b.record()
+    torch.cuda.synchronize()
+    rate = 2 * 4 * n * 10 / (a.elapsed_time(b) / 1e3)
+    del src, dst
+    torch.cuda.empty_cache()
+    return rate
 
 
 def algorithmic(sb, path):
@@ -345,6 +366,11 @@ def main():
     roof["alg_bytes_per_launch"] = r["alg_bytes"] / launches
     roof["alg_flops_per_launch"] = r["alg_flops"] / launches
     roof["avg_launch_ms"] = stage_ms[dom] / launches
+    # the practical stream rate of this GPU, beside the published peak
+    stream = measured_stream_peak() / 1e9
+    roof["measured_stream_GB_s"] = stream
+    if bound == "hbm":
+        roof["frac_of_measured_stream"] = roof["achieved"] / stream
 
     cfg = paths[0].sb.cfg
     out = {
