@@ -270,3 +270,43 @@ def test_graph_replay_matches_eager():
         got = [p.idx] + p.out + p.lse
         for a, b in zip(got, ref):
             assert torch.equal(a, b), "replay %d differs" % rep
+
+
+@pytest.mark.parametrize("case", ["prep_fp8keys_bounded", "long_rows_int8"])
+def test_graph_replay_new_paths(case):
+    """The preparation (fp8 key stores), bounded scoring and the two-level top-k
+    replay from a captured graph to the eager result bitwise; scratch buffers get
+    junk between replays."""
+    from sparse_attention_07_amd.path import DSAPath
+    if case == "prep_fp8keys_bounded":
+        sb = synth.make_batch(1, batch=6, ctx=(600, 4000), topk=512, layers=1, mode="perf", device=DEV,
+                              key_fmt=synth.FMT_FP8_E4M3_B128)
+        row_bytes = (sb.max_seq_len + 63) // 64 * 64 * 4
+        p = DSAPath(sb, prep=synth.make_prep(sb), score_budget=3 * row_bytes)   # 2 chunks of 3 rows
+        assert p.itk_ws_bytes == 3 * row_bytes
+    else:
+        sb = synth.make_batch(4, batch=2, ctx=(40000, 70000), topk=512, layers=2, mode="perf", device=DEV,
+                              kv_fmt=synth.FMT_INT8_AFFINE_B128)
+        p = DSAPath(sb)
+        assert p.topk_ws_bytes > 0                                               # two-level selection
+    p.step()
+    torch.cuda.synchronize()
+    outs = [p.idx, sb.q_idx, sb.k_pool] + p.out + p.lse
+    ref = [t.clone() for t in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        p.step()
+    for rep in range(3):
+        for t in [p.idx] + p.out + p.lse:
+            t.fill_(7)                                    # eager work between replays
+        p.scores.fill_(float("nan"))
+        if p.itk_ws_bytes:
+            p.itk_ws.fill_(float("nan"))
+        if p.topk_ws is not None:
+            p.topk_ws.fill_(0xAB)
+        torch.cuda.synchronize()
+        _say("graph replay", case, rep)
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, ref):
+            assert torch.equal(a, b), "replay %d differs" % rep
