@@ -149,6 +149,9 @@ __device__ inline void score_block(const Keys& kk, const int64_t (&off)[2], cons
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) acc[i][jj] = f32x16{};
     const uint8_t* qa = q_lds + r * kRowBytesLds + (lane & 31) * kHeadStrideLds + (lane >> 5) * 128;
+    // The sibling wave on this SIMD is usually in its epilogue (VALU); issuing
+    // this row's MFMAs first keeps the matrix core fed (prefill indexer -1.6%).
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(qa + ks * 16);
@@ -158,6 +161,7 @@ __device__ inline void score_block(const Keys& kk, const int64_t (&off)[2], cons
       acc[1][0] = mfma32(a0, kk.v[1][ks], acc[1][0]);
       acc[1][1] = mfma32(a1, kk.v[1][ks], acc[1][1]);
     }
+    __builtin_amdgcn_s_setprio(0);
     // Accumulator (i, lane) of a 32x32 tile holds head 8*(i/4) + 4*(lane/32) + i%4
     // and token column lane%32.
     const float* wr = w_lds + r * kHeads + 4 * (lane >> 5);
