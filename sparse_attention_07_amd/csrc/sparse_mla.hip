@@ -229,16 +229,23 @@ __device__ inline void preload_indices(int (&sv)[kIdxBatch], const int32_t* idx_
   }
 }
 
+// Per-wave slots after the tile masks in LDS: the waves' first usable slots,
+// then one flag the split merge uses.
+constexpr int kWaveSlots = 8;
+
 template <int NT = kThreads>
-__device__ inline int build_offsets(int64_t* offs, uint32_t* vmask, int* first_valid,
+__device__ inline int build_offsets(int64_t* offs, uint32_t* vmask, int* wmin,
                                     const int (&sv0)[kIdxBatch], const int32_t* idx_row,
                                     int j_begin, int j_end, int n_pad, int pos, int b,
                                     const int32_t* page_table, int pt_stride, int page_size,
                                     int num_pages, int64_t page_stride, int64_t row_stride, int tid) {
-  constexpr int kBatch = kIdxBatch;
-  if (tid == 0) *first_valid = INT32_MAX;
-  for (int i = tid; i < n_pad / kTileRows; i += NT) vmask[i] = 0u;
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  constexpr int kBatch = kIdxBatch, kW = NT / kWave;
+  static_assert(kW <= kWaveSlots, "one LDS slot per wave");
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  // The first usable slot of this wave's rows (rows grow with k and base, so
+  // the first non-empty ballot holds it).  Masks and minima come from ballots:
+  // LDS atomics from every row to one word serialised for microseconds.
+  int my_first = INT32_MAX;
   for (int base = 0; base < n_pad; base += kBatch * NT) {
     int sv[kBatch], pg[kBatch];
 #pragma unroll
@@ -256,19 +263,26 @@ __device__ inline int build_offsets(int64_t* offs, uint32_t* vmask, int* first_v
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       const int i = base + k * NT + tid;
-      if (i >= n_pad) continue;
       int64_t off = -1;
-      if (pg[k] >= 0 && pg[k] < num_pages)
+      if (i < n_pad && pg[k] >= 0 && pg[k] < num_pages)
         off = (int64_t)pg[k] * page_stride + (int64_t)(sv[k] % page_size) * row_stride;
-      offs[i] = off;
-      if (off >= 0) {
-        atomicMin(first_valid, i);
-        atomicOr(&vmask[i / kTileRows], 1u << (i % kTileRows));
+      if (i < n_pad) offs[i] = off;
+      // this wave's 64 rows start at a multiple of 64: tiles r0/32 and r0/32 + 1
+      const uint64_t m = __ballot(off >= 0);
+      const int r0 = base + k * NT + kWave * wave;
+      if (lane == 0 && r0 < n_pad) {  // n_pad is a multiple of 32: whole tiles
+        vmask[r0 / kTileRows] = (uint32_t)m;
+        if (r0 + kTileRows < n_pad) vmask[r0 / kTileRows + 1] = (uint32_t)(m >> 32);
       }
+      if (m != 0 && my_first == INT32_MAX) my_first = r0 + __ffsll((unsigned long long)m) - 1;
     }
   }
+  if (lane == 0) wmin[wave] = my_first;
   __syncthreads();
-  return *first_valid;
+  int fv = INT32_MAX;
+#pragma unroll
+  for (int w = 0; w < kW; ++w) fv = min(fv, wmin[w]);
+  return fv;
 }
 
 struct MlaArgs {
@@ -615,9 +629,9 @@ __global__ __launch_bounds__(kWideThreads, 1) void sparse_mla_wide(MlaArgs a, in
   f32x4* sbuf = reinterpret_cast<f32x4*>(smem + kWideBufs * kTileLds);  // 2 x partial scores
   int64_t* offs = reinterpret_cast<int64_t*>(smem + kWideBufs * kTileLds + 2 * kSbufWide);
   uint32_t* vmask = reinterpret_cast<uint32_t*>(offs + ntiles * kTileRows);  // usable rows per tile
-  int* first_valid = reinterpret_cast<int*>(vmask + ntiles);
+  int* wmin = reinterpret_cast<int*>(vmask + ntiles);  // kWaveSlots, then the merge's flag
 
-  const int fv = build_offsets<NT>(offs, vmask, first_valid, sv0, a.idx + (int64_t)t * a.K, j_begin, j_end,
+  const int fv = build_offsets<NT>(offs, vmask, wmin, sv0, a.idx + (int64_t)t * a.K, j_begin, j_end,
                                    ntiles * kTileRows, pos, b, a.page_table, a.pt_stride, a.page_size,
                                    a.num_pages, a.page_stride, a.row_stride, tid);
 
@@ -754,7 +768,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void sparse_mla_wide(MlaArgs a, in
     store_partials<64, kColTiles>(a, t, grp, n_groups, sp, hg * 32 + kColTiles * kh, lane, o, m_run, l_run,
                                   kh == 0 ? 16 * hg : -1);
     merge_splits_if_last<true, NT>(a, t, grp, n_groups, a.counters + (int64_t)t * n_groups + grp,
-                                   reinterpret_cast<float*>(tiles), first_valid + 1, tid);
+                                   reinterpret_cast<float*>(tiles), wmin + kWaveSlots, tid);
   }
 }
 
@@ -842,7 +856,7 @@ __global__ __launch_bounds__(kThreads, MINW) void sparse_mla_q16(MlaArgs a, int 
   f32x4* sbuf = reinterpret_cast<f32x4*>(smem + kTileLds);
   int64_t* offs = reinterpret_cast<int64_t*>(smem + kTileLds + kSbufLds);
   uint32_t* vmask = reinterpret_cast<uint32_t*>(offs + ntiles * kTileRows);
-  int* first_valid = reinterpret_cast<int*>(vmask + ntiles);
+  int* wmin = reinterpret_cast<int*>(vmask + ntiles);  // kWaveSlots, then the merge's flag
 
   // q for this wave's k half: lane (head c16, group g) holds dims 32 ks + 8 g .. +7.
   bf16x8 qreg[9];
@@ -851,7 +865,7 @@ __global__ __launch_bounds__(kThreads, MINW) void sparse_mla_q16(MlaArgs a, int 
 #pragma unroll
     for (int k = 0; k < 9; ++k) qreg[k] = *reinterpret_cast<const bf16x8*>(qp + k * 32);
   }
-  const int fv = build_offsets(offs, vmask, first_valid, sv0, a.idx + (int64_t)t * a.K, j_begin, j_end,
+  const int fv = build_offsets(offs, vmask, wmin, sv0, a.idx + (int64_t)t * a.K, j_begin, j_end,
                                ntiles * kTileRows, pos, b, a.page_table, a.pt_stride, a.page_size,
                                a.num_pages, a.page_stride, a.row_stride, tid);
 
@@ -922,7 +936,7 @@ __global__ __launch_bounds__(kThreads, MINW) void sparse_mla_q16(MlaArgs a, int 
   } else {
     store_partials<16, 8>(a, t, grp, n_groups, sp, wave * 8, lane, o, m_run, l_run, wave == 0 ? 0 : -1);
     merge_splits_if_last<false>(a, t, grp, n_groups, a.counters + (int64_t)t * n_groups + grp,
-                                reinterpret_cast<float*>(tile), first_valid + 1, tid);
+                                reinterpret_cast<float*>(tile), wmin + kWaveSlots, tid);
   }
 }
 
@@ -1025,7 +1039,7 @@ constexpr size_t kMaxLds = 160 * 1024;
 // scores, then the range's row offsets, tile masks and a flag.
 size_t mla_lds(int rps, size_t more) {
   const size_t ntiles = (size_t)(rps + kTileRows - 1) / kTileRows;
-  return kTileLds + more + ntiles * (kTileRows * 8 + 4) + 16;
+  return kTileLds + more + ntiles * (kTileRows * 8 + 4) + (kWaveSlots + 4) * sizeof(int);
 }
 
 template <typename Kernel>
