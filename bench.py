@@ -70,9 +70,9 @@ def parse():
 # counters were taken -- a changed kernel reports traffic null.
 # Copy calibration of those runs: FETCH_SIZE x 2.000, WRITE_SIZE x 1.000.
 TRAFFIC = {
-    ("decode16", "sparse_mla"): {"src": "23a72b49629aaf8a", "fetch_bytes": 1.57e+08, "write_bytes": 5.29e+06,
+    ("decode16", "sparse_mla"): {"src": "c32ab0631a36b060", "fetch_bytes": 1.57e+08, "write_bytes": 5.29e+06,
                                  "dispatches": 42},
-    ("decode16", "index_scores"): {"src": "8327363501a95fa5", "fetch_bytes": 8.101e+07, "write_bytes": 1.183e+06,
+    ("decode16", "index_scores"): {"src": "8e565c51f0c19117", "fetch_bytes": 8.101e+07, "write_bytes": 1.183e+06,
                                    "dispatches": 42},
     ("decode16", "topk"): {"src": "4e9ea48094ef7bbe", "fetch_bytes": 1.507e+06, "write_bytes": 7.552e+05,
                            "dispatches": 42},
