@@ -235,9 +235,10 @@ size_t dsa_topk_workspace_bytes(int32_t num_q_rows, int32_t max_seq_len, int32_t
  * kept (mstar PR 387 "GLM-5.2 with MLA, fp8 MoE and DSA", section "Body":
  * below index_topk the sparse pick is all tokens).  Output idx[t*k + j]:
  * selected positions in ascending order, then -1.  Only entries
- * s <= min(pos(t), ld-1) of each score row are read.  Scores must be
- * finite.
- * scores   device [T, ld] f32;  idx  device [T, k] int32
+ * s <= min(pos(t), ld-1) of each score row are used; when ld <= 32768 a
+ * row's whole storage (ld entries) may be read, before pos(t) is known.
+ * The used scores must be finite; the others may hold anything.
+ * scores   device [T, ld] f32 (all T*ld entries allocated);  idx  device [T, k] int32
  * ws       device workspace of dsa_topk_workspace_bytes() bytes (may be NULL when
  *          0; DSA_ERR_WORKSPACE when smaller).  Rows longer than 32768 entries
  *          are then selected in two levels: the exact top-k of each 32768-entry

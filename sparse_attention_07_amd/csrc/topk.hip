@@ -22,11 +22,12 @@ constexpr int kCache = 32768;
 
 // Top-K of row[0, n): emit(o, s) for the o-th selected position s, o < K, in
 // ascending s.
-template <bool Cached, typename Emit>
+template <bool Cached, bool PRE, typename Emit>
 __device__ inline void select_emit(const float* __restrict__ row, int n, int K, uint32_t* cache,
-                                   uint32_t* hist, uint32_t* wcount, uint32_t* pick, Emit emit) {
+                                   uint32_t* hist, uint32_t* wcount, uint32_t* pick, Emit emit,
+                                   const f32x4* pre = nullptr) {
   const bool vec = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
-  const topk::Threshold th = topk::select<kThreads, Cached>(row, vec, n, K, cache, hist, pick);
+  const topk::Threshold th = topk::select<kThreads, Cached, PRE>(row, vec, n, K, cache, hist, pick, pre);
   auto emit_k = [emit, K](uint32_t o, int s) {
     if (o < (uint32_t)K) emit(o, s);
   };
@@ -34,10 +35,11 @@ __device__ inline void select_emit(const float* __restrict__ row, int n, int K, 
   else topk::compact<kThreads, Cached>(row, vec, n, cache, th, wcount, emit_k);
 }
 
-template <bool Cached>
+template <bool Cached, bool PRE = false>
 __device__ inline void select_row(const float* __restrict__ row, int n, int K, int32_t* __restrict__ out,
-                                  uint32_t* cache, uint32_t* hist, uint32_t* wcount, uint32_t* pick) {
-  select_emit<Cached>(row, n, K, cache, hist, wcount, pick, [out](uint32_t o, int s) { out[o] = s; });
+                                  uint32_t* cache, uint32_t* hist, uint32_t* wcount, uint32_t* pick,
+                                  const f32x4* pre = nullptr) {
+  select_emit<Cached, PRE>(row, n, K, cache, hist, wcount, pick, [out](uint32_t o, int s) { out[o] = s; }, pre);
 }
 
 __global__ __launch_bounds__(kThreads) void topk_radix(const int32_t* __restrict__ cu_q,
@@ -45,13 +47,41 @@ __global__ __launch_bounds__(kThreads) void topk_radix(const int32_t* __restrict
                                                        const float* __restrict__ scores, int64_t ld,
                                                        int K, int32_t* __restrict__ idx, int row_lo) {
   __shared__ __align__(16) uint32_t cache[kCache];
-  __shared__ __align__(16) uint32_t hist[2 * topk::kHistWords];
+  __shared__ __align__(16) uint32_t hist[topk::kHistLdsWords];
   __shared__ uint32_t wcount[2 * kThreads / kWave];
   __shared__ uint32_t pick[3];
 
   const int t = row_lo + (int)blockIdx.x;  // score row t - row_lo, index row t
   const int tid = threadIdx.x;
-  const RowLoc loc = locate_row(cu_q, seq_lens, B, t);
+  const float* row = scores + (int64_t)(t - row_lo) * ld;
+  // Rows whose storage fits the cache are read in one round, issued before
+  // the lookup that gives the row's length.
+  const bool early = ld <= kCache;
+  // The lookup's first round (requests 0 .. 255, as in locate_row) is
+  // written out here so that the row read goes out between its loads and
+  // its search; later rounds are left to locate_row.
+  const int lane = tid & (kWave - 1);
+  int lo[4], hi[4], sl[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int i = min(c * kWave + lane, B - 1);  // B >= 1: this row exists
+    lo[c] = cu_q[i];
+    hi[c] = cu_q[i + 1];
+    sl[c] = seq_lens[i];
+  }
+  f32x4 pre[topk::kReadBatch];
+  if (early) topk::read_first_round<kThreads>(row, (reinterpret_cast<uintptr_t>(row) & 15) == 0, (int)ld, pre);
+  RowLoc loc{-1, 0};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint64_t m = __ballot(c * kWave + lane < B && lo[c] <= t && t < hi[c]);
+    if (m != 0 && loc.b < 0) {
+      const int src = __ffsll((unsigned long long)m) - 1;
+      const int q0 = __shfl(lo[c], src), q1 = __shfl(hi[c], src), s = __shfl(sl[c], src);
+      loc = RowLoc{c * kWave + src, s - (q1 - q0) + (t - q0)};
+    }
+  }
+  if (loc.b < 0) loc = locate_row(cu_q, seq_lens, B, t);
   const int n = (int)max<int64_t>(0, min<int64_t>((int64_t)loc.pos + 1, ld));
   int32_t* out = idx + (int64_t)t * K;
 
@@ -59,8 +89,8 @@ __global__ __launch_bounds__(kThreads) void topk_radix(const int32_t* __restrict
     for (int j = tid; j < K; j += kThreads) out[j] = j < n ? j : -1;
     return;
   }
-  const float* row = scores + (int64_t)(t - row_lo) * ld;
-  if (n <= kCache) select_row<true>(row, n, K, out, cache, hist, wcount, pick);
+  if (early) select_row<true, true>(row, n, K, out, cache, hist, wcount, pick, pre);
+  else if (n <= kCache) select_row<true>(row, n, K, out, cache, hist, wcount, pick);
   else select_row<false>(row, n, K, out, cache, hist, wcount, pick);
 }
 
@@ -83,7 +113,7 @@ __global__ __launch_bounds__(kThreads) void topk_segments(const int32_t* __restr
                                                           int K, int row_lo, int segs, float* __restrict__ cand_sc,
                                                           int32_t* __restrict__ cand_ix) {
   __shared__ __align__(16) uint32_t cache[kSegLen];
-  __shared__ __align__(16) uint32_t hist[2 * topk::kHistWords];
+  __shared__ __align__(16) uint32_t hist[topk::kHistLdsWords];
   __shared__ uint32_t wcount[2 * kThreads / kWave];
   __shared__ uint32_t pick[3];
 
@@ -102,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void topk_segments(const int32_t* __restr
     }
     return;
   }
-  select_emit<true>(row, len, K, cache, hist, wcount, pick, [=](uint32_t o, int s) {
+  select_emit<true, false>(row, len, K, cache, hist, wcount, pick, [=](uint32_t o, int s) {
     cand_ix[base + o] = s0 + s;
     cand_sc[base + o] = row[s];
   });
@@ -114,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void topk_merge(const int32_t* __restrict
                                                        const float* __restrict__ cand_sc,
                                                        const int32_t* __restrict__ cand_ix) {
   __shared__ __align__(16) uint32_t cache[kCache];
-  __shared__ __align__(16) uint32_t hist[2 * topk::kHistWords];
+  __shared__ __align__(16) uint32_t hist[topk::kHistLdsWords];
   __shared__ uint32_t wcount[2 * kThreads / kWave];
   __shared__ uint32_t pick[3];
 
@@ -131,8 +161,8 @@ __global__ __launch_bounds__(kThreads) void topk_merge(const int32_t* __restrict
   const float* row = cand_sc + (int64_t)(t - row_lo) * n2;
   const int32_t* ix = cand_ix + (int64_t)(t - row_lo) * n2;
   auto emit = [out, ix](uint32_t o, int s) { out[o] = ix[s]; };
-  if (n2 <= kCache) select_emit<true>(row, n2, K, cache, hist, wcount, pick, emit);
-  else select_emit<false>(row, n2, K, cache, hist, wcount, pick, emit);
+  if (n2 <= kCache) select_emit<true, false>(row, n2, K, cache, hist, wcount, pick, emit);
+  else select_emit<false, false>(row, n2, K, cache, hist, wcount, pick, emit);
 }
 
 }  // namespace

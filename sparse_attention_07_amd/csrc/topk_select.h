@@ -27,6 +27,14 @@ namespace topk {
 
 constexpr int kBins = 2048;
 constexpr int kHistWords = kBins + kBins / 32 * 4;  // four pad words per 32 bins
+// LDS histogram area: pass 0 counts into two copies (even and odd lanes; the
+// second starts 16 banks further on), pass 1 into a third histogram, pass 2
+// into the first copy again.  Scores crowd into a few of pass 0's bins, and
+// LDS atomics of one instruction that hit one address or bank serialise:
+// two copies halve the worst collisions.
+constexpr int kHistCopy1 = kHistWords + 16;
+constexpr int kHistPass1 = 2 * kHistWords + 16;
+constexpr int kHistLdsWords = 3 * kHistWords + 16;
 
 __device__ inline uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -48,17 +56,23 @@ __device__ inline uint32_t wave_sum(uint32_t x) {
 // bin containing the need-th largest element; writes (bin, need left inside
 // the bin, bin count) to pick[0..2].  Lane l owns the PER bins
 // NB-PER*(l+1) .. NB-1-PER*l.  The histogram's total must be >= need.
-template <int NB>
-__device__ inline void pick_bin(const uint32_t* hist, uint32_t need, uint32_t* pick) {
+template <int NB, bool TWO = false>
+__device__ inline void pick_bin(const uint32_t* hist, uint32_t need, uint32_t* pick,
+                                const uint32_t* hist2 = nullptr) {
   constexpr int kPer = NB / kWave;  // 32 or 16
   const int lane = threadIdx.x & (kWave - 1);
   const int lo = NB - kPer * (lane + 1);
   const u32x4* p = reinterpret_cast<const u32x4*>(hist + hslot((uint32_t)lo));
+  const u32x4* p2 = reinterpret_cast<const u32x4*>(hist2 + hslot((uint32_t)lo));
   uint32_t sum = 0;
 #pragma unroll
   for (int j = 0; j < kPer / 4; ++j) {
     const u32x4 v = p[j];
     sum += v[0] + v[1] + v[2] + v[3];
+    if (TWO) {
+      const u32x4 v2 = p2[j];
+      sum += v2[0] + v2[1] + v2[2] + v2[3];
+    }
   }
   const uint32_t inc = wave_incl_scan(sum);
   // The one lane whose range holds the need-th element hands it to the wave,
@@ -67,7 +81,8 @@ __device__ inline void pick_bin(const uint32_t* hist, uint32_t need, uint32_t* p
   const int src = __builtin_ctzll(owner);
   const int top_s = __builtin_amdgcn_readlane(lo + kPer - 1, src);
   const uint32_t acc = (uint32_t)__builtin_amdgcn_readlane((int)(inc - sum), src);
-  const uint32_t c = lane < kPer ? hist[hslot((uint32_t)(top_s - lane))] : 0u;
+  uint32_t c = lane < kPer ? hist[hslot((uint32_t)(top_s - lane))] : 0u;
+  if (TWO && lane < kPer) c += hist2[hslot((uint32_t)(top_s - lane))];
   const uint32_t before = acc + wave_incl_scan(c) - c;
   if (lane < kPer && before < need && need <= before + c) {
     pick[0] = (uint32_t)(top_s - lane);
@@ -102,25 +117,48 @@ struct Threshold {
 };
 
 // Threshold of the k best of the n > k scores row[0] .. row[n-1], for a
-// workgroup of NT threads.  hist: 2 * kHistWords LDS words, 16-byte aligned;
+// workgroup of NT threads.  hist: kHistLdsWords LDS words, 16-byte aligned;
 // pick: 3 LDS words; cache (Cached only): round_up(n, 4) LDS words,
 // 16-byte aligned.  Begins and ends with a barrier.
-template <int NT, bool Cached>
+// Quads in flight per thread while a row is read: one round of them covers
+// NT * kReadBatch * 4 positions.
+constexpr int kReadBatch = 8;
+
+// The first round of a row's quads, read up to `bound` positions (the row's
+// storage): issued before the row's length is known, so that the read
+// overlaps the request lookup.  Positions at or past the length are never
+// used.
+template <int NT>
+__device__ inline void read_first_round(const float* __restrict__ row, bool vec, int bound,
+                                        f32x4 (&v)[kReadBatch]) {
+  const int nq = (bound + 3) >> 2;
+#pragma unroll
+  for (int i = 0; i < kReadBatch; ++i) {
+    const int q = i * NT + threadIdx.x;
+    if (q < nq) v[i] = load_quad(row, q, bound, vec);
+  }
+}
+
+// pre (PRE only): the first round, from read_first_round with a bound >= n.
+template <int NT, bool Cached, bool PRE = false>
 __device__ inline Threshold select(const float* __restrict__ row, bool vec, int n, int k,
-                                   uint32_t* cache, uint32_t* hist, uint32_t* pick) {
-  constexpr int kBatch = 8;  // quads in flight per thread
+                                   uint32_t* cache, uint32_t* hist, uint32_t* pick,
+                                   const f32x4* pre = nullptr) {
+  constexpr int kBatch = kReadBatch;
   const int tid = threadIdx.x, wave = tid / kWave;
   const int nq = (n + 3) >> 2;
   u32x4* cache4 = reinterpret_cast<u32x4*>(cache);
-  for (int i = tid; i < 2 * kHistWords; i += NT) hist[i] = 0u;
+  for (int i = tid; i < kHistLdsWords; i += NT) hist[i] = 0u;
   __syncthreads();
+  uint32_t* h0 = hist + ((tid & 1) ? kHistCopy1 : 0);
   // Pass 0 (key bits 21..31) while the row is read.
   for (int q0 = 0; q0 < nq; q0 += kBatch * NT) {
     f32x4 v[kBatch];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const int q = q0 + i * NT + tid;
-      if (q < nq) v[i] = load_quad(row, q, n, vec);
+      if (PRE && q0 == 0) v[i] = pre[i];
+      else if (q < nq) v[i] = load_quad(row, q, n, vec);
     }
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
@@ -130,12 +168,12 @@ __device__ inline Threshold select(const float* __restrict__ row, bool vec, int 
         if (Cached) cache4[q] = u;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          if (4 * q + j < n) atomicAdd(&hist[hslot(u[j] >> 21)], 1u);
+          if (4 * q + j < n) atomicAdd(&h0[hslot(u[j] >> 21)], 1u);
       }
     }
   }
   __syncthreads();
-  if (wave == 0) pick_bin<kBins>(hist, (uint32_t)k, pick);
+  if (wave == 0) pick_bin<kBins, true>(hist, (uint32_t)k, pick, hist + kHistCopy1);
   __syncthreads();
   Threshold th{pick[0] << 21, 0xFFE00000u, pick[1]};
   bool done = pick[2] == th.need;  // the whole bin is taken
@@ -144,8 +182,8 @@ __device__ inline Threshold select(const float* __restrict__ row, bool vec, int 
   for (int pass = 1; pass < 3 && !done; ++pass) {
     const int shift = pass == 1 ? 10 : 0;
     const uint32_t bmask = pass == 1 ? 2047u : 1023u;
-    uint32_t* h = hist + (pass & 1) * kHistWords;
-    if (pass == 1)  // pass 0's histogram was read before the last barrier; pass 2 reuses it
+    uint32_t* h = pass == 1 ? hist + kHistPass1 : hist;
+    if (pass == 1)  // pass 0's histograms were read before the last barrier; pass 2 reuses the first
       for (int i = tid; i < kHistWords; i += NT) hist[i] = 0u;
     for (int q0 = 0; q0 < nq; q0 += kBatch * NT) {
       u32x4 u[kBatch];
