@@ -174,6 +174,35 @@ def test_topk_ties_and_lengths(K):
     _parity.check_idx_exact(idx, ref)
 
 
+@pytest.mark.parametrize("K", [5, 2048])
+def test_topk_rows_read_before_their_length_is_known(K):
+    # ld <= 32768: each row's whole storage is read before its length is known;
+    # entries past the length hold NaN and +-inf here and must not matter.
+    from sparse_attention_07_amd import dsa
+    g = torch.Generator().manual_seed(100 + K)
+    lens = [1, K, K + 1, 3 * K + 5, 1000, 4097, 20000, 32767, 32768]
+    ld = 32768
+    scores = torch.full((len(lens), ld), float("nan"))
+    scores[:, 1::7] = float("inf")
+    scores[:, 2::7] = -float("inf")
+    rows = []
+    for i, n in enumerate(lens):
+        r = (torch.randint(-3, 4, (n,), generator=g).float() / 2 if i % 2 else
+             torch.randint(-1000, 1000, (n,), generator=g).float() / 64)
+        scores[i, :n] = r
+        rows.append(r)
+    sb = _row_batch(rows, K)
+    ref = oracle.topk(sb, np.where(np.isfinite(scores.numpy()), scores.numpy(), 0.0).astype(np.float64), k=K)
+    _say("topk early read K=%d" % K)
+    b = dsa.make_batch(sb.cu_q.to(DEV), sb.seq_lens_t.to(DEV), sb.page_table.to(DEV), len(rows), 1,
+                       ld, 16, 1)
+    idx = torch.full((len(rows), K), 12345, dtype=torch.int32, device=DEV)
+    assert dsa.dsa_topk_workspace_bytes(len(rows), ld, K) == 0   # single level
+    dsa.dsa_topk(b, scores.to(DEV), ld, K, idx, None, 0)
+    torch.cuda.synchronize()
+    _parity.check_idx_exact(idx, ref)
+
+
 def test_mla_invalid_entries_and_closed_forms():
     from sparse_attention_07_amd import dsa
     from sparse_attention_07_amd.path import DSAPath
