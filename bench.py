@@ -74,7 +74,7 @@ TRAFFIC = {
                                  "dispatches": 42},
     ("decode16", "index_scores"): {"src": "8e565c51f0c19117", "fetch_bytes": 8.101e+07, "write_bytes": 1.183e+06,
                                    "dispatches": 42},
-    ("decode16", "topk"): {"src": "4e9ea48094ef7bbe", "fetch_bytes": 1.507e+06, "write_bytes": 7.552e+05,
+    ("decode16", "topk"): {"src": "f7f73c217c273b0f", "fetch_bytes": 2.378e+06, "write_bytes": 5.243e+05,
                            "dispatches": 42},
 }
 KERNEL_SOURCES = {"sparse_mla": ["sparse_mla.hip", "dsa_device.h"],
