@@ -130,6 +130,8 @@ constexpr int kLoadsPerStep = KFP8 ? 10 : 16;
 // page offsets off, -1 when unmapped) against the nr staged query rows; row r
 // sits at position pos_first + r (clamped to ld_last) and its output row is
 // row0 + r.
+constexpr int kMaxUnitRows = 8;  // query rows scored against one key block
+
 // max(x, 0) as a signed-integer max of the bit pattern: a negative float is a
 // negative integer (and -0 gives +0).  One v_max_i32, where fmaxf on an MFMA
 // result also costs a NaN-quieting v_max_f32 first.
@@ -140,7 +142,12 @@ __device__ inline void score_block(const Keys& kk, const int64_t (&off)[2], cons
                                    const float* w_lds, int nr, int s_base, int pos_first,
                                    int64_t ld_last, float* __restrict__ scores, int64_t row0,
                                    int64_t ld, int lane, const float* ksc = nullptr) {
-  for (int r = 0; r < nr; ++r) {
+  // Unrolled over the at most kMaxUnitRows rows: as a loop with score stores
+  // and no loads, the compiler would wait for every load in flight (the next
+  // block's keys included) before entering it.
+#pragma unroll
+  for (int r = 0; r < kMaxUnitRows; ++r) {
+    if (r >= nr) break;
     const int pos_r = (int)min<int64_t>((int64_t)pos_first + r, ld_last);
     if (s_base > pos_r) continue;
     f32x16 acc[2][2];
@@ -301,19 +308,43 @@ __global__ __launch_bounds__(kThreads, 2) void index_scores_bf16_mfma(
 constexpr int kFlatWaves = 8;
 constexpr int kFlatThreads = kFlatWaves * kWave;
 
-// Page offsets of the two 32-token halves a lane reads in block `blk` of
-// request b (-1 past pos_last or when unmapped).
-__device__ inline void block_offsets(int64_t (&off)[2], int blk_tok0, int pos_last,
-                                     const int32_t* __restrict__ page_table, int pt_stride,
-                                     int page_size, int num_pages, int b, int64_t page_stride,
+// A lane's two tokens in a block: s = blk_tok0 + 32 nt + lane % 32.  Their
+// page ids are loaded unconditionally (the table index is clamped to the
+// request's row, so every load is in bounds) and only checked when the
+// offsets are formed: no branch depends on a load, so the loads can stay in
+// flight while the wave does other work.  Vector loads complete in issue
+// order, so a wave sends a block's page ids before the keys of the block
+// ahead of it; forming that block's offsets then never waits on keys.
+__device__ inline void block_pages(int (&pid)[2], int blk_tok0, const int32_t* __restrict__ page_table,
+                                   int pt_stride, int page_size, int b, int lane) {
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int s = blk_tok0 + nt * 32 + (lane & 31);
+    pid[nt] = page_table[(int64_t)b * pt_stride + min(s / page_size, pt_stride - 1)];
+  }
+}
+
+// Offsets of those tokens from their page ids, as token_offset gives them
+// (-1 past pos_last, past the table row, or for a page id outside the pool).
+__device__ inline void block_offsets(int64_t (&off)[2], const int (&pid)[2], int blk_tok0, int pos_last,
+                                     int pt_stride, int page_size, int num_pages, int64_t page_stride,
                                      int64_t row_stride, int lane) {
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int s = blk_tok0 + nt * 32 + (lane & 31);
-    off[nt] = s <= pos_last ? token_offset(page_table, pt_stride, page_size, num_pages, b, s,
-                                           page_stride, row_stride)
-                            : -1;
+    const int lp = s / page_size;
+    const bool ok = s <= pos_last && lp < pt_stride && pid[nt] >= 0 && pid[nt] < num_pages;
+    off[nt] = ok ? (int64_t)pid[nt] * page_stride + (int64_t)(s - lp * page_size) * row_stride : -1;
   }
+}
+
+// s_waitcnt vmcnt(n) through the builtin, so that the compiler's own wait
+// tracking sees it (an inline-asm wait is opaque to it).  gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt (6:4) and lgkmcnt (11:8) at their maxima.
+template <int N>
+__device__ inline void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 // Last request b in [0, B) whose first block is at or below blk (the owner of
@@ -330,22 +361,42 @@ __device__ inline int last_at_or_below(const int* pre, int B, int blk) {
 
 struct FlatBlock {
   int u, tok;       // unit and its first token of the block
-  int64_t off[2];   // page offsets of this lane's two tokens
+  int pid[2];       // page ids of this lane's two tokens (loads possibly in flight)
+  int64_t off[2];   // their offsets, once formed
 };
 
-// Unit and page offsets of block blk, walking forward from unit u_from.
-__device__ inline void prep_block(FlatBlock& x, int blk, int u_from, const int* pre, const int* unr,
-                                  const int* upf, const int* ub, int64_t ld_last,
-                                  const int32_t* __restrict__ page_table, int pt_stride,
-                                  int page_size, int num_pages, int64_t page_stride,
-                                  int64_t row_stride, int lane) {
+// Unit and page-id loads of block blk, walking forward from unit u_from.
+__device__ inline void prep_pages(FlatBlock& x, int blk, int u_from, const int* pre, const int* ub,
+                                  const int32_t* __restrict__ page_table, int pt_stride, int page_size,
+                                  int lane) {
   int u = u_from;
   while (pre[u + 1] <= blk) ++u;
   x.u = u;
   x.tok = (blk - pre[u]) * kKeysPerStep;
-  const int pos_last = (int)min<int64_t>((int64_t)upf[u] + unr[u] - 1, ld_last);
-  block_offsets(x.off, x.tok, pos_last, page_table, pt_stride, page_size, num_pages, ub[u], page_stride,
-                row_stride, lane);
+  block_pages(x.pid, x.tok, page_table, pt_stride, page_size, ub[u], lane);
+}
+
+// prep_pages, or for a block past the wave's range the same two loads of
+// table entries that exist (request 0): every path issues the same loads, so
+// the compiler's wait counts stay exact.
+__device__ inline void prep_pages_or_none(FlatBlock& x, bool valid, int blk, int u_from, const int* pre,
+                                          const int* ub, const int32_t* __restrict__ page_table,
+                                          int pt_stride, int page_size, int lane) {
+  if (valid) {
+    prep_pages(x, blk, u_from, pre, ub, page_table, pt_stride, page_size, lane);
+  } else {
+    x.u = u_from;
+    x.tok = 0;
+    block_pages(x.pid, 0, page_table, pt_stride, page_size, 0, lane);
+  }
+}
+
+// Offsets of block x from its page ids (waits for those loads only).
+__device__ inline void finish_block(FlatBlock& x, const int* unr, const int* upf, int64_t ld_last,
+                                     int pt_stride, int page_size, int num_pages, int64_t page_stride,
+                                     int64_t row_stride, int lane) {
+  const int pos_last = (int)min<int64_t>((int64_t)upf[x.u] + unr[x.u] - 1, ld_last);
+  block_offsets(x.off, x.pid, x.tok, pos_last, pt_stride, page_size, num_pages, page_stride, row_stride, lane);
 }
 
 // Block exclusive scan over the workgroup of one int per thread (carry added);
@@ -461,18 +512,21 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
     const int hi = all_staged ? end : min(end, pre[u0 + 1]);
     const int u_hi = all_staged ? u_last : u0;
     // This wave's blocks lo + wave + 8 i < hi.  A, B, C: the block being scored
-    // and the next two (keys of B in flight, page lookups of C in flight).  The
-    // first two blocks' page lookups and A's keys go out before the staging
-    // copies, so waiting for them does not also wait for the copies.
+    // and the next two (keys of B in flight, page ids of C in flight).  The
+    // first three blocks' page ids go out together; then A's keys, the
+    // staging copies and B's keys.
     int j = lo + wave;
-    FlatBlock A{u0, 0, {-1, -1}}, Bk{u0, 0, {-1, -1}}, C{u0, 0, {-1, -1}};
-    if (j < hi) prep_block(A, j, u0, pre, unr, upf, ub, ld_last, page_table, pt_stride, page_size,
-                           num_pages, k_page_stride, k_row_stride, lane);
+    FlatBlock A{u0, 0, {0, 0}, {-1, -1}}, Bk = A, C = A;
+    prep_pages_or_none(A, j < hi, j, u0, pre, ub, page_table, pt_stride, page_size, lane);
+    prep_pages_or_none(Bk, j + kFlatWaves < hi, j + kFlatWaves, A.u, pre, ub, page_table, pt_stride,
+                       page_size, lane);
+    prep_pages_or_none(C, j + 2 * kFlatWaves < hi, j + 2 * kFlatWaves, Bk.u, pre, ub, page_table, pt_stride,
+                       page_size, lane);
+#define DSA_FINISH(X) \
+  finish_block(X, unr, upf, ld_last, pt_stride, page_size, num_pages, k_page_stride, k_row_stride, lane)
+    if (j < hi) DSA_FINISH(A);
     KeyRegs<KFP8> k0, k1;
     load_keys(k0, A.off, k_base, lane, A.tok, page_size, k_row_stride);
-    if (j + kFlatWaves < hi)
-      prep_block(Bk, j + kFlatWaves, A.u, pre, unr, upf, ub, ld_last, page_table, pt_stride,
-                 page_size, num_pages, k_page_stride, k_row_stride, lane);
     for (int uu = u0; uu <= u_hi; ++uu) {  // query rows and weights -> LDS slot uu - u0
       const int q0 = uq0[uu], nr = unr[uu];
       uint8_t* qd = q_area + (size_t)(uu - u0) * rg * kRowBytesLds;
@@ -491,47 +545,54 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
         if (base + tid < nr * (kHeads / 4)) copy16_to_lds(wsrc + (base + tid) * 16, wd + (base + wave * kWave) * 16);
     }
 
-    // B's keys go out after the copies: the wait below covers the copies (and
-    // everything issued before them) but not B's 16 key loads.
-    const bool has_b = j + kFlatWaves < hi;
-    if (has_b) {
-      load_keys(k1, Bk.off, k_base, lane, Bk.tok, page_size, k_row_stride);
-      if (KFP8) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-      static_assert(kLoadsPerStep<KFP8> == (KFP8 ? 10 : 16), "vmcnt above");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
+    // B's keys (or, past the range, a harmless read at pool offset 0) go out
+    // after the copies on every path, then everything but them is waited
+    // for: A's keys, the page ids and the copies.
+    if (j + kFlatWaves < hi) DSA_FINISH(Bk);
+    load_keys(k1, Bk.off, k_base, lane, Bk.tok, page_size, k_row_stride);
+    wait_vm<kLoadsPerStep<KFP8>>();
     lds_barrier();
 
 #define DSA_SCORE(KK, X)                                                                           \
   score_keys(KK, X.off, q_area + (size_t)(X.u - u0) * rg * kRowBytesLds,                          \
               w_area + (size_t)(X.u - u0) * rg * kHeads, unr[X.u], X.tok, upf[X.u], ld_last, scores, \
               (int64_t)uq0[X.u] - row_lo, ld, lane)
-    while (j < hi) {
-      // block j with k0 (loaded), block j + 8 with k1 (in flight)
-      const bool has1 = j + kFlatWaves < hi;
-      if (j + 2 * kFlatWaves < hi)
-        prep_block(C, j + 2 * kFlatWaves, Bk.u, pre, unr, upf, ub, ld_last, page_table, pt_stride,
-                   page_size, num_pages, k_page_stride, k_row_stride, lane);
+    // Each step issues the page ids two blocks ahead, then the keys one block
+    // ahead (into the registers just scored), whether or not those blocks
+    // exist, so the compiler's waits before scoring cover exactly the block
+    // being scored.  The empty asm statements pin the issue order: page ids,
+    // then keys, then the next block's scoring.
+    while (true) {
+      // block j: keys in k0; block j + 8: keys in k1 (in flight); block j + 16: page ids in flight
+      wait_vm<kLoadsPerStep<KFP8>>();  // all but the newest block's keys
       DSA_SCORE(k0, A);
-      if (!has1) break;
+      if (j + kFlatWaves >= hi) break;
       j += kFlatWaves;
       A = Bk;
       Bk = C;
-      const bool has1b = j + kFlatWaves < hi;
-      if (has1b) load_keys(k0, Bk.off, k_base, lane, Bk.tok, page_size, k_row_stride);
-      if (j + 2 * kFlatWaves < hi)
-        prep_block(C, j + 2 * kFlatWaves, Bk.u, pre, unr, upf, ub, ld_last, page_table, pt_stride,
-                   page_size, num_pages, k_page_stride, k_row_stride, lane);
+      prep_pages_or_none(C, j + 2 * kFlatWaves < hi, j + 2 * kFlatWaves, Bk.u, pre, ub, page_table,
+                         pt_stride, page_size, lane);
+      asm volatile("" ::: "memory");
+      if (j + kFlatWaves < hi) DSA_FINISH(Bk);
+      else Bk.off[0] = Bk.off[1] = -1;
+      load_keys(k0, Bk.off, k_base, lane, Bk.tok, page_size, k_row_stride);
+      asm volatile("" ::: "memory");
+      wait_vm<kLoadsPerStep<KFP8>>();
       DSA_SCORE(k1, A);
-      if (!has1b) break;
+      if (j + kFlatWaves >= hi) break;
       j += kFlatWaves;
       A = Bk;
       Bk = C;
-      if (j + kFlatWaves < hi) load_keys(k1, Bk.off, k_base, lane, Bk.tok, page_size, k_row_stride);
+      prep_pages_or_none(C, j + 2 * kFlatWaves < hi, j + 2 * kFlatWaves, Bk.u, pre, ub, page_table,
+                         pt_stride, page_size, lane);
+      asm volatile("" ::: "memory");
+      if (j + kFlatWaves < hi) DSA_FINISH(Bk);
+      else Bk.off[0] = Bk.off[1] = -1;
+      load_keys(k1, Bk.off, k_base, lane, Bk.tok, page_size, k_row_stride);
+      asm volatile("" ::: "memory");
     }
 #undef DSA_SCORE
+#undef DSA_FINISH
     lds_barrier();  // every wave is done with the staged rows
     lo = hi;
     if (lo < end) u0 = last_at_or_below(pre, n_units, lo);
