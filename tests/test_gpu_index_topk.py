@@ -85,3 +85,41 @@ def test_long_context_one_row_per_chunk():
     ref = oracle.topk(sb, oracle.index_scores(sb))
     _parity.check_idx_exact(idx, ref)
     assert np.all((idx.cpu().numpy() >= 0).sum(1) == 2048)
+
+
+@pytest.mark.parametrize("key_fmt", [None, synth.FMT_FP8_E4M3_B128])
+def test_scores_skip_unmapped_and_out_of_range_pages(key_fmt):
+    # Page ids are loaded without a branch and checked when the offsets are
+    # formed: a page id of -1 or past the pool leaves its tokens' scores
+    # unwritten, and every other score equals the oracle's (computed on the
+    # intact table).
+    from sparse_attention_07_amd.path import DSAPath
+    kw = dict(batch=5, ctx=(700, 3000), topk=512)
+    if key_fmt is not None:
+        kw["key_fmt"] = key_fmt
+    sb = synth.make_batch(1 if key_fmt is None else 4, device=DEV, layers=0, **kw)
+    ref = oracle.index_scores(sb)
+    P = sb.cfg.page_size
+    bad = {(0, 1): -1, (2, 3): sb.num_pages + 7, (4, 0): -5}   # (request, logical page) -> page id
+    pt = sb.page_table.clone()
+    for (b, lp), pid in bad.items():
+        assert lp * P < sb.seq_lens[b]
+        sb.page_table[b, lp] = pid
+    p = DSAPath(sb)
+    p.scores.fill_(float("nan"))
+    p.index_scores()
+    torch.cuda.synchronize()
+    got = p.scores.cpu().numpy().astype(np.float64)
+    cu = sb.cu_q.tolist()
+    for b in range(len(cu) - 1):
+        for t in range(cu[b], cu[b + 1]):
+            pos = sb.seq_lens[b] - (cu[b + 1] - cu[b]) + (t - cu[b])
+            skipped = np.zeros(got.shape[1], dtype=bool)
+            for (bb, lp), _ in bad.items():
+                if bb == b:
+                    skipped[lp * P:(lp + 1) * P] = True
+            s = np.arange(pos + 1)
+            keep = s[~skipped[:pos + 1]]
+            assert np.all(np.isnan(got[t, s[skipped[:pos + 1]]])), "row %d: a skipped page was written" % t
+            np.testing.assert_array_equal(got[t, keep], ref[t, keep].astype(np.float32).astype(np.float64))
+    sb.page_table.copy_(pt)
