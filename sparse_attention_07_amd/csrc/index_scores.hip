@@ -562,11 +562,13 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
     // exist, so the compiler's waits before scoring cover exactly the block
     // being scored.  The empty asm statements pin the issue order: page ids,
     // then keys, then the next block's scoring.
-    while (true) {
-      // block j: keys in k0; block j + 8: keys in k1 (in flight); block j + 16: page ids in flight
-      wait_vm<kLoadsPerStep<KFP8>>();  // all but the newest block's keys
-      DSA_SCORE(k0, A);
-      if (j + kFlatWaves >= hi) break;
+    // block j: keys in k0; block j + 8: keys in k1 (in flight); block j + 16:
+    // page ids in flight.  The first block is scored before the loop, whose
+    // steps each issue loads and then score: every scoring then follows its
+    // own wait on the same path.
+    wait_vm<kLoadsPerStep<KFP8>>();  // all but the newest block's keys
+    DSA_SCORE(k0, A);
+    while (j + kFlatWaves < hi) {
       j += kFlatWaves;
       A = Bk;
       Bk = C;
@@ -590,6 +592,8 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
       else Bk.off[0] = Bk.off[1] = -1;
       load_keys(k1, Bk.off, k_base, lane, Bk.tok, page_size, k_row_stride);
       asm volatile("" ::: "memory");
+      wait_vm<kLoadsPerStep<KFP8>>();
+      DSA_SCORE(k0, A);
     }
 #undef DSA_SCORE
 #undef DSA_FINISH
