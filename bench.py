@@ -72,7 +72,7 @@ def parse():
 TRAFFIC = {
     ("decode16", "sparse_mla"): {"src": "c32ab0631a36b060", "fetch_bytes": 1.57e+08, "write_bytes": 5.29e+06,
                                  "dispatches": 42},
-    ("decode16", "index_scores"): {"src": "b857ca39f9c4252e", "fetch_bytes": 8.141e+07, "write_bytes": 1.183e+06,
+    ("decode16", "index_scores"): {"src": "77689ed026855257", "fetch_bytes": 8.149e+07, "write_bytes": 1.183e+06,
                                    "dispatches": 42},
     ("decode16", "topk"): {"src": "f7f73c217c273b0f", "fetch_bytes": 2.378e+06, "write_bytes": 5.243e+05,
                            "dispatches": 42},
