@@ -6,16 +6,22 @@ where the workload has them).  Inputs are seeded synthetic tensors already
 resident in HBM; several independent input sets are rotated so the 256 MB
 MALL cannot serve repeat reads.
 
-Default workload: 64 decode requests, contexts U[1024, 8192], one query each,
-index_topk 2048, indexer 64 x 128 bf16, sparse MLA with 16 heads over a
-512+64 bf16 paged latent cache (page size 64, random page tables).
-`--config N` benchmarks another workload of the same family instead.
+Default workload (decode128): 256 decode requests, contexts U[2048, 32768],
+one query each, index_topk 2048, indexer 64 x 128 bf16, sparse MLA with all
+128 heads over a 512+64 bf16 paged latent cache (page size 64, random page
+tables), one full layer followed by two IndexShare layers that reuse its
+indices -- batch-256 steady decode, the largest decode workload that runs on
+one GPU.  `--config N` benchmarks another workload of the same family
+instead (1: the 16-head per-GPU share of tensor-parallel decode, 3: a
+chunked prefill, 4: long-context fp8 MTP decode).
 
 Prints one JSON line.  `value` is query rows through the whole path per
 second; `roofline` reports the dominant kernel against MI355X's HBM (8 TB/s)
 or dense bf16 MFMA (2.5 PFLOP/s) peak, with its average duration taken from
 HIP events on the launch stream inside the timed region; `cpu_baseline` is
-the CPU oracle on a bounded sample of the same workload.
+the CPU oracle on a bounded sample of the same workload.  Exactly `--steps`
+steps are timed, each a replay of one input set's captured step, with an
+event between consecutive steps: `step_ms` gives their median, p10 and p90.
 """
 from __future__ import annotations
 
@@ -39,9 +45,9 @@ MFMA_BF16_PEAK_TFS = 2500.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--sets", type=int, default=0, help="input sets rotated (0 = auto)")
     ap.add_argument("--mode", default="perf", choices=["perf", "parity"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -198,27 +204,60 @@ def key_fp8_overlap(path, cfg_id, mode):
     return float(np.mean(frac))
 
 
-def cpu_baseline(cfg_id, budget_s=20.0):
-    """The oracle on a bounded sample of the same workload (rows of one input set)."""
+def cpu_model():
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_rate(sb, threads, budget_s):
+    """Query rows per second of the oracle's whole path over rows of `sb`, on
+    `threads` threads, in chunks of one row per thread until about budget_s."""
     import oracle
-    from sparse_attention_07_amd import synth
-    sb = synth.make_batch(cfg_id, mode="perf", device="cpu", layers=1)
+    oracle.set_threads(threads)
     order = np.random.default_rng(0).permutation(sb.T)
     t0 = time.perf_counter()
     done = 0
-    # chunks of rows (one per oracle thread), repeated until about `budget_s` has passed
-    chunk = max(1, oracle.threads())
     while time.perf_counter() - t0 < budget_s:
-        for i in range(0, sb.T, chunk):
-            oracle.run_path(sb, rows=sorted(order[i:i + chunk].tolist()))
-            done += len(order[i:i + chunk])
+        for i in range(0, sb.T, threads):
+            oracle.run_path(sb, rows=sorted(order[i:i + threads].tolist()))
+            done += len(order[i:i + threads])
             if time.perf_counter() - t0 > budget_s:
                 break
-    dt = time.perf_counter() - t0
-    return {"value": done / dt, "unit": "queries/s", "cores": oracle.threads(), "kind": "oracle",
-            "sample": "%d query rows (batch of %d, %s workload, one input set, repeated) through "
-                      "the whole path (scores, top-k, 1 MLA layer) in float64, %.1f s"
-                      % (done, sb.T, sb.cfg.name, dt)}
+    return done, time.perf_counter() - t0
+
+
+def cpu_baseline(sb, budget_s=20.0, one_thread_s=6.0):
+    """The oracle on a bounded sample of the same workload: rows of the first
+    input set (its tensors stay on the GPU; the oracle copies the pages of the
+    requests that own each chunk's rows to the host), through scores, top-k and
+    every layer, on all host threads; then a short 1-thread run."""
+    import oracle
+    cores = oracle.threads()
+    done, dt = _oracle_rate(sb, cores, budget_s)
+    done1, dt1 = _oracle_rate(sb, 1, one_thread_s)
+    oracle.set_threads(cores)
+    layers = len(sb.q)
+    return {"value": done / dt, "unit": "queries/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": "%d query rows of one %d-row %s batch through the whole path (scores, top-k, "
+                      "%d MLA layer%s) in float64 on %d threads, %.1f s"
+                      % (done, sb.T, sb.cfg.name, layers, "s" if layers > 1 else "", cores, dt),
+            "one_thread": {"value": done1 / dt1, "unit": "queries/s",
+                           "sample": "%d query rows, same path, 1 thread, %.1f s" % (done1, dt1)}}
+
+
+def spread(xs):
+    """Median, p10 and p90 of a list of times (ms)."""
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "n": int(a.size)}
 
 
 def main():
@@ -235,6 +274,8 @@ def main():
 
     cfg_id = args.config
     base = synth.CONFIGS[cfg_id]
+    # independent input sets rotated so that the 256 MB MALL cannot serve
+    # repeat reads (decode16's and mtp_fp8's per-step data would fit in it)
     sets = args.sets or {0: 1, 1: 8, 2: 1, 3: 1, 4: 2}[cfg_id]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -295,29 +336,36 @@ def main():
     eager_ms_step = start.elapsed_time(stop) / n_eager
     eager_stage_ms = {s: float(np.mean([a.elapsed_time(b) for a, b in ev[s]])) for s in stages}
 
-    # Timed region: a HIP graph holding one step per input set (as a serving
-    # loop would replay it), replayed until `steps` steps have run.
-    g_step = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_step):
-        for p in paths:
+    # Timed region: exactly `steps` steps, step i a replay of input set
+    # i % sets's captured step (as a serving loop would replay it), with an
+    # event between consecutive steps for the per-step spread.
+    g_sets = []
+    for p in paths:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
             p.step()
-    reps = max(1, (args.steps + sets - 1) // sets)
-    g_step.replay()
+        g_sets.append(g)
+    for g in g_sets:
+        g.replay()
     torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(reps):
-        g_step.replay()
-    stop.record(stream)
+    n_steps = args.steps
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_steps + 1)]
+    step_ev[0].record(stream)
+    for i in range(n_steps):
+        g_sets[i % sets].replay()
+        step_ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    n_steps = reps * sets
-    ms_step = start.elapsed_time(stop) / n_steps
+    ms_step = step_ev[0].elapsed_time(step_ev[n_steps]) / n_steps
+    step_spread = spread([step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(n_steps)])
 
     # Per-kernel durations: one graph per stage over all input sets, events
-    # around its replays on the launch stream.  A graph holds at least 8
-    # launches (the rotation repeated when there are fewer sets), so that a
-    # short kernel's replays are not bound by the host's graph submissions.
-    stage_ms = {}
+    # around each of its replays on the launch stream.  A graph holds at least
+    # 8 launches (the rotation repeated when there are fewer sets), so that a
+    # short kernel's replays are not bound by the host's graph submissions;
+    # the spread is over replays (each the mean of its launches).
+    stage_ms, stage_spread = {}, {}
     rounds = max(1, (8 + sets - 1) // sets)
+    reps = max(3, (n_steps + sets - 1) // sets)
     for s in stages:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -326,12 +374,15 @@ def main():
                     run_stage(p, s)
         g.replay()
         torch.cuda.synchronize()
-        start.record(stream)
-        for _ in range(reps):
+        ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev_s[0].record(stream)
+        for r in range(reps):
             g.replay()
-        stop.record(stream)
+            ev_s[r + 1].record(stream)
         torch.cuda.synchronize()
-        stage_ms[s] = start.elapsed_time(stop) / (n_steps * rounds)
+        per = [ev_s[r].elapsed_time(ev_s[r + 1]) / (sets * rounds) for r in range(reps)]
+        stage_ms[s] = ev_s[0].elapsed_time(ev_s[reps]) / (reps * sets * rounds)
+        stage_spread[s] = spread(per)
 
     T = paths[0].sb.T
     alg = [algorithmic(p.sb, p) for p in paths]
@@ -341,7 +392,7 @@ def main():
         fl = float(np.mean([a[s]["flops"] for a in alg]))
         launches = alg[0][s].get("launches_per_step", 1)
         t = stage_ms[s] / 1e3
-        report[s] = {"ms": stage_ms[s], "launches_per_step": launches,
+        report[s] = {"ms": stage_ms[s], "ms_spread": stage_spread[s], "launches_per_step": launches,
                      "alg_bytes": by, "alg_flops": fl,
                      "GB_s": by / t / 1e9, "TFLOP_s": fl / t / 1e12,
                      "frac_hbm": by / t / 1e9 / HBM_PEAK_GBS,
@@ -378,6 +429,7 @@ def main():
         "value": T / (ms_step / 1e3),
         "unit": "queries/s",
         "n_gpus": 1, "steps": n_steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "step_ms": step_spread,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if cfg.q_fmt == 1 else "f32",
         "data": "synthetic (seeded, %s mode; %d rotated input sets)" % (args.mode, sets),
@@ -397,9 +449,10 @@ def main():
         "indexer_topk_rows_per_s": T / ((stage_ms["index_topk"] if "index_topk" in stage_ms
                                          else stage_ms["index_scores"] + stage_ms["topk"]) / 1e3),
         "sparse_mla_queries_per_s": T / (stage_ms["sparse_mla"] / len(paths[0].kv) / 1e3),
-        "timing": "HIP graph replay of whole steps (one per input set); stage times from "
-                  "per-stage graphs of >= 8 launches (input sets repeated when fewer); eager "
-                  "figures include host launch gaps",
+        "timing": "HIP graph replays of whole steps (one captured step per input set, sets "
+                  "rotated), an event between steps; stage times from per-stage graphs of >= 8 "
+                  "launches (input sets repeated when fewer), spread over replays; eager figures "
+                  "include host launch gaps",
         "eager_ms_per_step": eager_ms_step,
         "eager_stage_ms": eager_stage_ms,
         "stages": report,
@@ -409,7 +462,7 @@ def main():
         out["topk_overlap_vs_bf16_keys"] = key_fp8_overlap(paths[0], cfg_id, args.mode)
     if (not args.no_cpu and not args.key_fp8 and not args.prep and args.score_budget is None
             and args.kv is None):
-        out["cpu_baseline"] = cpu_baseline(cfg_id)
+        out["cpu_baseline"] = cpu_baseline(paths[0].sb)
     print(json.dumps(out), flush=True)
 
 

@@ -208,19 +208,27 @@ dsa_status dsa_indexer_prepare(const dsa_batch *batch, const void *q_in, void *q
  *          unmapped token is not written, so its place in the ranking is
  *          unspecified, though every access stays in bounds)
  * k, idx   as dsa_topk
- * ws       device workspace of ws_bytes; it must hold at least one score row
- *          of dsa_index_topk_workspace_bytes(1, max_seq_len, ...) bytes, else
- *          DSA_ERR_WORKSPACE.  Its contents need no initialisation.
+ * ws       device workspace of ws_bytes; it must hold at least
+ *          dsa_index_topk_workspace_bytes(1, max_seq_len, k, ...) bytes (one
+ *          row), else DSA_ERR_WORKSPACE; the chunk length is the number of rows
+ *          whose workspace fits in ws_bytes.  Its contents need no
+ *          initialisation.
  */
 dsa_status dsa_index_topk(const dsa_batch *batch, const void *q_idx, int32_t q_format, const float *w,
                           const dsa_pool *k_idx, int32_t n_heads, int32_t head_dim, int32_t k,
                           int32_t *idx, void *ws, size_t ws_bytes, void *stream);
 
-/* Workspace bytes dsa_index_topk uses within a budget: as many score rows of
- * round_up(max_seq_len, 64) f32 as fit in budget_bytes, at most num_q_rows.
- * Returns 0 when the budget is below the minimum of one score row (or when
- * num_q_rows <= 0): such a budget cannot run the call. */
-size_t dsa_index_topk_workspace_bytes(int32_t num_q_rows, int32_t max_seq_len, int64_t budget_bytes);
+/* Workspace bytes dsa_index_topk uses within a budget, for chunks of as many
+ * query rows (at most num_q_rows) as fit in budget_bytes.  Each row of a
+ * chunk takes one score row of round_up(max_seq_len, 64) f32; when
+ * max_seq_len exceeds both 32768 and k, it also takes the two-level top-k
+ * candidates dsa_topk_workspace_bytes counts for one row (an f32 score and an
+ * int32 position for each of k slots of each 32768-entry segment), so long
+ * rows are selected in two levels here as in dsa_topk.  Returns 0 when the
+ * budget is below the minimum of one row (or when num_q_rows <= 0 or
+ * k < 1): such a budget cannot run the call. */
+size_t dsa_index_topk_workspace_bytes(int32_t num_q_rows, int32_t max_seq_len, int32_t k,
+                                      int64_t budget_bytes);
 
 /* Workspace bytes dsa_topk needs for these sizes: 0 when max_seq_len <= 32768
  * or max_seq_len <= k; otherwise room for the candidates of a two-level
@@ -239,6 +247,9 @@ size_t dsa_topk_workspace_bytes(int32_t num_q_rows, int32_t max_seq_len, int32_t
  * row's whole storage (ld entries) may be read, before pos(t) is known.
  * The used scores must be finite; the others may hold anything.
  * scores   device [T, ld] f32 (all T*ld entries allocated);  idx  device [T, k] int32
+ * batch    only batch, num_q_rows, max_q_len, max_seq_len, cu_q_lens and
+ *          seq_lens are used: page_table may be NULL and the paging fields
+ *          are not checked.
  * ws       device workspace of dsa_topk_workspace_bytes() bytes (may be NULL when
  *          0; DSA_ERR_WORKSPACE when smaller).  Rows longer than 32768 entries
  *          are then selected in two levels: the exact top-k of each 32768-entry
@@ -270,14 +281,23 @@ size_t dsa_sparse_mla_workspace_bytes(int32_t num_q_rows, int32_t n_heads, int32
  * kv       latent pool, dim == dc+dr
  * idx      device [T, k] int32 (the dsa_topk output, or a shared layer's copy)
  * out      device [T, n_heads, dc], format q_format
- * ws       device workspace of dsa_sparse_mla_workspace_bytes() bytes.  It
- *          holds per-split partials and arrival counters; the caller must
- *          zero-fill it once before its first use, and every call returns it
- *          with the counters zero again.  Calls that may run at the same time
- *          (other streams) need workspaces of their own.
+ * ws       device workspace of dsa_sparse_mla_workspace_bytes() bytes (it may
+ *          be NULL when that is 0).  Its first 4096 bytes hold arrival
+ *          counters, at that place for every shape, format and entry point;
+ *          split partials follow them.  The caller zero-fills the workspace
+ *          once before its first use; every call returns the counters to zero
+ *          and never writes anything else into those 4096 bytes, so one
+ *          workspace, sized for the largest call, serves calls of any shape in
+ *          any order.  Calls that may run at the same time (other streams)
+ *          need workspaces of their own.
  * Built combinations: q DSA_BF16 with kv DSA_BF16, DSA_FP8_E4M3_B128 or DSA_INT8_AFFINE_B128,
  * dc 512, dr 64, n_heads a multiple of 16 up to 128 (MFMA); q and kv DSA_F32
- * with dc+dr <= 1024, n_heads <= 128, k <= 4096 (vector ALUs).
+ * with dc+dr <= 1024, n_heads <= 128, k <= 4096 (vector ALUs).  The MFMA
+ * kernels stage the byte offsets of all rows one workgroup attends in LDS:
+ * with n_heads a multiple of 64, a workgroup that attends more than 2304 rows
+ * (any prefill call with k > 2304; a decode call whose rows are not split,
+ * which happens when num_q_rows * n_heads / 64 >= 384) does not fit, and the
+ * call returns DSA_ERR_UNSUPPORTED before launching anything.
  * _decode and _prefill compute the same function; they differ only in how
  * the work is split across workgroups (decode splits the selected rows of
  * each query to fill the GPU, prefill does not).

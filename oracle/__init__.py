@@ -86,6 +86,8 @@ def _load():
         for f in (lib.oracle_index_scores, lib.oracle_topk, lib.oracle_sparse_mla):
             f.restype = c_int
         lib.oracle_threads.restype = c_int
+        lib.oracle_set_threads.argtypes = [c_int]
+        lib.oracle_set_threads.restype = None
         _lib = lib
     return _lib
 
@@ -223,6 +225,11 @@ def sparse_mla(batch, layer, idx, rows=None, k=None):
 def threads() -> int:
     """OpenMP threads the oracle's row loops run on."""
     return _load().oracle_threads()
+
+
+def set_threads(n: int) -> None:
+    """Run the oracle's row loops on n OpenMP threads from now on."""
+    _load().oracle_set_threads(int(n))
 
 
 def e4m3_to_double(byte: int) -> float:

@@ -441,3 +441,12 @@ int oracle_threads(void) {
   return 1;
 #endif
 }
+
+/* Sets the thread count of the loops above (no effect without OpenMP). */
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}

@@ -53,17 +53,19 @@ using dsa::PoolArgs;
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-// Shared batch checks.  Returns DSA_OK and fills `ba`, or an error.
-dsa_status check_batch(const dsa_batch* b, BatchArgs* ba) {
+// Shared batch checks.  Returns DSA_OK and fills `ba`, or an error.  Calls
+// that never touch a pool (top-k) pass paged = false: their page table may be
+// NULL and the paging fields are not checked.
+dsa_status check_batch(const dsa_batch* b, BatchArgs* ba, bool paged = true) {
   if (b == nullptr) return DSA_ERR_NULL;
-  if (b->batch < 1 || b->num_q_rows < 0 || b->max_q_len < 0 || b->max_seq_len < 0 ||
-      b->page_size < 1 || b->pt_stride < 1 || b->num_pages < 0)
+  if (b->batch < 1 || b->num_q_rows < 0 || b->max_q_len < 0 || b->max_seq_len < 0)
     return DSA_ERR_SHAPE;
+  if (paged && (b->page_size < 1 || b->pt_stride < 1 || b->num_pages < 0)) return DSA_ERR_SHAPE;
   if (b->num_q_rows > 0) {
-    if (b->cu_q_lens == nullptr || b->seq_lens == nullptr || b->page_table == nullptr)
+    if (b->cu_q_lens == nullptr || b->seq_lens == nullptr || (paged && b->page_table == nullptr))
       return DSA_ERR_NULL;
     if (b->max_q_len < 1 || (int64_t)b->max_q_len * b->batch < b->num_q_rows) return DSA_ERR_SHAPE;
-    if (!aligned(b->cu_q_lens, 4) || !aligned(b->seq_lens, 4) || !aligned(b->page_table, 4))
+    if (!aligned(b->cu_q_lens, 4) || !aligned(b->seq_lens, 4) || (paged && !aligned(b->page_table, 4)))
       return DSA_ERR_ALIGN;
   }
   *ba = BatchArgs{b->batch, b->num_q_rows, b->max_q_len, b->max_seq_len, b->cu_q_lens,
@@ -140,6 +142,26 @@ int64_t score_row_bytes(int32_t max_seq_len) {
   return (n + 63) / 64 * 64 * 4;
 }
 
+// dsa_index_topk's workspace for a chunk of `rows` query rows: their score
+// rows, then the two-level top-k candidates of those rows (none when the
+// rows fit the top-k's LDS cache).
+size_t index_topk_bytes(int64_t rows, int32_t max_seq_len, int32_t k) {
+  return (size_t)(rows * score_row_bytes(max_seq_len)) + dsa::topk_workspace_bytes((int)rows, max_seq_len, k);
+}
+
+// The most query rows per chunk whose workspace fits in `bytes` (at most T).
+int64_t index_topk_chunk_rows(int64_t T, int32_t max_seq_len, int32_t k, int64_t bytes) {
+  // per-row cost: a score row plus, for two-level rows, k candidates (score
+  // and position) per segment; the candidate layout pads once to 256 bytes
+  const int64_t cand = dsa::topk_workspace_bytes(1, max_seq_len, k) > 0
+                           ? (int64_t)(dsa::topk_workspace_bytes(2, max_seq_len, k) -
+                                       dsa::topk_workspace_bytes(1, max_seq_len, k))
+                           : 0;
+  int64_t rows = std::min<int64_t>(T, bytes / (score_row_bytes(max_seq_len) + cand));
+  while (rows > 0 && (int64_t)index_topk_bytes(rows, max_seq_len, k) > bytes) --rows;
+  return rows;
+}
+
 dsa_status sparse_mla(const dsa_batch* batch, const void* q, int32_t q_format, const dsa_pool* kv,
                       const int32_t* idx, int32_t k, int32_t n_heads, int32_t dc, int32_t dr,
                       float sm_scale, void* out, float* lse, void* ws, size_t ws_bytes,
@@ -161,6 +183,7 @@ dsa_status sparse_mla(const dsa_batch* batch, const void* q, int32_t q_format, c
     if (!aligned(q, 16) || !aligned(out, 16)) return DSA_ERR_ALIGN;
     const dsa::MlaPlan plan = dsa::plan_sparse_mla(ba.num_q_rows, n_heads, k, dc, prefill,
                                                    kv->format != DSA_BF16);
+    if (!dsa::sparse_mla_plan_fits(plan, n_heads)) return DSA_ERR_UNSUPPORTED;
     if (plan.ws_bytes > 0) {
       if (ws == nullptr) return DSA_ERR_WORKSPACE;
       if (ws_bytes < plan.ws_bytes) return DSA_ERR_WORKSPACE;
@@ -213,11 +236,11 @@ dsa_status dsa_index_scores(const dsa_batch* batch, const void* q_idx, int32_t q
   return hip_status(launch_index(ba, ia, scores, ld, static_cast<hipStream_t>(stream), 0, ba.num_q_rows));
 }
 
-size_t dsa_index_topk_workspace_bytes(int32_t num_q_rows, int32_t max_seq_len, int64_t budget_bytes) {
-  if (num_q_rows <= 0 || max_seq_len < 0 || budget_bytes <= 0) return 0;
-  const int64_t row = score_row_bytes(max_seq_len);
-  const int64_t rows = std::min<int64_t>(num_q_rows, budget_bytes / row);
-  return rows < 1 ? 0 : (size_t)(rows * row);
+size_t dsa_index_topk_workspace_bytes(int32_t num_q_rows, int32_t max_seq_len, int32_t k,
+                                      int64_t budget_bytes) {
+  if (num_q_rows <= 0 || max_seq_len < 0 || k < 1 || budget_bytes <= 0) return 0;
+  const int64_t rows = index_topk_chunk_rows(num_q_rows, max_seq_len, k, budget_bytes);
+  return rows < 1 ? 0 : index_topk_bytes(rows, max_seq_len, k);
 }
 
 dsa_status dsa_index_topk(const dsa_batch* batch, const void* q_idx, int32_t q_format, const float* w,
@@ -232,17 +255,22 @@ dsa_status dsa_index_topk(const dsa_batch* batch, const void* q_idx, int32_t q_f
   if ((st = check_index(ba, q_idx, q_format, w, k_idx, n_heads, head_dim, &ia)) != DSA_OK) return st;
   if (k < 1) return DSA_ERR_SHAPE;
   const int64_t row = score_row_bytes(ba.max_seq_len);
-  const int64_t per = ws == nullptr ? 0 : std::min<int64_t>(ba.num_q_rows, (int64_t)(ws_bytes / (size_t)row));
-  if (per < 1) return DSA_ERR_WORKSPACE;  // below the minimum: one score row
+  const int64_t per =
+      ws == nullptr ? 0 : index_topk_chunk_rows(ba.num_q_rows, ba.max_seq_len, k, (int64_t)ws_bytes);
+  if (per < 1) return DSA_ERR_WORKSPACE;  // below the minimum: one row's scores (and candidates)
   if (!aligned(ws, 16) || !aligned(idx, 4)) return DSA_ERR_ALIGN;
   float* scores = static_cast<float*>(ws);
+  // the chunk's two-level candidates follow its score rows (256-byte aligned)
+  uint8_t* cand = static_cast<uint8_t*>(ws) + per * row;
+  const size_t cand_bytes = dsa::topk_workspace_bytes((int)per, ba.max_seq_len, k);
   const int64_t ld = row / 4;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // Chunks of `per` query rows: each chunk's scores, then at once its top-k.
   for (int r0 = 0; r0 < ba.num_q_rows; r0 += (int)per) {
     const int r1 = (int)std::min<int64_t>(ba.num_q_rows, r0 + per);
     if ((st = hip_status(launch_index(ba, ia, scores, ld, s, r0, r1))) != DSA_OK) return st;
-    if ((st = hip_status(dsa::launch_topk(ba, scores, ld, k, idx, s, r0, r1))) != DSA_OK) return st;
+    if ((st = hip_status(dsa::launch_topk(ba, scores, ld, k, idx, s, r0, r1, cand, cand_bytes))) != DSA_OK)
+      return st;
   }
   return DSA_OK;
 }
@@ -297,7 +325,7 @@ size_t dsa_topk_workspace_bytes(int32_t num_q_rows, int32_t max_seq_len, int32_t
 dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld, int32_t k,
                     int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
   BatchArgs ba;
-  dsa_status st = check_batch(batch, &ba);
+  dsa_status st = check_batch(batch, &ba, /*paged=*/false);
   if (st != DSA_OK) return st;
   if (ba.num_q_rows == 0) return DSA_OK;
   if (scores == nullptr || idx == nullptr) return DSA_ERR_NULL;

@@ -53,14 +53,23 @@ hipError_t launch_topk(const BatchArgs& ba, const float* scores, int64_t ld, int
 
 // Split plan of the MFMA sparse-MLA kernel (rows of each query cut into `splits`
 // ranges of `rows_per_split`); workspace holds the partial results.
+// The workspace starts with kMlaCounterBytes of arrival counters, one per
+// (row, head group) of a split launch, always at the same place whatever the
+// shape of the call; the split partials follow.  A launch splits only when it
+// has fewer (row, head group) blocks than its workgroup target, so
+// kMlaCounterSlots counters always suffice.
+constexpr int kMlaCounterSlots = 512;
+constexpr size_t kMlaCounterBytes = 4096;
 struct MlaPlan {
   int splits;
   int rows_per_split;
-  size_t ws_bytes;         // split partials, then arrival counters (0 when splits == 1)
-  size_t counters_offset;  // byte offset of the counters in the workspace
+  size_t ws_bytes;  // counters, then split partials (0 when splits == 1)
 };
 // q8: the latent rows are 8-bit (fp8 or int8), which changes the 16-head split.
 MlaPlan plan_sparse_mla(int num_q_rows, int n_heads, int k, int dc, bool prefill, bool q8);
+// Whether the MFMA kernel can stage a plan's rows per split in LDS (checked
+// before launching; a plan that does not fit is refused as unsupported).
+bool sparse_mla_plan_fits(const MlaPlan& plan, int n_heads);
 
 hipError_t launch_sparse_mla_bf16(const BatchArgs& ba, const void* q, const PoolArgs& kv,
                                   const int32_t* idx, int k, int n_heads, float sm_scale,

@@ -299,7 +299,7 @@ struct MlaArgs {
   uint16_t* out;
   float* lse;
   float* ws;       // split partials: [T, head groups, splits] blocks of kPartBytes(heads per group)
-  int* counters;   // [T, head groups] arrivals per row and head group
+  int* counters;   // [T * head groups] arrivals per row and head group (< kMlaCounterSlots)
   int splits, rows_per_split;
 };
 
@@ -999,7 +999,7 @@ __global__ __launch_bounds__(kWave) void sparse_mla_f32_valu(
 }  // namespace
 
 MlaPlan plan_sparse_mla(int num_q_rows, int n_heads, int k, int dc, bool prefill, bool q8) {
-  MlaPlan p{1, k, 0, 0};
+  MlaPlan p{1, k, 0};
   if (dc != kDc || n_heads % 16 != 0 || k <= 0 || num_q_rows <= 0) return p;
   const bool wide = n_heads % 64 == 0;
   const int64_t blocks = (int64_t)num_q_rows * (wide ? n_heads / 64 : n_heads / 16);
@@ -1023,10 +1023,9 @@ MlaPlan plan_sparse_mla(int num_q_rows, int n_heads, int k, int dc, bool prefill
   p.splits = splits;
   p.rows_per_split = rps;
   if (splits > 1) {
-    // partials, then one arrival counter per (row, head group)
-    p.counters_offset = ((size_t)num_q_rows * n_heads * splits * (kDc * 2 + 8) + 255) / 256 * 256;
-    p.ws_bytes = p.counters_offset +
-                 ((size_t)num_q_rows * (wide ? n_heads / 64 : n_heads / 16) * sizeof(int) + 255) / 256 * 256;
+    // want > 1 means blocks < target <= kMlaCounterSlots: one counter per block fits
+    static_assert(kMlaCounterSlots >= 512, "a counter for every block of a split launch");
+    p.ws_bytes = kMlaCounterBytes + (size_t)num_q_rows * n_heads * splits * kPartBytes(16) / 16;
   }
   return p;
 }
@@ -1051,7 +1050,14 @@ hipError_t launch_with_lds(Kernel kernel, dim3 grid, int threads, size_t lds, hi
   return hipGetLastError();
 }
 
+size_t plan_lds(const MlaPlan& plan, int n_heads) {
+  return n_heads % 64 == 0 ? mla_lds(plan.rows_per_split, (kWideBufs - 1) * kTileLds + 2 * kSbufWide)
+                           : mla_lds(plan.rows_per_split, kSbufLds);
+}
+
 }  // namespace
+
+bool sparse_mla_plan_fits(const MlaPlan& plan, int n_heads) { return plan_lds(plan, n_heads) <= kMaxLds; }
 
 hipError_t launch_sparse_mla_bf16(const BatchArgs& ba, const void* q, const PoolArgs& kv,
                                   const int32_t* idx, int k, int n_heads, float sm_scale,
@@ -1059,15 +1065,14 @@ hipError_t launch_sparse_mla_bf16(const BatchArgs& ba, const void* q, const Pool
                                   hipStream_t stream) {
   const bool wide = n_heads % 64 == 0;
   const int fmt = kv.format == 2 ? kFmtFp8 : (kv.format == 3 ? kFmtInt8 : kFmtBf16);
-  const size_t lds = wide ? mla_lds(plan.rows_per_split, (kWideBufs - 1) * kTileLds + 2 * kSbufWide)
-                         : mla_lds(plan.rows_per_split, kSbufLds);
-  if (lds > kMaxLds) return hipErrorInvalidValue;
+  const size_t lds = plan_lds(plan, n_heads);
+  if (lds > kMaxLds) return hipErrorInvalidValue;  // the API refuses such plans before launching
   MlaArgs args{ba.cu_q, ba.seq_lens, ba.page_table, ba.batch, ba.pt_stride, ba.page_size,
                ba.num_pages, static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(kv.base),
                kv.page_stride, kv.row_stride, idx, k, n_heads, sm_scale * kLog2e,
-               static_cast<uint16_t*>(out), lse, static_cast<float*>(ws),
-               plan.splits > 1 ? reinterpret_cast<int*>(static_cast<uint8_t*>(ws) + plan.counters_offset)
-                               : nullptr,
+               static_cast<uint16_t*>(out), lse,
+               plan.splits > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kMlaCounterBytes) : nullptr,
+               plan.splits > 1 ? static_cast<int*>(ws) : nullptr,
                plan.splits, plan.rows_per_split};
   const int T = ba.num_q_rows;
   const int n_groups = wide ? n_heads / 64 : n_heads / 16;

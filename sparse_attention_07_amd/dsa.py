@@ -62,7 +62,7 @@ def _load():
     lib.dsa_indexer_prepare.restype = i32
     lib.dsa_index_topk.argtypes = [bp, vp, i32, vp, pp, i32, i32, i32, vp, vp, sz, vp]
     lib.dsa_index_topk.restype = i32
-    lib.dsa_index_topk_workspace_bytes.argtypes = [i32, i32, i64]
+    lib.dsa_index_topk_workspace_bytes.argtypes = [i32, i32, i32, i64]
     lib.dsa_index_topk_workspace_bytes.restype = sz
     lib.dsa_topk_workspace_bytes.argtypes = [i32, i32, i32]
     lib.dsa_topk_workspace_bytes.restype = sz
@@ -162,8 +162,8 @@ def dsa_indexer_prepare(batch, q_in, q_out, k_in, fmt, ln_weight, ln_bias, ln_ep
         ctypes.byref(k_pool), n_heads, head_dim, _stream(stream)))
 
 
-def dsa_index_topk_workspace_bytes(num_q_rows, max_seq_len, budget_bytes) -> int:
-    return _lib.dsa_index_topk_workspace_bytes(num_q_rows, max_seq_len, budget_bytes)
+def dsa_index_topk_workspace_bytes(num_q_rows, max_seq_len, k, budget_bytes) -> int:
+    return _lib.dsa_index_topk_workspace_bytes(num_q_rows, max_seq_len, k, budget_bytes)
 
 
 def dsa_index_topk(batch, q_idx, q_format, w, k_pool: dsa_pool, n_heads, head_dim, k, idx, ws, ws_bytes,

@@ -45,7 +45,7 @@ class DSAPath:
         # dsa_index_topk over a workspace of whole score rows instead of [T, ld]
         self.itk_ws_bytes = 0
         if score_budget is not None:
-            self.itk_ws_bytes = dsa.dsa_index_topk_workspace_bytes(T, sb.max_seq_len, score_budget)
+            self.itk_ws_bytes = dsa.dsa_index_topk_workspace_bytes(T, sb.max_seq_len, cfg.topk, score_budget)
             if self.itk_ws_bytes == 0 and T > 0:
                 raise ValueError("score budget %d B is below one score row" % score_budget)
             self.itk_ws = torch.empty((max(self.itk_ws_bytes, 16) // 4,), dtype=torch.float32, device=dev)

@@ -135,14 +135,30 @@ def test_indexer_prepare_validation():
 
 def test_index_topk_workspace_sizes():
     W = L.dsa_index_topk_workspace_bytes
-    row = 128 * 4                                   # max_seq_len 100 -> 128 entries
-    assert W(4, 100, 10 ** 9) == 4 * row            # never more rows than the batch
-    assert W(4, 100, 3 * row + 5) == 3 * row        # whole rows only
-    assert W(4, 100, row) == row
-    assert W(4, 100, row - 1) == 0                  # below the minimum: rejected
-    assert W(0, 100, 10 ** 9) == 0
-    assert W(4, 0, 10 ** 9) == 4 * 256              # an empty context still has a 64-entry row
-    assert W(3, 1 << 20, 1 << 30) == 3 * (1 << 22)  # 1M-token rows
+    row = 128 * 4                                      # max_seq_len 100 -> 128 entries
+    assert W(4, 100, 8, 10 ** 9) == 4 * row            # never more rows than the batch
+    assert W(4, 100, 8, 3 * row + 5) == 3 * row        # whole rows only
+    assert W(4, 100, 8, row) == row
+    assert W(4, 100, 8, row - 1) == 0                  # below the minimum: rejected
+    assert W(0, 100, 8, 10 ** 9) == 0
+    assert W(4, 100, 0, 10 ** 9) == 0                  # k < 1
+    assert W(4, 0, 8, 10 ** 9) == 4 * 256              # an empty context still has a 64-entry row
+    # rows past the top-k's 32768-entry LDS cache also carry their two-level
+    # candidates: an f32 score and an int32 position per slot of k per segment
+    T = dsa.dsa_topk_workspace_bytes
+    srow = (1 << 20) * 4
+    assert W(3, 1 << 20, 2048, 1 << 40) == 3 * srow + T(3, 1 << 20, 2048)
+    assert T(3, 1 << 20, 2048) == 3 * 32 * 2048 * 8
+    one = W(3, 1 << 20, 2048, 1 << 40) // 3
+    assert W(3, 1 << 20, 2048, one) == one and W(3, 1 << 20, 2048, one - 1) == 0
+    srow = 40064 * 4                                   # max_seq_len 40001 -> 40064 entries
+    assert W(5, 40001, 7, 10 ** 9) == 5 * srow + T(5, 40001, 7)
+    assert W(5, 40001, 40001, 10 ** 9) == 5 * srow    # k >= the row: no candidates
+    for budget in (10 ** 6, 3 * 10 ** 6 + 17, 10 ** 7):   # whole rows, within the budget
+        got = W(50, 40001, 7, budget)
+        rows = got // srow
+        assert 0 < got <= budget and got == rows * srow + T(rows, 40001, 7)
+        assert rows == 50 or (rows + 1) * srow + T(rows + 1, 40001, 7) > budget
 
 
 def _itopk(batch, ws=FAKE, ws_bytes=1 << 20, k=8, idx=FAKE, **kw):
@@ -170,6 +186,14 @@ def test_index_topk_validation():
 
 def test_topk_validation():
     b = _batch()
+    # top-k reads no pool: a NULL page table and unset paging fields are accepted
+    nopages = _batch()
+    nopages.page_table, nopages.page_size, nopages.pt_stride, nopages.num_pages = None, 0, 0, -1
+    assert L.dsa_topk(ctypes.byref(nopages), FAKE, 128, 8, ctypes.c_void_p(0x10002), None, 0, None) == 6
+    assert L.dsa_topk(ctypes.byref(nopages), FAKE, 50, 8, FAKE, None, 0, None) == 2
+    nocu = _batch()
+    nocu.cu_q_lens = None
+    assert L.dsa_topk(ctypes.byref(nocu), FAKE, 128, 8, FAKE, None, 0, None) == 1
     assert L.dsa_topk(None, FAKE, 128, 8, FAKE, None, 0, None) == 1
     assert L.dsa_topk(ctypes.byref(_batch(T=0)), None, 128, 8, None, None, 0, None) == 0
     assert L.dsa_topk(ctypes.byref(b), FAKE, 128, 0, FAKE, None, 0, None) == 2
@@ -221,17 +245,35 @@ def test_sparse_mla_validation():
     assert dsa.dsa_sparse_mla_workspace_bytes(4096, 128, 2048, 512, False) == 0
 
 
+def test_sparse_mla_refuses_plans_beyond_lds():
+    # 64-head workgroups stage every attended row's offset in LDS: up to 2304
+    # rows per workgroup.  Prefill never splits, so k = 2336 does not fit; it
+    # is refused before any launch, not reported as a failed launch.
+    assert _mla(_batch(), k=2304, prefill=True, q=ODD) == 6            # fits: reaches the later checks
+    assert _mla(_batch(), k=2336, prefill=True) == 3
+    assert _mla(_batch(), k=4096, H=64, prefill=True) == 3
+    # decode splits small batches (4 rows: the split plan fits), not large ones
+    big = _batch(T=512, B=512, max_q=1)
+    assert dsa.dsa_sparse_mla_workspace_bytes(512, 128, 2336, 512, False) == 0
+    assert _mla(big, k=2336) == 3
+    need = dsa.dsa_sparse_mla_workspace_bytes(4, 128, 2336, 512, False)
+    assert need > 0 and _mla(_batch(), k=2336, ws=FAKE, ws_bytes=need, q=ODD) == 6
+    # 16-head workgroups keep their own (larger) row budget
+    assert _mla(_batch(), k=2336, H=16, prefill=True, q=ODD) == 6
+
+
 @pytest.mark.parametrize("T,H,k", [(64, 16, 2048), (256, 128, 2048), (160, 128, 2048), (8, 16, 64),
-                                   (1, 128, 100), (3, 48, 33)])
+                                   (1, 128, 100), (3, 48, 33), (100, 16, 2048), (40, 128, 2048)])
 def test_split_workspace_is_consistent(T, H, k):
     ws = dsa.dsa_sparse_mla_workspace_bytes(T, H, k, 512, False)
     if ws:
-        # partials (512 bf16 + two f32 per row, head and split) and one int32
-        # counter per (row, head group), each region padded to 256 bytes
-        per = T * H * (512 * 2 + 8)
+        # 4096 bytes of arrival counters first (at most 512 (row, head group)
+        # blocks are split), then partials: 512 bf16 + two f32 per row, head
+        # and split
         groups = T * (H // 64 if H % 64 == 0 else H // 16)
-        cnt = (groups * 4 + 255) // 256 * 256
-        part = ws - cnt
+        assert groups < 512
+        per = T * H * (512 * 2 + 8)
+        part = ws - 4096
         splits = part // per
-        assert part - splits * per < 256 and part % 256 == 0
+        assert part == splits * per
         assert 2 <= splits <= min(64, max(1, k // 256))

@@ -36,9 +36,10 @@ def _bounded(sb, rows_per_chunk):
     from sparse_attention_07_amd import dsa
     cfg = sb.cfg
     b = dsa.batch_from(sb)
-    row = dsa.dsa_index_topk_workspace_bytes(1, sb.max_seq_len, 1 << 40)
-    ws_bytes = dsa.dsa_index_topk_workspace_bytes(sb.T, sb.max_seq_len, rows_per_chunk * row)
-    assert ws_bytes == min(rows_per_chunk, sb.T) * row
+    W = dsa.dsa_index_topk_workspace_bytes
+    row = W(1, sb.max_seq_len, cfg.topk, 1 << 40)   # one row: scores (and two-level candidates)
+    ws_bytes = W(sb.T, sb.max_seq_len, cfg.topk, rows_per_chunk * row)
+    assert ws_bytes == W(min(rows_per_chunk, sb.T), sb.max_seq_len, cfg.topk, 1 << 40)
     ws = torch.full((ws_bytes // 4,), float("nan"), device=DEV)   # stale contents must not matter
     idx = torch.full((sb.T, cfg.topk), 12345, dtype=torch.int32, device=DEV)
     dsa.dsa_index_topk(b, sb.q_idx, cfg.idx_fmt, sb.w, dsa.make_key_pool(sb), cfg.hi, cfg.di, cfg.topk, idx,
@@ -77,11 +78,13 @@ def test_bounded_matches_oracle_and_unbounded(name):
         assert torch.equal(idx, p.idx)
 
 
-def test_long_context_one_row_per_chunk():
-    # 5 draft rows over a 300K-token context: each chunk holds one 1.2 MB score row
+@pytest.mark.parametrize("per", [1, 2, 5])
+def test_long_context_rows_per_chunk(per):
+    # 5 draft rows over a 300K-token context: each chunk row holds a 1.2 MB
+    # score row and its two-level top-k candidates (10 segments of 32768)
     sb = synth.make_batch(4, device=DEV, layers=0, batch=1, ctx=(300000, 300000), topk=2048)
-    _say("long context T=%d max_seq=%d" % (sb.T, sb.max_seq_len))
-    idx = _bounded(sb, 1)
+    _say("long context T=%d max_seq=%d, %d rows per chunk" % (sb.T, sb.max_seq_len, per))
+    idx = _bounded(sb, per)
     ref = oracle.topk(sb, oracle.index_scores(sb))
     _parity.check_idx_exact(idx, ref)
     assert np.all((idx.cpu().numpy() >= 0).sum(1) == 2048)

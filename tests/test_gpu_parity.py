@@ -82,6 +82,13 @@ REDUCED = {
     "ragged_fp8_keys": dict(cfg=4, q_lens=[5, 0, 3, 1, 0, 5, 2], ctx=(600, 3000), topk=512,
                             key_fmt=synth.FMT_FP8_E4M3_B128),
     "prefill_fp8_keys": dict(cfg=3, q_len=130, ctx=(700, 700), topk=512, key_fmt=synth.FMT_FP8_E4M3_B128),
+    # 16-head groups with draft rows (causal inside the draft), over each cache format, and 16-head prefill
+    "decode16_drafts": dict(cfg=1, batch=4, q_len=5, ctx=(300, 3000), topk=512),
+    "decode16_drafts_fp8": dict(cfg=1, batch=3, q_len=5, ctx=(300, 3000), topk=512,
+                                kv_fmt=synth.FMT_FP8_E4M3_B128),
+    "decode16_drafts_int8": dict(cfg=1, batch=3, q_len=5, ctx=(509, 516), topk=512,
+                                 kv_fmt=synth.FMT_INT8_AFFINE_B128),
+    "prefill_h16": dict(cfg=3, q_len=100, ctx=(700, 700), topk=512, heads=16),
 }
 
 
@@ -339,3 +346,116 @@ def test_graph_replay_new_paths(case):
         torch.cuda.synchronize()
         for a, b in zip(outs, ref):
             assert torch.equal(a, b), "replay %d differs" % rep
+
+
+FP8_KEY_CASES = {
+    "decode16": dict(cfg=1, batch=6, ctx=(100, 3000), topk=512),
+    "mtp_drafts": dict(cfg=4, batch=3, ctx=(3000, 9000), topk=512),
+    "prefill_rows": dict(cfg=3, q_len=130, ctx=(2000, 2000), topk=512),
+}
+
+
+@pytest.mark.parametrize("name", list(FP8_KEY_CASES))
+def test_fp8_keys_at_quantiser_scales(name):
+    """fp8 index keys with each token's own amax/448 scale (the quantiser's
+    regime, not the exact power-of-two scale of the integer draws).  The kernel
+    applies a token's scale to its finished score, the oracle to the key: equal
+    in exact arithmetic, so scores agree to f32 rounding and the selections
+    overlap almost entirely."""
+    from sparse_attention_07_amd.path import DSAPath
+    kw = dict(FP8_KEY_CASES[name])
+    cfg = kw.pop("cfg")
+    sb = synth.make_batch(cfg, device=DEV, mode="perf", layers=0, key_fmt=synth.FMT_FP8_E4M3_B128, **kw)
+    _say("fp8 keys at quantiser scales", name, "T=%d" % sb.T)
+    p = DSAPath(sb)
+    p.index_scores()
+    p.topk()
+    torch.cuda.synchronize()
+    rows = _sample_rows(sb, n=8)
+    ref_scores = oracle.index_scores(sb, rows, ld=p.ld)
+    ref_idx = oracle.topk(sb, ref_scores, rows=rows)
+    g_idx = p.idx.cpu().numpy()[rows]
+    pos = sb.positions()
+    for i, t in enumerate(rows):
+        n = pos[t] + 1
+        g = p.scores[t, :n].double().cpu().numpy()
+        r = ref_scores[i, :n]
+        assert np.max(np.abs(g - r)) <= 1e-3 * max(1.0, np.max(np.abs(r))), "row %d scores" % t
+        a = set(g_idx[i][g_idx[i] >= 0].tolist())
+        b = set(ref_idx[i][ref_idx[i] >= 0].tolist())
+        assert len(a) == len(b) == min(n, sb.cfg.topk)
+        assert len(a & b) >= 0.99 * len(b), "row %d overlap %d of %d" % (t, len(a & b), len(b))
+
+
+def _grid_form_reached(B, max_q_len):
+    """The persistent indexer stages its unit tables in LDS next to at least one
+    unit of query rows; batches whose tables leave no room for one unit run the
+    grid-form kernel instead.  (Rule of the indexer's launcher: tables of
+    4B + 5 units + 10 ints, one unit = rows of 64 x 128 bf16 plus 64 f32
+    weights each.)"""
+    rg = max_q_len if max_q_len <= 8 else 8
+    units = B * ((max_q_len + rg - 1) // rg)
+    tables = ((4 * B + 1 + 5 * units + 1 + 8) * 4 + 15) // 16 * 16
+    per_unit = rg * (64 * 128 * 2 + 64 * 4)
+    return tables + per_unit > 160 * 1024
+
+
+@pytest.mark.parametrize("key_fmt,drafts", [(None, False), (synth.FMT_FP8_E4M3_B128, True)])
+def test_grid_form_indexer(key_fmt, drafts):
+    """More than ~4000 requests: the grid-form indexer kernel, bit-exact."""
+    from sparse_attention_07_amd.path import DSAPath
+    B = 4200
+    kw = dict(ctx=(1, 64), topk=16, layers=0)
+    if drafts:
+        kw["q_lens"] = [1 + (b * 7) % 3 for b in range(B)]
+    else:
+        kw["batch"] = B
+    if key_fmt is not None:
+        kw["key_fmt"] = key_fmt
+    sb = synth.make_batch(1, device=DEV, **kw)
+    assert _grid_form_reached(sb.B, sb.max_q_len)
+    _say("grid-form indexer B=%d T=%d fp8 keys=%s" % (sb.B, sb.T, key_fmt is not None))
+    p = DSAPath(sb)
+    p.scores.fill_(float("nan"))
+    p.index_scores()
+    p.topk()
+    torch.cuda.synchronize()
+    rows = list(range(sb.T))
+    ref_scores = oracle.index_scores(sb, rows, ld=p.ld)
+    _parity.check_scores_exact(p.scores, ref_scores, sb.positions())
+    _parity.check_idx_exact(p.idx, oracle.topk(sb, ref_scores, rows=rows))
+
+
+def test_one_workspace_serves_every_shape():
+    """One zero-filled workspace, sized for the largest call, reused by decode
+    calls of different row counts, head counts and cache formats in turn (each
+    a different split plan and partial layout): every result matches the
+    oracle, so the arrival counters never start from stale partials."""
+    from sparse_attention_07_amd import dsa
+    from sparse_attention_07_amd.path import DSAPath
+    shapes = [
+        ("h16 T=100 bf16", dict(cfg=1, batch=100, ctx=(1100, 3000), topk=1024)),
+        ("h16 T=64 bf16", dict(cfg=1, batch=64, ctx=(1100, 3000), topk=1024)),
+        ("h16 T=64 fp8", dict(cfg=1, batch=64, ctx=(1100, 3000), topk=1024, kv_fmt=synth.FMT_FP8_E4M3_B128)),
+        ("h128 T=40 bf16", dict(cfg=2, batch=40, ctx=(1100, 3000), topk=1024, layers=1)),
+        ("h16 T=100 int8", dict(cfg=1, batch=100, ctx=(1100, 3000), topk=1024, kv_fmt=synth.FMT_INT8_AFFINE_B128)),
+        ("h128 T=64 bf16", dict(cfg=2, batch=64, ctx=(1100, 3000), topk=1024, layers=1)),
+        ("h16 T=64 bf16 again", dict(cfg=1, batch=64, ctx=(1100, 3000), topk=1024)),
+    ]
+    batches = []
+    for name, kw in shapes:
+        kw = dict(kw)
+        cfg = kw.pop("cfg")
+        batches.append((name, synth.make_batch(cfg, device=DEV, **kw)))
+    need = max(dsa.dsa_sparse_mla_workspace_bytes(sb.T, sb.cfg.heads, sb.cfg.topk, 512, False)
+               for _, sb in batches)
+    ws = torch.zeros((need,), dtype=torch.uint8, device=DEV)
+    for name, sb in batches:
+        p = DSAPath(sb, prefill=False)
+        p.ws, p.ws_bytes = ws, need
+        assert dsa.dsa_sparse_mla_workspace_bytes(sb.T, sb.cfg.heads, sb.cfg.topk, 512, False) > 0
+        _say("shared workspace:", name)
+        p.step()
+        torch.cuda.synchronize()
+        _parity.check_path(sb, p, rows=_sample_rows(sb, n=6))
+    assert torch.all(ws[:4096] == 0), "arrival counters left non-zero"
