@@ -307,6 +307,30 @@ dsa_status dsa_sparse_mla_decode(const dsa_batch *batch, const void *q, int32_t 
                                  int32_t n_heads, int32_t dc, int32_t dr, float sm_scale,
                                  void *out, float *lse, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * dsa_sparse_mla_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same function, kernels and results, with the workspace
+ * taken from a device array the library owns, DSA_MLA_SCRATCH_BYTES per GPU,
+ * held by each GPU the library runs on until the process ends.  The call
+ * allocates nothing.  The caller passes inputs and outputs as for
+ * dsa_sparse_mla_decode, no workspace.
+ * - A call whose split plan needs more workspace than DSA_MLA_SCRATCH_BYTES
+ *   (what dsa_sparse_mla_workspace_bytes(num_q_rows, n_heads, k, dc, 0)
+ *   returns) gets DSA_ERR_WORKSPACE before anything is launched.
+ * - The first call on a device looks the array up on that device and clears
+ *   its arrival counters with one small kernel on `stream`; every call leaves
+ *   them at zero again.
+ * - All calls on one GPU share its array, which keeps the last call's
+ *   partials: calls that may overlap on one GPU (other streams, other host
+ *   threads) race on it and must be serialised by the caller.
+ */
+#define DSA_MLA_SCRATCH_BYTES (64u << 20)
+dsa_status dsa_sparse_mla_decode_static(const dsa_batch *batch, const void *q, int32_t q_format,
+                                        const dsa_pool *kv, const int32_t *idx, int32_t k,
+                                        int32_t n_heads, int32_t dc, int32_t dr, float sm_scale,
+                                        void *out, float *lse, void *stream);
+
 dsa_status dsa_sparse_mla_prefill(const dsa_batch *batch, const void *q, int32_t q_format,
                                   const dsa_pool *kv, const int32_t *idx, int32_t k,
                                   int32_t n_heads, int32_t dc, int32_t dr, float sm_scale,

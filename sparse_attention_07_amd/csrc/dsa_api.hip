@@ -162,6 +162,42 @@ int64_t index_topk_chunk_rows(int64_t T, int32_t max_seq_len, int32_t k, int64_t
   return rows;
 }
 
+// Workspace of dsa_sparse_mla_decode_static: a file-scope device array, one
+// per GPU (each device holds its own copy at its own address until the
+// process ends).  In host code `scratch` names a host-side stand-in, not the
+// device array: only the address hipGetSymbolAddress returns for the current
+// device is ever passed to a kernel or a copy.
+constexpr size_t kScratchBytes = DSA_MLA_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+__global__ void zero_counters(uint32_t* p, int words) {
+  for (int i = (int)threadIdx.x; i < words; i += (int)blockDim.x) p[i] = 0u;
+}
+
+// The current device's address of `scratch`, looked up (and its arrival
+// counters cleared by a small fill kernel on `stream`) on the first call on
+// that device.  Returns nullptr when a HIP call fails.
+void* scratch_for_current_device(hipStream_t stream) {
+  static std::mutex mu;
+  static std::map<int, void*> ptrs;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = ptrs.find(dev);
+  if (it != ptrs.end()) return it->second;
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+  hipLaunchKernelGGL(zero_counters, dim3(1), dim3(256), 0, stream, static_cast<uint32_t*>(ptr),
+                     (int)(dsa::kMlaCounterBytes / 4));
+  if (hipGetLastError() != hipSuccess) return nullptr;
+  ptrs[dev] = ptr;
+  return ptr;
+}
+
+// ws == kUseScratch: the caller passes no workspace and the call uses the
+// current device's `scratch` array (ws_bytes is then kScratchBytes).
+void* const kUseScratch = reinterpret_cast<void*>(~uintptr_t(0));
+
 dsa_status sparse_mla(const dsa_batch* batch, const void* q, int32_t q_format, const dsa_pool* kv,
                       const int32_t* idx, int32_t k, int32_t n_heads, int32_t dc, int32_t dr,
                       float sm_scale, void* out, float* lse, void* ws, size_t ws_bytes,
@@ -187,7 +223,11 @@ dsa_status sparse_mla(const dsa_batch* batch, const void* q, int32_t q_format, c
     if (plan.ws_bytes > 0) {
       if (ws == nullptr) return DSA_ERR_WORKSPACE;
       if (ws_bytes < plan.ws_bytes) return DSA_ERR_WORKSPACE;
-      if (!aligned(ws, 16)) return DSA_ERR_ALIGN;
+      if (ws != kUseScratch && !aligned(ws, 16)) return DSA_ERR_ALIGN;
+    }
+    if (ws == kUseScratch) {  // every check passed: only now touch the device
+      ws = plan.ws_bytes > 0 ? scratch_for_current_device(stream) : nullptr;
+      if (plan.ws_bytes > 0 && ws == nullptr) return DSA_ERR_HIP;
     }
     return hip_status(dsa::launch_sparse_mla_bf16(ba, q, pa, idx, k, n_heads, sm_scale, out, lse,
                                                   ws, plan, stream));
@@ -353,6 +393,14 @@ dsa_status dsa_sparse_mla_decode(const dsa_batch* batch, const void* q, int32_t 
                                  void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
   return sparse_mla(batch, q, q_format, kv, idx, k, n_heads, dc, dr, sm_scale, out, lse, ws,
                     ws_bytes, static_cast<hipStream_t>(stream), false);
+}
+
+dsa_status dsa_sparse_mla_decode_static(const dsa_batch* batch, const void* q, int32_t q_format,
+                                        const dsa_pool* kv, const int32_t* idx, int32_t k,
+                                        int32_t n_heads, int32_t dc, int32_t dr, float sm_scale,
+                                        void* out, float* lse, void* stream) {
+  return sparse_mla(batch, q, q_format, kv, idx, k, n_heads, dc, dr, sm_scale, out, lse, kUseScratch,
+                    kScratchBytes, static_cast<hipStream_t>(stream), false);
 }
 
 dsa_status dsa_sparse_mla_prefill(const dsa_batch* batch, const void* q, int32_t q_format,

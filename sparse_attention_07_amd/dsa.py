@@ -23,7 +23,8 @@ DSA_F32, DSA_BF16, DSA_FP8_E4M3_B128, DSA_INT8_AFFINE_B128 = 0, 1, 2, 3
 ENTRY_POINTS = ("dsa_version", "dsa_status_string", "dsa_indexer_prepare", "dsa_index_scores",
                 "dsa_index_topk", "dsa_index_topk_workspace_bytes", "dsa_topk_workspace_bytes",
                 "dsa_topk", "dsa_sparse_mla_workspace_bytes", "dsa_sparse_mla_decode",
-                "dsa_sparse_mla_prefill")
+                "dsa_sparse_mla_decode_static", "dsa_sparse_mla_prefill")
+DSA_MLA_SCRATCH_BYTES = 64 << 20
 
 
 class DSAError(RuntimeError):
@@ -72,7 +73,9 @@ def _load():
     mla = [bp, vp, i32, pp, vp, i32, i32, i32, i32, ctypes.c_float, vp, vp, vp, sz, vp]
     lib.dsa_sparse_mla_decode.argtypes = mla
     lib.dsa_sparse_mla_prefill.argtypes = mla
-    for f in (lib.dsa_index_scores, lib.dsa_topk, lib.dsa_sparse_mla_decode, lib.dsa_sparse_mla_prefill):
+    lib.dsa_sparse_mla_decode_static.argtypes = mla[:12] + [vp]
+    for f in (lib.dsa_index_scores, lib.dsa_topk, lib.dsa_sparse_mla_decode, lib.dsa_sparse_mla_prefill,
+              lib.dsa_sparse_mla_decode_static):
         f.restype = i32
     return lib
 
@@ -203,3 +206,10 @@ def dsa_sparse_mla_prefill(batch, q, q_format, kv, idx, k, n_heads, dc, dr, sm_s
                            lse=None, ws=None, ws_bytes=0, stream=None):
     _mla("dsa_sparse_mla_prefill", batch, q, q_format, kv, idx, k, n_heads, dc, dr, sm_scale, out,
          lse, ws, ws_bytes, stream)
+
+
+def dsa_sparse_mla_decode_static(batch, q, q_format, kv, idx, k, n_heads, dc, dr, sm_scale, out, lse=None,
+                                 stream=None):
+    _check("dsa_sparse_mla_decode_static", _lib.dsa_sparse_mla_decode_static(
+        ctypes.byref(batch), _ptr(q), q_format, ctypes.byref(kv), _ptr(idx), k, n_heads, dc, dr, sm_scale,
+        _ptr(out), _ptr(lse), _stream(stream)))

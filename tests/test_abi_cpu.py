@@ -277,3 +277,36 @@ def test_split_workspace_is_consistent(T, H, k):
         splits = part // per
         assert part == splits * per
         assert 2 <= splits <= min(64, max(1, k // 256))
+
+
+def _mla_static(batch, q_fmt=dsa.DSA_BF16, pool=None, k=2048, H=128, dc=512, dr=64, q=FAKE, out=FAKE):
+    pool = pool or _pool(dsa.DSA_BF16, 576, 1152)
+    st = L.dsa_sparse_mla_decode_static(ctypes.byref(batch) if batch is not None else None, q, q_fmt,
+                                        ctypes.byref(pool), FAKE, k, H, dc, dr, 0.07, out, None, None)
+    assert st != 5, "a validation case got as far as the device"
+    return st
+
+
+def test_sparse_mla_decode_static_validation():
+    # the entry point without a workspace argument validates exactly as
+    # dsa_sparse_mla_decode, before it touches the device
+    assert _mla_static(None) == 1
+    assert _mla_static(_batch(T=0)) == 0
+    assert _mla_static(_batch(), q=None) == 1
+    assert _mla_static(_batch(), k=0) == 2
+    assert _mla_static(_batch(), H=24) == 3
+    assert _mla_static(_batch(), pool=_pool(dsa.DSA_BF16, 512, 1152)) == 2
+    assert _mla_static(_batch(), q=ODD) == 6
+    assert _mla_static(_batch(T=512, B=512, max_q=1), k=2336) == 3
+
+
+def test_every_split_plan_fits_the_static_array():
+    # a launch splits only below its workgroup target, so split partials are
+    # bounded whatever the shape: every plan fits DSA_MLA_SCRATCH_BYTES
+    W = dsa.dsa_sparse_mla_workspace_bytes
+    worst = 0
+    for H in (16, 32, 48, 64, 112, 128):
+        for k in (32, 512, 2048, 2304, 16384):
+            for T in list(range(1, 80)) + list(range(80, 700, 7)):
+                worst = max(worst, W(T, H, k, 512, False))
+    assert 0 < worst <= dsa.DSA_MLA_SCRATCH_BYTES
