@@ -80,6 +80,15 @@ __device__ inline int64_t token_offset(const int32_t* __restrict__ page_table, i
   return (int64_t)page * page_stride + (int64_t)(s - lp * page_size) * row_stride;
 }
 
+// s_waitcnt vmcnt(N) through the builtin, so that the compiler's own wait
+// tracking sees it (an inline-asm wait is opaque to it).  gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt (6:4) and lgkmcnt (11:8) at their maxima.
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
 __device__ inline float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
 
 __device__ inline f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {

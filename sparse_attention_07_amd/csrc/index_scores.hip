@@ -338,14 +338,6 @@ __device__ inline void block_offsets(int64_t (&off)[2], const int (&pid)[2], int
   }
 }
 
-// s_waitcnt vmcnt(n) through the builtin, so that the compiler's own wait
-// tracking sees it (an inline-asm wait is opaque to it).  gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt (6:4) and lgkmcnt (11:8) at their maxima.
-template <int N>
-__device__ inline void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
 
 // Last request b in [0, B) whose first block is at or below blk (the owner of
 // block blk; requests without blocks are passed over).  pre is in LDS.
@@ -550,7 +542,7 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
     // for: A's keys, the page ids and the copies.
     if (j + kFlatWaves < hi) DSA_FINISH(Bk);
     load_keys(k1, Bk.off, k_base, lane, Bk.tok, page_size, k_row_stride);
-    wait_vm<kLoadsPerStep<KFP8>>();
+    wait_vmcnt<kLoadsPerStep<KFP8>>();
     lds_barrier();
 
 #define DSA_SCORE(KK, X)                                                                           \
@@ -566,7 +558,7 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
     // page ids in flight.  The first block is scored before the loop, whose
     // steps each issue loads and then score: every scoring then follows its
     // own wait on the same path.
-    wait_vm<kLoadsPerStep<KFP8>>();  // all but the newest block's keys
+    wait_vmcnt<kLoadsPerStep<KFP8>>();  // all but the newest block's keys
     DSA_SCORE(k0, A);
     while (j + kFlatWaves < hi) {
       j += kFlatWaves;
@@ -579,7 +571,7 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
       else Bk.off[0] = Bk.off[1] = -1;
       load_keys(k0, Bk.off, k_base, lane, Bk.tok, page_size, k_row_stride);
       asm volatile("" ::: "memory");
-      wait_vm<kLoadsPerStep<KFP8>>();
+      wait_vmcnt<kLoadsPerStep<KFP8>>();
       DSA_SCORE(k1, A);
       if (j + kFlatWaves >= hi) break;
       j += kFlatWaves;
@@ -592,7 +584,7 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
       else Bk.off[0] = Bk.off[1] = -1;
       load_keys(k1, Bk.off, k_base, lane, Bk.tok, page_size, k_row_stride);
       asm volatile("" ::: "memory");
-      wait_vm<kLoadsPerStep<KFP8>>();
+      wait_vmcnt<kLoadsPerStep<KFP8>>();
       DSA_SCORE(k0, A);
     }
 #undef DSA_SCORE

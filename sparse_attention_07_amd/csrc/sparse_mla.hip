@@ -180,6 +180,16 @@ __device__ inline void stage_load(Stage<F>& st, const int64_t* toffs, const uint
   if (roff >= 0) st.rope = *reinterpret_cast<const uint2*>(kv + roff + kRopeOff<F> + (tid & 15) * 8);
 }
 
+// LDS row of tile row a (0..31): a = 16h + 8j + 4b + m is stored at row
+// 16h + 4m + 2j + b.  The four tile rows one ds_read_b64_tr_b16 of the PV
+// operand fetches together (m = 0..3) then sit four LDS rows apart, which
+// with the 1168-byte row stride puts them in disjoint banks, while any 16
+// consecutive tile rows still fill 16 distinct 16-byte bank slots (QK
+// operand reads).
+__host__ __device__ constexpr int lds_row(int a) {
+  return (a & 16) | ((a & 3) << 2) | (((a >> 3) & 1) << 1) | ((a >> 2) & 1);
+}
+
 template <int F>
 __device__ inline void stage_store(const Stage<F>& st, uint8_t* tile, int tid) {
   constexpr bool Q8 = kQ8<F>;
@@ -188,7 +198,7 @@ __device__ inline void stage_store(const Stage<F>& st, uint8_t* tile, int tid) {
   const int r0 = Q8 ? (tid >> 5) : (tid >> 6);
 #pragma unroll
   for (int k = 0; k < kLat; ++k) {
-    uint8_t* dst = tile + (r0 + kStep * k) * kRowLds;
+    uint8_t* dst = tile + lds_row(r0 + kStep * k) * kRowLds;
     if (!Q8) {
       *reinterpret_cast<u32x4*>(dst + ch * 16) = st.lat[k];
     } else {
@@ -203,7 +213,7 @@ __device__ inline void stage_store(const Stage<F>& st, uint8_t* tile, int tid) {
       *reinterpret_cast<u32x4*>(dst + ch * 32 + 16) = hi;
     }
   }
-  *reinterpret_cast<uint2*>(tile + (tid >> 4) * kRowLds + 1024 + (tid & 15) * 8) = st.rope;
+  *reinterpret_cast<uint2*>(tile + lds_row(tid >> 4) * kRowLds + 1024 + (tid & 15) * 8) = st.rope;
 }
 
 // Prologue: byte offsets of the range's rows (page table applied; -1 when not
@@ -582,193 +592,526 @@ __device__ inline void merge_splits_if_last(const MlaArgs& a, int t, int grp, in
 // ---------------------------------------------------------------- 64 heads, 8 waves
 
 // A workgroup owns 64 heads of one query row and one range of its selected
-// rows, with eight waves: two per SIMD.  The siblings w and w+4 share 16 heads
-// (16(w&3) .. of the group):
-// * QK is split by k: wave w takes k steps 9(w>>2) .. +8 (half of the 576
-//   dims) over all 32 tile rows, with its half of q (36 VGPRs) as the B
-//   operand and the rows read from LDS as the A operand; the two partial
-//   score tiles are summed through LDS in a fixed order, so both siblings
-//   hold the same scores and run the same online softmax.
-// * PV is split by columns: wave w accumulates columns 256(w>>2) .. +255 of
-//   its 16 heads (64 accumulator registers), V read transposed from the tile.
-// The tiles are software-pipelined over three LDS tile buffers and two
-// partial-score buffers, with one barrier per tile: iteration i sums tile
-// i's partial scores, issues the QK MFMAs of tile i+1 while the softmax of
-// tile i runs on the VALU, then the PV MFMAs of tile i; tile i+2 is written
-// to LDS from registers and the gathers of tile i+4 are issued (two tiles of
-// gathers in flight in registers, two more waiting in LDS).
-constexpr int kWideThreads = 512;
-constexpr int kWideBufs = 3;                         // LDS tile buffers
-constexpr int kWideStages = 2;                       // register stages of gathers
-constexpr int kSbufWide = kWideThreads * 2 * 16;     // two f32x4 partial scores per thread
+// rows.  The heads form two groups of 32, each the M (or N) side of
+// v_mfma_f32_32x32x16_bf16, so one 1 KB operand read from LDS feeds 32 heads
+// (twice what a 16-head MFMA gets from it).  Eight waves, two per SIMD, in
+// two roles:
+// * Score waves 0..3 (group g = w & 1, k half kh = w >> 1): S^T = rows x q^T
+//   over their half of the 576 dims, with that half of q (32 heads x 288
+//   dims: 72 VGPRs) held as the B operand and the tile rows read from LDS as
+//   the A operand.  Each wave scales its partial scores and publishes them
+//   through LDS; both siblings then add the two halves (the same sum in
+//   both), take the same tile maximum and rescale decision, and each computes
+//   the probabilities of one of the tile's two 16-row k steps, published as
+//   bf16 already in the PV operand layout (kh = 0 also publishes the rescale
+//   factors).
+// * Value waves 4..7 (group g = w & 1, column half ch = (w >> 1) & 1): O +=
+//   P V for their 32 heads and 256 columns (128 accumulator registers), P
+//   read from LDS, V read transposed from the tile with ds_read_b64_tr_b16.
+// Wave w and wave w + 4 share a SIMD.  An iteration has two phases, each
+// pairing one wave's matrix work with the other's vector work:
+//   phase A  score waves: softmax of tile i+1 (VALU);
+//            value waves: PV of tile i (MFMA)
+//   phase B  every thread: tile i+3 stored from registers into the LDS
+//            buffer tile i used, then the gathers of tile i+3+S issued;
+//            then score waves: QK of tile i+2 (MFMA)
+// Three LDS tile buffers (tile j in buffer j % 3) and S = 3 register stages
+// of gathers (tile j in stage j % 3), so a tile's gathers have three
+// iterations to land.  P and the rescale factors rotate over three LDS slots
+// with the tiles.  The gathers are branch-free (an unusable row loads the
+// pool's first row and is zeroed when stored), so each stage store waits for
+// exactly its own loads.
+//
+// The output (O / l, bf16) is staged in LDS as [head][column] and written
+// with 16-byte stores: to `out` when the rows are not split, else to the
+// split's partial block, which the last split to finish merges.
+constexpr int kH64Threads = 512;
+constexpr int kH64Stages = 3;                        // register stages of gathers
+constexpr int kH64Bufs = 3;                          // LDS tile buffers
+constexpr int kH64Spart = 4 * 16 * 64 * 4;           // partial scores of the 4 score waves
+constexpr int kH64Pslot = 2 * 2 * 64 * 16;           // P per slot: [group][k step][64 lanes] x 16 B
+constexpr int kH64Aslot = 2 * 32 * 4 + 16;           // rescale factors per slot: [group][32], 2 flags
+constexpr int kH64Stats = 64 * 12;                   // per head: m, then l of each k step half
+constexpr int kH64Fixed =
+    kH64Bufs * kTileLds + kH64Spart + 3 * kH64Pslot + 3 * kH64Aslot + kH64Stats;
+static_assert(kH64Fixed % 16 == 0 && kH64Aslot % 16 == 0, "16-byte aligned regions");
+static_assert(kH64Bufs * kTileLds >= 64 * kDc * 2, "the output staging fits the tile buffers");
+
+// Loads per thread per gather stage (they are all issued together).
+template <int F>
+constexpr int kStageLoads = F == kFmtBf16 ? 5 : (F == kFmtFp8 ? 5 : 7);
+
+// One tile's gathers, branch-free: an unusable row (offset < 0) loads the
+// pool's first row instead.  Returns the thread's unusable-row bits (bit k:
+// latent item k, bit 4: rope) for stage_store_masked.
+template <int F>
+__device__ inline uint32_t stage_load_all(Stage<F>& st, const int64_t* toffs, const uint8_t* kv, int tid) {
+  constexpr bool Q8 = kQ8<F>;
+  constexpr int kLat = Q8 ? 2 : 4, kStep = Q8 ? 16 : 8;
+  const int ch = Q8 ? (tid & 31) : (tid & 63);
+  const int r0 = Q8 ? (tid >> 5) : (tid >> 6);
+  int64_t o[kLat + 1];
+#pragma unroll
+  for (int k = 0; k < kLat; ++k) o[k] = toffs[r0 + kStep * k];
+  o[kLat] = toffs[tid >> 4];
+  uint32_t bad = 0;
+#pragma unroll
+  for (int k = 0; k <= kLat; ++k) {
+    bad |= o[k] < 0 ? (1u << (k < kLat ? k : 4)) : 0u;
+    o[k] = o[k] < 0 ? 0 : o[k];
+  }
+#pragma unroll
+  for (int k = 0; k < kLat; ++k) {
+    const uint8_t* row = kv + o[k];
+    st.lat[k] = ld_global16(row + ch * 16);
+    if (Q8) st.sc[k] = *reinterpret_cast<const float*>(row + 512 + (ch >> 3) * 4);
+    if (F == kFmtInt8) st.bi[k] = *reinterpret_cast<const float*>(row + 528 + (ch >> 3) * 4);
+  }
+  st.rope = *reinterpret_cast<const uint2*>(kv + o[kLat] + kRopeOff<F> + (tid & 15) * 8);
+  return bad;
+}
+
+// stage_store with the unusable rows' values (bits from stage_load_all)
+// replaced by zeros.
+template <int F>
+__device__ inline void stage_store_masked(Stage<F>& st, uint32_t bad, uint8_t* tile, int tid) {
+  constexpr bool Q8 = kQ8<F>;
+  constexpr int kLat = Q8 ? 2 : 4;
+  if (bad != 0) {
+#pragma unroll
+    for (int k = 0; k < kLat; ++k) {
+      if ((bad >> k) & 1u) {
+        st.lat[k] = u32x4{};
+        if (Q8) st.sc[k] = 0.f;
+        if (F == kFmtInt8) st.bi[k] = 0.f;
+      }
+    }
+    if ((bad >> 4) & 1u) st.rope = uint2{0u, 0u};
+  }
+  stage_store<F>(st, tile, tid);
+}
+
+// 32x32 accumulator layout (v_mfma_f32_32x32x16_bf16): register i of lane l
+// holds row 8(i/4) + 4(l/32) + i%4 and column l%32.
+__device__ inline int acc32_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
+
+// Merge of the split partials of one (row, 64-head group) by the last split
+// to arrive (called by every thread after its split's block is stored).  A
+// block is O / l as bf16 [64 heads][512 columns], then (m, l) per head.
+template <int NT>
+__device__ inline void merge_splits_h64(const MlaArgs& a, int t, int grp, int n_groups, int* counter,
+                                        float* wgt, int* is_last, int tid) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's partial stores are done
+  __syncthreads();                                    // ... and every other thread's
+  if (tid == 0)
+    *is_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               a.splits - 1;
+  __syncthreads();
+  if (!*is_last) return;
+  constexpr int kNh = 64;
+  const int S = a.splits, h0 = grp * kNh;
+  const __amdgpu_buffer_rsrc_t rs = split_blocks(a, t, grp, n_groups, kNh);
+  constexpr int kStride = kPartBytes(kNh);
+  float* ls = wgt + kNh * S;
+  // statistics of (head h, split s) at index i = h * S + s
+  for (int i = tid; i < kNh * S; i += NT) {
+    const uint2 ml = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                   rs, (i % S) * kStride + kNh * kDc * 2 + 8 * (i / S), 0, kSc1));
+    wgt[i] = __uint_as_float(ml.x);
+    ls[i] = __uint_as_float(ml.y);
+  }
+  __syncthreads();
+  // merge weight of (h, s): l_s exp2(m_s - M) / L
+  float wnew[(kNh * 64 + NT - 1) / NT];
+#pragma unroll
+  for (int k = 0; k < (kNh * 64 + NT - 1) / NT; ++k) {
+    const int i = tid + k * NT, h = i / S;
+    wnew[k] = 0.f;
+    if (i < kNh * S) {
+      const float* mh = wgt + h * S;
+      const float* lh = ls + h * S;
+      float M = kNegInf;
+      for (int s = 0; s < S; ++s) M = fmaxf(M, mh[s]);
+      float L = 0.f;
+      if (M != kNegInf)
+        for (int s = 0; s < S; ++s) L += exp2_fast(mh[s] - M) * lh[s];  // empty split: 0
+      wnew[k] = L > 0.f ? exp2_fast(mh[i % S] - M) * lh[i % S] / L : 0.f;
+      if (i % S == 0 && a.lse != nullptr)
+        a.lse[(int64_t)t * a.H + h0 + h] = L > 0.f ? (M + __log2f(L)) * kLn2 : kNegInf;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < (kNh * 64 + NT - 1) / NT; ++k)
+    if (tid + k * NT < kNh * S) wgt[tid + k * NT] = wnew[k];
+  __syncthreads();
+  // 16-byte chunks c = h * 64 + col / 8 of the [64][512] block, eight rounds
+  // of NT chunks; each round loads up to kSp splits at once.
+  constexpr int kSp = 8, kRounds = kNh * kDc * 2 / 16 / NT;
+  uint16_t* outp = a.out + ((int64_t)t * a.H + h0) * kDc;
+#pragma unroll 1
+  for (int u = 0; u < kRounds; ++u) {
+    const int c = tid + u * NT, h = c >> 6;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int s0 = 0; s0 < S; s0 += kSp) {
+      u32x4 v[kSp];
+#pragma unroll
+      for (int s = 0; s < kSp; ++s)
+        if (s0 + s < S) v[s] = __builtin_amdgcn_raw_buffer_load_b128(rs, (s0 + s) * kStride + c * 16, 0, kSc1);
+#pragma unroll
+      for (int s = 0; s < kSp; ++s) {
+        if (s0 + s < S) {
+          const float wt = wgt[h * S + s0 + s];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += wt * __uint_as_float(v[s][e] << 16);
+            acc[2 * e + 1] += wt * __uint_as_float(v[s][e] & 0xFFFF0000u);
+          }
+        }
+      }
+    }
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
+    *reinterpret_cast<u32x4*>(outp + c * 8) = o;
+  }
+  if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// LDS regions of the 64-head kernel, shared by both roles.
+struct H64Lds {
+  uint8_t* tiles;   // three tile buffers; at the end, the output staging area
+  f32x4* spart;     // scaled partial scores: [score wave][4][64 lanes]
+  bf16x8* pbuf;     // P: [slot][group][k step][64 lanes]
+  float* alpha;     // rescale factors: [slot] -> [group][32 heads], then 2 flags
+  float* stats;     // per head: m, l of k step 0, l of k step 1
+};
+
+__device__ inline float* alpha_slot(const H64Lds& L, int slot) {
+  return L.alpha + slot * (kH64Aslot / 4);
+}
+
+// The tile pipeline of one role (the two roles run the same barriers in the
+// same order), then its part of the epilogue: the score waves publish (m, l)
+// per head, the value waves write O / l as bf16 [64 heads][512 columns] into
+// the staging area.  Every register array lives in one role only.
+template <int F, bool SCORE>
+__device__ inline void h64_role(const MlaArgs& a, const H64Lds& L, const int64_t* offs,
+                                const uint32_t* vmask, int t, int head0, int g, int hx, int ntiles,
+                                bool any_usable, int tid) {
+  constexpr int S = kH64Stages;
+  constexpr int kL = kStageLoads<F>;
+  static_assert(S == 3 && kH64Bufs == 3, "the tile loop is unrolled for three buffers and stages");
+  constexpr int kQSteps = 18;                  // k steps of 16 per half of the 576 dims
+  constexpr int kColTiles = 8;                 // value waves: 256 columns in tiles of 32
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hb = lane >> 5;
+  uint8_t* tiles = L.tiles;
+
+  // score waves: q half, own scaled partial scores, running max and the sum
+  // of this lane's probabilities of its k step
+  bf16x8 qreg[SCORE ? kQSteps : 1];
+  f32x16 own = f32x16{};
+  float m_run = kNegInf, l_run = 0.f;
+  // value waves: the accumulators
+  f32x16 o[SCORE ? 1 : kColTiles];
+#pragma unroll
+  for (int i = 0; i < (SCORE ? 1 : kColTiles); ++i) o[i] = f32x16{};
+
+  // Score waves: this wave's partial S^T of a tile times the softmax scale
+  // (accumulator register i: tile row acc32_row(i, lane), head l32), kept in
+  // `own` and written to LDS for the sibling.
+  // Two accumulators (even and odd k steps) keep consecutive MFMAs
+  // independent; operands are read from LDS six k steps ahead.
+  auto qk = [&](const uint8_t* tl) {
+    constexpr int kAhead = 6;
+    f32x16 acc0 = f32x16{}, acc1 = f32x16{};
+    const uint8_t* ap = tl + lds_row(l32) * kRowLds + (hx * 288 + 8 * hb) * 2;
+    bf16x8 ra[kAhead];
+#pragma unroll
+    for (int k = 0; k < kAhead; ++k) ra[k] = lds16(ap + k * 32);
+#pragma unroll
+    for (int ks = 0; ks < kQSteps; ++ks) {
+      const bf16x8 av = ra[ks % kAhead];
+      if (ks + kAhead < kQSteps) ra[ks % kAhead] = lds16(ap + (ks + kAhead) * 32);
+      const bf16x8 qv = qreg[ks < (SCORE ? kQSteps : 1) ? ks : 0];
+      if (ks & 1) acc1 = mfma32(av, qv, acc1);
+      else acc0 = mfma32(av, qv, acc0);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) own[i] = (acc0[i] + acc1[i]) * a.scale_log2;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      L.spart[(wave * 4 + r) * 64 + lane] = f32x4{own[4 * r], own[4 * r + 1], own[4 * r + 2], own[4 * r + 3]};
+  };
+  // Score waves: the tile's full scores (own half + sibling's half: the same
+  // sum in both siblings), online softmax over the tile, this wave's k step
+  // (hx) of P published into `slot`.  P's k slot e of k step ks (lane half
+  // hb) is tile row 16 ks + 8 (e / 4) + 4 hb + e % 4: exactly accumulator
+  // register 8 ks + e.
+  auto softmax = [&](uint32_t valid, int slot) {
+    float xv[16];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const f32x4 other = L.spart[((wave ^ 2) * 4 + r) * 64 + lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xv[4 * r + e] = own[4 * r + e] + other[e];
+    }
+    const bool full = valid == 0xFFFFFFFFu;   // wave-uniform
+    if (!full) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (!((valid >> acc32_row(i, lane)) & 1u)) xv[i] = kNegInf;
+    }
+    float mt = xv[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mt = fmaxf(mt, xv[i]);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+      mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const bool raise = mt > m_run + kRescaleSlack;
+    const bool any_raise = __any(raise);
+    float al = 1.f;
+    if (any_raise) {
+      const float m_new = raise ? mt : m_run;
+      al = (m_run == kNegInf) ? 0.f : exp2_fast(m_run - m_new);
+      m_run = m_new;
+      l_run *= al;
+    }
+    // this wave's k step (registers 8 hx .. 8 hx + 7), selected without a
+    // runtime register index (which would put the array in scratch)
+    float xk[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xk[e] = hx ? xv[8 + e] : xv[e];
+    bf16x8 pa;
+    if (full) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = exp2_fast(xk[e] - m_run);
+        l_run += p;
+        pa[e] = (__bf16)p;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = xk[e] == kNegInf ? 0.f : exp2_fast(xk[e] - m_run);
+        l_run += p;
+        pa[e] = (__bf16)p;
+      }
+    }
+    L.pbuf[((slot * 2 + g) * 2 + hx) * 64 + lane] = pa;
+    if (hx == 0) {
+      float* al_s = alpha_slot(L, slot);
+      if (any_raise && lane < 32) al_s[g * 32 + lane] = al;
+      if (lane == 0) reinterpret_cast<int*>(al_s + 64)[g] = any_raise ? 1 : 0;
+    }
+  };
+  // Value waves: O += P V over the tile, after the rescale the score waves
+  // flagged.  V is the B operand: lane (column l32, half hb) needs tile rows
+  // 16 ks + 4 hb + 0..3 and 16 ks + 8 + 4 hb + 0..3 of its column, two
+  // ds_read_b64_tr_b16 (in each 16-lane group lane j addresses row
+  // base + j / 4 at column block 4 (j % 4) of the group's 16 columns, and
+  // lane j receives column j of the four rows).
+  auto pv = [&](const uint8_t* tl, int slot) {
+    const float* al_s = alpha_slot(L, slot);
+    if (reinterpret_cast<const int*>(al_s + 64)[g]) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 al = *reinterpret_cast<const f32x4*>(al_s + g * 32 + 8 * j + 4 * hb);
+#pragma unroll
+        for (int ct = 0; ct < (SCORE ? 1 : kColTiles); ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[ct][4 * j + r] *= al[r];
+      }
+    }
+    const bf16x8 pa0 = L.pbuf[((slot * 2 + g) * 2 + 0) * 64 + lane];
+    const bf16x8 pa1 = L.pbuf[((slot * 2 + g) * 2 + 1) * 64 + lane];
+    // tile row 16 ks + 8 rd + 4 hb + jj / 4 (read rd of k step ks) is LDS
+    // row 16 ks + 4 (jj / 4) + 2 rd + hb
+    const int jj = lane & 15;
+    const uint8_t* vp = tl + (4 * (jj >> 2) + hb) * kRowLds + (hx * 256 + 16 * ((lane >> 4) & 1) + 4 * (jj & 3)) * 2;
+    constexpr int kAhead = 4;
+    // operand n: k step n / 8, column tile n % 8 (consecutive MFMAs update
+    // different accumulators)
+    auto vread = [&](int n) {
+      const uint8_t* p = vp + (n >> 3) * 16 * kRowLds + (n & 7) * 64;
+      return join(lds_read_tr16(p), lds_read_tr16(p + 2 * kRowLds));
+    };
+    bf16x8 vb[kAhead];
+#pragma unroll
+    for (int n = 0; n < kAhead; ++n) vb[n] = vread(n);
+#pragma unroll
+    for (int n = 0; n < 2 * kColTiles; ++n) {
+      const bf16x8 v = vb[n % kAhead];
+      if (n + kAhead < 2 * kColTiles) vb[n % kAhead] = vread(n + kAhead);
+      const int ct = (n & 7) < (SCORE ? 1 : kColTiles) ? (n & 7) : 0;
+      o[ct] = mfma32((n >> 3) ? pa1 : pa0, v, o[ct]);
+    }
+  };
+
+  if (any_usable) {
+    if (SCORE) {
+      const uint16_t* qp = a.q + ((int64_t)t * a.H + head0 + l32) * kD + hx * 288 + 8 * hb;
+#pragma unroll
+      for (int ks = 0; ks < (SCORE ? kQSteps : 1); ++ks) qreg[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
+    }
+    Stage<F> st[S];
+    uint32_t bad[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) bad[s] = stage_load_all<F>(st[s], offs + min(s, ntiles - 1) * kTileRows, a.kv, tid);
+    // tiles 0..2 to LDS buffers 0..2; stage s then gathers tile s + S
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      wait_vmcnt<(S - 1) * kL>();
+      if (s < ntiles) stage_store_masked<F>(st[s], bad[s], tiles + s * kTileLds, tid);
+      bad[s] = stage_load_all<F>(st[s], offs + min(s + S, ntiles - 1) * kTileRows, a.kv, tid);
+    }
+    lds_barrier();
+    if (SCORE) qk(tiles);
+    lds_barrier();
+    if (SCORE) softmax(vmask[0], 0);
+    lds_barrier();  // the sibling has read the partial scores of tile 0
+    if (SCORE && 1 < ntiles) qk(tiles + kTileLds);
+    lds_barrier();
+    // iteration i: tiles i, i+1, i+2 in buffers i % 3 .. ; tile i+3 in stage
+    // stg (= (i+3) % 3 = i % 3); P of tile i in slot i % 3
+    auto iter = [&](int i, int i3, Stage<F>& stg, uint32_t& stg_bad) {
+      uint8_t* b0 = tiles + i3 * kTileLds;                       // tile i
+      uint8_t* b2 = tiles + (i3 == 0 ? 2 : i3 - 1) * kTileLds;   // tile i+2
+      // phase A
+      if (SCORE) {
+        if (i + 1 < ntiles) softmax(vmask[i + 1], i3 == 2 ? 0 : i3 + 1);
+      } else {
+        pv(b0, i3);
+      }
+      lds_barrier();
+      // phase B: the stage first (its gathers have had three iterations to
+      // land), then the score waves' MFMAs
+      wait_vmcnt<(S - 1) * kL>();
+      if (i + 3 < ntiles) stage_store_masked<F>(stg, stg_bad, b0, tid);
+      stg_bad = stage_load_all<F>(stg, offs + min(i + 3 + S, ntiles - 1) * kTileRows, a.kv, tid);
+      if (SCORE && i + 2 < ntiles) qk(b2);
+      lds_barrier();
+    };
+    // Whole trips of three iterations, then the one or two left: a loop body
+    // with conditional iterations would let the compiler's wait counting
+    // assume no newer gathers on the skipped path, and drain every stage.
+    int i = 0;
+#pragma unroll 1
+    for (; i + 3 <= ntiles; i += 3) {
+      iter(i, 0, st[0], bad[0]);
+      iter(i + 1, 1, st[1], bad[1]);
+      iter(i + 2, 2, st[2], bad[2]);
+    }
+    if (i < ntiles) iter(i, 0, st[0], bad[0]);
+    if (i + 1 < ntiles) iter(i + 1, 1, st[1], bad[1]);
+    wait_vmcnt<0>();  // the last gathers (of no tile) are done
+  }
+
+  // m and each k step's l per head, from the score waves
+  if (SCORE) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+    const float l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    if (lane < 32) {
+      L.stats[3 * (32 * g + lane) + 1 + hx] = l;
+      if (hx == 0) L.stats[3 * (32 * g + lane)] = m_run;
+    }
+  }
+  lds_barrier();
+  // O / l as bf16 into the staging area, [64 heads][512 columns]
+  if (!SCORE) {
+    uint16_t* stage_out = reinterpret_cast<uint16_t*>(tiles);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = 32 * g + 8 * j + 4 * hb + r;
+        const float l = L.stats[3 * h + 1] + L.stats[3 * h + 2];
+        const float inv = l > 0.f ? __builtin_amdgcn_rcpf(l) : 0.f;
+#pragma unroll
+        for (int ct = 0; ct < (SCORE ? 1 : kColTiles); ++ct)
+          stage_out[h * kDc + hx * 256 + ct * 32 + l32] = __builtin_bit_cast(uint16_t, (__bf16)(o[ct][4 * j + r] * inv));
+      }
+    }
+  }
+  lds_barrier();
+}
 
 template <int F>
-__global__ __launch_bounds__(kWideThreads, 1) void sparse_mla_wide(MlaArgs a, int n_groups, int T) {
+__global__ __launch_bounds__(kH64Threads, 1) void sparse_mla_h64(MlaArgs a, int n_groups, int T) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  constexpr int NT = kWideThreads;
-  constexpr int STAGES = kWideStages;
+  constexpr int NT = kH64Threads;
   static_assert(NT == kStageThreads, "the gather layout assumes 512 threads");
-  constexpr int kColTiles = 16;                // 256 columns per wave
   const int x = blockIdx.x, sp = blockIdx.z;
   const int t = (x / (8 * n_groups)) * 8 + (x & 7);
   const int grp = (x >> 3) % n_groups;
   if (t >= T) return;                          // padding ids of the XCD-aware layout
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int g = lane >> 4, c16 = lane & 15;
-  const int hg = wave & 3, kh = wave >> 2;     // head group of 16, k / column half
-  const int head0 = grp * 64 + 16 * hg;
-  const int col0 = 256 * kh;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int g = wave & 1;                      // group of 32 heads
+  const int hx = (wave >> 1) & 1;              // score waves: k half; value waves: column half
   const int j_begin = sp * a.rows_per_split;
   const int j_end = min(a.K, j_begin + a.rows_per_split);
   const int ntiles = (j_end - j_begin + kTileRows - 1) / kTileRows;
   int sv0[kIdxBatch];
   preload_indices<NT>(sv0, a.idx + (int64_t)t * a.K, j_begin, j_end, ntiles * kTileRows, tid);
   const RowLoc loc = locate_row(a.cu_q, a.seq_lens, a.B, t);
-  const int b = loc.b, pos = loc.pos;
-  uint8_t* tiles = smem;                                                // kWideBufs tiles
-  f32x4* sbuf = reinterpret_cast<f32x4*>(smem + kWideBufs * kTileLds);  // 2 x partial scores
-  int64_t* offs = reinterpret_cast<int64_t*>(smem + kWideBufs * kTileLds + 2 * kSbufWide);
-  uint32_t* vmask = reinterpret_cast<uint32_t*>(offs + ntiles * kTileRows);  // usable rows per tile
+  H64Lds L;
+  uint8_t* p = smem;
+  L.tiles = p;
+  p += kH64Bufs * kTileLds;
+  L.spart = reinterpret_cast<f32x4*>(p);
+  p += kH64Spart;
+  L.pbuf = reinterpret_cast<bf16x8*>(p);
+  p += 3 * kH64Pslot;
+  L.alpha = reinterpret_cast<float*>(p);
+  p += 3 * kH64Aslot;
+  L.stats = reinterpret_cast<float*>(p);
+  int64_t* offs = reinterpret_cast<int64_t*>(smem + kH64Fixed);
+  uint32_t* vmask = reinterpret_cast<uint32_t*>(offs + ntiles * kTileRows);
   int* wmin = reinterpret_cast<int*>(vmask + ntiles);  // kWaveSlots, then the merge's flag
 
   const int fv = build_offsets<NT>(offs, vmask, wmin, sv0, a.idx + (int64_t)t * a.K, j_begin, j_end,
-                                   ntiles * kTileRows, pos, b, a.page_table, a.pt_stride, a.page_size,
-                                   a.num_pages, a.page_stride, a.row_stride, tid);
+                                   ntiles * kTileRows, loc.pos, loc.b, a.page_table, a.pt_stride,
+                                   a.page_size, a.num_pages, a.page_stride, a.row_stride, tid);
+  const int head0 = grp * 64 + 32 * g;
+  if (wave < 4) h64_role<F, true>(a, L, offs, vmask, t, head0, g, hx, ntiles, fv != INT32_MAX, tid);
+  else h64_role<F, false>(a, L, offs, vmask, t, head0, g, hx, ntiles, fv != INT32_MAX, tid);
 
-  f32x4 o[kColTiles];
-#pragma unroll
-  for (int i = 0; i < kColTiles; ++i) o[i] = f32x4{};
-  float m_run = kNegInf, l_run = 0.f;
-
-  if (fv != INT32_MAX) {
-    constexpr int kQSteps = 9;
-    const int ks0 = 9 * kh;
-    bf16x8 qreg[kQSteps];
-    {
-      const uint16_t* qp = a.q + ((int64_t)t * a.H + head0 + c16) * kD + g * 8 + ks0 * 32;
-#pragma unroll
-      for (int ks = 0; ks < kQSteps; ++ks) qreg[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32);
-    }
-    // Partial S^T of a tile over this wave's k half: accumulator r of lane =
-    // tile row nt*16 + 4g + r, head c16.
-    auto qk = [&](const uint8_t* tl, f32x4& p0, f32x4& p1) {
-      constexpr int kQkAhead = 3;
-      p0 = f32x4{};
-      p1 = f32x4{};
-      const uint8_t* ap = tl + c16 * kRowLds + g * 16 + ks0 * 64;
-      bf16x8 ra0[kQkAhead], ra1[kQkAhead];
-#pragma unroll
-      for (int k = 0; k < kQkAhead; ++k) {
-        ra0[k] = lds16(ap + k * 64);
-        ra1[k] = lds16(ap + 16 * kRowLds + k * 64);
-      }
-#pragma unroll
-      for (int ks = 0; ks < kQSteps; ++ks) {
-        const bf16x8 x0 = ra0[ks % kQkAhead], x1 = ra1[ks % kQkAhead];
-        if (ks + kQkAhead < kQSteps) {
-          ra0[ks % kQkAhead] = lds16(ap + (ks + kQkAhead) * 64);
-          ra1[ks % kQkAhead] = lds16(ap + 16 * kRowLds + (ks + kQkAhead) * 64);
-        }
-        p0 = mfma16(x0, qreg[ks], p0);
-        p1 = mfma16(x1, qreg[ks], p1);
-      }
-    };
-    auto write_partials = [&](int i, const f32x4& p0, const f32x4& p1) {
-      f32x4* sb = sbuf + (i & 1) * (2 * NT);
-      sb[(2 * wave) * 64 + lane] = p0;
-      sb[(2 * wave + 1) * 64 + lane] = p1;
-    };
-    // O[:, col0 + 16 i .. +16] += P V.  k slot (g, e) <-> tile row 4g + e,
-    // (g, 4 + e) <-> 16 + 4g + e, matching the S^T accumulator rows.
-    auto pv = [&](const uint8_t* tl, const bf16x8& pa) {
-      const uint8_t* vp = tl + (4 * g + (c16 >> 2)) * kRowLds + (col0 + 4 * (c16 & 3)) * 2;
-      constexpr int kPvAhead = 4;
-      bf16x8 vb[kPvAhead];  // both 16-row halves of a column tile, joined as they are read
-#pragma unroll
-      for (int k = 0; k < kPvAhead; ++k)
-        vb[k] = join(lds_read_tr16(vp + k * 32), lds_read_tr16(vp + 16 * kRowLds + k * 32));
-#pragma unroll
-      for (int i2 = 0; i2 < kColTiles; ++i2) {
-        const bf16x8 v = vb[i2 % kPvAhead];
-        if (i2 + kPvAhead < kColTiles)
-          vb[i2 % kPvAhead] = join(lds_read_tr16(vp + (i2 + kPvAhead) * 32),
-                                   lds_read_tr16(vp + 16 * kRowLds + (i2 + kPvAhead) * 32));
-        o[i2] = mfma16(pa, v, o[i2]);
-      }
-    };
-    // Iteration i: tiles i and i+1 are in LDS buffers b0 and b1, and tile i's
-    // partial scores are exchanged; tile i+2 goes to buffer b2 from stage
-    // st_next (i % 2).  The QK of tile i+1 and the store of tile i+2 also run
-    // past the last tile (on buffers no longer read; their results are dropped).
-    auto iter = [&](int i, Stage<F>& st_next, uint8_t* b0, uint8_t* b1, uint8_t* b2) {
-      const f32x4* sb = sbuf + (i & 1) * (2 * NT);
-      // same summation order in both siblings: k half 0, then k half 1
-      const f32x4 s0 = sb[(2 * hg) * 64 + lane] + sb[(2 * (hg + 4)) * 64 + lane];
-      const f32x4 s1 = sb[(2 * hg + 1) * 64 + lane] + sb[(2 * (hg + 4) + 1) * 64 + lane];
-      {
-        f32x4 p0, p1;
-        qk(b1, p0, p1);
-        write_partials(i + 1, p0, p1);
-      }
-      const bf16x8 pa = tile_softmax(s0, s1, vmask[i], a.scale_log2, m_run, l_run, o);
-      pv(b0, pa);
-      stage_store<F>(st_next, b2, tid);
-      if (i + 2 + STAGES < ntiles) stage_load<F>(st_next, offs + (i + 2 + STAGES) * kTileRows, a.kv, tid);
-      lds_barrier();
-    };
-    Stage<F> st[STAGES];
-#pragma unroll
-    for (int s = 0; s < STAGES; ++s)
-      if (s < ntiles) stage_load<F>(st[s], offs + s * kTileRows, a.kv, tid);
-    // tiles 0 and 1 to LDS, then tile 0's partial scores
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      stage_store<F>(st[s], tiles + s * kTileLds, tid);
-      if (s + STAGES < ntiles) stage_load<F>(st[s], offs + (s + STAGES) * kTileRows, a.kv, tid);
-    }
-    lds_barrier();
-    {
-      f32x4 p0, p1;
-      qk(tiles, p0, p1);
-      write_partials(0, p0, p1);
-    }
-    lds_barrier();
-    // buffers of tiles i, i+1, i+2 rotate; stage (i+2) % 2 == i % 2
-    uint8_t* b0 = tiles;
-    uint8_t* b1 = tiles + kTileLds;
-    uint8_t* b2 = tiles + 2 * kTileLds;
-#pragma unroll 1
-    for (int i = 0; i < ntiles; i += 2) {
-      iter(i, st[0], b0, b1, b2);
-      if (i + 1 < ntiles) iter(i + 1, st[1], b1, b2, b0);
-      uint8_t* const nb = b0;  // advance by two tiles
-      b0 = b2;
-      b2 = b1;
-      b1 = nb;
-    }
-  }
-
-  l_run = sum_over_groups(l_run);
-  // O accumulator r of lane: head 4g + r, column col0 + 16 i + c16.
+  const uint16_t* stage_out = reinterpret_cast<const uint16_t*>(L.tiles);
+  constexpr int kChunks = 64 * kDc * 2 / 16 / NT;  // 16-byte chunks per thread
   if (a.splits == 1) {
+    uint16_t* outp = a.out + ((int64_t)t * a.H + grp * 64) * kDc;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int h = 4 * g + r;
-      const float lh = __shfl(l_run, h);
-      const float inv = lh > 0.f ? 1.f / lh : 0.f;
-      uint16_t* op = a.out + ((int64_t)t * a.H + head0 + h) * kDc + col0 + c16;
-#pragma unroll
-      for (int i2 = 0; i2 < kColTiles; ++i2)
-        op[16 * i2] = __builtin_bit_cast(uint16_t, (__bf16)(o[i2][r] * inv));
+    for (int u = 0; u < kChunks; ++u) {
+      const int c = tid + u * NT;
+      *reinterpret_cast<u32x4*>(outp + c * 8) = *reinterpret_cast<const u32x4*>(stage_out + c * 8);
     }
-    if (a.lse != nullptr && kh == 0 && lane < 16)
-      a.lse[(int64_t)t * a.H + head0 + lane] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : kNegInf;
+    if (a.lse != nullptr && tid < 64) {
+      const float m = L.stats[3 * tid], l = L.stats[3 * tid + 1] + L.stats[3 * tid + 2];
+      a.lse[(int64_t)t * a.H + grp * 64 + tid] = l > 0.f ? (m + __log2f(l)) * kLn2 : kNegInf;
+    }
   } else {
-    // layout of the 64-head partials: tile slot (16 heads of group hg) x 32 + column tile
-    store_partials<64, kColTiles>(a, t, grp, n_groups, sp, hg * 32 + kColTiles * kh, lane, o, m_run, l_run,
-                                  kh == 0 ? 16 * hg : -1);
-    merge_splits_if_last<true, NT>(a, t, grp, n_groups, a.counters + (int64_t)t * n_groups + grp,
-                                   reinterpret_cast<float*>(tiles), wmin + kWaveSlots, tid);
+    const __amdgpu_buffer_rsrc_t rs = split_blocks(a, t, grp, n_groups, 64);
+    const int base = sp * kPartBytes(64);
+#pragma unroll
+    for (int u = 0; u < kChunks; ++u) {
+      const int c = tid + u * NT;
+      __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(stage_out + c * 8), rs,
+                                             base + c * 16, 0, kSc1);
+    }
+    if (tid < 64) {
+      const uint2 ml{__float_as_uint(L.stats[3 * tid]),
+                     __float_as_uint(L.stats[3 * tid + 1] + L.stats[3 * tid + 2])};
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((__vector_size__(2 * sizeof(int)))) int, ml),
+                                            rs, base + 64 * kDc * 2 + 8 * tid, 0, kSc1);
+    }
+    // the merge's weights overwrite the staging area only after every
+    // thread's copy out of it is complete (it waits and synchronises first)
+    merge_splits_h64<NT>(a, t, grp, n_groups, a.counters + (int64_t)t * n_groups + grp,
+                         reinterpret_cast<float*>(L.tiles), wmin + kWaveSlots, tid);
   }
 }
 
@@ -1051,7 +1394,7 @@ hipError_t launch_with_lds(Kernel kernel, dim3 grid, int threads, size_t lds, hi
 }
 
 size_t plan_lds(const MlaPlan& plan, int n_heads) {
-  return n_heads % 64 == 0 ? mla_lds(plan.rows_per_split, (kWideBufs - 1) * kTileLds + 2 * kSbufWide)
+  return n_heads % 64 == 0 ? mla_lds(plan.rows_per_split, kH64Fixed - kTileLds)
                            : mla_lds(plan.rows_per_split, kSbufLds);
 }
 
@@ -1082,9 +1425,9 @@ hipError_t launch_sparse_mla_bf16(const BatchArgs& ba, const void* q, const Pool
   hipError_t e;
   // Tiles of loads in flight per workgroup: two or three.
   if (wide)
-    e = fmt == kFmtFp8    ? launch_with_lds(sparse_mla_wide<kFmtFp8>, grid, kWideThreads, lds, stream, args, n_groups, T)
-        : fmt == kFmtInt8 ? launch_with_lds(sparse_mla_wide<kFmtInt8>, grid, kWideThreads, lds, stream, args, n_groups, T)
-                          : launch_with_lds(sparse_mla_wide<kFmtBf16>, grid, kWideThreads, lds, stream, args, n_groups, T);
+    e = fmt == kFmtFp8    ? launch_with_lds(sparse_mla_h64<kFmtFp8>, grid, kH64Threads, lds, stream, args, n_groups, T)
+        : fmt == kFmtInt8 ? launch_with_lds(sparse_mla_h64<kFmtInt8>, grid, kH64Threads, lds, stream, args, n_groups, T)
+                          : launch_with_lds(sparse_mla_h64<kFmtBf16>, grid, kH64Threads, lds, stream, args, n_groups, T);
   else if (fmt == kFmtFp8)
     e = launch_with_lds(sparse_mla_q16<kFmtFp8, 2, 2>, grid, kThreads, lds, stream, args, n_groups, T);
   else if (fmt == kFmtInt8)
