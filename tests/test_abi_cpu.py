@@ -245,21 +245,25 @@ def test_sparse_mla_validation():
     assert dsa.dsa_sparse_mla_workspace_bytes(4096, 128, 2048, 512, False) == 0
 
 
+MAX64 = 2624   # rows one 64-head workgroup can attend (documented in dsa.h)
+
+
 def test_sparse_mla_refuses_plans_beyond_lds():
-    # 64-head workgroups stage every attended row's offset in LDS: up to 2304
-    # rows per workgroup.  Prefill never splits, so k = 2336 does not fit; it
-    # is refused before any launch, not reported as a failed launch.
-    assert _mla(_batch(), k=2304, prefill=True, q=ODD) == 6            # fits: reaches the later checks
-    assert _mla(_batch(), k=2336, prefill=True) == 3
-    assert _mla(_batch(), k=4096, H=64, prefill=True) == 3
+    # 64-head workgroups stage every attended row's offset in LDS next to their
+    # tile buffers: up to MAX64 rows per workgroup.  Prefill never splits, so
+    # k = MAX64 + 32 does not fit; it is refused before any launch, not
+    # reported as a failed launch.
+    assert _mla(_batch(), k=MAX64, prefill=True, q=ODD) == 6            # fits: reaches the later checks
+    assert _mla(_batch(), k=MAX64 + 32, prefill=True) == 3
+    assert _mla(_batch(), k=8192, H=64, prefill=True) == 3
     # decode splits small batches (4 rows: the split plan fits), not large ones
     big = _batch(T=512, B=512, max_q=1)
-    assert dsa.dsa_sparse_mla_workspace_bytes(512, 128, 2336, 512, False) == 0
-    assert _mla(big, k=2336) == 3
-    need = dsa.dsa_sparse_mla_workspace_bytes(4, 128, 2336, 512, False)
-    assert need > 0 and _mla(_batch(), k=2336, ws=FAKE, ws_bytes=need, q=ODD) == 6
+    assert dsa.dsa_sparse_mla_workspace_bytes(512, 128, MAX64 + 32, 512, False) == 0
+    assert _mla(big, k=MAX64 + 32) == 3
+    need = dsa.dsa_sparse_mla_workspace_bytes(4, 128, MAX64 + 32, 512, False)
+    assert need > 0 and _mla(_batch(), k=MAX64 + 32, ws=FAKE, ws_bytes=need, q=ODD) == 6
     # 16-head workgroups keep their own (larger) row budget
-    assert _mla(_batch(), k=2336, H=16, prefill=True, q=ODD) == 6
+    assert _mla(_batch(), k=MAX64 + 32, H=16, prefill=True, q=ODD) == 6
 
 
 @pytest.mark.parametrize("T,H,k", [(64, 16, 2048), (256, 128, 2048), (160, 128, 2048), (8, 16, 64),
@@ -297,7 +301,7 @@ def test_sparse_mla_decode_static_validation():
     assert _mla_static(_batch(), H=24) == 3
     assert _mla_static(_batch(), pool=_pool(dsa.DSA_BF16, 512, 1152)) == 2
     assert _mla_static(_batch(), q=ODD) == 6
-    assert _mla_static(_batch(T=512, B=512, max_q=1), k=2336) == 3
+    assert _mla_static(_batch(T=512, B=512, max_q=1), k=MAX64 + 32) == 3
 
 
 def test_every_split_plan_fits_the_static_array():
