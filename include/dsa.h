@@ -294,8 +294,8 @@ size_t dsa_sparse_mla_workspace_bytes(int32_t num_q_rows, int32_t n_heads, int32
  * dc 512, dr 64, n_heads a multiple of 16 up to 128 (MFMA); q and kv DSA_F32
  * with dc+dr <= 1024, n_heads <= 128, k <= 4096 (vector ALUs).  The MFMA
  * kernels stage the byte offsets of all rows one workgroup attends in LDS:
- * with n_heads a multiple of 64, a workgroup that attends more than 2624 rows
- * (any prefill call with k > 2624; a decode call whose rows are not split,
+ * with n_heads a multiple of 64, a workgroup that attends more than 5184 rows
+ * (any prefill call with k > 5184; a decode call whose rows are not split,
  * which happens when num_q_rows * n_heads / 64 >= 384) does not fit, and the
  * call returns DSA_ERR_UNSUPPORTED before launching anything.
  * _decode and _prefill compute the same function; they differ only in how

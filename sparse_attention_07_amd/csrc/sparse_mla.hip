@@ -136,69 +136,38 @@ __device__ inline uint2 decode4(uint32_t x, float sc, float bi) {
   return u8x4_to_bf16x4(x, sc, bi);
 }
 
-// One tile's rows in flight in registers, for a workgroup of 512 threads.
-// Each thread keeps one chunk column, so its items differ only by row: bf16
-// rows -- latent chunk tid%64 (16 B) of rows tid/64 + 8k, k < 4; 8-bit rows --
-// latent chunk tid%32 (16 codes, with its block scale and bias) of rows
-// tid/32 + 16k, k < 2.  Every thread also loads 8 bytes of rope (bf16 dims
-// 4(tid%16) .. +3 of row tid/16).  A wave reads 1 KB (bf16) or 512 B (8-bit)
-// contiguous of a row per latent load.
-constexpr int kStageThreads = 512;
+// One tile's latent rows in flight in the registers of the 64-head kernel's
+// two gather waves (128 threads, gt = thread - 256): bf16 rows -- latent
+// chunk gt % 64 (16 B) of rows gt / 64 + 2k, k < 16; 8-bit rows -- latent
+// chunk gt % 32 (16 codes, with its block scale and bias) of rows gt / 32 +
+// 4k, k < 8.  Each load of a wave reads 1 KB of one row (bf16) or 512 B of
+// each of two rows (8-bit).  The rope of a tile is gathered by the value
+// waves (one 16-byte chunk per thread).
+constexpr int kGatherThreads = 128;
 
 template <int F>
 struct Stage {
-  u32x4 lat[kQ8<F> ? 2 : 4];
-  float sc[kQ8<F> ? 2 : 1];
-  float bi[F == kFmtInt8 ? 2 : 1];
-  uint2 rope;
+  static constexpr int kLat = kQ8<F> ? 8 : 16;   // latent items
+  static constexpr int kStep = kQ8<F> ? 4 : 2;   // row step between items
+  u32x4 lat[kLat];
+  float sc[kQ8<F> ? kLat : 1];
+  float bi[F == kFmtInt8 ? kLat : 1];
 };
 
 __device__ inline u32x4 ld_global16(const uint8_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Registers of a stage into one LDS tile buffer (row-major rows of
+// kRowLds bytes: latent as bf16 at bytes 0..1023, rope at 1024..1151);
+// 8-bit codes are decoded here.
 template <int F>
-__device__ inline void stage_load(Stage<F>& st, const int64_t* toffs, const uint8_t* kv, int tid) {
+__device__ inline void stage_store(const Stage<F>& st, uint8_t* tile, int gt) {
   constexpr bool Q8 = kQ8<F>;
-  constexpr int kLat = Q8 ? 2 : 4, kStep = Q8 ? 16 : 8;
-  const int ch = Q8 ? (tid & 31) : (tid & 63);
-  const int r0 = Q8 ? (tid >> 5) : (tid >> 6);
-  int64_t off[kLat];
-#pragma unroll
-  for (int k = 0; k < kLat; ++k) off[k] = toffs[r0 + kStep * k];
-  const int64_t roff = toffs[tid >> 4];
+  constexpr int kLat = Stage<F>::kLat, kStep = Stage<F>::kStep;
+  const int ch = Q8 ? (gt & 31) : (gt & 63);
+  const int r0 = Q8 ? (gt >> 5) : (gt >> 6);
 #pragma unroll
   for (int k = 0; k < kLat; ++k) {
-    st.lat[k] = u32x4{};
-    if (Q8) st.sc[k] = 0.f;
-    if (F == kFmtInt8) st.bi[k] = 0.f;
-    if (off[k] >= 0) {
-      st.lat[k] = ld_global16(kv + off[k] + ch * 16);
-      if (Q8) st.sc[k] = *reinterpret_cast<const float*>(kv + off[k] + 512 + (ch >> 3) * 4);
-      if (F == kFmtInt8) st.bi[k] = *reinterpret_cast<const float*>(kv + off[k] + 528 + (ch >> 3) * 4);
-    }
-  }
-  st.rope = uint2{0u, 0u};
-  if (roff >= 0) st.rope = *reinterpret_cast<const uint2*>(kv + roff + kRopeOff<F> + (tid & 15) * 8);
-}
-
-// LDS row of tile row a (0..31): a = 16h + 8j + 4b + m is stored at row
-// 16h + 4m + 2j + b.  The four tile rows one ds_read_b64_tr_b16 of the PV
-// operand fetches together (m = 0..3) then sit four LDS rows apart, which
-// with the 1168-byte row stride puts them in disjoint banks, while any 16
-// consecutive tile rows still fill 16 distinct 16-byte bank slots (QK
-// operand reads).
-__host__ __device__ constexpr int lds_row(int a) {
-  return (a & 16) | ((a & 3) << 2) | (((a >> 3) & 1) << 1) | ((a >> 2) & 1);
-}
-
-template <int F>
-__device__ inline void stage_store(const Stage<F>& st, uint8_t* tile, int tid) {
-  constexpr bool Q8 = kQ8<F>;
-  constexpr int kLat = Q8 ? 2 : 4, kStep = Q8 ? 16 : 8;
-  const int ch = Q8 ? (tid & 31) : (tid & 63);
-  const int r0 = Q8 ? (tid >> 5) : (tid >> 6);
-#pragma unroll
-  for (int k = 0; k < kLat; ++k) {
-    uint8_t* dst = tile + lds_row(r0 + kStep * k) * kRowLds;
+    uint8_t* dst = tile + (r0 + kStep * k) * kRowLds;
     if (!Q8) {
       *reinterpret_cast<u32x4*>(dst + ch * 16) = st.lat[k];
     } else {
@@ -213,7 +182,6 @@ __device__ inline void stage_store(const Stage<F>& st, uint8_t* tile, int tid) {
       *reinterpret_cast<u32x4*>(dst + ch * 32 + 16) = hi;
     }
   }
-  *reinterpret_cast<uint2*>(tile + lds_row(tid >> 4) * kRowLds + 1024 + (tid & 15) * 8) = st.rope;
 }
 
 // Prologue: byte offsets of the range's rows (page table applied; -1 when not
@@ -592,108 +560,115 @@ __device__ inline void merge_splits_if_last(const MlaArgs& a, int t, int grp, in
 // ---------------------------------------------------------------- 64 heads, 8 waves
 
 // A workgroup owns 64 heads of one query row and one range of its selected
-// rows.  The heads form two groups of 32, each the M (or N) side of
-// v_mfma_f32_32x32x16_bf16, so one 1 KB operand read from LDS feeds 32 heads
-// (twice what a 16-head MFMA gets from it).  Eight waves, two per SIMD, in
-// two roles:
-// * Score waves 0..3 (group g = w & 1, k half kh = w >> 1): S^T = rows x q^T
-//   over their half of the 576 dims, with that half of q (32 heads x 288
-//   dims: 72 VGPRs) held as the B operand and the tile rows read from LDS as
-//   the A operand.  Each wave scales its partial scores and publishes them
-//   through LDS; both siblings then add the two halves (the same sum in
-//   both), take the same tile maximum and rescale decision, and each computes
-//   the probabilities of one of the tile's two 16-row k steps, published as
-//   bf16 already in the PV operand layout (kh = 0 also publishes the rescale
-//   factors).
-// * Value waves 4..7 (group g = w & 1, column half ch = (w >> 1) & 1): O +=
-//   P V for their 32 heads and 256 columns (128 accumulator registers), P
-//   read from LDS, V read transposed from the tile with ds_read_b64_tr_b16.
-// Wave w and wave w + 4 share a SIMD.  An iteration has two phases, each
-// pairing one wave's matrix work with the other's vector work:
-//   phase A  score waves: softmax of tile i+1 (VALU);
-//            value waves: PV of tile i (MFMA)
-//   phase B  every thread: tile i+3 stored from registers into the LDS
-//            buffer tile i used, then the gathers of tile i+3+S issued;
-//            then score waves: QK of tile i+2 (MFMA)
-// Three LDS tile buffers (tile j in buffer j % 3) and S = 3 register stages
-// of gathers (tile j in stage j % 3), so a tile's gathers have three
-// iterations to land.  P and the rescale factors rotate over three LDS slots
-// with the tiles.  The gathers are branch-free (an unusable row loads the
-// pool's first row and is zeroed when stored), so each stage store waits for
-// exactly its own loads.
+// rows, with eight waves in three roles.  Waves w and w + 4 share a SIMD
+// (waves 0..3 sit on four distinct SIMDs), so the roles are placed to give
+// every SIMD about the same MFMA time per 32-row tile:
+// * score waves 0, 1 (head block g = w, 32 heads): S^T = K Q^T for all 32
+//   tile rows on v_mfma_f32_32x32x16_bf16 over the 576 dims (36 MFMAs), q
+//   held as the B operand (144 VGPRs).  Each lane then holds 16 of the 32
+//   rows of one head, so the tile maximum needs one permlane swap and no
+//   LDS exchange; the wave takes the online-softmax step for its heads and
+//   writes P (bf16) and the rescale factors into LDS.
+// * value waves 2, 3, 6, 7 (column quarter cq): O += P V for all 64 heads
+//   and 128 columns (16 MFMAs, 128 accumulator registers), V read once per
+//   tile with ds_read_b64_tr_b16.
+// * gather waves 4, 5: the tiles' latent gathers, three tiles in flight in
+//   registers (one stage per tile), stored into the LDS tile buffers; the
+//   value waves gather the rope (16 B per thread per tile) the same way.
+// Per phase i (each ends with a barrier): score waves QK + softmax of tile
+// i+1; value waves PV of tile i; gather and value waves store tile i+2
+// (waiting for exactly its loads) and issue the gathers of tile i+5.  Tile j lives in LDS
+// buffer j % 3 and register stage j % 3; P and rescale factors of tile j in
+// slot j % 2.  The gathers are branch-free (an unusable row loads the pool's
+// first row, and the tile's unusable rows are zeroed in LDS when it is stored).
 //
 // The output (O / l, bf16) is staged in LDS as [head][column] and written
 // with 16-byte stores: to `out` when the rows are not split, else to the
 // split's partial block, which the last split to finish merges.
 constexpr int kH64Threads = 512;
-constexpr int kH64Stages = 3;                        // register stages of gathers
 constexpr int kH64Bufs = 3;                          // LDS tile buffers
-constexpr int kH64Spart = 4 * 16 * 64 * 4;           // partial scores of the 4 score waves
-constexpr int kH64Pslot = 2 * 2 * 64 * 16;           // P per slot: [group][k step][64 lanes] x 16 B
-constexpr int kH64Aslot = 2 * 32 * 4 + 16;           // rescale factors per slot: [group][32], 2 flags
-constexpr int kH64Stats = 64 * 12;                   // per head: m, then l of each k step half
-constexpr int kH64Fixed =
-    kH64Bufs * kTileLds + kH64Spart + 3 * kH64Pslot + 3 * kH64Aslot + kH64Stats;
-static_assert(kH64Fixed % 16 == 0 && kH64Aslot % 16 == 0, "16-byte aligned regions");
+constexpr int kH64Stages = 3;                        // register stages of the gather waves
+constexpr int kH64Pslot = 64 * 32 * 2;               // P of one tile: [row half][k step][64 heads][8] bf16
+constexpr int kH64Aslot = 64 * 4 + 16;               // rescale factors [64 heads], then 2 flags
+constexpr int kH64Stats = 64 * 12;                   // per head: m, l, 0
+constexpr int kH64Fixed = kH64Bufs * kTileLds + 2 * kH64Pslot + 2 * kH64Aslot + kH64Stats;
+static_assert(kH64Fixed % 16 == 0 && kH64Aslot % 16 == 0 && kH64Pslot % 16 == 0, "16-byte aligned regions");
 static_assert(kH64Bufs * kTileLds >= 64 * kDc * 2, "the output staging fits the tile buffers");
 
-// Loads per thread per gather stage (they are all issued together).
+// Loads per gather thread per stage (they are all issued together).
 template <int F>
-constexpr int kStageLoads = F == kFmtBf16 ? 5 : (F == kFmtFp8 ? 5 : 7);
+constexpr int kStageLoads = F == kFmtBf16 ? 16 : (F == kFmtFp8 ? 16 : 24);
 
 // One tile's gathers, branch-free: an unusable row (offset < 0) loads the
-// pool's first row instead.  Returns the thread's unusable-row bits (bit k:
-// latent item k, bit 4: rope) for stage_store_masked.
+// pool's first row instead (zeroed when the tile is stored).
 template <int F>
-__device__ inline uint32_t stage_load_all(Stage<F>& st, const int64_t* toffs, const uint8_t* kv, int tid) {
+__device__ inline void stage_load_all(Stage<F>& st, const int64_t* toffs, const uint8_t* kv, int gt) {
   constexpr bool Q8 = kQ8<F>;
-  constexpr int kLat = Q8 ? 2 : 4, kStep = Q8 ? 16 : 8;
-  const int ch = Q8 ? (tid & 31) : (tid & 63);
-  const int r0 = Q8 ? (tid >> 5) : (tid >> 6);
-  int64_t o[kLat + 1];
+  constexpr int kLat = Stage<F>::kLat, kStep = Stage<F>::kStep;
+  const int ch = Q8 ? (gt & 31) : (gt & 63);
+  const int r0 = Q8 ? (gt >> 5) : (gt >> 6);
+  if (!Q8) {
+    // bf16: a wave's rows r0 + 2k are wave-uniform.  Lane k < 16 reads row
+    // r0 + 2k's offset; each row base then moves to scalar registers, and the
+    // loads take it as their scalar base with a 32-bit lane offset.
+    const int64_t mine = toffs[r0 + 2 * (gt & 15)];
+    const int lo = (int)(uint32_t)mine, hi = (int)(mine >> 32);
 #pragma unroll
-  for (int k = 0; k < kLat; ++k) o[k] = toffs[r0 + kStep * k];
-  o[kLat] = toffs[tid >> 4];
-  uint32_t bad = 0;
-#pragma unroll
-  for (int k = 0; k <= kLat; ++k) {
-    bad |= o[k] < 0 ? (1u << (k < kLat ? k : 4)) : 0u;
-    o[k] = o[k] < 0 ? 0 : o[k];
+    for (int k = 0; k < kLat; ++k) {
+      const int64_t o = ((int64_t)__builtin_amdgcn_readlane(hi, k) << 32) |
+                        (uint32_t)__builtin_amdgcn_readlane(lo, k);
+      st.lat[k] = ld_global16(kv + (o < 0 ? 0 : o) + (uint32_t)(ch * 16));
+    }
+    return;
   }
 #pragma unroll
   for (int k = 0; k < kLat; ++k) {
-    const uint8_t* row = kv + o[k];
+    // at most six rows' addresses live at once (the gather waves hold three
+    // stages in their registers)
+    if (k % 6 == 0 && k > 0) asm volatile("" ::: "memory");
+    const int64_t o = toffs[r0 + kStep * k];
+    const uint8_t* row = kv + (o < 0 ? 0 : o);
     st.lat[k] = ld_global16(row + ch * 16);
     if (Q8) st.sc[k] = *reinterpret_cast<const float*>(row + 512 + (ch >> 3) * 4);
     if (F == kFmtInt8) st.bi[k] = *reinterpret_cast<const float*>(row + 528 + (ch >> 3) * 4);
   }
-  st.rope = *reinterpret_cast<const uint2*>(kv + o[kLat] + kRopeOff<F> + (tid & 15) * 8);
-  return bad;
 }
 
-// stage_store with the unusable rows' values (bits from stage_load_all)
-// replaced by zeros.
+// The rope chunk vt % 8 (bf16 dims 8 (vt % 8) .. +7) of tile row vt / 8, for
+// value-wave thread vt < 256; an unusable row loads the pool's first row.
 template <int F>
-__device__ inline void stage_store_masked(Stage<F>& st, uint32_t bad, uint8_t* tile, int tid) {
+__device__ inline u32x4 rope_load(const int64_t* toffs, const uint8_t* kv, int vt) {
+  const int64_t o = toffs[vt >> 3];
+  return ld_global16(kv + (o < 0 ? 0 : o) + kRopeOff<F> + (vt & 7) * 16);
+}
+
+// ... into the tile buffer, zeros for an unusable row (clear bit of `vm`).
+__device__ inline void rope_store(u32x4 x, uint32_t vm, uint8_t* tile, int vt) {
+  const int r = vt >> 3;
+  *reinterpret_cast<u32x4*>(tile + r * kRowLds + 1024 + (vt & 7) * 16) = ((vm >> r) & 1u) ? x : u32x4{};
+}
+
+// stage_store, then zeros over this thread's latent items of the unusable
+// rows (clear bits of the tile's usable-row mask `vm`).
+template <int F>
+__device__ inline void stage_store_masked(const Stage<F>& st, uint32_t vm, uint8_t* tile, int gt) {
   constexpr bool Q8 = kQ8<F>;
-  constexpr int kLat = Q8 ? 2 : 4;
-  if (bad != 0) {
+  stage_store<F>(st, tile, gt);
+  if (vm != 0xFFFFFFFFu) {
+    constexpr int kLat = Stage<F>::kLat, kStep = Stage<F>::kStep;
+    const int ch = Q8 ? (gt & 31) : (gt & 63);
+    const int r0 = Q8 ? (gt >> 5) : (gt >> 6);
 #pragma unroll
     for (int k = 0; k < kLat; ++k) {
-      if ((bad >> k) & 1u) {
-        st.lat[k] = u32x4{};
-        if (Q8) st.sc[k] = 0.f;
-        if (F == kFmtInt8) st.bi[k] = 0.f;
+      const int r = r0 + kStep * k;
+      if (!((vm >> r) & 1u)) {
+        uint8_t* dst = tile + r * kRowLds + ch * (Q8 ? 32 : 16);
+        *reinterpret_cast<u32x4*>(dst) = u32x4{};
+        if (Q8) *reinterpret_cast<u32x4*>(dst + 16) = u32x4{};
       }
     }
-    if ((bad >> 4) & 1u) st.rope = uint2{0u, 0u};
   }
-  stage_store<F>(st, tile, tid);
 }
-
-// 32x32 accumulator layout (v_mfma_f32_32x32x16_bf16): register i of lane l
-// holds row 8(i/4) + 4(l/32) + i%4 and column l%32.
-__device__ inline int acc32_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
 
 // Merge of the split partials of one (row, 64-head group) by the last split
 // to arrive (called by every thread after its split's block is stored).  A
@@ -780,165 +755,168 @@ __device__ inline void merge_splits_h64(const MlaArgs& a, int t, int grp, int n_
   if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// LDS regions of the 64-head kernel, shared by both roles.
+// LDS regions of the 64-head kernel.
 struct H64Lds {
   uint8_t* tiles;   // three tile buffers; at the end, the output staging area
-  f32x4* spart;     // scaled partial scores: [score wave][4][64 lanes]
-  bf16x8* pbuf;     // P: [slot][group][k step][64 lanes]
-  float* alpha;     // rescale factors: [slot] -> [group][32 heads], then 2 flags
-  float* stats;     // per head: m, l of k step 0, l of k step 1
+  uint8_t* pbuf;    // P, two slots of kH64Pslot bytes
+  float* alpha;     // rescale factors, two slots: [64 heads], then 2 int flags (per head block)
+  float* stats;     // per head: m, l, 0
 };
 
-__device__ inline float* alpha_slot(const H64Lds& L, int slot) {
-  return L.alpha + slot * (kH64Aslot / 4);
+__device__ inline float* alpha_slot(const H64Lds& L, int slot) { return L.alpha + slot * (kH64Aslot / 4); }
+__device__ inline int* flag_slot(const H64Lds& L, int slot) {
+  return reinterpret_cast<int*>(alpha_slot(L, slot) + 64);
 }
 
-// The tile pipeline of one role (the two roles run the same barriers in the
+// Byte offset in a P slot of the 8 bf16 that score lane (head, row half hb)
+// holds for k step ks of the PV operand: [hb][ks][64 heads][8], so the score
+// waves' writes and the value waves' operand reads are lane-linear 16-byte
+// accesses.
+__device__ inline int p_off(int hb, int ks, int head) { return ((hb * 2 + ks) * 64 + head) * 16; }
+
+// Max / sum of a lane's value and that of the lane 32 away (one permlane swap;
+// both lanes get the same result).
+__device__ inline float max_over_halves(float x) {
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float sum_over_halves(float x) {
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+constexpr int kRoleScore = 0, kRoleValue = 1, kRoleGather = 2;
+
+// The tile pipeline of one role (every role runs the same barriers in the
 // same order), then its part of the epilogue: the score waves publish (m, l)
 // per head, the value waves write O / l as bf16 [64 heads][512 columns] into
 // the staging area.  Every register array lives in one role only.
-template <int F, bool SCORE>
+template <int F, int ROLE>
 __device__ inline void h64_role(const MlaArgs& a, const H64Lds& L, const int64_t* offs,
-                                const uint32_t* vmask, int t, int head0, int g, int hx, int ntiles,
-                                bool any_usable, int tid) {
-  constexpr int S = kH64Stages;
+                                const uint32_t* vmask, int t, int grp, int ntiles, bool any_usable,
+                                int tid) {
+  constexpr bool S = ROLE == kRoleScore, V = ROLE == kRoleValue, G = ROLE == kRoleGather;
+  static_assert(kH64Bufs == 3 && kH64Stages == 3, "the tile loop is unrolled for three buffers and stages");
+  constexpr int kQSteps = 36;                  // k steps of 16 over the 576 dims
+  constexpr int kColTiles = 4;                 // value waves: 128 columns in tiles of 32
   constexpr int kL = kStageLoads<F>;
-  static_assert(S == 3 && kH64Bufs == 3, "the tile loop is unrolled for three buffers and stages");
-  constexpr int kQSteps = 18;                  // k steps of 16 per half of the 576 dims
-  constexpr int kColTiles = 8;                 // value waves: 256 columns in tiles of 32
   const int lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, hb = lane >> 5;
+  const int l32 = lane & 31, hb = lane >> 5;   // 32x32 layouts: column, lane half
   uint8_t* tiles = L.tiles;
 
-  // score waves: q half, own scaled partial scores, running max and the sum
-  // of this lane's probabilities of its k step
-  bf16x8 qreg[SCORE ? kQSteps : 1];
-  f32x16 own = f32x16{};
-  float m_run = kNegInf, l_run = 0.f;
-  // value waves: the accumulators
-  f32x16 o[SCORE ? 1 : kColTiles];
+  // ---- score waves: head block g (32 heads)
+  const int g = wave & 1;
+  bf16x8 q[S ? kQSteps : 1];                   // lane: head 32 g + l32, dims 16 ks + 8 hb .. +7
+  float m_run = kNegInf;                       // running max (log2 units) of head 32 g + l32
+  float l_run = 0.f;                           // this lane's share of that head's sum
+  // ---- value waves: column quarter cq
+  const int cq = (wave & 1) | ((wave >> 1) & 2);
+  f32x16 o[V ? 2 : 1][V ? kColTiles : 1];
 #pragma unroll
-  for (int i = 0; i < (SCORE ? 1 : kColTiles); ++i) o[i] = f32x16{};
+  for (int mb = 0; mb < (V ? 2 : 1); ++mb)
+#pragma unroll
+    for (int ct = 0; ct < (V ? kColTiles : 1); ++ct) o[mb][ct] = f32x16{};
+  u32x4 rs[V ? kH64Stages : 1];                // rope of the tiles in flight (value waves)
+  const int vt = cq * 64 + lane;
+  // ---- gather waves
+  const int gt = tid - 4 * 64;
+  Stage<F> st[G ? kH64Stages : 1];
 
-  // Score waves: this wave's partial S^T of a tile times the softmax scale
-  // (accumulator register i: tile row acc32_row(i, lane), head l32), kept in
-  // `own` and written to LDS for the sibling.
-  // Two accumulators (even and odd k steps) keep consecutive MFMAs
-  // independent; operands are read from LDS six k steps ahead.
-  auto qk = [&](const uint8_t* tl) {
-    constexpr int kAhead = 6;
-    f32x16 acc0 = f32x16{}, acc1 = f32x16{};
-    const uint8_t* ap = tl + lds_row(l32) * kRowLds + (hx * 288 + 8 * hb) * 2;
+  // Score waves: S^T of the tile (A operand: lane row l32, dims 16 ks + 8 hb
+  // .. +7, read from LDS eight k steps ahead; B: q); then the online-softmax
+  // step.  D lane (l32, hb) register i holds
+  // tile row 8 (i / 4) + 4 hb + i % 4 of head 32 g + l32.  The running max is
+  // raised (O and l rescaled) only when the tile beats it by more than
+  // kRescaleSlack; the decision is taken per wave, and the factors (1 for
+  // heads not raised) go to LDS with a flag.  P goes to `slot` as bf16,
+  // registers 8 ks .. 8 ks + 7 as k step ks of the PV operand.
+  auto qk_softmax = [&](const uint8_t* tl, uint32_t valid, int slot) {
+    constexpr int kAhead = 8;
+    const uint8_t* ap = tl + l32 * kRowLds + 16 * hb;
     bf16x8 ra[kAhead];
 #pragma unroll
-    for (int k = 0; k < kAhead; ++k) ra[k] = lds16(ap + k * 32);
+    for (int k = 0; k < kAhead; ++k) ra[k] = lds16(ap + 32 * k);
+    f32x16 c = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < kQSteps; ++ks) {
       const bf16x8 av = ra[ks % kAhead];
-      if (ks + kAhead < kQSteps) ra[ks % kAhead] = lds16(ap + (ks + kAhead) * 32);
-      const bf16x8 qv = qreg[ks < (SCORE ? kQSteps : 1) ? ks : 0];
-      if (ks & 1) acc1 = mfma32(av, qv, acc1);
-      else acc0 = mfma32(av, qv, acc0);
+      if (ks + kAhead < kQSteps) ra[ks % kAhead] = lds16(ap + 32 * (ks + kAhead));
+      c = mfma32(av, q[S ? ks : 0], c);
     }
+    float sv[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) own[i] = (acc0[i] + acc1[i]) * a.scale_log2;
+    for (int i = 0; i < 16; ++i) sv[i] = c[i] * a.scale_log2;
+    if (valid != 0xFFFFFFFFu) {                // a partial tile (uniform branch)
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      L.spart[(wave * 4 + r) * 64 + lane] = f32x4{own[4 * r], own[4 * r + 1], own[4 * r + 2], own[4 * r + 3]};
-  };
-  // Score waves: the tile's full scores (own half + sibling's half: the same
-  // sum in both siblings), online softmax over the tile, this wave's k step
-  // (hx) of P published into `slot`.  P's k slot e of k step ks (lane half
-  // hb) is tile row 16 ks + 8 (e / 4) + 4 hb + e % 4: exactly accumulator
-  // register 8 ks + e.
-  auto softmax = [&](uint32_t valid, int slot) {
-    float xv[16];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const f32x4 other = L.spart[((wave ^ 2) * 4 + r) * 64 + lane];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) xv[4 * r + e] = own[4 * r + e] + other[e];
+      for (int i = 0; i < 16; ++i) {
+        const int row = 8 * (i >> 2) + 4 * hb + (i & 3);
+        if (!((valid >> row) & 1u)) sv[i] = kNegInf;
+      }
     }
-    const bool full = valid == 0xFFFFFFFFu;   // wave-uniform
-    if (!full) {
+    float m = sv[0];
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (!((valid >> acc32_row(i, lane)) & 1u)) xv[i] = kNegInf;
-    }
-    float mt = xv[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mt = fmaxf(mt, xv[i]);
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
-      mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    const bool raise = mt > m_run + kRescaleSlack;
+    for (int i = 1; i < 16; ++i) m = fmaxf(m, sv[i]);
+    m = max_over_halves(m);
+    const bool raise = m > m_run + kRescaleSlack;
     const bool any_raise = __any(raise);
-    float al = 1.f;
     if (any_raise) {
-      const float m_new = raise ? mt : m_run;
-      al = (m_run == kNegInf) ? 0.f : exp2_fast(m_run - m_new);
+      const float m_new = raise ? m : m_run;
+      const float al = (m_run == kNegInf) ? 0.f : exp2_fast(m_run - m_new);
       m_run = m_new;
       l_run *= al;
+      if (hb == 0) alpha_slot(L, slot)[32 * g + l32] = al;
     }
-    // this wave's k step (registers 8 hx .. 8 hx + 7), selected without a
-    // runtime register index (which would put the array in scratch)
-    float xk[8];
+    if (lane == 0) flag_slot(L, slot)[g] = any_raise ? 1 : 0;
+    // exp2(-inf - m) is 0 for a finite m; m_run is -inf only while every
+    // score seen so far is -inf
+    const float mu = m_run == kNegInf ? 0.f : m_run;
+    u32x4 pk[2];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) xk[e] = hx ? xv[8 + e] : xv[e];
-    bf16x8 pa;
-    if (full) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = exp2_fast(xk[e] - m_run);
-        l_run += p;
-        pa[e] = (__bf16)p;
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = xk[e] == kNegInf ? 0.f : exp2_fast(xk[e] - m_run);
-        l_run += p;
-        pa[e] = (__bf16)p;
-      }
+    for (int i = 0; i < 16; i += 2) {
+      const float p0 = exp2_fast(sv[i] - mu), p1 = exp2_fast(sv[i + 1] - mu);
+      l_run += p0 + p1;
+      pk[i >> 3][(i & 7) >> 1] = pack_bf16x2(p0, p1);
     }
-    L.pbuf[((slot * 2 + g) * 2 + hx) * 64 + lane] = pa;
-    if (hx == 0) {
-      float* al_s = alpha_slot(L, slot);
-      if (any_raise && lane < 32) al_s[g * 32 + lane] = al;
-      if (lane == 0) reinterpret_cast<int*>(al_s + 64)[g] = any_raise ? 1 : 0;
-    }
+    uint8_t* pslot = L.pbuf + slot * kH64Pslot;
+    *reinterpret_cast<u32x4*>(pslot + p_off(hb, 0, 32 * g + l32)) = pk[0];
+    *reinterpret_cast<u32x4*>(pslot + p_off(hb, 1, 32 * g + l32)) = pk[1];
   };
-  // Value waves: O += P V over the tile, after the rescale the score waves
-  // flagged.  V is the B operand: lane (column l32, half hb) needs tile rows
-  // 16 ks + 4 hb + 0..3 and 16 ks + 8 + 4 hb + 0..3 of its column, two
-  // ds_read_b64_tr_b16 (in each 16-lane group lane j addresses row
-  // base + j / 4 at column block 4 (j % 4) of the group's 16 columns, and
-  // lane j receives column j of the four rows).
+
+  // Value waves: O[64 heads][128 columns] += P V over the tile, after the
+  // rescale of the head blocks the score waves flagged.  P is the A operand
+  // (lane: head 32 mb + l32, k step ks: tile rows 16 ks + 8 (e / 4) + 4 hb +
+  // e % 4); V the B operand (lane: column l32 of the column tile, the same
+  // rows), two ds_read_b64_tr_b16 per operand: in each 16-lane group lane j
+  // addresses tile row base + j / 4 at column block 4 (j % 4) of the group's
+  // 16 columns and receives column j of the four rows.
   auto pv = [&](const uint8_t* tl, int slot) {
-    const float* al_s = alpha_slot(L, slot);
-    if (reinterpret_cast<const int*>(al_s + 64)[g]) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 al = *reinterpret_cast<const f32x4*>(al_s + g * 32 + 8 * j + 4 * hb);
+    for (int mb = 0; mb < 2; ++mb) {
+      if (flag_slot(L, slot)[mb]) {
+        const float* al_s = alpha_slot(L, slot);
 #pragma unroll
-        for (int ct = 0; ct < (SCORE ? 1 : kColTiles); ++ct)
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 al = *reinterpret_cast<const f32x4*>(al_s + 32 * mb + 8 * j + 4 * hb);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[ct][4 * j + r] *= al[r];
+          for (int ct = 0; ct < (V ? kColTiles : 1); ++ct)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[V ? mb : 0][ct][4 * j + r] *= al[r];
+        }
       }
     }
-    const bf16x8 pa0 = L.pbuf[((slot * 2 + g) * 2 + 0) * 64 + lane];
-    const bf16x8 pa1 = L.pbuf[((slot * 2 + g) * 2 + 1) * 64 + lane];
-    // tile row 16 ks + 8 rd + 4 hb + jj / 4 (read rd of k step ks) is LDS
-    // row 16 ks + 4 (jj / 4) + 2 rd + hb
-    const int jj = lane & 15;
-    const uint8_t* vp = tl + (4 * (jj >> 2) + hb) * kRowLds + (hx * 256 + 16 * ((lane >> 4) & 1) + 4 * (jj & 3)) * 2;
-    constexpr int kAhead = 4;
-    // operand n: k step n / 8, column tile n % 8 (consecutive MFMAs update
-    // different accumulators)
+    const uint8_t* pslot = L.pbuf + slot * kH64Pslot;
+    bf16x8 pa[2][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) pa[mb][ks] = lds16(pslot + p_off(hb, ks, 32 * mb + l32));
+    const int jj = lane & 15, g16 = (lane >> 4) & 1;
+    const uint8_t* vp = tl + (4 * hb + (jj >> 2)) * kRowLds + (cq * 128 + 16 * g16 + 4 * (jj & 3)) * 2;
+    constexpr int kAhead = 3;
+    // operand n: k step n / 4, column tile n % 4
     auto vread = [&](int n) {
-      const uint8_t* p = vp + (n >> 3) * 16 * kRowLds + (n & 7) * 64;
-      return join(lds_read_tr16(p), lds_read_tr16(p + 2 * kRowLds));
+      const uint8_t* pp = vp + (n >> 2) * 16 * kRowLds + (n & 3) * 64;
+      return join(lds_read_tr16(pp), lds_read_tr16(pp + 8 * kRowLds));
     };
     bf16x8 vb[kAhead];
 #pragma unroll
@@ -947,93 +925,106 @@ __device__ inline void h64_role(const MlaArgs& a, const H64Lds& L, const int64_t
     for (int n = 0; n < 2 * kColTiles; ++n) {
       const bf16x8 v = vb[n % kAhead];
       if (n + kAhead < 2 * kColTiles) vb[n % kAhead] = vread(n + kAhead);
-      const int ct = (n & 7) < (SCORE ? 1 : kColTiles) ? (n & 7) : 0;
-      o[ct] = mfma32((n >> 3) ? pa1 : pa0, v, o[ct]);
+      const int ct = V ? (n & 3) : 0;
+#pragma unroll
+      for (int mb = 0; mb < (V ? 2 : 1); ++mb) o[mb][ct] = mfma32(pa[mb][n >> 2], v, o[mb][ct]);
+    }
+  };
+
+  // Gather waves: tile j from stage j % 3 into buffer j % 3 (its loads are
+  // the oldest in flight: the two later tiles' loads may still be pending),
+  // then the gathers of tile j + 3 into the same stage.  Tile numbers are
+  // clamped to the last tile, so every call issues the same loads (a tile
+  // past the end lands in a buffer no phase reads).
+  // The value waves do the same for the tile's rope (one load per tile).
+  auto store_issue = [&](int j, int sx) {
+    if (G) {
+      wait_vmcnt<2 * kL>();
+      stage_store_masked<F>(st[sx], vmask[min(j, ntiles - 1)], tiles + sx * kTileLds, gt);
+      stage_load_all<F>(st[sx], offs + min(j + 3, ntiles - 1) * kTileRows, a.kv, gt);
+    } else if (V) {
+      wait_vmcnt<2>();
+      rope_store(rs[sx], vmask[min(j, ntiles - 1)], tiles + sx * kTileLds, vt);
+      rs[sx] = rope_load<F>(offs + min(j + 3, ntiles - 1) * kTileRows, a.kv, vt);
     }
   };
 
   if (any_usable) {
-    if (SCORE) {
-      const uint16_t* qp = a.q + ((int64_t)t * a.H + head0 + l32) * kD + hx * 288 + 8 * hb;
+    if (G) {
 #pragma unroll
-      for (int ks = 0; ks < (SCORE ? kQSteps : 1); ++ks) qreg[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
+      for (int j = 0; j < kH64Stages; ++j)
+        stage_load_all<F>(st[j], offs + min(j, ntiles - 1) * kTileRows, a.kv, gt);
     }
-    Stage<F> st[S];
-    uint32_t bad[S];
+    if (V) {
 #pragma unroll
-    for (int s = 0; s < S; ++s) bad[s] = stage_load_all<F>(st[s], offs + min(s, ntiles - 1) * kTileRows, a.kv, tid);
-    // tiles 0..2 to LDS buffers 0..2; stage s then gathers tile s + S
+      for (int j = 0; j < kH64Stages; ++j) rs[j] = rope_load<F>(offs + min(j, ntiles - 1) * kTileRows, a.kv, vt);
+    }
+    store_issue(0, 0);
+    if (S) {
+      const uint16_t* qp = a.q + ((int64_t)t * a.H + grp * 64 + 32 * g + l32) * kD + 8 * hb;
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      wait_vmcnt<(S - 1) * kL>();
-      if (s < ntiles) stage_store_masked<F>(st[s], bad[s], tiles + s * kTileLds, tid);
-      bad[s] = stage_load_all<F>(st[s], offs + min(s + S, ntiles - 1) * kTileRows, a.kv, tid);
+      for (int ks = 0; ks < (S ? kQSteps : 1); ++ks) q[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks);
     }
     lds_barrier();
-    if (SCORE) qk(tiles);
+    if (S) qk_softmax(tiles, vmask[0], 0);
+    store_issue(1, 1);  // unconditional (tile 1 clamped), so the loop sees one wait state
     lds_barrier();
-    if (SCORE) softmax(vmask[0], 0);
-    lds_barrier();  // the sibling has read the partial scores of tile 0
-    if (SCORE && 1 < ntiles) qk(tiles + kTileLds);
-    lds_barrier();
-    // iteration i: tiles i, i+1, i+2 in buffers i % 3 .. ; tile i+3 in stage
-    // stg (= (i+3) % 3 = i % 3); P of tile i in slot i % 3
-    auto iter = [&](int i, int i3, Stage<F>& stg, uint32_t& stg_bad) {
-      uint8_t* b0 = tiles + i3 * kTileLds;                       // tile i
-      uint8_t* b2 = tiles + (i3 == 0 ? 2 : i3 - 1) * kTileLds;   // tile i+2
-      // phase A
-      if (SCORE) {
-        if (i + 1 < ntiles) softmax(vmask[i + 1], i3 == 2 ? 0 : i3 + 1);
-      } else {
-        pv(b0, i3);
-      }
-      lds_barrier();
-      // phase B: the stage first (its gathers have had three iterations to
-      // land), then the score waves' MFMAs
-      wait_vmcnt<(S - 1) * kL>();
-      if (i + 3 < ntiles) stage_store_masked<F>(stg, stg_bad, b0, tid);
-      stg_bad = stage_load_all<F>(stg, offs + min(i + 3 + S, ntiles - 1) * kTileRows, a.kv, tid);
-      if (SCORE && i + 2 < ntiles) qk(b2);
+    // phase i (i3 = i % 3, i2 = i % 2); `checked` phases test the tile count
+    auto phase = [&](int i, int i3, int i2, bool checked) {
+      if (S && (!checked || i + 1 < ntiles)) qk_softmax(tiles + (i3 == 2 ? 0 : i3 + 1) * kTileLds, vmask[i + 1], i2 ^ 1);
+      if (V) pv(tiles + i3 * kTileLds, i2);
+      if (!checked || i + 2 < ntiles) store_issue(i + 2, i3 == 0 ? 2 : i3 - 1);
       lds_barrier();
     };
-    // Whole trips of three iterations, then the one or two left: a loop body
-    // with conditional iterations would let the compiler's wait counting
-    // assume no newer gathers on the skipped path, and drain every stage.
+    // whole trips of six phases in which every role has its work, then the rest
     int i = 0;
 #pragma unroll 1
-    for (; i + 3 <= ntiles; i += 3) {
-      iter(i, 0, st[0], bad[0]);
-      iter(i + 1, 1, st[1], bad[1]);
-      iter(i + 2, 2, st[2], bad[2]);
+    for (; i + 8 <= ntiles; i += 6) {
+      phase(i, 0, 0, false);
+      phase(i + 1, 1, 1, false);
+      phase(i + 2, 2, 0, false);
+      phase(i + 3, 0, 1, false);
+      phase(i + 4, 1, 0, false);
+      phase(i + 5, 2, 1, false);
     }
-    if (i < ntiles) iter(i, 0, st[0], bad[0]);
-    if (i + 1 < ntiles) iter(i + 1, 1, st[1], bad[1]);
+    if (i < ntiles) phase(i, 0, 0, true);
+    if (i + 1 < ntiles) phase(i + 1, 1, 1, true);
+    if (i + 2 < ntiles) phase(i + 2, 2, 0, true);
+    if (i + 3 < ntiles) phase(i + 3, 0, 1, true);
+    if (i + 4 < ntiles) phase(i + 4, 1, 0, true);
+    if (i + 5 < ntiles) phase(i + 5, 2, 1, true);
+    if (i + 6 < ntiles) phase(i + 6, 0, 0, true);
     wait_vmcnt<0>();  // the last gathers (of no tile) are done
   }
 
-  // m and each k step's l per head, from the score waves
-  if (SCORE) {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
-    const float l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    if (lane < 32) {
-      L.stats[3 * (32 * g + lane) + 1 + hx] = l;
-      if (hx == 0) L.stats[3 * (32 * g + lane)] = m_run;
+  // m and l per head, from the score waves
+  if (S) {
+    const float l = sum_over_halves(l_run);
+    if (hb == 0) {
+      const int h = 32 * g + l32;
+      L.stats[3 * h] = m_run;
+      L.stats[3 * h + 1] = l;
+      L.stats[3 * h + 2] = 0.f;
     }
   }
   lds_barrier();
   // O / l as bf16 into the staging area, [64 heads][512 columns]
-  if (!SCORE) {
+  if (V) {
     uint16_t* stage_out = reinterpret_cast<uint16_t*>(tiles);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int h = 32 * g + 8 * j + 4 * hb + r;
-        const float l = L.stats[3 * h + 1] + L.stats[3 * h + 2];
-        const float inv = l > 0.f ? __builtin_amdgcn_rcpf(l) : 0.f;
+      for (int j = 0; j < 4; ++j) {
 #pragma unroll
-        for (int ct = 0; ct < (SCORE ? 1 : kColTiles); ++ct)
-          stage_out[h * kDc + hx * 256 + ct * 32 + l32] = __builtin_bit_cast(uint16_t, (__bf16)(o[ct][4 * j + r] * inv));
+        for (int r = 0; r < 4; ++r) {
+          const int h = 32 * mb + 8 * j + 4 * hb + r;
+          const float l = L.stats[3 * h + 1] + L.stats[3 * h + 2];
+          const float inv = l > 0.f ? __builtin_amdgcn_rcpf(l) : 0.f;
+#pragma unroll
+          for (int ct = 0; ct < kColTiles; ++ct)
+            stage_out[h * kDc + cq * 128 + ct * 32 + l32] =
+                __builtin_bit_cast(uint16_t, (__bf16)(o[V ? mb : 0][V ? ct : 0][4 * j + r] * inv));
+        }
       }
     }
   }
@@ -1044,14 +1035,12 @@ template <int F>
 __global__ __launch_bounds__(kH64Threads, 1) void sparse_mla_h64(MlaArgs a, int n_groups, int T) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int NT = kH64Threads;
-  static_assert(NT == kStageThreads, "the gather layout assumes 512 threads");
+  static_assert(NT == 8 * 64 && kGatherThreads == 2 * 64, "two score, four value and two gather waves");
   const int x = blockIdx.x, sp = blockIdx.z;
   const int t = (x / (8 * n_groups)) * 8 + (x & 7);
   const int grp = (x >> 3) % n_groups;
   if (t >= T) return;                          // padding ids of the XCD-aware layout
   const int tid = threadIdx.x, wave = tid >> 6;
-  const int g = wave & 1;                      // group of 32 heads
-  const int hx = (wave >> 1) & 1;              // score waves: k half; value waves: column half
   const int j_begin = sp * a.rows_per_split;
   const int j_end = min(a.K, j_begin + a.rows_per_split);
   const int ntiles = (j_end - j_begin + kTileRows - 1) / kTileRows;
@@ -1062,12 +1051,10 @@ __global__ __launch_bounds__(kH64Threads, 1) void sparse_mla_h64(MlaArgs a, int 
   uint8_t* p = smem;
   L.tiles = p;
   p += kH64Bufs * kTileLds;
-  L.spart = reinterpret_cast<f32x4*>(p);
-  p += kH64Spart;
-  L.pbuf = reinterpret_cast<bf16x8*>(p);
-  p += 3 * kH64Pslot;
+  L.pbuf = p;
+  p += 2 * kH64Pslot;
   L.alpha = reinterpret_cast<float*>(p);
-  p += 3 * kH64Aslot;
+  p += 2 * kH64Aslot;
   L.stats = reinterpret_cast<float*>(p);
   int64_t* offs = reinterpret_cast<int64_t*>(smem + kH64Fixed);
   uint32_t* vmask = reinterpret_cast<uint32_t*>(offs + ntiles * kTileRows);
@@ -1076,9 +1063,10 @@ __global__ __launch_bounds__(kH64Threads, 1) void sparse_mla_h64(MlaArgs a, int 
   const int fv = build_offsets<NT>(offs, vmask, wmin, sv0, a.idx + (int64_t)t * a.K, j_begin, j_end,
                                    ntiles * kTileRows, loc.pos, loc.b, a.page_table, a.pt_stride,
                                    a.page_size, a.num_pages, a.page_stride, a.row_stride, tid);
-  const int head0 = grp * 64 + 32 * g;
-  if (wave < 4) h64_role<F, true>(a, L, offs, vmask, t, head0, g, hx, ntiles, fv != INT32_MAX, tid);
-  else h64_role<F, false>(a, L, offs, vmask, t, head0, g, hx, ntiles, fv != INT32_MAX, tid);
+  const bool any = fv != INT32_MAX;
+  if (wave < 2) h64_role<F, kRoleScore>(a, L, offs, vmask, t, grp, ntiles, any, tid);
+  else if (wave == 4 || wave == 5) h64_role<F, kRoleGather>(a, L, offs, vmask, t, grp, ntiles, any, tid);
+  else h64_role<F, kRoleValue>(a, L, offs, vmask, t, grp, ntiles, any, tid);
 
   const uint16_t* stage_out = reinterpret_cast<const uint16_t*>(L.tiles);
   constexpr int kChunks = 64 * kDc * 2 / 16 / NT;  // 16-byte chunks per thread

@@ -245,7 +245,7 @@ def test_sparse_mla_validation():
     assert dsa.dsa_sparse_mla_workspace_bytes(4096, 128, 2048, 512, False) == 0
 
 
-MAX64 = 2624   # rows one 64-head workgroup can attend (documented in dsa.h)
+MAX64 = 5184   # rows one 64-head workgroup can attend (documented in dsa.h)
 
 
 def test_sparse_mla_refuses_plans_beyond_lds():
