@@ -670,6 +670,34 @@ __device__ inline void stage_store_masked(const Stage<F>& st, uint32_t vm, uint8
   }
 }
 
+// stage_store_masked of one tile, then stage_load_all of the next one into the
+// same stage.  For bf16 rows the two are interleaved item by item, so the
+// texture path takes the next tile's loads while LDS takes this tile's stores.
+template <int F>
+__device__ inline void stage_cycle(Stage<F>& st, uint32_t vm, uint8_t* tile, const int64_t* next_offs,
+                                   const uint8_t* kv, int gt) {
+  if (kQ8<F>) {
+    stage_store_masked<F>(st, vm, tile, gt);
+    stage_load_all<F>(st, next_offs, kv, gt);
+    return;
+  }
+  constexpr int kLat = Stage<F>::kLat;
+  const int ch = gt & 63, r0 = gt >> 6;
+  const int64_t mine = next_offs[r0 + 2 * (gt & 15)];
+  const int lo = (int)(uint32_t)mine, hi = (int)(mine >> 32);
+#pragma unroll
+  for (int k = 0; k < kLat; ++k) {
+    *reinterpret_cast<u32x4*>(tile + (r0 + 2 * k) * kRowLds + ch * 16) = st.lat[k];
+    const int64_t o = ((int64_t)__builtin_amdgcn_readlane(hi, k) << 32) | (uint32_t)__builtin_amdgcn_readlane(lo, k);
+    st.lat[k] = ld_global16(kv + (o < 0 ? 0 : o) + (uint32_t)(ch * 16));
+  }
+  if (vm != 0xFFFFFFFFu) {
+#pragma unroll
+    for (int k = 0; k < kLat; ++k)
+      if (!((vm >> (r0 + 2 * k)) & 1u)) *reinterpret_cast<u32x4*>(tile + (r0 + 2 * k) * kRowLds + ch * 16) = u32x4{};
+  }
+}
+
 // Merge of the split partials of one (row, 64-head group) by the last split
 // to arrive (called by every thread after its split's block is stored).  A
 // block is O / l as bf16 [64 heads][512 columns], then (m, l) per head.
@@ -890,20 +918,8 @@ __device__ inline void h64_role(const MlaArgs& a, const H64Lds& L, const int64_t
   // addresses tile row base + j / 4 at column block 4 (j % 4) of the group's
   // 16 columns and receives column j of the four rows.
   auto pv = [&](const uint8_t* tl, int slot) {
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      if (flag_slot(L, slot)[mb]) {
-        const float* al_s = alpha_slot(L, slot);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f32x4 al = *reinterpret_cast<const f32x4*>(al_s + 32 * mb + 8 * j + 4 * hb);
-#pragma unroll
-          for (int ct = 0; ct < (V ? kColTiles : 1); ++ct)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) o[V ? mb : 0][ct][4 * j + r] *= al[r];
-        }
-      }
-    }
+    // the P operands, the first V operands and the flags are read together,
+    // so the wave waits for LDS once before its MFMAs
     const uint8_t* pslot = L.pbuf + slot * kH64Pslot;
     bf16x8 pa[2][2];
 #pragma unroll
@@ -921,6 +937,21 @@ __device__ inline void h64_role(const MlaArgs& a, const H64Lds& L, const int64_t
     bf16x8 vb[kAhead];
 #pragma unroll
     for (int n = 0; n < kAhead; ++n) vb[n] = vread(n);
+    const int2 fl = *reinterpret_cast<const int2*>(flag_slot(L, slot));
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      if (mb == 0 ? fl.x : fl.y) {
+        const float* al_s = alpha_slot(L, slot);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 al = *reinterpret_cast<const f32x4*>(al_s + 32 * mb + 8 * j + 4 * hb);
+#pragma unroll
+          for (int ct = 0; ct < (V ? kColTiles : 1); ++ct)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[V ? mb : 0][ct][4 * j + r] *= al[r];
+        }
+      }
+    }
 #pragma unroll
     for (int n = 0; n < 2 * kColTiles; ++n) {
       const bf16x8 v = vb[n % kAhead];
@@ -940,8 +971,8 @@ __device__ inline void h64_role(const MlaArgs& a, const H64Lds& L, const int64_t
   auto store_issue = [&](int j, int sx) {
     if (G) {
       wait_vmcnt<2 * kL>();
-      stage_store_masked<F>(st[sx], vmask[min(j, ntiles - 1)], tiles + sx * kTileLds, gt);
-      stage_load_all<F>(st[sx], offs + min(j + 3, ntiles - 1) * kTileRows, a.kv, gt);
+      stage_cycle<F>(st[sx], vmask[min(j, ntiles - 1)], tiles + sx * kTileLds,
+                     offs + min(j + 3, ntiles - 1) * kTileRows, a.kv, gt);
     } else if (V) {
       wait_vmcnt<2>();
       rope_store(rs[sx], vmask[min(j, ntiles - 1)], tiles + sx * kTileLds, vt);
