@@ -211,15 +211,22 @@ def key_fp8_overlap(path, cfg_id, mode):
 
 
 def cpu_model():
-    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    """The host CPU as /proc/cpuinfo names it (first processor: model name, family and
+    model numbers), with the logical CPUs this process may use and the total."""
+    f = {}
     try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if not line.strip():
+                    break
+                k, _, v = line.partition(":")
+                f[k.strip()] = v.strip()
     except OSError:
         pass
-    return "unknown"
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return "%s (family %s, model %s, stepping %s; %d of %d logical CPUs usable)" % (
+        f.get("model name", "unknown"), f.get("cpu family", "?"), f.get("model", "?"), f.get("stepping", "?"),
+        usable, os.cpu_count() or 0)
 
 
 def _oracle_rate(sb, threads, budget_s):
