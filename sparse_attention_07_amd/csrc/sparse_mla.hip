@@ -68,6 +68,7 @@ constexpr int kTileRows = 32;
 constexpr int kRowLds = 73 * 16;                       // 1152 B of row + one 16-byte pad
 constexpr int kTileLds = kTileRows * kRowLds;          // 37376 B
 constexpr int kSbufLds = kThreads * 16;                // one f32x4 of partial scores per thread
+constexpr int kQ8TabLds = 2 * 4 * 4 * 16 * 4;           // 8-bit rows: block scales and biases, [wave][block][16 rows]
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kRescaleSlack = 8.f;                   // log2 units
 
@@ -309,9 +310,14 @@ __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 // l rescaled) only when the tile beats it by more than kRescaleSlack.
 // Returns P as the PV A operand (k slot (g, e) <-> row 4g + e, (g, 4 + e) <->
 // row 16 + 4g + e).  O accumulator r of lane (g, c16) holds head 4g + r.
-template <int TILES>
+// SCALED (8-bit rows, block scale deferred to P): P is multiplied by the k
+// slot's row scale psc before it is rounded to bf16, and with BIAS (affine
+// int8) bacc += p * the slot's row bias, rescaled with O; l takes p itself.
+template <int TILES, bool SCALED = false, bool BIAS = false>
 __device__ inline bf16x8 tile_softmax(const f32x4& s0, const f32x4& s1, uint32_t valid, float scale_log2,
-                                      float& m_run, float& l_run, f32x4 (&o)[TILES]) {
+                                      float& m_run, float& l_run, f32x4 (&o)[TILES],
+                                      const float* psc = nullptr, const float* pbi = nullptr,
+                                      float* bacc = nullptr) {
   const int lane = threadIdx.x & (kWave - 1), g = lane >> 4;
   float xv[8];
   if (valid == 0xFFFFFFFFu) {  // wave-uniform: every row usable
@@ -336,6 +342,7 @@ __device__ inline bf16x8 tile_softmax(const f32x4& s0, const f32x4& s1, uint32_t
     const float alpha = (m_run == kNegInf) ? 0.f : exp2_fast(m_run - m_new);
     m_run = m_new;
     l_run *= alpha;
+    if (BIAS) *bacc *= alpha;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float ar = __shfl(alpha, 4 * g + r);  // O row r holds head 4g + r
@@ -349,14 +356,16 @@ __device__ inline bf16x8 tile_softmax(const f32x4& s0, const f32x4& s1, uint32_t
     for (int i2 = 0; i2 < 8; ++i2) {
       const float p = exp2_fast(xv[i2] - m_run);
       l_run += p;
-      pa[i2] = (__bf16)p;
+      if (BIAS) *bacc = fmaf(p, pbi[i2], *bacc);
+      pa[i2] = (__bf16)(SCALED ? p * psc[i2] : p);
     }
   } else {
 #pragma unroll
     for (int i2 = 0; i2 < 8; ++i2) {
       const float p = xv[i2] == kNegInf ? 0.f : exp2_fast(xv[i2] - m_run);
       l_run += p;
-      pa[i2] = (__bf16)p;
+      if (BIAS) *bacc = fmaf(p, pbi[i2], *bacc);
+      pa[i2] = (__bf16)(SCALED ? p * psc[i2] : p);
     }
   }
   return pa;
@@ -1145,6 +1154,10 @@ __global__ __launch_bounds__(kH64Threads, 1) void sparse_mla_h64(MlaArgs a, int 
 // which every wave then reads V for its quarter (128) of the output columns.
 // Partial scores of the two k halves are summed through LDS in a fixed order.
 // Registers: 36 of q, 32 of accumulator, 36 per tile in flight (two tiles).
+// 8-bit rows: the first of the 8 latent dims lane group g supplies in k step
+// ks < 16 (the sum over dims runs in any order; q follows the same map).
+__host__ __device__ constexpr int q8_dim(int ks, int g) { return 64 * (ks >> 1) + 16 * g + 8 * (ks & 1); }
+
 template <int F>
 struct RegTile {
   u32x4 v[9];   // bf16: 16 B per k step; 8-bit: 8 latent codes (v.x, v.y) or 16 B of rope
@@ -1167,8 +1180,19 @@ __device__ inline void regtile_load(RegTile<F>& st, int64_t off, const uint8_t* 
     if (!Q8) {
       st.v[k] = ld_global16(row + ks * 64 + g * 16);
     } else if (ks < 16) {
-      const uint2 x = *reinterpret_cast<const uint2*>(row + ks * 32 + g * 8);
-      st.v[k] = u32x4{x.x, x.y, 0u, 0u};
+      // 8-bit: k steps 2j and 2j+1 take dims 64 j + 16 g .. +15 (q8_dim), so
+      // one 16-byte load serves both when the wave has both steps
+      if ((ks & 1) == 0 && k + 1 < 9) {
+        const u32x4 x = ld_global16(row + q8_dim(ks, g));
+        st.v[k] = u32x4{x[0], x[1], 0u, 0u};
+        st.v[k + 1] = u32x4{x[2], x[3], 0u, 0u};
+      } else if ((ks & 1) == 1 && k == 0) {
+        const uint2 x = *reinterpret_cast<const uint2*>(row + q8_dim(ks, g));
+        st.v[k] = u32x4{x.x, x.y, 0u, 0u};
+      } else if ((ks & 1) == 0) {
+        const uint2 x = *reinterpret_cast<const uint2*>(row + q8_dim(ks, g));
+        st.v[k] = u32x4{x.x, x.y, 0u, 0u};
+      }
     } else {
       st.v[k] = ld_global16(row + kRopeOff<F> + ((ks - 16) * 32 + g * 8) * 2);
     }
@@ -1177,15 +1201,86 @@ __device__ inline void regtile_load(RegTile<F>& st, int64_t off, const uint8_t* 
   if (F == kFmtInt8) st.bi = *reinterpret_cast<const f32x4*>(row + 528);
 }
 
-// The bf16 A operand of k step ks (8-bit: decoded with the block scale and
-// bias, rounded to bf16).
+// The bf16 A operand of k step ks.  8-bit latent dims give their codes
+// exactly (every e4m3 value is a bf16; int8 codes centred, code - 128, an
+// integer in -128..127); the block scale, and the int8 bias (then bi + 128
+// sc), is applied to the scores and to P instead.  Centring keeps sc times
+// the code near the decoded value when a block's range is centred near zero,
+// so rounding P times the scale to bf16 costs no more than rounding the
+// decoded value would.
 template <int F>
 __device__ inline bf16x8 regtile_operand(const RegTile<F>& st, int k, int ks) {
   if (!kQ8<F> || ks >= 16) return __builtin_bit_cast(bf16x8, st.v[k]);
-  const float sc = st.sc[ks >> 2], bi = F == kFmtInt8 ? st.bi[ks >> 2] : 0.f;
-  const uint2 p0 = decode4<F>(st.v[k][0], sc, bi), p1 = decode4<F>(st.v[k][1], sc, bi);
-  const u32x4 r = {p0.x, p0.y, p1.x, p1.y};
+  u32x4 r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t x = st.v[k][h];
+    if (F == kFmtFp8) {
+      r[2 * h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false));
+      r[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true));
+    } else {
+      r[2 * h] = pack_bf16x2((float)(x & 0xFFu) - 128.f, (float)((x >> 8) & 0xFFu) - 128.f);
+      r[2 * h + 1] = pack_bf16x2((float)((x >> 16) & 0xFFu) - 128.f, (float)(x >> 24) - 128.f);
+    }
+  }
   return __builtin_bit_cast(bf16x8, r);
+}
+
+// QK of one tile for the k steps KS0 .. KS0+8 of 8-bit rows: one accumulator
+// per 128-dim block the steps touch (the rope steps 16, 17 in the last), each
+// scaled by its row's block scale (and, int8, plus the row's block bias for
+// the centred codes times q's sum over the wave's dims of the block), as
+// exact codes go in.  sct /
+// bit: this wave's [block][16 rows] scale and bias tables in LDS; rows of the
+// D layout: 4 g + i.  trow: the lane's LDS tile row (latent codes as bf16).
+template <int F, int KS0>
+__device__ inline f32x4 qk_q8(const RegTile<F>& st, const bf16x8 (&qreg)[9], uint8_t* trow,
+                              const float* sct, const float* bit, const float (&qsum)[3], int g) {
+  f32x4 acc[3] = {f32x4{}, f32x4{}, f32x4{}};
+#pragma unroll
+  for (int k = 0; k < 9; ++k) {
+    const int ks = KS0 + k;
+    const bf16x8 av = regtile_operand<F>(st, k, ks);
+    if (ks < 16) *reinterpret_cast<bf16x8*>(trow + 2 * q8_dim(ks, g)) = av;  // latent codes feed PV
+    const int slot = (ks < 16 ? ks >> 2 : 4) - (KS0 >> 2);
+    acc[slot] = mfma16(av, qreg[k], acc[slot]);
+  }
+  f32x4 s = f32x4{};
+#pragma unroll
+  for (int slot = 0; slot < 3; ++slot) {
+    const int b = slot + (KS0 >> 2);  // 4: the rope
+    if (b < 4) {
+      const f32x4 sc = *reinterpret_cast<const f32x4*>(sct + b * 16 + 4 * g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[i] = fmaf(acc[slot][i], sc[i], s[i]);
+      if (F == kFmtInt8) {
+        const f32x4 bi = *reinterpret_cast<const f32x4*>(bit + b * 16 + 4 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[i] = fmaf(bi[i], qsum[slot], s[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[i] += acc[slot][i];
+    }
+  }
+  return s;
+}
+
+// q's sum over the dims of each block slot of the k steps KS0 .. KS0+8
+// (lane: head c16, the lane's 8 dims per step; summed over the four lane
+// groups), for the int8 bias term of the scores.
+template <int KS0>
+__device__ inline void qsum_q8(const bf16x8 (&qreg)[9], float (&qsum)[3]) {
+  float part[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < 9; ++k) {
+    const int ks = KS0 + k;
+    const int slot = (ks < 16 ? ks >> 2 : 4) - (KS0 >> 2);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[slot] += (float)qreg[k][e];
+  }
+#pragma unroll
+  for (int slot = 0; slot < 3; ++slot) qsum[slot] = sum_over_groups(part[slot]);
 }
 
 // MINW: workgroups per CU the register budget is sized for (1 when the grid
@@ -1216,16 +1311,21 @@ __global__ __launch_bounds__(kThreads, MINW) void sparse_mla_q16(MlaArgs a, int 
   const int b = loc.b, pos = loc.pos;
   uint8_t* tile = smem;
   f32x4* sbuf = reinterpret_cast<f32x4*>(smem + kTileLds);
-  int64_t* offs = reinterpret_cast<int64_t*>(smem + kTileLds + kSbufLds);
+  float* q8tab = reinterpret_cast<float*>(smem + kTileLds + kSbufLds);  // [scale, bias][wave][block][16 rows]
+  int64_t* offs = reinterpret_cast<int64_t*>(smem + kTileLds + kSbufLds + kQ8TabLds);
   uint32_t* vmask = reinterpret_cast<uint32_t*>(offs + ntiles * kTileRows);
   int* wmin = reinterpret_cast<int*>(vmask + ntiles);  // kWaveSlots, then the merge's flag
 
   // q for this wave's k half: lane (head c16, group g) holds dims 32 ks + 8 g .. +7.
   bf16x8 qreg[9];
   {
-    const uint16_t* qp = a.q + ((int64_t)t * a.H + head0 + c16) * kD + g * 8 + ks0 * 32;
+    const uint16_t* qh = a.q + ((int64_t)t * a.H + head0 + c16) * kD;
 #pragma unroll
-    for (int k = 0; k < 9; ++k) qreg[k] = *reinterpret_cast<const bf16x8*>(qp + k * 32);
+    for (int k = 0; k < 9; ++k) {
+      const int ks = ks0 + k;
+      const int d = (kQ8<F> && ks < 16) ? q8_dim(ks, g) : 32 * ks + 8 * g;  // 8-bit rows: their dim map
+      qreg[k] = *reinterpret_cast<const bf16x8*>(qh + d);
+    }
   }
   const int fv = build_offsets(offs, vmask, wmin, sv0, a.idx + (int64_t)t * a.K, j_begin, j_end,
                                ntiles * kTileRows, pos, b, a.page_table, a.pt_stride, a.page_size,
@@ -1235,6 +1335,15 @@ __global__ __launch_bounds__(kThreads, MINW) void sparse_mla_q16(MlaArgs a, int 
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = f32x4{};
   float m_run = kNegInf, l_run = 0.f;
+  constexpr bool Q8 = kQ8<F>, BIAS = F == kFmtInt8;
+  float qsum[3] = {0.f, 0.f, 0.f};  // int8: q summed over each block slot of the wave's dims
+  if (BIAS) {
+    if (ks0 == 0) qsum_q8<0>(qreg, qsum);
+    else qsum_q8<9>(qreg, qsum);
+  }
+  float bacc = 0.f;                 // int8: this lane's share of sum_r p * bias (head c16), rescaled with O
+  float* sct = q8tab + wave * 64;   // this wave's [block][16 rows] scales; biases 256 floats on
+  float* bit = sct + 256;
 
   if (fv != INT32_MAX) {
     const int my_row = 16 * rb + c16;
@@ -1242,12 +1351,22 @@ __global__ __launch_bounds__(kThreads, MINW) void sparse_mla_q16(MlaArgs a, int 
       lds_barrier();                                       // every wave is done with tile i-1
       f32x4 spart = f32x4{};
       uint8_t* trow = tile + my_row * kRowLds + g * 16;
+      if (Q8) {
+        // the rows' block scales (and biases) into this wave's tables: lane
+        // (g, c16) writes block g of row c16
+        sct[g * 16 + c16] = st.sc[g];
+        if (BIAS) bit[g * 16 + c16] = fmaf(128.f, st.sc[g], st.bi[g]);  // the centred codes' bias
+        uint8_t* trow8 = tile + my_row * kRowLds;
+        spart = ks0 == 0 ? qk_q8<F, 0>(st, qreg, trow8, sct, bit, qsum, g)
+                         : qk_q8<F, 9>(st, qreg, trow8, sct, bit, qsum, g);
+      } else {
 #pragma unroll
-      for (int k = 0; k < 9; ++k) {
-        const int ks = ks0 + k;
-        const bf16x8 av = regtile_operand<F>(st, k, ks);
-        if (ks < 16) *reinterpret_cast<bf16x8*>(trow + ks * 64) = av;  // latent dims feed PV
-        spart = mfma16(av, qreg[k], spart);
+        for (int k = 0; k < 9; ++k) {
+          const int ks = ks0 + k;
+          const bf16x8 av = regtile_operand<F>(st, k, ks);
+          if (ks < 16) *reinterpret_cast<bf16x8*>(trow + ks * 64) = av;  // latent dims feed PV
+          spart = mfma16(av, qreg[k], spart);
+        }
       }
       sbuf[wave * 64 + lane] = spart;
       if (i + STAGES < ntiles) regtile_load<F>(st, offs[(i + STAGES) * kTileRows + my_row], a.kv, ks0, g);
@@ -1256,7 +1375,32 @@ __global__ __launch_bounds__(kThreads, MINW) void sparse_mla_q16(MlaArgs a, int 
       // rows 0..15 from waves 0 and 2, rows 16..31 from waves 1 and 3; k half 0 first
       const f32x4 s0 = sbuf[0 * 64 + lane] + sbuf[2 * 64 + lane];
       const f32x4 s1 = sbuf[1 * 64 + lane] + sbuf[3 * 64 + lane];
-      const bf16x8 pa = tile_softmax(s0, s1, valid, a.scale_log2, m_run, l_run, o);
+      bf16x8 pa;
+      if (Q8) {
+        // P for this wave's columns (block `wave`) carries the rows' scale of
+        // that block: k slot (g, e) is row 4g + e (waves 0, 2 hold rows 0..15),
+        // (g, 4 + e) row 16 + 4g + e (waves 1, 3)
+        float psc[8], pbi[8];
+        const f32x4 c0 = *reinterpret_cast<const f32x4*>(q8tab + 0 * 64 + wave * 16 + 4 * g);
+        const f32x4 c1 = *reinterpret_cast<const f32x4*>(q8tab + 1 * 64 + wave * 16 + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          psc[e] = c0[e];
+          psc[4 + e] = c1[e];
+        }
+        if (BIAS) {
+          const f32x4 d0 = *reinterpret_cast<const f32x4*>(q8tab + 256 + 0 * 64 + wave * 16 + 4 * g);
+          const f32x4 d1 = *reinterpret_cast<const f32x4*>(q8tab + 256 + 1 * 64 + wave * 16 + 4 * g);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pbi[e] = d0[e];
+            pbi[4 + e] = d1[e];
+          }
+        }
+        pa = tile_softmax<8, true, BIAS>(s0, s1, valid, a.scale_log2, m_run, l_run, o, psc, pbi, &bacc);
+      } else {
+        pa = tile_softmax(s0, s1, valid, a.scale_log2, m_run, l_run, o);
+      }
       // O[:, col0 + 16 i .. +16] += P V.  k slot (g, e) <-> tile row 4g + e,
       // (g, 4 + e) <-> 16 + 4g + e, matching the S^T accumulator rows.
       const uint8_t* vp = tile + (4 * g + (c16 >> 2)) * kRowLds + (col0 + 4 * (c16 & 3)) * 2;
@@ -1281,6 +1425,15 @@ __global__ __launch_bounds__(kThreads, MINW) void sparse_mla_q16(MlaArgs a, int 
     }
   }
 
+  if (BIAS) {  // the bias term, the same for every column of the wave's block
+    const float bt = sum_over_groups(bacc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float br = __shfl(bt, 4 * g + r);
+#pragma unroll
+      for (int i2 = 0; i2 < 8; ++i2) o[i2][r] += br;
+    }
+  }
   l_run = sum_over_groups(l_run);
   // O accumulator r of lane: head 4g + r, column col0 + 16 i + c16.
   if (a.splits == 1) {
@@ -1414,7 +1567,7 @@ hipError_t launch_with_lds(Kernel kernel, dim3 grid, int threads, size_t lds, hi
 
 size_t plan_lds(const MlaPlan& plan, int n_heads) {
   return n_heads % 64 == 0 ? mla_lds(plan.rows_per_split, kH64Fixed - kTileLds)
-                           : mla_lds(plan.rows_per_split, kSbufLds);
+                           : mla_lds(plan.rows_per_split, kSbufLds + kQ8TabLds);
 }
 
 }  // namespace
