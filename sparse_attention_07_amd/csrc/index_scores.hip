@@ -22,9 +22,12 @@
 // Keys are read in place (no copy of the cache), once per row group.
 //
 // Reduction-index layout: the dot product over the 128 dims is summed in any
-// order, so the k slots of each MFMA are mapped to dims such that every lane
-// reads 128 contiguous bytes of one key: lane l (group g = l/32) supplies dims
-// g*64 + ks*8 .. +7 in step ks.  The query operand uses the same mapping.
+// order, so the k slots of each MFMA are mapped to dims to suit the key
+// loads.  bf16 keys (256 B, two 128-byte lines per token): lane l (group g =
+// l/32) supplies dims 16 ks + 8 g .. +7 in step ks, so lanes l and l + 32 read
+// neighbouring 16 bytes of one line and a load instruction touches 32 lines,
+// not 64.  fp8 keys (128 B, one line per token): dims g*64 + ks*8 .. +7, each
+// lane reading 64 contiguous bytes.  The query operand uses the keys' mapping.
 #include <algorithm>
 #include <type_traits>
 
@@ -70,9 +73,9 @@ __device__ inline void load_keys(Keys& kk, const int64_t (&off)[2], const uint8_
                                  int, int64_t) {
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
-    const uint8_t* p = k_base + (off[nt] < 0 ? 0 : off[nt]) + (lane >> 5) * 128;
+    const uint8_t* p = k_base + (off[nt] < 0 ? 0 : off[nt]) + (lane >> 5) * 16;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) kk.v[nt][ks] = *reinterpret_cast<const bf16x8*>(p + ks * 16);
+    for (int ks = 0; ks < 8; ++ks) kk.v[nt][ks] = *reinterpret_cast<const bf16x8*>(p + ks * 32);
   }
 }
 
@@ -101,8 +104,8 @@ __device__ inline void load_keys(Keys8& kk, const int64_t (&off)[2], const uint8
   }
 }
 
-// e4m3 codes -> bf16 (exact: every e4m3 value is a bf16), in the bf16 key
-// layout (step ks: dims 8 ks .. +7 of the lane's 64).
+// e4m3 codes -> bf16 (exact: every e4m3 value is a bf16), step ks: dims
+// 8 ks .. +7 of the lane's 64 (the fp8 keys' mapping).
 __device__ inline void keys_from_fp8(Keys& kk, const Keys8& k8) {
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt)
@@ -155,14 +158,16 @@ __device__ inline void score_block(const Keys& kk, const int64_t (&off)[2], cons
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) acc[i][jj] = f32x16{};
-    const uint8_t* qa = q_lds + r * kRowBytesLds + (lane & 31) * kHeadStrideLds + (lane >> 5) * 128;
+    // the query operand in the keys' dim mapping (bf16 keys: 16 ks + 8 g; fp8: 64 g + 8 ks)
+    const uint8_t* qa = q_lds + r * kRowBytesLds + (lane & 31) * kHeadStrideLds + (lane >> 5) * (SCALED ? 128 : 16);
+    constexpr int kStepBytes = SCALED ? 16 : 32;
     // The sibling wave on this SIMD is usually in its epilogue (VALU); issuing
     // this row's MFMAs first keeps the matrix core fed (prefill indexer -1.6%).
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(qa + ks * 16);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(qa + 32 * kHeadStrideLds + ks * 16);
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(qa + ks * kStepBytes);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(qa + 32 * kHeadStrideLds + ks * kStepBytes);
       acc[0][0] = mfma32(a0, kk.v[0][ks], acc[0][0]);
       acc[0][1] = mfma32(a1, kk.v[0][ks], acc[0][1]);
       acc[1][0] = mfma32(a0, kk.v[1][ks], acc[1][0]);
