@@ -124,22 +124,27 @@ struct Threshold {
 // NT * kReadBatch * 4 positions.
 constexpr int kReadBatch = 8;
 
-// The first round of a row's quads, read up to `bound` positions (the row's
-// storage): issued before the row's length is known, so that the read
-// overlaps the request lookup.  Positions at or past the length are never
-// used.
+// The early part of a row's first round: its first kEarlyBatch quads per
+// thread (NT * kEarlyBatch * 4 positions), read up to `bound` positions (the
+// row's storage) before the row's length is known, so that the read overlaps
+// the request lookup.  Only this part is read blind: the rest of the row is
+// read once the length is known, so a row much shorter than its storage
+// costs little more than its own length.  Positions at or past the length
+// are never used.
+constexpr int kEarlyBatch = 2;
 template <int NT>
 __device__ inline void read_first_round(const float* __restrict__ row, bool vec, int bound,
                                         f32x4 (&v)[kReadBatch]) {
   const int nq = (bound + 3) >> 2;
 #pragma unroll
-  for (int i = 0; i < kReadBatch; ++i) {
+  for (int i = 0; i < kEarlyBatch; ++i) {
     const int q = i * NT + threadIdx.x;
     if (q < nq) v[i] = load_quad(row, q, bound, vec);
   }
 }
 
-// pre (PRE only): the first round, from read_first_round with a bound >= n.
+// pre (PRE only): the early part of the first round, from read_first_round
+// with a bound >= n.
 template <int NT, bool Cached, bool PRE = false>
 __device__ inline Threshold select(const float* __restrict__ row, bool vec, int n, int k,
                                    uint32_t* cache, uint32_t* hist, uint32_t* pick,
@@ -157,7 +162,7 @@ __device__ inline Threshold select(const float* __restrict__ row, bool vec, int 
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const int q = q0 + i * NT + tid;
-      if (PRE && q0 == 0) v[i] = pre[i];
+      if (PRE && q0 == 0 && i < kEarlyBatch) v[i] = pre[i];
       else if (q < nq) v[i] = load_quad(row, q, n, vec);
     }
 #pragma unroll
