@@ -21,25 +21,33 @@ constexpr int kThreads = 1024;
 constexpr int kCache = 32768;
 
 // Top-K of row[0, n): emit(o, s) for the o-th selected position s, o < K, in
-// ascending s.
-template <bool Cached, bool PRE, typename Emit>
-__device__ inline void select_emit(const float* __restrict__ row, int n, int K, uint32_t* cache,
-                                   uint32_t* hist, uint32_t* wcount, uint32_t* pick, Emit emit,
-                                   const f32x4* pre = nullptr) {
-  const bool vec = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
-  const topk::Threshold th = topk::select<kThreads, Cached, PRE>(row, vec, n, K, cache, hist, pick, pre);
-  auto emit_k = [emit, K](uint32_t o, int s) {
-    if (o < (uint32_t)K) emit(o, s);
-  };
-  if (Cached) topk::compact_cached<kThreads>(n, cache, th, wcount, emit_k);
-  else topk::compact<kThreads, Cached>(row, vec, n, cache, th, wcount, emit_k);
+// ascending s.  Cached: n <= kCache.  VEC: the row may be read as 16-byte
+// quads (topk::quads_ok); PRE implies both, with pre its early reads.
+template <bool Cached, bool PRE, bool VEC, typename Emit>
+__device__ __attribute__((always_inline)) inline void select_emit(const float* __restrict__ row, int n, int K,
+                                                                  uint32_t* cache, uint32_t* hist, uint32_t* wcount,
+                                                                  uint32_t* pick, Emit emit,
+                                                                  const f32x4* pre = nullptr) {
+  const topk::RowReader<VEC> rd(row, n);
+  if (Cached) {
+    topk::select_cached<kThreads, PRE, VEC>(rd, n, K, cache, hist, pick, wcount, emit, pre);
+  } else {
+    const topk::Threshold th = topk::select<kThreads, VEC>(rd, n, K, hist, pick);
+    topk::compact<kThreads, false>(row, VEC, n, cache, th, wcount, [emit, K](uint32_t o, int s) {
+      if (o < (uint32_t)K) emit(o, s);
+    });
+  }
 }
 
-template <bool Cached, bool PRE = false>
-__device__ inline void select_row(const float* __restrict__ row, int n, int K, int32_t* __restrict__ out,
-                                  uint32_t* cache, uint32_t* hist, uint32_t* wcount, uint32_t* pick,
-                                  const f32x4* pre = nullptr) {
-  select_emit<Cached, PRE>(row, n, K, cache, hist, wcount, pick, [out](uint32_t o, int s) { out[o] = s; }, pre);
+// select_emit for a row of n <= kCache entries with `bound` entries of
+// storage from row.
+template <typename Emit>
+__device__ __attribute__((always_inline)) inline void select_cached_row(const float* __restrict__ row, int n,
+                                                                        int64_t bound, int K, uint32_t* cache,
+                                                                        uint32_t* hist, uint32_t* wcount,
+                                                                        uint32_t* pick, Emit emit) {
+  if (topk::quads_ok(row, n, bound)) select_emit<true, false, true>(row, n, K, cache, hist, wcount, pick, emit);
+  else select_emit<true, false, false>(row, n, K, cache, hist, wcount, pick, emit);
 }
 
 __global__ __launch_bounds__(kThreads) void topk_radix(const int32_t* __restrict__ cu_q,
@@ -54,9 +62,10 @@ __global__ __launch_bounds__(kThreads) void topk_radix(const int32_t* __restrict
   const int t = row_lo + (int)blockIdx.x;  // score row t - row_lo, index row t
   const int tid = threadIdx.x;
   const float* row = scores + (int64_t)(t - row_lo) * ld;
-  // Rows whose storage fits the cache are read in one round, issued before
-  // the lookup that gives the row's length.
-  const bool early = ld <= kCache;
+  // Rows whose storage fits the cache as whole 16-byte quads, 16-byte
+  // aligned, have the first part of their read issued before the lookup that
+  // gives the row's length.
+  const bool early = ld >= 4 && ld <= kCache && (ld & 3) == 0 && (reinterpret_cast<uintptr_t>(row) & 15) == 0;
   // The lookup's first round (requests 0 .. 255, as in locate_row) is
   // written out here so that the row read goes out between its loads and
   // its search; later rounds are left to locate_row.
@@ -69,8 +78,8 @@ __global__ __launch_bounds__(kThreads) void topk_radix(const int32_t* __restrict
     hi[c] = cu_q[i + 1];
     sl[c] = seq_lens[i];
   }
-  f32x4 pre[topk::kReadBatch];
-  if (early) topk::read_first_round<kThreads>(row, (reinterpret_cast<uintptr_t>(row) & 15) == 0, (int)ld, pre);
+  f32x4 pre[topk::kEarlyBatch];
+  if (early) topk::read_first_round<kThreads>(row, (int)ld, pre);
   RowLoc loc{-1, 0};
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
@@ -89,9 +98,10 @@ __global__ __launch_bounds__(kThreads) void topk_radix(const int32_t* __restrict
     for (int j = tid; j < K; j += kThreads) out[j] = j < n ? j : -1;
     return;
   }
-  if (early) select_row<true, true>(row, n, K, out, cache, hist, wcount, pick, pre);
-  else if (n <= kCache) select_row<true>(row, n, K, out, cache, hist, wcount, pick);
-  else select_row<false>(row, n, K, out, cache, hist, wcount, pick);
+  auto emit = [out](uint32_t o, int s) { out[o] = s; };
+  if (early) select_emit<true, true, true>(row, n, K, cache, hist, wcount, pick, emit, pre);
+  else if (n <= kCache) select_cached_row(row, n, ld, K, cache, hist, wcount, pick, emit);
+  else select_emit<false, false, false>(row, n, K, cache, hist, wcount, pick, emit);  // rare: no workspace
 }
 
 // Two-level selection for rows longer than the LDS cache.  Level 1: each
@@ -132,9 +142,9 @@ __global__ __launch_bounds__(kThreads) void topk_segments(const int32_t* __restr
     }
     return;
   }
-  select_emit<true, false>(row, len, K, cache, hist, wcount, pick, [=](uint32_t o, int s) {
+  select_cached_row(row, len, ld - s0, K, cache, hist, wcount, pick, [=](uint32_t o, int s) {
     cand_ix[base + o] = s0 + s;
-    cand_sc[base + o] = row[s];
+    cand_sc[base + o] = row[min(s, len - 1)];  // s < len always; the min only bounds the read
   });
 }
 
@@ -160,9 +170,9 @@ __global__ __launch_bounds__(kThreads) void topk_merge(const int32_t* __restrict
   const int n2 = segs * K;
   const float* row = cand_sc + (int64_t)(t - row_lo) * n2;
   const int32_t* ix = cand_ix + (int64_t)(t - row_lo) * n2;
-  auto emit = [out, ix](uint32_t o, int s) { out[o] = ix[s]; };
-  if (n2 <= kCache) select_emit<true, false>(row, n2, K, cache, hist, wcount, pick, emit);
-  else select_emit<false, false>(row, n2, K, cache, hist, wcount, pick, emit);
+  auto emit = [out, ix, n2](uint32_t o, int s) { out[o] = ix[min(s, n2 - 1)]; };  // s < n2 always
+  if (n2 <= kCache) select_cached_row(row, n2, n2, K, cache, hist, wcount, pick, emit);
+  else select_emit<false, false, false>(row, n2, K, cache, hist, wcount, pick, emit);
 }
 
 }  // namespace

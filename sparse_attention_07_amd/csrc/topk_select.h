@@ -4,20 +4,19 @@
 // to +0.0.  Scores map to 32-bit keys whose unsigned order is the score
 // order.  Up to three histogram passes over 11, 11 and 10 key bits (LDS
 // histograms, LDS atomics) narrow down the key prefix of the k-th best
-// element; the first pass runs while the row is read (and cached in LDS as
-// keys when it fits), and the passes stop as soon as the chosen bin is taken
-// whole.  After each pass a single wave scans the histogram to find the bin
-// holding the k-th element.  The selection is then "key prefix above the
-// chosen one, or equal to it and among the first `need` such positions".
-// Compaction: each wave owns a contiguous range of the row, counts its
-// selected elements, one workgroup-wide prefix over the wave counts places
-// the ranges, and a second walk hands every selected position with its rank
-// in ascending position order to the caller -- the ascending output and the
-// position tie-break come without sorting.
+// element; the first pass runs while the row is read, and the passes stop as
+// soon as the chosen bin is taken whole.  After each pass a single wave scans
+// the histogram to find the bin holding the k-th element.  The selection is
+// then "key prefix above the chosen one, or equal to it and among the first
+// `need` such positions", emitted in ascending position order, so the
+// ascending output and the position tie-break come without sorting.
 //
-// The row is read in quads (four consecutive positions): 16-byte loads when
-// the row is 16-byte aligned, and 16-byte LDS accesses for the key cache, so
-// that one round of loads per thread covers a whole cached row.
+// Rows that fit the LDS cache are read once (coalesced 16-byte quads through
+// a raw buffer resource, whose bounds check returns zeros past the row, so
+// every load is issued without a branch), their keys cached in LDS, and then
+// held in registers as one contiguous run per thread: the later passes and
+// the compaction work from registers.  Longer rows are re-read in each pass
+// and compacted by waves (compact()).
 #pragma once
 
 #include "dsa_device.h"
@@ -34,9 +33,17 @@ constexpr int kHistWords = kBins + kBins / 32 * 4;  // four pad words per 32 bin
 // two copies halve the worst collisions.
 constexpr int kHistCopy1 = kHistWords + 16;
 constexpr int kHistPass1 = 2 * kHistWords + 16;
-constexpr int kHistLdsWords = 3 * kHistWords + 16;
+// 64 words after the histograms, one per lane: pass 0 adds an element past
+// the row to its lane's word instead of branching around the add.
+constexpr int kHistDummy = 3 * kHistWords + 16;
+constexpr int kHistLdsWords = kHistDummy + kWave;
 
-__device__ inline uint32_t order_key(float f) {
+// Every function below is inlined into its kernel, so that LDS pointers stay
+// in the LDS address space and the compiler can keep several LDS reads in
+// flight (an out-of-line call sees generic pointers and waits after each).
+#define DSA_TOPK_INLINE __device__ __attribute__((always_inline)) inline
+
+DSA_TOPK_INLINE uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
   if (u == 0x80000000u) u = 0u;                          // -0.0 ranks with +0.0
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);     // unsigned order == float order
@@ -46,9 +53,9 @@ __device__ inline uint32_t order_key(float f) {
 // multiple of its length is contiguous and 16-byte aligned, and the 32-bin
 // runs of consecutive lanes start 36 words apart (distinct banks for 16-byte
 // reads).
-__device__ inline int hslot(uint32_t bin) { return (int)(bin + (bin >> 5) * 4); }
+DSA_TOPK_INLINE int hslot(uint32_t bin) { return (int)(bin + (bin >> 5) * 4); }
 
-__device__ inline uint32_t wave_sum(uint32_t x) {
+DSA_TOPK_INLINE uint32_t wave_sum(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(x), kWave - 1);
 }
 
@@ -57,7 +64,7 @@ __device__ inline uint32_t wave_sum(uint32_t x) {
 // the bin, bin count) to pick[0..2].  Lane l owns the PER bins
 // NB-PER*(l+1) .. NB-1-PER*l.  The histogram's total must be >= need.
 template <int NB, bool TWO = false>
-__device__ inline void pick_bin(const uint32_t* hist, uint32_t need, uint32_t* pick,
+DSA_TOPK_INLINE void pick_bin(const uint32_t* hist, uint32_t need, uint32_t* pick,
                                 const uint32_t* hist2 = nullptr) {
   constexpr int kPer = NB / kWave;  // 32 or 16
   const int lane = threadIdx.x & (kWave - 1);
@@ -92,8 +99,8 @@ __device__ inline void pick_bin(const uint32_t* hist, uint32_t need, uint32_t* p
 }
 
 // Scores of positions 4q .. 4q+3 of a row of n (positions >= n read as 0).
-// vec: the row is 16-byte aligned.
-__device__ inline f32x4 load_quad(const float* __restrict__ row, int q, int n, bool vec) {
+// vec: the row is 16-byte aligned.  (Long rows' compaction.)
+DSA_TOPK_INLINE f32x4 load_quad(const float* __restrict__ row, int q, int n, bool vec) {
   const int s = 4 * q;
   if (vec && s + 3 < n) return *reinterpret_cast<const f32x4*>(row + s);
   f32x4 v = {0.f, 0.f, 0.f, 0.f};
@@ -103,52 +110,79 @@ __device__ inline f32x4 load_quad(const float* __restrict__ row, int q, int n, b
   return v;
 }
 
-__device__ inline u32x4 quad_keys(f32x4 v) {
+DSA_TOPK_INLINE u32x4 quad_keys(f32x4 v) {
   return u32x4{order_key(v[0]), order_key(v[1]), order_key(v[2]), order_key(v[3])};
 }
 
 // Lanes below this one whose bit is set in m.
-__device__ inline uint32_t lanes_below(uint64_t m) {
+DSA_TOPK_INLINE uint32_t lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// A row's quads through a raw buffer resource.  VEC: one 16-byte load per
+// quad over round_up(n, 4) entries (the row start 16-byte aligned and the
+// storage holding that many); otherwise four 4-byte loads over exactly n.
+// Loads past the resource return zeros without touching memory, so no load
+// needs a branch; positions at or past n are never used.
+constexpr int kRawBufferWord3 = 0x00020000;  // gfx9-family raw buffer descriptor flags
+template <bool VEC>
+struct RowReader {
+  __amdgpu_buffer_rsrc_t rs;
+  // n is the same in every lane (readfirstlane tells the compiler so, which
+  // keeps the descriptor in scalar registers).
+  DSA_TOPK_INLINE RowReader(const float* row, int n)
+      : rs(__builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(row), (short)0,
+                                             __builtin_amdgcn_readfirstlane((VEC ? (n + 3) & ~3 : n) * 4),
+                                             kRawBufferWord3)) {}
+  DSA_TOPK_INLINE f32x4 quad(int q) const {
+    if (VEC) return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, q * 16, 0, 0));
+    f32x4 v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      v[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (4 * q + j) * 4, 0, 0));
+    return v;
+  }
+};
+
+// Whether a row of n entries at `row`, with `bound` >= n entries of storage
+// from there, may be read as 16-byte quads.
+DSA_TOPK_INLINE bool quads_ok(const float* row, int n, int64_t bound) {
+  return (reinterpret_cast<uintptr_t>(row) & 15) == 0 && (int64_t)((n + 3) & ~3) <= bound;
 }
 
 struct Threshold {
   uint32_t prefix, mask, need;
 };
 
-// Threshold of the k best of the n > k scores row[0] .. row[n-1], for a
-// workgroup of NT threads.  hist: kHistLdsWords LDS words, 16-byte aligned;
-// pick: 3 LDS words; cache (Cached only): round_up(n, 4) LDS words,
-// 16-byte aligned.  Begins and ends with a barrier.
 // Quads in flight per thread while a row is read: one round of them covers
-// NT * kReadBatch * 4 positions.
+// NT * kReadBatch * 4 positions, a whole cached row.
 constexpr int kReadBatch = 8;
 
 // The early part of a row's first round: its first kEarlyBatch quads per
-// thread (NT * kEarlyBatch * 4 positions), read up to `bound` positions (the
-// row's storage) before the row's length is known, so that the read overlaps
-// the request lookup.  Only this part is read blind: the rest of the row is
-// read once the length is known, so a row much shorter than its storage
-// costs little more than its own length.  Positions at or past the length
-// are never used.
+// thread (NT * kEarlyBatch * 4 positions), read before the row's length is
+// known so that the read overlaps the request lookup, within the row's
+// storage of `bound` entries (a multiple of 4, the row 16-byte aligned).
+// Only this part is read blind: the rest of the row is read once the length
+// is known, so a row much shorter than its storage costs little more than its
+// own length.  Positions at or past the length are never used.  Plain global
+// loads (lanes past the storage re-read its last quad): the lookup's loads
+// are global too, and the compiler then waits for exactly those.
 constexpr int kEarlyBatch = 2;
 template <int NT>
-__device__ inline void read_first_round(const float* __restrict__ row, bool vec, int bound,
-                                        f32x4 (&v)[kReadBatch]) {
-  const int nq = (bound + 3) >> 2;
+DSA_TOPK_INLINE void read_first_round(const float* __restrict__ row, int bound, f32x4 (&v)[kEarlyBatch]) {
+  const int last = (bound >> 2) - 1;
 #pragma unroll
-  for (int i = 0; i < kEarlyBatch; ++i) {
-    const int q = i * NT + threadIdx.x;
-    if (q < nq) v[i] = load_quad(row, q, bound, vec);
-  }
+  for (int i = 0; i < kEarlyBatch; ++i)
+    v[i] = *reinterpret_cast<const f32x4*>(row + 4 * min(i * NT + (int)threadIdx.x, last));
 }
 
-// pre (PRE only): the early part of the first round, from read_first_round
-// with a bound >= n.
-template <int NT, bool Cached, bool PRE = false>
-__device__ inline Threshold select(const float* __restrict__ row, bool vec, int n, int k,
-                                   uint32_t* cache, uint32_t* hist, uint32_t* pick,
-                                   const f32x4* pre = nullptr) {
+// Pass 0 (key bits 21..31) while the row is read, the bin pick after it.
+// Cached (n <= NT * kReadBatch * 4, one round of reads): the keys are also
+// written to cache.  pre (PRE only): the early part of the round.  Begins by
+// clearing the histograms and ends with a barrier after the pick.
+template <int NT, bool Cached, bool PRE, bool VEC>
+DSA_TOPK_INLINE Threshold pass0(const RowReader<VEC>& rd, int n, int k, uint32_t* cache, uint32_t* hist,
+                                uint32_t* pick, const f32x4* pre, bool& done) {
   constexpr int kBatch = kReadBatch;
   const int tid = threadIdx.x, wave = tid / kWave;
   const int nq = (n + 3) >> 2;
@@ -156,14 +190,15 @@ __device__ inline Threshold select(const float* __restrict__ row, bool vec, int 
   for (int i = tid; i < kHistLdsWords; i += NT) hist[i] = 0u;
   __syncthreads();
   uint32_t* h0 = hist + ((tid & 1) ? kHistCopy1 : 0);
-  // Pass 0 (key bits 21..31) while the row is read.
-  for (int q0 = 0; q0 < nq; q0 += kBatch * NT) {
+  uint32_t* dummy = hist + kHistDummy + (tid & (kWave - 1));
+  const int rounds = Cached ? 1 : (nq + kBatch * NT - 1) / (kBatch * NT);
+  for (int r = 0; r < rounds; ++r) {
+    const int q0 = r * kBatch * NT;
     f32x4 v[kBatch];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
-      const int q = q0 + i * NT + tid;
-      if (PRE && q0 == 0 && i < kEarlyBatch) v[i] = pre[i];
-      else if (q < nq) v[i] = load_quad(row, q, n, vec);
+      if (PRE && i < kEarlyBatch) v[i] = pre[i];
+      else v[i] = rd.quad(q0 + i * NT + tid);
     }
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
@@ -173,15 +208,47 @@ __device__ inline Threshold select(const float* __restrict__ row, bool vec, int 
         if (Cached) cache4[q] = u;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          if (4 * q + j < n) atomicAdd(&h0[hslot(u[j] >> 21)], 1u);
+          atomicAdd(4 * q + j < n ? &h0[hslot(u[j] >> 21)] : dummy, 1u);
       }
     }
   }
   __syncthreads();
   if (wave == 0) pick_bin<kBins, true>(hist, (uint32_t)k, pick, hist + kHistCopy1);
   __syncthreads();
-  Threshold th{pick[0] << 21, 0xFFE00000u, pick[1]};
-  bool done = pick[2] == th.need;  // the whole bin is taken
+  const Threshold th{pick[0] << 21, 0xFFE00000u, pick[1]};
+  done = pick[2] == th.need;  // the whole bin is taken
+  return th;
+}
+
+// After a refining pass's counting: the bin of its histogram holding the
+// need-th element narrows the threshold.  Begins and ends with a barrier.
+template <int NT>
+DSA_TOPK_INLINE void refine(Threshold& th, bool& done, int pass, const uint32_t* h, uint32_t* pick) {
+  const int wave = threadIdx.x / kWave;
+  const int shift = pass == 1 ? 10 : 0;
+  const uint32_t bmask = pass == 1 ? 2047u : 1023u;
+  __syncthreads();
+  if (wave == 0) {
+    if (pass == 1) pick_bin<2048>(h, th.need, pick);
+    else pick_bin<1024>(h, th.need, pick);
+  }
+  __syncthreads();
+  th.prefix |= pick[0] << shift;
+  th.mask |= bmask << shift;
+  th.need = pick[1];
+  done = pick[2] == th.need;
+}
+
+// Threshold of the k best of the n > k scores of a row longer than the LDS
+// cache, re-reading the row in every pass.  hist: kHistLdsWords LDS words,
+// 16-byte aligned; pick: 3 LDS words.  Begins and ends with a barrier.
+template <int NT, bool VEC>
+DSA_TOPK_INLINE Threshold select(const RowReader<VEC>& rd, int n, int k, uint32_t* hist, uint32_t* pick) {
+  constexpr int kBatch = kReadBatch;
+  const int tid = threadIdx.x;
+  const int nq = (n + 3) >> 2;
+  bool done;
+  Threshold th = pass0<NT, false, false, VEC>(rd, n, k, nullptr, hist, pick, nullptr, done);
   // Passes 1 (bits 10..20) and 2 (bits 0..9) over the elements of the chosen prefix.
 #pragma unroll 1
   for (int pass = 1; pass < 3 && !done; ++pass) {
@@ -193,41 +260,135 @@ __device__ inline Threshold select(const float* __restrict__ row, bool vec, int 
     for (int q0 = 0; q0 < nq; q0 += kBatch * NT) {
       u32x4 u[kBatch];
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i) {
-        const int q = q0 + i * NT + tid;
-        if (q < nq) u[i] = Cached ? cache4[q] : quad_keys(load_quad(row, q, n, vec));
-      }
+      for (int i = 0; i < kBatch; ++i) u[i] = quad_keys(rd.quad(q0 + i * NT + tid));
 #pragma unroll
       for (int i = 0; i < kBatch; ++i) {
         const int q = q0 + i * NT + tid;
-        if (q < nq) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (4 * q + j < n && (u[i][j] & th.mask) == th.prefix)
-              atomicAdd(&h[hslot((u[i][j] >> shift) & bmask)], 1u);
-        }
+        for (int j = 0; j < 4; ++j)
+          if (q < nq && 4 * q + j < n && (u[i][j] & th.mask) == th.prefix)
+            atomicAdd(&h[hslot((u[i][j] >> shift) & bmask)], 1u);
       }
     }
-    __syncthreads();
-    if (wave == 0) {
-      if (pass == 1) pick_bin<2048>(h, th.need, pick);
-      else pick_bin<1024>(h, th.need, pick);
-    }
-    __syncthreads();
-    th.prefix |= pick[0] << shift;
-    th.mask |= bmask << shift;
-    th.need = pick[1];
-    done = pick[2] == th.need;
+    refine<NT>(th, done, pass, h, pick);
   }
   __syncthreads();  // pick may be rewritten by the next selection
   return th;
+}
+
+// Most quads a thread holds when a cached row is walked from registers: rows
+// of up to 4 * NT * kRegQuads positions (36864 at NT = 1024).
+constexpr int kRegQuads = 9;
+
+// Selection of the k best of the n > k scores of a row of at most
+// 4 * NT * kReadBatch positions, calling emit(o, s) for every selected
+// position s with o its rank (0 .. k-1) in ascending position order; the
+// calls go out in order of o, consecutive o to consecutive threads.
+//
+// Pass 0 reads the row (coalesced, quads interleaved over the threads) and
+// caches its keys in LDS.  Then every thread takes a contiguous run of Q
+// quads from the cache into registers, Q odd so that the 16-byte reads of 16
+// lanes, 16 Q bytes apart, meet 16 distinct bank quartets.  The later passes
+// count the runs' keys from registers.  The compaction counts each run's
+// selected elements, places the runs by one packed wave scan and one
+// workgroup prefix over the wave totals, and stages every selected position
+// at its rank in LDS (over the cache, which every thread has read by then),
+// from where the workgroup emits them.
+// cache: 4 * NT * kReadBatch LDS words, 16-byte aligned (k <= that many);
+// hist: kHistLdsWords LDS words, 16-byte aligned; pick: 3 LDS words; wcount:
+// NT / 64 LDS words.  Begins and ends with a barrier.
+template <int NT, bool PRE, bool VEC, typename Emit>
+DSA_TOPK_INLINE void select_cached(const RowReader<VEC>& rd, int n, int k, uint32_t* cache, uint32_t* hist,
+                                   uint32_t* pick, uint32_t* wcount, Emit emit, const f32x4* pre = nullptr) {
+  static_assert(kRegQuads * NT >= kReadBatch * NT + NT, "a run of Q <= kRegQuads quads covers a cached row");
+  constexpr int kW = NT / kWave;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int nq = (n + 3) >> 2;
+  bool done;
+  Threshold th = pass0<NT, true, PRE, VEC>(rd, n, k, cache, hist, pick, pre, done);
+  // This thread's run: quads tid*Q .. tid*Q+Q-1 (the cache was complete at
+  // pass 0's last barrier).  Positions at or past n hold key 0, the lowest:
+  // they all lie after the row's last position, so even when 0 is the
+  // threshold prefix they are never staged (at least `need` elements of the
+  // row at the prefix come first); and were they counted in a refining pass's
+  // lowest bin, the pick would not change, since the need-th element lies in
+  // that bin only when no other bin can hold it.
+  const int Q = __builtin_amdgcn_readfirstlane(((nq + NT - 1) / NT) | 1);
+  const int q_first = tid * Q;
+  const int p_first = 4 * q_first;
+  const u32x4* cache4 = reinterpret_cast<const u32x4*>(cache);
+  u32x4 r[kRegQuads];
+#pragma unroll
+  for (int j = 0; j < kRegQuads; ++j) {
+    r[j] = u32x4{0u, 0u, 0u, 0u};
+    if (j < Q) {
+      if (q_first + j < nq) r[j] = cache4[q_first + j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[j][e] = p_first + 4 * j + e < n ? r[j][e] : 0u;
+    }
+  }
+#pragma unroll 1
+  for (int pass = 1; pass < 3 && !done; ++pass) {
+    const int shift = pass == 1 ? 10 : 0;
+    const uint32_t bmask = pass == 1 ? 2047u : 1023u;
+    uint32_t* h = pass == 1 ? hist + kHistPass1 : hist;
+    if (pass == 1)  // pass 0's histograms were read before the last barrier; pass 2 reuses the first
+      for (int i = tid; i < kHistWords; i += NT) hist[i] = 0u;
+#pragma unroll
+    for (int j = 0; j < kRegQuads; ++j) {
+      if (j < Q) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if ((r[j][e] & th.mask) == th.prefix) atomicAdd(&h[hslot((r[j][e] >> shift) & bmask)], 1u);
+      }
+    }
+    refine<NT>(th, done, pass, h, pick);
+  }
+  // Compaction.  Bit 4j+e of gm / em: element e of quad j of the run is
+  // above / at the threshold prefix.  Counts packed: above in the low half,
+  // at in the high half (a row's totals stay below 2^16).
+  uint64_t gm = 0, em = 0;
+#pragma unroll
+  for (int j = 0; j < kRegQuads; ++j) {
+    if (j < Q) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t u = r[j][e] & th.mask;
+        gm |= (uint64_t)(u > th.prefix ? 1u : 0u) << (4 * j + e);
+        em |= (uint64_t)(u == th.prefix ? 1u : 0u) << (4 * j + e);
+      }
+    }
+  }
+  const uint32_t cnt = (uint32_t)__popcll(gm) | ((uint32_t)__popcll(em) << 16);
+  const uint32_t inc = wave_incl_scan(cnt);
+  if (lane == kWave - 1) wcount[wave] = inc;
+  __syncthreads();  // also: every thread has read its run from the cache
+  uint32_t before = inc - cnt;
+#pragma unroll
+  for (int w = 0; w < kW; ++w) before += w < wave ? wcount[w] : 0u;
+  uint32_t gt = before & 0xFFFFu, eq = before >> 16;
+  // The run's selected elements in position order, each staged at its rank.
+  for (uint64_t m = gm | em; m != 0; m &= m - 1) {
+    const int b = __builtin_ctzll(m);
+    const uint32_t pos = (uint32_t)(p_first + b);
+    if ((gm >> b) & 1u) {
+      cache[gt + min(eq, th.need)] = pos;
+      ++gt;
+    } else {
+      if (eq < th.need) cache[gt + eq] = pos;
+      ++eq;
+    }
+  }
+  __syncthreads();
+  for (int o = tid; o < k; o += NT) emit((uint32_t)o, (int)cache[o]);
+  __syncthreads();  // pick, wcount and the cache may be rewritten by the next selection
 }
 
 // Calls emit(o, s) for every selected position s, o = its rank (0 .. k-1) in
 // ascending position order.  Selected: (key & mask) > prefix, or == prefix
 // among the first `need` such positions.  wcount: 2 * NT / 64 LDS words.
 template <int NT, bool Cached, typename Emit>
-__device__ inline void compact(const float* __restrict__ row, bool vec, int n, const uint32_t* cache,
+DSA_TOPK_INLINE void compact(const float* __restrict__ row, bool vec, int n, const uint32_t* cache,
                                Threshold th, uint32_t* wcount, Emit emit) {
   constexpr int kW = NT / kWave;
   constexpr int kChunk = 4 * kWave;          // positions per wave step: a quad per lane
@@ -308,65 +469,6 @@ __device__ inline void compact(const float* __restrict__ row, bool vec, int n, c
     }
   }
   __syncthreads();  // wcount may be rewritten by the next compaction
-}
-
-// compact() for a row cached in LDS as keys, in one walk of the row: each
-// wave stages the positions of its range's elements above or at the
-// threshold prefix in its own part of the cache (tagged by bit 31 when at
-// it; the staged count never passes the positions already read, so it
-// overwrites only keys already consumed), then, once the waves' counts are
-// known, walks its staged list to apply the global cut among the elements at
-// the prefix and emit.  Same result as compact().
-template <int NT, typename Emit>
-__device__ inline void compact_cached(int n, uint32_t* cache, Threshold th, uint32_t* wcount, Emit emit) {
-  constexpr int kW = NT / kWave;
-  constexpr int kBatch = 8;  // 64-position steps in flight
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int R = ((n + kW - 1) / kW + kWave - 1) / kWave * kWave;
-  const int r0 = wave * R, r1 = min(n, r0 + R);
-  uint32_t n_gt = 0, n_eq = 0, n_st = 0;  // wave-uniform
-  for (int c = r0; c < r1; c += kBatch * kWave) {
-    uint32_t u[kBatch];
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const int s = c + b * kWave + lane;
-      u[b] = s < r1 ? cache[s] & th.mask : 0u;
-    }
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const int s = c + b * kWave + lane;
-      const bool in = s < r1;
-      const bool gt = in && u[b] > th.prefix, eq = in && u[b] == th.prefix;
-      const uint64_t mg = __ballot(gt), me = __ballot(eq), m = mg | me;
-      if (gt || eq) cache[r0 + n_st + lanes_below(m)] = (uint32_t)s | (eq ? 0x80000000u : 0u);
-      n_st += (uint32_t)__popcll(m);
-      n_gt += (uint32_t)__popcll(mg);
-      n_eq += (uint32_t)__popcll(me);
-    }
-  }
-  if (lane == 0) {
-    wcount[wave] = n_gt;
-    wcount[kW + wave] = n_eq;
-  }
-  __syncthreads();
-  uint32_t gt_before = 0, run_eq = 0;
-  for (int w = 0; w < wave; ++w) {
-    gt_before += wcount[w];
-    run_eq += wcount[kW + w];
-  }
-  uint32_t run_sel = gt_before + min(run_eq, th.need);
-  for (uint32_t i0 = 0; i0 < n_st; i0 += kWave) {
-    const bool in = i0 + lane < n_st;
-    const uint32_t e = in ? cache[r0 + i0 + lane] : 0u;
-    const bool at = in && (e >> 31) != 0u;
-    const uint64_t meq = __ballot(at);
-    const bool sel = in && (!at || run_eq + lanes_below(meq) < th.need);
-    const uint64_t msel = __ballot(sel);
-    if (sel) emit(run_sel + lanes_below(msel), (int)(e & 0x7FFFFFFFu));
-    run_sel += (uint32_t)__popcll(msel);
-    run_eq += (uint32_t)__popcll(meq);
-  }
-  __syncthreads();  // wcount and the cache may be rewritten by the next row
 }
 
 }  // namespace topk
