@@ -3,11 +3,13 @@
 //
 // Output: the selected positions in ascending order, then -1.  When
 // pos(t)+1 <= k the row keeps every valid position (mstar PR 387, section
-// "Body": below index_topk the pick is all tokens).  One workgroup of 1024
-// threads per query row; the selection itself (order, ties, passes,
-// compaction) is in topk_select.h.  Rows of up to 32768 entries are cached in
-// LDS as keys after one read; longer rows are re-read in each pass (the two
-// cases are separate instantiations), or, when the caller gives a workspace,
+// "Body": below index_topk the pick is all tokens).  A workgroup of 1024
+// threads selects one query row at a time: one row per workgroup when the
+// rows fit the CUs (topk_radix), else a workgroup per CU walking its rows
+// with the next row read ahead (topk_rows).  The selection itself (order,
+// ties, passes, compaction) is in topk_select.h.  Rows of up to 32768 entries
+// are cached in LDS after one read and then selected from registers; longer
+// rows are re-read in each pass, or, when the caller gives a workspace,
 // selected in two levels (topk_segments, then topk_merge).
 #include "dsa_device.h"
 #include "dsa_launch.h"
@@ -22,15 +24,16 @@ constexpr int kCache = 32768;
 
 // Top-K of row[0, n): emit(o, s) for the o-th selected position s, o < K, in
 // ascending s.  Cached: n <= kCache.  VEC: the row may be read as 16-byte
-// quads (topk::quads_ok); PRE implies both, with pre its early reads.
-template <bool Cached, bool PRE, bool VEC, typename Emit>
+// quads (topk::quads_ok).  NPRE > 0 (cached, VEC rows only): pre holds the
+// first NPRE quads per thread of the row's read.
+template <bool Cached, int NPRE, bool VEC, typename Emit>
 __device__ __attribute__((always_inline)) inline void select_emit(const float* __restrict__ row, int n, int K,
                                                                   uint32_t* cache, uint32_t* hist, uint32_t* wcount,
                                                                   uint32_t* pick, Emit emit,
                                                                   const f32x4* pre = nullptr) {
   const topk::RowReader<VEC> rd(row, n);
   if (Cached) {
-    topk::select_cached<kThreads, PRE, VEC>(rd, n, K, cache, hist, pick, wcount, emit, pre);
+    topk::select_cached<kThreads, NPRE, VEC>(rd, n, K, cache, hist, pick, wcount, emit, pre);
   } else {
     const topk::Threshold th = topk::select<kThreads, VEC>(rd, n, K, hist, pick);
     topk::compact<kThreads, false>(row, VEC, n, cache, th, wcount, [emit, K](uint32_t o, int s) {
@@ -46,9 +49,53 @@ __device__ __attribute__((always_inline)) inline void select_cached_row(const fl
                                                                         int64_t bound, int K, uint32_t* cache,
                                                                         uint32_t* hist, uint32_t* wcount,
                                                                         uint32_t* pick, Emit emit) {
-  if (topk::quads_ok(row, n, bound)) select_emit<true, false, true>(row, n, K, cache, hist, wcount, pick, emit);
-  else select_emit<true, false, false>(row, n, K, cache, hist, wcount, pick, emit);
+  if (topk::quads_ok(row, n, bound)) select_emit<true, 0, true>(row, n, K, cache, hist, wcount, pick, emit);
+  else select_emit<true, 0, false>(row, n, K, cache, hist, wcount, pick, emit);
 }
+
+// The thread's index as a value the compiler cannot see through: in a loop
+// over rows, everything derived from it is then computed inside the loop
+// instead of being hoisted and held (or spilled) across it.
+__device__ __attribute__((always_inline)) inline int opaque_tid() {
+  int x = (int)threadIdx.x;
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// The request lookup's first R rounds (requests 0 .. R * 64 - 1, as in
+// locate_row): their loads are the same for every row, so a workgroup that
+// handles several rows issues them once.  Later rounds are left to
+// locate_row.
+template <int R>
+struct RequestTable {
+  int lo[R], hi[R], sl[R];
+  __device__ __attribute__((always_inline)) void load(const int32_t* __restrict__ cu_q,
+                                                      const int32_t* __restrict__ seq_lens, int B, int lane) {
+#pragma unroll
+    for (int c = 0; c < R; ++c) {
+      const int i = min(c * kWave + lane, B - 1);  // B >= 1
+      lo[c] = cu_q[i];
+      hi[c] = cu_q[i + 1];
+      sl[c] = seq_lens[i];
+    }
+  }
+  __device__ __attribute__((always_inline)) RowLoc find(const int32_t* __restrict__ cu_q,
+                                                        const int32_t* __restrict__ seq_lens, int B, int t,
+                                                        int lane) const {
+    RowLoc loc{-1, 0};
+#pragma unroll
+    for (int c = 0; c < R; ++c) {
+      const uint64_t m = __ballot(c * kWave + lane < B && lo[c] <= t && t < hi[c]);
+      if (m != 0 && loc.b < 0) {
+        const int src = __ffsll((unsigned long long)m) - 1;
+        const int q0 = __shfl(lo[c], src), q1 = __shfl(hi[c], src), s = __shfl(sl[c], src);
+        loc = RowLoc{c * kWave + src, s - (q1 - q0) + (t - q0)};
+      }
+    }
+    if (loc.b < 0) loc = locate_row(cu_q, seq_lens, B, t);
+    return loc;
+  }
+};
 
 __global__ __launch_bounds__(kThreads) void topk_radix(const int32_t* __restrict__ cu_q,
                                                        const int32_t* __restrict__ seq_lens, int B,
@@ -66,31 +113,14 @@ __global__ __launch_bounds__(kThreads) void topk_radix(const int32_t* __restrict
   // aligned, have the first part of their read issued before the lookup that
   // gives the row's length.
   const bool early = ld >= 4 && ld <= kCache && (ld & 3) == 0 && (reinterpret_cast<uintptr_t>(row) & 15) == 0;
-  // The lookup's first round (requests 0 .. 255, as in locate_row) is
-  // written out here so that the row read goes out between its loads and
-  // its search; later rounds are left to locate_row.
+  // The lookup's loads go out first, then the row read, then the lookup's
+  // search.
   const int lane = tid & (kWave - 1);
-  int lo[4], hi[4], sl[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int i = min(c * kWave + lane, B - 1);  // B >= 1: this row exists
-    lo[c] = cu_q[i];
-    hi[c] = cu_q[i + 1];
-    sl[c] = seq_lens[i];
-  }
-  f32x4 pre[topk::kEarlyBatch];
-  if (early) topk::read_first_round<kThreads>(row, (int)ld, pre);
-  RowLoc loc{-1, 0};
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const uint64_t m = __ballot(c * kWave + lane < B && lo[c] <= t && t < hi[c]);
-    if (m != 0 && loc.b < 0) {
-      const int src = __ffsll((unsigned long long)m) - 1;
-      const int q0 = __shfl(lo[c], src), q1 = __shfl(hi[c], src), s = __shfl(sl[c], src);
-      loc = RowLoc{c * kWave + src, s - (q1 - q0) + (t - q0)};
-    }
-  }
-  if (loc.b < 0) loc = locate_row(cu_q, seq_lens, B, t);
+  RequestTable<4> req;
+  req.load(cu_q, seq_lens, B, lane);
+  f32x4 pre[topk::kReadBatch];
+  if (early) topk::read_first_round<kThreads, topk::kEarlyBatch>(row, (int)ld, pre);
+  const RowLoc loc = req.find(cu_q, seq_lens, B, t, lane);
   const int n = (int)max<int64_t>(0, min<int64_t>((int64_t)loc.pos + 1, ld));
   int32_t* out = idx + (int64_t)t * K;
 
@@ -99,9 +129,53 @@ __global__ __launch_bounds__(kThreads) void topk_radix(const int32_t* __restrict
     return;
   }
   auto emit = [out](uint32_t o, int s) { out[o] = s; };
-  if (early) select_emit<true, true, true>(row, n, K, cache, hist, wcount, pick, emit, pre);
+  if (early) select_emit<true, topk::kEarlyBatch, true>(row, n, K, cache, hist, wcount, pick, emit, pre);
   else if (n <= kCache) select_cached_row(row, n, ld, K, cache, hist, wcount, pick, emit);
-  else select_emit<false, false, false>(row, n, K, cache, hist, wcount, pick, emit);  // rare: no workspace
+  else select_emit<false, 0, false>(row, n, K, cache, hist, wcount, pick, emit);  // rare: no workspace
+}
+
+// Persistent form for launches with more rows than CUs: workgroup w takes
+// rows w, w + G, ... (G = gridDim.x).  Once a row is in registers (after its
+// pass 0), the next row's whole storage is read blind into the registers pass
+// 0 took the row from, so that read runs under the row's refining passes and
+// compaction; the request lookup's loads go out once.  Needs a row storage
+// that fits the cache as whole 16-byte quads (4 <= ld <= kCache, ld % 4 == 0,
+// scores 16-byte aligned).
+__global__ __launch_bounds__(kThreads) void topk_rows(const int32_t* __restrict__ cu_q,
+                                                      const int32_t* __restrict__ seq_lens, int B,
+                                                      const float* __restrict__ scores, int64_t ld, int K,
+                                                      int32_t* __restrict__ idx, int row_lo, int rows) {
+  __shared__ __align__(16) uint32_t cache[kCache];
+  __shared__ __align__(16) uint32_t hist[topk::kHistLdsWords];
+  __shared__ uint32_t wcount[2 * kThreads / kWave];
+  __shared__ uint32_t pick[3];
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int G = (int)gridDim.x;
+  RequestTable<1> req;  // registers are scarce here: one round, later ones from locate_row
+  req.load(cu_q, seq_lens, B, lane);
+  f32x4 nxt[topk::kReadBatch];
+  topk::read_first_round<kThreads, topk::kReadBatch>(scores + (int64_t)blockIdx.x * ld, (int)ld, nxt);
+  for (int rr = (int)blockIdx.x; rr < rows; rr += G) {
+    const int tid_r = opaque_tid();
+    const int t = row_lo + rr;
+    const float* row = scores + (int64_t)rr * ld;
+    const RowLoc loc = req.find(cu_q, seq_lens, B, t, lane);
+    const int n = (int)max<int64_t>(0, min<int64_t>((int64_t)loc.pos + 1, ld));
+    int32_t* out = idx + (int64_t)t * K;
+    // the next row of this workgroup (the last row reads itself again: the
+    // read stays in bounds and goes unused)
+    const float* row_next = scores + (int64_t)(rr + G < rows ? rr + G : rr) * ld;
+    auto read_next = [&]() { topk::read_first_round<kThreads, topk::kReadBatch>(row_next, (int)ld, nxt, tid_r); };
+    if (n <= K) {
+      for (int j = tid_r; j < K; j += kThreads) out[j] = j < n ? j : -1;
+      read_next();
+      continue;
+    }
+    topk::select_cached<kThreads, topk::kReadBatch, true>(topk::RowReader<true>(row, n), n, K, cache, hist, pick,
+                                                          wcount, [out](uint32_t o, int s) { out[o] = s; }, nxt,
+                                                          read_next, tid_r);
+  }
 }
 
 // Two-level selection for rows longer than the LDS cache.  Level 1: each
@@ -172,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void topk_merge(const int32_t* __restrict
   const int32_t* ix = cand_ix + (int64_t)(t - row_lo) * n2;
   auto emit = [out, ix, n2](uint32_t o, int s) { out[o] = ix[min(s, n2 - 1)]; };  // s < n2 always
   if (n2 <= kCache) select_cached_row(row, n2, n2, K, cache, hist, wcount, pick, emit);
-  else select_emit<false, false, false>(row, n2, K, cache, hist, wcount, pick, emit);
+  else select_emit<false, 0, false>(row, n2, K, cache, hist, wcount, pick, emit);
 }
 
 }  // namespace
@@ -189,6 +263,8 @@ hipError_t launch_topk(const BatchArgs& ba, const float* scores, int64_t ld, int
   if (row_hi <= row_lo) return hipSuccess;
   const int rows = row_hi - row_lo;
   const size_t need = topk_workspace_bytes(rows, ba.max_seq_len, k);
+  // topk_rows reads rows blind as whole 16-byte quads
+  const bool rows_ok = ld >= 4 && ld % 4 == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
   if (need > 0 && ws != nullptr && ws_bytes >= need) {
     const int segs = (ba.max_seq_len + kSegLen - 1) / kSegLen;
     float* cand_sc = static_cast<float*>(ws);
@@ -202,8 +278,12 @@ hipError_t launch_topk(const BatchArgs& ba, const float* scores, int64_t ld, int
                        k, idx, row_lo, segs, cand_sc, cand_ix);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(topk_radix, dim3(rows), dim3(kThreads), 0, stream, ba.cu_q,
-                     ba.seq_lens, ba.batch, scores, ld, k, idx, row_lo);
+  if (rows_ok && ld <= kCache && rows > device_cu_count())
+    hipLaunchKernelGGL(topk_rows, dim3(device_cu_count()), dim3(kThreads), 0, stream, ba.cu_q, ba.seq_lens,
+                       ba.batch, scores, ld, k, idx, row_lo, rows);
+  else
+    hipLaunchKernelGGL(topk_radix, dim3(rows), dim3(kThreads), 0, stream, ba.cu_q,
+                       ba.seq_lens, ba.batch, scores, ld, k, idx, row_lo);
   return hipGetLastError();
 }
 

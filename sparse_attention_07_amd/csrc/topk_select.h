@@ -168,23 +168,26 @@ constexpr int kReadBatch = 8;
 // loads (lanes past the storage re-read its last quad): the lookup's loads
 // are global too, and the compiler then waits for exactly those.
 constexpr int kEarlyBatch = 2;
-template <int NT>
-DSA_TOPK_INLINE void read_first_round(const float* __restrict__ row, int bound, f32x4 (&v)[kEarlyBatch]) {
+// The first NPRE quads per thread of a row's round, from a row storage of
+// `bound` entries (bound >= 4 and a multiple of 4, the row 16-byte aligned).
+template <int NT, int NPRE>
+DSA_TOPK_INLINE void read_first_round(const float* __restrict__ row, int bound, f32x4 (&v)[kReadBatch],
+                                      int tid = (int)threadIdx.x) {
   const int last = (bound >> 2) - 1;
 #pragma unroll
-  for (int i = 0; i < kEarlyBatch; ++i)
-    v[i] = *reinterpret_cast<const f32x4*>(row + 4 * min(i * NT + (int)threadIdx.x, last));
+  for (int i = 0; i < NPRE; ++i) v[i] = *reinterpret_cast<const f32x4*>(row + 4 * min(i * NT + tid, last));
 }
 
 // Pass 0 (key bits 21..31) while the row is read, the bin pick after it.
 // Cached (n <= NT * kReadBatch * 4, one round of reads): the keys are also
-// written to cache.  pre (PRE only): the early part of the round.  Begins by
-// clearing the histograms and ends with a barrier after the pick.
-template <int NT, bool Cached, bool PRE, bool VEC>
+// written to cache.  pre: the round's first NPRE quads per thread, already
+// read (read_first_round).  Begins by clearing the histograms and ends with a
+// barrier after the pick.
+template <int NT, bool Cached, int NPRE, bool VEC>
 DSA_TOPK_INLINE Threshold pass0(const RowReader<VEC>& rd, int n, int k, uint32_t* cache, uint32_t* hist,
-                                uint32_t* pick, const f32x4* pre, bool& done) {
+                                uint32_t* pick, const f32x4* pre, bool& done, int tid) {
   constexpr int kBatch = kReadBatch;
-  const int tid = threadIdx.x, wave = tid / kWave;
+  const int wave = tid / kWave;
   const int nq = (n + 3) >> 2;
   u32x4* cache4 = reinterpret_cast<u32x4*>(cache);
   for (int i = tid; i < kHistLdsWords; i += NT) hist[i] = 0u;
@@ -197,7 +200,7 @@ DSA_TOPK_INLINE Threshold pass0(const RowReader<VEC>& rd, int n, int k, uint32_t
     f32x4 v[kBatch];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
-      if (PRE && i < kEarlyBatch) v[i] = pre[i];
+      if (i < NPRE) v[i] = pre[i];
       else v[i] = rd.quad(q0 + i * NT + tid);
     }
 #pragma unroll
@@ -223,8 +226,8 @@ DSA_TOPK_INLINE Threshold pass0(const RowReader<VEC>& rd, int n, int k, uint32_t
 // After a refining pass's counting: the bin of its histogram holding the
 // need-th element narrows the threshold.  Begins and ends with a barrier.
 template <int NT>
-DSA_TOPK_INLINE void refine(Threshold& th, bool& done, int pass, const uint32_t* h, uint32_t* pick) {
-  const int wave = threadIdx.x / kWave;
+DSA_TOPK_INLINE void refine(Threshold& th, bool& done, int pass, const uint32_t* h, uint32_t* pick, int tid) {
+  const int wave = tid / kWave;
   const int shift = pass == 1 ? 10 : 0;
   const uint32_t bmask = pass == 1 ? 2047u : 1023u;
   __syncthreads();
@@ -245,10 +248,10 @@ DSA_TOPK_INLINE void refine(Threshold& th, bool& done, int pass, const uint32_t*
 template <int NT, bool VEC>
 DSA_TOPK_INLINE Threshold select(const RowReader<VEC>& rd, int n, int k, uint32_t* hist, uint32_t* pick) {
   constexpr int kBatch = kReadBatch;
-  const int tid = threadIdx.x;
+  const int tid = (int)threadIdx.x;
   const int nq = (n + 3) >> 2;
   bool done;
-  Threshold th = pass0<NT, false, false, VEC>(rd, n, k, nullptr, hist, pick, nullptr, done);
+  Threshold th = pass0<NT, false, 0, VEC>(rd, n, k, nullptr, hist, pick, nullptr, done, tid);
   // Passes 1 (bits 10..20) and 2 (bits 0..9) over the elements of the chosen prefix.
 #pragma unroll 1
   for (int pass = 1; pass < 3 && !done; ++pass) {
@@ -270,7 +273,7 @@ DSA_TOPK_INLINE Threshold select(const RowReader<VEC>& rd, int n, int k, uint32_
             atomicAdd(&h[hslot((u[i][j] >> shift) & bmask)], 1u);
       }
     }
-    refine<NT>(th, done, pass, h, pick);
+    refine<NT>(th, done, pass, h, pick, tid);
   }
   __syncthreads();  // pick may be rewritten by the next selection
   return th;
@@ -293,19 +296,26 @@ constexpr int kRegQuads = 9;
 // selected elements, places the runs by one packed wave scan and one
 // workgroup prefix over the wave totals, and stages every selected position
 // at its rank in LDS (over the cache, which every thread has read by then),
-// from where the workgroup emits them.
+// from where the workgroup emits them.  pre: the first NPRE quads per thread
+// of pass 0's round, already read.  after_pass0() runs once the row is in
+// registers: pre (and the cache until the compaction) is free from then on,
+// so a caller can start reading its next row there.
 // cache: 4 * NT * kReadBatch LDS words, 16-byte aligned (k <= that many);
 // hist: kHistLdsWords LDS words, 16-byte aligned; pick: 3 LDS words; wcount:
 // NT / 64 LDS words.  Begins and ends with a barrier.
-template <int NT, bool PRE, bool VEC, typename Emit>
+struct NoHook {
+  DSA_TOPK_INLINE void operator()() const {}
+};
+template <int NT, int NPRE, bool VEC, typename Emit, typename Hook = NoHook>
 DSA_TOPK_INLINE void select_cached(const RowReader<VEC>& rd, int n, int k, uint32_t* cache, uint32_t* hist,
-                                   uint32_t* pick, uint32_t* wcount, Emit emit, const f32x4* pre = nullptr) {
+                                   uint32_t* pick, uint32_t* wcount, Emit emit, const f32x4* pre = nullptr,
+                                   Hook after_pass0 = Hook(), int tid = (int)threadIdx.x) {
   static_assert(kRegQuads * NT >= kReadBatch * NT + NT, "a run of Q <= kRegQuads quads covers a cached row");
   constexpr int kW = NT / kWave;
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int lane = tid % kWave, wave = tid / kWave;
   const int nq = (n + 3) >> 2;
   bool done;
-  Threshold th = pass0<NT, true, PRE, VEC>(rd, n, k, cache, hist, pick, pre, done);
+  Threshold th = pass0<NT, true, NPRE, VEC>(rd, n, k, cache, hist, pick, pre, done, tid);
   // This thread's run: quads tid*Q .. tid*Q+Q-1 (the cache was complete at
   // pass 0's last barrier).  Positions at or past n hold key 0, the lowest:
   // they all lie after the row's last position, so even when 0 is the
@@ -327,6 +337,7 @@ DSA_TOPK_INLINE void select_cached(const RowReader<VEC>& rd, int n, int k, uint3
       for (int e = 0; e < 4; ++e) r[j][e] = p_first + 4 * j + e < n ? r[j][e] : 0u;
     }
   }
+  after_pass0();
 #pragma unroll 1
   for (int pass = 1; pass < 3 && !done; ++pass) {
     const int shift = pass == 1 ? 10 : 0;
@@ -342,7 +353,7 @@ DSA_TOPK_INLINE void select_cached(const RowReader<VEC>& rd, int n, int k, uint3
           if ((r[j][e] & th.mask) == th.prefix) atomicAdd(&h[hslot((r[j][e] >> shift) & bmask)], 1u);
       }
     }
-    refine<NT>(th, done, pass, h, pick);
+    refine<NT>(th, done, pass, h, pick, tid);
   }
   // Compaction.  Bit 4j+e of gm / em: element e of quad j of the run is
   // above / at the threshold prefix.  Counts packed: above in the low half,

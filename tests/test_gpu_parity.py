@@ -210,6 +210,71 @@ def test_topk_rows_read_before_their_length_is_known(K):
     _parity.check_idx_exact(idx, ref)
 
 
+@pytest.mark.parametrize("K", [7, 2048])
+def test_topk_persistent_rows(K):
+    # More rows than CUs: workgroups walk several rows each and read the next
+    # row ahead.  Rows of mixed lengths (some with n <= K), ties, NaN and
+    # +-inf past each length; each row its own request, so the lookup also
+    # goes past its first round of 64 requests.
+    from sparse_attention_07_amd import dsa
+    g = torch.Generator().manual_seed(300 + K)
+    cycle = [1, K - 1, K, K + 1, 3 * K + 5, 1000, 4097, 20000, 32767, 32768]
+    lens = [max(1, cycle[i % len(cycle)]) for i in range(600)]
+    ld = 32768
+    scores = torch.full((len(lens), ld), float("nan"))
+    scores[:, 1::7] = float("inf")
+    scores[:, 2::7] = -float("inf")
+    rows = []
+    for i, n in enumerate(lens):
+        if i % 3 == 0:
+            r = torch.randint(-3, 4, (n,), generator=g).float() / 2
+        elif i % 3 == 1:
+            r = torch.randint(-1000, 1000, (n,), generator=g).float() / 64
+        else:
+            r = torch.randn(n, generator=g)
+        r[::13] = -0.0
+        scores[i, :n] = r
+        rows.append(r)
+    sb = _row_batch(rows, K)
+    ref = oracle.topk(sb, np.where(np.isfinite(scores.numpy()), scores.numpy(), 0.0).astype(np.float64), k=K)
+    _say("topk persistent rows K=%d" % K)
+    b = dsa.make_batch(sb.cu_q.to(DEV), sb.seq_lens_t.to(DEV), sb.page_table.to(DEV), len(rows), 1,
+                       ld, 16, 1)
+    idx = torch.full((len(rows), K), 12345, dtype=torch.int32, device=DEV)
+    dsa.dsa_topk(b, scores.to(DEV), ld, K, idx, None, 0)
+    torch.cuda.synchronize()
+    _parity.check_idx_exact(idx, ref)
+
+
+@pytest.mark.parametrize("K", [64, 2048])
+def test_topk_many_segments(K):
+    # Rows longer than the LDS cache in more (row, segment) items than CUs,
+    # short rows and rows ending inside a segment included, stale workspace.
+    from sparse_attention_07_amd import dsa
+    g = torch.Generator().manual_seed(400 + K)
+    cycle = [70001, 32769, 65536, 40000, K + 1, 1, 69999, 32768, 50001, 3 * K + 5]
+    lens = [cycle[i % len(cycle)] for i in range(100)]
+    ld = 70004
+    scores = torch.full((len(lens), ld), float("nan"))
+    rows = []
+    for i, n in enumerate(lens):
+        r = (torch.randint(-3, 4, (n,), generator=g).float() / 2 if i % 2 else torch.randn(n, generator=g))
+        scores[i, :n] = r
+        rows.append(r)
+    sb = _row_batch(rows, K)
+    ref = oracle.topk(sb, np.where(np.isfinite(scores.numpy()), scores.numpy(), 0.0).astype(np.float64), k=K)
+    _say("topk persistent segments K=%d" % K)
+    b = dsa.make_batch(sb.cu_q.to(DEV), sb.seq_lens_t.to(DEV), sb.page_table.to(DEV), len(rows), 1,
+                       ld, 16, 1)
+    idx = torch.full((len(rows), K), 12345, dtype=torch.int32, device=DEV)
+    ws_bytes = dsa.dsa_topk_workspace_bytes(len(rows), ld, K)
+    assert ws_bytes > 0
+    ws = torch.full((ws_bytes,), 0xAB, dtype=torch.uint8, device=DEV)
+    dsa.dsa_topk(b, scores.to(DEV), ld, K, idx, ws, ws_bytes)
+    torch.cuda.synchronize()
+    _parity.check_idx_exact(idx, ref)
+
+
 def test_mla_invalid_entries_and_closed_forms():
     from sparse_attention_07_amd import dsa
     from sparse_attention_07_amd.path import DSAPath
