@@ -18,6 +18,13 @@ Parity status of each function (what pins it; see tests/test_oracle_pins.py):
   sparse_mla    pinned: dense invariant below K vs torch SDPA, absorption
                 identity, mask equivalence, closed forms (K=1, q=0), re-masking
   e4m3 decode   pinned: all 256 codes against torch.float8_e4m3fn
+  e4m3 encode   pinned: round trip of every finite code; every tie, its two
+                float32 neighbours and random values against torch's
+                float32 -> float8_e4m3fn conversion
+  fp8 queries (quantize_q_fp8, index_scores(q_fp8=True)) pinned: the scale
+                rule as a property over random and edge magnitudes; a head
+                quantised by hand; exact on parity draws; e4m3's rounding
+                bound on random queries
   fp8 index keys (page-blocked codes + per-token scales) pinned: a hand-built
                 page decoded against values written out by hand
   int8 latent rows (affine codes, per-128 scale and bias) pinned: a hand-built
@@ -32,6 +39,7 @@ Parity status of each function (what pins it; see tests/test_oracle_pins.py):
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 
@@ -74,6 +82,8 @@ def _load():
                                           f64p, f64p]
         lib.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
         lib.oracle_e4m3_to_double.restype = ctypes.c_double
+        lib.oracle_e4m3_encode.argtypes = [ctypes.c_double]
+        lib.oracle_e4m3_encode.restype = ctypes.c_uint8
         lib.oracle_decode_fp8_rows.argtypes = [ctypes.c_void_p, c_i64, c_int, c_int, f64p]
         lib.oracle_decode_int8_rows.argtypes = [ctypes.c_void_p, c_i64, c_int, c_int, f64p]
         lib.oracle_decode_fp8_keys.argtypes = [ctypes.c_void_p, c_i64, c_int, c_int, c_i64, c_i64, f64p]
@@ -147,13 +157,20 @@ class _View:
         return x.index_select(0, self.rows_t.to(x.device)).cpu()
 
 
-def index_scores(batch, rows=None, ld=None):
-    """Scores [n_rows, ld] (float64, NaN beyond each row's pos)."""
+def index_scores(batch, rows=None, ld=None, q_fp8=False):
+    """Scores [n_rows, ld] (float64, NaN beyond each row's pos).
+
+    q_fp8: the queries are first quantised per (row, head) as
+    quantize_q_fp8 describes and the formula is applied to the values the
+    codes stand for."""
     lib = _load()
     v = _View(batch, rows)
     cfg = batch.cfg
     ld = ld or max(batch.max_seq_len, 1)
     q = _f64(v.per_row(batch.q_idx))
+    if q_fp8:
+        codes, e = quantize_q_fp8(q)
+        q = dequantize_q_fp8(codes, e)
     w = _f64(v.per_row(batch.w))
     if cfg.key_fmt == FMT_FP8:  # page-blocked fp8 keys: decoded to doubles first
         k = decode_fp8_keys(v.pool(batch.k_pool), cfg.page_size, cfg.di)
@@ -230,6 +247,46 @@ def threads() -> int:
 def set_threads(n: int) -> None:
     """Run the oracle's row loops on n OpenMP threads from now on."""
     _load().oracle_set_threads(int(n))
+
+
+def e4m3_encode(x: float) -> int:
+    """The e4m3fn code nearest to x (ties to the even code, |x| > 448 gives 448)."""
+    return int(_load().oracle_e4m3_encode(float(x)))
+
+
+def q_fp8_exponent(amax: float) -> int:
+    """The smallest integer e with amax <= 448 * 2^e (0 when amax is 0).
+
+    With amax = m * 2^k, m in [0.5, 1): 448 * 2^(k-9) = 0.875 * 2^k covers
+    amax when m <= 0.875, else 448 * 2^(k-8) = 1.75 * 2^k does; 448 * 2^(k-10)
+    = 0.4375 * 2^k never does."""
+    if amax == 0.0:
+        return 0
+    m, k = math.frexp(amax)
+    return k - 9 if m <= 0.875 else k - 8
+
+
+def quantize_q_fp8(q):
+    """Per-(row, head) fp8 queries: q [..., D] float64 -> (codes uint8 [..., D],
+    exponents int [...]).  Each head's D values are scaled by 2^-e, e from its
+    largest magnitude (q_fp8_exponent: the scaled values stay within 448), and
+    rounded to e4m3fn codes; the head stands for code * 2^e."""
+    q = np.asarray(q, dtype=np.float64)
+    lead = q.shape[:-1]
+    flat = q.reshape(-1, q.shape[-1])
+    codes = np.zeros(flat.shape, dtype=np.uint8)
+    e = np.zeros(flat.shape[0], dtype=np.int64)
+    for i in range(flat.shape[0]):
+        e[i] = q_fp8_exponent(float(np.max(np.abs(flat[i]))))
+        for d in range(flat.shape[1]):
+            codes[i, d] = e4m3_encode(math.ldexp(float(flat[i, d]), -int(e[i])))
+    return codes.reshape(q.shape), e.reshape(lead)
+
+
+def dequantize_q_fp8(codes, e):
+    """The values fp8 queries stand for: e4m3(code) * 2^e."""
+    table = np.array([e4m3_to_double(c) for c in range(256)], dtype=np.float64)
+    return table[np.asarray(codes)] * np.ldexp(1.0, np.asarray(e))[..., None]
 
 
 def e4m3_to_double(byte: int) -> float:

@@ -105,6 +105,41 @@ double oracle_e4m3_to_double(uint8_t byte) {
   return sign ? -mag : mag;
 }
 
+/* The e4m3fn code nearest to x, ties to the even code (the one whose
+ * mantissa field is even).  Magnitudes past 448, the largest finite value,
+ * give 448; NaN gives the NaN code.  The e4m3fn values of one binade
+ * [2^E, 2^(E+1)), E >= -6, are spaced 2^(E-3); below 2^-6 (subnormals) the
+ * spacing is 2^-9. */
+uint8_t oracle_e4m3_encode(double x) {
+  if (isnan(x)) return 0x7F;
+  const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+  double a = fabs(x);
+  if (a == 0.0) return sign;
+  if (a >= 448.0) return sign | 0x7E;
+  int k;
+  frexp(a, &k);            /* a = m * 2^k, m in [0.5, 1): binade E = k - 1 */
+  int E = k - 1;
+  if (E < -6) E = -6;      /* subnormals share the spacing of the lowest binade */
+  const double quantum = ldexp(1.0, E - 3);
+  const double units = a / quantum; /* exact: quantum is a power of two */
+  double n = floor(units);
+  const double frac = units - n;
+  if (frac > 0.5 || (frac == 0.5 && fmod(n, 2.0) != 0.0)) n += 1.0;
+  /* n quanta of 2^(E-3): 8 <= n <= 16 in a normal binade, 0 <= n <= 8 below */
+  int expo, mant;
+  if (k - 1 < -6) {        /* subnormal range: n in [0, 8]; n == 8 is 2^-6 */
+    if (n >= 8.0) { expo = 1; mant = 0; }
+    else { expo = 0; mant = (int)n; }
+  } else if (n >= 16.0) {  /* rounded up into the next binade */
+    expo = E + 7 + 1; mant = 0;
+  } else {
+    expo = E + 7; mant = (int)n - 8;
+  }
+  if (expo > 15 || (expo == 15 && mant == 7)) { expo = 15; mant = 6; }
+  if (n == 0.0) return sign;
+  return (uint8_t)(sign | (expo << 3) | mant);
+}
+
 /* bfloat16 is the upper half of an IEEE binary32. */
 static double bf16_bits_to_double(uint16_t bits) {
   uint32_t u = (uint32_t)bits << 16;

@@ -397,6 +397,81 @@ def test_fp8_keys_exact_integers_give_bf16_scores():
     assert np.array_equal(oracle.topk(a, sa), oracle.topk(b, sb_))
 
 
+# ---------------------------------------------------------------- fp8 queries
+
+
+def test_e4m3_encoder_round_trips_every_code():
+    for c in range(256):
+        if c & 0x7F == 0x7F:
+            continue  # the two NaN codes
+        assert oracle.e4m3_encode(oracle.e4m3_to_double(c)) == c, hex(c)
+
+
+def test_e4m3_encoder_matches_torch_rounding():
+    # every tie between neighbouring finite values, the float32 values either
+    # side of it, and random values over the whole range (subnormals included)
+    vals = sorted({oracle.e4m3_to_double(c) for c in range(0x7F)})
+    xs = []
+    for a, b in zip(vals, vals[1:]):
+        mid = np.float32((a + b) / 2)
+        xs += [mid, np.nextafter(mid, np.float32(0)), np.nextafter(mid, np.float32(np.inf))]
+    g = torch.Generator().manual_seed(5)
+    xs += list((torch.rand(4000, generator=g) * 448).numpy())
+    xs += list((torch.rand(1000, generator=g) * 2.0 ** -5).numpy())
+    x32 = torch.tensor(np.array(xs, dtype=np.float32))
+    x32 = torch.cat([x32, -x32])
+    want = x32.to(torch.float8_e4m3fn).view(torch.uint8).tolist()
+    got = [oracle.e4m3_encode(float(x)) for x in x32.tolist()]
+    assert got == want
+
+
+def test_q_fp8_scale_rule():
+    # e is the smallest exponent with amax <= 448 * 2^e
+    g = torch.Generator().manual_seed(6)
+    amaxes = [448.0, 449.0, 1.0, 15.0, 0.875, 0.87500001, 1.75, 2.0 ** -130, 3e38, 224.0, 224.5]
+    amaxes += (torch.rand(200, generator=g).double() * torch.exp2(torch.randint(-40, 40, (200,), generator=g)
+                                                                   .double())).tolist()
+    for a in amaxes:
+        e = oracle.q_fp8_exponent(a)
+        assert a <= math.ldexp(448.0, e) and a > math.ldexp(448.0, e - 1), (a, e)
+    assert oracle.q_fp8_exponent(0.0) == 0
+
+
+def test_q_fp8_hand_quantised_head():
+    # amax 2.5 = 0.625 * 2^2, so e = -7 and the head is scaled by 128:
+    # 1.0 -> 128 = 2^7 exactly (code 0x70); 0.3 -> 38.4, in [32, 64) where e4m3
+    # steps by 4: 9.6 steps round to 10, i.e. 40 (exponent field 12, mantissa
+    # 2: 0x62); -2.5 -> -320, in [256, 512) where the step is 32: exactly 10
+    # steps (exponent field 15, mantissa 2, sign: 0xFA); 0 -> 0.
+    q = np.array([[[1.0, 0.3, -2.5, 0.0]]])
+    codes, e = oracle.quantize_q_fp8(q)
+    assert e.tolist() == [[-7]]
+    assert codes[0, 0].tolist() == [0x70, 0x62, 0xFA, 0x00]
+    assert oracle.dequantize_q_fp8(codes, e)[0, 0].tolist() == [1.0, 0.3125, -2.5, 0.0]
+
+
+def test_q_fp8_exact_on_parity_draws():
+    # parity draws are n/8, |n| <= 8: scaled by 2^-e they are e4m3 values, so
+    # quantising the queries changes no score
+    b = synth.make_batch(4, batch=3, ctx=(200, 700), topk=128, layers=0, key_fmt=synth.FMT_FP8_E4M3_B128)
+    s1, s2 = oracle.index_scores(b), oracle.index_scores(b, q_fp8=True)
+    assert np.array_equal(np.isnan(s1), np.isnan(s2))
+    assert np.array_equal(np.nan_to_num(s1), np.nan_to_num(s2))
+
+
+def test_q_fp8_within_e4m3_rounding():
+    # each value moves by at most half a step of its binade (2^-4 relative),
+    # or half the subnormal step 2^(e-10); the head's largest value keeps its
+    # binade, so amax is reproduced within the same bound
+    g = torch.Generator().manual_seed(7)
+    q = (torch.randn(5, 7, 128, generator=g) * torch.exp2(torch.randint(-6, 6, (5, 7, 1), generator=g))).double().numpy()
+    codes, e = oracle.quantize_q_fp8(q)
+    dq = oracle.dequantize_q_fp8(codes, e)
+    bound = np.abs(q) * 2.0 ** -4 + np.ldexp(1.0, e - 10)[..., None]
+    assert np.all(np.abs(dq - q) <= bound)
+    assert np.all(np.abs(dq).max(-1) <= np.ldexp(448.0, e))
+
+
 # ---------------------------------------------------------------- indexer preparation
 
 
