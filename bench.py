@@ -40,6 +40,7 @@ sys.path.insert(0, ROOT)
 METRIC = "sparse-MLA decode queries/s + indexer top-k rows/s; % HBM / MFMA roofline"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFS = 2500.0
+MFMA_FP8_PEAK_TFS = 5000.0
 
 
 def parse():
@@ -63,6 +64,9 @@ def parse():
     ap.add_argument("--key-fp8", action="store_true",
                     help="indexer keys cached as e4m3 codes with one f32 scale per token "
                          "(queries stay bf16); reports the top-k overlap with bf16 keys")
+    ap.add_argument("--q-fp8", action="store_true",
+                    help="with --key-fp8: the indexer's queries are quantised per (row, head) to e4m3 "
+                         "at a power-of-two scale and contracted on the fp8 matrix cores")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (f32 multiply by 1) four times, the "
                          "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
@@ -279,6 +283,9 @@ def main():
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(use --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.q_fp8 and not args.key_fp8:
+        print("--q-fp8 contracts fp8 queries with fp8 keys: add --key-fp8", file=sys.stderr)
+        sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
         return
@@ -301,8 +308,9 @@ def main():
                                "int8": synth.FMT_INT8_AFFINE_B128}[args.kv])
         paths.append(DSAPath(sb, prep=synth.make_prep(sb, seed=4242 + i) if args.prep else None,
                              score_budget=None if args.score_budget is None
-                             else int(args.score_budget * 2 ** 20)))
-    workload = (base.name + ("+fp8keys" if args.key_fp8 else "") + ("+prep" if args.prep else "")
+                             else int(args.score_budget * 2 ** 20), q_fp8=args.q_fp8))
+    workload = (base.name + ("+fp8keys" if args.key_fp8 else "") + ("+fp8q" if args.q_fp8 else "")
+                + ("+prep" if args.prep else "")
                 + ("+kv-" + args.kv if args.kv is not None else "")
                 + ("+budget" if args.score_budget is not None else ""))
     torch.cuda.synchronize()
@@ -400,6 +408,9 @@ def main():
     T = paths[0].sb.T
     alg = [algorithmic(p.sb, p) for p in paths]
     report = {}
+    # the indexer's contraction runs on the fp8 matrix cores with fp8 queries
+    peak_tfs = {s: (MFMA_FP8_PEAK_TFS if args.q_fp8 and s in ("index_scores", "index_topk") else MFMA_BF16_PEAK_TFS)
+                for s in stages}
     for s in stages:
         by = float(np.mean([a[s]["bytes"] for a in alg]))
         fl = float(np.mean([a[s]["flops"] for a in alg]))
@@ -409,12 +420,12 @@ def main():
                      "alg_bytes": by, "alg_flops": fl,
                      "GB_s": by / t / 1e9, "TFLOP_s": fl / t / 1e12,
                      "frac_hbm": by / t / 1e9 / HBM_PEAK_GBS,
-                     "frac_mfma": fl / t / 1e12 / MFMA_BF16_PEAK_TFS,
+                     "frac_mfma": fl / t / 1e12 / peak_tfs[s],
                      "traffic": traffic(workload, s)}
     dom = max(stages, key=lambda s: stage_ms[s])
     r = report[dom]
     t_hbm = r["alg_bytes"] / (HBM_PEAK_GBS * 1e9)
-    t_mfma = r["alg_flops"] / (MFMA_BF16_PEAK_TFS * 1e12)
+    t_mfma = r["alg_flops"] / (peak_tfs[dom] * 1e12)
     bound = "hbm" if t_hbm >= t_mfma else "mfma"
     launches = r["launches_per_step"]
     if bound == "hbm":
@@ -423,8 +434,8 @@ def main():
                 "frac": ach / HBM_PEAK_GBS, "traffic": None}
     else:
         ach = r["alg_flops"] / (stage_ms[dom] / 1e3) / 1e12
-        roof = {"bound": "mfma", "achieved": ach, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                "frac": ach / MFMA_BF16_PEAK_TFS, "traffic": None}
+        roof = {"bound": "mfma", "achieved": ach, "peak": peak_tfs[dom], "unit": "TFLOP/s",
+                "frac": ach / peak_tfs[dom], "traffic": None}
     roof["traffic"] = r["traffic"]
     roof["kernel"] = dom
     roof["alg_bytes_per_launch"] = r["alg_bytes"] / launches
@@ -453,6 +464,8 @@ def main():
                                   {0: "f32", 1: "bf16", 2: "fp8-e4m3-b128", 3: "int8-affine-b128"}[cfg.kv_fmt],
                                   cfg.page_size, cfg.layers)
                                + (", fp8 index keys (per-token scale)" if args.key_fp8 else "")
+                               + (", fp8 index queries (per-head power-of-two scale) on fp8 MFMA"
+                                  if args.q_fp8 else "")
                                + (", indexer preparation in the step" if args.prep else "")
                                + (", scores + top-k in a %.0f MB workspace (%d rows per chunk)"
                                   % (paths[0].itk_ws_bytes / 2 ** 20,

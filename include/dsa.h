@@ -90,6 +90,15 @@ typedef int32_t dsa_status;
  * 128*i..128*i+127), then the 64 rope dims as bf16;
  * latent dim d = scale[d/128] * code[d] + bias[d/128].  Latent pools only. */
 #define DSA_INT8_AFFINE_B128 3
+/* Indexer queries only (q_format of dsa_index_scores / dsa_index_topk, with
+ * DSA_FP8_E4M3_B128 keys): bf16 queries in memory, contracted as fp8.  Each
+ * (row, head) of 128 dims is scaled by 2^-e, e the smallest integer with the
+ * head's largest magnitude <= 448 * 2^e (e = 0 for an all-zero head), and
+ * rounded to e4m3fn codes (nearest, ties to even); the scores are the plain
+ * formula over code * 2^e, on the fp8 matrix cores of gfx950 (the
+ * "MFMA bf16/fp8 tiles" of the indexer's q.k; a reading of this library: the
+ * pages quantise the keys, not how fp8 queries are scaled). */
+#define DSA_BF16_TO_FP8 4
 
 /* A ragged batch of B requests and T = cu_q_lens[B] query rows. */
 typedef struct {
@@ -141,7 +150,10 @@ const char *dsa_status_string(dsa_status status);
  * scores   device [T, ld] f32, ld >= max_seq_len.  Entries s > pos(t), and
  *          entries of tokens whose page is not mapped, are NOT written.
  * Built combinations: (DSA_BF16, n_heads 64, head_dim 128) on MFMA, with bf16
- * or fp8 keys; (DSA_F32, n_heads <= 64, head_dim <= 256) on the vector ALUs.
+ * or fp8 keys; (DSA_BF16_TO_FP8, n_heads 64, head_dim 128, fp8 keys) on fp8
+ * MFMA -- DSA_ERR_UNSUPPORTED with other keys, and for batches whose tables
+ * (about 24 bytes per request) leave no room for one unit of staged query
+ * rows in LDS; (DSA_F32, n_heads <= 64, head_dim <= 256) on the vector ALUs.
  */
 dsa_status dsa_index_scores(const dsa_batch *batch, const void *q_idx, int32_t q_format,
                             const float *w, const dsa_pool *k_idx, int32_t n_heads,

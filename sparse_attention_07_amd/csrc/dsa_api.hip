@@ -90,18 +90,23 @@ struct IndexArgs {
   const void* q_idx;
   const float* w;
   PoolArgs pa;
-  int q_format, n_heads, head_dim;
+  int q_format, n_heads, head_dim;  // q_format DSA_BF16 also stands for DSA_BF16_TO_FP8
+  bool q_fp8;                       // DSA_BF16_TO_FP8: queries contracted as fp8 codes
 };
 
 dsa_status check_index(const BatchArgs& ba, const void* q_idx, int32_t q_format, const float* w,
                        const dsa_pool* k_idx, int32_t n_heads, int32_t head_dim, IndexArgs* ia) {
   if (q_idx == nullptr || w == nullptr || k_idx == nullptr) return DSA_ERR_NULL;
   if (n_heads < 1 || head_dim < 1) return DSA_ERR_SHAPE;
+  // fp8 queries: bf16 in memory, quantised in the kernel; fp8 keys only
+  const bool q_fp8 = q_format == DSA_BF16_TO_FP8;
+  if (q_fp8 && k_idx->format != DSA_FP8_E4M3_B128) return DSA_ERR_UNSUPPORTED;
+  if (q_fp8) q_format = DSA_BF16;
   const bool fp8_keys = q_format == DSA_BF16 && k_idx->format == DSA_FP8_E4M3_B128;
   if ((k_idx->format != q_format && !fp8_keys) || k_idx->dim != head_dim) return DSA_ERR_SHAPE;
   if (!aligned(w, 4)) return DSA_ERR_ALIGN;
   dsa_status st;
-  *ia = IndexArgs{q_idx, w, PoolArgs{}, q_format, n_heads, head_dim};
+  *ia = IndexArgs{q_idx, w, PoolArgs{}, q_format, n_heads, head_dim, q_fp8};
   if (q_format == DSA_BF16) {
     if (n_heads != 64 || head_dim != 128) return DSA_ERR_UNSUPPORTED;
     if (fp8_keys) {
@@ -113,6 +118,7 @@ dsa_status check_index(const BatchArgs& ba, const void* q_idx, int32_t q_format,
       return st;
     }
     if (!aligned(q_idx, 16) || !aligned(w, 16)) return DSA_ERR_ALIGN;
+    if (q_fp8 && !dsa::index_scores_fp8q_fits(ba)) return DSA_ERR_UNSUPPORTED;
     return DSA_OK;
   }
   if (q_format == DSA_F32) {
@@ -129,7 +135,7 @@ hipError_t launch_index(const BatchArgs& ba, const IndexArgs& ia, float* scores,
                         hipStream_t s, int row_lo, int row_hi) {
   if (ia.q_format == DSA_BF16) {
     if (ba.num_pages == 0) return hipSuccess;  // no token is mapped: nothing is written
-    return dsa::launch_index_scores_bf16(ba, ia.q_idx, ia.w, ia.pa, scores, ld, s, row_lo, row_hi);
+    return dsa::launch_index_scores_bf16(ba, ia.q_idx, ia.w, ia.pa, scores, ld, s, row_lo, row_hi, ia.q_fp8);
   }
   return dsa::launch_index_scores_f32(ba, ia.q_idx, ia.w, ia.pa, ia.n_heads, ia.head_dim, scores, ld,
                                       s, row_lo, row_hi);

@@ -32,7 +32,9 @@ int device_cu_count();
 // stored at scores + (t - row_lo) * ld (index rows keep their absolute t).
 hipError_t launch_index_scores_bf16(const BatchArgs& ba, const void* q_idx, const float* w,
                                     const PoolArgs& pool, float* scores, int64_t ld,
-                                    hipStream_t stream, int row_lo, int row_hi);
+                                    hipStream_t stream, int row_lo, int row_hi, bool q_fp8);
+// Whether a batch's fp8-query launch fits the persistent form's LDS plan.
+bool index_scores_fp8q_fits(const BatchArgs& ba);
 hipError_t launch_index_scores_f32(const BatchArgs& ba, const void* q_idx, const float* w,
                                    const PoolArgs& pool, int n_heads, int head_dim, float* scores,
                                    int64_t ld, hipStream_t stream, int row_lo, int row_hi);

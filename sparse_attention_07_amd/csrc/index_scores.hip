@@ -49,8 +49,18 @@ constexpr int kHeadSlots = 17;                                    // 16 chunks o
 constexpr int kHeadStrideLds = kHeadSlots * 16;                   // 272 B: heads start on distinct banks
 constexpr int kRowSlots = kHeads * kHeadSlots;                    // 1088
 constexpr int kRowBytesLds = kRowSlots * 16;                      // 17408 B per staged query row
+// fp8 queries (codes in the keys' dim order, 128 B per head): heads 144 B
+// apart, so the 16-byte operand reads of 16 lanes (16 heads) meet distinct
+// bank quartets.
+constexpr int kHeadStrideLds8 = 144;
+constexpr int kRowBytesLds8 = kHeads * kHeadStrideLds8;             // 9216 B per staged query row
+template <bool QFP8>
+constexpr int kQRowBytes = QFP8 ? kRowBytesLds8 : kRowBytesLds;
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;            // fp8 MFMA operand
+typedef __attribute__((__vector_size__(8 * sizeof(uint32_t)))) uint32_t u32x8;
+typedef short s16x2 __attribute__((ext_vector_type(2)));                        // packed fp8 pair
 
 // 16-byte copy HBM -> LDS for every active lane of the wave: lane i's bytes land
 // at lds_wave_base + 16 i (global_load_lds_dwordx4, LDS base in M0).
@@ -219,6 +229,123 @@ __device__ inline void score_keys(const Keys8& k8, const int64_t (&off)[2], cons
   Keys kk;
   keys_from_fp8(kk, k8);
   score_block<true>(kk, off, q_lds, w_lds, nr, s_base, pos_first, ld_last, scores, row0, ld, lane, k8.sc);
+}
+
+// fp8 queries against fp8 keys on v_mfma_scale_f32_32x32x64_f8f6f4 (scales
+// 1): per row two 64-dim k steps for each of the four 32x32 (heads, tokens)
+// tiles.  A lane's 32 codes of step i are dims 64 g + 32 i .. +31 (g = lane
+// half) in both operands, the keys' load layout: the keys' codes enter the
+// contraction as loaded.  The query heads' power-of-two scales are in the
+// staged weights and each token's key scale multiplies its score, as in
+// score_block<true>.
+__device__ inline i32x8 join8(u32x4 lo, u32x4 hi) {
+  return __builtin_bit_cast(i32x8, u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+}
+
+__device__ inline f32x16 mfma32_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ inline void score_keys_fp8q(const Keys8& k8, const int64_t (&off)[2], const uint8_t* q_lds,
+                                       const float* w_lds, int nr, int s_base, int pos_first, int64_t ld_last,
+                                       float* __restrict__ scores, int64_t row0, int64_t ld, int lane) {
+  i32x8 kb[2][2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) kb[nt][i] = join8(k8.v[nt][2 * i], k8.v[nt][2 * i + 1]);
+#pragma unroll
+  for (int r = 0; r < kMaxUnitRows; ++r) {
+    if (r >= nr) break;
+    const int pos_r = (int)min<int64_t>((int64_t)pos_first + r, ld_last);
+    if (s_base > pos_r) continue;
+    const uint8_t* qa = q_lds + r * kRowBytesLds8 + (lane & 31) * kHeadStrideLds8 + (lane >> 5) * 64;
+    i32x8 qa8[2][2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint8_t* p = qa + mt * 32 * kHeadStrideLds8 + i * 32;
+        qa8[mt][i] = join8(*reinterpret_cast<const u32x4*>(p), *reinterpret_cast<const u32x4*>(p + 16));
+      }
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) acc[nt][mt] = f32x16{};
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) acc[nt][mt] = mfma32_fp8(qa8[mt][i], kb[nt][i], acc[nt][mt]);
+    __builtin_amdgcn_s_setprio(0);
+    const float* wr = w_lds + r * kHeads + 4 * (lane >> 5);
+    float part[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      part[nt] = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 wq = *reinterpret_cast<const f32x4*>(wr + mt * 32 + 8 * q4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) part[nt] += wq[e] * relu_bits(acc[nt][mt][4 * q4 + e]);
+        }
+    }
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[1]),
+                                                     false, false);
+    const int nt = lane >> 5;
+    const float score = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * (nt ? k8.sc[1] : k8.sc[0]);
+    const int s = s_base + lane;
+    if (s <= pos_r && (nt ? off[1] : off[0]) >= 0) scores[(row0 + r) * ld + s] = score;
+  }
+}
+
+// Quantised staging of one unit's query rows for fp8 contraction: each head's
+// 128 dims are scaled by 2^-e, e the smallest exponent with the head's
+// largest magnitude <= 448 * 2^e (0 for an all-zero head), and rounded to
+// e4m3 codes (nearest, ties to even); 2^e goes into the head's staged
+// weight.  A thread takes 8 dims (16 bytes) of one head, the 16 threads of a
+// head are 16 consecutive lanes.
+__device__ inline void stage_fp8_queries(const uint16_t* __restrict__ qsrc, const float* __restrict__ wsrc,
+                                         int nr, uint8_t* qd, float* wd, int tid, int nthreads) {
+  const int n_chunks = nr * kHeads * 16;
+  for (int c0 = 0; c0 < n_chunks; c0 += nthreads) {
+    const int c = c0 + tid;
+    const bool in = c < n_chunks;
+    const int r = c / (kHeads * 16), h = (c / 16) % kHeads, ch = c % 16;
+    u32x4 raw = in ? *reinterpret_cast<const u32x4*>(qsrc + ((r * kHeads + h) * kDim + ch * 8)) : u32x4{};
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = __uint_as_float(raw[j] << 16);
+      x[2 * j + 1] = __uint_as_float(raw[j] & 0xFFFF0000u);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[j]));
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+    int k = 0;
+    const float mant = frexpf(amax, &k);  // amax = mant * 2^k, mant in [0.5, 1)
+    const int e = amax == 0.f ? 0 : (mant <= 0.875f ? k - 9 : k - 8);
+    s16x2 pk[2] = {{0, 0}, {0, 0}};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      pk[j] = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(pk[j], ldexpf(x[4 * j], -e), ldexpf(x[4 * j + 1], -e),
+                                                       1.0f, false);
+      pk[j] = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(pk[j], ldexpf(x[4 * j + 2], -e),
+                                                       ldexpf(x[4 * j + 3], -e), 1.0f, true);
+    }
+    if (in) {
+      *reinterpret_cast<uint2*>(qd + r * kRowBytesLds8 + h * kHeadStrideLds8 + ch * 8) =
+          uint2{__builtin_bit_cast(uint32_t, pk[0]), __builtin_bit_cast(uint32_t, pk[1])};
+      if (ch == 0) wd[r * kHeads + h] = ldexpf(wsrc[r * kHeads + h], e);
+    }
+  }
 }
 
 template <bool KFP8>
@@ -414,7 +541,19 @@ __device__ inline int flat_excl_scan(int v, int* wsum, int& carry, int lane, int
   return before + x - v;
 }
 
-template <bool KFP8>
+// Scores of one key step: fp8 queries (QFP8, fp8 keys only) on the fp8
+// matrix cores, else score_keys.
+template <bool QFP8, typename K>
+__device__ inline void score_step(const K& kk, const int64_t (&off)[2], const uint8_t* q_lds, const float* w_lds,
+                                  int nr, int s_base, int pos_first, int64_t ld_last, float* __restrict__ scores,
+                                  int64_t row0, int64_t ld, int lane) {
+  if constexpr (QFP8) score_keys_fp8q(kk, off, q_lds, w_lds, nr, s_base, pos_first, ld_last, scores, row0, ld, lane);
+  else score_keys(kk, off, q_lds, w_lds, nr, s_base, pos_first, ld_last, scores, row0, ld, lane);
+}
+
+// QFP8: the query rows are staged as fp8 codes (stage_fp8_queries) and
+// contracted on the fp8 matrix cores; fp8 keys only.
+template <bool KFP8, bool QFP8>
 __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_lens, int B,
     const int32_t* __restrict__ page_table, int pt_stride, int page_size, int num_pages,
@@ -424,7 +563,8 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   // LDS: nslots staged units (query rows, then their weights), then the tables.
   uint8_t* q_area = smem;
-  float* w_area = reinterpret_cast<float*>(smem + (size_t)nslots * rg * kRowBytesLds);
+  static_assert(!QFP8 || KFP8, "fp8 queries contract with fp8 keys");
+  float* w_area = reinterpret_cast<float*>(smem + (size_t)nslots * rg * kQRowBytes<QFP8>);
   int* rq0 = reinterpret_cast<int*>(w_area + nslots * rg * kHeads);  // [B] first row in the window
   int* rql = rq0 + B;                                             // [B] its rows in the window
   int* rpf = rql + B;                                             // [B] position of the first
@@ -526,7 +666,12 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
     load_keys(k0, A.off, k_base, lane, A.tok, page_size, k_row_stride);
     for (int uu = u0; uu <= u_hi; ++uu) {  // query rows and weights -> LDS slot uu - u0
       const int q0 = uq0[uu], nr = unr[uu];
-      uint8_t* qd = q_area + (size_t)(uu - u0) * rg * kRowBytesLds;
+      uint8_t* qd = q_area + (size_t)(uu - u0) * rg * kQRowBytes<QFP8>;
+      if constexpr (QFP8) {
+        stage_fp8_queries(q_idx + (int64_t)q0 * kHeads * kDim, w + (int64_t)q0 * kHeads, nr, qd,
+                          w_area + (size_t)(uu - u0) * rg * kHeads, tid, kFlatThreads);
+        continue;
+      }
       const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(q_idx + (int64_t)q0 * kHeads * kDim);
       const int n_slots = nr * kRowSlots;  // padded per head; the pad slot repeats chunk 15
       for (int base = 0; base < n_slots; base += kFlatThreads) {
@@ -551,7 +696,7 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
     lds_barrier();
 
 #define DSA_SCORE(KK, X)                                                                           \
-  score_keys(KK, X.off, q_area + (size_t)(X.u - u0) * rg * kRowBytesLds,                          \
+  score_step<QFP8>(KK, X.off, q_area + (size_t)(X.u - u0) * rg * kQRowBytes<QFP8>,                \
               w_area + (size_t)(X.u - u0) * rg * kHeads, unr[X.u], X.tok, upf[X.u], ld_last, scores, \
               (int64_t)uq0[X.u] - row_lo, ld, lane)
     // Each step issues the page ids two blocks ahead, then the keys one block
@@ -638,7 +783,7 @@ __global__ __launch_bounds__(256) void index_scores_f32_valu(
 
 namespace {
 
-template <bool KFP8>
+template <bool KFP8, bool QFP8>
 hipError_t launch_index_scores_mfma(const BatchArgs& ba, const void* q_idx, const float* w,
                                     const PoolArgs& pool, float* scores, int64_t ld,
                                     hipStream_t stream, int row_lo, int row_hi) {
@@ -650,14 +795,14 @@ hipError_t launch_index_scores_mfma(const BatchArgs& ba, const void* q_idx, cons
     const int rg = ba.max_q_len <= 8 ? ba.max_q_len : 8;
     const int64_t u_max = (int64_t)ba.batch * ((ba.max_q_len + rg - 1) / rg);
     const size_t tables = ((size_t)(4 * (int64_t)ba.batch + 1 + 5 * u_max + 1 + kFlatWaves) * sizeof(int) + 15) / 16 * 16;
-    const size_t per_unit = (size_t)rg * (kRowBytesLds + kHeads * sizeof(float));
+    const size_t per_unit = (size_t)rg * (kQRowBytes<QFP8> + kHeads * sizeof(float));
     const size_t avail = tables < 160 * 1024 ? 160 * 1024 - tables : 0;
     const int nslots = (int)std::min<size_t>(8, avail / per_unit);
     const size_t lds = tables + (size_t)nslots * per_unit;
     if (nslots >= 1) {
-      hipError_t e = ensure_max_lds(reinterpret_cast<const void*>(index_scores_flat<KFP8>));
+      hipError_t e = ensure_max_lds(reinterpret_cast<const void*>(index_scores_flat<KFP8, QFP8>));
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(index_scores_flat<KFP8>, dim3(device_cu_count()), dim3(kFlatThreads), lds, stream,
+      hipLaunchKernelGGL((index_scores_flat<KFP8, QFP8>), dim3(device_cu_count()), dim3(kFlatThreads), lds, stream,
                          ba.cu_q, ba.seq_lens, ba.batch, ba.page_table, ba.pt_stride, ba.page_size,
                          ba.num_pages, static_cast<const uint16_t*>(q_idx), w,
                          static_cast<const uint8_t*>(pool.base), pool.page_stride, pool.row_stride,
@@ -665,6 +810,9 @@ hipError_t launch_index_scores_mfma(const BatchArgs& ba, const void* q_idx, cons
       return hipGetLastError();
     }
   }
+  // fp8 queries have no grid form: the API refuses such launches up front
+  // (index_scores_fp8q_fits)
+  if (QFP8) return hipErrorNotSupported;
   // Row groups: the whole draft for decode-sized q_len, four rows for long
   // prefill chunks (LDS: 17 KB per staged row).
   int rg = ba.max_q_len <= 8 ? ba.max_q_len : 4;
@@ -689,10 +837,19 @@ hipError_t launch_index_scores_mfma(const BatchArgs& ba, const void* q_idx, cons
 
 hipError_t launch_index_scores_bf16(const BatchArgs& ba, const void* q_idx, const float* w,
                                     const PoolArgs& pool, float* scores, int64_t ld,
-                                    hipStream_t stream, int row_lo, int row_hi) {
+                                    hipStream_t stream, int row_lo, int row_hi, bool q_fp8) {
+  if (q_fp8) return launch_index_scores_mfma<true, true>(ba, q_idx, w, pool, scores, ld, stream, row_lo, row_hi);
   return pool.format == 2
-             ? launch_index_scores_mfma<true>(ba, q_idx, w, pool, scores, ld, stream, row_lo, row_hi)
-             : launch_index_scores_mfma<false>(ba, q_idx, w, pool, scores, ld, stream, row_lo, row_hi);
+             ? launch_index_scores_mfma<true, false>(ba, q_idx, w, pool, scores, ld, stream, row_lo, row_hi)
+             : launch_index_scores_mfma<false, false>(ba, q_idx, w, pool, scores, ld, stream, row_lo, row_hi);
+}
+
+bool index_scores_fp8q_fits(const BatchArgs& ba) {
+  const int rg = ba.max_q_len <= 8 ? std::max(ba.max_q_len, 1) : 8;
+  const int64_t u_max = (int64_t)ba.batch * ((ba.max_q_len + rg - 1) / rg);
+  const size_t tables = ((size_t)(4 * (int64_t)ba.batch + 1 + 5 * u_max + 1 + kFlatWaves) * sizeof(int) + 15) / 16 * 16;
+  const size_t per_unit = (size_t)rg * (kRowBytesLds8 + kHeads * sizeof(float));
+  return tables + per_unit <= 160 * 1024;
 }
 
 hipError_t launch_index_scores_f32(const BatchArgs& ba, const void* q_idx, const float* w,

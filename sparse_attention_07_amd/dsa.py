@@ -19,6 +19,7 @@ DSA_OK = 0
 STATUS_NAMES = {0: "DSA_OK", 1: "DSA_ERR_NULL", 2: "DSA_ERR_SHAPE", 3: "DSA_ERR_UNSUPPORTED",
                 4: "DSA_ERR_WORKSPACE", 5: "DSA_ERR_HIP", 6: "DSA_ERR_ALIGN"}
 DSA_F32, DSA_BF16, DSA_FP8_E4M3_B128, DSA_INT8_AFFINE_B128 = 0, 1, 2, 3
+DSA_BF16_TO_FP8 = 4  # indexer queries: bf16 in memory, contracted as fp8 (fp8 keys)
 
 ENTRY_POINTS = ("dsa_version", "dsa_status_string", "dsa_indexer_prepare", "dsa_index_scores",
                 "dsa_index_topk", "dsa_index_topk_workspace_bytes", "dsa_topk_workspace_bytes",

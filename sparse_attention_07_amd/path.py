@@ -14,9 +14,12 @@ from .synth import torch_dtype
 
 
 class DSAPath:
-    def __init__(self, sb, prefill: bool | None = None, prep=None, score_budget: int | None = None):
+    def __init__(self, sb, prefill: bool | None = None, prep=None, score_budget: int | None = None,
+                 q_fp8: bool = False):
         cfg = sb.cfg
         self.sb = sb
+        # q_fp8: the indexer contracts its queries as fp8 codes (fp8 keys only)
+        self.idx_q_fmt = dsa.DSA_BF16_TO_FP8 if q_fp8 else cfg.idx_fmt
         # optional indexer preparation inputs (synth.Prep): when given, each step
         # first rotates them into sb.q_idx and stores the keys into the key pool
         self.prep = prep
@@ -58,7 +61,7 @@ class DSAPath:
 
     def index_scores(self, stream=None):
         c = self.cfg
-        dsa.dsa_index_scores(self.batch, self.sb.q_idx, c.idx_fmt, self.sb.w, self.k_pool, c.hi, c.di,
+        dsa.dsa_index_scores(self.batch, self.sb.q_idx, self.idx_q_fmt, self.sb.w, self.k_pool, c.hi, c.di,
                              self.scores, self.ld, stream)
 
     def topk(self, stream=None):
@@ -67,7 +70,7 @@ class DSAPath:
 
     def index_topk(self, stream=None):
         c = self.cfg
-        dsa.dsa_index_topk(self.batch, self.sb.q_idx, c.idx_fmt, self.sb.w, self.k_pool, c.hi, c.di, c.topk,
+        dsa.dsa_index_topk(self.batch, self.sb.q_idx, self.idx_q_fmt, self.sb.w, self.k_pool, c.hi, c.di, c.topk,
                            self.idx, self.itk_ws, self.itk_ws_bytes, stream)
 
     def mla(self, layer: int, idx=None, stream=None):

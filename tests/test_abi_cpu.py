@@ -66,6 +66,13 @@ def test_index_scores_validation():
     assert _scores(_batch(), pool=_pool(dsa.DSA_BF16, 128, 256, base=ODD)) == 6
     assert _scores(_batch(), pool=_pool(dsa.DSA_BF16, 128, 128)) == 2  # row stride too small
     assert _scores(_batch(), q_fmt=dsa.DSA_F32, pool=_pool(dsa.DSA_F32, 300, 1200), H=4, D=300) == 3
+    # fp8 queries contract with fp8 keys only, at 64 x 128
+    fp8k = dsa.dsa_pool(FAKE.value, dsa.DSA_FP8_E4M3_B128, 128, 16 * 132, 128)  # codes, then scales
+    assert _scores(_batch(), q_fmt=dsa.DSA_BF16_TO_FP8) == 3                  # bf16 keys
+    assert _scores(_batch(), q_fmt=dsa.DSA_BF16_TO_FP8, pool=fp8k, H=32) == 3
+    assert _scores(_batch(), q_fmt=dsa.DSA_BF16_TO_FP8, pool=fp8k, q=ODD) == 6
+    # a batch whose tables leave no LDS for one unit of staged query rows
+    assert _scores(_batch(B=7000, T=7000, max_q=1), q_fmt=dsa.DSA_BF16_TO_FP8, pool=fp8k) == 3
     bad = _batch()
     bad.page_size = 0
     assert _scores(bad) == 2
