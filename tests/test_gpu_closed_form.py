@@ -17,7 +17,9 @@ rows with a single usable index and rows with none (out = 0, lse = -inf).
 
 The variants: 16-head groups split and unsplit, with draft rows, over bf16,
 fp8 and int8 caches; 64-head groups (64 and 128 heads) split and unsplit in
-decode, and prefill.
+decode, and prefill; unsplit 64-head launches with more row x head-group
+items than CUs over int8 and fp8 caches, with draft rows, more than 256
+requests and a partial last tile.
 """
 import sys
 
@@ -120,6 +122,13 @@ VARIANTS = {
     "h128_prefill": dict(cfg=3, q_len=130, ctx=(1500, 1500), topk=1024, prefill=True),
     "h128_prefill_fp8": dict(cfg=3, q_len=70, ctx=(1500, 1500), topk=1024, prefill=True,
                              kv_fmt=synth.FMT_FP8_E4M3_B128),
+    # 64-head groups, unsplit, more row x head-group items than CUs (several rounds)
+    "h128_rounds_int8": dict(cfg=2, batch=200, ctx=(300, 900), topk=512, layers=1,
+                                 kv_fmt=synth.FMT_INT8_AFFINE_B128),
+    "h128_rounds_drafts_fp8": dict(cfg=4, batch=40, ctx=(1100, 3000), topk=1024),
+    "h128_rounds_300_requests": dict(cfg=2, batch=300, ctx=(300, 1400), topk=600, layers=1),
+    "h128_rounds_prefill_fp8": dict(cfg=3, q_len=200, ctx=(1500, 1500), topk=1024, prefill=True,
+                                        kv_fmt=synth.FMT_FP8_E4M3_B128),
 }
 
 
