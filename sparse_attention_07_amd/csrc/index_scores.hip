@@ -150,11 +150,64 @@ constexpr int kMaxUnitRows = 8;  // query rows scored against one key block
 // result also costs a NaN-quieting v_max_f32 first.
 __device__ inline float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
-template <bool SCALED = false>
+// Where a wave's scores of one block go.  put(r, s, lane, score, valid):
+// lane's token s of unit row r, valid when s is at or before the row's
+// position and its page is mapped; skip(r): row r has no token in the block.
+// GlobalSink stores the valid scores straight into the score rows.
+struct GlobalSink {
+  float* __restrict__ scores;
+  int64_t row0, ld;
+  __device__ void put(int r, int s, int, float score, bool valid) const {
+    if (valid) scores[(row0 + r) * ld + s] = score;
+  }
+  __device__ void skip(int) const {}
+};
+
+// The kernel's dynamic LDS (the same array in every function that names it).
+__device__ inline uint8_t* dyn_lds() {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  return smem;
+}
+
+// The persistent kernel's sink: with `defer` (uniform), the block's scores
+// go to slot slot0 + r of an LDS stage (64 floats each, from byte data_off)
+// and the ballot of valid tokens to the slot's mask (from byte mask_off), to
+// be written out once every key of the segment has been read
+// (flush_scores); otherwise as GlobalSink.  The stage is named by 32-bit LDS
+// offsets: a generic pointer would cost the kernel a register pair it does
+// not have.
+struct ScoreSink {
+  bool defer;
+  uint32_t data_off, mask_off;
+  int slot0;
+  float* __restrict__ scores;
+  int64_t row0, ld;
+  __device__ void put(int r, int s, int lane, float score, bool valid) const {
+    if (defer) {
+      reinterpret_cast<float*>(dyn_lds() + data_off)[(slot0 + r) * kWave + lane] = score;
+      const uint64_t m = __ballot(valid);
+      if (lane == 0) reinterpret_cast<uint64_t*>(dyn_lds() + mask_off)[slot0 + r] = m;
+    } else if (valid) {
+      scores[(row0 + r) * ld + s] = score;
+    }
+  }
+  __device__ void skip(int r) const {
+    if (defer) {
+      // every lane writes the same zero mask; the zero is made here (a
+      // hoisted constant would hold a register pair through the loop)
+      uint32_t z = 0;
+      asm volatile("" : "+v"(z));
+      uint32_t* m = reinterpret_cast<uint32_t*>(dyn_lds() + mask_off) + 2 * (slot0 + r);
+      m[0] = z;
+      m[1] = z;
+    }
+  }
+};
+
+template <bool SCALED, typename Sink>
 __device__ inline void score_block(const Keys& kk, const int64_t (&off)[2], const uint8_t* q_lds,
                                    const float* w_lds, int nr, int s_base, int pos_first,
-                                   int64_t ld_last, float* __restrict__ scores, int64_t row0,
-                                   int64_t ld, int lane, const float* ksc = nullptr) {
+                                   int64_t ld_last, const Sink& sink, int lane, const float* ksc = nullptr) {
   // Unrolled over the at most kMaxUnitRows rows: as a loop with score stores
   // and no loads, the compiler would wait for every load in flight (the next
   // block's keys included) before entering it.
@@ -162,7 +215,10 @@ __device__ inline void score_block(const Keys& kk, const int64_t (&off)[2], cons
   for (int r = 0; r < kMaxUnitRows; ++r) {
     if (r >= nr) break;
     const int pos_r = (int)min<int64_t>((int64_t)pos_first + r, ld_last);
-    if (s_base > pos_r) continue;
+    if (s_base > pos_r) {
+      sink.skip(r);
+      continue;
+    }
     f32x16 acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -211,24 +267,26 @@ __device__ inline void score_block(const Keys& kk, const int64_t (&off)[2], cons
     // a token's non-negative scale factors out of the ReLU and the head sum
     if (SCALED) score *= nt ? ksc[1] : ksc[0];
     const int s = s_base + lane;
-    if (s <= pos_r && (nt ? off[1] : off[0]) >= 0) scores[(row0 + r) * ld + s] = score;
+    sink.put(r, s, lane, score, s <= pos_r && (nt ? off[1] : off[0]) >= 0);
   }
 }
 
 // Scores of one key step from its key registers (fp8 codes are converted to
 // bf16 first and each token's scale applied to its scores).
+template <typename Sink>
 __device__ inline void score_keys(const Keys& kk, const int64_t (&off)[2], const uint8_t* q_lds,
                                   const float* w_lds, int nr, int s_base, int pos_first, int64_t ld_last,
-                                  float* __restrict__ scores, int64_t row0, int64_t ld, int lane) {
-  score_block<false>(kk, off, q_lds, w_lds, nr, s_base, pos_first, ld_last, scores, row0, ld, lane);
+                                  const Sink& sink, int lane) {
+  score_block<false>(kk, off, q_lds, w_lds, nr, s_base, pos_first, ld_last, sink, lane);
 }
 
+template <typename Sink>
 __device__ inline void score_keys(const Keys8& k8, const int64_t (&off)[2], const uint8_t* q_lds,
                                   const float* w_lds, int nr, int s_base, int pos_first, int64_t ld_last,
-                                  float* __restrict__ scores, int64_t row0, int64_t ld, int lane) {
+                                  const Sink& sink, int lane) {
   Keys kk;
   keys_from_fp8(kk, k8);
-  score_block<true>(kk, off, q_lds, w_lds, nr, s_base, pos_first, ld_last, scores, row0, ld, lane, k8.sc);
+  score_block<true>(kk, off, q_lds, w_lds, nr, s_base, pos_first, ld_last, sink, lane, k8.sc);
 }
 
 // fp8 queries against fp8 keys on v_mfma_scale_f32_32x32x64_f8f6f4 (scales
@@ -246,9 +304,10 @@ __device__ inline f32x16 mfma32_fp8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+template <typename Sink>
 __device__ inline void score_keys_fp8q(const Keys8& k8, const int64_t (&off)[2], const uint8_t* q_lds,
                                        const float* w_lds, int nr, int s_base, int pos_first, int64_t ld_last,
-                                       float* __restrict__ scores, int64_t row0, int64_t ld, int lane) {
+                                       const Sink& sink, int lane) {
   i32x8 kb[2][2];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt)
@@ -258,7 +317,10 @@ __device__ inline void score_keys_fp8q(const Keys8& k8, const int64_t (&off)[2],
   for (int r = 0; r < kMaxUnitRows; ++r) {
     if (r >= nr) break;
     const int pos_r = (int)min<int64_t>((int64_t)pos_first + r, ld_last);
-    if (s_base > pos_r) continue;
+    if (s_base > pos_r) {
+      sink.skip(r);
+      continue;
+    }
     const uint8_t* qa = q_lds + r * kRowBytesLds8 + (lane & 31) * kHeadStrideLds8 + (lane >> 5) * 64;
     i32x8 qa8[2][2];
 #pragma unroll
@@ -300,7 +362,7 @@ __device__ inline void score_keys_fp8q(const Keys8& k8, const int64_t (&off)[2],
     const int nt = lane >> 5;
     const float score = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * (nt ? k8.sc[1] : k8.sc[0]);
     const int s = s_base + lane;
-    if (s <= pos_r && (nt ? off[1] : off[0]) >= 0) scores[(row0 + r) * ld + s] = score;
+    sink.put(r, s, lane, score, s <= pos_r && (nt ? off[1] : off[0]) >= 0);
   }
 }
 
@@ -423,7 +485,8 @@ __global__ __launch_bounds__(kThreads, 2) void index_scores_bf16_mfma(
   for (int j = 0; j < kSteps; ++j) {
     const int s_base = k0 + (j * kWaves + wave) * kKeysPerStep;
     if (s_base > pos_last) break;                        // later steps are further right
-    score_keys(kk[j], off[j], q_lds, w_lds, nr, s_base, pos_first, ld_last, scores, row0 - row_lo, ld, lane);
+    score_keys(kk[j], off[j], q_lds, w_lds, nr, s_base, pos_first, ld_last, GlobalSink{scores, row0 - row_lo, ld},
+               lane);
   }
 }
 
@@ -541,19 +604,52 @@ __device__ inline int flat_excl_scan(int v, int* wsum, int& carry, int lane, int
   return before + x - v;
 }
 
+// Segments of at least this many blocks hold their scores back when they fit
+// (for fewer the write burst buys nothing and its latency shows).
+constexpr int kDeferMinBlocks = 64;
+
+// Writes a segment's held-back scores: row r of block lo + b from stage slot
+// b * rg + r, 16 bytes per thread and step, the blocks in order so each
+// row's stores run contiguously; tokens whose mask bit is clear are not
+// written.
+__device__ inline void flush_scores(const float* sdata, const uint64_t* smask, int lo, int hi, int rg, int u0,
+                                    const int* pre, const int* unr, const int* uq0, float* __restrict__ scores,
+                                    int64_t ld, int row_lo, int tid, int nthreads) {
+  const int items = (hi - lo) * rg * 16;
+  int u = u0;
+  for (int q = tid; q < items; q += nthreads) {
+    const int bi = q / (rg * 16), rem = q - bi * rg * 16, r = rem >> 4, c = rem & 15;
+    const int blk = lo + bi;
+    while (pre[u + 1] <= blk) ++u;  // blocks grow with q: walk forward
+    if (r >= unr[u]) continue;
+    const uint32_t bits = (uint32_t)(smask[bi * rg + r] >> (4 * c)) & 0xFu;
+    if (bits == 0) continue;
+    const float* src = sdata + (bi * rg + r) * kWave + 4 * c;
+    float* dst = scores + ((int64_t)uq0[u] - row_lo + r) * ld + (int64_t)(blk - pre[u]) * kKeysPerStep + 4 * c;
+    if (bits == 0xFu && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+      *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<const f32x4*>(src);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((bits >> e) & 1u) dst[e] = src[e];
+    }
+  }
+}
+
 // Scores of one key step: fp8 queries (QFP8, fp8 keys only) on the fp8
 // matrix cores, else score_keys.
-template <bool QFP8, typename K>
+template <bool QFP8, typename K, typename Sink>
 __device__ inline void score_step(const K& kk, const int64_t (&off)[2], const uint8_t* q_lds, const float* w_lds,
-                                  int nr, int s_base, int pos_first, int64_t ld_last, float* __restrict__ scores,
-                                  int64_t row0, int64_t ld, int lane) {
-  if constexpr (QFP8) score_keys_fp8q(kk, off, q_lds, w_lds, nr, s_base, pos_first, ld_last, scores, row0, ld, lane);
-  else score_keys(kk, off, q_lds, w_lds, nr, s_base, pos_first, ld_last, scores, row0, ld, lane);
+                                  int nr, int s_base, int pos_first, int64_t ld_last, const Sink& sink, int lane) {
+  if constexpr (QFP8) score_keys_fp8q(kk, off, q_lds, w_lds, nr, s_base, pos_first, ld_last, sink, lane);
+  else score_keys(kk, off, q_lds, w_lds, nr, s_base, pos_first, ld_last, sink, lane);
 }
 
 // QFP8: the query rows are staged as fp8 codes (stage_fp8_queries) and
 // contracted on the fp8 matrix cores; fp8 keys only.
-template <bool KFP8, bool QFP8>
+// DEFER: segments may hold their scores back (the launcher instantiates it
+// for units of up to four rows; longer units keep the direct stores).
+template <bool KFP8, bool QFP8, bool DEFER>
 __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_lens, int B,
     const int32_t* __restrict__ page_table, int pt_stride, int page_size, int num_pages,
@@ -648,6 +744,20 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
   while (lo < end) {
     const int hi = all_staged ? end : min(end, pre[u0 + 1]);
     const int u_hi = all_staged ? u_last : u0;
+    // The staged-row slots this segment leaves unused hold its scores back
+    // when they all fit: they leave in one burst once every key of the
+    // segment has been read, instead of as 256-byte writes between the key
+    // loads (written between them, decode128's 17.8 MB of scores cost 23-25
+    // us of the stream).
+    const int n_used = u_hi - u0 + 1;
+    const size_t free_bytes = (size_t)(nslots - n_used) * rg * kQRowBytes<QFP8>;
+    const bool defer = DEFER && hi - lo >= kDeferMinBlocks &&
+                       (size_t)(hi - lo) * rg * (kWave * sizeof(float) + sizeof(uint64_t)) <= free_bytes;
+    // (scalar: the values come from LDS tables the compiler cannot see are uniform)
+    const uint32_t sdata_off = __builtin_amdgcn_readfirstlane((uint32_t)(q_area - smem) +
+                                                             (uint32_t)n_used * rg * kQRowBytes<QFP8>);
+    const uint32_t smask_off =
+        __builtin_amdgcn_readfirstlane(sdata_off + (uint32_t)(hi - lo) * rg * kWave * sizeof(float));
     // This wave's blocks lo + wave + 8 i < hi.  A, B, C: the block being scored
     // and the next two (keys of B in flight, page ids of C in flight).  The
     // first three blocks' page ids go out together; then A's keys, the
@@ -695,10 +805,22 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
     wait_vmcnt<kLoadsPerStep<KFP8>>();
     lds_barrier();
 
-#define DSA_SCORE(KK, X)                                                                           \
-  score_step<QFP8>(KK, X.off, q_area + (size_t)(X.u - u0) * rg * kQRowBytes<QFP8>,                \
-              w_area + (size_t)(X.u - u0) * rg * kHeads, unr[X.u], X.tok, upf[X.u], ld_last, scores, \
-              (int64_t)uq0[X.u] - row_lo, ld, lane)
+    // JB: the block's number; past the range (a placeholder block, no valid
+    // token) nothing is written anywhere
+#define DSA_SCORE(KK, X, JB)                                                                         \
+  do {                                                                                               \
+    const uint8_t* qx = q_area + (size_t)(X.u - u0) * rg * kQRowBytes<QFP8>;                        \
+    const float* wx = w_area + (size_t)(X.u - u0) * rg * kHeads;                                     \
+    if constexpr (DEFER)                                                                             \
+      score_step<QFP8>(KK, X.off, qx, wx, unr[X.u], X.tok, upf[X.u], ld_last,                        \
+                       ScoreSink{defer && (JB) < hi, sdata_off, smask_off,                           \
+                                 __builtin_amdgcn_readfirstlane(((JB) - lo) * rg), scores,           \
+                                 (int64_t)uq0[X.u] - row_lo, ld},                                    \
+                       lane);                                                                        \
+    else                                                                                             \
+      score_step<QFP8>(KK, X.off, qx, wx, unr[X.u], X.tok, upf[X.u], ld_last,                        \
+                       GlobalSink{scores, (int64_t)uq0[X.u] - row_lo, ld}, lane);                    \
+  } while (0)
     // Each step issues the page ids two blocks ahead, then the keys one block
     // ahead (into the registers just scored), whether or not those blocks
     // exist, so the compiler's waits before scoring cover exactly the block
@@ -709,7 +831,7 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
     // steps each issue loads and then score: every scoring then follows its
     // own wait on the same path.
     wait_vmcnt<kLoadsPerStep<KFP8>>();  // all but the newest block's keys
-    DSA_SCORE(k0, A);
+    DSA_SCORE(k0, A, j);
     while (j + kFlatWaves < hi) {
       j += kFlatWaves;
       A = Bk;
@@ -722,7 +844,7 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
       load_keys(k0, Bk.off, k_base, lane, Bk.tok, page_size, k_row_stride);
       asm volatile("" ::: "memory");
       wait_vmcnt<kLoadsPerStep<KFP8>>();
-      DSA_SCORE(k1, A);
+      DSA_SCORE(k1, A, j);
       if (j + kFlatWaves >= hi) break;
       j += kFlatWaves;
       A = Bk;
@@ -735,11 +857,16 @@ __global__ __launch_bounds__(kFlatThreads, 1) void index_scores_flat(
       load_keys(k1, Bk.off, k_base, lane, Bk.tok, page_size, k_row_stride);
       asm volatile("" ::: "memory");
       wait_vmcnt<kLoadsPerStep<KFP8>>();
-      DSA_SCORE(k0, A);
+      DSA_SCORE(k0, A, j);
     }
 #undef DSA_SCORE
 #undef DSA_FINISH
-    lds_barrier();  // every wave is done with the staged rows
+    lds_barrier();  // every wave is done with the staged rows and the stage
+    if (DEFER && defer) {
+      flush_scores(reinterpret_cast<const float*>(smem + sdata_off), reinterpret_cast<const uint64_t*>(smem + smask_off),
+                   lo, hi, rg, u0, pre, unr, uq0, scores, ld, row_lo, tid, kFlatThreads);
+      lds_barrier();  // the stage is read before the next segment's copies land there
+    }
     lo = hi;
     if (lo < end) u0 = last_at_or_below(pre, n_units, lo);
   }
@@ -783,6 +910,20 @@ __global__ __launch_bounds__(256) void index_scores_f32_valu(
 
 namespace {
 
+template <bool KFP8, bool QFP8, bool DEFER>
+hipError_t launch_flat(const BatchArgs& ba, const void* q_idx, const float* w, const PoolArgs& pool,
+                       float* scores, int64_t ld, hipStream_t stream, int row_lo, int row_hi, int rg,
+                       int nslots, int64_t u_max, size_t lds) {
+  hipError_t e = ensure_max_lds(reinterpret_cast<const void*>(index_scores_flat<KFP8, QFP8, DEFER>));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((index_scores_flat<KFP8, QFP8, DEFER>), dim3(device_cu_count()), dim3(kFlatThreads), lds,
+                     stream, ba.cu_q, ba.seq_lens, ba.batch, ba.page_table, ba.pt_stride, ba.page_size,
+                     ba.num_pages, static_cast<const uint16_t*>(q_idx), w,
+                     static_cast<const uint8_t*>(pool.base), pool.page_stride, pool.row_stride,
+                     scores, ld, rg, nslots, (int)u_max, row_lo, row_hi);
+  return hipGetLastError();
+}
+
 template <bool KFP8, bool QFP8>
 hipError_t launch_index_scores_mfma(const BatchArgs& ba, const void* q_idx, const float* w,
                                     const PoolArgs& pool, float* scores, int64_t ld,
@@ -799,16 +940,17 @@ hipError_t launch_index_scores_mfma(const BatchArgs& ba, const void* q_idx, cons
     const size_t avail = tables < 160 * 1024 ? 160 * 1024 - tables : 0;
     const int nslots = (int)std::min<size_t>(8, avail / per_unit);
     const size_t lds = tables + (size_t)nslots * per_unit;
-    if (nslots >= 1) {
-      hipError_t e = ensure_max_lds(reinterpret_cast<const void*>(index_scores_flat<KFP8, QFP8>));
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((index_scores_flat<KFP8, QFP8>), dim3(device_cu_count()), dim3(kFlatThreads), lds, stream,
-                         ba.cu_q, ba.seq_lens, ba.batch, ba.page_table, ba.pt_stride, ba.page_size,
-                         ba.num_pages, static_cast<const uint16_t*>(q_idx), w,
-                         static_cast<const uint8_t*>(pool.base), pool.page_stride, pool.row_stride,
-                         scores, ld, rg, nslots, (int)u_max, row_lo, row_hi);
-      return hipGetLastError();
-    }
+    // Units of up to four rows (decode, short drafts) may hold their scores
+    // back when a workgroup's share can reach kDeferMinBlocks blocks (bounded
+    // from the host's batch bounds); longer units, and launches too small for
+    // that, store them as they are made.
+    const int64_t max_blocks = u_max * (((int64_t)ba.max_seq_len + kKeysPerStep - 1) / kKeysPerStep);
+    const bool defer = rg <= 4 && max_blocks >= (int64_t)kDeferMinBlocks * device_cu_count();
+    if (nslots >= 1)
+      return defer ? launch_flat<KFP8, QFP8, true>(ba, q_idx, w, pool, scores, ld, stream, row_lo, row_hi, rg,
+                                                    nslots, u_max, lds)
+                   : launch_flat<KFP8, QFP8, false>(ba, q_idx, w, pool, scores, ld, stream, row_lo, row_hi, rg,
+                                                     nslots, u_max, lds);
   }
   // fp8 queries have no grid form: the API refuses such launches up front
   // (index_scores_fp8q_fits)
