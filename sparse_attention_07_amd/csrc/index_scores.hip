@@ -499,7 +499,9 @@ __global__ __launch_bounds__(kThreads, 2) void index_scores_bf16_mfma(
 // in segments of one unit: the unit's query rows and weights are staged in LDS
 // (all units of the share at once when they fit), then wave w scores blocks
 // w, w+8, ... of the segment with the page lookups two blocks ahead and the
-// key loads one block ahead.
+// key loads one block ahead.  A segment's scores go straight to the score
+// rows, or (DEFER) are held in the staged-row slots the segment leaves
+// unused and written in one burst once its keys are read.
 constexpr int kFlatWaves = 8;
 constexpr int kFlatThreads = kFlatWaves * kWave;
 
