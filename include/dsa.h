@@ -289,6 +289,9 @@ size_t dsa_sparse_mla_workspace_bytes(int32_t num_q_rows, int32_t n_heads, int32
  *
  * A j is usable when 0 <= idx[t,j] <= pos(t) and its page is mapped; others
  * are skipped.  A row with no usable j gives out = 0 and lse = -inf.
+ * sm_scale must be positive, with sm_scale * log2(e) finite (the kernels take
+ *          the maximum of the unscaled dot products and scale it, in log2
+ *          units); DSA_ERR_UNSUPPORTED otherwise.
  * q        device [T, n_heads, dc+dr], format q_format, contiguous
  * kv       latent pool, dim == dc+dr
  * idx      device [T, k] int32 (the dsa_topk output, or a shared layer's copy)

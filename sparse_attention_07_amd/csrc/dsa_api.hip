@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <map>
 #include <mutex>
 #include <set>
@@ -215,6 +216,9 @@ dsa_status sparse_mla(const dsa_batch* batch, const void* q, int32_t q_format, c
   if (q == nullptr || kv == nullptr || idx == nullptr || out == nullptr) return DSA_ERR_NULL;
   if (k < 1 || n_heads < 1 || dc < 1 || dr < 0) return DSA_ERR_SHAPE;
   if (kv->dim != dc + dr) return DSA_ERR_SHAPE;
+  // the kernels take the maximum of the unscaled scores and scale it, and
+  // work in log2 units (sm_scale * log2 e must stay finite)
+  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale * 1.4426950408889634f)) return DSA_ERR_UNSUPPORTED;
   if (!aligned(idx, 4) || (lse != nullptr && !aligned(lse, 4))) return DSA_ERR_ALIGN;
   PoolArgs pa;
   if (q_format == DSA_BF16 && (kv->format == DSA_BF16 || kv->format == DSA_FP8_E4M3_B128 ||

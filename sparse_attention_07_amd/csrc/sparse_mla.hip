@@ -860,15 +860,22 @@ __device__ inline void h64_role(const MlaArgs& a, const H64Lds& L, const int64_t
   Stage<F> st[G ? kH64Stages : 1];
 
   // Score waves: S^T of the tile (A operand: lane row l32, dims 16 ks + 8 hb
-  // .. +7, read from LDS eight k steps ahead; B: q); then the online-softmax
+  // .. +7, read from LDS four k steps ahead; B: q); then the online-softmax
   // step.  D lane (l32, hb) register i holds
   // tile row 8 (i / 4) + 4 hb + i % 4 of head 32 g + l32.  The running max is
   // raised (O and l rescaled) only when the tile beats it by more than
   // kRescaleSlack; the decision is taken per wave, and the factors (1 for
   // heads not raised) go to LDS with a flag.  P goes to `slot` as bf16,
   // registers 8 ks .. 8 ks + 7 as k step ks of the PV operand.
+  // * The MFMAs form one accumulator chain, so each waits for its A operand:
+  //   the scheduling barrier after every step keeps each read four steps
+  //   ahead of its MFMA (left to itself the compiler issues the reads in
+  //   pairs right before their MFMAs, and every pair waits out a whole LDS
+  //   round trip: 640 against 570 us for three decode128 layers).
+  // * The scale (positive, checked by the caller) is applied in the exponent's
+  //   fma: the maximum of the scaled scores is the scaled maximum.
   auto qk_softmax = [&](const uint8_t* tl, uint32_t valid, int slot) {
-    constexpr int kAhead = 8;
+    constexpr int kAhead = 4;
     const uint8_t* ap = tl + l32 * kRowLds + 16 * hb;
     bf16x8 ra[kAhead];
 #pragma unroll
@@ -876,24 +883,25 @@ __device__ inline void h64_role(const MlaArgs& a, const H64Lds& L, const int64_t
     f32x16 c = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < kQSteps; ++ks) {
-      const bf16x8 av = ra[ks % kAhead];
+      c = mfma32(ra[ks % kAhead], q[S ? ks : 0], c);
       if (ks + kAhead < kQSteps) ra[ks % kAhead] = lds16(ap + 32 * (ks + kAhead));
-      c = mfma32(av, q[S ? ks : 0], c);
+      __builtin_amdgcn_sched_barrier(0);
     }
     float sv[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sv[i] = c[i] * a.scale_log2;
+    for (int i = 0; i < 16; ++i) sv[i] = c[i];
     if (valid != 0xFFFFFFFFu) {                // a partial tile (uniform branch)
+      // this lane half's rows: bit 8 (i / 4) + i % 4 of vs (literal masks,
+      // nothing kept in registers across the loop)
+      const uint32_t vs = valid >> (4 * hb);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = 8 * (i >> 2) + 4 * hb + (i & 3);
-        if (!((valid >> row) & 1u)) sv[i] = kNegInf;
-      }
+      for (int i = 0; i < 16; ++i)
+        if (!(vs & (1u << (8 * (i >> 2) + (i & 3))))) sv[i] = kNegInf;
     }
     float m = sv[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) m = fmaxf(m, sv[i]);
-    m = max_over_halves(m);
+    m = max_over_halves(m) * a.scale_log2;
     const bool raise = m > m_run + kRescaleSlack;
     const bool any_raise = __any(raise);
     if (any_raise) {
@@ -910,7 +918,8 @@ __device__ inline void h64_role(const MlaArgs& a, const H64Lds& L, const int64_t
     u32x4 pk[2];
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
-      const float p0 = exp2_fast(sv[i] - mu), p1 = exp2_fast(sv[i + 1] - mu);
+      const float p0 = exp2_fast(fmaf(sv[i], a.scale_log2, -mu));
+      const float p1 = exp2_fast(fmaf(sv[i + 1], a.scale_log2, -mu));
       l_run += p0 + p1;
       pk[i >> 3][(i & 7) >> 1] = pack_bf16x2(p0, p1);
     }

@@ -222,11 +222,11 @@ def test_topk_validation():
 
 
 def _mla(batch, q_fmt=dsa.DSA_BF16, pool=None, k=2048, H=128, dc=512, dr=64, ws=None, ws_bytes=0,
-         q=FAKE, out=FAKE, prefill=False):
+         q=FAKE, out=FAKE, prefill=False, scale=0.07):
     pool = pool or _pool(dsa.DSA_BF16, 576, 1152)
     fn = L.dsa_sparse_mla_prefill if prefill else L.dsa_sparse_mla_decode
     return fn(ctypes.byref(batch) if batch is not None else None, q, q_fmt, ctypes.byref(pool), FAKE,
-              k, H, dc, dr, 0.07, out, None, ws, ws_bytes, None)
+              k, H, dc, dr, scale, out, None, ws, ws_bytes, None)
 
 
 def test_sparse_mla_validation():
@@ -250,6 +250,17 @@ def test_sparse_mla_validation():
     # prefill never splits
     assert dsa.dsa_sparse_mla_workspace_bytes(4, 128, 2048, 512, True) == 0
     assert dsa.dsa_sparse_mla_workspace_bytes(4096, 128, 2048, 512, False) == 0
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.0, -0.07, float("nan"), float("inf"), 3e38])
+def test_sparse_mla_refuses_scales_that_are_not_positive_and_finite(scale):
+    # the kernels scale the maximum of the unscaled scores, in log2 units
+    assert _mla(_batch(), scale=scale, prefill=True) == 3
+    assert _mla(_batch(), scale=scale, q_fmt=dsa.DSA_F32, pool=_pool(dsa.DSA_F32, 576, 2304),
+                prefill=True) == 3
+    assert _mla_static(_batch(), scale=scale) == 3
+    # a tiny positive scale passes and reaches the later checks
+    assert _mla(_batch(), scale=1e-30, q=ODD, prefill=True) == 6
 
 
 MAX64 = 5184   # rows one 64-head workgroup can attend (documented in dsa.h)
@@ -290,10 +301,11 @@ def test_split_workspace_is_consistent(T, H, k):
         assert 2 <= splits <= min(64, max(1, k // 256))
 
 
-def _mla_static(batch, q_fmt=dsa.DSA_BF16, pool=None, k=2048, H=128, dc=512, dr=64, q=FAKE, out=FAKE):
+def _mla_static(batch, q_fmt=dsa.DSA_BF16, pool=None, k=2048, H=128, dc=512, dr=64, q=FAKE, out=FAKE,
+                scale=0.07):
     pool = pool or _pool(dsa.DSA_BF16, 576, 1152)
     st = L.dsa_sparse_mla_decode_static(ctypes.byref(batch) if batch is not None else None, q, q_fmt,
-                                        ctypes.byref(pool), FAKE, k, H, dc, dr, 0.07, out, None, None)
+                                        ctypes.byref(pool), FAKE, k, H, dc, dr, scale, out, None, None)
     assert st != 5, "a validation case got as far as the device"
     return st
 
