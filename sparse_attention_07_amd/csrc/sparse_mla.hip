@@ -99,17 +99,14 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // Four e4m3 bytes (one dword, byte 0 first) -> four bf16 of e4m3 * sc.  The
-// hardware conversion at scale 1 is exact (every e4m3 value is a bf16; its
-// scale operand only takes a power of two), then the block scale is applied
-// in f32 and rounded to bf16 once -- the same value as decoding e4m3 into f32
-// and rounding the product.
+// hardware conversion to f32 at scale 1 is exact (its scale operand only
+// takes a power of two), then the block scale is applied in f32 and the
+// product rounded to bf16 once: two conversions, four multiplies and two
+// packs per four codes.
 __device__ inline uint2 fp8x4_to_bf16x4(uint32_t x, float sc) {
-  const uint32_t a = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false));
-  const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true));
-  uint2 r;
-  r.x = pack_bf16x2(__uint_as_float(a << 16) * sc, __uint_as_float(a & 0xFFFF0000u) * sc);
-  r.y = pack_bf16x2(__uint_as_float(b << 16) * sc, __uint_as_float(b & 0xFFFF0000u) * sc);
-  return r;
+  const auto a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(x, 1.0f, false);  // bytes 0, 1
+  const auto b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(x, 1.0f, true);   // bytes 2, 3
+  return uint2{pack_bf16x2(a[0] * sc, a[1] * sc), pack_bf16x2(b[0] * sc, b[1] * sc)};
 }
 
 // Four unsigned 8-bit codes (one dword, byte 0 first) -> four bf16 of
