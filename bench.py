@@ -81,16 +81,16 @@ def parse():
 # Copy calibration of those runs: FETCH_SIZE x 2.000, WRITE_SIZE x 1.000.
 TRAFFIC = {
     ("decode128", "index_scores"): {"src": "ed9bbcfdbb2c6e95", "fetch_bytes": 1153000000.0, "write_bytes": 17840000.0, "dispatches": 50},
-    ("decode128", "sparse_mla"): {"src": "4baa29cd2fcd7401", "fetch_bytes": 646000000.0, "write_bytes": 33690000.0, "dispatches": 150},
+    ("decode128", "sparse_mla"): {"src": "94deeeeeb4ee34d3", "fetch_bytes": 645700000.0, "write_bytes": 33690000.0, "dispatches": 150},
     ("decode128", "topk"): {"src": "fe973313bb18ed5f", "fetch_bytes": 18690000.0, "write_bytes": 2097000.0, "dispatches": 50},
-    ("decode16", "index_scores"): {"src": "ed9bbcfdbb2c6e95", "fetch_bytes": 81180000.0, "write_bytes": 1182000.0, "dispatches": 49},
-    ("decode16", "sparse_mla"): {"src": "4baa29cd2fcd7401", "fetch_bytes": 157000000.0, "write_bytes": 5290000.0, "dispatches": 49},
+    ("decode16", "index_scores"): {"src": "ed9bbcfdbb2c6e95", "fetch_bytes": 81190000.0, "write_bytes": 1182000.0, "dispatches": 49},
+    ("decode16", "sparse_mla"): {"src": "94deeeeeb4ee34d3", "fetch_bytes": 157000000.0, "write_bytes": 5290000.0, "dispatches": 49},
     ("decode16", "topk"): {"src": "fe973313bb18ed5f", "fetch_bytes": 2290000.0, "write_bytes": 524300.0, "dispatches": 49},
     ("mtp_fp8", "index_scores"): {"src": "ed9bbcfdbb2c6e95", "fetch_bytes": 848200000.0, "write_bytes": 64380000.0, "dispatches": 43},
-    ("mtp_fp8", "sparse_mla"): {"src": "4baa29cd2fcd7401", "fetch_bytes": 346600000.0, "write_bytes": 63350000.0, "dispatches": 43},
-    ("mtp_fp8", "topk"): {"src": "fe973313bb18ed5f", "fetch_bytes": 84340000.0, "write_bytes": 11800000.0, "dispatches": 43},
-    ("prefill", "index_scores"): {"src": "ed9bbcfdbb2c6e95", "fetch_bytes": 885500000.0, "write_bytes": 302100000.0, "dispatches": 50},
-    ("prefill", "sparse_mla"): {"src": "4baa29cd2fcd7401", "fetch_bytes": 5243000000.0, "write_bytes": 539000000.0, "dispatches": 50},
+    ("mtp_fp8", "sparse_mla"): {"src": "94deeeeeb4ee34d3", "fetch_bytes": 345800000.0, "write_bytes": 63350000.0, "dispatches": 43},
+    ("mtp_fp8", "topk"): {"src": "fe973313bb18ed5f", "fetch_bytes": 85520000.0, "write_bytes": 11800000.0, "dispatches": 43},
+    ("prefill", "index_scores"): {"src": "ed9bbcfdbb2c6e95", "fetch_bytes": 885400000.0, "write_bytes": 302100000.0, "dispatches": 50},
+    ("prefill", "sparse_mla"): {"src": "94deeeeeb4ee34d3", "fetch_bytes": 5241000000.0, "write_bytes": 539000000.0, "dispatches": 50},
     ("prefill", "topk"): {"src": "fe973313bb18ed5f", "fetch_bytes": 335800000.0, "write_bytes": 33550000.0, "dispatches": 50},
 }
 KERNEL_SOURCES = {"sparse_mla": ["sparse_mla.hip", "dsa_device.h"],
